@@ -1,0 +1,191 @@
+"""ctypes binding of libdflash.so: argument marshalling only.
+
+Every step of the draft path runs in the library's HIP kernels; this module
+passes device pointers (torch tensors' data_ptr()), sizes and the current HIP
+stream, and turns negative status codes into exceptions.  PyTorch supplies
+device memory and streams.  There is no CPU fallback: if the library is missing
+it is built, and if it cannot be loaded the call fails.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdflash.so")
+MAX_LAYERS = 8
+BLOCK = 8
+
+W_Q4K, W_BF16 = 0, 1
+PROBE_NONE, PROBE_LM_HEAD, PROBE_FFN_GATE_UP = 0, 1, 2
+
+c_int, c_float, c_void_p, c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, c_int) for n in ("n_layers", "hidden", "ffn", "n_q_heads", "n_kv_heads",
+                                     "head_dim", "window", "vocab", "n_taps", "block", "top_k",
+                                     "sel_rank", "weight_fmt")] + \
+               [(n, c_float) for n in ("rms_eps", "rope_theta", "pair_scale")]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("wq", "wk", "wv", "wo", "wg", "wu", "wd", "in_norm",
+                                        "post_norm", "q_norm", "k_norm", "w_conv")]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("fc", c_void_p), ("hidden_norm", c_void_p),
+                ("layer", LayerWeights * MAX_LAYERS)] + \
+               [(n, c_void_p) for n in ("final_norm", "embed", "lm_head", "mask_emb", "sel_proj",
+                                        "code_a", "code_b")]
+
+
+class Probe(ctypes.Structure):
+    _fields_ = [("kernel", c_int), ("layer", c_int), ("ev_start", c_void_p), ("ev_stop", c_void_p)]
+
+
+class DflashError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib():
+    """Load libdflash.so (building it first if it is not there)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build
+        build.build()
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    L.dflash_workspace_bytes.argtypes = [P(Config), c_int, c_int]
+    L.dflash_workspace_bytes.restype = c_size_t
+    L.dflash_draft_step.argtypes = [P(Config), P(Weights), c_int, c_void_p, c_int, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, P(Probe),
+                                    c_void_p]
+    L.dflash_draft_step.restype = c_int
+    L.dflash_verify_prefix.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p,
+                                       c_void_p]
+    L.dflash_verify_prefix.restype = c_int
+    L.q4k_gemm_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    L.q4k_gemm_workspace_bytes.restype = c_size_t
+    L.q4k_gemm.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_size_t,
+                           c_void_p]
+    L.q4k_gemm.restype = c_int
+    L.q4k_dequantize.argtypes = [c_void_p, c_void_p, ctypes.c_longlong, c_void_p]
+    L.q4k_dequantize.restype = c_int
+    L.dflash_status_str.argtypes = [c_int]
+    L.dflash_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+EXPORTS = ["dflash_workspace_bytes", "dflash_draft_step", "dflash_verify_prefix",
+           "q4k_gemm_workspace_bytes", "q4k_gemm", "q4k_dequantize", "dflash_status_str"]
+
+
+def check(rc):
+    if rc != 0:
+        raise DflashError(f"dflash status {rc}: {lib().dflash_status_str(rc).decode()}")
+
+
+def make_config(shape):
+    """Config struct from a synth.Shape-like object."""
+    return Config(shape.n_layers, shape.hidden, shape.ffn, shape.n_q, shape.n_kv, shape.head_dim,
+                  shape.window, shape.vocab, shape.n_taps, shape.block, shape.top_k,
+                  shape.sel_rank, W_Q4K if shape.weight_fmt == "q4k" else W_BF16,
+                  shape.rms_eps, shape.rope_theta, shape.pair_scale)
+
+
+def workspace_bytes(cfg, batch, t_new):
+    n = lib().dflash_workspace_bytes(ctypes.byref(cfg), batch, t_new)
+    if n == 0:
+        raise DflashError("unsupported configuration")
+    return n
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class DeviceWeights:
+    """Drafter weights resident in device memory, plus the C struct pointing at them.
+
+    `W` is the host weight dict of synth.make_weights (linear weights as
+    ("q4k", bytes) or ("bf16", uint16 array); the rest uint16 arrays).
+    """
+
+    def __init__(self, shape, W, device="cuda"):
+        import torch
+        self.shape = shape
+        self.tensors = {}
+        shared = {}
+
+        def up(name, arr):
+            arr = np.ascontiguousarray(arr)
+            key = arr.__array_interface__["data"][0]
+            if key in shared:                      # tied embedding / output head
+                t = shared[key]
+            else:
+                dt = torch.uint8 if arr.dtype == np.uint8 else torch.int16
+                t = torch.from_numpy(arr.view(np.uint8 if arr.dtype == np.uint8 else np.int16))
+                t = t.to(device, dtype=dt)
+                shared[key] = t
+            self.tensors[name] = t
+            return t.data_ptr()
+
+        s = Weights()
+        for name, val in W.items():
+            arr = val[1] if isinstance(val, tuple) else val
+            p = up(name, arr)
+            if name.startswith("l"):
+                l, field = name[1:].split(".", 1)
+                setattr(s.layer[int(l)], field, p)
+            else:
+                setattr(s, name, p)
+        self.struct = s
+
+
+def draft_step(cfg, dw, taps, last_token, ctx_len, k_cache, v_cache, draft_tokens, cand_ids,
+               cand_logp, workspace, dbg_hidden=None, dbg_logits=None, probe=None):
+    """Enqueue one draft step on the current stream (all arguments torch tensors on device)."""
+    B, t_new = taps.shape[0], taps.shape[1]
+    cap = k_cache.shape[3]
+    rc = lib().dflash_draft_step(ctypes.byref(cfg), ctypes.byref(dw.struct), B, _ptr(taps), t_new,
+                                 _ptr(last_token), _ptr(ctx_len), _ptr(k_cache), _ptr(v_cache),
+                                 cap, _ptr(draft_tokens), _ptr(cand_ids), _ptr(cand_logp),
+                                 _ptr(dbg_hidden), _ptr(dbg_logits), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(),
+                                 None if probe is None else ctypes.byref(probe), _stream())
+    check(rc)
+
+
+def verify_prefix(draft, target, accept_len, out_tokens):
+    B, n = draft.shape
+    check(lib().dflash_verify_prefix(_ptr(draft), _ptr(target), B, n, _ptr(accept_len),
+                                     _ptr(out_tokens), _stream()))
+
+
+def q4k_gemm(w, x, y, workspace):
+    M, K = x.shape
+    N = y.shape[1]
+    check(lib().q4k_gemm(_ptr(w), _ptr(x), _ptr(y), M, N, K, _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream()))
+
+
+def q4k_gemm_workspace_bytes(M, N, K):
+    return lib().q4k_gemm_workspace_bytes(M, N, K)
+
+
+def q4k_dequantize(w, out):
+    check(lib().q4k_dequantize(_ptr(w), _ptr(out), out.numel() // 256, _stream()))

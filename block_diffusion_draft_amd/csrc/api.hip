@@ -1,0 +1,414 @@
+// C ABI of the draft-step library: argument checks, workspace plan and the
+// launch sequence of one step on the caller's stream.  Nothing is allocated.
+#include "../../include/dflash.h"
+#include "kernels.h"
+
+#include <string.h>
+
+int topk_chunk_size();
+
+namespace {
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+    int B, T, P, t_new, H, F, n_q, n_kv, d, qd, kd, V, K, r, L;
+    int M_blk, M_ctx, M_qkv, R, G, QR;
+    int attn_chunk, attn_nch;
+    int topk_nch;
+    bool lm_skinny;
+    // byte offsets into the workspace
+    size_t o_valid, o_h, o_xc, o_fcout, o_qkv, o_Q, o_Kb, o_Vb, o_attnO, o_attnML, o_Y, o_mid,
+        o_f, o_logits, o_pv, o_pi, o_pm, o_ps, o_part;
+    size_t total;
+};
+
+size_t gemm_part_bytes(int fmt, int M, int N, int K) {
+    if (fmt == DFLASH_W_Q4K) {
+        const Q4kPlan p = q4k_plan(M, N, K);
+        return (size_t)p.splits * M * N * 4;
+    }
+    return (size_t)M * N * 4;
+}
+
+bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
+    p.B = B;
+    p.T = c->block;
+    p.P = c->block - 1;
+    p.t_new = t_new;
+    p.H = c->hidden;
+    p.F = c->ffn;
+    p.n_q = c->n_q_heads;
+    p.n_kv = c->n_kv_heads;
+    p.d = c->head_dim;
+    p.qd = p.n_q * p.d;
+    p.kd = p.n_kv * p.d;
+    p.V = c->vocab;
+    p.K = c->top_k;
+    p.r = c->sel_rank;
+    p.L = c->n_layers;
+    p.M_blk = B * p.T;
+    p.M_ctx = B * t_new;
+    p.M_qkv = p.M_blk + p.M_ctx;
+    p.R = B * p.P;
+    p.G = p.n_q / p.n_kv;
+    p.QR = p.G * p.T;
+    // keys per attention workgroup: 64 at batch 1 (more workgroups), larger when
+    // the batch already fills the chip (fewer partials to merge)
+    const int win = c->window;
+    const long long wgs64 = (long long)B * p.n_kv * ((win + 63) / 64);
+    p.attn_chunk = wgs64 >= 16384 ? 256 : (wgs64 >= 4096 ? 128 : 64);
+    p.attn_nch = win > 0 ? (win + p.attn_chunk - 1) / p.attn_chunk : 0;
+    p.topk_nch = (p.V + topk_chunk_size() - 1) / topk_chunk_size();
+    p.lm_skinny = p.R <= 16 && p.H <= 5120 && p.H % 128 == 0;
+
+    size_t part = 0;
+    const int fmt = c->weight_fmt;
+    auto upd = [&](size_t x) { if (x > part) part = x; };
+    upd(gemm_part_bytes(fmt, p.M_ctx, p.H, c->n_taps * p.H));
+    upd(gemm_part_bytes(fmt, p.M_qkv, p.qd + 2 * p.kd, p.H));
+    upd(gemm_part_bytes(fmt, p.M_blk, p.H, p.qd));
+    upd(gemm_part_bytes(fmt, p.M_blk, 2 * p.F, p.H));
+    upd(gemm_part_bytes(fmt, p.M_blk, p.H, p.F));
+
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+    p.o_valid = take((size_t)B * 4);
+    p.o_h = take((size_t)p.M_blk * p.H * 4);
+    p.o_xc = take((size_t)p.M_qkv * p.H * 2);
+    p.o_fcout = take((size_t)p.M_ctx * p.H * 4);
+    p.o_qkv = take((size_t)p.M_qkv * (p.qd + 2 * p.kd) * 4);
+    p.o_Q = take((size_t)p.M_blk * p.qd * 2);
+    p.o_Kb = take((size_t)p.M_blk * p.kd * 2);
+    p.o_Vb = take((size_t)p.M_blk * p.kd * 2);
+    const size_t nslots = (size_t)B * p.n_kv * (p.attn_nch + 1) * p.QR;
+    p.o_attnO = take(nslots * p.d * 4);
+    p.o_attnML = take(nslots * 2 * 4);
+    p.o_Y = take((size_t)p.M_blk * p.qd * 2);
+    p.o_mid = take((size_t)p.M_blk * p.F * 2);
+    p.o_f = take((size_t)p.R * p.H * 2);
+    p.o_logits = take((size_t)p.R * p.V * 4);
+    p.o_pv = take((size_t)p.R * p.topk_nch * p.K * 4);
+    p.o_pi = take((size_t)p.R * p.topk_nch * p.K * 4);
+    p.o_pm = take((size_t)p.R * p.topk_nch * 4);
+    p.o_ps = take((size_t)p.R * p.topk_nch * 4);
+    p.o_part = take(part);
+    p.total = o;
+    return true;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+int check_config(const dflash_config *c) {
+    if (!c) return DFLASH_EINVAL;
+    if (c->n_layers < 1 || c->n_layers > DFLASH_MAX_LAYERS) return DFLASH_ESHAPE;
+    if (c->hidden <= 0 || c->hidden % 256 || c->ffn <= 0 || c->ffn % 256) return DFLASH_ESHAPE;
+    if (c->head_dim != 64 && c->head_dim != 128) return DFLASH_ESHAPE;
+    if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->n_q_heads % c->n_kv_heads) return DFLASH_ESHAPE;
+    if (c->n_q_heads / c->n_kv_heads > 4) return DFLASH_ESHAPE;
+    const int qd = c->n_q_heads * c->head_dim;
+    if (qd % 256 || qd > 8192) return DFLASH_ESHAPE;
+    if (c->block != DFLASH_BLOCK) return DFLASH_ESHAPE;
+    if (c->n_taps < 1 || c->n_taps > 16) return DFLASH_ESHAPE;
+    if (c->top_k < 1 || c->top_k > DFLASH_MAX_TOPK) return DFLASH_ESHAPE;
+    if (c->vocab < c->top_k || c->vocab % 16) return DFLASH_ESHAPE;
+    // the candidate merge holds at most 2048 (chunk, rank) entries per row
+    if ((long long)((c->vocab + topk_chunk_size() - 1) / topk_chunk_size()) * c->top_k > 2048)
+        return DFLASH_ESHAPE;
+    if (c->sel_rank < 8 || c->sel_rank % 8 || c->sel_rank > 512) return DFLASH_ESHAPE;
+    if (c->window < 0) return DFLASH_EINVAL;
+    if (c->weight_fmt != DFLASH_W_Q4K && c->weight_fmt != DFLASH_W_BF16) return DFLASH_EINVAL;
+    if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return DFLASH_EINVAL;
+    return DFLASH_OK;
+}
+
+#define HIPCHK(x)                                 \
+    do {                                          \
+        if ((x) != hipSuccess) return DFLASH_EHIP; \
+    } while (0)
+
+struct Ctx {
+    const dflash_config *c;
+    const Plan *p;
+    unsigned char *ws;
+    hipStream_t st;
+    template <class T> T *at(size_t off) const { return reinterpret_cast<T *>(ws + off); }
+};
+
+// y = A . W^T over up to 3 stacked weight matrices, then the reduction epilogue
+int run_gemm(const Ctx &x, const void *const *w, const int *seg_n, int nseg, const uint16_t *A,
+             int lda, int M, int K, int mode, float *of, uint16_t *ob, int ldo) {
+    int N = 0;
+    int seg_end[3] = {0, 0, 0};
+    for (int i = 0; i < nseg; i++) {
+        N += seg_n[i];
+        seg_end[i] = N;
+    }
+    float *part = x.at<float>(x.p->o_part);
+    int splits = 1;
+    if (x.c->weight_fmt == DFLASH_W_Q4K) {
+        Q4kGemmArgs a;
+        for (int i = 0; i < 3; i++) {
+            a.w[i] = (const unsigned char *)(i < nseg ? w[i] : w[0]);
+            a.seg_end[i] = seg_end[i];
+        }
+        a.nseg = nseg;
+        a.A = A;
+        a.lda = lda;
+        a.M = M;
+        a.N = N;
+        a.KB = K / 256;
+        const Q4kPlan p = q4k_plan(M, N, K);
+        a.kb_per = p.kb_per;
+        a.part = part;
+        HIPCHK(launch_q4k_gemm(a, p, x.st));
+        splits = p.splits;
+    } else {
+        Bf16GemmArgs a;
+        for (int i = 0; i < 3; i++) {
+            a.w[i] = (const uint16_t *)(i < nseg ? w[i] : w[0]);
+            a.seg_end[i] = seg_end[i];
+        }
+        a.nseg = nseg;
+        a.A = A;
+        a.lda = lda;
+        a.M = M;
+        a.N = N;
+        a.K = K;
+        a.C = part;
+        a.ldc = N;
+        HIPCHK(launch_bf16_gemm_tiled(a, x.st));
+    }
+    HIPCHK(launch_reduce_epilogue(part, splits, M, N, mode, of, ob, ldo, x.st));
+    return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dflash_status_str(int s) {
+    switch (s) {
+        case DFLASH_OK: return "ok";
+        case DFLASH_EINVAL: return "invalid argument (null pointer or value out of range)";
+        case DFLASH_ESHAPE: return "shape not supported";
+        case DFLASH_EALIGN: return "pointer not 16-byte aligned";
+        case DFLASH_EWORKSPACE: return "workspace missing or too small";
+        case DFLASH_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t dflash_workspace_bytes(const dflash_config *cfg, int batch, int t_new) {
+    if (check_config(cfg) != DFLASH_OK || batch < 1 || t_new < 1 || t_new > DFLASH_BLOCK) return 0;
+    Plan p;
+    make_plan(cfg, batch, t_new, p);
+    return p.total;
+}
+
+int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int batch,
+                      const uint16_t *taps, int t_new, const int32_t *last_token,
+                      const int32_t *ctx_len, uint16_t *k_cache, uint16_t *v_cache,
+                      int cache_cap, int32_t *draft_tokens, int32_t *cand_ids,
+                      float *cand_logp, float *dbg_hidden, float *dbg_logits,
+                      void *workspace, size_t ws_bytes, const dflash_probe *probe,
+                      void *stream) {
+    int rc = check_config(cfg);
+    if (rc != DFLASH_OK) return rc;
+    if (!w || !taps || !last_token || !ctx_len || !k_cache || !v_cache || !draft_tokens ||
+        !cand_ids || !cand_logp)
+        return DFLASH_EINVAL;
+    if (batch < 1 || batch > 4096 || t_new < 1 || t_new > DFLASH_BLOCK || cache_cap < t_new)
+        return DFLASH_EINVAL;
+    if (!w->fc || !w->hidden_norm || !w->final_norm || !w->embed || !w->lm_head ||
+        !w->mask_emb || !w->code_a || !w->code_b)
+        return DFLASH_EINVAL;
+    const void *ptrs[] = {w->fc, w->hidden_norm, w->final_norm, w->embed, w->lm_head,
+                          w->mask_emb, w->code_a, w->code_b, taps, k_cache, v_cache,
+                          workspace, dbg_hidden, dbg_logits};
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return DFLASH_EALIGN;
+    for (int l = 0; l < cfg->n_layers; l++) {
+        const dflash_layer_weights &lw = w->layer[l];
+        const void *lp[] = {lw.wq, lw.wk, lw.wv, lw.wo, lw.wg, lw.wu, lw.wd, lw.in_norm,
+                            lw.post_norm, lw.q_norm, lw.k_norm, lw.w_conv};
+        for (const void *q : lp) {
+            if (!q) return DFLASH_EINVAL;
+            if (!aligned16(q)) return DFLASH_EALIGN;
+        }
+    }
+    Plan p;
+    make_plan(cfg, batch, t_new, p);
+    if (!workspace || ws_bytes < p.total || ((uintptr_t)workspace & 255)) return DFLASH_EWORKSPACE;
+
+    Ctx x{cfg, &p, (unsigned char *)workspace, (hipStream_t)stream};
+    const int H = p.H, L = p.L;
+    float *h = x.at<float>(p.o_h);
+    uint16_t *xc = x.at<uint16_t>(p.o_xc);
+    int32_t *valid = x.at<int32_t>(p.o_valid);
+    const size_t cache_layer = (size_t)batch * p.n_kv * cache_cap * p.d;
+
+    // S0: block assembly (and per-sequence validity)
+    HIPCHK(launch_embed(w->embed, w->mask_emb, last_token, ctx_len, batch, p.T, H, p.V, t_new,
+                        cache_cap, h, valid, x.st));
+    if (dbg_hidden)
+        HIPCHK(hipMemcpyAsync(dbg_hidden, h, (size_t)p.M_blk * H * 4, hipMemcpyDeviceToDevice, x.st));
+
+    // S1: fused taps c = RMSNorm(X . W_fc^T) -> rows [M_blk, M_qkv) of xc
+    {
+        const void *ws[1] = {w->fc};
+        const int sn[1] = {H};
+        rc = run_gemm(x, ws, sn, 1, taps, cfg->n_taps * H, p.M_ctx, cfg->n_taps * H,
+                      EPI_STORE_F32, x.at<float>(p.o_fcout), nullptr, H);
+        if (rc) return rc;
+        HIPCHK(launch_rmsnorm(x.at<float>(p.o_fcout), p.M_ctx, H, 1, 1, 0, w->hidden_norm,
+                              cfg->rms_eps, xc + (size_t)p.M_blk * H, H, x.st));
+    }
+
+    for (int l = 0; l < L; l++) {
+        const dflash_layer_weights &lw = w->layer[l];
+        uint16_t *kc = k_cache + (size_t)l * cache_layer;
+        uint16_t *vc = v_cache + (size_t)l * cache_layer;
+        // S2: x = RMSNorm(h) -> rows [0, M_blk) of xc
+        HIPCHK(launch_rmsnorm(h, p.M_blk, H, 1, 1, 0, lw.in_norm, cfg->rms_eps, xc, H, x.st));
+        // S3: [Q | K | V] of block rows and K, V of context rows
+        {
+            const void *ws[3] = {lw.wq, lw.wk, lw.wv};
+            const int sn[3] = {p.qd, p.kd, p.kd};
+            rc = run_gemm(x, ws, sn, 3, xc, H, p.M_qkv, H, EPI_STORE_F32, x.at<float>(p.o_qkv),
+                          nullptr, p.qd + 2 * p.kd);
+            if (rc) return rc;
+        }
+        // S4: per-head norms, rotary embedding, cache append
+        {
+            RopeArgs a;
+            a.qkv = x.at<float>(p.o_qkv);
+            a.B = batch; a.T = p.T; a.t_new = t_new; a.n_q = p.n_q; a.n_kv = p.n_kv; a.d = p.d;
+            a.q_norm = lw.q_norm; a.k_norm = lw.k_norm; a.eps = cfg->rms_eps;
+            a.theta = cfg->rope_theta; a.ctx_len = ctx_len; a.valid = valid;
+            a.Q = x.at<uint16_t>(p.o_Q); a.Kb = x.at<uint16_t>(p.o_Kb); a.Vb = x.at<uint16_t>(p.o_Vb);
+            a.k_cache = kc; a.v_cache = vc; a.cap = cache_cap;
+            HIPCHK(launch_qk_norm_rope(a, x.st));
+        }
+        // S5: split-window attention partials
+        {
+            AttnArgs a;
+            a.Q = x.at<uint16_t>(p.o_Q); a.Kb = x.at<uint16_t>(p.o_Kb); a.Vb = x.at<uint16_t>(p.o_Vb);
+            a.k_cache = kc; a.v_cache = vc; a.ctx_len = ctx_len; a.valid = valid;
+            a.B = batch; a.T = p.T; a.t_new = t_new; a.n_q = p.n_q; a.n_kv = p.n_kv; a.d = p.d;
+            a.window = cfg->window; a.cap = cache_cap; a.chunk = p.attn_chunk;
+            a.n_chunks = p.attn_nch; a.O = x.at<float>(p.o_attnO); a.ml = x.at<float>(p.o_attnML);
+            HIPCHK(launch_attention(a, x.st));
+        }
+        // S6: merge + two-tap dynamic convolution -> Y
+        {
+            MergeConvArgs a;
+            a.O = x.at<float>(p.o_attnO); a.ml = x.at<float>(p.o_attnML);
+            a.ctx_len = ctx_len; a.valid = valid;
+            a.B = batch; a.T = p.T; a.t_new = t_new; a.n_q = p.n_q; a.n_kv = p.n_kv; a.d = p.d;
+            a.window = cfg->window; a.chunk = p.attn_chunk; a.n_chunks = p.attn_nch;
+            a.w_conv = lw.w_conv; a.Y = x.at<uint16_t>(p.o_Y);
+            HIPCHK(launch_merge_conv(a, x.st));
+        }
+        // S7: h += Y . W_o^T
+        {
+            const void *ws[1] = {lw.wo};
+            const int sn[1] = {H};
+            rc = run_gemm(x, ws, sn, 1, x.at<uint16_t>(p.o_Y), p.qd, p.M_blk, p.qd, EPI_ADD_F32,
+                          h, nullptr, H);
+            if (rc) return rc;
+        }
+        // S8: u = RMSNorm(h); h += (silu(u Wg^T) * u Wu^T) Wd^T
+        HIPCHK(launch_rmsnorm(h, p.M_blk, H, 1, 1, 0, lw.post_norm, cfg->rms_eps, xc, H, x.st));
+        {
+            const void *ws[2] = {lw.wg, lw.wu};
+            const int sn[2] = {p.F, p.F};
+            const bool probe_ffn = probe && probe->kernel == DFLASH_PROBE_FFN_GATE_UP && probe->layer == l;
+            if (probe_ffn) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_start, x.st));
+            rc = run_gemm(x, ws, sn, 2, xc, H, p.M_blk, H, EPI_SWIGLU_BF16, nullptr,
+                          x.at<uint16_t>(p.o_mid), p.F);
+            if (rc) return rc;
+            if (probe_ffn) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_stop, x.st));
+        }
+        {
+            const void *ws[1] = {lw.wd};
+            const int sn[1] = {H};
+            rc = run_gemm(x, ws, sn, 1, x.at<uint16_t>(p.o_mid), p.F, p.M_blk, p.F, EPI_ADD_F32,
+                          h, nullptr, H);
+            if (rc) return rc;
+        }
+        if (dbg_hidden)
+            HIPCHK(hipMemcpyAsync(dbg_hidden + (size_t)(l + 1) * p.M_blk * H, h,
+                                  (size_t)p.M_blk * H * 4, hipMemcpyDeviceToDevice, x.st));
+    }
+
+    // S9: final norm of proposal rows 1..7
+    uint16_t *f = x.at<uint16_t>(p.o_f);
+    HIPCHK(launch_rmsnorm(h, p.R, H, p.P, p.T, 1, w->final_norm, cfg->rms_eps, f, H, x.st));
+
+    // S10: logits with the shared output head, then log-softmax statistics and top-K
+    float *logits = dbg_logits ? dbg_logits : x.at<float>(p.o_logits);
+    {
+        Bf16GemmArgs a;
+        a.w[0] = a.w[1] = a.w[2] = w->lm_head;
+        a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = p.V;
+        a.nseg = 1;
+        a.A = f; a.lda = H; a.M = p.R; a.N = p.V; a.K = H; a.C = logits; a.ldc = p.V;
+        const bool probe_lm = probe && probe->kernel == DFLASH_PROBE_LM_HEAD;
+        if (probe_lm) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_start, x.st));
+        if (p.lm_skinny) HIPCHK(launch_bf16_gemm_skinny(a, x.st));
+        else HIPCHK(launch_bf16_gemm_tiled(a, x.st));
+        if (probe_lm) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_stop, x.st));
+    }
+    HIPCHK(launch_topk_partial(logits, p.R, p.V, 0, p.K, x.at<float>(p.o_pv),
+                               x.at<int32_t>(p.o_pi), x.at<float>(p.o_pm), x.at<float>(p.o_ps), x.st));
+    HIPCHK(launch_topk_merge(x.at<float>(p.o_pv), x.at<int32_t>(p.o_pi), x.at<float>(p.o_pm),
+                             x.at<float>(p.o_ps), p.R, p.topk_nch, p.K, p.P, valid, cand_ids,
+                             cand_logp, x.st));
+    // S11: selector path
+    HIPCHK(launch_viterbi(cand_ids, cand_logp, w->code_a, w->code_b, batch, p.P, p.K, p.r,
+                          cfg->pair_scale, valid, draft_tokens, x.st));
+    return DFLASH_OK;
+}
+
+int dflash_verify_prefix(const int32_t *draft, const int32_t *target, int batch, int n,
+                         int32_t *accept_len, int32_t *out_tokens, void *stream) {
+    if (!draft || !target || !accept_len || !out_tokens) return DFLASH_EINVAL;
+    if (batch < 1 || n < 1 || n > 64) return DFLASH_EINVAL;
+    HIPCHK(launch_verify(draft, target, batch, n, accept_len, out_tokens, (hipStream_t)stream));
+    return DFLASH_OK;
+}
+
+size_t q4k_gemm_workspace_bytes(int M, int N, int K) {
+    if (M < 1 || M > 4096 || N < 16 || N % 16 || K < 256 || K % 256) return 0;
+    return align256(gemm_part_bytes(DFLASH_W_Q4K, M, N, K));
+}
+
+int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
+             void *workspace, size_t ws_bytes, void *stream) {
+    if (!w || !x || !y) return DFLASH_EINVAL;
+    if (M < 1 || M > 4096 || N < 16 || N % 16 || K < 256 || K % 256) return DFLASH_ESHAPE;
+    if (!aligned16(w) || !aligned16(x) || !aligned16(y)) return DFLASH_EALIGN;
+    const size_t need = q4k_gemm_workspace_bytes(M, N, K);
+    if (!workspace || ws_bytes < need || !aligned16(workspace)) return DFLASH_EWORKSPACE;
+    const Q4kPlan p = q4k_plan(M, N, K);
+    Q4kGemmArgs a;
+    a.w[0] = a.w[1] = a.w[2] = (const unsigned char *)w;
+    a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = N;
+    a.nseg = 1;
+    a.A = x; a.lda = K; a.M = M; a.N = N; a.KB = K / 256; a.kb_per = p.kb_per;
+    a.part = (float *)workspace;
+    HIPCHK(launch_q4k_gemm(a, p, (hipStream_t)stream));
+    HIPCHK(launch_reduce_epilogue((float *)workspace, p.splits, M, N, EPI_STORE_BF16, nullptr, y,
+                                  N, (hipStream_t)stream));
+    return DFLASH_OK;
+}
+
+int q4k_dequantize(const void *w, float *out, long long n_blocks, void *stream) {
+    if (!w || !out || n_blocks < 1) return DFLASH_EINVAL;
+    if (!aligned16(w) || !aligned16(out)) return DFLASH_EALIGN;
+    HIPCHK(launch_q4k_dequant(w, out, n_blocks, (hipStream_t)stream));
+    return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Launch interface of the draft-step kernels (host side of each .hip file).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// ---------------------------------------------------------------- Q4_K GEMM
+struct Q4kGemmArgs {
+    const unsigned char *w[3];   // up to 3 weight matrices stacked along N
+    int seg_end[3];              // cumulative column count after each segment
+    int nseg;
+    const uint16_t *A;           // bf16 activations [M][lda]
+    int lda;
+    int M, N, KB;                // KB = K / 256
+    int kb_per;                  // super-blocks per split
+    float *part;                 // fp32 partials [splits][M][N]
+};
+struct Q4kPlan {
+    int KB, kb_per, splits, row_groups, grid_x;
+    size_t lds_bytes;
+};
+Q4kPlan q4k_plan(int M, int N, int K);
+hipError_t launch_q4k_gemm(const Q4kGemmArgs &a, const Q4kPlan &p, hipStream_t st);
+hipError_t launch_q4k_dequant(const void *w, float *out, long long n_blocks, hipStream_t st);
+
+// ---------------------------------------------------------------- bf16 GEMMs
+struct Bf16GemmArgs {
+    const uint16_t *w[3];        // bf16 weights [N_seg][K], stacked along N
+    int seg_end[3];
+    int nseg;
+    const uint16_t *A;           // bf16 [M][lda]
+    int lda;
+    int M, N, K;
+    float *C;                    // fp32 [M][ldc]
+    int ldc;
+};
+// tiled 128x128 MFMA GEMM, any M
+hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st);
+// rows <= 16, K <= 5120: split-K over the 4 waves of a workgroup, activations in VGPRs
+hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------- layer ops
+enum EpiMode { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_SWIGLU_BF16 = 2, EPI_STORE_BF16 = 3 };
+hipError_t launch_reduce_epilogue(const float *part, int splits, int M, int N, int mode,
+                                  float *out_f32, uint16_t *out_bf16, int ldo, hipStream_t st);
+
+// per-sequence validity flags + block assembly h[b][0] = E[last], h[b][1..] = mask
+hipError_t launch_embed(const uint16_t *embed, const uint16_t *mask_emb, const int32_t *last,
+                        const int32_t *ctx_len, int B, int T, int H, int V, int t_new, int cap,
+                        float *h, int32_t *valid, hipStream_t st);
+
+// out[r] = bf16(RMSNorm(in[row(r)]) * g), row(r) = (r / per) * in_group + in_off + r % per
+hipError_t launch_rmsnorm(const float *in, int R, int H, int per, int in_group, int in_off,
+                          const uint16_t *gain, float eps, uint16_t *out, int ldo,
+                          hipStream_t st);
+
+struct RopeArgs {
+    const float *qkv;            // fp32 [B*(T + t_new)][qd + 2 kd]: block rows then context rows
+    int B, T, t_new, n_q, n_kv, d;
+    const uint16_t *q_norm, *k_norm;
+    float eps, theta;
+    const int32_t *ctx_len, *valid;
+    uint16_t *Q, *Kb, *Vb;       // bf16 [B][T][heads][d]
+    uint16_t *k_cache, *v_cache; // layer base, [B][n_kv][cap][d]
+    int cap;
+};
+hipError_t launch_qk_norm_rope(const RopeArgs &a, hipStream_t st);
+
+struct AttnArgs {
+    const uint16_t *Q, *Kb, *Vb;
+    const uint16_t *k_cache, *v_cache;   // layer base, [B][n_kv][cap][d]
+    const int32_t *ctx_len, *valid;
+    int B, T, t_new, n_q, n_kv, d, window, cap;
+    int chunk;                   // keys per workgroup (multiple of 64)
+    int n_chunks;                // cache chunks per sequence (max); grid.x = n_chunks + 1
+    float *O;                    // fp32 [B][n_kv][n_chunks+1][QR][d] unnormalised
+    float *ml;                   // fp32 [B][n_kv][n_chunks+1][QR][2] (max, sum)
+};
+hipError_t launch_attention(const AttnArgs &a, hipStream_t st);
+
+struct MergeConvArgs {
+    const float *O, *ml;
+    const int32_t *ctx_len, *valid;
+    int B, T, t_new, n_q, n_kv, d, window, chunk, n_chunks;
+    const uint16_t *w_conv;      // bf16 [2 n_q][n_q d]
+    uint16_t *Y;                 // bf16 [B*T][n_q d]
+};
+hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------- LM head / top-K
+hipError_t launch_topk_partial(const float *logits, int R, int V, int chunk, int K,
+                               float *pv, int32_t *pi, float *pm, float *ps, hipStream_t st);
+hipError_t launch_topk_merge(const float *pv, const int32_t *pi, const float *pm, const float *ps,
+                             int R, int n_chunks, int K, int rows_per_seq, const int32_t *valid,
+                             int32_t *cand_ids, float *cand_logp, hipStream_t st);
+
+// ---------------------------------------------------------------- selector / verify
+hipError_t launch_viterbi(const int32_t *cand_ids, const float *cand_logp, const uint16_t *code_a,
+                          const uint16_t *code_b, int B, int P, int K, int r, float pair_scale,
+                          const int32_t *valid, int32_t *draft_tokens, hipStream_t st);
+hipError_t launch_verify(const int32_t *draft, const int32_t *target, int B, int n,
+                         int32_t *accept_len, int32_t *out_tokens, hipStream_t st);

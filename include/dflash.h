@@ -1,0 +1,176 @@
+/*
+ * dflash.h - C ABI of the MI355X (gfx950) DFlash 2 block-draft library.
+ *
+ * The library runs one step of DFlash 2 speculative drafting on one GPU:
+ *
+ *   dflash_draft_step    the drafter reads five tapped target features, proposes
+ *                        a block of 8 tokens in one forward (position 0 = the last
+ *                        accepted token, positions 1..7 = mask positions), keeps
+ *                        the top-K candidates of the shared output head at each of
+ *                        the 7 proposal positions and picks one path through them.
+ *                        FastFlowLM card "Qwen3.8-27B-DFlash2-NPU2": spec table
+ *                        rows "Draft", "Weights", "Taps"; section "How it is used".
+ *   dflash_verify_prefix greedy acceptance: keep the longest drafted prefix the
+ *                        target agrees with, plus one target token.  Same card,
+ *                        sections "How it is used" and "FastFlowLM measurements".
+ *   q4k_gemm             y = x . W^T with W in Q4_K super-blocks (the format of
+ *                        the draft's fc, q/k/v/o and MLP matrices: same card,
+ *                        "Weights" row), fp32 accumulation, bf16 output.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE memory owned by the caller.  The library
+ *     allocates nothing, keeps no state between calls and writes only the
+ *     buffers documented as outputs, the caller's workspace and the KV-cache rows
+ *     named below.
+ *   - bf16 tensors are passed as uint16_t bit patterns; all arrays are dense and
+ *     row-major in the order their shapes are written.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *     work and return; results are valid once the stream has reached them.
+ *   - Arguments are validated on the host before anything is enqueued: a
+ *     negative dflash_status is returned and nothing is launched.  A HIP launch
+ *     error after validation returns DFLASH_EHIP.  Nothing is thrown across the
+ *     ABI.  Calls on distinct workspaces may run concurrently.
+ *   - Values held in device memory (token ids, context lengths) cannot be seen
+ *     by the host check; the kernels guard every access against them (see each
+ *     entry point).
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_MAX_LAYERS 8
+#define DFLASH_BLOCK 8          /* block of 8 = 1 anchor + 7 proposals */
+#define DFLASH_MAX_TOPK 16
+
+typedef enum {
+    DFLASH_OK = 0,
+    DFLASH_EINVAL = -1,       /* null pointer or value out of range */
+    DFLASH_ESHAPE = -2,       /* shape not supported by the kernels */
+    DFLASH_EALIGN = -3,       /* pointer misaligned (16-byte alignment required) */
+    DFLASH_EWORKSPACE = -4,   /* workspace missing or too small */
+    DFLASH_EHIP = -5          /* a HIP call failed */
+} dflash_status;
+
+typedef enum { DFLASH_W_Q4K = 0, DFLASH_W_BF16 = 1 } dflash_weight_fmt;
+
+/* Drafter shape.  The 27B draft: 5 layers, hidden 5120, FFN 17408, 32 query and
+ * 8 KV heads of 128, window 2048, vocab 248320, 5 taps, block 8, top 16, rank
+ * 256 (FastFlowLM card spec table "Draft" row; aiqre page "Specification").
+ * Supported by the kernels: hidden, ffn and n_q*head_dim multiples of 256;
+ * head_dim 64 or 128; n_q a multiple of n_kv; block == 8; 1 <= top_k <= 16;
+ * sel_rank a multiple of 8 up to 512; vocab >= top_k. */
+typedef struct {
+    int n_layers, hidden, ffn, n_q_heads, n_kv_heads, head_dim, window, vocab;
+    int n_taps, block, top_k, sel_rank, weight_fmt;
+    float rms_eps;     /* RMSNorm epsilon (1e-6) */
+    float rope_theta;  /* rotary base */
+    float pair_scale;  /* selector pair-score scale, 1/sqrt(sel_rank) */
+} dflash_config;
+
+/* Linear weights are [out][in] row-major (y = x . W^T).  In Q4_K each row is
+ * in/256 consecutive 144-byte super-blocks; in bf16 it is `in` values. */
+typedef struct {
+    const void *wq, *wk, *wv, *wo, *wg, *wu, *wd;
+    const uint16_t *in_norm, *post_norm;   /* [hidden] */
+    const uint16_t *q_norm, *k_norm;       /* [head_dim], per-head RMSNorm gains */
+    const uint16_t *w_conv;                /* [2 n_q][n_q head_dim] dynamic-conv taps */
+} dflash_layer_weights;
+
+typedef struct {
+    const void *fc;                        /* [hidden][n_taps hidden] */
+    const uint16_t *hidden_norm;           /* [hidden] norm of the fused taps */
+    dflash_layer_weights layer[DFLASH_MAX_LAYERS];
+    const uint16_t *final_norm;            /* [hidden] */
+    const uint16_t *embed;                 /* [vocab][hidden] target embedding table */
+    const uint16_t *lm_head;               /* [vocab][hidden] target output head (may alias embed) */
+    const uint16_t *mask_emb;              /* [hidden] embedding of the mask positions */
+    const uint16_t *sel_proj;              /* [sel_rank][hidden] selector projection (not read) */
+    const uint16_t *code_a, *code_b;       /* [vocab][sel_rank] selector codebooks */
+} dflash_weights;
+
+/* Optional live timing of one kernel inside dflash_draft_step: HIP events
+ * recorded on `stream` immediately before and after that kernel's launch. */
+typedef enum { DFLASH_PROBE_NONE = 0, DFLASH_PROBE_LM_HEAD = 1, DFLASH_PROBE_FFN_GATE_UP = 2 } dflash_probe_kernel;
+typedef struct {
+    int kernel;            /* dflash_probe_kernel */
+    int layer;             /* layer index for per-layer kernels */
+    void *ev_start, *ev_stop;   /* hipEvent_t */
+} dflash_probe;
+
+/* Bytes of workspace dflash_draft_step needs for (cfg, batch, t_new); 0 on bad
+ * arguments. */
+size_t dflash_workspace_bytes(const dflash_config *cfg, int batch, int t_new);
+
+/*
+ * One draft step for `batch` independent sequences.
+ *
+ *  taps         bf16 [batch][t_new][n_taps*hidden]: the target's residual stream
+ *               at its tapped layers for the t_new newest context positions,
+ *               concatenated in the listed layer order (FastFlowLM card "Taps").
+ *  t_new        1..8 context rows appended this step.
+ *  last_token   int32 [batch] device: last accepted token (block position 0).
+ *  ctx_len      int32 [batch] device: rows already cached before the step (n).
+ *  k_cache,     bf16 [n_layers][batch][n_kv][cache_cap][head_dim] device.
+ *  v_cache      Rows [n, n+t_new) are written (keys after per-head norm and
+ *               rotary embedding at positions n..n+t_new-1; values as projected);
+ *               rows [max(0, n+t_new-window), n) are read.  Block position t
+ *               sits at rotary position n+t_new+t.
+ *  draft_tokens int32 [batch][7]: the chosen path.
+ *  cand_ids     int32 [batch][7][top_k], cand_logp fp32 [batch][7][top_k]:
+ *               candidates ordered by (logit desc, id asc) and their log-softmax.
+ *  dbg_hidden   nullable fp32 [n_layers+1][batch][8][hidden]: the residual stream
+ *               after block assembly and after each layer.
+ *  dbg_logits   nullable fp32 [batch][7][vocab].
+ *  workspace    device, >= dflash_workspace_bytes(cfg, batch, t_new), 256-byte aligned.
+ *  probe        nullable; see dflash_probe.
+ *
+ * A sequence whose ctx_len is negative or whose n+t_new exceeds cache_cap, or
+ * whose last_token is outside [0, vocab), is not computed: its draft tokens are
+ * set to -1, its candidates to -1 / -inf, and no cache row is written.
+ */
+int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int batch,
+                      const uint16_t *taps, int t_new, const int32_t *last_token,
+                      const int32_t *ctx_len, uint16_t *k_cache, uint16_t *v_cache,
+                      int cache_cap, int32_t *draft_tokens, int32_t *cand_ids,
+                      float *cand_logp, float *dbg_hidden, float *dbg_logits,
+                      void *workspace, size_t ws_bytes, const dflash_probe *probe,
+                      void *stream);
+
+/*
+ * Greedy prefix acceptance for `batch` rows.
+ *  draft      int32 [batch][n] drafted tokens (n = 7 for a block of 8).
+ *  target     int32 [batch][n+1]: target[j] is the target's greedy token after
+ *             block position j.
+ *  accept_len int32 [batch]: k = number of leading j with draft[j] == target[j].
+ *  out_tokens int32 [batch][n+1]: draft[0..k-1], target[k], then -1.
+ * 1 <= n <= 64.
+ */
+int dflash_verify_prefix(const int32_t *draft, const int32_t *target, int batch, int n,
+                         int32_t *accept_len, int32_t *out_tokens, void *stream);
+
+/* Workspace bytes q4k_gemm needs for an M x N x K product. */
+size_t q4k_gemm_workspace_bytes(int M, int N, int K);
+
+/*
+ * y[M][N] (bf16) = x[M][K] (bf16) . W^T, W [N][K] in Q4_K, fp32 accumulation.
+ * K % 256 == 0, N % 16 == 0, 1 <= M <= 4096.  w, x, y and workspace 16-byte aligned.
+ */
+int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
+             void *workspace, size_t ws_bytes, void *stream);
+
+/* Decode n_blocks consecutive Q4_K super-blocks to fp32 (256 values each). */
+int q4k_dequantize(const void *w, float *out, long long n_blocks, void *stream);
+
+/* Text of a dflash_status code. */
+const char *dflash_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

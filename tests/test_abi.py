@@ -1,0 +1,117 @@
+"""The C-ABI library: it loads, exports every declared entry point, and rejects bad
+arguments on the host before touching a device (CPU only: no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diffusion_draft_amd import binding, synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "dflash.h")
+FAKE = 0x10000          # a non-null, 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("dflash_draft_step", "dflash_verify_prefix", "q4k_gemm", "q4k_dequantize",
+              "dflash_workspace_bytes", "q4k_gemm_workspace_bytes", "dflash_status_str"):
+        assert n in names
+    assert sorted(binding.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = binding.lib()
+    for rc in (0, -1, -2, -3, -4, -5):
+        assert L.dflash_status_str(rc)
+    assert b"unknown" in L.dflash_status_str(42)
+
+
+def tiny_cfg(**kw):
+    s = synth.TINY
+    c = binding.make_config(s)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_workspace_query():
+    L = binding.lib()
+    assert L.dflash_workspace_bytes(ctypes.byref(tiny_cfg()), 1, 8) > 0
+    assert L.dflash_workspace_bytes(ctypes.byref(tiny_cfg(head_dim=96)), 1, 8) == 0
+    assert L.dflash_workspace_bytes(ctypes.byref(tiny_cfg()), 1, 9) == 0
+    assert L.dflash_workspace_bytes(ctypes.byref(tiny_cfg()), 0, 8) == 0
+    assert L.dflash_workspace_bytes(None, 1, 8) == 0
+    full = binding.make_config(synth.FULL)
+    assert L.dflash_workspace_bytes(ctypes.byref(full), 16, 8) > \
+        L.dflash_workspace_bytes(ctypes.byref(full), 1, 8)
+
+
+def fake_weights(cfg):
+    w = binding.Weights()
+    for f in ("fc", "hidden_norm", "final_norm", "embed", "lm_head", "mask_emb", "sel_proj",
+              "code_a", "code_b"):
+        setattr(w, f, FAKE)
+    for l in range(cfg.n_layers):
+        for f, _ in binding.LayerWeights._fields_:
+            setattr(w.layer[l], f, FAKE)
+    return w
+
+
+def call_step(cfg, w, batch=1, t_new=8, taps=FAKE, ws=FAKE, ws_bytes=1 << 40, cap=64):
+    L = binding.lib()
+    return L.dflash_draft_step(ctypes.byref(cfg), ctypes.byref(w) if w is not None else None,
+                               batch, taps, t_new, FAKE, FAKE, FAKE, FAKE, cap, FAKE, FAKE, FAKE,
+                               None, None, ws, ws_bytes, None, None)
+
+
+def test_draft_step_rejects_bad_arguments_before_launch():
+    cfg = tiny_cfg()
+    w = fake_weights(cfg)
+    assert call_step(cfg, None) == -1                       # EINVAL: no weights
+    assert call_step(cfg, w, taps=None) == -1
+    assert call_step(cfg, w, batch=0) == -1
+    assert call_step(cfg, w, t_new=0) == -1
+    assert call_step(cfg, w, t_new=9) == -1
+    assert call_step(cfg, w, cap=4) == -1                   # cache smaller than t_new
+    assert call_step(tiny_cfg(head_dim=96), w) == -2        # ESHAPE
+    assert call_step(tiny_cfg(top_k=17), w) == -2
+    assert call_step(tiny_cfg(block=5), w) == -2
+    assert call_step(tiny_cfg(n_kv_heads=3), w) == -2
+    assert call_step(tiny_cfg(hidden=200), w) == -2
+    assert call_step(tiny_cfg(sel_rank=12), w) == -2
+    assert call_step(tiny_cfg(weight_fmt=7), w) == -1
+    assert call_step(cfg, w, taps=FAKE + 2) == -3           # EALIGN
+    assert call_step(cfg, w, ws=None) == -4                 # EWORKSPACE
+    assert call_step(cfg, w, ws_bytes=16) == -4
+    assert call_step(cfg, w, ws=FAKE + 16) == -4            # workspace must be 256-aligned
+    w.layer[0].wq = None
+    assert call_step(cfg, w) == -1
+
+
+def test_q4k_gemm_and_verify_reject_bad_arguments():
+    L = binding.lib()
+    assert L.q4k_gemm(FAKE, FAKE, FAKE, 8, 5120, 5000, FAKE, 1 << 40, None) == -2
+    assert L.q4k_gemm(FAKE, FAKE, FAKE, 8, 5121, 5120, FAKE, 1 << 40, None) == -2
+    assert L.q4k_gemm(FAKE, FAKE, FAKE, 0, 5120, 5120, FAKE, 1 << 40, None) == -2
+    assert L.q4k_gemm(FAKE + 4, FAKE, FAKE, 8, 5120, 5120, FAKE, 1 << 40, None) == -3
+    assert L.q4k_gemm(FAKE, FAKE, FAKE, 8, 5120, 5120, FAKE, 16, None) == -4
+    assert L.q4k_gemm(None, FAKE, FAKE, 8, 5120, 5120, FAKE, 1 << 40, None) == -1
+    assert L.q4k_gemm_workspace_bytes(8, 5120, 25600) > 0
+    assert L.q4k_gemm_workspace_bytes(8, 5120, 100) == 0
+    assert L.dflash_verify_prefix(FAKE, FAKE, 1, 0, FAKE, FAKE, None) == -1
+    assert L.dflash_verify_prefix(None, FAKE, 1, 7, FAKE, FAKE, None) == -1
+    assert L.q4k_dequantize(FAKE, FAKE, 0, None) == -1

@@ -1,0 +1,108 @@
+"""GPU parity of the Q4_K kernels and of prefix acceptance against the oracle.
+
+Q4_K decode is bit-exact (every block of every drafter matrix shape at full
+size); the GEMM matches the oracle's float64 product to the bf16 rounding of
+its output.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_draft_amd import binding, synth
+from oracle import q4k as oq4k
+from oracle.bf16 import bf16_to_f64
+from oracle.verify import verify_prefix
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+@pytest.mark.parametrize("name,N,K", synth.GEMM_SHAPES)
+def test_q4k_dequantize_bit_exact_full_matrix(name, N, K):
+    say(f"[q4k_dequantize] {name} {N}x{K}")
+    w, _ = synth.gemm_inputs(name, N, K)
+    wd = dev_u8(w)
+    rows_per = max(1, (1 << 24) // K)
+    for r0 in range(0, N, rows_per):
+        r1 = min(N, r0 + rows_per)
+        nb = (r1 - r0) * (K // 256)
+        out = torch.empty(nb * 256, dtype=torch.float32, device="cuda")
+        seg = wd[r0 * (K // 256) * 144: r1 * (K // 256) * 144]
+        binding.q4k_dequantize(seg, out)
+        got = out.cpu().numpy()
+        ref = oq4k.decode_matrix(w[r0 * (K // 256) * 144: r1 * (K // 256) * 144], r1 - r0, K)
+        assert np.array_equal(got.view(np.uint32),
+                              ref.astype(np.float32).reshape(-1).view(np.uint32)), (name, r0)
+
+
+def gemm_check(w, x, N, K, M):
+    wd = dev_u8(w)
+    xd = dev_bf16(x)
+    y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    ws = torch.empty(binding.q4k_gemm_workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+    binding.q4k_gemm(wd, xd, y, ws)
+    got = bf16_to_f64(y.cpu().numpy().view(np.uint16))
+    ref = bf16_to_f64(x) @ oq4k.decode_matrix(w, N, K).T
+    # output rounded to bf16 (<= 2^-9 relative) plus fp32 accumulation
+    err = np.abs(got - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-5 * np.sqrt(np.mean(ref ** 2))
+    assert np.all(err <= bound), float((err / np.maximum(bound, 1e-30)).max())
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+@pytest.mark.parametrize("name,N,K", synth.GEMM_SHAPES)
+def test_q4k_gemm_drafter_shapes_m8(name, N, K):
+    say(f"[q4k_gemm] {name} M=8 {N}x{K}")
+    w, x = synth.gemm_inputs(name, N, K, M=8)
+    rel = gemm_check(w, x, N, K, 8)
+    assert rel < 3e-3
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 40, 64, 65, 128])
+def test_q4k_gemm_row_counts(M):
+    """Ragged row counts across MFMA row tiles and row groups."""
+    N, K = 272, 1280
+    say(f"[q4k_gemm] M={M} {N}x{K}")
+    w = synth.q4k_normal(5, "rows", N, K, 0.02)
+    x = synth.normal_bf16(5, "rows.x", (M, K), 1.0)
+    gemm_check(w, x, N, K, M)
+
+
+def test_q4k_gemm_one_block_edge():
+    """Smallest shape: one super-block, one column tile."""
+    N, K, M = 16, 256, 2
+    w = synth.q4k_normal(6, "edge", N, K, 0.02)
+    x = synth.normal_bf16(6, "edge.x", (M, K), 1.0)
+    gemm_check(w, x, N, K, M)
+
+
+def test_verify_prefix_all_lengths_and_random():
+    rng = np.random.default_rng(0)
+    B, n = 64, 7
+    draft = rng.integers(0, 248320, size=(B, n)).astype(np.int32)
+    tgt = rng.integers(0, 248320, size=(B, n + 1)).astype(np.int32)
+    for b in range(B):
+        k = b % (n + 1)
+        tgt[b, :k] = draft[b, :k]
+        if k < n:
+            tgt[b, k] = (draft[b, k] + 1) % 248320
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, n + 1), dtype=torch.int32, device="cuda")
+    binding.verify_prefix(torch.from_numpy(draft).cuda(), torch.from_numpy(tgt).cuda(), acc, out)
+    ra, ro = verify_prefix(draft, tgt)
+    assert np.array_equal(acc.cpu().numpy(), ra)
+    assert np.array_equal(out.cpu().numpy(), ro)

@@ -1,0 +1,173 @@
+"""GPU parity of the whole draft step against the float64 oracle.
+
+Bars: per-layer hidden-state relative L2 <= 2e-2 and logits max-abs <= 5e-2
+(bf16 activations vs float64); top-K ids exact when re-anchored on the GPU's own
+logits and valid within a 0.1 band against the oracle's; the path equal to the
+Viterbi path over the GPU's own candidates (near ties aside); appended cache
+rows within bf16 rounding; prefix acceptance exact; two runs bitwise equal.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_draft_amd import runner, synth
+from oracle.bf16 import bf16_to_f64
+from oracle.verify import verify_prefix
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_outputs(bufs):
+    torch.cuda.synchronize()
+    return dict(hidden=bufs.dbg_hidden.cpu().numpy().astype(np.float64),
+                logits=bufs.dbg_logits.cpu().numpy(),
+                ids=bufs.cand_ids.cpu().numpy(),
+                lp=bufs.cand_logp.cpu().numpy(),
+                draft=bufs.draft.cpu().numpy())
+
+
+def full_check(wl, bufs, ref, seqs=None):
+    g = gpu_outputs(bufs)
+    if seqs is not None:
+        for k in ("hidden",):
+            g[k] = g[k][:, seqs]
+        for k in ("logits", "ids", "lp", "draft"):
+            g[k] = g[k][seqs]
+    worst = parity.check_hidden(g["hidden"], ref["hidden"])
+    dl = np.abs(g["logits"] - ref["logits"]).max()
+    assert dl <= parity.LOGIT_MAX_ABS, dl
+    parity.check_topk_reanchored(g["logits"], g["ids"], g["lp"], wl.shape.top_k)
+    differ = parity.check_topk_valid(ref["logits"], g["ids"], wl.shape.top_k)
+    W = bufs.host_W
+    ties = parity.check_paths(g["ids"], g["lp"], g["draft"], W["code_a"], W["code_b"],
+                              wl.shape.pair_scale)
+    for which, key in (("k", "new_k"), ("v", "new_v")):
+        got = bf16_to_f64(bufs.new_rows(which))
+        if seqs is not None:
+            got = got[:, seqs]
+        want = bf16_to_f64(ref[key])
+        assert np.allclose(got, want, rtol=2 ** -7, atol=2e-2), which
+    say(f"  hidden worst rel L2 {worst:.2e}, logits max-abs {dl:.2e}, "
+        f"top-K rows differing within band {differ}, path near-ties {ties}")
+    return g
+
+
+def check_verify(bufs, g):
+    P = g["draft"].shape[1]
+    B = g["draft"].shape[0]
+    for k in range(P + 1):
+        tgt = np.zeros((B, P + 1), dtype=np.int32)
+        tgt[:, :k] = g["draft"][:, :k]
+        if k < P:
+            tgt[:, k] = g["draft"][:, k] + 1
+        tgt[:, k + 1:] = 7
+        bufs.verify(torch.from_numpy(tgt).cuda())
+        torch.cuda.synchronize()
+        ra, ro = verify_prefix(g["draft"], tgt)
+        assert np.array_equal(bufs.accept_len.cpu().numpy(), ra)
+        assert np.array_equal(bufs.out_tokens.cpu().numpy(), ro)
+
+
+def test_tiny_step_parity_and_determinism():
+    wl = synth.WORKLOADS["tiny"]
+    say(f"[step] {wl.name}")
+    bufs = runner.StepBuffers(wl)
+    bufs.step()
+    ref = parity.run_oracle(wl, bufs.host_W, bufs.inputs)
+    g = full_check(wl, bufs, ref)
+    check_verify(bufs, g)
+    first = {k: v.copy() for k, v in g.items()}
+    bufs.step()
+    g2 = gpu_outputs(bufs)
+    for k in first:
+        assert np.array_equal(first[k], g2[k]), k
+
+
+def test_tiny_step_gain_path_and_batch():
+    """Norm gains 1 + 0.1 N(0,1), 3 sequences with different context lengths
+    (one shorter than the window, one whose window starts mid-cache)."""
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], batch=3, seed=11, cache_extra=4)
+    say(f"[step] tiny gains, batch 3")
+    W = synth.make_weights(wl.shape, wl.seed, gain_jitter=0.1)
+    inputs = synth.make_step_inputs(wl, ctx_len=[48, 10, 0])
+    bufs = runner.StepBuffers(wl, weights=W, inputs=inputs)
+    bufs.step()
+    ref = parity.run_oracle(wl, W, inputs)
+    full_check(wl, bufs, ref)
+
+
+def test_tiny_step_short_tnew():
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], t_new=3, seed=12)
+    say("[step] tiny t_new=3")
+    bufs = runner.StepBuffers(wl)
+    bufs.step()
+    full_check(wl, bufs, parity.run_oracle(wl, bufs.host_W, bufs.inputs))
+
+
+def test_tiny_step_invalid_sequence_is_skipped():
+    """ctx_len out of range for one sequence: its outputs are -1 / -inf, the
+    others are unaffected, and no cache row of it is written."""
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], batch=2, seed=13)
+    say("[step] tiny invalid sequence")
+    good = runner.StepBuffers(wl)
+    good.step()
+    g_ok = gpu_outputs(good)
+    inputs = dict(good.inputs)
+    inputs["ctx_len"] = np.array([48, 10 ** 6], dtype=np.int32)
+    bad = runner.StepBuffers(wl, weights=good.host_W, inputs=inputs)
+    kc_before = bad.k_cache.clone()
+    bad.step()
+    g = gpu_outputs(bad)
+    assert np.array_equal(g["draft"][1], [-1] * 7)
+    assert (g["ids"][1] == -1).all() and np.isneginf(g["lp"][1]).all()
+    assert np.array_equal(g["draft"][0], g_ok["draft"][0])
+    assert np.array_equal(g["logits"][0], g_ok["logits"][0])
+    assert torch.equal(bad.k_cache[:, 1], kc_before[:, 1])
+
+
+def test_tiny_step_rows_outside_window_unread():
+    """NaN in every cache row outside the window leaves the outputs finite and
+    bitwise equal to a run with finite data there."""
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], seed=14, cache_extra=6)
+    say("[step] tiny poison")
+    a = runner.StepBuffers(wl)
+    a.step()
+    ga = gpu_outputs(a)
+    inp = dict(a.inputs)
+    n, T_new, Wn = wl.ctx_len, wl.t_new, wl.shape.window
+    lo = n + T_new - Wn
+    for c in ("k_cache", "v_cache"):
+        arr = inp[c].copy()
+        arr[:, :, :, :lo, :] = runner.BF16_NAN
+        arr[:, :, :, n + T_new:, :] = runner.BF16_NAN
+        inp[c] = arr
+    b = runner.StepBuffers(wl, weights=a.host_W, inputs=inp)
+    b.step()
+    gb = gpu_outputs(b)
+    assert np.isfinite(gb["logits"]).all()
+    for k in ga:
+        assert np.array_equal(ga[k], gb[k]), k
+
+
+@pytest.mark.timeout(900)
+def test_full_step_b1_parity():
+    """The pages' draft shape, one sequence, 4096 cached rows."""
+    wl = synth.WORKLOADS["full_b1"]
+    say(f"[step] {wl.name}: generating inputs")
+    bufs = runner.StepBuffers(wl)
+    say("  running GPU step")
+    bufs.step()
+    torch.cuda.synchronize()
+    say("  running oracle")
+    ref = parity.run_oracle(wl, bufs.host_W, bufs.inputs)
+    g = full_check(wl, bufs, ref)
+    check_verify(bufs, g)
