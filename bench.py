@@ -1,0 +1,221 @@
+"""Throughput of the DFlash 2 block-draft step on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic inputs
+resident in HBM: dflash_draft_step (tap fusion, 5 drafter layers, shared output
+head with top-16, Viterbi selector) followed by dflash_verify_prefix.  The
+workload is the pages' 27B-draft shape at batch 1 with a 4096-row context.
+
+Prints one JSON line: draft blocks/s, the roofline of the dominant kernel (the
+248320 x 5120 bf16 output head, timed live with HIP events around its launch
+inside every timed step), and the float64 CPU reference timed on this host on
+a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "full_b1"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm_bf16.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "block_diffusion_draft_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(alg_bytes):
+    """HBM bytes per output-head launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "lm_head_counters.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, bufs, budget_s=30.0):
+    """The oracle as it stands, on this host, on a bounded sample of the step.
+
+    Sample: the oracle's tap fusion, every drafter layer and the selector run in
+    full; the output head (the bulk of the work) runs on a contiguous slice of the
+    vocabulary and its time is scaled to the whole vocabulary.
+    """
+    import dataclasses
+    from oracle import draft as od
+    from oracle import select as osel
+    from oracle.bf16 import bf16_to_f64
+    s = wl.shape
+    W = bufs.host_W
+    inp = bufs.inputs
+    threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    # fusion + layers: run the oracle step with a vocabulary-sliced output head
+    vs = 16384
+    W2 = dict(W)
+    W2["lm_head"] = W["lm_head"][:vs]
+    cfg = dict(s.as_dict())
+    out = od.draft_step(cfg, W2, inp["taps"], inp["last_token"], inp["ctx_len"], inp["k_cache"],
+                        inp["v_cache"], want_logits=False)
+    t1 = time.perf_counter()
+    # time the head slice alone, to scale it to the full vocabulary
+    f = out["final"]
+    od.lm_head_topk(f, W["lm_head"][:vs], s.top_k, want_logits=False)
+    t2 = time.perf_counter()
+    head_slice = t2 - t1
+    body = (t1 - t0) - head_slice
+    head_full = head_slice * (s.vocab / vs)
+    # selector on the sample's candidates
+    t3 = time.perf_counter()
+    A, B = bf16_to_f64(W["code_a"]), bf16_to_f64(W["code_b"])
+    for b in range(wl.batch):
+        T = osel.pair_scores(out["cand_ids"][b], A, B, s.pair_scale)
+        osel.viterbi(out["cand_logp"][b], T)
+    t4 = time.perf_counter()
+    step_s = body + head_full + (t4 - t3)
+    return {"value": wl.batch / step_s, "unit": "draft blocks/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"one {wl.name} step: tap fusion, {s.n_layers} layers and selector in "
+                       f"full; output head on {vs} of {s.vocab} vocabulary rows, scaled "
+                       f"({t4 - t0:.1f} s of CPU work; step estimate {step_s:.1f} s)")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; the batch-1 draft step is "
+                          "measured on one MI355X (multi-GPU sharding is design-only)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from block_diffusion_draft_amd import binding, runner, synth
+
+    wl = synth.WORKLOADS[WORKLOAD]
+    s = wl.shape
+    print(f"[bench] preparing {wl.name}", file=sys.stderr, flush=True)
+    bufs = runner.StepBuffers(wl, dbg=False)
+    # target tokens agreeing with the draft on a 4-token prefix
+    bufs.step(dbg=False)
+    torch.cuda.synchronize()
+    d = bufs.draft.cpu().numpy()
+    tgt = np.zeros((wl.batch, s.block), dtype=np.int32)
+    tgt[:, :4] = d[:, :4]
+    tgt[:, 4] = (d[:, 4] + 1) % s.vocab
+    tgt[:, 5:] = synth.randint(wl.seed, "target_tail", (wl.batch, s.block - 5), 0, s.vocab)
+    target = torch.from_numpy(tgt).cuda()
+
+    K, Wm = args.steps, args.warmup
+    ev = [(binding.HipEvent(), binding.HipEvent()) for _ in range(K)]
+    probes = [binding.make_probe(binding.PROBE_LM_HEAD, a, b) for a, b in ev]
+
+    def one_step(probe=None):
+        bufs.step(dbg=False, probe=probe)
+        bufs.verify(target)
+
+    for _ in range(Wm):
+        one_step()
+    torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        # graphs replay the exact launches; the head's probe events are taken
+        # from an eager pass over the same steps
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            one_step()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                one_step()
+        torch.cuda.synchronize()
+        for _ in range(Wm):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    t_start, t_stop = binding.HipEvent(), binding.HipEvent()
+    torch.cuda.synchronize()
+    t_start.record()
+    if graph is not None:
+        for i in range(K):
+            graph.replay()
+    else:
+        for i in range(K):
+            one_step(probes[i])
+    t_stop.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_ms(t_stop) / K
+
+    # live timing of the dominant kernel (eager pass with probes)
+    for i in range(K):
+        one_step(probes[i])
+    torch.cuda.synchronize()
+    head_ms = float(np.mean([a.elapsed_ms(b) for a, b in ev]))
+    R = wl.batch * (s.block - 1)
+    alg = s.vocab * s.hidden * 2 + R * s.hidden * 2
+    achieved = alg / (head_ms * 1e-3) / 1e9
+    traffic = load_traffic(alg)
+
+    res = {
+        "metric": "draft blocks/s (8 tok) at 27B-draft shape, 1 GPU; % of HBM roofline",
+        "value": wl.batch / (ms * 1e-3),
+        "unit": "draft blocks/s",
+        "n_gpus": 1, "steps": K, "warmup": Wm, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "ctx_len": wl.ctx_len,
+                   "t_new": wl.t_new, "layers": s.n_layers, "hidden": s.hidden,
+                   "vocab": s.vocab, "top_k": s.top_k, "weights": s.weight_fmt,
+                   "step": "draft_step + verify_prefix", "hip_graph": bool(graph)},
+        "roofline": {"kernel": "output head (bf16 skinny MFMA GEMM, 248320 x 5120)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "launch_ms": head_ms, "algorithmic_bytes": alg},
+        "step_hbm_frac": None,
+    }
+    step_bytes = step_algorithmic_bytes(wl)
+    res["step_hbm_frac"] = step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU reference", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, bufs)
+    print(json.dumps(res))
+
+
+def step_algorithmic_bytes(wl):
+    """Bytes the step must move at least once: every weight byte, the output
+    head, the KV window of each sequence and layer, the appended rows, the taps,
+    the codebook rows the selector gathers and the outputs."""
+    s = wl.shape
+    B = wl.batch
+    qd, kd = s.n_q * s.head_dim, s.n_kv * s.head_dim
+    lin = s.n_taps * s.hidden * s.hidden + s.n_layers * (
+        qd * s.hidden + 2 * kd * s.hidden + s.hidden * qd + 3 * s.ffn * s.hidden)
+    wbytes = lin * 144 // 256 if s.weight_fmt == "q4k" else lin * 2
+    small = s.n_layers * (2 * s.hidden + 2 * s.head_dim + 2 * s.n_q * qd) * 2 + 3 * s.hidden * 2
+    head = s.vocab * s.hidden * 2
+    win = min(s.window, wl.ctx_len + wl.t_new)
+    kv = B * s.n_layers * 2 * (win * kd * 2)
+    taps = B * wl.t_new * s.n_taps * s.hidden * 2
+    codes = B * (s.block - 2) * 2 * s.top_k * s.sel_rank * 2
+    outs = B * (s.block - 1) * (1 + 2 * s.top_k) * 4
+    return wbytes + small + head + kv + taps + codes + outs
+
+
+if __name__ == "__main__":
+    main()

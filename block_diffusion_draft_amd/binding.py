@@ -8,6 +8,7 @@ it is built, and if it cannot be loaded the call fails.
 """
 import ctypes
 import os
+import re
 
 import numpy as np
 
@@ -148,9 +149,9 @@ class DeviceWeights:
         for name, val in W.items():
             arr = val[1] if isinstance(val, tuple) else val
             p = up(name, arr)
-            if name.startswith("l"):
-                l, field = name[1:].split(".", 1)
-                setattr(s.layer[int(l)], field, p)
+            m = re.match(r"^l(\d+)\.(\w+)$", name)
+            if m:
+                setattr(s.layer[int(m.group(1))], m.group(2), p)
             else:
                 setattr(s, name, p)
         self.struct = s
@@ -189,3 +190,52 @@ def q4k_gemm_workspace_bytes(M, N, K):
 
 def q4k_dequantize(w, out):
     check(lib().q4k_dequantize(_ptr(w), _ptr(out), out.numel() // 256, _stream()))
+
+
+# ---------------------------------------------------------------------------
+# HIP events for live per-kernel timing (recorded by the library on its stream)
+# ---------------------------------------------------------------------------
+_hip = None
+
+
+def hip():
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreate.argtypes = [ctypes.POINTER(c_void_p)]
+        h.hipEventDestroy.argtypes = [c_void_p]
+        h.hipEventSynchronize.argtypes = [c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(c_float), c_void_p, c_void_p]
+        h.hipEventRecord.argtypes = [c_void_p, c_void_p]
+        _hip = h
+    return _hip
+
+
+class HipEvent:
+    def __init__(self):
+        self.ev = c_void_p()
+        rc = hip().hipEventCreate(ctypes.byref(self.ev))
+        if rc != 0:
+            raise DflashError(f"hipEventCreate failed: {rc}")
+
+    def record(self):
+        hip().hipEventRecord(self.ev, _stream())
+
+    def elapsed_ms(self, later):
+        hip().hipEventSynchronize(later.ev)
+        ms = c_float()
+        rc = hip().hipEventElapsedTime(ctypes.byref(ms), self.ev, later.ev)
+        if rc != 0:
+            raise DflashError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def __del__(self):
+        try:
+            if self.ev:
+                hip().hipEventDestroy(self.ev)
+        except Exception:
+            pass
+
+
+def make_probe(kernel, start, stop, layer=0):
+    return Probe(kernel, layer, start.ev, stop.ev)

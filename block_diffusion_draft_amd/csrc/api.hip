@@ -18,8 +18,8 @@ struct Plan {
     int topk_nch;
     bool lm_skinny;
     // byte offsets into the workspace
-    size_t o_valid, o_h, o_xc, o_fcout, o_qkv, o_Q, o_Kb, o_Vb, o_attnO, o_attnML, o_Y, o_mid,
-        o_f, o_logits, o_pv, o_pi, o_pm, o_ps, o_part;
+    size_t o_valid, o_h, o_xc, o_u2, o_fcout, o_qkv, o_Q, o_Kb, o_Vb, o_attnO, o_attnML, o_o,
+        o_zp, o_Y, o_mid2, o_f, o_logits, o_pv, o_pi, o_pm, o_ps, o_part;
     size_t total;
 };
 
@@ -60,7 +60,7 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
     p.attn_chunk = wgs64 >= 16384 ? 256 : (wgs64 >= 4096 ? 128 : 64);
     p.attn_nch = win > 0 ? (win + p.attn_chunk - 1) / p.attn_chunk : 0;
     p.topk_nch = (p.V + topk_chunk_size() - 1) / topk_chunk_size();
-    p.lm_skinny = p.R <= 16 && p.H <= 5120 && p.H % 128 == 0;
+    p.lm_skinny = p.R <= 8 && p.H % 32 == 0 && (size_t)(p.H / 32) * 512 <= 160 * 1024;
 
     size_t part = 0;
     const int fmt = c->weight_fmt;
@@ -68,14 +68,16 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
     upd(gemm_part_bytes(fmt, p.M_ctx, p.H, c->n_taps * p.H));
     upd(gemm_part_bytes(fmt, p.M_qkv, p.qd + 2 * p.kd, p.H));
     upd(gemm_part_bytes(fmt, p.M_blk, p.H, p.qd));
-    upd(gemm_part_bytes(fmt, p.M_blk, 2 * p.F, p.H));
-    upd(gemm_part_bytes(fmt, p.M_blk, p.H, p.F));
+    // the MLP runs over [hi rows; lo rows] of its bf16-pair activations
+    upd(gemm_part_bytes(fmt, 2 * p.M_blk, 2 * p.F, p.H));
+    upd(gemm_part_bytes(fmt, 2 * p.M_blk, p.H, p.F));
 
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     p.o_valid = take((size_t)B * 4);
     p.o_h = take((size_t)p.M_blk * p.H * 4);
     p.o_xc = take((size_t)p.M_qkv * p.H * 2);
+    p.o_u2 = take((size_t)2 * p.M_blk * p.H * 2);
     p.o_fcout = take((size_t)p.M_ctx * p.H * 4);
     p.o_qkv = take((size_t)p.M_qkv * (p.qd + 2 * p.kd) * 4);
     p.o_Q = take((size_t)p.M_blk * p.qd * 2);
@@ -84,8 +86,10 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
     const size_t nslots = (size_t)B * p.n_kv * (p.attn_nch + 1) * p.QR;
     p.o_attnO = take(nslots * p.d * 4);
     p.o_attnML = take(nslots * 2 * 4);
+    p.o_o = take((size_t)p.M_blk * p.qd * 4);
+    p.o_zp = take((size_t)B * p.n_q * p.T * 2 * p.n_q * 4);
     p.o_Y = take((size_t)p.M_blk * p.qd * 2);
-    p.o_mid = take((size_t)p.M_blk * p.F * 2);
+    p.o_mid2 = take((size_t)2 * p.M_blk * p.F * 2);
     p.o_f = take((size_t)p.R * p.H * 2);
     p.o_logits = take((size_t)p.R * p.V * 4);
     p.o_pv = take((size_t)p.R * p.topk_nch * p.K * 4);
@@ -136,8 +140,11 @@ struct Ctx {
 };
 
 // y = A . W^T over up to 3 stacked weight matrices, then the reduction epilogue
+// pair: A holds [hi rows; lo rows] of M output rows (2 M GEMM rows), summed in the epilogue
 int run_gemm(const Ctx &x, const void *const *w, const int *seg_n, int nseg, const uint16_t *A,
-             int lda, int M, int K, int mode, float *of, uint16_t *ob, int ldo) {
+             int lda, int M_out, bool pair, int K, int mode, float *of, uint16_t *ob,
+             uint16_t *ob_lo, int ldo) {
+    const int M = pair ? 2 * M_out : M_out;
     int N = 0;
     int seg_end[3] = {0, 0, 0};
     for (int i = 0; i < nseg; i++) {
@@ -179,7 +186,8 @@ int run_gemm(const Ctx &x, const void *const *w, const int *seg_n, int nseg, con
         a.ldc = N;
         HIPCHK(launch_bf16_gemm_tiled(a, x.st));
     }
-    HIPCHK(launch_reduce_epilogue(part, splits, M, N, mode, of, ob, ldo, x.st));
+    HIPCHK(launch_reduce_epilogue(part, splits, M_out, N, pair ? M_out : 0, mode, of, ob, ob_lo,
+                                  ldo, x.st));
     return DFLASH_OK;
 }
 
@@ -258,11 +266,11 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
     {
         const void *ws[1] = {w->fc};
         const int sn[1] = {H};
-        rc = run_gemm(x, ws, sn, 1, taps, cfg->n_taps * H, p.M_ctx, cfg->n_taps * H,
-                      EPI_STORE_F32, x.at<float>(p.o_fcout), nullptr, H);
+        rc = run_gemm(x, ws, sn, 1, taps, cfg->n_taps * H, p.M_ctx, false, cfg->n_taps * H,
+                      EPI_STORE_F32, x.at<float>(p.o_fcout), nullptr, nullptr, H);
         if (rc) return rc;
         HIPCHK(launch_rmsnorm(x.at<float>(p.o_fcout), p.M_ctx, H, 1, 1, 0, w->hidden_norm,
-                              cfg->rms_eps, xc + (size_t)p.M_blk * H, H, x.st));
+                              cfg->rms_eps, xc + (size_t)p.M_blk * H, nullptr, H, x.st));
     }
 
     for (int l = 0; l < L; l++) {
@@ -270,13 +278,13 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
         uint16_t *kc = k_cache + (size_t)l * cache_layer;
         uint16_t *vc = v_cache + (size_t)l * cache_layer;
         // S2: x = RMSNorm(h) -> rows [0, M_blk) of xc
-        HIPCHK(launch_rmsnorm(h, p.M_blk, H, 1, 1, 0, lw.in_norm, cfg->rms_eps, xc, H, x.st));
+        HIPCHK(launch_rmsnorm(h, p.M_blk, H, 1, 1, 0, lw.in_norm, cfg->rms_eps, xc, nullptr, H, x.st));
         // S3: [Q | K | V] of block rows and K, V of context rows
         {
             const void *ws[3] = {lw.wq, lw.wk, lw.wv};
             const int sn[3] = {p.qd, p.kd, p.kd};
-            rc = run_gemm(x, ws, sn, 3, xc, H, p.M_qkv, H, EPI_STORE_F32, x.at<float>(p.o_qkv),
-                          nullptr, p.qd + 2 * p.kd);
+            rc = run_gemm(x, ws, sn, 3, xc, H, p.M_qkv, false, H, EPI_STORE_F32,
+                          x.at<float>(p.o_qkv), nullptr, nullptr, p.qd + 2 * p.kd);
             if (rc) return rc;
         }
         // S4: per-head norms, rotary embedding, cache append
@@ -307,34 +315,39 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
             a.ctx_len = ctx_len; a.valid = valid;
             a.B = batch; a.T = p.T; a.t_new = t_new; a.n_q = p.n_q; a.n_kv = p.n_kv; a.d = p.d;
             a.window = cfg->window; a.chunk = p.attn_chunk; a.n_chunks = p.attn_nch;
-            a.w_conv = lw.w_conv; a.Y = x.at<uint16_t>(p.o_Y);
+            a.w_conv = lw.w_conv; a.o = x.at<float>(p.o_o); a.zp = x.at<float>(p.o_zp);
+            a.Y = x.at<uint16_t>(p.o_Y);
             HIPCHK(launch_merge_conv(a, x.st));
         }
         // S7: h += Y . W_o^T
         {
             const void *ws[1] = {lw.wo};
             const int sn[1] = {H};
-            rc = run_gemm(x, ws, sn, 1, x.at<uint16_t>(p.o_Y), p.qd, p.M_blk, p.qd, EPI_ADD_F32,
-                          h, nullptr, H);
+            rc = run_gemm(x, ws, sn, 1, x.at<uint16_t>(p.o_Y), p.qd, p.M_blk, false, p.qd,
+                          EPI_ADD_F32, h, nullptr, nullptr, H);
             if (rc) return rc;
         }
-        // S8: u = RMSNorm(h); h += (silu(u Wg^T) * u Wu^T) Wd^T
-        HIPCHK(launch_rmsnorm(h, p.M_blk, H, 1, 1, 0, lw.post_norm, cfg->rms_eps, xc, H, x.st));
+        // S8: u = RMSNorm(h); h += (silu(u Wg^T) * u Wu^T) Wd^T, with u and the SwiGLU
+        // output carried as bf16 (hi, lo) pairs: the MLP inputs dominate the rounding error
+        uint16_t *u2 = x.at<uint16_t>(p.o_u2);
+        uint16_t *mid2 = x.at<uint16_t>(p.o_mid2);
+        HIPCHK(launch_rmsnorm(h, p.M_blk, H, 1, 1, 0, lw.post_norm, cfg->rms_eps, u2,
+                              u2 + (size_t)p.M_blk * H, H, x.st));
         {
             const void *ws[2] = {lw.wg, lw.wu};
             const int sn[2] = {p.F, p.F};
             const bool probe_ffn = probe && probe->kernel == DFLASH_PROBE_FFN_GATE_UP && probe->layer == l;
             if (probe_ffn) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_start, x.st));
-            rc = run_gemm(x, ws, sn, 2, xc, H, p.M_blk, H, EPI_SWIGLU_BF16, nullptr,
-                          x.at<uint16_t>(p.o_mid), p.F);
+            rc = run_gemm(x, ws, sn, 2, u2, H, p.M_blk, true, H, EPI_SWIGLU_BF16, nullptr, mid2,
+                          mid2 + (size_t)p.M_blk * p.F, p.F);
             if (rc) return rc;
             if (probe_ffn) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_stop, x.st));
         }
         {
             const void *ws[1] = {lw.wd};
             const int sn[1] = {H};
-            rc = run_gemm(x, ws, sn, 1, x.at<uint16_t>(p.o_mid), p.F, p.M_blk, p.F, EPI_ADD_F32,
-                          h, nullptr, H);
+            rc = run_gemm(x, ws, sn, 1, mid2, p.F, p.M_blk, true, p.F, EPI_ADD_F32, h, nullptr,
+                          nullptr, H);
             if (rc) return rc;
         }
         if (dbg_hidden)
@@ -344,7 +357,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
 
     // S9: final norm of proposal rows 1..7
     uint16_t *f = x.at<uint16_t>(p.o_f);
-    HIPCHK(launch_rmsnorm(h, p.R, H, p.P, p.T, 1, w->final_norm, cfg->rms_eps, f, H, x.st));
+    HIPCHK(launch_rmsnorm(h, p.R, H, p.P, p.T, 1, w->final_norm, cfg->rms_eps, f, nullptr, H, x.st));
 
     // S10: logits with the shared output head, then log-softmax statistics and top-K
     float *logits = dbg_logits ? dbg_logits : x.at<float>(p.o_logits);
@@ -399,8 +412,8 @@ int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
     a.A = x; a.lda = K; a.M = M; a.N = N; a.KB = K / 256; a.kb_per = p.kb_per;
     a.part = (float *)workspace;
     HIPCHK(launch_q4k_gemm(a, p, (hipStream_t)stream));
-    HIPCHK(launch_reduce_epilogue((float *)workspace, p.splits, M, N, EPI_STORE_BF16, nullptr, y,
-                                  N, (hipStream_t)stream));
+    HIPCHK(launch_reduce_epilogue((float *)workspace, p.splits, M, N, 0, EPI_STORE_BF16, nullptr, y,
+                                  nullptr, N, (hipStream_t)stream));
     return DFLASH_OK;
 }
 

@@ -4,11 +4,11 @@
 //    steps of 32 staged through double-buffered LDS in MFMA lane order.  Used for
 //    the unquantised drafter matrices at many rows and for the shared output head
 //    when more than 16 rows need logits.
-//  * skinny: at most 16 rows (one draft block of one sequence).  The workgroup's
-//    4 waves split K; each wave holds its quarter of the activation rows in VGPRs
-//    for the whole launch and streams 16 weight rows per tile from HBM, so the
-//    output head (248320 x 5120 bf16, the bulk of the step's bytes) is read
-//    exactly once with 16-byte loads.  Partial tiles are summed through LDS.
+//  * skinny: at most 8 rows (the 7 proposal rows of one draft block).  The rows
+//    sit in LDS for the whole launch; every wave streams its own contiguous run
+//    of 16-row weight tiles over the full K with 8 fragment loads in flight, so
+//    the output head (248320 x 5120 bf16, the bulk of the step's bytes) is read
+//    exactly once with 16-byte loads and no cross-wave reduction.
 #include "common.h"
 #include "kernels.h"
 
@@ -98,52 +98,73 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_tiled(Bf16GemmArgs a) {
         }
 }
 
-constexpr int SKINNY_MAXKS = 40;    // k-steps of 32 per wave: K <= 4 * 40 * 32 = 5120
+// Skinny product for at most 8 activation rows (one block's 7 proposal rows).
+// The rows live in LDS for the whole launch, already in MFMA lane order, so each
+// wave can run the full K of its own weight tiles with no cross-wave reduction.
+// Each wave owns a contiguous range of 16-row weight tiles and streams them as a
+// flat sequence of (tile, k-step) fragments with LM_PD loads in flight.
+constexpr int LM_PD = 8;
 
-__global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a) {
-    __shared__ f32x4_t red[4][64];
+__global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a, int tiles_per_wave) {
+    extern __shared__ __align__(16) u32x4_t Alds[];        // [nks][32]: lanes with row < 8
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
-    const int kq = a.K / 4;
-    const int nks = kq / 32;
-    const int kbase = wave * kq;
-
-    u32x4_t af[SKINNY_MAXKS];
-    const bool row_ok = c < a.M;
-#pragma unroll
-    for (int ks = 0; ks < SKINNY_MAXKS; ks++) {
-        if (ks < nks && row_ok)
-            af[ks] = *reinterpret_cast<const u32x4_t *>(a.A + (size_t)c * a.lda + kbase + ks * 32 + 8 * g);
-        else
-            af[ks] = (u32x4_t){0, 0, 0, 0};
-    }
-
+    const int nks = a.K / 32;
     const int ntiles = a.N / 16;
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int n = tile * 16 + c;
-        const uint16_t *wr = seg_row(a, n) + kbase + 8 * g;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const int t0 = (blockIdx.x * 4 + wave) * tiles_per_wave;
+    const int t1 = min(t0 + tiles_per_wave, ntiles);
+    const int steps = t1 > t0 ? (t1 - t0) * nks : 0;
+
+    // first weight fragments before the activations are staged
+    u32x4_t eb[LM_PD];
+    int lt = t0, lk = 0;                 // tile / k-step of the next fragment to load
+    auto wptr = [&](int tile, int ks) {
+        return seg_row(a, tile * 16 + c) + ks * 32 + 8 * g;
+    };
 #pragma unroll
-        for (int k0 = 0; k0 < SKINNY_MAXKS; k0 += 8) {
-            u32x4_t b[8];
-#pragma unroll
-            for (int u = 0; u < 8; u++)
-                if (k0 + u < nks) b[u] = *reinterpret_cast<const u32x4_t *>(wr + (k0 + u) * 32);
-#pragma unroll
-            for (int u = 0; u < 8; u++)
-                if (k0 + u < nks) acc = mfma16x16x32(af[k0 + u], b[u], acc);
+    for (int u = 0; u < LM_PD - 1; u++) {
+        if (u < steps) {
+            eb[u] = *reinterpret_cast<const u32x4_t *>(wptr(lt, lk));
+            if (++lk == nks) { lk = 0; lt++; }
         }
-        red[wave][lane] = acc;
-        __syncthreads();
-        if (wave == 0) {
-            f32x4_t s = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+    }
+    for (int e = tid; e < nks * 32; e += 256) {
+        const int ks = e >> 5, slot = e & 31, gg = slot >> 3, r = slot & 7;
+        u32x4_t v = {0, 0, 0, 0};
+        if (r < a.M) v = *reinterpret_cast<const u32x4_t *>(a.A + (size_t)r * a.lda + ks * 32 + 8 * gg);
+        Alds[e] = v;
+    }
+    __syncthreads();
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    int ct = t0, ck = 0;                 // tile / k-step being computed
+    for (int s0 = 0; s0 < steps; s0 += LM_PD) {
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const int m = 4 * g + v;
-                if (m < a.M) a.C[(size_t)m * a.ldc + n] = s[v];
+        for (int u = 0; u < LM_PD; u++) {
+            const int i = s0 + u;
+            if (i + LM_PD - 1 < steps) {
+                eb[(u + LM_PD - 1) % LM_PD] = *reinterpret_cast<const u32x4_t *>(wptr(lt, lk));
+                if (++lk == nks) { lk = 0; lt++; }
+            }
+            if (i < steps) {
+                u32x4_t af = {0, 0, 0, 0};
+                if (c < 8) af = Alds[ck * 32 + g * 8 + c];
+                acc = mfma16x16x32(af, eb[u], acc);
+                if (++ck == nks) {
+                    const int n = ct * 16 + c;
+                    if (g < 2) {
+#pragma unroll
+                        for (int v = 0; v < 4; v++) {
+                            const int m = 4 * g + v;
+                            if (m < a.M) a.C[(size_t)m * a.ldc + n] = acc[v];
+                        }
+                    }
+                    acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                    ck = 0;
+                    ct++;
+                }
             }
         }
-        __syncthreads();
     }
 }
 
@@ -157,7 +178,16 @@ hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st) {
 
 hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st) {
     const int ntiles = a.N / 16;
-    const int grid = ntiles < 1024 ? ntiles : 1024;
-    hipLaunchKernelGGL(k_bf16_gemm_skinny, dim3(grid), dim3(256), 0, st, a);
+    const int tpw = ceil_div(ntiles, 2048);               // ~2048 waves, 2 workgroups per CU
+    const int waves = ceil_div(ntiles, tpw);
+    const size_t lds = (size_t)(a.K / 32) * 32 * 16;
+    static size_t lds_set = 0;
+    if (lds > 65536 && lds > lds_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_bf16_gemm_skinny,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        lds_set = lds;
+    }
+    hipLaunchKernelGGL(k_bf16_gemm_skinny, dim3(ceil_div(waves, 4)), dim3(256), lds, st, a, tpw);
     return hipGetLastError();
 }

@@ -16,7 +16,7 @@ struct Q4kGemmArgs {
     float *part;                 // fp32 partials [splits][M][N]
 };
 struct Q4kPlan {
-    int KB, kb_per, splits, row_groups, grid_x;
+    int KB, kb_per, splits, row_groups, grid_x, rt;
     size_t lds_bytes;
 };
 Q4kPlan q4k_plan(int M, int N, int K);
@@ -36,23 +36,27 @@ struct Bf16GemmArgs {
 };
 // tiled 128x128 MFMA GEMM, any M
 hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st);
-// rows <= 16, K <= 5120: split-K over the 4 waves of a workgroup, activations in VGPRs
+// rows <= 8: activations resident in LDS, every wave streams whole weight tiles
 hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------- layer ops
 enum EpiMode { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_SWIGLU_BF16 = 2, EPI_STORE_BF16 = 3 };
-hipError_t launch_reduce_epilogue(const float *part, int splits, int M, int N, int mode,
-                                  float *out_f32, uint16_t *out_bf16, int ldo, hipStream_t st);
+// out row r = sum over splits of partial rows r (+ r + pair); SWIGLU writes bf16 hi
+// (and lo when out_bf16_lo) of silu(gate) * up, gate in columns [0, N/2)
+hipError_t launch_reduce_epilogue(const float *part, int splits, int M, int N, int pair,
+                                  int mode, float *out_f32, uint16_t *out_bf16,
+                                  uint16_t *out_bf16_lo, int ldo, hipStream_t st);
 
 // per-sequence validity flags + block assembly h[b][0] = E[last], h[b][1..] = mask
 hipError_t launch_embed(const uint16_t *embed, const uint16_t *mask_emb, const int32_t *last,
                         const int32_t *ctx_len, int B, int T, int H, int V, int t_new, int cap,
                         float *h, int32_t *valid, hipStream_t st);
 
-// out[r] = bf16(RMSNorm(in[row(r)]) * g), row(r) = (r / per) * in_group + in_off + r % per
+// out[r] = bf16(RMSNorm(in[row(r)]) * g), row(r) = (r / per) * in_group + in_off + r % per;
+// out_lo (nullable) receives the bf16 residual of each value
 hipError_t launch_rmsnorm(const float *in, int R, int H, int per, int in_group, int in_off,
-                          const uint16_t *gain, float eps, uint16_t *out, int ldo,
-                          hipStream_t st);
+                          const uint16_t *gain, float eps, uint16_t *out, uint16_t *out_lo,
+                          int ldo, hipStream_t st);
 
 struct RopeArgs {
     const float *qkv;            // fp32 [B*(T + t_new)][qd + 2 kd]: block rows then context rows
@@ -83,6 +87,8 @@ struct MergeConvArgs {
     const int32_t *ctx_len, *valid;
     int B, T, t_new, n_q, n_kv, d, window, chunk, n_chunks;
     const uint16_t *w_conv;      // bf16 [2 n_q][n_q d]
+    float *o;                    // fp32 [B*T][n_q d] merged attention output
+    float *zp;                   // fp32 [B][n_q][T][2 n_q] per-head conv-tap partials
     uint16_t *Y;                 // bf16 [B*T][n_q d]
 };
 hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st);

@@ -35,9 +35,11 @@ __global__ __launch_bounds__(256) void k_embed(const uint16_t *embed, const uint
 }
 
 // ---------------------------------------------------------------- RMSNorm -> bf16
+// With out_lo, the value is also kept as a bf16 pair: out_lo = bf16(v - bf16(v)),
+// so a GEMM over [hi rows; lo rows] sees 16 significant bits of the activation.
 __global__ __launch_bounds__(256) void k_rmsnorm(const float *in, int H, int per, int in_group,
                                                  int in_off, const uint16_t *gain, float eps,
-                                                 uint16_t *out, int ldo) {
+                                                 uint16_t *out, uint16_t *out_lo, int ldo) {
     __shared__ float scratch[4];
     const int r = blockIdx.x;
     const float *x = in + ((size_t)(r / per) * in_group + in_off + r % per) * H;
@@ -46,20 +48,31 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *in, int H, int per
     ss = block_sum_256(ss, scratch);
     const float inv = rsqrtf(ss / (float)H + eps);
     uint16_t *o = out + (size_t)r * ldo;
-    for (int i = threadIdx.x; i < H; i += 256) o[i] = f32_to_bf16(x[i] * inv * bf16_to_f32(gain[i]));
+    uint16_t *ol = out_lo ? out_lo + (size_t)r * ldo : nullptr;
+    for (int i = threadIdx.x; i < H; i += 256) {
+        const float v = x[i] * inv * bf16_to_f32(gain[i]);
+        const uint16_t hb = f32_to_bf16(v);
+        o[i] = hb;
+        if (ol) ol[i] = f32_to_bf16(v - bf16_to_f32(hb));
+    }
 }
 
 // ---------------------------------------------------------------- split-K reduction
+// Output row r sums the partial rows r (and r + pair when the GEMM ran over
+// [hi rows; lo rows]) over all splits in a fixed order.
 __global__ __launch_bounds__(256) void k_reduce(const float *part, int splits, int M, int N,
-                                                int mode, float *of, uint16_t *ob, int ldo) {
+                                                int pair, int mode, float *of, uint16_t *ob,
+                                                uint16_t *ob_lo, int ldo) {
     const int Nout = mode == EPI_SWIGLU_BF16 ? N / 2 : N;
     const size_t total = (size_t)M * Nout;
-    const size_t stride = (size_t)M * N;
+    const int Min = pair ? 2 * M : M;
+    const size_t stride = (size_t)Min * N;
     for (size_t e = blockIdx.x * 256ull + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
         const int r = (int)(e / Nout), c = (int)(e % Nout);
         const float *p = part + (size_t)r * N + c;
+        const float *q = part + (size_t)(r + pair) * N + c;
         float s = 0.f;
-        for (int k = 0; k < splits; k++) s += p[k * stride];
+        for (int k = 0; k < splits; k++) s += p[k * stride] + (pair ? q[k * stride] : 0.f);
         if (mode == EPI_STORE_F32) {
             of[(size_t)r * ldo + c] = s;
         } else if (mode == EPI_ADD_F32) {
@@ -68,9 +81,13 @@ __global__ __launch_bounds__(256) void k_reduce(const float *part, int splits, i
             ob[(size_t)r * ldo + c] = f32_to_bf16(s);
         } else {
             float u = 0.f;
-            for (int k = 0; k < splits; k++) u += p[k * stride + Nout];
+            for (int k = 0; k < splits; k++)
+                u += p[k * stride + Nout] + (pair ? q[k * stride + Nout] : 0.f);
             const float act = s / (1.f + expf(-s));          // silu(gate)
-            ob[(size_t)r * ldo + c] = f32_to_bf16(act * u);
+            const float v = act * u;
+            const uint16_t hb = f32_to_bf16(v);
+            ob[(size_t)r * ldo + c] = hb;
+            if (ob_lo) ob_lo[(size_t)r * ldo + c] = f32_to_bf16(v - bf16_to_f32(hb));
         }
     }
 }
@@ -130,84 +147,95 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
 }
 
 // ---------------------------------------------------------------- merge + dynamic conv
-// One workgroup per (sequence, block row t): merges the split-window attention
-// partials of rows t and t-1 for every query head, then
-//   z_t = W_c . vec(o_t),  y_{t,h} = z_t[h] o_{t,h} + z_t[n_q + h] o_{t-1,h}.
-__global__ __launch_bounds__(256) void k_merge_conv(MergeConvArgs a) {
-    extern __shared__ float sm[];
-    const int b = blockIdx.x / a.T, t = blockIdx.x % a.T;
-    const int tid = threadIdx.x;
-    const int qd = a.n_q * a.d, G = a.n_q / a.n_kv, QR = G * a.T;
+// k_attn_merge: one workgroup per (query head h, sequence b).  Combines the
+// split-window partials of the 8 block rows of head h (log-sum-exp merge) into
+// o[b][t][h*d..] (fp32), and contributes head h's share of the convolution taps
+//     zp[b][h][t][q] = sum_e W_c[q][h d + e] o[b][t][h][e],   q < 2 n_q,
+// so that z_t = W_c . vec(o_t) = sum_h zp[b][h][t][:].
+__global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int d = a.d, T = a.T, G = a.n_q / a.n_kv, QR = G * T, qd = a.n_q * d;
+    const int kvh = h / G, hq = h % G;
     const int nch1 = a.n_chunks + 1;
-    float *o_cur = sm;                 // [qd]
-    float *o_prev = sm + qd;           // [qd]
-    float *wts = sm + 2 * qd;          // [2][n_q][nch1] merge weights
-    float *z = wts + 2 * a.n_q * nch1; // [2 n_q]
-    uint16_t *Y = a.Y + (size_t)blockIdx.x * qd;
+    const int nq2 = 2 * a.n_q;
+    extern __shared__ float sm[];
+    float *o = sm;                      // [T][d]
+    float *w = sm + T * d;              // [T][nch1]
     if (!a.valid[b]) {
-        for (int i = tid; i < qd; i += 256) Y[i] = 0;
+        for (int e = tid; e < T * d; e += 256) a.o[((size_t)b * T + e / d) * qd + h * d + e % d] = 0.f;
+        for (int e = tid; e < T * nq2; e += 256) a.zp[(((size_t)b * a.n_q + h) * T) * nq2 + e] = 0.f;
         return;
     }
     const int n = a.ctx_len[b];
     const int hi = n + a.t_new;
     const int lo = hi - a.window > 0 ? hi - a.window : 0;
     const int nch_b = ceil_div(hi - lo, a.chunk);
-
-    // merge weights exp(m_c - M) / L for (row t, row t-1) x heads
-    for (int p = tid; p < 2 * a.n_q; p += 256) {
-        const int which = p / a.n_q, h = p % a.n_q;
-        const int tt = t - which;
-        float *w = wts + (size_t)p * nch1;
-        if (tt < 0) {
-            for (int c = 0; c < nch1; c++) w[c] = 0.f;
-            continue;
-        }
-        const int kvh = h / G, row = (h % G) * a.T + tt;
-        const float *ml = a.ml + ((size_t)(b * a.n_kv + kvh) * nch1) * QR * 2;
+    const float *ml = a.ml + ((size_t)(b * a.n_kv + kvh) * nch1) * QR * 2;
+    if (tid < T) {
+        const int row = hq * T + tid;
         float M = -INFINITY;
-        for (int c = 0; c < nch1; c++) {
-            if (c >= nch_b && c != a.n_chunks) continue;
-            M = fmaxf(M, ml[((size_t)c * QR + row) * 2]);
-        }
+        for (int c = 0; c < nch1; c++)
+            if (c < nch_b || c == a.n_chunks) M = fmaxf(M, ml[((size_t)c * QR + row) * 2]);
         float L = 0.f;
         for (int c = 0; c < nch1; c++) {
-            if (c >= nch_b && c != a.n_chunks) { w[c] = 0.f; continue; }
-            const float e = expf(ml[((size_t)c * QR + row) * 2] - M);
-            w[c] = e;
-            L += e * ml[((size_t)c * QR + row) * 2 + 1];
+            float e = 0.f;
+            if (c < nch_b || c == a.n_chunks) {
+                e = expf(ml[((size_t)c * QR + row) * 2] - M);
+                L += e * ml[((size_t)c * QR + row) * 2 + 1];
+            }
+            w[tid * nch1 + c] = e;
         }
-        const float invL = 1.f / L;
-        for (int c = 0; c < nch1; c++) w[c] *= invL;
+        const float inv = 1.f / L;
+        for (int c = 0; c < nch1; c++) w[tid * nch1 + c] *= inv;
     }
     __syncthreads();
-    for (int e = tid; e < 2 * qd; e += 256) {
-        const int which = e / qd, i = e % qd;
-        const int tt = t - which;
+    const float *O = a.O + ((size_t)(b * a.n_kv + kvh) * nch1) * QR * d;
+    for (int e = tid; e < T * d; e += 256) {
+        const int t = e / d, col = e % d, row = hq * T + t;
         float acc = 0.f;
-        if (tt >= 0) {
-            const int h = i / a.d, col = i % a.d;
-            const int kvh = h / G, row = (h % G) * a.T + tt;
-            const float *w = wts + (size_t)(which * a.n_q + h) * nch1;
-            const float *O = a.O + ((size_t)(b * a.n_kv + kvh) * nch1) * QR * a.d;
-            for (int c = 0; c < nch1; c++)
-                if (w[c] != 0.f) acc += w[c] * O[((size_t)c * QR + row) * a.d + col];
+        for (int c = 0; c < nch1; c++) {
+            const float wc = w[t * nch1 + c];
+            if (wc != 0.f) acc += wc * O[((size_t)c * QR + row) * d + col];
         }
-        (which == 0 ? o_cur : o_prev)[i] = acc;
+        o[e] = acc;
+        a.o[((size_t)b * T + t) * qd + h * d + col] = acc;
     }
     __syncthreads();
-    // z = W_c . o_t : wave w computes outputs w, w+4, ...
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int q = wave; q < 2 * a.n_q; q += 4) {
-        const uint16_t *wr = a.w_conv + (size_t)q * qd;
+    for (int e = tid; e < T * nq2; e += 256) {
+        const int t = e / nq2, q = e % nq2;
+        const uint16_t *wr = a.w_conv + (size_t)q * qd + h * d;
+        const float *ot = o + t * d;
         float s = 0.f;
-        for (int i = lane; i < qd; i += 64) s += bf16_to_f32(wr[i]) * o_cur[i];
-        s = wave_sum(s);
-        if (lane == 0) z[q] = s;
+        for (int i = 0; i < d; i += 8) {
+            const u32x4_t wv = *reinterpret_cast<const u32x4_t *>(wr + i);
+            s += bf16_to_f32(wv.x & 0xFFFF) * ot[i] + bf16_to_f32(wv.x >> 16) * ot[i + 1];
+            s += bf16_to_f32(wv.y & 0xFFFF) * ot[i + 2] + bf16_to_f32(wv.y >> 16) * ot[i + 3];
+            s += bf16_to_f32(wv.z & 0xFFFF) * ot[i + 4] + bf16_to_f32(wv.z >> 16) * ot[i + 5];
+            s += bf16_to_f32(wv.w & 0xFFFF) * ot[i + 6] + bf16_to_f32(wv.w >> 16) * ot[i + 7];
+        }
+        a.zp[(((size_t)b * a.n_q + h) * T + t) * nq2 + q] = s;
+    }
+}
+
+// k_conv_apply: one workgroup per (sequence, block row t):
+//   z_t = sum_h zp[b][h][t];  y_{t,h} = z_t[h] o_{t,h} + z_t[n_q + h] o_{t-1,h},  o_{-1} = 0.
+__global__ __launch_bounds__(256) void k_conv_apply(MergeConvArgs a) {
+    __shared__ float z[2 * 256];
+    const int b = blockIdx.x / a.T, t = blockIdx.x % a.T, tid = threadIdx.x;
+    const int qd = a.n_q * a.d, nq2 = 2 * a.n_q;
+    for (int q = tid; q < nq2; q += 256) {
+        float s = 0.f;
+        for (int h = 0; h < a.n_q; h++) s += a.zp[(((size_t)b * a.n_q + h) * a.T + t) * nq2 + q];
+        z[q] = s;
     }
     __syncthreads();
+    const float *ot = a.o + ((size_t)b * a.T + t) * qd;
+    const float *op = ot - qd;
+    uint16_t *Y = a.Y + ((size_t)b * a.T + t) * qd;
     for (int i = tid; i < qd; i += 256) {
         const int h = i / a.d;
-        Y[i] = f32_to_bf16(z[h] * o_cur[i] + z[a.n_q + h] * o_prev[i]);
+        const float prev = t > 0 ? op[i] : 0.f;
+        Y[i] = f32_to_bf16(z[h] * ot[i] + z[a.n_q + h] * prev);
     }
 }
 
@@ -222,20 +250,21 @@ hipError_t launch_embed(const uint16_t *embed, const uint16_t *mask_emb, const i
 }
 
 hipError_t launch_rmsnorm(const float *in, int R, int H, int per, int in_group, int in_off,
-                          const uint16_t *gain, float eps, uint16_t *out, int ldo,
-                          hipStream_t st) {
+                          const uint16_t *gain, float eps, uint16_t *out, uint16_t *out_lo,
+                          int ldo, hipStream_t st) {
     hipLaunchKernelGGL(k_rmsnorm, dim3(R), dim3(256), 0, st, in, H, per, in_group, in_off, gain,
-                       eps, out, ldo);
+                       eps, out, out_lo, ldo);
     return hipGetLastError();
 }
 
-hipError_t launch_reduce_epilogue(const float *part, int splits, int M, int N, int mode,
-                                  float *out_f32, uint16_t *out_bf16, int ldo, hipStream_t st) {
+hipError_t launch_reduce_epilogue(const float *part, int splits, int M, int N, int pair,
+                                  int mode, float *out_f32, uint16_t *out_bf16,
+                                  uint16_t *out_bf16_lo, int ldo, hipStream_t st) {
     const size_t total = (size_t)M * (mode == EPI_SWIGLU_BF16 ? N / 2 : N);
     size_t grid = (total + 255) / 256;
     if (grid > 8192) grid = 8192;
-    hipLaunchKernelGGL(k_reduce, dim3((unsigned)grid), dim3(256), 0, st, part, splits, M, N, mode,
-                       out_f32, out_bf16, ldo);
+    hipLaunchKernelGGL(k_reduce, dim3((unsigned)grid), dim3(256), 0, st, part, splits, M, N, pair,
+                       mode, out_f32, out_bf16, out_bf16_lo, ldo);
     return hipGetLastError();
 }
 
@@ -246,7 +275,10 @@ hipError_t launch_qk_norm_rope(const RopeArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st) {
-    const size_t lds = (size_t)(2 * a.n_q * a.d + 2 * a.n_q * (a.n_chunks + 1) + 2 * a.n_q) * 4;
-    hipLaunchKernelGGL(k_merge_conv, dim3(a.B * a.T), dim3(256), lds, st, a);
+    const size_t lds = (size_t)(a.T * a.d + a.T * (a.n_chunks + 1)) * 4;
+    hipLaunchKernelGGL(k_attn_merge, dim3(a.n_q, a.B), dim3(256), lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_conv_apply, dim3(a.B * a.T), dim3(256), 0, st, a);
     return hipGetLastError();
 }

@@ -52,15 +52,49 @@ __device__ __forceinline__ u32x4_t nibbles_to_bf16(uint32_t p0, uint32_t p1) {
     return b;
 }
 
+// Weight bytes of one super-block for one lane: the 16-byte header of its column
+// and its 8 quant bytes in each of the 4 64-weight chunks.
+struct WStage {
+    u32x4_t hdr;
+    u32x2_t q[4];
+};
+
+__device__ __forceinline__ WStage load_stage(const unsigned char *blk, int g) {
+    WStage s;
+    s.hdr = *reinterpret_cast<const u32x4_t *>(blk);
+#pragma unroll
+    for (int c = 0; c < 4; c++) s.q[c] = *reinterpret_cast<const u32x2_t *>(blk + 16 + 32 * c + 8 * g);
+    return s;
+}
+
+constexpr int PD = 4;              // super-blocks in flight per wave
+
+template <int RT>
 __global__ __launch_bounds__(256) void k_q4k_gemm(Q4kGemmArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int split = blockIdx.y;
-    const int row0 = blockIdx.z * (MAX_RT * 16);
-    const int rt_n = min(MAX_RT, ceil_div(a.M - row0, 16));
+    const int row0 = blockIdx.z * (RT * 16);
+    const int rt_n = min(RT, ceil_div(a.M - row0, 16));
     const int sb0 = split * a.kb_per;
     const int nsb = min(a.kb_per, a.KB - sb0);
     if (nsb <= 0) return;                                   // uniform over the workgroup
+
+    const int ct = blockIdx.x * 4 + wave;            // column tile of this wave
+    const bool active = ct * 16 < a.N;
+    const int n = ct * 16 + (lane & 15);
+    const int g = lane >> 4;
+    // weight segment of this column tile (segments are multiples of 16 columns)
+    int si = 0;
+    while (si + 1 < a.nseg && ct * 16 >= a.seg_end[si]) si++;
+    const int nloc = n - (si == 0 ? 0 : a.seg_end[si - 1]);
+    const unsigned char *wrow = a.w[si] + ((size_t)nloc * a.KB + sb0) * 144;
+
+    // start streaming weights before the activations are staged
+    WStage st[PD];
+#pragma unroll
+    for (int u = 0; u < PD - 1; u++)
+        if (active && u < nsb) st[u] = load_stage(wrow + (size_t)u * 144, g);
 
     u32x4_t *A_lds = reinterpret_cast<u32x4_t *>(lds);      // [nsb][8][rt_n][64]
     float *S_lds = reinterpret_cast<float *>(lds + (size_t)nsb * 8 * rt_n * 64 * 16);  // [nsb][8][rt_n*16]
@@ -73,11 +107,11 @@ __global__ __launch_bounds__(256) void k_q4k_gemm(Q4kGemmArgs a) {
         const int rt = rest % rt_n; rest /= rt_n;
         const int j = rest & 7;
         const int sbi = rest >> 3;
-        const int r = ln & 15, g = ln >> 4;
+        const int r = ln & 15, gg = ln >> 4;
         const int row = row0 + rt * 16 + r;
         u32x4_t v = {0u, 0u, 0u, 0u};
         if (row < a.M) {
-            const size_t k = (size_t)(sb0 + sbi) * 256 + 32 * j + 8 * g;
+            const size_t k = (size_t)(sb0 + sbi) * 256 + 32 * j + 8 * gg;
             v = *reinterpret_cast<const u32x4_t *>(a.A + (size_t)row * a.lda + k);
         }
         float s = 0.f;
@@ -88,74 +122,67 @@ __global__ __launch_bounds__(256) void k_q4k_gemm(Q4kGemmArgs a) {
         s += __shfl_xor(s, 16, WAVE);
         s += __shfl_xor(s, 32, WAVE);
         A_lds[e] = permute_slots(v);
-        if (g == 0) S_lds[((sbi * 8 + j) * rt_n + rt) * 16 + r] = s;
+        if (gg == 0) S_lds[((sbi * 8 + j) * rt_n + rt) * 16 + r] = s;
     }
     __syncthreads();
+    if (!active) return;
 
-    const int ct = blockIdx.x * 4 + wave;            // column tile of this wave
-    if (ct * 16 >= a.N) return;
-    const int n = ct * 16 + (lane & 15);
-    const int g = lane >> 4;
-    // weight segment of this column tile (segments are multiples of 16 columns)
-    int si = 0;
-    while (si + 1 < a.nseg && ct * 16 >= a.seg_end[si]) si++;
-    const int nloc = n - (si == 0 ? 0 : a.seg_end[si - 1]);
-    const unsigned char *wrow = a.w[si] + (size_t)nloc * a.KB * 144;
+    f32x4_t acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) acc[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    f32x4_t acc[MAX_RT];
+    for (int s0 = 0; s0 < nsb; s0 += PD) {
 #pragma unroll
-    for (int rt = 0; rt < MAX_RT; rt++) acc[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-
-    for (int sbi = 0; sbi < nsb; sbi++) {
-        const unsigned char *blk = wrow + (size_t)(sb0 + sbi) * 144;
-        const u32x4_t hdr = *reinterpret_cast<const u32x4_t *>(blk);
-        u32x2_t qd[4];
+        for (int u = 0; u < PD; u++) {
+            const int sbi = s0 + u;
+            const int nx = sbi + PD - 1;
+            if (nx < nsb) st[(u + PD - 1) % PD] = load_stage(wrow + (size_t)nx * 144, g);
+            if (sbi < nsb) {
+                const WStage &w = st[u];
+                const float d = half_bits_to_f32(w.hdr.x & 0xFFFF);
+                const float dmin = half_bits_to_f32(w.hdr.x >> 16);
+                const uint32_t s0w = w.hdr.y, s1w = w.hdr.z, s2w = w.hdr.w;
+                const uint32_t sc_lo = s0w & 0x3F3F3F3Fu;
+                const uint32_t m_lo = s1w & 0x3F3F3F3Fu;
+                const uint32_t sc_hi = (s2w & 0x0F0F0F0Fu) | ((s0w >> 2) & 0x30303030u);
+                const uint32_t m_hi = ((s2w >> 4) & 0x0F0F0F0Fu) | ((s1w >> 2) & 0x30303030u);
+                f32x4_t tacc[RT], bias[RT];
 #pragma unroll
-        for (int c = 0; c < 4; c++)
-            qd[c] = *reinterpret_cast<const u32x2_t *>(blk + 16 + 32 * c + 8 * g);
-        const float d = half_bits_to_f32(hdr.x & 0xFFFF);
-        const float dmin = half_bits_to_f32(hdr.x >> 16);
-        const uint32_t s0 = hdr.y, s1 = hdr.z, s2 = hdr.w;
-        const uint32_t sc_lo = s0 & 0x3F3F3F3Fu;
-        const uint32_t m_lo = s1 & 0x3F3F3F3Fu;
-        const uint32_t sc_hi = (s2 & 0x0F0F0F0Fu) | ((s0 >> 2) & 0x30303030u);
-        const uint32_t m_hi = ((s2 >> 4) & 0x0F0F0F0Fu) | ((s1 >> 2) & 0x30303030u);
-
-        f32x4_t tacc[MAX_RT], bias[MAX_RT];
-#pragma unroll
-        for (int rt = 0; rt < MAX_RT; rt++) {
-            tacc[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-            bias[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const uint32_t scw = j < 4 ? sc_lo : sc_hi;
-            const uint32_t mw = j < 4 ? m_lo : m_hi;
-            const float sc = (float)((scw >> (8 * (j & 3))) & 0xFF);
-            const float mm = (float)((mw >> (8 * (j & 3))) & 0xFF);
-            const float coef = 128.f * d * sc + dmin * mm;
-            uint32_t p0 = qd[j >> 1].x, p1 = qd[j >> 1].y;
-            if (j & 1) { p0 >>= 4; p1 >>= 4; }
-            const u32x4_t b = nibbles_to_bf16(p0, p1);
-#pragma unroll
-            for (int rt = 0; rt < MAX_RT; rt++) {
-                if (rt < rt_n) {
-                    const u32x4_t av = A_lds[((sbi * 8 + j) * rt_n + rt) * 64 + lane];
-                    const f32x4_t D = mfma16x16x32(av, b, (f32x4_t){0.f, 0.f, 0.f, 0.f});
-                    const f32x4_t S = *reinterpret_cast<const f32x4_t *>(
-                        &S_lds[((sbi * 8 + j) * rt_n + rt) * 16 + 4 * g]);
-                    tacc[rt] += sc * D;
-                    bias[rt] += coef * S;
+                for (int rt = 0; rt < RT; rt++) {
+                    tacc[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                    bias[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
                 }
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    const uint32_t scw = j < 4 ? sc_lo : sc_hi;
+                    const uint32_t mw = j < 4 ? m_lo : m_hi;
+                    const float sc = (float)((scw >> (8 * (j & 3))) & 0xFF);
+                    const float mm = (float)((mw >> (8 * (j & 3))) & 0xFF);
+                    const float coef = 128.f * d * sc + dmin * mm;
+                    uint32_t p0 = w.q[j >> 1].x, p1 = w.q[j >> 1].y;
+                    if (j & 1) { p0 >>= 4; p1 >>= 4; }
+                    const u32x4_t b = nibbles_to_bf16(p0, p1);
+#pragma unroll
+                    for (int rt = 0; rt < RT; rt++) {
+                        if (RT == 1 || rt < rt_n) {
+                            const u32x4_t av = A_lds[((sbi * 8 + j) * rt_n + rt) * 64 + lane];
+                            const f32x4_t D = mfma16x16x32(av, b, (f32x4_t){0.f, 0.f, 0.f, 0.f});
+                            const f32x4_t S = *reinterpret_cast<const f32x4_t *>(
+                                &S_lds[((sbi * 8 + j) * rt_n + rt) * 16 + 4 * g]);
+                            tacc[rt] += sc * D;
+                            bias[rt] += coef * S;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int rt = 0; rt < RT; rt++) acc[rt] += d * tacc[rt] - bias[rt];
             }
         }
-#pragma unroll
-        for (int rt = 0; rt < MAX_RT; rt++) acc[rt] += d * tacc[rt] - bias[rt];
     }
 
     float *out = a.part + (size_t)split * a.M * a.N;
 #pragma unroll
-    for (int rt = 0; rt < MAX_RT; rt++) {
+    for (int rt = 0; rt < RT; rt++) {
         if (rt < rt_n) {
 #pragma unroll
             for (int v = 0; v < 4; v++) {
@@ -200,24 +227,30 @@ Q4kPlan q4k_plan(int M, int N, int K) {
     Q4kPlan p;
     p.KB = K / 256;
     const int rt_total = ceil_div(M, 16);
-    p.row_groups = ceil_div(rt_total, MAX_RT);
-    const int rt = rt_total < MAX_RT ? rt_total : MAX_RT;
+    p.rt = rt_total <= 1 ? 1 : (rt_total <= 2 ? 2 : MAX_RT);
+    p.row_groups = ceil_div(rt_total, p.rt);
     const int tiles = N / 16;
-    int s_target = ceil_div(4096, tiles * p.row_groups);
+    // aim for ~8192 waves; at most 4 super-blocks x row tiles per workgroup in LDS
+    int s_target = ceil_div(8192, tiles * p.row_groups);
     if (s_target < 1) s_target = 1;
-    int kb_max = 7 / rt;
+    int kb_max = 4 / p.rt;
     if (kb_max < 1) kb_max = 1;
     int kb = ceil_div(p.KB, s_target);
     p.kb_per = kb < kb_max ? kb : kb_max;
     p.splits = ceil_div(p.KB, p.kb_per);
-    p.lds_bytes = (size_t)p.kb_per * 8 * rt * (64 * 16 + 16 * 4);
+    p.lds_bytes = (size_t)p.kb_per * 8 * p.rt * (64 * 16 + 16 * 4);
     p.grid_x = ceil_div(tiles, 4);
     return p;
 }
 
 hipError_t launch_q4k_gemm(const Q4kGemmArgs &a, const Q4kPlan &p, hipStream_t st) {
-    hipLaunchKernelGGL(k_q4k_gemm, dim3(p.grid_x, p.splits, p.row_groups), dim3(256),
-                       p.lds_bytes, st, a);
+    dim3 grid(p.grid_x, p.splits, p.row_groups);
+    if (p.rt == 1)
+        hipLaunchKernelGGL(k_q4k_gemm<1>, grid, dim3(256), p.lds_bytes, st, a);
+    else if (p.rt == 2)
+        hipLaunchKernelGGL(k_q4k_gemm<2>, grid, dim3(256), p.lds_bytes, st, a);
+    else
+        hipLaunchKernelGGL(k_q4k_gemm<MAX_RT>, grid, dim3(256), p.lds_bytes, st, a);
     return hipGetLastError();
 }
 
