@@ -106,63 +106,65 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_tiled(Bf16GemmArgs a) {
 constexpr int LM_PD = 8;
 
 __global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a, int tiles_per_wave) {
-    extern __shared__ __align__(16) u32x4_t Alds[];        // [nks][32]: lanes with row < 8
+    extern __shared__ __align__(16) u32x4_t Alds[];   // [nks][32] lanes with row < 8, + 1 zero entry
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
-    const int nks = a.K / 32;
+    const int nks = a.K / 32;                        // a multiple of LM_PD
     const int ntiles = a.N / 16;
     const int t0 = (blockIdx.x * 4 + wave) * tiles_per_wave;
     const int t1 = min(t0 + tiles_per_wave, ntiles);
     const int steps = t1 > t0 ? (t1 - t0) * nks : 0;
 
-    // first weight fragments before the activations are staged
-    u32x4_t eb[LM_PD];
-    int lt = t0, lk = 0;                 // tile / k-step of the next fragment to load
-    auto wptr = [&](int tile, int ks) {
-        return seg_row(a, tile * 16 + c) + ks * 32 + 8 * g;
+    // flat stream of fragments (tile, k-step); loads past the wave's range are
+    // clamped to its last fragment (in bounds, value unused)
+    const uint16_t *W = a.w[0] + (size_t)c * a.K + 8 * g;
+    const size_t tile_stride = (size_t)16 * a.K;
+    int lt = t0, lk = 0, nload = 0;
+    auto load_next = [&]() -> u32x4_t {
+        const bool ok = nload < steps;
+        const int tt = ok ? lt : t1 - 1, kk = ok ? lk : nks - 1;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(W + (size_t)tt * tile_stride + kk * 32);
+        nload++;
+        lk++;
+        const bool wrap = lk == nks;
+        lk = wrap ? 0 : lk;
+        lt += wrap ? 1 : 0;
+        return v;
     };
+    u32x4_t eb[LM_PD];
+    if (steps > 0) {
 #pragma unroll
-    for (int u = 0; u < LM_PD - 1; u++) {
-        if (u < steps) {
-            eb[u] = *reinterpret_cast<const u32x4_t *>(wptr(lt, lk));
-            if (++lk == nks) { lk = 0; lt++; }
-        }
+        for (int u = 0; u < LM_PD - 1; u++) eb[u] = load_next();
     }
-    for (int e = tid; e < nks * 32; e += 256) {
+    for (int e = tid; e < nks * 32 + 1; e += 256) {
         const int ks = e >> 5, slot = e & 31, gg = slot >> 3, r = slot & 7;
         u32x4_t v = {0, 0, 0, 0};
-        if (r < a.M) v = *reinterpret_cast<const u32x4_t *>(a.A + (size_t)r * a.lda + ks * 32 + 8 * gg);
+        if (e < nks * 32 && r < a.M)
+            v = *reinterpret_cast<const u32x4_t *>(a.A + (size_t)r * a.lda + ks * 32 + 8 * gg);
         Alds[e] = v;
     }
     __syncthreads();
 
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    int ct = t0, ck = 0;                 // tile / k-step being computed
-    for (int s0 = 0; s0 < steps; s0 += LM_PD) {
+    // lanes of rows >= 8 read the zero entry
+    const int aoff = c < 8 ? g * 8 + c : 0;
+    const int astep = c < 8 ? 32 : 0;
+    const int abase = c < 8 ? 0 : nks * 32;
+    for (int tile = t0; tile < t1; tile++) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int ks0 = 0; ks0 < nks; ks0 += LM_PD) {
 #pragma unroll
-        for (int u = 0; u < LM_PD; u++) {
-            const int i = s0 + u;
-            if (i + LM_PD - 1 < steps) {
-                eb[(u + LM_PD - 1) % LM_PD] = *reinterpret_cast<const u32x4_t *>(wptr(lt, lk));
-                if (++lk == nks) { lk = 0; lt++; }
-            }
-            if (i < steps) {
-                u32x4_t af = {0, 0, 0, 0};
-                if (c < 8) af = Alds[ck * 32 + g * 8 + c];
+            for (int u = 0; u < LM_PD; u++) {
+                eb[(u + LM_PD - 1) % LM_PD] = load_next();
+                const u32x4_t af = Alds[abase + (ks0 + u) * astep + aoff];
                 acc = mfma16x16x32(af, eb[u], acc);
-                if (++ck == nks) {
-                    const int n = ct * 16 + c;
-                    if (g < 2) {
+            }
+        }
+        if (g < 2) {
+            const int n = tile * 16 + c;
 #pragma unroll
-                        for (int v = 0; v < 4; v++) {
-                            const int m = 4 * g + v;
-                            if (m < a.M) a.C[(size_t)m * a.ldc + n] = acc[v];
-                        }
-                    }
-                    acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-                    ck = 0;
-                    ct++;
-                }
+            for (int v = 0; v < 4; v++) {
+                const int m = 4 * g + v;
+                if (m < a.M) a.C[(size_t)m * a.ldc + n] = acc[v];
             }
         }
     }
@@ -180,7 +182,7 @@ hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st) {
     const int ntiles = a.N / 16;
     const int tpw = ceil_div(ntiles, 2048);               // ~2048 waves, 2 workgroups per CU
     const int waves = ceil_div(ntiles, tpw);
-    const size_t lds = (size_t)(a.K / 32) * 32 * 16;
+    const size_t lds = ((size_t)(a.K / 32) * 32 + 1) * 16;
     static size_t lds_set = 0;
     if (lds > 65536 && lds > lds_set) {
         hipError_t e = hipFuncSetAttribute((const void *)k_bf16_gemm_skinny,

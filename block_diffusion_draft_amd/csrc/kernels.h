@@ -36,7 +36,8 @@ struct Bf16GemmArgs {
 };
 // tiled 128x128 MFMA GEMM, any M
 hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st);
-// rows <= 8: activations resident in LDS, every wave streams whole weight tiles
+// rows <= 8, one weight matrix (nseg == 1): activations resident in LDS, every wave
+// streams whole weight tiles
 hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------- layer ops

@@ -68,6 +68,7 @@ __device__ __forceinline__ WStage load_stage(const unsigned char *blk, int g) {
 }
 
 constexpr int PD = 4;              // super-blocks in flight per wave
+constexpr int KB_LDS = 4;          // super-blocks x row tiles staged per workgroup
 
 template <int RT>
 __global__ __launch_bounds__(256) void k_q4k_gemm(Q4kGemmArgs a) {
@@ -77,55 +78,71 @@ __global__ __launch_bounds__(256) void k_q4k_gemm(Q4kGemmArgs a) {
     const int row0 = blockIdx.z * (RT * 16);
     const int rt_n = min(RT, ceil_div(a.M - row0, 16));
     const int sb0 = split * a.kb_per;
-    const int nsb = min(a.kb_per, a.KB - sb0);
-    if (nsb <= 0) return;                                   // uniform over the workgroup
+    const int nsb = min(a.kb_per, a.KB - sb0);        // >= 1 by construction of the grid
 
-    const int ct = blockIdx.x * 4 + wave;            // column tile of this wave
-    const bool active = ct * 16 < a.N;
-    const int n = ct * 16 + (lane & 15);
+    // column tile of this wave; a tile past N (last workgroup only) computes on
+    // the last valid tile and stores nothing
+    const int ntile = a.N / 16;
+    const int ct = blockIdx.x * 4 + wave;
+    const bool active = ct < ntile;
+    const int cte = active ? ct : ntile - 1;
+    const int c16 = cte * 16;
+    const int n = c16 + (lane & 15);
     const int g = lane >> 4;
-    // weight segment of this column tile (segments are multiples of 16 columns)
-    int si = 0;
-    while (si + 1 < a.nseg && ct * 16 >= a.seg_end[si]) si++;
-    const int nloc = n - (si == 0 ? 0 : a.seg_end[si - 1]);
-    const unsigned char *wrow = a.w[si] + ((size_t)nloc * a.KB + sb0) * 144;
+    // weight segment (segments are multiples of 16 columns); no dynamic indexing
+    const int si = (a.nseg > 1 && c16 >= a.seg_end[0]) + (a.nseg > 2 && c16 >= a.seg_end[1]);
+    const unsigned char *wseg = si == 0 ? a.w[0] : (si == 1 ? a.w[1] : a.w[2]);
+    const int nbase = si == 0 ? 0 : (si == 1 ? a.seg_end[0] : a.seg_end[1]);
+    const unsigned char *wrow = wseg + ((size_t)(n - nbase) * a.KB + sb0) * 144;
+    auto blk = [&](int i) { return wrow + (size_t)min(i, nsb - 1) * 144; };
 
-    // start streaming weights before the activations are staged
-    WStage st[PD];
-#pragma unroll
-    for (int u = 0; u < PD - 1; u++)
-        if (active && u < nsb) st[u] = load_stage(wrow + (size_t)u * 144, g);
-
-    u32x4_t *A_lds = reinterpret_cast<u32x4_t *>(lds);      // [nsb][8][rt_n][64]
-    float *S_lds = reinterpret_cast<float *>(lds + (size_t)nsb * 8 * rt_n * 64 * 16);  // [nsb][8][rt_n*16]
-
-    // ---- stage activations (rows row0.., super-blocks sb0..) in lane order
+    // 1) activation loads for the LDS stage (at most 8 per thread)
+    constexpr int MAXA = 2 * KB_LDS;
     const int entries = nsb * 8 * rt_n * 64;
-    for (int e = tid; e < entries; e += 256) {
+    // branch-free: indices are clamped into range and out-of-range values zeroed
+    u32x4_t av[MAXA];
+#pragma unroll
+    for (int i = 0; i < MAXA; i++) {
+        const int e = min(tid + 256 * i, entries - 1);
         const int ln = e & 63;
         int rest = e >> 6;
         const int rt = rest % rt_n; rest /= rt_n;
-        const int j = rest & 7;
-        const int sbi = rest >> 3;
-        const int r = ln & 15, gg = ln >> 4;
-        const int row = row0 + rt * 16 + r;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (row < a.M) {
-            const size_t k = (size_t)(sb0 + sbi) * 256 + 32 * j + 8 * gg;
-            v = *reinterpret_cast<const u32x4_t *>(a.A + (size_t)row * a.lda + k);
+        const int j = rest & 7, sbi = rest >> 3;
+        const int row = row0 + rt * 16 + (ln & 15);
+        const size_t k = (size_t)(sb0 + sbi) * 256 + 32 * j + 8 * (ln >> 4);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(a.A + (size_t)min(row, a.M - 1) * a.lda + k);
+        const bool ok = row < a.M && tid + 256 * i < entries;
+        av[i] = ok ? v : (u32x4_t){0u, 0u, 0u, 0u};
+    }
+    // 2) weight stream starts before the stage completes
+    WStage st[PD];
+#pragma unroll
+    for (int u = 0; u < PD - 1; u++) st[u] = load_stage(blk(u), g);
+
+    // 3) activations -> LDS in MFMA lane order, with per-sub-block row sums
+    u32x4_t *A_lds = reinterpret_cast<u32x4_t *>(lds);      // [nsb][8][rt_n][64]
+    float *S_lds = reinterpret_cast<float *>(lds + (size_t)nsb * 8 * rt_n * 64 * 16);  // [nsb][8][rt_n*16]
+#pragma unroll
+    for (int i = 0; i < MAXA; i++) {
+        const int e = tid + 256 * i;
+        if (e < entries) {                               // uniform per wave
+            const u32x4_t v = av[i];
+            const int ln = e & 63;
+            int rest = e >> 6;
+            const int rt = rest % rt_n; rest /= rt_n;
+            const int j = rest & 7, sbi = rest >> 3;
+            float s = 0.f;
+            s += bf16_to_f32(v.x & 0xFFFF) + bf16_to_f32(v.x >> 16);
+            s += bf16_to_f32(v.y & 0xFFFF) + bf16_to_f32(v.y >> 16);
+            s += bf16_to_f32(v.z & 0xFFFF) + bf16_to_f32(v.z >> 16);
+            s += bf16_to_f32(v.w & 0xFFFF) + bf16_to_f32(v.w >> 16);
+            s += __shfl_xor(s, 16, WAVE);
+            s += __shfl_xor(s, 32, WAVE);
+            A_lds[e] = permute_slots(v);
+            if ((ln >> 4) == 0) S_lds[((sbi * 8 + j) * rt_n + rt) * 16 + (ln & 15)] = s;
         }
-        float s = 0.f;
-        s += bf16_to_f32(v.x & 0xFFFF) + bf16_to_f32(v.x >> 16);
-        s += bf16_to_f32(v.y & 0xFFFF) + bf16_to_f32(v.y >> 16);
-        s += bf16_to_f32(v.z & 0xFFFF) + bf16_to_f32(v.z >> 16);
-        s += bf16_to_f32(v.w & 0xFFFF) + bf16_to_f32(v.w >> 16);
-        s += __shfl_xor(s, 16, WAVE);
-        s += __shfl_xor(s, 32, WAVE);
-        A_lds[e] = permute_slots(v);
-        if (gg == 0) S_lds[((sbi * 8 + j) * rt_n + rt) * 16 + r] = s;
     }
     __syncthreads();
-    if (!active) return;
 
     f32x4_t acc[RT];
 #pragma unroll
@@ -135,51 +152,51 @@ __global__ __launch_bounds__(256) void k_q4k_gemm(Q4kGemmArgs a) {
 #pragma unroll
         for (int u = 0; u < PD; u++) {
             const int sbi = s0 + u;
-            const int nx = sbi + PD - 1;
-            if (nx < nsb) st[(u + PD - 1) % PD] = load_stage(wrow + (size_t)nx * 144, g);
-            if (sbi < nsb) {
-                const WStage &w = st[u];
-                const float d = half_bits_to_f32(w.hdr.x & 0xFFFF);
-                const float dmin = half_bits_to_f32(w.hdr.x >> 16);
-                const uint32_t s0w = w.hdr.y, s1w = w.hdr.z, s2w = w.hdr.w;
-                const uint32_t sc_lo = s0w & 0x3F3F3F3Fu;
-                const uint32_t m_lo = s1w & 0x3F3F3F3Fu;
-                const uint32_t sc_hi = (s2w & 0x0F0F0F0Fu) | ((s0w >> 2) & 0x30303030u);
-                const uint32_t m_hi = ((s2w >> 4) & 0x0F0F0F0Fu) | ((s1w >> 2) & 0x30303030u);
-                f32x4_t tacc[RT], bias[RT];
+            st[(u + PD - 1) % PD] = load_stage(blk(sbi + PD - 1), g);
+            const bool live = sbi < nsb;
+            const int sbl = live ? sbi : 0;              // stays inside the LDS stage
+            const WStage &w = st[u];
+            const float d = half_bits_to_f32(w.hdr.x & 0xFFFF);
+            const float dmin = half_bits_to_f32(w.hdr.x >> 16);
+            const uint32_t s0w = w.hdr.y, s1w = w.hdr.z, s2w = w.hdr.w;
+            const uint32_t sc_lo = s0w & 0x3F3F3F3Fu;
+            const uint32_t m_lo = s1w & 0x3F3F3F3Fu;
+            const uint32_t sc_hi = (s2w & 0x0F0F0F0Fu) | ((s0w >> 2) & 0x30303030u);
+            const uint32_t m_hi = ((s2w >> 4) & 0x0F0F0F0Fu) | ((s1w >> 2) & 0x30303030u);
+            f32x4_t tacc[RT], bias[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; rt++) {
+                tacc[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                bias[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const uint32_t scw = j < 4 ? sc_lo : sc_hi;
+                const uint32_t mw = j < 4 ? m_lo : m_hi;
+                const float sc = (float)((scw >> (8 * (j & 3))) & 0xFF);
+                const float mm = (float)((mw >> (8 * (j & 3))) & 0xFF);
+                const float coef = 128.f * d * sc + dmin * mm;
+                uint32_t p0 = w.q[j >> 1].x, p1 = w.q[j >> 1].y;
+                if (j & 1) { p0 >>= 4; p1 >>= 4; }
+                const u32x4_t b = nibbles_to_bf16(p0, p1);
 #pragma unroll
                 for (int rt = 0; rt < RT; rt++) {
-                    tacc[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-                    bias[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                    const int rtl = rt < rt_n ? rt : 0;
+                    const u32x4_t av2 = A_lds[((sbl * 8 + j) * rt_n + rtl) * 64 + lane];
+                    const f32x4_t D = mfma16x16x32(av2, b, (f32x4_t){0.f, 0.f, 0.f, 0.f});
+                    const f32x4_t S = *reinterpret_cast<const f32x4_t *>(
+                        &S_lds[((sbl * 8 + j) * rt_n + rtl) * 16 + 4 * g]);
+                    tacc[rt] += sc * D;
+                    bias[rt] += coef * S;
                 }
-#pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    const uint32_t scw = j < 4 ? sc_lo : sc_hi;
-                    const uint32_t mw = j < 4 ? m_lo : m_hi;
-                    const float sc = (float)((scw >> (8 * (j & 3))) & 0xFF);
-                    const float mm = (float)((mw >> (8 * (j & 3))) & 0xFF);
-                    const float coef = 128.f * d * sc + dmin * mm;
-                    uint32_t p0 = w.q[j >> 1].x, p1 = w.q[j >> 1].y;
-                    if (j & 1) { p0 >>= 4; p1 >>= 4; }
-                    const u32x4_t b = nibbles_to_bf16(p0, p1);
-#pragma unroll
-                    for (int rt = 0; rt < RT; rt++) {
-                        if (RT == 1 || rt < rt_n) {
-                            const u32x4_t av = A_lds[((sbi * 8 + j) * rt_n + rt) * 64 + lane];
-                            const f32x4_t D = mfma16x16x32(av, b, (f32x4_t){0.f, 0.f, 0.f, 0.f});
-                            const f32x4_t S = *reinterpret_cast<const f32x4_t *>(
-                                &S_lds[((sbi * 8 + j) * rt_n + rt) * 16 + 4 * g]);
-                            tacc[rt] += sc * D;
-                            bias[rt] += coef * S;
-                        }
-                    }
-                }
-#pragma unroll
-                for (int rt = 0; rt < RT; rt++) acc[rt] += d * tacc[rt] - bias[rt];
             }
+            const float on = live ? 1.f : 0.f;
+#pragma unroll
+            for (int rt = 0; rt < RT; rt++) acc[rt] += on * (d * tacc[rt] - bias[rt]);
         }
     }
 
+    if (!active) return;
     float *out = a.part + (size_t)split * a.M * a.N;
 #pragma unroll
     for (int rt = 0; rt < RT; rt++) {
@@ -233,7 +250,7 @@ Q4kPlan q4k_plan(int M, int N, int K) {
     // aim for ~8192 waves; at most 4 super-blocks x row tiles per workgroup in LDS
     int s_target = ceil_div(8192, tiles * p.row_groups);
     if (s_target < 1) s_target = 1;
-    int kb_max = 4 / p.rt;
+    int kb_max = KB_LDS / p.rt;
     if (kb_max < 1) kb_max = 1;
     int kb = ceil_div(p.KB, s_target);
     p.kb_per = kb < kb_max ? kb : kb_max;
