@@ -33,6 +33,15 @@ struct Bf16GemmArgs {
     int M, N, K;
     float *C;                    // fp32 [M][ldc]
     int ldc;
+    // skinny kernel only: a_norm != 0 stages A row r as bf16(RMSNorm(af[src(r)]) * again),
+    // src(r) = (r / aper) * agroup + aoff + r % aper, with the row's sum of squares taken
+    // from assq[src(r)][0 .. an_groups)
+    int a_norm;
+    const float *af;
+    const uint16_t *again;
+    const float *assq;
+    int an_groups, aper, agroup, aoff;
+    float aeps;
 };
 // tiled 128x128 MFMA GEMM, any M
 hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st);
@@ -48,10 +57,12 @@ hipError_t launch_reduce_epilogue(const float *part, int splits, int M, int N, i
                                   int mode, float *out_f32, uint16_t *out_bf16,
                                   uint16_t *out_bf16_lo, int ldo, hipStream_t st);
 
-// per-sequence validity flags + block assembly h[b][0] = E[last], h[b][1..] = mask
+// per-sequence validity flags + block assembly h[b][0] = E[last], h[b][1..] = mask, with
+// each row's sum of squares (ssq[row]); also zeroes n_counters fixup counters
 hipError_t launch_embed(const uint16_t *embed, const uint16_t *mask_emb, const int32_t *last,
                         const int32_t *ctx_len, int B, int T, int H, int V, int t_new, int cap,
-                        float *h, int32_t *valid, hipStream_t st);
+                        float *h, float *ssq, int32_t *valid, int *counters, int n_counters,
+                        hipStream_t st);
 
 // out[r] = bf16(RMSNorm(in[row(r)]) * g), row(r) = (r / per) * in_group + in_off + r % per;
 // out_lo (nullable) receives the bf16 residual of each value
@@ -107,3 +118,46 @@ hipError_t launch_viterbi(const int32_t *cand_ids, const float *cand_logp, const
                           const int32_t *valid, int32_t *draft_tokens, hipStream_t st);
 hipError_t launch_verify(const int32_t *draft, const int32_t *target, int B, int n,
                          int32_t *accept_len, int32_t *out_tokens, hipStream_t st);
+
+// ---------------------------------------------------------------- fused Q4_K GEMM
+// Activation source of a fused Q4_K GEMM: bf16 rows A[r][lda] (r < M).
+struct Q4kSrc {
+    const uint16_t *A;
+    int lda;
+};
+// Epilogue applied by the last workgroup of each column group.
+struct Q4kOut {
+    int mode;                    // EpiMode
+    float *f;                    // STORE_F32 / ADD_F32 target [M_out][ldo]
+    uint16_t *b, *b_lo;          // bf16 targets (SWIGLU hi/lo, STORE_BF16)
+    int ldo;
+    float *ssq;                  // nullable: [M_out][n_groups] sums of squares of stored rows
+    int pair;                    // output row r = GEMM rows r + (r + pair)
+    int M_out;
+};
+struct Q4kFusedArgs {
+    const unsigned char *w[3];
+    int seg_end[3];
+    int nseg;
+    int M, N, KB;                // GEMM rows (2 M_out with hilo), columns, K/256
+    int paired;                  // SWIGLU: workgroup pairs gate tiles with the matching up tiles
+    Q4kSrc src;
+    Q4kOut out;
+    float *part;                 // [splits][M][N]
+    int *counters;               // [grid_x], zero on entry, left zero
+};
+struct Q4kFusedPlan {
+    int rt, nsb, ct, steps, splits, row_groups, grid_x;
+    size_t lds_bytes, part_bytes;
+};
+Q4kFusedPlan q4k_fused_plan(int M, int N, int K, int paired);
+hipError_t launch_q4k_fused(const Q4kFusedArgs &a, const Q4kFusedPlan &p, hipStream_t st);
+// zero n ints (workspace counters) with a kernel
+hipError_t launch_zero_i32(int *p, int n, hipStream_t st);
+
+// out rows r < R: bf16(RMSNorm(in[src(r)]) * gain), src(r) = (r / per) * in_group + in_off
+// + r % per, the row's sum of squares read from ssq[src(r)][0 .. n_groups); with out_lo
+// the bf16 residual of each value goes to out_lo (same layout)
+hipError_t launch_rownorm(const float *in, const float *ssq, int n_groups, int R, int H, int per,
+                          int in_group, int in_off, const uint16_t *gain, float eps, uint16_t *out,
+                          uint16_t *out_lo, int ldo, hipStream_t st);

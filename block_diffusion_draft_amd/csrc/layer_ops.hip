@@ -21,17 +21,31 @@ __device__ __forceinline__ float block_sum_256(float v, float *scratch) {
 }
 
 // ---------------------------------------------------------------- block assembly
+// h[b][0] = E[last token], h[b][1..] = mask embedding; the row's sum of squares for
+// the first layer's fused normalisation; workgroup 0 also clears the GEMM fixup
+// counters of the step.
 __global__ __launch_bounds__(256) void k_embed(const uint16_t *embed, const uint16_t *mask,
                                                const int32_t *last, const int32_t *ctx_len,
                                                int T, int H, int V, int t_new, int cap,
-                                               float *h, int32_t *valid) {
+                                               float *h, float *ssq, int32_t *valid,
+                                               int *counters, int n_counters) {
+    __shared__ float scratch[4];
     const int b = blockIdx.x / T, t = blockIdx.x % T;
     const int n = ctx_len[b], tok = last[b];
     const bool ok = n >= 0 && n <= cap - t_new && tok >= 0 && tok < V;
     if (t == 0 && threadIdx.x == 0) valid[b] = ok ? 1 : 0;
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < n_counters; i += 256) counters[i] = 0;
     float *row = h + (size_t)blockIdx.x * H;
     const uint16_t *src = t == 0 ? embed + (size_t)(ok ? tok : 0) * H : mask;
-    for (int i = threadIdx.x; i < H; i += 256) row[i] = ok ? bf16_to_f32(src[i]) : 0.f;
+    float s = 0.f;
+    for (int i = threadIdx.x; i < H; i += 256) {
+        const float v = ok ? bf16_to_f32(src[i]) : 0.f;
+        row[i] = v;
+        s += v * v;
+    }
+    s = block_sum_256(s, scratch);
+    if (threadIdx.x == 0) ssq[blockIdx.x] = s;
 }
 
 // ---------------------------------------------------------------- RMSNorm -> bf16
@@ -54,6 +68,42 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *in, int H, int per
         const uint16_t hb = f32_to_bf16(v);
         o[i] = hb;
         if (ol) ol[i] = f32_to_bf16(v - bf16_to_f32(hb));
+    }
+}
+
+// ---------------------------------------------------------------- RMSNorm from sums of squares
+// Workgroup (row r, 1024-column chunk): the row's sum of squares is the sum of the
+// producer's per-column-group partials (fixed order), the chunk is scaled by the
+// gain and written as bf16, and optionally its bf16 residual.
+__global__ __launch_bounds__(256) void k_rownorm(const float *in, const float *ssq, int n_groups,
+                                                 int H, int per, int in_group, int in_off,
+                                                 const uint16_t *gain, float eps, uint16_t *out,
+                                                 uint16_t *out_lo, int ldo) {
+    __shared__ float inv_s;
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int src = (r / per) * in_group + in_off + r % per;
+    if (tid < 64) {
+        float s = 0.f;
+        for (int i = tid; i < n_groups; i += 64) s += ssq[(size_t)src * n_groups + i];
+        s = wave_sum(s);
+        if (tid == 0) inv_s = rsqrtf(s / (float)H + eps);
+    }
+    __syncthreads();
+    const float inv = inv_s;
+    const int k = blockIdx.y * 1024 + tid * 4;
+    if (k >= H) return;
+    const f32x4_t x = *reinterpret_cast<const f32x4_t *>(in + (size_t)src * H + k);
+    const uint32_t g01 = *reinterpret_cast<const uint32_t *>(gain + k);
+    const uint32_t g23 = *reinterpret_cast<const uint32_t *>(gain + k + 2);
+    const float v0 = x.x * inv * bf16_to_f32(g01 & 0xFFFF), v1 = x.y * inv * bf16_to_f32(g01 >> 16);
+    const float v2 = x.z * inv * bf16_to_f32(g23 & 0xFFFF), v3 = x.w * inv * bf16_to_f32(g23 >> 16);
+    const uint32_t h01 = pack_bf16x2(v0, v1), h23 = pack_bf16x2(v2, v3);
+    u32x2_t hv = {h01, h23};
+    *reinterpret_cast<u32x2_t *>(out + (size_t)r * ldo + k) = hv;
+    if (out_lo) {
+        u32x2_t lv = {pack_bf16x2(v0 - bf16_to_f32(h01 & 0xFFFF), v1 - bf16_to_f32(h01 >> 16)),
+                      pack_bf16x2(v2 - bf16_to_f32(h23 & 0xFFFF), v3 - bf16_to_f32(h23 >> 16))};
+        *reinterpret_cast<u32x2_t *>(out_lo + (size_t)r * ldo + k) = lv;
     }
 }
 
@@ -160,7 +210,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
     const int nq2 = 2 * a.n_q;
     extern __shared__ float sm[];
     float *o = sm;                      // [T][d]
-    float *w = sm + T * d;              // [T][nch1]
+    float *w = sm + T * d;              // [T][nch1] merge weights
+    float *mx = w + T * nch1;           // [T]
     if (!a.valid[b]) {
         for (int e = tid; e < T * d; e += 256) a.o[((size_t)b * T + e / d) * qd + h * d + e % d] = 0.f;
         for (int e = tid; e < T * nq2; e += 256) a.zp[(((size_t)b * a.n_q + h) * T) * nq2 + e] = 0.f;
@@ -171,32 +222,53 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
     const int lo = hi - a.window > 0 ? hi - a.window : 0;
     const int nch_b = ceil_div(hi - lo, a.chunk);
     const float *ml = a.ml + ((size_t)(b * a.n_kv + kvh) * nch1) * QR * 2;
+    // all (row, chunk) statistics are loaded in parallel
+    for (int e = tid; e < T * nch1; e += 256) {
+        const int t = e / nch1, c = e % nch1;
+        const bool used = c < nch_b || c == a.n_chunks;
+        w[e] = used ? ml[((size_t)c * QR + hq * T + t) * 2] : -INFINITY;
+    }
+    __syncthreads();
     if (tid < T) {
-        const int row = hq * T + tid;
         float M = -INFINITY;
-        for (int c = 0; c < nch1; c++)
-            if (c < nch_b || c == a.n_chunks) M = fmaxf(M, ml[((size_t)c * QR + row) * 2]);
+        for (int c = 0; c < nch1; c++) M = fmaxf(M, w[tid * nch1 + c]);
+        mx[tid] = M;
+    }
+    __syncthreads();
+    for (int e = tid; e < T * nch1; e += 256) {
+        const int t = e / nch1, c = e % nch1;
+        const float m = w[e];
+        w[e] = m == -INFINITY ? 0.f : expf(m - mx[t]) * ml[((size_t)c * QR + hq * T + t) * 2 + 1];
+    }
+    __syncthreads();
+    if (tid < T) {
         float L = 0.f;
-        for (int c = 0; c < nch1; c++) {
-            float e = 0.f;
-            if (c < nch_b || c == a.n_chunks) {
-                e = expf(ml[((size_t)c * QR + row) * 2] - M);
-                L += e * ml[((size_t)c * QR + row) * 2 + 1];
-            }
-            w[tid * nch1 + c] = e;
-        }
-        const float inv = 1.f / L;
-        for (int c = 0; c < nch1; c++) w[tid * nch1 + c] *= inv;
+        for (int c = 0; c < nch1; c++) L += w[tid * nch1 + c];
+        mx[tid] = 1.f / L;
+    }
+    __syncthreads();
+    // weights exp(m_c - M) / L multiply the unnormalised partials (l_c already folded in
+    // the sum above, so divide it back out per chunk)
+    for (int e = tid; e < T * nch1; e += 256) {
+        const int t = e / nch1, c = e % nch1;
+        const float lc = ml[((size_t)c * QR + hq * T + t) * 2 + 1];
+        w[e] = w[e] == 0.f ? 0.f : w[e] / lc * mx[t];
     }
     __syncthreads();
     const float *O = a.O + ((size_t)(b * a.n_kv + kvh) * nch1) * QR * d;
     for (int e = tid; e < T * d; e += 256) {
         const int t = e / d, col = e % d, row = hq * T + t;
-        float acc = 0.f;
-        for (int c = 0; c < nch1; c++) {
-            const float wc = w[t * nch1 + c];
-            if (wc != 0.f) acc += wc * O[((size_t)c * QR + row) * d + col];
+        const float *wt = w + t * nch1;
+        float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+        int c = 0;
+        for (; c + 4 <= nch1; c += 4) {
+            acc0 += wt[c] * O[((size_t)c * QR + row) * d + col];
+            acc1 += wt[c + 1] * O[((size_t)(c + 1) * QR + row) * d + col];
+            acc2 += wt[c + 2] * O[((size_t)(c + 2) * QR + row) * d + col];
+            acc3 += wt[c + 3] * O[((size_t)(c + 3) * QR + row) * d + col];
         }
+        for (; c < nch1; c++) acc0 += wt[c] * O[((size_t)c * QR + row) * d + col];
+        const float acc = (acc0 + acc1) + (acc2 + acc3);
         o[e] = acc;
         a.o[((size_t)b * T + t) * qd + h * d + col] = acc;
     }
@@ -220,15 +292,21 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
 // k_conv_apply: one workgroup per (sequence, block row t):
 //   z_t = sum_h zp[b][h][t];  y_{t,h} = z_t[h] o_{t,h} + z_t[n_q + h] o_{t-1,h},  o_{-1} = 0.
 __global__ __launch_bounds__(256) void k_conv_apply(MergeConvArgs a) {
+    __shared__ float zpart[256];
     __shared__ float z[2 * 256];
     const int b = blockIdx.x / a.T, t = blockIdx.x % a.T, tid = threadIdx.x;
     const int qd = a.n_q * a.d, nq2 = 2 * a.n_q;
-    for (int q = tid; q < nq2; q += 256) {
+    // z_t[q] = sum over heads of zp[b][h][t][q]: (q, head-quarter) per thread
+    for (int q0 = 0; q0 < nq2; q0 += 64) {
+        const int q = q0 + (tid & 63), part = tid >> 6;
         float s = 0.f;
-        for (int h = 0; h < a.n_q; h++) s += a.zp[(((size_t)b * a.n_q + h) * a.T + t) * nq2 + q];
-        z[q] = s;
+        if (q < nq2)
+            for (int h = part; h < a.n_q; h += 4) s += a.zp[(((size_t)b * a.n_q + h) * a.T + t) * nq2 + q];
+        zpart[tid] = s;
+        __syncthreads();
+        if (tid < 64 && q0 + tid < nq2) z[q0 + tid] = (zpart[tid] + zpart[tid + 64]) + (zpart[tid + 128] + zpart[tid + 192]);
+        __syncthreads();
     }
-    __syncthreads();
     const float *ot = a.o + ((size_t)b * a.T + t) * qd;
     const float *op = ot - qd;
     uint16_t *Y = a.Y + ((size_t)b * a.T + t) * qd;
@@ -243,9 +321,10 @@ __global__ __launch_bounds__(256) void k_conv_apply(MergeConvArgs a) {
 
 hipError_t launch_embed(const uint16_t *embed, const uint16_t *mask_emb, const int32_t *last,
                         const int32_t *ctx_len, int B, int T, int H, int V, int t_new, int cap,
-                        float *h, int32_t *valid, hipStream_t st) {
-    hipLaunchKernelGGL(k_embed, dim3(B * T), dim3(256), 0, st, embed, mask_emb, last, ctx_len,
-                       T, H, V, t_new, cap, h, valid);
+                        float *h, float *ssq, int32_t *valid, int *counters, int n_counters,
+                        hipStream_t st) {
+    hipLaunchKernelGGL(k_embed, dim3(B * T), dim3(256), 0, st, embed, mask_emb, last, ctx_len, T, H,
+                       V, t_new, cap, h, ssq, valid, counters, n_counters);
     return hipGetLastError();
 }
 
@@ -275,10 +354,19 @@ hipError_t launch_qk_norm_rope(const RopeArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st) {
-    const size_t lds = (size_t)(a.T * a.d + a.T * (a.n_chunks + 1)) * 4;
+    const size_t lds = (size_t)(a.T * a.d + a.T * (a.n_chunks + 1) + a.T) * 4;
     hipLaunchKernelGGL(k_attn_merge, dim3(a.n_q, a.B), dim3(256), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_conv_apply, dim3(a.B * a.T), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_rownorm(const float *in, const float *ssq, int n_groups, int R, int H, int per,
+                          int in_group, int in_off, const uint16_t *gain, float eps, uint16_t *out,
+                          uint16_t *out_lo, int ldo, hipStream_t st) {
+    dim3 grid(R, ceil_div(H, 1024));
+    hipLaunchKernelGGL(k_rownorm, grid, dim3(256), 0, st, in, ssq, n_groups, H, per, in_group,
+                       in_off, gain, eps, out, out_lo, ldo);
     return hipGetLastError();
 }

@@ -8,10 +8,6 @@
 // chosen candidates u (earlier) and v (later), maximised by Viterbi; ties go to
 // the lowest candidate index.
 //
-// One workgroup per sequence: the codebook rows of each adjacent position pair
-// are gathered into LDS, the K x K pair scores are dot products of r bf16 values
-// in fp32, and the dynamic programme runs on K threads.
-//
 // Acceptance (same card, "How it is used" and "FastFlowLM measurements"): the
 // longest drafted prefix equal to the target's greedy tokens, plus one target
 // token.
@@ -22,75 +18,82 @@ namespace {
 
 constexpr int MAXK = 16;
 constexpr int MAXP = 16;
-constexpr int MAXR = 512;
 
+// One workgroup per sequence.  The pair scores of adjacent positions are K x K
+// products of gathered codebook rows, T_t = s A[ids_t] B[ids_{t+1}]^T, computed as
+// 16x16xr MFMA tiles (exact bf16 products, fp32 accumulation) straight from the
+// gathered rows: lane (i, k-group) loads its 16-byte fragments of A[ids_t[i]] and
+// B[ids_{t+1}[i]] for every k-step, all loads in flight at once.  Wave w handles
+// positions t = w, w + 4, ...; the dynamic programme then runs on K lanes.
 __global__ __launch_bounds__(256) void k_viterbi(const int32_t *cand_ids, const float *cand_logp,
                                                  const uint16_t *code_a, const uint16_t *code_b,
                                                  int P, int K, int r, float s, const int32_t *valid,
                                                  int32_t *draft) {
     __shared__ int ids[MAXP][MAXK];
     __shared__ float lp[MAXP][MAXK];
-    __shared__ __align__(16) uint16_t Ar[MAXK * MAXR];
-    __shared__ __align__(16) uint16_t Br[MAXK * MAXR];
     __shared__ float Tm[MAXP][MAXK][MAXK];
     __shared__ float delta[2][MAXK];
     __shared__ int psi[MAXP][MAXK];
-    const int b = blockIdx.x, tid = threadIdx.x;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (!valid[b]) {
         if (tid < P) draft[(size_t)b * P + tid] = -1;
         return;
     }
-    for (int e = tid; e < P * K; e += 256) {
-        ids[e / K][e % K] = cand_ids[(size_t)b * P * K + e];
-        lp[e / K][e % K] = cand_logp[(size_t)b * P * K + e];
+    for (int e = tid; e < P * MAXK; e += 256) {
+        const int t = e / MAXK, i = e % MAXK;
+        ids[t][i] = i < K ? cand_ids[(size_t)b * P * K + t * K + i] : -1;
+        lp[t][i] = i < K ? cand_logp[(size_t)b * P * K + t * K + i] : -INFINITY;
     }
     __syncthreads();
-    for (int t = 0; t + 1 < P; t++) {
-        // gather A rows of position t and B rows of position t+1 (16-byte pieces)
-        const int pieces = r / 8;
-        for (int e = tid; e < K * pieces; e += 256) {
-            const int i = e / pieces, q = e % pieces;
-            const int ua = ids[t][i], vb = ids[t + 1][i];
-            const u32x4_t z = {0, 0, 0, 0};
-            *reinterpret_cast<u32x4_t *>(&Ar[i * r + 8 * q]) =
-                ua >= 0 ? *reinterpret_cast<const u32x4_t *>(code_a + (size_t)ua * r + 8 * q) : z;
-            *reinterpret_cast<u32x4_t *>(&Br[i * r + 8 * q]) =
-                vb >= 0 ? *reinterpret_cast<const u32x4_t *>(code_b + (size_t)vb * r + 8 * q) : z;
+    const int c = lane & 15, g = lane >> 4;
+    const int nks = r / 32;
+    for (int t = wave; t + 1 < P; t += 4) {
+        const int ua = ids[t][c], vb = ids[t + 1][c];
+        const uint16_t *ar = code_a + (size_t)(ua >= 0 ? ua : 0) * r + 8 * g;
+        const uint16_t *br = code_b + (size_t)(vb >= 0 ? vb : 0) * r + 8 * g;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < nks; ks++) {
+            u32x4_t av = *reinterpret_cast<const u32x4_t *>(ar + ks * 32);
+            u32x4_t bv = *reinterpret_cast<const u32x4_t *>(br + ks * 32);
+            if (ua < 0) av = (u32x4_t){0, 0, 0, 0};
+            if (vb < 0) bv = (u32x4_t){0, 0, 0, 0};
+            acc = mfma16x16x32(av, bv, acc);
         }
-        __syncthreads();
-        if (tid < K * K) {
-            const int i = tid / K, j = tid % K;
-            float acc = 0.f;
-            for (int k = 0; k < r; k++) acc += bf16_to_f32(Ar[i * r + k]) * bf16_to_f32(Br[j * r + k]);
-            Tm[t][i][j] = s * acc;
-        }
-        __syncthreads();
+#pragma unroll
+        for (int v = 0; v < 4; v++) Tm[t][4 * g + v][c] = s * acc[v];
     }
-    if (tid < K) delta[0][tid] = lp[0][tid];
     __syncthreads();
-    for (int t = 0; t + 1 < P; t++) {
-        const int cur = t & 1;
-        if (tid < K) {
-            const int j = tid;
-            float best = delta[cur][0] + Tm[t][0][j];
+    if (wave == 0) {
+        // delta over candidates j < K on lanes 0..K-1; ties to the lowest index
+        const int j = lane;
+        float dcur = j < K ? lp[0][j] : -INFINITY;
+        for (int t = 0; t + 1 < P; t++) {
+            if (j < K) delta[t & 1][j] = dcur;
+            __builtin_amdgcn_wave_barrier();
+            float best = -INFINITY;
             int bi = 0;
-            for (int i = 1; i < K; i++) {
-                const float v = delta[cur][i] + Tm[t][i][j];
-                if (v > best) { best = v; bi = i; }
+            if (j < K) {
+                best = delta[t & 1][0] + Tm[t][0][j];
+                for (int i = 1; i < K; i++) {
+                    const float v = delta[t & 1][i] + Tm[t][i][j];
+                    if (v > best) { best = v; bi = i; }
+                }
+                psi[t + 1][j] = bi;
+                dcur = lp[t + 1][j] + best;
             }
-            delta[cur ^ 1][j] = lp[t + 1][j] + best;
-            psi[t + 1][j] = bi;
+            __builtin_amdgcn_wave_barrier();
         }
-        __syncthreads();
-    }
-    if (tid == 0) {
-        const int fin = (P - 1) & 1;
-        int j = 0;
-        for (int i = 1; i < K; i++)
-            if (delta[fin][i] > delta[fin][j]) j = i;
-        for (int t = P - 1; t >= 0; t--) {
-            draft[(size_t)b * P + t] = ids[t][j];
-            if (t > 0) j = psi[t][j];
+        if (j < K) delta[(P - 1) & 1][j] = dcur;
+        __builtin_amdgcn_wave_barrier();
+        if (lane == 0) {
+            const int fin = (P - 1) & 1;
+            int jj = 0;
+            for (int i = 1; i < K; i++)
+                if (delta[fin][i] > delta[fin][jj]) jj = i;
+            for (int t = P - 1; t >= 0; t--) {
+                draft[(size_t)b * P + t] = ids[t][jj];
+                if (t > 0) jj = psi[t][jj];
+            }
         }
     }
 }

@@ -92,7 +92,7 @@ def test_draft_step_rejects_bad_arguments_before_launch():
     assert call_step(tiny_cfg(block=5), w) == -2
     assert call_step(tiny_cfg(n_kv_heads=3), w) == -2
     assert call_step(tiny_cfg(hidden=200), w) == -2
-    assert call_step(tiny_cfg(sel_rank=12), w) == -2
+    assert call_step(tiny_cfg(sel_rank=48), w) == -2
     assert call_step(tiny_cfg(weight_fmt=7), w) == -1
     assert call_step(cfg, w, taps=FAKE + 2) == -3           # EALIGN
     assert call_step(cfg, w, ws=None) == -4                 # EWORKSPACE
