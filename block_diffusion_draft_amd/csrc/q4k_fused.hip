@@ -10,8 +10,8 @@
 //  * A nibble q enters the MFMA as the bf16 value 128 + q (bits 0x4300 | q); the
 //    MFMA accumulator starts at -128 S_rj, so D_j = sum_k x_rk q_k exactly up to
 //    fp32 accumulation.  Then sum_j sc_j D_j takes 4 FMAs per sub-block and lane.
-//  * sum_j m_j S_rj is one more MFMA per super-block: A carries (hi, lo) bf16 pairs
-//    of S_rj (16 significant bits), B the small integers m_j (exact in bf16).
+//  * sum_j m_j S_rj is one more MFMA per super-block: A carries each fp32 S_rj as four
+//    bf16 terms that add up to it exactly, B the small integers m_j (exact in bf16).
 //
 // Work split.  A workgroup (4 waves) owns a column group and a range of NSB
 // super-blocks (split-K).  Its bf16 activation rows for that range are staged once
@@ -158,21 +158,25 @@ void k_q4k_fused(Q4kFusedArgs a) {
         }
     }
     __syncthreads();
-    // bias operand: lane (row r, group gg): gg 0 -> (S_0..3 hi, lo), gg 1 -> S_4..7, else 0
+    // bias operand: lane (row r, group gg) holds S_j for j = 2 gg and 2 gg + 1, each as four
+    // bf16 terms whose sum is the fp32 value exactly (8 + 8 + 8 + 8 >= 24 bits)
     if (tid < nsb * rt_n * 64) {
         const int ln = tid & 63, rest = tid >> 6;
         const int rt = rest % rt_n, sbi = rest / rt_n;
         const int r = ln & 15, gg = ln >> 4;
-        uint32_t o[4] = {0u, 0u, 0u, 0u};
-        if (gg < 2) {
+        uint32_t o[4];
 #pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-                const int j = 4 * gg + jj;
-                const float S = C_lds[((sbi * 8 + j) * rt_n + rt) * 16 + r] * (-1.f / 128.f);
-                const uint16_t hb = f32_to_bf16(S);
-                const uint16_t lb = f32_to_bf16(S - bf16_to_f32(hb));
-                o[jj] = (uint32_t)hb | ((uint32_t)lb << 16);
+        for (int jj = 0; jj < 2; jj++) {
+            const int j = 2 * gg + jj;
+            float rem = C_lds[((sbi * 8 + j) * rt_n + rt) * 16 + r] * (-1.f / 128.f);
+            uint16_t t[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                t[q] = f32_to_bf16(rem);
+                rem -= bf16_to_f32(t[q]);
             }
+            o[2 * jj] = (uint32_t)t[0] | ((uint32_t)t[1] << 16);
+            o[2 * jj + 1] = (uint32_t)t[2] | ((uint32_t)t[3] << 16);
         }
         B_lds[tid] = (u32x4_t){o[0], o[1], o[2], o[3]};
     }
@@ -220,14 +224,10 @@ void k_q4k_fused(Q4kFusedArgs a) {
                 }
             }
         }
-        // bias: sum_j m_j S_j via one MFMA (B: m_j of this lane's column)
-        const uint32_t mw = g == 0 ? m_lo : m_hi;
-        u32x4_t bb;
-        bb.x = int_byte_bf16x2(mw, 0);
-        bb.y = int_byte_bf16x2(mw, 1);
-        bb.z = int_byte_bf16x2(mw, 2);
-        bb.w = int_byte_bf16x2(mw, 3);
-        if (g >= 2) bb = (u32x4_t){0u, 0u, 0u, 0u};
+        // bias: sum_j m_j S_j via one MFMA; B slots of lane group g: m_{2g} x4, m_{2g+1} x4
+        const uint32_t mw = g < 2 ? m_lo : m_hi;
+        const uint32_t m0 = int_byte_bf16x2(mw, (2 * g) & 3), m1 = int_byte_bf16x2(mw, (2 * g + 1) & 3);
+        const u32x4_t bb = {m0, m0, m1, m1};
 #pragma unroll
         for (int rt = 0; rt < RT; rt++) {
             const int rtl = rt < rt_n ? rt : 0;
