@@ -18,16 +18,14 @@ struct Plan {
     int topk_nch;
     bool lm_skinny;
     // byte offsets into the workspace
-    size_t o_valid, o_h, o_xc, o_u2, o_fcout, o_qkv, o_Q, o_Kb, o_Vb, o_attnO, o_attnML, o_o,
-        o_zp, o_Y, o_mid2, o_f, o_logits, o_pv, o_pi, o_pm, o_ps, o_part, o_ssq_h, o_ssq_c,
-        o_counters;
+    size_t o_valid, o_h, o_xc, o_u2, o_fcout, o_Q, o_Kb, o_Vb, o_attnO, o_attnML, o_o, o_zp,
+        o_Y, o_mid2, o_f, o_logits, o_pv, o_pi, o_pm, o_ps, o_ssq, o_part;
     size_t total;
 };
 
-constexpr int N_COUNTERS = 4096;
-
-size_t gemm_part_bytes(int fmt, int M, int N, int K, int paired = 0) {
-    if (fmt == DFLASH_W_Q4K) return q4k_fused_plan(M, N, K, paired).part_bytes;
+// fp32 partial sums of one GEMM: [splits][M][N] (Q4_K split-K) or [M][N] (bf16)
+size_t gemm_part_bytes(int fmt, int M, int N, int K) {
+    if (fmt == DFLASH_W_Q4K) return q4k_fused_plan(M, N, K).part_bytes;
     return (size_t)M * N * 4;
 }
 
@@ -70,7 +68,7 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
     upd(gemm_part_bytes(fmt, p.M_qkv, p.qd + 2 * p.kd, p.H));
     upd(gemm_part_bytes(fmt, p.M_blk, p.H, p.qd));
     // the MLP runs over [hi rows; lo rows] of its bf16-pair activations
-    upd(gemm_part_bytes(fmt, 2 * p.M_blk, 2 * p.F, p.H, 1));
+    upd(gemm_part_bytes(fmt, 2 * p.M_blk, 2 * p.F, p.H));
     upd(gemm_part_bytes(fmt, 2 * p.M_blk, p.H, p.F));
 
     size_t o = 0;
@@ -80,7 +78,6 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
     p.o_xc = take((size_t)p.M_qkv * p.H * 2);
     p.o_u2 = take((size_t)2 * p.M_blk * p.H * 2);
     p.o_fcout = take((size_t)p.M_ctx * p.H * 4);
-    p.o_qkv = take((size_t)p.M_qkv * (p.qd + 2 * p.kd) * 4);
     p.o_Q = take((size_t)p.M_blk * p.qd * 2);
     p.o_Kb = take((size_t)p.M_blk * p.kd * 2);
     p.o_Vb = take((size_t)p.M_blk * p.kd * 2);
@@ -97,10 +94,8 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
     p.o_pi = take((size_t)p.R * p.topk_nch * p.K * 4);
     p.o_pm = take((size_t)p.R * p.topk_nch * 4);
     p.o_ps = take((size_t)p.R * p.topk_nch * 4);
+    p.o_ssq = take((size_t)p.M_blk * (p.H / 256) * 4);
     p.o_part = take(part);
-    p.o_ssq_h = take((size_t)p.M_blk * (p.H / 16) * 4);
-    p.o_ssq_c = take((size_t)p.M_ctx * (p.H / 16) * 4);
-    p.o_counters = take((size_t)N_COUNTERS * 4);
     p.total = o;
     return true;
 }
@@ -142,20 +137,36 @@ struct Ctx {
     template <class T> T *at(size_t off) const { return reinterpret_cast<T *>(ws + off); }
 };
 
-// y = A . W^T over up to 3 stacked weight matrices, then the reduction epilogue
-// bf16 weights: y = A . W^T over up to 3 stacked matrices (tiled MFMA GEMM), then the
-// reduction epilogue.  pair: A holds [hi rows; lo rows] of M_out output rows.
-int run_gemm_bf16(const Ctx &x, const void *const *w, const int *seg_n, int nseg,
-                  const uint16_t *A, int lda, int M_out, bool pair, int K, int mode, float *of,
-                  uint16_t *ob, uint16_t *ob_lo, int ldo) {
-    const int M = pair ? 2 * M_out : M_out;
+// y = A . W^T over up to 3 weight matrices stacked along N, as fp32 partial sums in
+// the workspace's partial buffer: Q4_K -> [splits][M][N] from the dequantize-fused
+// MFMA kernel; bf16 -> [M][N] (one split) from the tiled MFMA kernel.  Returns the
+// number of splits (> 0) or a negative status.
+int run_gemm(const Ctx &x, const void *const *w, const int *seg_n, int nseg, const uint16_t *A,
+             int lda, int M, int K) {
     int N = 0;
     int seg_end[3] = {0, 0, 0};
-    for (int i = 0; i < nseg; i++) {
-        N += seg_n[i];
+    for (int i = 0; i < 3; i++) {
+        if (i < nseg) N += seg_n[i];
         seg_end[i] = N;
     }
     float *part = x.at<float>(x.p->o_part);
+    if (x.c->weight_fmt == DFLASH_W_Q4K) {
+        Q4kFusedArgs a;
+        for (int i = 0; i < 3; i++) {
+            a.w[i] = (const unsigned char *)(i < nseg ? w[i] : w[0]);
+            a.seg_end[i] = seg_end[i];
+        }
+        a.nseg = nseg;
+        a.M = M;
+        a.N = N;
+        a.KB = K / 256;
+        a.src.A = A;
+        a.src.lda = lda;
+        a.part = part;
+        const Q4kFusedPlan p = q4k_fused_plan(M, N, K);
+        HIPCHK(launch_q4k_fused(a, p, x.st));
+        return p.splits;
+    }
     Bf16GemmArgs a = {};
     for (int i = 0; i < 3; i++) {
         a.w[i] = (const uint16_t *)(i < nseg ? w[i] : w[0]);
@@ -170,54 +181,7 @@ int run_gemm_bf16(const Ctx &x, const void *const *w, const int *seg_n, int nseg
     a.C = part;
     a.ldc = N;
     HIPCHK(launch_bf16_gemm_tiled(a, x.st));
-    HIPCHK(launch_reduce_epilogue(part, 1, M_out, N, pair ? M_out : 0, mode, of, ob, ob_lo, ldo,
-                                  x.st));
-    return DFLASH_OK;
-}
-
-// Q4_K weights: one fused launch (normalised staging, split-K fixup, epilogue).
-// Returns the number of column groups (the row sums-of-squares count) via n_groups.
-int run_q4k(const Ctx &x, const void *const *w, const int *seg_n, int nseg, int M, int K,
-            int paired, const Q4kSrc &src, const Q4kOut &out, int *n_groups) {
-    Q4kFusedArgs a;
-    int N = 0;
-    for (int i = 0; i < 3; i++) {
-        if (i < nseg) N += seg_n[i];
-        a.seg_end[i] = N;
-        a.w[i] = (const unsigned char *)(i < nseg ? w[i] : w[0]);
-    }
-    a.nseg = nseg;
-    a.M = M;
-    a.N = N;
-    a.KB = K / 256;
-    a.paired = paired;
-    a.src = src;
-    a.out = out;
-    a.part = x.at<float>(x.p->o_part);
-    a.counters = x.at<int>(x.p->o_counters);
-    const Q4kFusedPlan p = q4k_fused_plan(M, N, K, paired);
-    if (p.grid_x > N_COUNTERS) return DFLASH_ESHAPE;
-    HIPCHK(launch_q4k_fused(a, p, x.st));
-    if (n_groups) *n_groups = p.grid_x;
-    return DFLASH_OK;
-}
-
-Q4kSrc src_bf16(const uint16_t *A, int lda) {
-    Q4kSrc s;
-    s.A = A;
-    s.lda = lda;
-    return s;
-}
-
-Q4kOut out_f32(int mode, float *f, int ldo, float *ssq, int M_out, int pair) {
-    Q4kOut o = {};
-    o.mode = mode;
-    o.f = f;
-    o.ldo = ldo;
-    o.ssq = ssq;
-    o.M_out = M_out;
-    o.pair = pair;
-    return o;
+    return 1;
 }
 
 }  // namespace
@@ -280,71 +244,56 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
 
     Ctx x{cfg, &p, (unsigned char *)workspace, (hipStream_t)stream};
     const int H = p.H, L = p.L;
-    const bool q4 = cfg->weight_fmt == DFLASH_W_Q4K;
     float *h = x.at<float>(p.o_h);
     uint16_t *xc = x.at<uint16_t>(p.o_xc);
     int32_t *valid = x.at<int32_t>(p.o_valid);
-    float *ssq_h = x.at<float>(p.o_ssq_h);
-    float *ssq_c = x.at<float>(p.o_ssq_c);
     float *fcout = x.at<float>(p.o_fcout);
+    float *part = x.at<float>(p.o_part);
+    float *ssq = x.at<float>(p.o_ssq);
     uint16_t *u2 = x.at<uint16_t>(p.o_u2);
     uint16_t *mid2 = x.at<uint16_t>(p.o_mid2);
+    uint16_t *f = x.at<uint16_t>(p.o_f);
+    const float eps = cfg->rms_eps;
     const size_t cache_layer = (size_t)batch * p.n_kv * cache_cap * p.d;
-    int n_h = 1, n_c = 1;        // column groups behind the row sums of squares of h and c
+    int splits;
+#define GEMM(...)                              \
+    do {                                       \
+        splits = run_gemm(x, __VA_ARGS__);     \
+        if (splits < 0) return splits;         \
+    } while (0)
 
-    // S0: block assembly, per-sequence validity, row sums of squares; fixup counters zeroed
+    // S0: block assembly h, per-sequence validity, first layer's input x = RMSNorm(h)
     HIPCHK(launch_embed(w->embed, w->mask_emb, last_token, ctx_len, batch, p.T, H, p.V, t_new,
-                        cache_cap, h, ssq_h, valid, x.at<int>(p.o_counters), N_COUNTERS, x.st));
+                        cache_cap, h, w->layer[0].in_norm, eps, xc, valid, x.st));
     if (dbg_hidden)
         HIPCHK(hipMemcpyAsync(dbg_hidden, h, (size_t)p.M_blk * H * 4, hipMemcpyDeviceToDevice, x.st));
 
-    // S1: fused taps c = RMSNorm(X . W_fc^T)
+    // S1: fused taps c = RMSNorm(X . W_fc^T), the context rows of the K/V projection input
     {
         const void *ws[1] = {w->fc};
         const int sn[1] = {H};
-        if (q4) {
-            rc = run_q4k(x, ws, sn, 1, p.M_ctx, cfg->n_taps * H, 0, src_bf16(taps, cfg->n_taps * H),
-                         out_f32(EPI_STORE_F32, fcout, H, ssq_c, p.M_ctx, 0), &n_c);
-            if (rc) return rc;
-            HIPCHK(launch_rownorm(fcout, ssq_c, n_c, p.M_ctx, H, 1, 1, 0, w->hidden_norm,
-                                  cfg->rms_eps, xc + (size_t)p.M_blk * H, nullptr, H, x.st));
-        } else {
-            rc = run_gemm_bf16(x, ws, sn, 1, taps, cfg->n_taps * H, p.M_ctx, false, cfg->n_taps * H,
-                               EPI_STORE_F32, fcout, nullptr, nullptr, H);
-            if (rc) return rc;
-            HIPCHK(launch_rmsnorm(fcout, p.M_ctx, H, 1, 1, 0, w->hidden_norm, cfg->rms_eps,
-                                  xc + (size_t)p.M_blk * H, nullptr, H, x.st));
-        }
+        GEMM(ws, sn, 1, taps, cfg->n_taps * H, p.M_ctx, cfg->n_taps * H);
+        HIPCHK(launch_reduce_norm(part, splits, p.M_ctx, H, 0, 0, fcout, ssq, w->hidden_norm, eps,
+                                  xc + (size_t)p.M_blk * H, nullptr, H, 0, x.st));
     }
 
     for (int l = 0; l < L; l++) {
         const dflash_layer_weights &lw = w->layer[l];
+        const bool last = l == L - 1;
         uint16_t *kc = k_cache + (size_t)l * cache_layer;
         uint16_t *vc = v_cache + (size_t)l * cache_layer;
-        // S2 + S3: x = RMSNorm(h); [Q | K | V] of the block rows, K and V of the context rows
+        // S2 + S3: [Q | K | V] of the block rows, K and V of the context rows
         {
             const void *ws[3] = {lw.wq, lw.wk, lw.wv};
             const int sn[3] = {p.qd, p.kd, p.kd};
-            if (q4) {
-                HIPCHK(launch_rownorm(h, ssq_h, n_h, p.M_blk, H, 1, 1, 0, lw.in_norm, cfg->rms_eps,
-                                      xc, nullptr, H, x.st));
-                rc = run_q4k(x, ws, sn, 3, p.M_qkv, H, 0, src_bf16(xc, H),
-                             out_f32(EPI_STORE_F32, x.at<float>(p.o_qkv), p.qd + 2 * p.kd, nullptr,
-                                     p.M_qkv, 0), nullptr);
-            } else {
-                HIPCHK(launch_rmsnorm(h, p.M_blk, H, 1, 1, 0, lw.in_norm, cfg->rms_eps, xc, nullptr,
-                                      H, x.st));
-                rc = run_gemm_bf16(x, ws, sn, 3, xc, H, p.M_qkv, false, H, EPI_STORE_F32,
-                                   x.at<float>(p.o_qkv), nullptr, nullptr, p.qd + 2 * p.kd);
-            }
-            if (rc) return rc;
+            GEMM(ws, sn, 3, xc, H, p.M_qkv, H);
         }
-        // S4: per-head norms, rotary embedding, cache append
+        // S4: split sum, per-head norms, rotary embedding, cache append
         {
             RopeArgs a;
-            a.qkv = x.at<float>(p.o_qkv);
+            a.qkv = part; a.splits = splits;
             a.B = batch; a.T = p.T; a.t_new = t_new; a.n_q = p.n_q; a.n_kv = p.n_kv; a.d = p.d;
-            a.q_norm = lw.q_norm; a.k_norm = lw.k_norm; a.eps = cfg->rms_eps;
+            a.q_norm = lw.q_norm; a.k_norm = lw.k_norm; a.eps = eps;
             a.theta = cfg->rope_theta; a.ctx_len = ctx_len; a.valid = valid;
             a.Q = x.at<uint16_t>(p.o_Q); a.Kb = x.at<uint16_t>(p.o_Kb); a.Vb = x.at<uint16_t>(p.o_Vb);
             a.k_cache = kc; a.v_cache = vc; a.cap = cache_cap;
@@ -371,58 +320,44 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
             a.Y = x.at<uint16_t>(p.o_Y);
             HIPCHK(launch_merge_conv(a, x.st));
         }
-        // S7: h += Y . W_o^T
+        // S7: h += Y . W_o^T; u = RMSNorm(h) as bf16 (hi, lo) pairs
         {
             const void *ws[1] = {lw.wo};
             const int sn[1] = {H};
-            if (q4)
-                rc = run_q4k(x, ws, sn, 1, p.M_blk, p.qd, 0, src_bf16(x.at<uint16_t>(p.o_Y), p.qd),
-                             out_f32(EPI_ADD_F32, h, H, ssq_h, p.M_blk, 0), &n_h);
-            else
-                rc = run_gemm_bf16(x, ws, sn, 1, x.at<uint16_t>(p.o_Y), p.qd, p.M_blk, false, p.qd,
-                                   EPI_ADD_F32, h, nullptr, nullptr, H);
-            if (rc) return rc;
+            GEMM(ws, sn, 1, x.at<uint16_t>(p.o_Y), p.qd, p.M_blk, p.qd);
+            HIPCHK(launch_reduce_norm(part, splits, p.M_blk, H, 0, 1, h, ssq, lw.post_norm, eps, u2,
+                                      u2 + (size_t)p.M_blk * H, H, 0, x.st));
         }
-        // S8: u = RMSNorm(h); h += (silu(u Wg^T) * u Wu^T) Wd^T, with u and the SwiGLU
-        // output carried as bf16 (hi, lo) pairs: the MLP inputs dominate the rounding error
+        // S8: h += (silu(u Wg^T) * u Wu^T) Wd^T.  u and the SwiGLU output are carried as
+        // bf16 (hi, lo) pairs (the MLP inputs dominate the rounding error), so both
+        // products run over [hi rows; lo rows] and the reductions add row r and r + M.
         {
             const void *ws[2] = {lw.wg, lw.wu};
             const int sn[2] = {p.F, p.F};
             const bool probe_ffn = probe && probe->kernel == DFLASH_PROBE_FFN_GATE_UP && probe->layer == l;
             if (probe_ffn) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_start, x.st));
-            if (q4) {
-                HIPCHK(launch_rownorm(h, ssq_h, n_h, p.M_blk, H, 1, 1, 0, lw.post_norm, cfg->rms_eps,
-                                      u2, u2 + (size_t)p.M_blk * H, H, x.st));
-                Q4kOut out = {};
-                out.mode = EPI_SWIGLU_BF16; out.b = mid2; out.b_lo = mid2 + (size_t)p.M_blk * p.F;
-                out.ldo = p.F; out.pair = p.M_blk; out.M_out = p.M_blk;
-                rc = run_q4k(x, ws, sn, 2, 2 * p.M_blk, H, 1, src_bf16(u2, H), out, nullptr);
-            } else {
-                HIPCHK(launch_rmsnorm(h, p.M_blk, H, 1, 1, 0, lw.post_norm, cfg->rms_eps, u2,
-                                      u2 + (size_t)p.M_blk * H, H, x.st));
-                rc = run_gemm_bf16(x, ws, sn, 2, u2, H, p.M_blk, true, H, EPI_SWIGLU_BF16, nullptr,
-                                   mid2, mid2 + (size_t)p.M_blk * p.F, p.F);
-            }
-            if (rc) return rc;
+            GEMM(ws, sn, 2, u2, H, 2 * p.M_blk, H);
             if (probe_ffn) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_stop, x.st));
+            HIPCHK(launch_reduce_epilogue(part, splits, p.M_blk, 2 * p.F, p.M_blk, EPI_SWIGLU_BF16,
+                                          nullptr, mid2, mid2 + (size_t)p.M_blk * p.F, p.F, x.st));
         }
+        // down projection + residual; then the next layer's input norm, or after the last
+        // layer the final norm of the proposal rows (block positions 1..7) for the head
         {
             const void *ws[1] = {lw.wd};
             const int sn[1] = {H};
-            if (q4)
-                rc = run_q4k(x, ws, sn, 1, 2 * p.M_blk, p.F, 0, src_bf16(mid2, p.F),
-                             out_f32(EPI_ADD_F32, h, H, ssq_h, p.M_blk, p.M_blk), &n_h);
-            else
-                rc = run_gemm_bf16(x, ws, sn, 1, mid2, p.F, p.M_blk, true, p.F, EPI_ADD_F32, h,
-                                   nullptr, nullptr, H);
-            if (rc) return rc;
+            GEMM(ws, sn, 1, mid2, p.F, 2 * p.M_blk, p.F);
+            const uint16_t *gain = last ? w->final_norm : w->layer[l + 1].in_norm;
+            HIPCHK(launch_reduce_norm(part, splits, p.M_blk, H, p.M_blk, 1, h, ssq, gain, eps,
+                                      last ? f : xc, nullptr, H, last ? 1 : 0, x.st));
         }
         if (dbg_hidden)
             HIPCHK(hipMemcpyAsync(dbg_hidden + (size_t)(l + 1) * p.M_blk * H, h,
                                   (size_t)p.M_blk * H * 4, hipMemcpyDeviceToDevice, x.st));
     }
+#undef GEMM
 
-    // S9 + S10: final norm of the proposal rows 1..7, logits with the shared output head,
+    // S9 + S10: logits of the proposal rows with the shared output head,
     // then log-softmax statistics and top-K
     float *logits = dbg_logits ? dbg_logits : x.at<float>(p.o_logits);
     {
@@ -431,16 +366,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
         a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = p.V;
         a.nseg = 1;
         a.M = p.R; a.N = p.V; a.K = H; a.C = logits; a.ldc = p.V;
-        const bool norm_in_head = p.lm_skinny && q4;
-        uint16_t *f = x.at<uint16_t>(p.o_f);
-        if (norm_in_head) {
-            a.a_norm = 1; a.af = h; a.again = w->final_norm; a.assq = ssq_h; a.an_groups = n_h;
-            a.aper = p.P; a.agroup = p.T; a.aoff = 1; a.aeps = cfg->rms_eps;
-        } else {
-            HIPCHK(launch_rmsnorm(h, p.R, H, p.P, p.T, 1, w->final_norm, cfg->rms_eps, f, nullptr, H,
-                                  x.st));
-            a.A = f; a.lda = H;
-        }
+        a.A = f; a.lda = H;
         const bool probe_lm = probe && probe->kernel == DFLASH_PROBE_LM_HEAD;
         if (probe_lm) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_start, x.st));
         if (p.lm_skinny) HIPCHK(launch_bf16_gemm_skinny(a, x.st));
@@ -468,7 +394,7 @@ int dflash_verify_prefix(const int32_t *draft, const int32_t *target, int batch,
 
 size_t q4k_gemm_workspace_bytes(int M, int N, int K) {
     if (M < 1 || M > 4096 || N < 16 || N % 16 || K < 256 || K % 256) return 0;
-    return align256(gemm_part_bytes(DFLASH_W_Q4K, M, N, K)) + N_COUNTERS * 4;
+    return gemm_part_bytes(DFLASH_W_Q4K, M, N, K);
 }
 
 int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
@@ -478,20 +404,19 @@ int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
     if (!aligned16(w) || !aligned16(x) || !aligned16(y)) return DFLASH_EALIGN;
     const size_t need = q4k_gemm_workspace_bytes(M, N, K);
     if (!workspace || ws_bytes < need || !aligned16(workspace)) return DFLASH_EWORKSPACE;
-    const Q4kFusedPlan p = q4k_fused_plan(M, N, K, 0);
-    if (p.grid_x > N_COUNTERS) return DFLASH_ESHAPE;
+    const hipStream_t st = (hipStream_t)stream;
+    const Q4kFusedPlan p = q4k_fused_plan(M, N, K);
     Q4kFusedArgs a;
     a.w[0] = a.w[1] = a.w[2] = (const unsigned char *)w;
     a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = N;
     a.nseg = 1;
-    a.M = M; a.N = N; a.KB = K / 256; a.paired = 0;
-    a.src = src_bf16(x, K);
-    a.out = {};
-    a.out.mode = EPI_STORE_BF16; a.out.b = y; a.out.ldo = N; a.out.M_out = M;
+    a.M = M; a.N = N; a.KB = K / 256;
+    a.src.A = x;
+    a.src.lda = K;
     a.part = (float *)workspace;
-    a.counters = (int *)((char *)workspace + align256(gemm_part_bytes(DFLASH_W_Q4K, M, N, K)));
-    HIPCHK(launch_zero_i32(a.counters, p.grid_x, (hipStream_t)stream));
-    HIPCHK(launch_q4k_fused(a, p, (hipStream_t)stream));
+    HIPCHK(launch_q4k_fused(a, p, st));
+    HIPCHK(launch_reduce_epilogue(a.part, p.splits, M, N, 0, EPI_STORE_BF16, nullptr, y, nullptr, N,
+                                  st));
     return DFLASH_OK;
 }
 

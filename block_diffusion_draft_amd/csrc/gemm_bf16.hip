@@ -136,40 +136,11 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a, int ti
 #pragma unroll
         for (int u = 0; u < LM_PD - 1; u++) eb[u] = load_next();
     }
-    __shared__ float inv_rms[8];
-    if (a.a_norm) {
-        if (tid < 32) {
-            const int r = tid >> 2, q = tid & 3;
-            const int src = (r / a.aper) * a.agroup + a.aoff + r % a.aper;
-            float s = 0.f;
-            if (r < a.M)
-                for (int i = q; i < a.an_groups; i += 4) s += a.assq[(size_t)src * a.an_groups + i];
-            s += __shfl_xor(s, 1, WAVE);
-            s += __shfl_xor(s, 2, WAVE);
-            if (q == 0) inv_rms[r] = rsqrtf(s / (float)a.K + a.aeps);
-        }
-        __syncthreads();
-    }
     for (int e = tid; e < nks * 32 + 1; e += 256) {
         const int ks = e >> 5, slot = e & 31, gg = slot >> 3, r = slot & 7;
         u32x4_t v = {0, 0, 0, 0};
-        if (e < nks * 32 && r < a.M) {
-            const int k = ks * 32 + 8 * gg;
-            if (a.a_norm) {
-                const int src = (r / a.aper) * a.agroup + a.aoff + r % a.aper;
-                const float *x = a.af + (size_t)src * a.K + k;
-                const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(x);
-                const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(x + 4);
-                const u32x4_t gv = *reinterpret_cast<const u32x4_t *>(a.again + k);
-                const float inv = inv_rms[r];
-                v.x = pack_bf16x2(x0.x * inv * bf16_to_f32(gv.x & 0xFFFF), x0.y * inv * bf16_to_f32(gv.x >> 16));
-                v.y = pack_bf16x2(x0.z * inv * bf16_to_f32(gv.y & 0xFFFF), x0.w * inv * bf16_to_f32(gv.y >> 16));
-                v.z = pack_bf16x2(x1.x * inv * bf16_to_f32(gv.z & 0xFFFF), x1.y * inv * bf16_to_f32(gv.z >> 16));
-                v.w = pack_bf16x2(x1.z * inv * bf16_to_f32(gv.w & 0xFFFF), x1.w * inv * bf16_to_f32(gv.w >> 16));
-            } else {
-                v = *reinterpret_cast<const u32x4_t *>(a.A + (size_t)r * a.lda + k);
-            }
-        }
+        if (e < nks * 32 && r < a.M)
+            v = *reinterpret_cast<const u32x4_t *>(a.A + (size_t)r * a.lda + ks * 32 + 8 * gg);
         Alds[e] = v;
     }
     __syncthreads();

@@ -4,23 +4,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-// ---------------------------------------------------------------- Q4_K GEMM
-struct Q4kGemmArgs {
-    const unsigned char *w[3];   // up to 3 weight matrices stacked along N
-    int seg_end[3];              // cumulative column count after each segment
-    int nseg;
-    const uint16_t *A;           // bf16 activations [M][lda]
-    int lda;
-    int M, N, KB;                // KB = K / 256
-    int kb_per;                  // super-blocks per split
-    float *part;                 // fp32 partials [splits][M][N]
-};
-struct Q4kPlan {
-    int KB, kb_per, splits, row_groups, grid_x, rt;
-    size_t lds_bytes;
-};
-Q4kPlan q4k_plan(int M, int N, int K);
-hipError_t launch_q4k_gemm(const Q4kGemmArgs &a, const Q4kPlan &p, hipStream_t st);
+// ---------------------------------------------------------------- Q4_K decode
 hipError_t launch_q4k_dequant(const void *w, float *out, long long n_blocks, hipStream_t st);
 
 // ---------------------------------------------------------------- bf16 GEMMs
@@ -33,15 +17,6 @@ struct Bf16GemmArgs {
     int M, N, K;
     float *C;                    // fp32 [M][ldc]
     int ldc;
-    // skinny kernel only: a_norm != 0 stages A row r as bf16(RMSNorm(af[src(r)]) * again),
-    // src(r) = (r / aper) * agroup + aoff + r % aper, with the row's sum of squares taken
-    // from assq[src(r)][0 .. an_groups)
-    int a_norm;
-    const float *af;
-    const uint16_t *again;
-    const float *assq;
-    int an_groups, aper, agroup, aoff;
-    float aeps;
 };
 // tiled 128x128 MFMA GEMM, any M
 hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st);
@@ -57,21 +32,17 @@ hipError_t launch_reduce_epilogue(const float *part, int splits, int M, int N, i
                                   int mode, float *out_f32, uint16_t *out_bf16,
                                   uint16_t *out_bf16_lo, int ldo, hipStream_t st);
 
-// per-sequence validity flags + block assembly h[b][0] = E[last], h[b][1..] = mask, with
-// each row's sum of squares (ssq[row]); also zeroes n_counters fixup counters
+// per-sequence validity flags + block assembly h[b][0] = E[last], h[b][1..] = mask, and
+// the first layer's normalised input x = bf16(RMSNorm(h) * gain), [B*T][H]
 hipError_t launch_embed(const uint16_t *embed, const uint16_t *mask_emb, const int32_t *last,
                         const int32_t *ctx_len, int B, int T, int H, int V, int t_new, int cap,
-                        float *h, float *ssq, int32_t *valid, int *counters, int n_counters,
+                        float *h, const uint16_t *gain, float eps, uint16_t *x, int32_t *valid,
                         hipStream_t st);
 
-// out[r] = bf16(RMSNorm(in[row(r)]) * g), row(r) = (r / per) * in_group + in_off + r % per;
-// out_lo (nullable) receives the bf16 residual of each value
-hipError_t launch_rmsnorm(const float *in, int R, int H, int per, int in_group, int in_off,
-                          const uint16_t *gain, float eps, uint16_t *out, uint16_t *out_lo,
-                          int ldo, hipStream_t st);
-
 struct RopeArgs {
-    const float *qkv;            // fp32 [B*(T + t_new)][qd + 2 kd]: block rows then context rows
+    const float *qkv;            // fp32 partials [splits][B*(T + t_new)][qd + 2 kd]: block rows
+                                 // then context rows, summed here in split order
+    int splits;
     int B, T, t_new, n_q, n_kv, d;
     const uint16_t *q_norm, *k_norm;
     float eps, theta;
@@ -125,39 +96,26 @@ struct Q4kSrc {
     const uint16_t *A;
     int lda;
 };
-// Epilogue applied by the last workgroup of each column group.
-struct Q4kOut {
-    int mode;                    // EpiMode
-    float *f;                    // STORE_F32 / ADD_F32 target [M_out][ldo]
-    uint16_t *b, *b_lo;          // bf16 targets (SWIGLU hi/lo, STORE_BF16)
-    int ldo;
-    float *ssq;                  // nullable: [M_out][n_groups] sums of squares of stored rows
-    int pair;                    // output row r = GEMM rows r + (r + pair)
-    int M_out;
-};
 struct Q4kFusedArgs {
     const unsigned char *w[3];
     int seg_end[3];
     int nseg;
-    int M, N, KB;                // GEMM rows (2 M_out with hilo), columns, K/256
-    int paired;                  // SWIGLU: workgroup pairs gate tiles with the matching up tiles
+    int M, N, KB;                // GEMM rows, columns, K/256
     Q4kSrc src;
-    Q4kOut out;
     float *part;                 // [splits][M][N]
-    int *counters;               // [grid_x], zero on entry, left zero
 };
 struct Q4kFusedPlan {
     int rt, nsb, ct, steps, splits, row_groups, grid_x;
     size_t lds_bytes, part_bytes;
 };
-Q4kFusedPlan q4k_fused_plan(int M, int N, int K, int paired);
+Q4kFusedPlan q4k_fused_plan(int M, int N, int K);
 hipError_t launch_q4k_fused(const Q4kFusedArgs &a, const Q4kFusedPlan &p, hipStream_t st);
-// zero n ints (workspace counters) with a kernel
-hipError_t launch_zero_i32(int *p, int n, hipStream_t st);
 
-// out rows r < R: bf16(RMSNorm(in[src(r)]) * gain), src(r) = (r / per) * in_group + in_off
-// + r % per, the row's sum of squares read from ssq[src(r)][0 .. n_groups); with out_lo
-// the bf16 residual of each value goes to out_lo (same layout)
-hipError_t launch_rownorm(const float *in, const float *ssq, int n_groups, int R, int H, int per,
-                          int in_group, int in_off, const uint16_t *gain, float eps, uint16_t *out,
-                          uint16_t *out_lo, int ldo, hipStream_t st);
+// Output rows r < M_out: v = sum over splits of partial rows r (+ r + pair), N a multiple
+// of 256; add ? f[r] += v : f[r] = v (fp32), with per-256-column sums of squares in
+// ssq [M_out][N/256].  Then, if out: the row's RMSNorm * gain as bf16 (and its residual
+// in out_lo) at output row map(r): map 0 -> r; map 1 -> the proposal rows of each block
+// of 8 (row r % 8 == 0 skipped, others to (r / 8) * 7 + r % 8 - 1).
+hipError_t launch_reduce_norm(const float *part, int splits, int M_out, int N, int pair, int add,
+                              float *f, float *ssq, const uint16_t *gain, float eps, uint16_t *out,
+                              uint16_t *out_lo, int ldo, int map, hipStream_t st);

@@ -1,6 +1,6 @@
 // Per-layer elementwise and row kernels of the draft step, gfx950:
-//   block assembly, RMSNorm, split-K reduction with fused epilogues (residual add,
-//   SwiGLU), per-head q/k RMSNorm + rotary embedding + KV-cache append, and the
+//   block assembly (+ first RMSNorm), split-K reductions with fused epilogues
+//   (residual add + RMSNorm, SwiGLU), per-head q/k RMSNorm + rotary embedding + KV-cache append, and the
 //   attention-partial merge fused with the two-tap dynamic convolution.
 // Sources: FastFlowLM card "Qwen3.8-27B-DFlash2-NPU2", spec table "Draft" row
 // (Qwen3-style layers, 32 query / 8 KV heads of 128, two-tap dynamic
@@ -21,21 +21,18 @@ __device__ __forceinline__ float block_sum_256(float v, float *scratch) {
 }
 
 // ---------------------------------------------------------------- block assembly
-// h[b][0] = E[last token], h[b][1..] = mask embedding; the row's sum of squares for
-// the first layer's fused normalisation; workgroup 0 also clears the GEMM fixup
-// counters of the step.
+// h[b][0] = E[last token], h[b][1..] = mask embedding, and the first layer's input
+// x = bf16(RMSNorm(h) * gain)
 __global__ __launch_bounds__(256) void k_embed(const uint16_t *embed, const uint16_t *mask,
                                                const int32_t *last, const int32_t *ctx_len,
                                                int T, int H, int V, int t_new, int cap,
-                                               float *h, float *ssq, int32_t *valid,
-                                               int *counters, int n_counters) {
+                                               float *h, const uint16_t *gain, float eps,
+                                               uint16_t *x, int32_t *valid) {
     __shared__ float scratch[4];
     const int b = blockIdx.x / T, t = blockIdx.x % T;
     const int n = ctx_len[b], tok = last[b];
     const bool ok = n >= 0 && n <= cap - t_new && tok >= 0 && tok < V;
     if (t == 0 && threadIdx.x == 0) valid[b] = ok ? 1 : 0;
-    if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i < n_counters; i += 256) counters[i] = 0;
     float *row = h + (size_t)blockIdx.x * H;
     const uint16_t *src = t == 0 ? embed + (size_t)(ok ? tok : 0) * H : mask;
     float s = 0.f;
@@ -45,66 +42,64 @@ __global__ __launch_bounds__(256) void k_embed(const uint16_t *embed, const uint
         s += v * v;
     }
     s = block_sum_256(s, scratch);
-    if (threadIdx.x == 0) ssq[blockIdx.x] = s;
+    const float inv = rsqrtf(s / (float)H + eps);
+    uint16_t *xr = x + (size_t)blockIdx.x * H;
+    for (int i = threadIdx.x; i < H; i += 256) xr[i] = f32_to_bf16(row[i] * inv * bf16_to_f32(gain[i]));
 }
 
-// ---------------------------------------------------------------- RMSNorm -> bf16
-// With out_lo, the value is also kept as a bf16 pair: out_lo = bf16(v - bf16(v)),
-// so a GEMM over [hi rows; lo rows] sees 16 significant bits of the activation.
-__global__ __launch_bounds__(256) void k_rmsnorm(const float *in, int H, int per, int in_group,
-                                                 int in_off, const uint16_t *gain, float eps,
-                                                 uint16_t *out, uint16_t *out_lo, int ldo) {
+// ---------------------------------------------------------------- reduction + residual + RMSNorm
+// Phase 1, workgroup per (256 columns, output row): the 4 waves sum interleaved subsets
+// of the splits (each lane 4 adjacent columns), combined through LDS in a fixed order,
+// so the result is deterministic.  v (+ f when adding) is stored to f, and the
+// workgroup's sum of v^2 goes to ssq[r][blockIdx.x].
+__global__ __launch_bounds__(256) void k_reduce_rows(const float *part, int splits, int M_out, int N,
+                                                     int pair, int add, float *f, float *ssq) {
+    __shared__ float4 red[4][64];
     __shared__ float scratch[4];
-    const int r = blockIdx.x;
-    const float *x = in + ((size_t)(r / per) * in_group + in_off + r % per) * H;
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += 256) ss += x[i] * x[i];
-    ss = block_sum_256(ss, scratch);
-    const float inv = rsqrtf(ss / (float)H + eps);
-    uint16_t *o = out + (size_t)r * ldo;
-    uint16_t *ol = out_lo ? out_lo + (size_t)r * ldo : nullptr;
-    for (int i = threadIdx.x; i < H; i += 256) {
-        const float v = x[i] * inv * bf16_to_f32(gain[i]);
-        const uint16_t hb = f32_to_bf16(v);
-        o[i] = hb;
-        if (ol) ol[i] = f32_to_bf16(v - bf16_to_f32(hb));
+    const int r = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c0 = blockIdx.x * 256;
+    const size_t stride = (size_t)(pair ? 2 * M_out : M_out) * N;
+    const float *p = part + (size_t)r * N + c0 + 4 * lane;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int k = wave; k < splits; k += 4) {
+        const float4 a = *reinterpret_cast<const float4 *>(p + k * stride);
+        s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
+        if (pair) {
+            const float4 b = *reinterpret_cast<const float4 *>(p + k * stride + (size_t)pair * N);
+            s.x += b.x; s.y += b.y; s.z += b.z; s.w += b.w;
+        }
     }
+    red[wave][lane] = s;
+    __syncthreads();
+    const float *rf = reinterpret_cast<const float *>(red);
+    const int c = tid;                              // column c0 + c: lane c / 4, element c % 4
+    float v = ((rf[c] + rf[256 + c]) + rf[512 + c]) + rf[768 + c];
+    float *fp = f + (size_t)r * N + c0 + c;
+    if (add) v += *fp;
+    *fp = v;
+    const float sq = block_sum_256(v * v, scratch);
+    if (tid == 0) ssq[(size_t)r * gridDim.x + blockIdx.x] = sq;
 }
 
-// ---------------------------------------------------------------- RMSNorm from sums of squares
-// Workgroup (row r, 1024-column chunk): the row's sum of squares is the sum of the
-// producer's per-column-group partials (fixed order), the chunk is scaled by the
-// gain and written as bf16, and optionally its bf16 residual.
-__global__ __launch_bounds__(256) void k_rownorm(const float *in, const float *ssq, int n_groups,
-                                                 int H, int per, int in_group, int in_off,
-                                                 const uint16_t *gain, float eps, uint16_t *out,
-                                                 uint16_t *out_lo, int ldo) {
-    __shared__ float inv_s;
-    const int r = blockIdx.x, tid = threadIdx.x;
-    const int src = (r / per) * in_group + in_off + r % per;
-    if (tid < 64) {
-        float s = 0.f;
-        for (int i = tid; i < n_groups; i += 64) s += ssq[(size_t)src * n_groups + i];
-        s = wave_sum(s);
-        if (tid == 0) inv_s = rsqrtf(s / (float)H + eps);
+// Phase 2, workgroup per (256 columns, output row): out = bf16(v * rsqrt(mean v^2 + eps)
+// * gain) (+ its bf16 residual in out_lo) at output row map(r).
+__global__ __launch_bounds__(256) void k_norm_rows(const float *f, const float *ssq, int nchunk, int N,
+                                                   const uint16_t *gain, float eps, uint16_t *out,
+                                                   uint16_t *out_lo, int ldo, int map) {
+    const int r = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+    int orow = r;
+    if (map == 1) {
+        if (r % 8 == 0) return;
+        orow = (r / 8) * 7 + r % 8 - 1;
     }
-    __syncthreads();
-    const float inv = inv_s;
-    const int k = blockIdx.y * 1024 + tid * 4;
-    if (k >= H) return;
-    const f32x4_t x = *reinterpret_cast<const f32x4_t *>(in + (size_t)src * H + k);
-    const uint32_t g01 = *reinterpret_cast<const uint32_t *>(gain + k);
-    const uint32_t g23 = *reinterpret_cast<const uint32_t *>(gain + k + 2);
-    const float v0 = x.x * inv * bf16_to_f32(g01 & 0xFFFF), v1 = x.y * inv * bf16_to_f32(g01 >> 16);
-    const float v2 = x.z * inv * bf16_to_f32(g23 & 0xFFFF), v3 = x.w * inv * bf16_to_f32(g23 >> 16);
-    const uint32_t h01 = pack_bf16x2(v0, v1), h23 = pack_bf16x2(v2, v3);
-    u32x2_t hv = {h01, h23};
-    *reinterpret_cast<u32x2_t *>(out + (size_t)r * ldo + k) = hv;
-    if (out_lo) {
-        u32x2_t lv = {pack_bf16x2(v0 - bf16_to_f32(h01 & 0xFFFF), v1 - bf16_to_f32(h01 >> 16)),
-                      pack_bf16x2(v2 - bf16_to_f32(h23 & 0xFFFF), v3 - bf16_to_f32(h23 >> 16))};
-        *reinterpret_cast<u32x2_t *>(out_lo + (size_t)r * ldo + k) = lv;
-    }
+    float ss = 0.f;
+    for (int i = 0; i < nchunk; i++) ss += ssq[(size_t)r * nchunk + i];
+    const float inv = rsqrtf(ss / (float)N + eps);
+    const float x = f[(size_t)r * N + c] * inv * bf16_to_f32(gain[c]);
+    const uint16_t hb = f32_to_bf16(x);
+    out[(size_t)orow * ldo + c] = hb;
+    if (out_lo) out_lo[(size_t)orow * ldo + c] = f32_to_bf16(x - bf16_to_f32(hb));
 }
 
 // ---------------------------------------------------------------- split-K reduction
@@ -164,8 +159,13 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
     const bool is_q = hh < a.n_q, is_k = !is_q && hh < a.n_q + a.n_kv;
     if (is_q && !is_blk) return;                      // context rows need K and V only
     const float *x = a.qkv + (size_t)r * (qd + 2 * kd) + (size_t)hh * d;
+    const size_t pstride = (size_t)a.B * (a.T + a.t_new) * (qd + 2 * kd);
     float x1 = 0.f, x2 = 0.f;
-    if (lane < half) { x1 = x[lane]; x2 = x[lane + half]; }
+    if (lane < half)
+        for (int s = 0; s < a.splits; s++) {
+            x1 += x[s * pstride + lane];
+            x2 += x[s * pstride + lane + half];
+        }
     if (is_q || is_k) {
         const uint16_t *g = is_q ? a.q_norm : a.k_norm;
         const float ss = wave_sum(x1 * x1 + x2 * x2);
@@ -321,18 +321,10 @@ __global__ __launch_bounds__(256) void k_conv_apply(MergeConvArgs a) {
 
 hipError_t launch_embed(const uint16_t *embed, const uint16_t *mask_emb, const int32_t *last,
                         const int32_t *ctx_len, int B, int T, int H, int V, int t_new, int cap,
-                        float *h, float *ssq, int32_t *valid, int *counters, int n_counters,
+                        float *h, const uint16_t *gain, float eps, uint16_t *x, int32_t *valid,
                         hipStream_t st) {
     hipLaunchKernelGGL(k_embed, dim3(B * T), dim3(256), 0, st, embed, mask_emb, last, ctx_len, T, H,
-                       V, t_new, cap, h, ssq, valid, counters, n_counters);
-    return hipGetLastError();
-}
-
-hipError_t launch_rmsnorm(const float *in, int R, int H, int per, int in_group, int in_off,
-                          const uint16_t *gain, float eps, uint16_t *out, uint16_t *out_lo,
-                          int ldo, hipStream_t st) {
-    hipLaunchKernelGGL(k_rmsnorm, dim3(R), dim3(256), 0, st, in, H, per, in_group, in_off, gain,
-                       eps, out, out_lo, ldo);
+                       V, t_new, cap, h, gain, eps, x, valid);
     return hipGetLastError();
 }
 
@@ -362,11 +354,14 @@ hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_rownorm(const float *in, const float *ssq, int n_groups, int R, int H, int per,
-                          int in_group, int in_off, const uint16_t *gain, float eps, uint16_t *out,
-                          uint16_t *out_lo, int ldo, hipStream_t st) {
-    dim3 grid(R, ceil_div(H, 1024));
-    hipLaunchKernelGGL(k_rownorm, grid, dim3(256), 0, st, in, ssq, n_groups, H, per, in_group,
-                       in_off, gain, eps, out, out_lo, ldo);
+hipError_t launch_reduce_norm(const float *part, int splits, int M_out, int N, int pair, int add,
+                              float *f, float *ssq, const uint16_t *gain, float eps, uint16_t *out,
+                              uint16_t *out_lo, int ldo, int map, hipStream_t st) {
+    const dim3 grid(N / 256, M_out);
+    hipLaunchKernelGGL(k_reduce_rows, grid, dim3(256), 0, st, part, splits, M_out, N, pair, add, f,
+                       ssq);
+    if (out)
+        hipLaunchKernelGGL(k_norm_rows, grid, dim3(256), 0, st, f, ssq, N / 256, N, gain, eps, out,
+                           out_lo, ldo, map);
     return hipGetLastError();
 }

@@ -1,4 +1,4 @@
-// Q4_K dequantize-fused GEMM with fused input normalisation and split-K fixup, gfx950.
+// Q4_K dequantize-fused GEMM (split-K partials), gfx950.
 //
 // Format (FastFlowLM card "Qwen3.8-27B-DFlash2-NPU2", "Weights" row: the draft's fc,
 // q/k/v/o and MLP matrices in Q4_K): 144-byte super-blocks of 256 weights along K,
@@ -18,10 +18,9 @@
 // in LDS in MFMA lane order with their per-sub-block sums.  Each wave streams STEPS
 // (column tile, super-block) pairs
 // from HBM with 4 super-blocks in flight, in a fully unrolled loop (no branch, so
-// the loads stay in flight).  Partials go to [split][M][N]; the last workgroup to
-// finish a column group (device-scope counter) sums them in split order -- so the
-// result does not depend on scheduling -- and applies the epilogue: store, residual
-// add with the new rows' sums of squares, or SwiGLU into bf16 (hi, lo).
+// the loads stay in flight).  Partials go to [split][M][N]; a reduction kernel sums
+// them in split order (deterministic) and applies the epilogue.  Workgroups never
+// communicate, so no device-scope fence (an L2 write-back on this chip) is needed.
 #include "common.h"
 #include "kernels.h"
 
@@ -81,7 +80,6 @@ void k_q4k_fused(Q4kFusedArgs a) {
     constexpr int PD = STEPS < PD_MAX ? STEPS : PD_MAX;
     constexpr int MAXA = 2 * NSB * RT;               // staged fragments per thread
     extern __shared__ __align__(16) unsigned char lds[];
-    __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, cl = lane & 15;
     const int split = blockIdx.y;
@@ -92,9 +90,7 @@ void k_q4k_fused(Q4kFusedArgs a) {
     const int ntile = a.N / 16;
 
     // ---- column tiles of this wave and their weight rows
-    int tile0;
-    if (a.paired) tile0 = (wave < 2 ? 0 : ntile / 2) + blockIdx.x * 2 * CT + (wave & 1) * CT;
-    else tile0 = blockIdx.x * 4 * CT + wave * CT;
+    const int tile0 = blockIdx.x * 4 * CT + wave * CT;
     const unsigned char *wrow[CT];
 #pragma unroll
     for (int ti = 0; ti < CT; ti++) {
@@ -242,8 +238,7 @@ void k_q4k_fused(Q4kFusedArgs a) {
 #pragma unroll
     for (int ti = 0; ti < CT; ti++) {
         const int tile = tile0 + ti;
-        const bool tok = a.paired ? true : tile < ntile;
-        if (!tok) continue;
+        if (tile >= ntile) continue;
         const int n = tile * 16 + cl;
 #pragma unroll
         for (int rt = 0; rt < RT; rt++) {
@@ -256,79 +251,11 @@ void k_q4k_fused(Q4kFusedArgs a) {
         }
     }
 
-    // ---- 6) the last workgroup of this column group reduces and applies the epilogue
-    __syncthreads();
-    if (tid == 0) {
-        __threadfence();
-        const int arrivals = (int)(gridDim.y * gridDim.z);
-        const int prev = atomicAdd(&a.counters[blockIdx.x], 1);
-        const int last = prev == arrivals - 1;
-        if (last) a.counters[blockIdx.x] = 0;
-        s_last = last;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
-    const int splits = (int)gridDim.y;
-    const size_t pstride = (size_t)a.M * a.N;
-    const Q4kOut &o = a.out;
-    if (a.paired) {
-        // SwiGLU over this group's gate columns; up columns sit N/2 further
-        const int half = a.N / 2;
-        const int ncols = 2 * CT * 16;
-        const int c0 = blockIdx.x * ncols;
-        for (int e = tid; e < o.M_out * ncols; e += 256) {
-            const int r = e / ncols, c = c0 + e % ncols;
-            float gsum = 0.f, usum = 0.f;
-            for (int s = 0; s < splits; s++) {
-                const float *p = a.part + s * pstride;
-                gsum += p[(size_t)r * a.N + c] + (o.pair ? p[(size_t)(r + o.pair) * a.N + c] : 0.f);
-                usum += p[(size_t)r * a.N + half + c] +
-                        (o.pair ? p[(size_t)(r + o.pair) * a.N + half + c] : 0.f);
-            }
-            const float v = gsum / (1.f + expf(-gsum)) * usum;
-            const uint16_t hb = f32_to_bf16(v);
-            o.b[(size_t)r * o.ldo + c] = hb;
-            if (o.b_lo) o.b_lo[(size_t)r * o.ldo + c] = f32_to_bf16(v - bf16_to_f32(hb));
-        }
-        return;
-    }
-    const int ncols = 4 * CT * 16;
-    const int c0 = blockIdx.x * ncols;
-    for (int r = wave; r < o.M_out; r += 4) {
-        float sq = 0.f;
-        for (int cc = lane; cc < ncols; cc += 64) {
-            const int c = c0 + cc;
-            if (c >= a.N) continue;
-            float v = 0.f;
-            for (int s = 0; s < splits; s++) {
-                const float *p = a.part + s * pstride;
-                v += p[(size_t)r * a.N + c] + (o.pair ? p[(size_t)(r + o.pair) * a.N + c] : 0.f);
-            }
-            if (o.mode == EPI_STORE_F32) {
-                o.f[(size_t)r * o.ldo + c] = v;
-            } else if (o.mode == EPI_ADD_F32) {
-                v += o.f[(size_t)r * o.ldo + c];
-                o.f[(size_t)r * o.ldo + c] = v;
-            } else {
-                o.b[(size_t)r * o.ldo + c] = f32_to_bf16(v);
-            }
-            sq += v * v;
-        }
-        sq = wave_sum(sq);
-        if (o.ssq && lane == 0) o.ssq[(size_t)r * gridDim.x + blockIdx.x] = sq;
-    }
-}
-
-__global__ void k_zero_i32(int *p, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0;
 }
 
 }  // namespace
 
-Q4kFusedPlan q4k_fused_plan(int M, int N, int K, int paired) {
+Q4kFusedPlan q4k_fused_plan(int M, int N, int K) {
     Q4kFusedPlan p;
     const int KB = K / 256;
     const int rt_total = ceil_div(M, 16);
@@ -346,7 +273,7 @@ Q4kFusedPlan q4k_fused_plan(int M, int N, int K, int paired) {
     if (p.steps < p.nsb) p.steps = p.nsb;
     p.ct = p.steps / p.nsb;
     p.splits = KB / p.nsb;
-    p.grid_x = paired ? (tiles / 2) / (2 * p.ct) : ceil_div(tiles, 4 * p.ct);
+    p.grid_x = ceil_div(tiles, 4 * p.ct);
     p.lds_bytes = (size_t)p.nsb * p.rt * (8 * 1088 + 1024);
     p.part_bytes = (size_t)p.splits * M * N * 4;
     return p;
@@ -370,7 +297,3 @@ hipError_t launch_q4k_fused(const Q4kFusedArgs &a, const Q4kFusedPlan &p, hipStr
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_zero_i32(int *p, int n, hipStream_t st) {
-    hipLaunchKernelGGL(k_zero_i32, dim3(ceil_div(n, 256)), dim3(256), 0, st, p, n);
-    return hipGetLastError();
-}
