@@ -1,0 +1,149 @@
+"""Summaries of rocprofv3 CSV output (``-f csv``) for the committed profiles.
+
+    python -m block_diffusion_draft_amd.rocprof_summary stats DIR
+        per-kernel statistics (``*kernel_stats.csv``).
+    python -m block_diffusion_draft_amd.rocprof_summary trace DIR [PATTERN]
+        per (kernel, grid) average durations from ``*kernel_trace.csv``.
+    python -m block_diffusion_draft_amd.rocprof_summary traffic --fetch DIR --write DIR
+            --kernel PATTERN --copy-bytes N [--out FILE]
+        HBM bytes per launch of the kernels matching PATTERN from a FETCH_SIZE run and
+        a WRITE_SIZE run, each counter scaled by what it reads for a plain device copy
+        of N bytes in the same run (N bytes fetched, N written): the mean over the
+        --copies largest copy-kernel dispatches.
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import re
+import statistics
+import sys
+
+
+def _find(d, suffix):
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits
+
+
+def _rows(d, suffix):
+    out = []
+    for p in _find(d, suffix):
+        with open(p, newline="") as f:
+            out.extend(csv.DictReader(f))
+    return out
+
+
+def short(name, n=64):
+    name = name.replace("(anonymous namespace)::", "")
+    name = re.sub(r"^void ", "", name)
+    name = re.sub(r"\(.*$", "", name)
+    return name if len(name) <= n else name[:n - 3] + "..."
+
+
+def stats(d, out=sys.stdout):
+    rows = _rows(d, "kernel_stats.csv")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out.write(f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} "
+              f"{'total_us':>10s} {'pct':>6s}\n")
+    for r in rows:
+        out.write(f"{short(r['Name']):64s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.1f} "
+                  f"{float(r['MinNs']) / 1e3:9.1f} {float(r['MaxNs']) / 1e3:9.1f} "
+                  f"{float(r['TotalDurationNs']) / 1e3:10.1f} {float(r['Percentage']):6.1f}\n")
+
+
+def trace(d, pattern="", out=sys.stdout):
+    rows = _rows(d, "kernel_trace.csv")
+    agg = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if pattern and not re.search(pattern, name):
+            continue
+        grid = (r.get("Grid_Size_X") or r.get("Grid_Size", ""), r.get("Grid_Size_Y", ""),
+                r.get("Grid_Size_Z", ""))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        agg.setdefault((short(name, 56), grid), []).append(dur)
+    out.write(f"{'kernel':56s} {'grid (threads)':>24s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s}\n")
+    for (n, g), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        gs = "x".join(x for x in g if x)
+        out.write(f"{n:56s} {gs:>24s} {len(v):6d} {sum(v) / len(v):9.1f} "
+                  f"{statistics.median(v):9.1f}\n")
+
+
+def _counter(d, name, kernel_pat):
+    """{kernel dispatch -> counter value} for kernels matching kernel_pat."""
+    vals = {}
+    grids = {}
+    for r in _rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] != name or not re.search(kernel_pat, r["Kernel_Name"]):
+            continue
+        key = r["Dispatch_Id"]
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        grids[key] = int(r.get("Grid_Size") or 0)
+    return vals, grids
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic(fetch_dir, write_dir, kernel, copy_bytes, copies=3, copy_pat="copyBuffer"):
+    res = {}
+    for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        k, _ = _counter(d, cname, kernel)
+        c, _ = _counter(d, cname, copy_pat)
+        if not k or len(c) < copies:
+            raise SystemExit(f"{cname}: no dispatches of {kernel!r} or too few copy dispatches")
+        cv = sorted(c.values())[-copies:]
+        kib_per_copy = sum(cv) / len(cv)
+        scale = copy_bytes / (kib_per_copy * 1024.0)
+        kv = list(k.values())
+        res[cname] = dict(kib_per_launch=sum(kv) / len(kv), launches=len(kv),
+                          copy_kib=kib_per_copy, copies=len(cv), scale=scale,
+                          bytes_per_launch=sum(kv) / len(kv) * 1024.0 * scale)
+    res["hbm_bytes_per_launch"] = res["FETCH_SIZE"]["bytes_per_launch"] + \
+        res["WRITE_SIZE"]["bytes_per_launch"]
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats"); a.add_argument("dir")
+    a = sub.add_parser("trace"); a.add_argument("dir"); a.add_argument("pattern", nargs="?", default="")
+    a = sub.add_parser("traffic")
+    a.add_argument("--fetch", required=True); a.add_argument("--write", required=True)
+    a.add_argument("--kernel", required=True); a.add_argument("--copy-bytes", type=int, required=True)
+    a.add_argument("--copies", type=int, default=3)
+    a.add_argument("--source", nargs="*", default=[], help="kernel sources to fingerprint")
+    a.add_argument("--out")
+    args = ap.parse_args()
+    if args.cmd == "stats":
+        stats(args.dir)
+    elif args.cmd == "trace":
+        trace(args.dir, args.pattern)
+    else:
+        r = traffic(args.fetch, args.write, args.kernel, args.copy_bytes, args.copies)
+        lines = [f"kernel_pattern {args.kernel}",
+                 f"hbm_bytes_per_launch {r['hbm_bytes_per_launch']:.0f}"]
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            x = r[c]
+            lines.append(f"{c.lower()}_kib_per_launch {x['kib_per_launch']:.1f} launches {x['launches']}")
+            lines.append(f"{c.lower()}_copy_kib {x['copy_kib']:.1f} copies {x['copies']} "
+                         f"copy_bytes {args.copy_bytes} scale {x['scale']:.4f}")
+        if args.source:
+            lines.append(f"kernel_source_sha256_16 {source_hash(args.source)}")
+        text = "\n".join(lines) + "\n"
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        sys.stdout.write(text)
+
+
+if __name__ == "__main__":
+    main()
