@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdflash.so")
-SOURCES = ["api.hip", "q4k_dequant.hip", "q4k_fused.hip", "gemm_bf16.hip", "layer_ops.hip", "attention.hip",
+SOURCES = ["api.hip", "q4k_dequant.hip", "q4k_fused.hip", "q4k_stream.hip", "gemm_bf16.hip", "layer_ops.hip", "attention.hip",
            "topk.hip", "select.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -20,9 +20,13 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Wno-unused-result"]
 
 
+# per-file extras: MFMA results in VGPRs (no accumulator-register round trips)
+EXTRA = {"q4k_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -25,7 +25,9 @@ struct Plan {
 
 // fp32 partial sums of one GEMM: [splits][M][N] (Q4_K split-K) or [M][N] (bf16)
 size_t gemm_part_bytes(int fmt, int M, int N, int K) {
-    if (fmt == DFLASH_W_Q4K) return q4k_fused_plan(M, N, K).part_bytes;
+    if (fmt == DFLASH_W_Q4K)
+        return q4k_stream_ok(M, N, K) ? q4k_stream_plan(M, N, K).part_bytes
+                                      : q4k_fused_plan(M, N, K).part_bytes;
     return (size_t)M * N * 4;
 }
 
@@ -137,6 +139,20 @@ struct Ctx {
     template <class T> T *at(size_t off) const { return reinterpret_cast<T *>(ws + off); }
 };
 
+// Q4_K product into partials: the streaming kernel for up to 16 rows, else the tiled
+// one.  Returns the number of splits or a negative status.
+int run_q4k(const Q4kFusedArgs &a, hipStream_t st) {
+    const int K = a.KB * 256;
+    if (q4k_stream_ok(a.M, a.N, K)) {
+        const Q4kStreamPlan p = q4k_stream_plan(a.M, a.N, K);
+        HIPCHK(launch_q4k_stream(a, p, st));
+        return p.splits;
+    }
+    const Q4kFusedPlan p = q4k_fused_plan(a.M, a.N, K);
+    HIPCHK(launch_q4k_fused(a, p, st));
+    return p.splits;
+}
+
 // y = A . W^T over up to 3 weight matrices stacked along N, as fp32 partial sums in
 // the workspace's partial buffer: Q4_K -> [splits][M][N] from the dequantize-fused
 // MFMA kernel; bf16 -> [M][N] (one split) from the tiled MFMA kernel.  Returns the
@@ -163,9 +179,7 @@ int run_gemm(const Ctx &x, const void *const *w, const int *seg_n, int nseg, con
         a.src.A = A;
         a.src.lda = lda;
         a.part = part;
-        const Q4kFusedPlan p = q4k_fused_plan(M, N, K);
-        HIPCHK(launch_q4k_fused(a, p, x.st));
-        return p.splits;
+        return run_q4k(a, x.st);
     }
     Bf16GemmArgs a = {};
     for (int i = 0; i < 3; i++) {
@@ -405,7 +419,6 @@ int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
     const size_t need = q4k_gemm_workspace_bytes(M, N, K);
     if (!workspace || ws_bytes < need || !aligned16(workspace)) return DFLASH_EWORKSPACE;
     const hipStream_t st = (hipStream_t)stream;
-    const Q4kFusedPlan p = q4k_fused_plan(M, N, K);
     Q4kFusedArgs a;
     a.w[0] = a.w[1] = a.w[2] = (const unsigned char *)w;
     a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = N;
@@ -414,8 +427,9 @@ int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
     a.src.A = x;
     a.src.lda = K;
     a.part = (float *)workspace;
-    HIPCHK(launch_q4k_fused(a, p, st));
-    HIPCHK(launch_reduce_epilogue(a.part, p.splits, M, N, 0, EPI_STORE_BF16, nullptr, y, nullptr, N,
+    const int splits = run_q4k(a, st);
+    if (splits < 0) return splits;
+    HIPCHK(launch_reduce_epilogue(a.part, splits, M, N, 0, EPI_STORE_BF16, nullptr, y, nullptr, N,
                                   st));
     return DFLASH_OK;
 }

@@ -111,6 +111,16 @@ struct Q4kFusedPlan {
 Q4kFusedPlan q4k_fused_plan(int M, int N, int K);
 hipError_t launch_q4k_fused(const Q4kFusedArgs &a, const Q4kFusedPlan &p, hipStream_t st);
 
+// Streaming variant for M <= 16 rows and K/256 a multiple of 4: splits of 4 super-blocks,
+// each wave streams tpw consecutive column tiles.  Same partial layout [splits][M][N].
+struct Q4kStreamPlan {
+    int splits, tpw, grid_x;
+    size_t lds_bytes, part_bytes;
+};
+bool q4k_stream_ok(int M, int N, int K);
+Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves = 2048);
+hipError_t launch_q4k_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st);
+
 // Output rows r < M_out: v = sum over splits of partial rows r (+ r + pair), N a multiple
 // of 256; add ? f[r] += v : f[r] = v (fp32), with per-256-column sums of squares in
 // ssq [M_out][N/256].  Then, if out: the row's RMSNorm * gain as bf16 (and its residual

@@ -1,0 +1,238 @@
+// Q4_K dequantize-fused GEMM for at most 16 activation rows (one draft block of 8 rows,
+// or its bf16 hi/lo pair), gfx950.  Split-K partials [split][M][N].
+//
+// Format (FastFlowLM card "Qwen3.8-27B-DFlash2-NPU2", "Weights" row: the draft's fc,
+// q/k/v/o and MLP matrices in Q4_K): 144-byte super-blocks of 256 weights along K,
+// w = d * sc_j * q - dmin * m_j for sub-block j (32 weights), q in 0..15.
+//
+// Arithmetic, per output column n, row r and super-block:
+//     sum_k x_rk w_k = d (sum_j sc_j sum_k x_rk q_k) - dmin sum_j m_j S_rj,
+//     S_rj = sum of x_rk over sub-block j.
+//  * A nibble q enters a bf16 MFMA as the value 128 + q (bytes 0x43, q: one byte
+//    permute per two weights), so D_j = sum_k x_rk (128 + q_k) with fp32 accumulation;
+//  * T = sum_j sc_j D_j takes 4 FMAs per sub-block and lane;
+//  * sum_j sc_j S_rj and sum_j m_j S_rj are two more MFMAs per super-block whose A
+//    operand holds each fp32 S_rj as four bf16 terms summing to it exactly and whose B
+//    operand holds the 6-bit sc_j or m_j (exact in bf16);
+//  * the super-block adds d (T - 128 sum_j sc_j S_rj) - dmin sum_j m_j S_rj.
+//
+// Work split: a workgroup (4 waves) owns one split of 4 super-blocks (1024 values of
+// K) and 4 runs of tpw consecutive 16-column tiles, one run per wave.  The split's
+// activation rows are staged once in LDS in MFMA lane order, with the bias operand.
+// Each wave then streams its tiles' super-blocks from HBM as one flat sequence of
+// (tile, super-block) stages, 4 stages in flight, in a branch-free loop (loads past
+// the end are clamped to the last stage, in bounds and unused), so the loads stay in
+// flight across tiles.  Each tile's 16 x M partial is stored when its 4 super-blocks
+// are done.  Workgroups never communicate; a reduction kernel sums the splits.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int SNSB = 4;        // super-blocks per split
+constexpr int SPD = 4;         // stages in flight per wave (divides SNSB)
+
+struct SStage {
+    u32x4_t hdr;               // d, dmin, 12 scale bytes (same for the 4 lane groups)
+    u32x2_t q[4];              // 8 nibble bytes of each 32-byte chunk, lane group g
+};
+
+__device__ __forceinline__ SStage s_load(const unsigned char *blk, int g) {
+    SStage s;
+    s.hdr = *reinterpret_cast<const u32x4_t *>(blk);
+#pragma unroll
+    for (int c = 0; c < 4; c++) s.q[c] = *reinterpret_cast<const u32x2_t *>(blk + 16 + 32 * c + 8 * g);
+    return s;
+}
+
+// 8 quant bytes -> bf16 (128 + q) operands, natural k order: low nibbles (first
+// sub-block of the chunk) and high nibbles (second sub-block)
+__device__ __forceinline__ void s_decode(u32x2_t q, u32x4_t &lo, u32x4_t &hi) {
+    const uint32_t C = 0x43434343u;
+    const uint32_t lx = q.x & 0x0F0F0F0Fu, ly = q.y & 0x0F0F0F0Fu;
+    const uint32_t hx = (q.x >> 4) & 0x0F0F0F0Fu, hy = (q.y >> 4) & 0x0F0F0F0Fu;
+    // byte selectors: {q0, 0x43, q1, 0x43} and {q2, 0x43, q3, 0x43}
+    lo.x = __builtin_amdgcn_perm(C, lx, 0x04010400u);
+    lo.y = __builtin_amdgcn_perm(C, lx, 0x04030402u);
+    lo.z = __builtin_amdgcn_perm(C, ly, 0x04010400u);
+    lo.w = __builtin_amdgcn_perm(C, ly, 0x04030402u);
+    hi.x = __builtin_amdgcn_perm(C, hx, 0x04010400u);
+    hi.y = __builtin_amdgcn_perm(C, hx, 0x04030402u);
+    hi.z = __builtin_amdgcn_perm(C, hy, 0x04010400u);
+    hi.w = __builtin_amdgcn_perm(C, hy, 0x04030402u);
+}
+
+// bf16 of the small non-negative integer in byte k of w, in both halves
+__device__ __forceinline__ uint32_t byte_bf16x2(uint32_t w, int k) {
+    const uint32_t fb = __float_as_uint((float)((w >> (8 * k)) & 0xFF));
+    return (fb >> 16) | (fb & 0xFFFF0000u);
+}
+
+__global__ __launch_bounds__(256) void k_q4k_stream(Q4kFusedArgs a, int tpw) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    u32x4_t *A_lds = reinterpret_cast<u32x4_t *>(lds);              // [SNSB][8][64]
+    u32x4_t *B_lds = A_lds + SNSB * 8 * 64;                          // [SNSB][64]
+    float *S_lds = reinterpret_cast<float *>(B_lds + SNSB * 64);     // [SNSB][8][16]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+    const int g = lane >> 4, cl = lane & 15;
+    const int split = blockIdx.y, sb0 = split * SNSB;
+    const int ntile = a.N / 16;
+    const int t0 = (blockIdx.x * 4 + wave) * tpw;
+    const int t1 = min(t0 + tpw, ntile);
+    const int nst = t1 > t0 ? (t1 - t0) * SNSB : 0;
+    const int tlast = (t1 > t0 ? t1 : ntile) - 1;       // clamp target, always a real tile
+
+    // ---- weight stream: (tile, super-block) stages in order, clamped past the end.
+    // The stage address is a wave-uniform base (scalar registers) plus a per-lane
+    // offset that never changes: column cl's row and lane group g's 8 bytes.
+    const int row_bytes = a.KB * 144;
+    const int lane_off = cl * row_bytes + sb0 * 144;
+    int lt = t0, lsb = 0, nload = 0;
+    auto load_next = [&]() -> SStage {
+        const bool ok = nload < nst;
+        const int tt = ok ? lt : tlast, sbb = ok ? lsb : SNSB - 1;
+        const int c16 = tt * 16;
+        const int si = (a.nseg > 1 && c16 >= a.seg_end[0]) + (a.nseg > 2 && c16 >= a.seg_end[1]);
+        const unsigned char *wseg = si == 0 ? a.w[0] : (si == 1 ? a.w[1] : a.w[2]);
+        const int nbase = si == 0 ? 0 : (si == 1 ? a.seg_end[0] : a.seg_end[1]);
+        const unsigned char *ubase = wseg + (size_t)(c16 - nbase) * row_bytes + sbb * 144;
+        nload++;
+        lsb++;
+        const bool wrap = lsb == SNSB;
+        lsb = wrap ? 0 : lsb;
+        lt += wrap ? 1 : 0;
+        return s_load(ubase + lane_off, g);
+    };
+    SStage st[SPD];
+#pragma unroll
+    for (int u = 0; u < SPD - 1; u++) st[u] = load_next();
+
+    // ---- activations of this split -> LDS (lane order), sub-block sums S
+    constexpr int PER = SNSB * 8 * 64 / 256;
+    u32x4_t av[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int e = tid + 256 * i;
+        const int ln = e & 63, rest = e >> 6;
+        const int j = rest & 7, sbi = rest >> 3;
+        const int R = ln & 15;
+        const int Rc = min(R, a.M - 1);
+        const size_t k = (size_t)(sb0 + sbi) * 256 + 32 * j + 8 * (ln >> 4);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(a.src.A + (size_t)Rc * a.src.lda + k);
+        av[i] = R < a.M ? v : (u32x4_t){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int e = tid + 256 * i;
+        const int ln = e & 63, rest = e >> 6;
+        const u32x4_t v = av[i];
+        float s = 0.f;
+        s += bf16_to_f32(v.x & 0xFFFF) + bf16_to_f32(v.x >> 16);
+        s += bf16_to_f32(v.y & 0xFFFF) + bf16_to_f32(v.y >> 16);
+        s += bf16_to_f32(v.z & 0xFFFF) + bf16_to_f32(v.z >> 16);
+        s += bf16_to_f32(v.w & 0xFFFF) + bf16_to_f32(v.w >> 16);
+        s += __shfl_xor(s, 16, WAVE);
+        s += __shfl_xor(s, 32, WAVE);
+        A_lds[e] = v;
+        if ((ln >> 4) == 0) S_lds[rest * 16 + (ln & 15)] = s;
+    }
+    __syncthreads();
+    // bias operand: lane (row r, group gg) holds S_j for j = 2 gg, 2 gg + 1 as four bf16
+    // terms each (8 + 8 + 8 + 8 bits >= the 24 of an fp32 significand: exact)
+    {
+        const int sbi = tid >> 6, ln = tid & 63;
+        const int r = ln & 15, gg = ln >> 4;
+        uint32_t o[4];
+#pragma unroll
+        for (int jj = 0; jj < 2; jj++) {
+            float rem = S_lds[(sbi * 8 + 2 * gg + jj) * 16 + r];
+            uint16_t t[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                t[q] = f32_to_bf16(rem);
+                rem -= bf16_to_f32(t[q]);
+            }
+            o[2 * jj] = (uint32_t)t[0] | ((uint32_t)t[1] << 16);
+            o[2 * jj + 1] = (uint32_t)t[2] | ((uint32_t)t[3] << 16);
+        }
+        B_lds[tid] = (u32x4_t){o[0], o[1], o[2], o[3]};
+    }
+    __syncthreads();
+
+    // ---- stream
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    float *part = a.part + (size_t)split * a.M * a.N;
+    int a_off = lane, b_off = lane;
+    for (int t = t0; t < t1; t++) {
+        // opaque to the compiler: keeps the 32 activation fragments in LDS instead of
+        // hoisting them into registers (which would halve the waves per SIMD)
+        asm volatile("" : "+v"(a_off), "+v"(b_off));
+        f32x4_t acc = zero;
+#pragma unroll
+        for (int sb = 0; sb < SNSB; sb++) {
+            st[(sb + SPD - 1) % SPD] = load_next();
+            const SStage &w = st[sb % SPD];
+            const float d = half_bits_to_f32(w.hdr.x & 0xFFFF);
+            const float dmin = half_bits_to_f32(w.hdr.x >> 16);
+            const uint32_t s0w = w.hdr.y, s1w = w.hdr.z, s2w = w.hdr.w;
+            const uint32_t sc_lo = s0w & 0x3F3F3F3Fu;
+            const uint32_t m_lo = s1w & 0x3F3F3F3Fu;
+            const uint32_t sc_hi = (s2w & 0x0F0F0F0Fu) | ((s0w >> 2) & 0x30303030u);
+            const uint32_t m_hi = ((s2w >> 4) & 0x0F0F0F0Fu) | ((s1w >> 2) & 0x30303030u);
+            f32x4_t tacc = zero;
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                u32x4_t blo, bhi;
+                s_decode(w.q[c], blo, bhi);
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const int j = 2 * c + h;
+                    const uint32_t scw = j < 4 ? sc_lo : sc_hi;
+                    const float sc = (float)((scw >> (8 * (j & 3))) & 0xFF);
+                    const f32x4_t D = mfma16x16x32(A_lds[(sb * 8 + j) * 64 + a_off], h ? bhi : blo, zero);
+                    tacc += sc * D;
+                }
+            }
+            // B slots of lane group g: {m_2g x4, m_2g+1 x4} and the same for sc
+            const uint32_t mw = g < 2 ? m_lo : m_hi, sw = g < 2 ? sc_lo : sc_hi;
+            const int k0 = (2 * g) & 3, k1 = (2 * g + 1) & 3;
+            const uint32_t m0 = byte_bf16x2(mw, k0), m1 = byte_bf16x2(mw, k1);
+            const uint32_t c0 = byte_bf16x2(sw, k0), c1 = byte_bf16x2(sw, k1);
+            const u32x4_t ab = B_lds[sb * 64 + b_off];
+            const f32x4_t Dm = mfma16x16x32(ab, (u32x4_t){m0, m0, m1, m1}, zero);
+            const f32x4_t Ds = mfma16x16x32(ab, (u32x4_t){c0, c0, c1, c1}, zero);
+            acc += d * (tacc - 128.f * Ds) - dmin * Dm;
+        }
+        const int n = t * 16 + cl;
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int R = 4 * g + v;
+            if (R < a.M) part[(size_t)R * a.N + n] = acc[v];
+        }
+    }
+}
+
+}  // namespace
+
+bool q4k_stream_ok(int M, int N, int K) { return M >= 1 && M <= 16 && (K / 256) % SNSB == 0 && N % 16 == 0; }
+
+Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves) {
+    Q4kStreamPlan p;
+    const int KB = K / 256, ntile = N / 16;
+    p.splits = KB / SNSB;
+    const long long wave_tiles = (long long)ntile * p.splits;
+    int tpw = (int)((wave_tiles + target_waves - 1) / target_waves);
+    if (tpw < 1) tpw = 1;
+    p.tpw = tpw;
+    p.grid_x = ceil_div(ceil_div(ntile, tpw), 4);
+    p.lds_bytes = (size_t)SNSB * 8 * 64 * 16 + SNSB * 64 * 16 + SNSB * 8 * 16 * 4;
+    p.part_bytes = (size_t)p.splits * M * N * 4;
+    return p;
+}
+
+hipError_t launch_q4k_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st) {
+    hipLaunchKernelGGL(k_q4k_stream, dim3(p.grid_x, p.splits), dim3(256), p.lds_bytes, st, a, p.tpw);
+    return hipGetLastError();
+}
