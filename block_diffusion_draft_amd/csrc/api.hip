@@ -19,7 +19,7 @@ struct Plan {
     bool lm_skinny;
     // byte offsets into the workspace
     size_t o_valid, o_h, o_xc, o_u2, o_fcout, o_Q, o_Kb, o_Vb, o_attnO, o_attnML, o_o, o_zp,
-        o_Y, o_mid2, o_f, o_logits, o_pv, o_pi, o_pm, o_ps, o_ssq, o_part;
+        o_Y, o_mid2, o_f, o_logits, o_topk, o_ssq_x, o_ssq_c, o_ssq_u, o_part;
     size_t total;
 };
 
@@ -87,16 +87,15 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
     p.o_attnO = take(nslots * p.d * 4);
     p.o_attnML = take(nslots * 2 * 4);
     p.o_o = take((size_t)p.M_blk * p.qd * 4);
-    p.o_zp = take((size_t)B * p.n_q * p.T * 2 * p.n_q * 4);
+    p.o_zp = take((size_t)B * p.n_q * (p.d / 32) * p.T * 2 * p.n_q * 4);
     p.o_Y = take((size_t)p.M_blk * p.qd * 2);
     p.o_mid2 = take((size_t)2 * p.M_blk * p.F * 2);
     p.o_f = take((size_t)p.R * p.H * 2);
     p.o_logits = take((size_t)p.R * p.V * 4);
-    p.o_pv = take((size_t)p.R * p.topk_nch * p.K * 4);
-    p.o_pi = take((size_t)p.R * p.topk_nch * p.K * 4);
-    p.o_pm = take((size_t)p.R * p.topk_nch * 4);
-    p.o_ps = take((size_t)p.R * p.topk_nch * 4);
-    p.o_ssq = take((size_t)p.M_blk * (p.H / 256) * 4);
+    p.o_topk = take(topk_workspace_floats(p.R, p.V) * 4);
+    p.o_ssq_x = take((size_t)p.M_blk * (p.H / 256) * 4);
+    p.o_ssq_c = take((size_t)p.M_ctx * (p.H / 256) * 4);
+    p.o_ssq_u = take((size_t)p.M_blk * (p.H / 256) * 4);
     p.o_part = take(part);
     p.total = o;
     return true;
@@ -107,10 +106,11 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 int check_config(const dflash_config *c) {
     if (!c) return DFLASH_EINVAL;
     if (c->n_layers < 1 || c->n_layers > DFLASH_MAX_LAYERS) return DFLASH_ESHAPE;
-    if (c->hidden <= 0 || c->hidden % 256 || c->ffn <= 0 || c->ffn % 256) return DFLASH_ESHAPE;
+    if (c->hidden <= 0 || c->hidden % 256 || c->hidden > 8192 || c->ffn <= 0 || c->ffn % 256)
+        return DFLASH_ESHAPE;
     if (c->head_dim != 64 && c->head_dim != 128) return DFLASH_ESHAPE;
     if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->n_q_heads % c->n_kv_heads) return DFLASH_ESHAPE;
-    if (c->n_q_heads / c->n_kv_heads > 4) return DFLASH_ESHAPE;
+    if (c->n_q_heads / c->n_kv_heads > 4 || c->n_q_heads % 2) return DFLASH_ESHAPE;
     const int qd = c->n_q_heads * c->head_dim;
     if (qd % 256 || qd > 8192) return DFLASH_ESHAPE;
     if (c->block != DFLASH_BLOCK) return DFLASH_ESHAPE;
@@ -121,6 +121,7 @@ int check_config(const dflash_config *c) {
     if ((c->vocab + topk_chunk_size() - 1) / topk_chunk_size() > 1024) return DFLASH_ESHAPE;
     if (c->sel_rank < 32 || c->sel_rank % 32 || c->sel_rank > 4096) return DFLASH_ESHAPE;
     if (c->window < 0) return DFLASH_EINVAL;
+    if (c->window > 65536) return DFLASH_ESHAPE;     // attention-merge weights live in LDS
     if (c->weight_fmt != DFLASH_W_Q4K && c->weight_fmt != DFLASH_W_BF16) return DFLASH_EINVAL;
     if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return DFLASH_EINVAL;
     return DFLASH_OK;
@@ -263,11 +264,18 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
     int32_t *valid = x.at<int32_t>(p.o_valid);
     float *fcout = x.at<float>(p.o_fcout);
     float *part = x.at<float>(p.o_part);
-    float *ssq = x.at<float>(p.o_ssq);
+    const float eps = cfg->rms_eps;
+    float *ssq_x = x.at<float>(p.o_ssq_x);      // row sums of squares behind each deferred norm
+    float *ssq_c = x.at<float>(p.o_ssq_c);
+    float *ssq_u = x.at<float>(p.o_ssq_u);
+    auto rowscale = [&](const float *ssq, int map) {
+        RowScale r;
+        r.ssq = ssq; r.nchunk = H / 256; r.map = map; r.n = (float)H; r.eps = eps;
+        return r;
+    };
     uint16_t *u2 = x.at<uint16_t>(p.o_u2);
     uint16_t *mid2 = x.at<uint16_t>(p.o_mid2);
     uint16_t *f = x.at<uint16_t>(p.o_f);
-    const float eps = cfg->rms_eps;
     const size_t cache_layer = (size_t)batch * p.n_kv * cache_cap * p.d;
     int splits;
 #define GEMM(...)                              \
@@ -276,9 +284,10 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
         if (splits < 0) return splits;         \
     } while (0)
 
-    // S0: block assembly h, per-sequence validity, first layer's input x = RMSNorm(h)
+    // S0: block assembly h, per-sequence validity, first layer's input bf16(h * g_in)
+    // (RMSNorms are deferred: the GEMM consumer scales each output row by 1 / rms)
     HIPCHK(launch_embed(w->embed, w->mask_emb, last_token, ctx_len, batch, p.T, H, p.V, t_new,
-                        cache_cap, h, w->layer[0].in_norm, eps, xc, valid, x.st));
+                        cache_cap, h, w->layer[0].in_norm, xc, ssq_x, valid, x.st));
     if (dbg_hidden)
         HIPCHK(hipMemcpyAsync(dbg_hidden, h, (size_t)p.M_blk * H * 4, hipMemcpyDeviceToDevice, x.st));
 
@@ -287,7 +296,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
         const void *ws[1] = {w->fc};
         const int sn[1] = {H};
         GEMM(ws, sn, 1, taps, cfg->n_taps * H, p.M_ctx, cfg->n_taps * H);
-        HIPCHK(launch_reduce_norm(part, splits, p.M_ctx, H, 0, 0, fcout, ssq, w->hidden_norm, eps,
+        HIPCHK(launch_reduce_norm(part, splits, p.M_ctx, H, 0, 0, fcout, ssq_c, w->hidden_norm,
                                   xc + (size_t)p.M_blk * H, nullptr, H, 0, x.st));
     }
 
@@ -307,6 +316,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
             RopeArgs a;
             a.qkv = part; a.splits = splits;
             a.B = batch; a.T = p.T; a.t_new = t_new; a.n_q = p.n_q; a.n_kv = p.n_kv; a.d = p.d;
+            a.blk = rowscale(ssq_x, 0); a.ctx = rowscale(ssq_c, 0);
             a.q_norm = lw.q_norm; a.k_norm = lw.k_norm; a.eps = eps;
             a.theta = cfg->rope_theta; a.ctx_len = ctx_len; a.valid = valid;
             a.Q = x.at<uint16_t>(p.o_Q); a.Kb = x.at<uint16_t>(p.o_Kb); a.Vb = x.at<uint16_t>(p.o_Vb);
@@ -339,7 +349,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
             const void *ws[1] = {lw.wo};
             const int sn[1] = {H};
             GEMM(ws, sn, 1, x.at<uint16_t>(p.o_Y), p.qd, p.M_blk, p.qd);
-            HIPCHK(launch_reduce_norm(part, splits, p.M_blk, H, 0, 1, h, ssq, lw.post_norm, eps, u2,
+            HIPCHK(launch_reduce_norm(part, splits, p.M_blk, H, 0, 1, h, ssq_u, lw.post_norm, u2,
                                       u2 + (size_t)p.M_blk * H, H, 0, x.st));
         }
         // S8: h += (silu(u Wg^T) * u Wu^T) Wd^T.  u and the SwiGLU output are carried as
@@ -352,8 +362,8 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
             if (probe_ffn) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_start, x.st));
             GEMM(ws, sn, 2, u2, H, 2 * p.M_blk, H);
             if (probe_ffn) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_stop, x.st));
-            HIPCHK(launch_reduce_epilogue(part, splits, p.M_blk, 2 * p.F, p.M_blk, EPI_SWIGLU_BF16,
-                                          nullptr, mid2, mid2 + (size_t)p.M_blk * p.F, p.F, x.st));
+            HIPCHK(launch_swiglu(part, splits, p.M_blk, 2 * p.F, p.M_blk, mid2,
+                                 mid2 + (size_t)p.M_blk * p.F, p.F, rowscale(ssq_u, 0), x.st));
         }
         // down projection + residual; then the next layer's input norm, or after the last
         // layer the final norm of the proposal rows (block positions 1..7) for the head
@@ -362,7 +372,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
             const int sn[1] = {H};
             GEMM(ws, sn, 1, mid2, p.F, 2 * p.M_blk, p.F);
             const uint16_t *gain = last ? w->final_norm : w->layer[l + 1].in_norm;
-            HIPCHK(launch_reduce_norm(part, splits, p.M_blk, H, p.M_blk, 1, h, ssq, gain, eps,
+            HIPCHK(launch_reduce_norm(part, splits, p.M_blk, H, p.M_blk, 1, h, ssq_x, gain,
                                       last ? f : xc, nullptr, H, last ? 1 : 0, x.st));
         }
         if (dbg_hidden)
@@ -381,17 +391,15 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
         a.nseg = 1;
         a.M = p.R; a.N = p.V; a.K = H; a.C = logits; a.ldc = p.V;
         a.A = f; a.lda = H;
+        a.rs = rowscale(ssq_x, 1);             // the final norm of the proposal rows
         const bool probe_lm = probe && probe->kernel == DFLASH_PROBE_LM_HEAD;
         if (probe_lm) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_start, x.st));
         if (p.lm_skinny) HIPCHK(launch_bf16_gemm_skinny(a, x.st));
         else HIPCHK(launch_bf16_gemm_tiled(a, x.st));
         if (probe_lm) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_stop, x.st));
     }
-    HIPCHK(launch_topk_partial(logits, p.R, p.V, 0, p.K, x.at<float>(p.o_pv),
-                               x.at<int32_t>(p.o_pi), x.at<float>(p.o_pm), x.at<float>(p.o_ps), x.st));
-    HIPCHK(launch_topk_merge(x.at<float>(p.o_pv), x.at<int32_t>(p.o_pi), x.at<float>(p.o_pm),
-                             x.at<float>(p.o_ps), p.R, p.topk_nch, p.K, p.P, valid, cand_ids,
-                             cand_logp, x.st));
+    HIPCHK(launch_topk(logits, p.R, p.V, p.K, p.P, valid, x.at<float>(p.o_topk), cand_ids, cand_logp,
+                       x.st));
     // S11: selector path
     HIPCHK(launch_viterbi(cand_ids, cand_logp, w->code_a, w->code_b, batch, p.P, p.K, p.r,
                           cfg->pair_scale, valid, draft_tokens, x.st));
@@ -430,7 +438,7 @@ int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
     const int splits = run_q4k(a, st);
     if (splits < 0) return splits;
     HIPCHK(launch_reduce_epilogue(a.part, splits, M, N, 0, EPI_STORE_BF16, nullptr, y, nullptr, N,
-                                  st));
+                                  RowScale{}, st));
     return DFLASH_OK;
 }
 

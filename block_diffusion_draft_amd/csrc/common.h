@@ -55,3 +55,22 @@ __device__ __forceinline__ bool cand_better(float va, int ia, float vb, int ib) 
 }
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Deferred RMSNorm: a row's activations enter a GEMM as bf16(v * gain) and the GEMM's
+// output row is multiplied by 1 / rms(v) = rsqrt(sum(v^2) / n + eps) afterwards (the
+// norm is a per-row scale).  sum(v^2) is kept as nchunk partial sums per row.
+struct RowScale {
+    const float *ssq;          // [rows][nchunk]; null: scale 1
+    int nchunk;
+    int map;                   // 0: row r; 1: proposal row r of blocks of 8 -> row (r/7)*8 + r%7 + 1
+    float n, eps;
+};
+
+__device__ __forceinline__ float row_inv(const RowScale &s, int r) {
+    if (!s.ssq) return 1.f;
+    const int br = s.map ? (r / 7) * 8 + r % 7 + 1 : r;
+    const float *p = s.ssq + (size_t)br * s.nchunk;
+    float ss = 0.f;
+    for (int i = 0; i < s.nchunk; i++) ss += p[i];
+    return rsqrtf(ss / s.n + s.eps);
+}

@@ -84,6 +84,14 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_tiled(Bf16GemmArgs a) {
     }
 
     const int g = lane >> 4, c = lane & 15;
+    float rinv[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int m = m0 + 64 * wm + 16 * i + 4 * g + v;
+            rinv[i][v] = m < a.M ? row_inv(a.rs, m) : 0.f;
+        }
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -93,7 +101,7 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_tiled(Bf16GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const int m = m0 + 64 * wm + 16 * i + 4 * g + v;
-                if (m < a.M) a.C[(size_t)m * a.ldc + n] = acc[i][j][v];
+                if (m < a.M) a.C[(size_t)m * a.ldc + n] = acc[i][j][v] * rinv[i][v];
             }
         }
 }
@@ -145,6 +153,16 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a, int ti
     }
     __syncthreads();
 
+    // deferred RMSNorm of the rows this lane stores (rows 4g + v, g < 2): computed for
+    // all 8 rows with wave-uniform (scalar) loads, which do not wait behind the weight
+    // loads already in flight
+    float inv8[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++) inv8[r] = r < a.M ? row_inv(a.rs, r) : 0.f;
+    float rinv[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) rinv[v] = g == 0 ? inv8[v] : (g == 1 ? inv8[4 + v] : 0.f);
+
     // lanes of rows >= 8 read the zero entry
     const int aoff = c < 8 ? g * 8 + c : 0;
     const int astep = c < 8 ? 32 : 0;
@@ -164,7 +182,7 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a, int ti
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const int m = 4 * g + v;
-                if (m < a.M) a.C[(size_t)m * a.ldc + n] = acc[v];
+                if (m < a.M) a.C[(size_t)m * a.ldc + n] = acc[v] * rinv[v];
             }
         }
     }

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "common.h"
+
 // ---------------------------------------------------------------- Q4_K decode
 hipError_t launch_q4k_dequant(const void *w, float *out, long long n_blocks, hipStream_t st);
 
@@ -17,6 +19,7 @@ struct Bf16GemmArgs {
     int M, N, K;
     float *C;                    // fp32 [M][ldc]
     int ldc;
+    RowScale rs;                 // output row r multiplied by row_inv(rs, r) (ssq null: none)
 };
 // tiled 128x128 MFMA GEMM, any M
 hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st);
@@ -26,17 +29,25 @@ hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------- layer ops
 enum EpiMode { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_SWIGLU_BF16 = 2, EPI_STORE_BF16 = 3 };
-// out row r = sum over splits of partial rows r (+ r + pair); SWIGLU writes bf16 hi
-// (and lo when out_bf16_lo) of silu(gate) * up, gate in columns [0, N/2)
+// out row r = sum over splits of partial rows r (+ r + pair), times row_inv(rs, r);
+// SWIGLU writes bf16 hi (and lo when out_bf16_lo) of silu(gate) * up, gate in columns
+// [0, N/2)
 hipError_t launch_reduce_epilogue(const float *part, int splits, int M, int N, int pair,
                                   int mode, float *out_f32, uint16_t *out_bf16,
-                                  uint16_t *out_bf16_lo, int ldo, hipStream_t st);
+                                  uint16_t *out_bf16_lo, int ldo, const RowScale &rs,
+                                  hipStream_t st);
+
+// SwiGLU of a [gate | up] product's split partials (N = 2F columns, rows r and r + pair
+// summed): out = bf16 hi / lo of silu(g * inv) * (u * inv), inv = row_inv(rs, r)
+hipError_t launch_swiglu(const float *part, int splits, int M, int N, int pair, uint16_t *out,
+                         uint16_t *out_lo, int ldo, const RowScale &rs, hipStream_t st);
 
 // per-sequence validity flags + block assembly h[b][0] = E[last], h[b][1..] = mask, and
-// the first layer's normalised input x = bf16(RMSNorm(h) * gain), [B*T][H]
+// the first layer's input x = bf16(h * gain), [B*T][H], with its row sums of squares
+// in ssq[row][0] (ssq[row][1 .. H/256) = 0)
 hipError_t launch_embed(const uint16_t *embed, const uint16_t *mask_emb, const int32_t *last,
                         const int32_t *ctx_len, int B, int T, int H, int V, int t_new, int cap,
-                        float *h, const uint16_t *gain, float eps, uint16_t *x, int32_t *valid,
+                        float *h, const uint16_t *gain, uint16_t *x, float *ssq, int32_t *valid,
                         hipStream_t st);
 
 struct RopeArgs {
@@ -44,6 +55,7 @@ struct RopeArgs {
                                  // then context rows, summed here in split order
     int splits;
     int B, T, t_new, n_q, n_kv, d;
+    RowScale blk, ctx;           // deferred input norms of the block rows and context rows
     const uint16_t *q_norm, *k_norm;
     float eps, theta;
     const int32_t *ctx_len, *valid;
@@ -71,17 +83,19 @@ struct MergeConvArgs {
     int B, T, t_new, n_q, n_kv, d, window, chunk, n_chunks;
     const uint16_t *w_conv;      // bf16 [2 n_q][n_q d]
     float *o;                    // fp32 [B*T][n_q d] merged attention output
-    float *zp;                   // fp32 [B][n_q][T][2 n_q] per-head conv-tap partials
+    float *zp;                   // fp32 [B][n_q][d/32][T][2 n_q] conv-tap partials per 32-column slice
     uint16_t *Y;                 // bf16 [B*T][n_q d]
 };
 hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------- LM head / top-K
-hipError_t launch_topk_partial(const float *logits, int R, int V, int chunk, int K,
-                               float *pv, int32_t *pi, float *pm, float *ps, hipStream_t st);
-hipError_t launch_topk_merge(const float *pv, const int32_t *pi, const float *pm, const float *ps,
-                             int R, int n_chunks, int K, int rows_per_seq, const int32_t *valid,
-                             int32_t *cand_ids, float *cand_logp, hipStream_t st);
+// log-softmax statistics and top-K per row of fp32 logits [R][V] (ids by logit desc,
+// id asc; logp = logit - logsumexp); rows of invalid sequences get -1 / -inf.
+// ws: topk_workspace_floats(R, V) floats.
+size_t topk_workspace_floats(int R, int V);
+hipError_t launch_topk(const float *logits, int R, int V, int K, int rows_per_seq,
+                       const int32_t *valid, float *ws, int32_t *cand_ids, float *cand_logp,
+                       hipStream_t st);
 
 // ---------------------------------------------------------------- selector / verify
 hipError_t launch_viterbi(const int32_t *cand_ids, const float *cand_logp, const uint16_t *code_a,
@@ -115,17 +129,19 @@ hipError_t launch_q4k_fused(const Q4kFusedArgs &a, const Q4kFusedPlan &p, hipStr
 // each wave streams tpw consecutive column tiles.  Same partial layout [splits][M][N].
 struct Q4kStreamPlan {
     int splits, tpw, grid_x;
+    int tp, pd;                  // column tiles per loop iteration, stages in flight
     size_t lds_bytes, part_bytes;
 };
 bool q4k_stream_ok(int M, int N, int K);
-Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves = 2048);
+Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves = 2048, int tp = 1, int pd = 4);
 hipError_t launch_q4k_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st);
 
 // Output rows r < M_out: v = sum over splits of partial rows r (+ r + pair), N a multiple
 // of 256; add ? f[r] += v : f[r] = v (fp32), with per-256-column sums of squares in
-// ssq [M_out][N/256].  Then, if out: the row's RMSNorm * gain as bf16 (and its residual
-// in out_lo) at output row map(r): map 0 -> r; map 1 -> the proposal rows of each block
-// of 8 (row r % 8 == 0 skipped, others to (r / 8) * 7 + r % 8 - 1).
+// ssq [M_out][N/256].  Then, if out: bf16(v * gain) (and its residual in out_lo) at
+// output row map(r): map 0 -> r; map 1 -> the proposal rows of each block of 8 (row
+// r % 8 == 0 skipped, others to (r / 8) * 7 + r % 8 - 1).  The consumer applies the
+// row's 1 / rms (RowScale).
 hipError_t launch_reduce_norm(const float *part, int splits, int M_out, int N, int pair, int add,
-                              float *f, float *ssq, const uint16_t *gain, float eps, uint16_t *out,
+                              float *f, float *ssq, const uint16_t *gain, uint16_t *out,
                               uint16_t *out_lo, int ldo, int map, hipStream_t st);

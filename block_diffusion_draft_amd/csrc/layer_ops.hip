@@ -22,38 +22,79 @@ __device__ __forceinline__ float block_sum_256(float v, float *scratch) {
 
 // ---------------------------------------------------------------- block assembly
 // h[b][0] = E[last token], h[b][1..] = mask embedding, and the first layer's input
-// x = bf16(RMSNorm(h) * gain)
+// x = bf16(h * gain) with the row's sum of squares in ssq[row][0] (the other partials
+// of the row are zero; the consumer applies 1 / rms).  Each thread owns up to EMB_V
+// runs of 8 values, loaded together (H <= 256 * 8 * EMB_V).
+constexpr int EMB_V = 4;
+
 __global__ __launch_bounds__(256) void k_embed(const uint16_t *embed, const uint16_t *mask,
                                                const int32_t *last, const int32_t *ctx_len,
                                                int T, int H, int V, int t_new, int cap,
-                                               float *h, const uint16_t *gain, float eps,
-                                               uint16_t *x, int32_t *valid) {
+                                               float *h, const uint16_t *gain, uint16_t *x,
+                                               float *ssq, int32_t *valid) {
     __shared__ float scratch[4];
-    const int b = blockIdx.x / T, t = blockIdx.x % T;
+    const int b = blockIdx.x / T, t = blockIdx.x % T, tid = threadIdx.x;
     const int n = ctx_len[b], tok = last[b];
     const bool ok = n >= 0 && n <= cap - t_new && tok >= 0 && tok < V;
-    if (t == 0 && threadIdx.x == 0) valid[b] = ok ? 1 : 0;
-    float *row = h + (size_t)blockIdx.x * H;
+    if (t == 0 && tid == 0) valid[b] = ok ? 1 : 0;
     const uint16_t *src = t == 0 ? embed + (size_t)(ok ? tok : 0) * H : mask;
+    const int nv = H / 8;
+    u32x4_t raw[EMB_V], gw[EMB_V];
+#pragma unroll
+    for (int u = 0; u < EMB_V; u++) {
+        const int v = tid + 256 * u;
+        const int vc = v < nv ? v : nv - 1;
+        raw[u] = *reinterpret_cast<const u32x4_t *>(src + 8 * vc);
+        gw[u] = *reinterpret_cast<const u32x4_t *>(gain + 8 * vc);
+    }
     float s = 0.f;
-    for (int i = threadIdx.x; i < H; i += 256) {
-        const float v = ok ? bf16_to_f32(src[i]) : 0.f;
-        row[i] = v;
-        s += v * v;
+    float val[EMB_V][8];
+#pragma unroll
+    for (int u = 0; u < EMB_V; u++) {
+        const bool in = tid + 256 * u < nv;
+        const uint32_t wv[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float f = bf16_to_f32((uint16_t)(wv[i / 2] >> (16 * (i & 1))));
+            val[u][i] = (ok && in) ? f : 0.f;
+            s += val[u][i] * val[u][i];
+        }
     }
     s = block_sum_256(s, scratch);
-    const float inv = rsqrtf(s / (float)H + eps);
+    const int nchunk = H / 256;
+    if (tid < nchunk) ssq[(size_t)blockIdx.x * nchunk + tid] = tid == 0 ? s : 0.f;
+    float *row = h + (size_t)blockIdx.x * H;
     uint16_t *xr = x + (size_t)blockIdx.x * H;
-    for (int i = threadIdx.x; i < H; i += 256) xr[i] = f32_to_bf16(row[i] * inv * bf16_to_f32(gain[i]));
+#pragma unroll
+    for (int u = 0; u < EMB_V; u++) {
+        const int v = tid + 256 * u;
+        if (v < nv) {
+            const uint32_t g4[4] = {gw[u].x, gw[u].y, gw[u].z, gw[u].w};
+            float4 *hp = reinterpret_cast<float4 *>(row + 8 * v);
+            hp[0] = make_float4(val[u][0], val[u][1], val[u][2], val[u][3]);
+            hp[1] = make_float4(val[u][4], val[u][5], val[u][6], val[u][7]);
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float g0 = bf16_to_f32((uint16_t)(g4[i] & 0xFFFF)), g1 = bf16_to_f32((uint16_t)(g4[i] >> 16));
+                o[i] = pack_bf16x2(val[u][2 * i] * g0, val[u][2 * i + 1] * g1);
+            }
+            *reinterpret_cast<u32x4_t *>(xr + 8 * v) = (u32x4_t){o[0], o[1], o[2], o[3]};
+        }
+    }
 }
 
-// ---------------------------------------------------------------- reduction + residual + RMSNorm
-// Phase 1, workgroup per (256 columns, output row): the 4 waves sum interleaved subsets
-// of the splits (each lane 4 adjacent columns), combined through LDS in a fixed order,
-// so the result is deterministic.  v (+ f when adding) is stored to f, and the
-// workgroup's sum of v^2 goes to ssq[r][blockIdx.x].
+// ---------------------------------------------------------------- reduction + residual (+ norm input)
+// Workgroup per (256 columns, output row): the 4 waves sum interleaved subsets of the
+// splits (each lane 4 adjacent columns), combined through LDS in a fixed order, so the
+// result is deterministic.  v (+ f when adding) is stored to f, the workgroup's sum of
+// v^2 goes to ssq[r][blockIdx.x], and with out the next GEMM's input bf16(v * gain)
+// (+ its bf16 residual in out_lo) goes to output row map(r).  The RMSNorm's 1 / rms is
+// applied by the consumer of that GEMM (RowScale).
 __global__ __launch_bounds__(256) void k_reduce_rows(const float *part, int splits, int M_out, int N,
-                                                     int pair, int add, float *f, float *ssq) {
+                                                     int pair, int add, float *f, float *ssq,
+                                                     const uint16_t *gain, uint16_t *out,
+                                                     uint16_t *out_lo, int ldo, int map) {
     __shared__ float4 red[4][64];
     __shared__ float scratch[4];
     const int r = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -80,26 +121,12 @@ __global__ __launch_bounds__(256) void k_reduce_rows(const float *part, int spli
     *fp = v;
     const float sq = block_sum_256(v * v, scratch);
     if (tid == 0) ssq[(size_t)r * gridDim.x + blockIdx.x] = sq;
-}
-
-// Phase 2, workgroup per (256 columns, output row): out = bf16(v * rsqrt(mean v^2 + eps)
-// * gain) (+ its bf16 residual in out_lo) at output row map(r).
-__global__ __launch_bounds__(256) void k_norm_rows(const float *f, const float *ssq, int nchunk, int N,
-                                                   const uint16_t *gain, float eps, uint16_t *out,
-                                                   uint16_t *out_lo, int ldo, int map) {
-    const int r = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
-    int orow = r;
-    if (map == 1) {
-        if (r % 8 == 0) return;
-        orow = (r / 8) * 7 + r % 8 - 1;
-    }
-    float ss = 0.f;
-    for (int i = 0; i < nchunk; i++) ss += ssq[(size_t)r * nchunk + i];
-    const float inv = rsqrtf(ss / (float)N + eps);
-    const float x = f[(size_t)r * N + c] * inv * bf16_to_f32(gain[c]);
+    if (!out || (map == 1 && r % 8 == 0)) return;
+    const int orow = map == 1 ? (r / 8) * 7 + r % 8 - 1 : r;
+    const float x = v * bf16_to_f32(gain[c0 + c]);
     const uint16_t hb = f32_to_bf16(x);
-    out[(size_t)orow * ldo + c] = hb;
-    if (out_lo) out_lo[(size_t)orow * ldo + c] = f32_to_bf16(x - bf16_to_f32(hb));
+    out[(size_t)orow * ldo + c0 + c] = hb;
+    if (out_lo) out_lo[(size_t)orow * ldo + c0 + c] = f32_to_bf16(x - bf16_to_f32(hb));
 }
 
 // ---------------------------------------------------------------- split-K reduction
@@ -107,7 +134,7 @@ __global__ __launch_bounds__(256) void k_norm_rows(const float *f, const float *
 // [hi rows; lo rows]) over all splits in a fixed order.
 __global__ __launch_bounds__(256) void k_reduce(const float *part, int splits, int M, int N,
                                                 int pair, int mode, float *of, uint16_t *ob,
-                                                uint16_t *ob_lo, int ldo) {
+                                                uint16_t *ob_lo, int ldo, RowScale rs) {
     const int Nout = mode == EPI_SWIGLU_BF16 ? N / 2 : N;
     const size_t total = (size_t)M * Nout;
     const int Min = pair ? 2 * M : M;
@@ -118,6 +145,8 @@ __global__ __launch_bounds__(256) void k_reduce(const float *part, int splits, i
         const float *q = part + (size_t)(r + pair) * N + c;
         float s = 0.f;
         for (int k = 0; k < splits; k++) s += p[k * stride] + (pair ? q[k * stride] : 0.f);
+        const float inv = row_inv(rs, r);
+        s *= inv;
         if (mode == EPI_STORE_F32) {
             of[(size_t)r * ldo + c] = s;
         } else if (mode == EPI_ADD_F32) {
@@ -128,6 +157,7 @@ __global__ __launch_bounds__(256) void k_reduce(const float *part, int splits, i
             float u = 0.f;
             for (int k = 0; k < splits; k++)
                 u += p[k * stride + Nout] + (pair ? q[k * stride + Nout] : 0.f);
+            u *= inv;
             const float act = s / (1.f + expf(-s));          // silu(gate)
             const float v = act * u;
             const uint16_t hb = f32_to_bf16(v);
@@ -135,6 +165,39 @@ __global__ __launch_bounds__(256) void k_reduce(const float *part, int splits, i
             if (ob_lo) ob_lo[(size_t)r * ldo + c] = f32_to_bf16(v - bf16_to_f32(hb));
         }
     }
+}
+
+// ---------------------------------------------------------------- SwiGLU from split partials
+// Workgroup per (256 columns, output row r): gate and up (columns c and c + N/2 of the
+// [gate | up] product) summed over the splits and the [hi; lo] row pair, scaled by the
+// row's deferred 1 / rms, then silu(gate) * up as a bf16 (hi, lo) pair.
+__global__ __launch_bounds__(256) void k_swiglu(const float *part, int splits, int M, int N, int pair,
+                                                uint16_t *ob, uint16_t *ob_lo, int ldo, RowScale rs) {
+    const int r = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+    const int F = N / 2;
+    if (c >= F) return;
+    const size_t stride = (size_t)(pair ? 2 * M : M) * N;
+    const float *p = part + (size_t)r * N + c;
+    float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
+    int k = 0;
+    for (; k + 2 <= splits; k += 2) {
+        const float *p0 = p + k * stride, *p1 = p0 + stride;
+        g0 += p0[0] + (pair ? p0[(size_t)pair * N] : 0.f);
+        u0 += p0[F] + (pair ? p0[(size_t)pair * N + F] : 0.f);
+        g1 += p1[0] + (pair ? p1[(size_t)pair * N] : 0.f);
+        u1 += p1[F] + (pair ? p1[(size_t)pair * N + F] : 0.f);
+    }
+    for (; k < splits; k++) {
+        const float *p0 = p + k * stride;
+        g0 += p0[0] + (pair ? p0[(size_t)pair * N] : 0.f);
+        u0 += p0[F] + (pair ? p0[(size_t)pair * N + F] : 0.f);
+    }
+    const float inv = row_inv(rs, r);
+    const float gt = (g0 + g1) * inv, up = (u0 + u1) * inv;
+    const float v = gt / (1.f + expf(-gt)) * up;
+    const uint16_t hb = f32_to_bf16(v);
+    ob[(size_t)r * ldo + c] = hb;
+    if (ob_lo) ob_lo[(size_t)r * ldo + c] = f32_to_bf16(v - bf16_to_f32(hb));
 }
 
 // ---------------------------------------------------------------- q/k norm, rotary, append
@@ -166,6 +229,10 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
             x1 += x[s * pstride + lane];
             x2 += x[s * pstride + lane + half];
         }
+    // the projection input's deferred RMSNorm
+    const float rinv = is_blk ? row_inv(a.blk, r) : row_inv(a.ctx, r - nblk);
+    x1 *= rinv;
+    x2 *= rinv;
     if (is_q || is_k) {
         const uint16_t *g = is_q ? a.q_norm : a.k_norm;
         const float ss = wave_sum(x1 * x1 + x2 * x2);
@@ -197,24 +264,31 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
 }
 
 // ---------------------------------------------------------------- merge + dynamic conv
-// k_attn_merge: one workgroup per (query head h, sequence b).  Combines the
-// split-window partials of the 8 block rows of head h (log-sum-exp merge) into
-// o[b][t][h*d..] (fp32), and contributes head h's share of the convolution taps
-//     zp[b][h][t][q] = sum_e W_c[q][h d + e] o[b][t][h][e],   q < 2 n_q,
-// so that z_t = W_c . vec(o_t) = sum_h zp[b][h][t][:].
+// k_attn_merge: one workgroup per (query head h, 32-column slice cc of the head,
+// sequence b); thread (t, col) of the 8 x 32 block.  Combines the split-window
+// partials of head h (log-sum-exp merge: weight exp(m_c - M) / sum_c exp(m_c - M) l_c
+// on the unnormalised chunk outputs) into o[b][t][h d + 32 cc + col] (fp32), then
+// contributes this slice's share of the convolution taps
+//     zp[b][h][cc][t][q] = sum_{e in slice} W_c[q][h d + e] o[b][t][h d + e],  q < 2 n_q,
+// so that z_t = W_c . vec(o_t) = the sum of zp over (h, cc).
+constexpr int MC = 32;              // columns per merge workgroup
+
 __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int h = blockIdx.x, cc = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int d = a.d, T = a.T, G = a.n_q / a.n_kv, QR = G * T, qd = a.n_q * d;
     const int kvh = h / G, hq = h % G;
     const int nch1 = a.n_chunks + 1;
-    const int nq2 = 2 * a.n_q;
+    const int nq2 = 2 * a.n_q, CC = d / MC;
+    const int t = tid / MC, col = tid % MC;             // T * MC == 256
+    const int c0 = h * d + cc * MC;
     extern __shared__ float sm[];
-    float *o = sm;                      // [T][d]
-    float *w = sm + T * d;              // [T][nch1] merge weights
-    float *mx = w + T * nch1;           // [T]
+    float *w = sm;                      // [T][nch1] merge weights
+    float *os = sm + T * nch1;          // [T][MC]
+    float *zp = a.zp + (((size_t)b * a.n_q + h) * CC + cc) * T * nq2;
     if (!a.valid[b]) {
-        for (int e = tid; e < T * d; e += 256) a.o[((size_t)b * T + e / d) * qd + h * d + e % d] = 0.f;
-        for (int e = tid; e < T * nq2; e += 256) a.zp[(((size_t)b * a.n_q + h) * T) * nq2 + e] = 0.f;
+        a.o[((size_t)b * T + t) * qd + c0 + col] = 0.f;
+        for (int e = tid; e < T * nq2; e += 256) zp[e] = 0.f;
         return;
     }
     const int n = a.ctx_len[b];
@@ -222,98 +296,99 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
     const int lo = hi - a.window > 0 ? hi - a.window : 0;
     const int nch_b = ceil_div(hi - lo, a.chunk);
     const float *ml = a.ml + ((size_t)(b * a.n_kv + kvh) * nch1) * QR * 2;
-    // all (row, chunk) statistics are loaded in parallel
-    for (int e = tid; e < T * nch1; e += 256) {
-        const int t = e / nch1, c = e % nch1;
-        const bool used = c < nch_b || c == a.n_chunks;
-        w[e] = used ? ml[((size_t)c * QR + hq * T + t) * 2] : -INFINITY;
-    }
-    __syncthreads();
-    if (tid < T) {
+    // merge weights: wave per row (rows wave, wave + 4), lanes over chunks
+    for (int tr = wave; tr < T; tr += 4) {
         float M = -INFINITY;
-        for (int c = 0; c < nch1; c++) M = fmaxf(M, w[tid * nch1 + c]);
-        mx[tid] = M;
-    }
-    __syncthreads();
-    for (int e = tid; e < T * nch1; e += 256) {
-        const int t = e / nch1, c = e % nch1;
-        const float m = w[e];
-        w[e] = m == -INFINITY ? 0.f : expf(m - mx[t]) * ml[((size_t)c * QR + hq * T + t) * 2 + 1];
-    }
-    __syncthreads();
-    if (tid < T) {
+        for (int c = lane; c < nch1; c += 64) {
+            const bool used = c < nch_b || c == a.n_chunks;
+            if (used) M = fmaxf(M, ml[((size_t)c * QR + hq * T + tr) * 2]);
+        }
+        M = wave_max(M);
         float L = 0.f;
-        for (int c = 0; c < nch1; c++) L += w[tid * nch1 + c];
-        mx[tid] = 1.f / L;
-    }
-    __syncthreads();
-    // weights exp(m_c - M) / L multiply the unnormalised partials (l_c already folded in
-    // the sum above, so divide it back out per chunk)
-    for (int e = tid; e < T * nch1; e += 256) {
-        const int t = e / nch1, c = e % nch1;
-        const float lc = ml[((size_t)c * QR + hq * T + t) * 2 + 1];
-        w[e] = w[e] == 0.f ? 0.f : w[e] / lc * mx[t];
-    }
-    __syncthreads();
-    const float *O = a.O + ((size_t)(b * a.n_kv + kvh) * nch1) * QR * d;
-    for (int e = tid; e < T * d; e += 256) {
-        const int t = e / d, col = e % d, row = hq * T + t;
-        const float *wt = w + t * nch1;
-        float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-        int c = 0;
-        for (; c + 4 <= nch1; c += 4) {
-            acc0 += wt[c] * O[((size_t)c * QR + row) * d + col];
-            acc1 += wt[c + 1] * O[((size_t)(c + 1) * QR + row) * d + col];
-            acc2 += wt[c + 2] * O[((size_t)(c + 2) * QR + row) * d + col];
-            acc3 += wt[c + 3] * O[((size_t)(c + 3) * QR + row) * d + col];
+        for (int c = lane; c < nch1; c += 64) {
+            const bool used = c < nch_b || c == a.n_chunks;
+            float e = 0.f;
+            if (used) {
+                const float *s = ml + ((size_t)c * QR + hq * T + tr) * 2;
+                e = expf(s[0] - M);
+                L += e * s[1];
+            }
+            w[tr * nch1 + c] = e;
         }
-        for (; c < nch1; c++) acc0 += wt[c] * O[((size_t)c * QR + row) * d + col];
-        const float acc = (acc0 + acc1) + (acc2 + acc3);
-        o[e] = acc;
-        a.o[((size_t)b * T + t) * qd + h * d + col] = acc;
+        L = wave_sum(L);
+        const float invL = 1.f / L;
+        for (int c = lane; c < nch1; c += 64) w[tr * nch1 + c] *= invL;
     }
     __syncthreads();
+    // merged output: thread (t, col) over the chunks, 4 independent partial sums
+    const float *O = a.O + ((size_t)(b * a.n_kv + kvh) * nch1 * QR + hq * T + t) * d + cc * MC + col;
+    const size_t cstride = (size_t)QR * d;
+    const float *wt = w + t * nch1;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    int c = 0;
+    for (; c + 4 <= nch1; c += 4) {
+        s0 += wt[c] * O[(size_t)c * cstride];
+        s1 += wt[c + 1] * O[(size_t)(c + 1) * cstride];
+        s2 += wt[c + 2] * O[(size_t)(c + 2) * cstride];
+        s3 += wt[c + 3] * O[(size_t)(c + 3) * cstride];
+    }
+    for (; c < nch1; c++) s0 += wt[c] * O[(size_t)c * cstride];
+    const float ov = (s0 + s1) + (s2 + s3);
+    os[t * MC + col] = ov;
+    a.o[((size_t)b * T + t) * qd + c0 + col] = ov;
+    __syncthreads();
+    // conv-tap partials of this slice: (t, q) pairs over the threads
     for (int e = tid; e < T * nq2; e += 256) {
-        const int t = e / nq2, q = e % nq2;
-        const uint16_t *wr = a.w_conv + (size_t)q * qd + h * d;
-        const float *ot = o + t * d;
-        float s = 0.f;
-        for (int i = 0; i < d; i += 8) {
+        const int tt = e / nq2, q = e % nq2;
+        const uint16_t *wr = a.w_conv + (size_t)q * qd + c0;
+        const float *ot = os + tt * MC;
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < MC; i += 8) {
             const u32x4_t wv = *reinterpret_cast<const u32x4_t *>(wr + i);
-            s += bf16_to_f32(wv.x & 0xFFFF) * ot[i] + bf16_to_f32(wv.x >> 16) * ot[i + 1];
-            s += bf16_to_f32(wv.y & 0xFFFF) * ot[i + 2] + bf16_to_f32(wv.y >> 16) * ot[i + 3];
-            s += bf16_to_f32(wv.z & 0xFFFF) * ot[i + 4] + bf16_to_f32(wv.z >> 16) * ot[i + 5];
-            s += bf16_to_f32(wv.w & 0xFFFF) * ot[i + 6] + bf16_to_f32(wv.w >> 16) * ot[i + 7];
+            acc += bf16_to_f32(wv.x & 0xFFFF) * ot[i] + bf16_to_f32(wv.x >> 16) * ot[i + 1];
+            acc += bf16_to_f32(wv.y & 0xFFFF) * ot[i + 2] + bf16_to_f32(wv.y >> 16) * ot[i + 3];
+            acc += bf16_to_f32(wv.z & 0xFFFF) * ot[i + 4] + bf16_to_f32(wv.z >> 16) * ot[i + 5];
+            acc += bf16_to_f32(wv.w & 0xFFFF) * ot[i + 6] + bf16_to_f32(wv.w >> 16) * ot[i + 7];
         }
-        a.zp[(((size_t)b * a.n_q + h) * T + t) * nq2 + q] = s;
+        zp[e] = acc;
     }
 }
 
-// k_conv_apply: one workgroup per (sequence, block row t):
-//   z_t = sum_h zp[b][h][t];  y_{t,h} = z_t[h] o_{t,h} + z_t[n_q + h] o_{t-1,h},  o_{-1} = 0.
+// k_conv_apply: one workgroup per (sequence b, block row t, pair of heads):
+//   z_t[h], z_t[n_q + h] for the two heads = sums of the (h', cc) partials;
+//   y_{t,h} = z_t[h] o_{t,h} + z_t[n_q + h] o_{t-1,h},  o_{-1} = 0.
+constexpr int CONV_HEADS = 2;       // heads per conv workgroup
+
 __global__ __launch_bounds__(256) void k_conv_apply(MergeConvArgs a) {
     __shared__ float zpart[256];
-    __shared__ float z[2 * 256];
+    __shared__ float z[2 * CONV_HEADS];
     const int b = blockIdx.x / a.T, t = blockIdx.x % a.T, tid = threadIdx.x;
-    const int qd = a.n_q * a.d, nq2 = 2 * a.n_q;
-    // z_t[q] = sum over heads of zp[b][h][t][q]: (q, head-quarter) per thread
-    for (int q0 = 0; q0 < nq2; q0 += 64) {
-        const int q = q0 + (tid & 63), part = tid >> 6;
-        float s = 0.f;
-        if (q < nq2)
-            for (int h = part; h < a.n_q; h += 4) s += a.zp[(((size_t)b * a.n_q + h) * a.T + t) * nq2 + q];
-        zpart[tid] = s;
-        __syncthreads();
-        if (tid < 64 && q0 + tid < nq2) z[q0 + tid] = (zpart[tid] + zpart[tid + 64]) + (zpart[tid + 128] + zpart[tid + 192]);
-        __syncthreads();
+    const int qd = a.n_q * a.d, nq2 = 2 * a.n_q, CC = a.d / MC;
+    const int np = a.n_q * CC;                          // partials per (b, t, q)
+    const int h0 = blockIdx.y * CONV_HEADS;
+    // the 2 CONV_HEADS tap values this workgroup needs: q = h0 + k (a) and n_q + h0 + k (b)
+    constexpr int NQ = 2 * CONV_HEADS, PER_Q = 256 / NQ;
+    const int qi = tid / PER_Q, part = tid % PER_Q;
+    const int q = qi < CONV_HEADS ? h0 + qi : a.n_q + h0 + qi - CONV_HEADS;
+    float s = 0.f;
+    for (int p = part; p < np; p += PER_Q) s += a.zp[(((size_t)b * np + p) * a.T + t) * nq2 + q];
+    zpart[tid] = s;
+    __syncthreads();
+    if (tid < NQ) {
+        float acc = 0.f;
+        for (int i = 0; i < PER_Q; i++) acc += zpart[tid * PER_Q + i];
+        z[tid] = acc;
     }
+    __syncthreads();
     const float *ot = a.o + ((size_t)b * a.T + t) * qd;
     const float *op = ot - qd;
     uint16_t *Y = a.Y + ((size_t)b * a.T + t) * qd;
-    for (int i = tid; i < qd; i += 256) {
-        const int h = i / a.d;
+    const int i0 = h0 * a.d, i1 = min(i0 + CONV_HEADS * a.d, qd);
+    for (int i = i0 + tid; i < i1; i += 256) {
+        const int k = (i - i0) / a.d;
         const float prev = t > 0 ? op[i] : 0.f;
-        Y[i] = f32_to_bf16(z[h] * ot[i] + z[a.n_q + h] * prev);
+        Y[i] = f32_to_bf16(z[k] * ot[i] + z[CONV_HEADS + k] * prev);
     }
 }
 
@@ -321,21 +396,29 @@ __global__ __launch_bounds__(256) void k_conv_apply(MergeConvArgs a) {
 
 hipError_t launch_embed(const uint16_t *embed, const uint16_t *mask_emb, const int32_t *last,
                         const int32_t *ctx_len, int B, int T, int H, int V, int t_new, int cap,
-                        float *h, const uint16_t *gain, float eps, uint16_t *x, int32_t *valid,
+                        float *h, const uint16_t *gain, uint16_t *x, float *ssq, int32_t *valid,
                         hipStream_t st) {
     hipLaunchKernelGGL(k_embed, dim3(B * T), dim3(256), 0, st, embed, mask_emb, last, ctx_len, T, H,
-                       V, t_new, cap, h, gain, eps, x, valid);
+                       V, t_new, cap, h, gain, x, ssq, valid);
     return hipGetLastError();
 }
 
 hipError_t launch_reduce_epilogue(const float *part, int splits, int M, int N, int pair,
                                   int mode, float *out_f32, uint16_t *out_bf16,
-                                  uint16_t *out_bf16_lo, int ldo, hipStream_t st) {
+                                  uint16_t *out_bf16_lo, int ldo, const RowScale &rs,
+                                  hipStream_t st) {
     const size_t total = (size_t)M * (mode == EPI_SWIGLU_BF16 ? N / 2 : N);
     size_t grid = (total + 255) / 256;
     if (grid > 8192) grid = 8192;
     hipLaunchKernelGGL(k_reduce, dim3((unsigned)grid), dim3(256), 0, st, part, splits, M, N, pair,
-                       mode, out_f32, out_bf16, out_bf16_lo, ldo);
+                       mode, out_f32, out_bf16, out_bf16_lo, ldo, rs);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const float *part, int splits, int M, int N, int pair, uint16_t *out,
+                         uint16_t *out_lo, int ldo, const RowScale &rs, hipStream_t st) {
+    hipLaunchKernelGGL(k_swiglu, dim3(ceil_div(N / 2, 256), M), dim3(256), 0, st, part, splits, M, N,
+                       pair, out, out_lo, ldo, rs);
     return hipGetLastError();
 }
 
@@ -346,22 +429,18 @@ hipError_t launch_qk_norm_rope(const RopeArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st) {
-    const size_t lds = (size_t)(a.T * a.d + a.T * (a.n_chunks + 1) + a.T) * 4;
-    hipLaunchKernelGGL(k_attn_merge, dim3(a.n_q, a.B), dim3(256), lds, st, a);
+    const size_t lds = (size_t)(a.T * (a.n_chunks + 1) + a.T * MC) * 4;
+    hipLaunchKernelGGL(k_attn_merge, dim3(a.n_q, a.d / MC, a.B), dim3(256), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_conv_apply, dim3(a.B * a.T), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_conv_apply, dim3(a.B * a.T, a.n_q / CONV_HEADS), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 hipError_t launch_reduce_norm(const float *part, int splits, int M_out, int N, int pair, int add,
-                              float *f, float *ssq, const uint16_t *gain, float eps, uint16_t *out,
+                              float *f, float *ssq, const uint16_t *gain, uint16_t *out,
                               uint16_t *out_lo, int ldo, int map, hipStream_t st) {
-    const dim3 grid(N / 256, M_out);
-    hipLaunchKernelGGL(k_reduce_rows, grid, dim3(256), 0, st, part, splits, M_out, N, pair, add, f,
-                       ssq);
-    if (out)
-        hipLaunchKernelGGL(k_norm_rows, grid, dim3(256), 0, st, f, ssq, N / 256, N, gain, eps, out,
-                           out_lo, ldo, map);
+    hipLaunchKernelGGL(k_reduce_rows, dim3(N / 256, M_out), dim3(256), 0, st, part, splits, M_out, N,
+                       pair, add, f, ssq, gain, out, out_lo, ldo, map);
     return hipGetLastError();
 }

@@ -30,7 +30,6 @@
 namespace {
 
 constexpr int SNSB = 4;        // super-blocks per split
-constexpr int SPD = 4;         // stages in flight per wave (divides SNSB)
 
 struct SStage {
     u32x4_t hdr;               // d, dmin, 12 scale bytes (same for the 4 lane groups)
@@ -68,7 +67,11 @@ __device__ __forceinline__ uint32_t byte_bf16x2(uint32_t w, int k) {
     return (fb >> 16) | (fb & 0xFFFF0000u);
 }
 
-__global__ __launch_bounds__(256) void k_q4k_stream(Q4kFusedArgs a, int tpw) {
+template <int TP, int PD>
+__global__ __launch_bounds__(256)
+void k_q4k_stream(Q4kFusedArgs a, int tpw) {
+    constexpr int SPI = SNSB * TP;                  // stages per loop iteration
+    static_assert(SPI % PD == 0, "ring slots must be static");
     extern __shared__ __align__(16) unsigned char lds[];
     u32x4_t *A_lds = reinterpret_cast<u32x4_t *>(lds);              // [SNSB][8][64]
     u32x4_t *B_lds = A_lds + SNSB * 8 * 64;                          // [SNSB][64]
@@ -81,7 +84,8 @@ __global__ __launch_bounds__(256) void k_q4k_stream(Q4kFusedArgs a, int tpw) {
     const int ntile = a.N / 16;
     const int t0 = (blockIdx.x * 4 + wave) * tpw;
     const int t1 = min(t0 + tpw, ntile);
-    const int nst = t1 > t0 ? (t1 - t0) * SNSB : 0;
+    const int nit = t1 > t0 ? (t1 - t0 + TP - 1) / TP : 0;   // iterations of TP tiles
+    const int nst = nit * SPI;
     const int tlast = (t1 > t0 ? t1 : ntile) - 1;       // clamp target, always a real tile
 
     // ---- weight stream: (tile, super-block) stages in order, clamped past the end.
@@ -89,25 +93,30 @@ __global__ __launch_bounds__(256) void k_q4k_stream(Q4kFusedArgs a, int tpw) {
     // offset that never changes: column cl's row and lane group g's 8 bytes.
     const int row_bytes = a.KB * 144;
     const int lane_off = cl * row_bytes + sb0 * 144;
-    int lt = t0, lsb = 0, nload = 0;
+    // stream order: iteration, super-block, tile of the iteration
+    int lit = t0, lsb = 0, ltl = 0, nload = 0;
     auto load_next = [&]() -> SStage {
-        const bool ok = nload < nst;
-        const int tt = ok ? lt : tlast, sbb = ok ? lsb : SNSB - 1;
+        const int traw = lit + ltl;
+        const bool ok = nload < nst && traw < t1;
+        const int tt = ok ? traw : tlast, sbb = ok ? lsb : SNSB - 1;
         const int c16 = tt * 16;
         const int si = (a.nseg > 1 && c16 >= a.seg_end[0]) + (a.nseg > 2 && c16 >= a.seg_end[1]);
         const unsigned char *wseg = si == 0 ? a.w[0] : (si == 1 ? a.w[1] : a.w[2]);
         const int nbase = si == 0 ? 0 : (si == 1 ? a.seg_end[0] : a.seg_end[1]);
         const unsigned char *ubase = wseg + (size_t)(c16 - nbase) * row_bytes + sbb * 144;
         nload++;
-        lsb++;
-        const bool wrap = lsb == SNSB;
-        lsb = wrap ? 0 : lsb;
-        lt += wrap ? 1 : 0;
+        ltl++;
+        const bool wt = ltl == TP;
+        ltl = wt ? 0 : ltl;
+        lsb += wt ? 1 : 0;
+        const bool ws = lsb == SNSB;
+        lsb = ws ? 0 : lsb;
+        lit += ws ? TP : 0;
         return s_load(ubase + lane_off, g);
     };
-    SStage st[SPD];
+    SStage st[PD];
 #pragma unroll
-    for (int u = 0; u < SPD - 1; u++) st[u] = load_next();
+    for (int u = 0; u < PD - 1; u++) st[u] = load_next();
 
     // ---- activations of this split -> LDS (lane order), sub-block sums S
     constexpr int PER = SNSB * 8 * 64 / 256;
@@ -165,51 +174,71 @@ __global__ __launch_bounds__(256) void k_q4k_stream(Q4kFusedArgs a, int tpw) {
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
     float *part = a.part + (size_t)split * a.M * a.N;
     int a_off = lane, b_off = lane;
-    for (int t = t0; t < t1; t++) {
+#pragma nounroll
+    for (int it = 0; it < nit; it++) {
         // opaque to the compiler: keeps the 32 activation fragments in LDS instead of
-        // hoisting them into registers (which would halve the waves per SIMD)
+        // hoisting them into registers (which would cost waves per SIMD)
         asm volatile("" : "+v"(a_off), "+v"(b_off));
-        f32x4_t acc = zero;
+        f32x4_t acc[TP];
+#pragma unroll
+        for (int tl = 0; tl < TP; tl++) acc[tl] = zero;
 #pragma unroll
         for (int sb = 0; sb < SNSB; sb++) {
-            st[(sb + SPD - 1) % SPD] = load_next();
-            const SStage &w = st[sb % SPD];
-            const float d = half_bits_to_f32(w.hdr.x & 0xFFFF);
-            const float dmin = half_bits_to_f32(w.hdr.x >> 16);
-            const uint32_t s0w = w.hdr.y, s1w = w.hdr.z, s2w = w.hdr.w;
-            const uint32_t sc_lo = s0w & 0x3F3F3F3Fu;
-            const uint32_t m_lo = s1w & 0x3F3F3F3Fu;
-            const uint32_t sc_hi = (s2w & 0x0F0F0F0Fu) | ((s0w >> 2) & 0x30303030u);
-            const uint32_t m_hi = ((s2w >> 4) & 0x0F0F0F0Fu) | ((s1w >> 2) & 0x30303030u);
-            f32x4_t tacc = zero;
 #pragma unroll
-            for (int c = 0; c < 4; c++) {
-                u32x4_t blo, bhi;
-                s_decode(w.q[c], blo, bhi);
+            for (int tl = 0; tl < TP; tl++) {
+                const int slot = sb * TP + tl;
+                st[(slot + PD - 1) % PD] = load_next();
+                // keep each stage's work in program order: loads issued here, this
+                // stage's LDS reads and math not hoisted into earlier stages
+                __builtin_amdgcn_sched_barrier(0);
+                const SStage &w = st[slot % PD];
+                const float d = half_bits_to_f32(w.hdr.x & 0xFFFF);
+                const float dmin = half_bits_to_f32(w.hdr.x >> 16);
+                const uint32_t s0w = w.hdr.y, s1w = w.hdr.z, s2w = w.hdr.w;
+                const uint32_t sc_lo = s0w & 0x3F3F3F3Fu;
+                const uint32_t m_lo = s1w & 0x3F3F3F3Fu;
+                const uint32_t sc_hi = (s2w & 0x0F0F0F0Fu) | ((s0w >> 2) & 0x30303030u);
+                const uint32_t m_hi = ((s2w >> 4) & 0x0F0F0F0Fu) | ((s1w >> 2) & 0x30303030u);
+                f32x4_t tacc = zero;
 #pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    const int j = 2 * c + h;
-                    const uint32_t scw = j < 4 ? sc_lo : sc_hi;
-                    const float sc = (float)((scw >> (8 * (j & 3))) & 0xFF);
-                    const f32x4_t D = mfma16x16x32(A_lds[(sb * 8 + j) * 64 + a_off], h ? bhi : blo, zero);
-                    tacc += sc * D;
+                for (int c = 0; c < 4; c++) {
+                    u32x4_t blo, bhi;
+                    s_decode(w.q[c], blo, bhi);
+#pragma unroll
+                    for (int h = 0; h < 2; h++) {
+                        const int j = 2 * c + h;
+                        const uint32_t scw = j < 4 ? sc_lo : sc_hi;
+                        const float sc = (float)((scw >> (8 * (j & 3))) & 0xFF);
+                        const f32x4_t D = mfma16x16x32(A_lds[(sb * 8 + j) * 64 + a_off], h ? bhi : blo, zero);
+                        tacc += sc * D;
+                    }
                 }
+                // B slots of lane group g: {m_2g x4, m_2g+1 x4} and the same for sc
+                const uint32_t mw = g < 2 ? m_lo : m_hi, sw = g < 2 ? sc_lo : sc_hi;
+                const int k0 = (2 * g) & 3, k1 = (2 * g + 1) & 3;
+                const uint32_t m0 = byte_bf16x2(mw, k0), m1 = byte_bf16x2(mw, k1);
+                const uint32_t c0 = byte_bf16x2(sw, k0), c1 = byte_bf16x2(sw, k1);
+                const u32x4_t ab = B_lds[sb * 64 + b_off];
+                const f32x4_t Dm = mfma16x16x32(ab, (u32x4_t){m0, m0, m1, m1}, zero);
+                const f32x4_t Ds = mfma16x16x32(ab, (u32x4_t){c0, c0, c1, c1}, zero);
+                acc[tl] += d * (tacc - 128.f * Ds) - dmin * Dm;
             }
-            // B slots of lane group g: {m_2g x4, m_2g+1 x4} and the same for sc
-            const uint32_t mw = g < 2 ? m_lo : m_hi, sw = g < 2 ? sc_lo : sc_hi;
-            const int k0 = (2 * g) & 3, k1 = (2 * g + 1) & 3;
-            const uint32_t m0 = byte_bf16x2(mw, k0), m1 = byte_bf16x2(mw, k1);
-            const uint32_t c0 = byte_bf16x2(sw, k0), c1 = byte_bf16x2(sw, k1);
-            const u32x4_t ab = B_lds[sb * 64 + b_off];
-            const f32x4_t Dm = mfma16x16x32(ab, (u32x4_t){m0, m0, m1, m1}, zero);
-            const f32x4_t Ds = mfma16x16x32(ab, (u32x4_t){c0, c0, c1, c1}, zero);
-            acc += d * (tacc - 128.f * Ds) - dmin * Dm;
         }
-        const int n = t * 16 + cl;
+        // tiles past t1 (the ragged end of the last iteration) store tile 0's result
+        // again to tile 0's address: no branch around the stores (a branch there
+        // makes the compiler keep far more registers live)
+        const int tfirst = t0 + it * TP;
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const int R = 4 * g + v;
-            if (R < a.M) part[(size_t)R * a.N + n] = acc[v];
+        for (int tl = 0; tl < TP; tl++) {
+            const int t = tfirst + tl;
+            const bool real = t < t1;
+            const int n = (real ? t : tfirst) * 16 + cl;
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int R = 4 * g + v;
+                const float val = real ? acc[tl][v] : acc[0][v];
+                if (R < a.M) part[(size_t)R * a.N + n] = val;
+            }
         }
     }
 }
@@ -218,8 +247,10 @@ __global__ __launch_bounds__(256) void k_q4k_stream(Q4kFusedArgs a, int tpw) {
 
 bool q4k_stream_ok(int M, int N, int K) { return M >= 1 && M <= 16 && (K / 256) % SNSB == 0 && N % 16 == 0; }
 
-Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves) {
+Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves, int tp, int pd) {
     Q4kStreamPlan p;
+    p.tp = tp;
+    p.pd = pd;
     const int KB = K / 256, ntile = N / 16;
     p.splits = KB / SNSB;
     const long long wave_tiles = (long long)ntile * p.splits;
@@ -233,6 +264,16 @@ Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves) {
 }
 
 hipError_t launch_q4k_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st) {
-    hipLaunchKernelGGL(k_q4k_stream, dim3(p.grid_x, p.splits), dim3(256), p.lds_bytes, st, a, p.tpw);
-    return hipGetLastError();
+    const dim3 grid(p.grid_x, p.splits);
+#define QS_CASE(TP, PD)                                                                          \
+    if (p.tp == TP && p.pd == PD) {                                                               \
+        hipLaunchKernelGGL((k_q4k_stream<TP, PD>), grid, dim3(256), p.lds_bytes, st, a, p.tpw);   \
+        return hipGetLastError();                                                                 \
+    }
+    QS_CASE(1, 4)
+    QS_CASE(2, 4)
+    QS_CASE(2, 8)
+    QS_CASE(4, 8)
+#undef QS_CASE
+    return hipErrorInvalidValue;
 }

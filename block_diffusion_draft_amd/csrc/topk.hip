@@ -5,19 +5,28 @@
 // position (section "How it is used").  Candidates are ordered by (logit desc,
 // token id asc); cand_logp = logit - logsumexp(logits).
 //
-// Two passes over the fp32 logits: per (row, 1024-logit chunk) a wave keeps its
-// chunk's max, sum of exp(logit - max) and top-K; one workgroup per row then
-// merges the chunk lists and statistics.  Every selection is an arg-max under the
-// (value desc, id asc) order, so the result is exact and independent of thread
-// scheduling.
+// Threshold selection, four short passes per row of V fp32 logits:
+//  1. wave per 1024-logit chunk: the chunk's max and sum of exp(logit - max);
+//  2. wave per row: logsumexp, and theta = the K-th largest of the 64 lanes' maxima
+//     of the chunk maxima (a wave sort).  Those K maxima are K distinct logits, so
+//     the row's K-th largest logit is >= theta: every top-K candidate is >= theta;
+//  3. wave per chunk: every logit >= theta is appended to the row's candidate list
+//     (an integer atomic hands out slots; the order of the list does not matter);
+//  4. wave per row: the K best candidates by (value desc, id asc): a wave sort when
+//     at most 64 reached theta, else K rounds of arg-max.  If more than CAP logits
+//     reach theta (many equal logits), the row is selected by an exact scan of all
+//     its chunks instead.
+// Every choice is an arg-max under a total order, so the result is exact and does
+// not depend on thread scheduling.
 #include "common.h"
 #include "kernels.h"
 
 namespace {
 
 constexpr int PER_LANE = 16;
-constexpr int CHUNK = 64 * PER_LANE;     // logits per wave in the first pass
-constexpr int LPT = 4;                   // chunk lists per thread in the merge
+constexpr int CHUNK = 64 * PER_LANE;     // logits per wave in passes 1 and 3
+constexpr int CAP = 1024;                // candidate slots per row
+constexpr int CPL = CAP / 64;            // candidates per lane in pass 4
 
 __device__ __forceinline__ bool take(float v, int i, float bv, int bi) {
     return i >= 0 && (bi < 0 || cand_better(v, i, bv, bi));
@@ -32,22 +41,50 @@ __device__ __forceinline__ void wave_best(float &v, int &i) {
     }
 }
 
-// One wave per 1024-logit chunk of one row: chunk max, sum of exp(logit - max)
-// and the chunk's top-K in (value desc, id asc) order, with shuffles only.
-__global__ __launch_bounds__(256) void k_topk_partial(const float *logits, int V, int K, int nch,
-                                                      float *pv, int32_t *pi, float *pm,
-                                                      float *ps) {
+// (value desc, id asc) as one unsigned 64-bit key: larger key = better candidate
+__device__ __forceinline__ unsigned long long cand_key(float v, int id) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);    // order-preserving
+    return ((unsigned long long)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+__device__ __forceinline__ float key_value(unsigned long long k) {
+    const uint32_t o = (uint32_t)(k >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int key_id(unsigned long long k) {
+    return (int)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+// bitonic sort of one value per lane across the wave, descending (lane 0 = largest)
+template <class Key>
+__device__ __forceinline__ Key wave_sort_desc(Key x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const Key o = __shfl_xor(x, j, WAVE);
+            const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+            x = keep_max ? (x > o ? x : o) : (x < o ? x : o);
+        }
+    }
+    return x;
+}
+
+// 1. chunk max and sum of exp(logit - max)
+__global__ __launch_bounds__(256) void k_chunk_stats(const float *logits, int V, int nch, float *pm,
+                                                     float *ps) {
     const int lane = threadIdx.x & 63;
     const int c = blockIdx.x * 4 + (threadIdx.x >> 6), r = blockIdx.y;
     if (c >= nch) return;
-    const int base = c * CHUNK;
-    const float *row = logits + (size_t)r * V;
+    const float *row = logits + (size_t)r * V + (size_t)c * CHUNK;
+    const int n = min(CHUNK, V - c * CHUNK);
     float val[PER_LANE];
     float mx = -INFINITY;
 #pragma unroll
     for (int k = 0; k < PER_LANE; k++) {
-        const int id = base + lane + 64 * k;
-        val[k] = id < V ? row[id] : -INFINITY;
+        const int i = lane + 64 * k;
+        val[k] = i < n ? row[i] : -INFINITY;
         mx = fmaxf(mx, val[k]);
     }
     mx = wave_max(mx);
@@ -55,107 +92,195 @@ __global__ __launch_bounds__(256) void k_topk_partial(const float *logits, int V
 #pragma unroll
     for (int k = 0; k < PER_LANE; k++) se += val[k] == -INFINITY ? 0.f : expf(val[k] - mx);
     se = wave_sum(se);
-    const size_t o = (size_t)r * nch + c;
     if (lane == 0) {
-        pm[o] = mx;
-        ps[o] = se;
-    }
-    for (int round = 0; round < K; round++) {
-        float bv = -INFINITY;
-        int bi = -1;
-#pragma unroll
-        for (int k = 0; k < PER_LANE; k++) {
-            const int id = base + lane + 64 * k;
-            if (val[k] != -INFINITY && take(val[k], id, bv, bi)) { bv = val[k]; bi = id; }
-        }
-        wave_best(bv, bi);
-        if (lane == 0) {
-            pv[o * K + round] = bv;
-            pi[o * K + round] = bi;
-        }
-#pragma unroll
-        for (int k = 0; k < PER_LANE; k++)
-            if (base + lane + 64 * k == bi) val[k] = -INFINITY;
+        pm[(size_t)r * nch + c] = mx;
+        ps[(size_t)r * nch + c] = se;
     }
 }
 
-// One workgroup per row: log-sum-exp from the chunk statistics, then a K-way
-// selection over the chunks' sorted lists (each thread owns up to LPT lists and
-// offers the best of their heads each round).
-__global__ __launch_bounds__(256) void k_topk_merge(const float *pv, const int32_t *pi,
-                                                    const float *pm, const float *ps, int nch,
-                                                    int K, int rows_per_seq, const int32_t *valid,
-                                                    int32_t *cand_ids, float *cand_logp) {
-    __shared__ float sf[4];
-    __shared__ float wv[4];
-    __shared__ int wi[4];
-    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// 2. one wave per row: logsumexp and the threshold; resets the row's candidate count
+__global__ __launch_bounds__(64) void k_row_threshold(const float *pm, const float *ps, int nch, int K,
+                                                      float *thr, float *lse, int *count) {
+    const int r = blockIdx.x, lane = threadIdx.x;
+    float m[PER_LANE], s[PER_LANE];
     float mx = -INFINITY;
-    for (int c = tid; c < nch; c += 256) mx = fmaxf(mx, pm[(size_t)r * nch + c]);
-    mx = wave_max(mx);
-    if (lane == 0) sf[wave] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(sf[0], sf[1]), fmaxf(sf[2], sf[3]));
-    __syncthreads();
-    float se = 0.f;
-    for (int c = tid; c < nch; c += 256) {
-        const float m = pm[(size_t)r * nch + c];
-        if (m != -INFINITY) se += ps[(size_t)r * nch + c] * expf(m - mx);
+#pragma unroll
+    for (int k = 0; k < PER_LANE; k++) {
+        const int c = lane + 64 * k;
+        m[k] = c < nch ? pm[(size_t)r * nch + c] : -INFINITY;
+        s[k] = c < nch ? ps[(size_t)r * nch + c] : 0.f;
+        mx = fmaxf(mx, m[k]);
     }
+    mx = wave_max(mx);
+    float se = 0.f;
+#pragma unroll
+    for (int k = 0; k < PER_LANE; k++) se += m[k] == -INFINITY ? 0.f : s[k] * expf(m[k] - mx);
     se = wave_sum(se);
-    if (lane == 0) sf[wave] = se;
-    __syncthreads();
-    const float lse = mx + logf((sf[0] + sf[1]) + (sf[2] + sf[3]));
-    const bool ok = valid[r / rows_per_seq] != 0;
-    int ptr[LPT];
+    // theta = the K-th largest of the 64 lane maxima (each lane maximum is a chunk
+    // maximum, i.e. a distinct logit, so K logits are >= theta)
+    float lm = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < LPT; q++) ptr[q] = 0;
-    for (int round = 0; round < K; round++) {
-        float bv = -INFINITY;
-        int bi = -1, bq = -1;
+    for (int k = 0; k < PER_LANE; k++) lm = fmaxf(lm, m[k]);
+    const float sorted = wave_sort_desc(lm);
+    const float th = __shfl(sorted, K - 1, WAVE);
+    if (lane == 0) {
+        thr[r] = th;
+        lse[r] = mx + logf(se);
+        count[r] = 0;
+    }
+}
+
+// 3. wave per chunk: append the logits >= theta to the row's candidate list
+__global__ __launch_bounds__(256) void k_collect(const float *logits, int V, int nch, const float *thr,
+                                                 int *count, float *cv, int32_t *ci) {
+    const int lane = threadIdx.x & 63;
+    const int c = blockIdx.x * 4 + (threadIdx.x >> 6), r = blockIdx.y;
+    if (c >= nch) return;
+    const float th = thr[r];
+    const float *row = logits + (size_t)r * V + (size_t)c * CHUNK;
+    const int n = min(CHUNK, V - c * CHUNK);
+    float val[PER_LANE];
+    unsigned long long mask[PER_LANE];
+    int total = 0;
 #pragma unroll
-        for (int q = 0; q < LPT; q++) {
-            const int c = tid + 256 * q;
-            if (c < nch && ptr[q] < K) {
-                const size_t at = ((size_t)r * nch + c) * K + ptr[q];
-                const int id = pi[at];
-                const float v = pv[at];
-                if (take(v, id, bv, bi)) { bv = v; bi = id; bq = q; }
+    for (int k = 0; k < PER_LANE; k++) {
+        const int i = lane + 64 * k;
+        val[k] = i < n ? row[i] : -INFINITY;
+        mask[k] = __ballot(i < n && val[k] >= th);
+        total += __popcll(mask[k]);
+    }
+    if (total == 0) return;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(count + r, total);
+    base = __shfl(base, 0, WAVE);
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int off = base;
+#pragma unroll
+    for (int k = 0; k < PER_LANE; k++) {
+        if ((mask[k] >> lane) & 1ull) {
+            const int slot = off + __popcll(mask[k] & below);
+            if (slot < CAP) {
+                cv[(size_t)r * CAP + slot] = val[k];
+                ci[(size_t)r * CAP + slot] = c * CHUNK + lane + 64 * k;
             }
         }
-        float wbv = bv;
-        int wbi = bi;
-        wave_best(wbv, wbi);
-        __syncthreads();
-        if (lane == 0) { wv[wave] = wbv; wi[wave] = wbi; }
-        __syncthreads();
-        float gv = wv[0];
-        int gi = wi[0];
-        for (int w = 1; w < 4; w++)
-            if (take(wv[w], wi[w], gv, gi)) { gv = wv[w]; gi = wi[w]; }
-        if (bi >= 0 && bi == gi) ptr[bq]++;          // ids are unique across lists
-        if (tid == 0) {
-            cand_ids[(size_t)r * K + round] = ok ? gi : -1;
-            cand_logp[(size_t)r * K + round] = ok && gi >= 0 ? gv - lse : -INFINITY;
+        off += __popcll(mask[k]);
+    }
+}
+
+// 4. wave per row: exact top-K of the candidates (or of the whole row on overflow)
+__global__ __launch_bounds__(64) void k_select(const float *logits, int V, int nch, int K,
+                                               const int *count, const float *cv, const int32_t *ci,
+                                               const float *lse, int rows_per_seq,
+                                               const int32_t *valid, int32_t *cand_ids,
+                                               float *cand_logp) {
+    const int r = blockIdx.x, lane = threadIdx.x;
+    const bool ok = valid[r / rows_per_seq] != 0;
+    if (!ok) {
+        if (lane < K) {
+            cand_ids[(size_t)r * K + lane] = -1;
+            cand_logp[(size_t)r * K + lane] = -INFINITY;
         }
+        return;
+    }
+    const float L = lse[r];
+    const int n = count[r];
+    if (n <= 64) {
+        // one candidate per lane: sort the wave, the first K lanes are the answer
+        const unsigned long long key = lane < n ? cand_key(cv[(size_t)r * CAP + lane],
+                                                           ci[(size_t)r * CAP + lane])
+                                                : 0ull;
+        const unsigned long long sk = wave_sort_desc(key);
+        if (lane < K) {
+            const bool have = lane < n;
+            cand_ids[(size_t)r * K + lane] = have ? key_id(sk) : -1;
+            cand_logp[(size_t)r * K + lane] = have ? key_value(sk) - L : -INFINITY;
+        }
+        return;
+    }
+    if (n <= CAP) {
+        float v[CPL];
+        int id[CPL];
+#pragma unroll
+        for (int k = 0; k < CPL; k++) {
+            const int s = lane + 64 * k;
+            v[k] = s < n ? cv[(size_t)r * CAP + s] : -INFINITY;
+            id[k] = s < n ? ci[(size_t)r * CAP + s] : -1;
+        }
+        for (int round = 0; round < K; round++) {
+            float bv = -INFINITY;
+            int bi = -1;
+#pragma unroll
+            for (int k = 0; k < CPL; k++)
+                if (take(v[k], id[k], bv, bi)) { bv = v[k]; bi = id[k]; }
+            wave_best(bv, bi);
+#pragma unroll
+            for (int k = 0; k < CPL; k++)
+                if (id[k] == bi) id[k] = -1;
+            if (lane == 0) {
+                cand_ids[(size_t)r * K + round] = bi;
+                cand_logp[(size_t)r * K + round] = bi >= 0 ? bv - L : -INFINITY;
+            }
+        }
+        return;
+    }
+    // overflow: running top-K over every chunk of the row (lanes < K hold the list)
+    float lv = -INFINITY;
+    int li = -1;
+    const float *row = logits + (size_t)r * V;
+    for (int c = 0; c < nch; c++) {
+        float v[PER_LANE];
+        int id[PER_LANE];
+#pragma unroll
+        for (int k = 0; k < PER_LANE; k++) {
+            const int i = c * CHUNK + lane + 64 * k;
+            v[k] = i < V ? row[i] : -INFINITY;
+            id[k] = i < V ? i : -1;
+        }
+        float nv = -INFINITY;
+        int ni = -1;
+        for (int round = 0; round < K; round++) {
+            float bv = lv;
+            int bi = li;
+#pragma unroll
+            for (int k = 0; k < PER_LANE; k++)
+                if (take(v[k], id[k], bv, bi)) { bv = v[k]; bi = id[k]; }
+            wave_best(bv, bi);
+            if (li == bi) li = -1;
+#pragma unroll
+            for (int k = 0; k < PER_LANE; k++)
+                if (id[k] == bi) id[k] = -1;
+            if (lane == round) { nv = bv; ni = bi; }
+        }
+        lv = nv;
+        li = ni;
+    }
+    if (lane < K) {
+        cand_ids[(size_t)r * K + lane] = li;
+        cand_logp[(size_t)r * K + lane] = li >= 0 ? lv - L : -INFINITY;
     }
 }
 
 }  // namespace
 
-hipError_t launch_topk_partial(const float *logits, int R, int V, int chunk, int K, float *pv,
-                               int32_t *pi, float *pm, float *ps, hipStream_t st) {
-    (void)chunk;
+size_t topk_workspace_floats(int R, int V) {
     const int nch = ceil_div(V, CHUNK);
-    dim3 grid(ceil_div(nch, 4), R);
-    hipLaunchKernelGGL(k_topk_partial, grid, dim3(256), 0, st, logits, V, K, nch, pv, pi, pm, ps);
-    return hipGetLastError();
+    return (size_t)R * (2 * nch + 3 + 2 * CAP);
 }
 
-hipError_t launch_topk_merge(const float *pv, const int32_t *pi, const float *pm, const float *ps,
-                             int R, int n_chunks, int K, int rows_per_seq, const int32_t *valid,
-                             int32_t *cand_ids, float *cand_logp, hipStream_t st) {
-    hipLaunchKernelGGL(k_topk_merge, dim3(R), dim3(256), 0, st, pv, pi, pm, ps, n_chunks, K,
+hipError_t launch_topk(const float *logits, int R, int V, int K, int rows_per_seq,
+                       const int32_t *valid, float *ws, int32_t *cand_ids, float *cand_logp,
+                       hipStream_t st) {
+    const int nch = ceil_div(V, CHUNK);
+    float *pm = ws, *ps = pm + (size_t)R * nch, *thr = ps + (size_t)R * nch, *lse = thr + R;
+    int *count = reinterpret_cast<int *>(lse + R);
+    float *cv = reinterpret_cast<float *>(count + R);
+    int32_t *ci = reinterpret_cast<int32_t *>(cv + (size_t)R * CAP);
+    const dim3 grid(ceil_div(nch, 4), R);
+    hipLaunchKernelGGL(k_chunk_stats, grid, dim3(256), 0, st, logits, V, nch, pm, ps);
+    hipLaunchKernelGGL(k_row_threshold, dim3(R), dim3(64), 0, st, pm, ps, nch, K, thr, lse, count);
+    hipLaunchKernelGGL(k_collect, grid, dim3(256), 0, st, logits, V, nch, thr, count, cv, ci);
+    hipLaunchKernelGGL(k_select, dim3(R), dim3(64), 0, st, logits, V, nch, K, count, cv, ci, lse,
                        rows_per_seq, valid, cand_ids, cand_logp);
     return hipGetLastError();
 }

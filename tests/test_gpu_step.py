@@ -171,3 +171,23 @@ def test_full_step_b1_parity():
     ref = parity.run_oracle(wl, bufs.host_W, bufs.inputs)
     g = full_check(wl, bufs, ref)
     check_verify(bufs, g)
+
+
+def test_tiny_step_tied_logits_take_lowest_ids():
+    """Every output-head row equal: all logits of a row tie, more of them reach the
+    selection threshold than the candidate list holds, and the exact fallback scan
+    must return ids 0..K-1 (ties broken by id) with log-prob -log(V)."""
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], seed=15)
+    say("[step] tiny tied logits")
+    W = synth.make_weights(wl.shape, wl.seed)
+    E = np.repeat(W["embed"][:1], wl.shape.vocab, axis=0)
+    W["embed"] = E
+    W["lm_head"] = E
+    bufs = runner.StepBuffers(wl, weights=W)
+    bufs.step()
+    g = gpu_outputs(bufs)
+    K, V = wl.shape.top_k, wl.shape.vocab
+    assert (g["ids"] == np.arange(K)).all()
+    assert np.allclose(g["lp"], -np.log(V), atol=1e-4)
+    ref = parity.run_oracle(wl, W, bufs.inputs)
+    assert (ref["cand_ids"] == np.arange(K)).all()
