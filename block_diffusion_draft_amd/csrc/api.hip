@@ -61,7 +61,8 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
     p.attn_nch = win > 0 ? (win + p.attn_chunk - 1) / p.attn_chunk : 0;
     p.topk_nch = (p.V + topk_chunk_size() - 1) / topk_chunk_size();
     // output-head rows held in LDS: K/32 fragments of 512 bytes (+1 zero entry)
-    p.lm_skinny = p.R <= 8 && p.H % 256 == 0 && ((size_t)(p.H / 32) * 32 + 1) * 16 <= 160 * 1024;
+    p.lm_skinny = p.R <= 8 && p.H % 256 == 0 &&
+                  ((size_t)(p.H / 32) * 32 + 16 + 8 * 512) * 16 <= 160 * 1024;
 
     size_t part = 0;
     const int fmt = c->weight_fmt;

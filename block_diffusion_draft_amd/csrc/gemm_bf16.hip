@@ -188,6 +188,103 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a, int ti
     }
 }
 
+// Output head for at most 8 activation rows, weights read as whole cache lines.
+// One workgroup of 8 waves per CU; the rows sit in LDS in MFMA lane order.  A wave
+// streams its run of 16-row weight tiles in groups of 16 rows x 128 columns: each of a
+// group's 4 loads reads 4 rows x 256 contiguous bytes (non-temporal: read once), so
+// every load covers full lines.  The group passes through a 4 KB per-wave LDS buffer
+// (16-byte chunks XOR-swizzled by row: conflict-free writes and fragment reads) into
+// MFMA lane order.  Groups are loaded HS_D - 1 ahead in registers, across tiles.
+constexpr int HS_WAVES = 8;
+constexpr int HS_D = 4;
+
+__global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a, int tiles_per_wave) {
+    extern __shared__ __align__(16) u32x4_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, c = lane & 15;
+    const int nks = a.K / 32;
+    const int ngr = a.K / 128;                       // groups per tile, a multiple of HS_D
+    const int ntiles = a.N / 16;
+    const int t0 = (blockIdx.x * HS_WAVES + wave) * tiles_per_wave;
+    const int t1 = min(t0 + tiles_per_wave, ntiles);
+    const int nst = t1 > t0 ? (t1 - t0) * ngr : 0;
+    const int tlast = (t1 > t0 ? t1 : ntiles) - 1;
+    u32x4_t *Alds = lds;                                          // [nks][32] + zero entry
+    u32x4_t *Tb = lds + nks * 32 + 16 + wave * 512;               // 2 x [16 rows][16 chunks]
+
+    // load lane mapping: row 4 i + lr of the tile, 16-byte chunk ls of the group
+    const int lr = lane >> 4, ls = lane & 15;
+    const uint16_t *Wl = a.w[0] + (size_t)lr * a.K + 8 * ls;
+    int lt = t0, lq = 0, nload = 0;
+    auto load_group = [&](u32x4_t (&v)[4]) {
+        const bool ok = nload < nst;
+        const int tt = ok ? lt : tlast, qq = ok ? lq : ngr - 1;
+        const uint16_t *p = Wl + (size_t)tt * 16 * a.K + qq * 128;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p + (size_t)(4 * i) * a.K));
+        nload++;
+        lq++;
+        const bool wrap = lq == ngr;
+        lq = wrap ? 0 : lq;
+        lt += wrap ? 1 : 0;
+    };
+    u32x4_t ring[HS_D][4];
+#pragma unroll
+    for (int u = 0; u < HS_D - 1; u++) load_group(ring[u]);
+
+    for (int e = tid; e < nks * 32 + 16; e += 512) {
+        const int ks = e >> 5, slot = e & 31, gg = slot >> 3, r = slot & 7;
+        u32x4_t v = {0, 0, 0, 0};
+        if (e < nks * 32 && r < a.M)
+            v = *reinterpret_cast<const u32x4_t *>(a.A + (size_t)r * a.lda + ks * 32 + 8 * gg);
+        Alds[e] = v;
+    }
+    __syncthreads();
+
+    float inv8[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++) inv8[r] = r < a.M ? row_inv(a.rs, r) : 0.f;
+    float rinv[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) rinv[v] = g == 0 ? inv8[v] : (g == 1 ? inv8[4 + v] : 0.f);
+
+    // lanes of rows >= 8 read the zero entry
+    const int aoff = c < 8 ? g * 8 + c : 0;
+    const int astep = c < 8 ? 32 : 0;
+    const int abase = c < 8 ? 0 : nks * 32;
+    for (int tile = t0; tile < t1; tile++) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int q0 = 0; q0 < ngr; q0 += HS_D) {
+#pragma unroll
+            for (int u = 0; u < HS_D; u++) {
+                load_group(ring[(u + HS_D - 1) % HS_D]);
+                u32x4_t *T = Tb + (u & 1) * 256;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int r = 4 * i + lr;
+                    T[r * 16 + (ls ^ r)] = ring[u][i];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const u32x4_t bf = T[c * 16 + ((4 * j + g) ^ c)];
+                    const u32x4_t af = Alds[abase + ((q0 + u) * 4 + j) * astep + aoff];
+                    acc = mfma16x16x32(af, bf, acc);
+                }
+            }
+        }
+        if (g < 2) {
+            const int n = tile * 16 + c;
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int m = 4 * g + v;
+                if (m < a.M) a.C[(size_t)m * a.ldc + n] = acc[v] * rinv[v];
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st) {
@@ -198,6 +295,21 @@ hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st) {
 
 hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st) {
     const int ntiles = a.N / 16;
+    if (a.K % (128 * HS_D) == 0) {
+        // one workgroup of HS_WAVES waves per CU
+        const int tpw = ceil_div(ntiles, 256 * HS_WAVES);
+        const int waves = ceil_div(ntiles, tpw);
+        const size_t lds = ((size_t)(a.K / 32) * 32 + 16 + HS_WAVES * 512) * 16;
+        static size_t hs_lds_set = 0;
+        if (lds > hs_lds_set) {
+            hipError_t e = hipFuncSetAttribute((const void *)k_head_stream,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            hs_lds_set = lds;
+        }
+        hipLaunchKernelGGL(k_head_stream, dim3(ceil_div(waves, HS_WAVES)), dim3(512), lds, st, a, tpw);
+        return hipGetLastError();
+    }
     const int tpw = ceil_div(ntiles, 2048);               // ~2048 waves, 2 workgroups per CU
     const int waves = ceil_div(ntiles, tpw);
     const size_t lds = ((size_t)(a.K / 32) * 32 + 1) * 16;
