@@ -129,11 +129,11 @@ hipError_t launch_q4k_fused(const Q4kFusedArgs &a, const Q4kFusedPlan &p, hipStr
 // each wave streams tpw consecutive column tiles.  Same partial layout [splits][M][N].
 struct Q4kStreamPlan {
     int splits, tpw, grid_x;
-    int tp, pd;                  // column tiles per loop iteration, stages in flight
+    int wpg;                     // waves per workgroup
     size_t lds_bytes, part_bytes;
 };
 bool q4k_stream_ok(int M, int N, int K);
-Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves = 2048, int tp = 1, int pd = 4);
+Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves = 2048, int wpg = 4);
 hipError_t launch_q4k_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st);
 
 // Output rows r < M_out: v = sum over splits of partial rows r (+ r + pair), N a multiple

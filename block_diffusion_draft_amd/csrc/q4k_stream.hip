@@ -36,11 +36,13 @@ struct SStage {
     u32x2_t q[4];              // 8 nibble bytes of each 32-byte chunk, lane group g
 };
 
-__device__ __forceinline__ SStage s_load(const unsigned char *blk, int g) {
+// one stage: a wave-uniform base address plus this lane's 32-bit byte offsets: the
+// column's super-block (header) and lane group g's 8 bytes within it (+ 8 g)
+__device__ __forceinline__ SStage s_load(const unsigned char *base, uint32_t off, uint32_t goff) {
     SStage s;
-    s.hdr = *reinterpret_cast<const u32x4_t *>(blk);
+    s.hdr = *reinterpret_cast<const u32x4_t *>(base + off);
 #pragma unroll
-    for (int c = 0; c < 4; c++) s.q[c] = *reinterpret_cast<const u32x2_t *>(blk + 16 + 32 * c + 8 * g);
+    for (int c = 0; c < 4; c++) s.q[c] = *reinterpret_cast<const u32x2_t *>(base + (off + goff + 16 + 32 * c));
     return s;
 }
 
@@ -61,17 +63,18 @@ __device__ __forceinline__ void s_decode(u32x2_t q, u32x4_t &lo, u32x4_t &hi) {
     hi.w = __builtin_amdgcn_perm(C, hy, 0x04030402u);
 }
 
-// bf16 of the small non-negative integer in byte k of w, in both halves
-__device__ __forceinline__ uint32_t byte_bf16x2(uint32_t w, int k) {
-    const uint32_t fb = __float_as_uint((float)((w >> (8 * k)) & 0xFF));
-    return (fb >> 16) | (fb & 0xFFFF0000u);
+// bias B operand of lane group g: bf16(v_{2g}) | bf16(v_{2g+1}) << 16 for the 6-bit
+// values v_0..3 in the bytes of lo and v_4..7 in the bytes of hi (sel picks bytes 2g,
+// 2g+1 of {hi, lo})
+__device__ __forceinline__ uint32_t bias_pair(uint32_t lo, uint32_t hi, uint32_t sel) {
+    const uint32_t y = __builtin_amdgcn_perm(hi, lo, sel);
+    const float fa = (float)(y & 0xFF), fb = (float)((y >> 8) & 0xFF);
+    return __builtin_amdgcn_perm(__float_as_uint(fb), __float_as_uint(fa), 0x07060302u);
 }
 
-template <int TP, int PD>
-__global__ __launch_bounds__(256)
-void k_q4k_stream(Q4kFusedArgs a, int tpw) {
-    constexpr int SPI = SNSB * TP;                  // stages per loop iteration
-    static_assert(SPI % PD == 0, "ring slots must be static");
+template <int WPG>
+__global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw) {
+    constexpr int NT = 64 * WPG;                    // threads per workgroup
     extern __shared__ __align__(16) unsigned char lds[];
     u32x4_t *A_lds = reinterpret_cast<u32x4_t *>(lds);              // [SNSB][8][64]
     u32x4_t *B_lds = A_lds + SNSB * 8 * 64;                          // [SNSB][64]
@@ -82,48 +85,41 @@ void k_q4k_stream(Q4kFusedArgs a, int tpw) {
     const int g = lane >> 4, cl = lane & 15;
     const int split = blockIdx.y, sb0 = split * SNSB;
     const int ntile = a.N / 16;
-    const int t0 = (blockIdx.x * 4 + wave) * tpw;
+    const int t0 = (blockIdx.x * WPG + wave) * tpw;
     const int t1 = min(t0 + tpw, ntile);
-    const int nit = t1 > t0 ? (t1 - t0 + TP - 1) / TP : 0;   // iterations of TP tiles
-    const int nst = nit * SPI;
     const int tlast = (t1 > t0 ? t1 : ntile) - 1;       // clamp target, always a real tile
 
-    // ---- weight stream: (tile, super-block) stages in order, clamped past the end.
-    // The stage address is a wave-uniform base (scalar registers) plus a per-lane
-    // offset that never changes: column cl's row and lane group g's 8 bytes.
+    // ---- weight stream.  Stage (tile t, super-block sb) sits at tile_base(t) + sb * 144
+    // + this lane's offset (column cl's row, lane group g's bytes); loads run 3 stages
+    // ahead, so tile t's loop issues (t, 3) and (t + 1, 0..2); tiles past t1 - 1 clamp
+    // to tlast (in bounds, unused).
     const int row_bytes = a.KB * 144;
-    const int lane_off = cl * row_bytes + sb0 * 144;
-    // stream order: iteration, super-block, tile of the iteration
-    int lit = t0, lsb = 0, ltl = 0, nload = 0;
-    auto load_next = [&]() -> SStage {
-        const int traw = lit + ltl;
-        const bool ok = nload < nst && traw < t1;
-        const int tt = ok ? traw : tlast, sbb = ok ? lsb : SNSB - 1;
+    const uint32_t lane_off = (uint32_t)(cl * row_bytes + sb0 * 144), goff = 8 * g;
+    auto tile_base = [&](int t) -> const unsigned char * {
+        const int tt = t < t1 ? t : tlast;
         const int c16 = tt * 16;
         const int si = (a.nseg > 1 && c16 >= a.seg_end[0]) + (a.nseg > 2 && c16 >= a.seg_end[1]);
         const unsigned char *wseg = si == 0 ? a.w[0] : (si == 1 ? a.w[1] : a.w[2]);
         const int nbase = si == 0 ? 0 : (si == 1 ? a.seg_end[0] : a.seg_end[1]);
-        const unsigned char *ubase = wseg + (size_t)(c16 - nbase) * row_bytes + sbb * 144;
-        nload++;
-        ltl++;
-        const bool wt = ltl == TP;
-        ltl = wt ? 0 : ltl;
-        lsb += wt ? 1 : 0;
-        const bool ws = lsb == SNSB;
-        lsb = ws ? 0 : lsb;
-        lit += ws ? TP : 0;
-        return s_load(ubase + lane_off, g);
+        return wseg + (size_t)(c16 - nbase) * row_bytes;
     };
-    SStage st[PD];
-#pragma unroll
-    for (int u = 0; u < PD - 1; u++) st[u] = load_next();
+    auto stage = [&](const unsigned char *tb, int sb) -> SStage {
+        return s_load(tb + sb * 144, lane_off, goff);
+    };
+    SStage st[4];
+    {
+        const unsigned char *b0 = tile_base(t0);
+        st[0] = stage(b0, 0);
+        st[1] = stage(b0, 1);
+        st[2] = stage(b0, 2);
+    }
 
     // ---- activations of this split -> LDS (lane order), sub-block sums S
-    constexpr int PER = SNSB * 8 * 64 / 256;
+    constexpr int PER = SNSB * 8 * 64 / NT;
     u32x4_t av[PER];
 #pragma unroll
     for (int i = 0; i < PER; i++) {
-        const int e = tid + 256 * i;
+        const int e = tid + NT * i;
         const int ln = e & 63, rest = e >> 6;
         const int j = rest & 7, sbi = rest >> 3;
         const int R = ln & 15;
@@ -134,7 +130,7 @@ void k_q4k_stream(Q4kFusedArgs a, int tpw) {
     }
 #pragma unroll
     for (int i = 0; i < PER; i++) {
-        const int e = tid + 256 * i;
+        const int e = tid + NT * i;
         const int ln = e & 63, rest = e >> 6;
         const u32x4_t v = av[i];
         float s = 0.f;
@@ -148,97 +144,79 @@ void k_q4k_stream(Q4kFusedArgs a, int tpw) {
         if ((ln >> 4) == 0) S_lds[rest * 16 + (ln & 15)] = s;
     }
     __syncthreads();
-    // bias operand: lane (row r, group gg) holds S_j for j = 2 gg, 2 gg + 1 as four bf16
-    // terms each (8 + 8 + 8 + 8 bits >= the 24 of an fp32 significand: exact)
-    {
+    // bias A operand: lane (row r, group gg) holds S_a, S_b (a = 2 gg, b = 2 gg + 1) as
+    // four bf16 terms each (8 + 8 + 8 + 8 bits >= the 24 of an fp32 significand: exact),
+    // interleaved: dword q = term q of S_a | term q of S_b << 16
+    if (tid < SNSB * 64) {
         const int sbi = tid >> 6, ln = tid & 63;
         const int r = ln & 15, gg = ln >> 4;
-        uint32_t o[4];
+        uint16_t t[2][4];
 #pragma unroll
         for (int jj = 0; jj < 2; jj++) {
             float rem = S_lds[(sbi * 8 + 2 * gg + jj) * 16 + r];
-            uint16_t t[4];
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                t[q] = f32_to_bf16(rem);
-                rem -= bf16_to_f32(t[q]);
+                t[jj][q] = f32_to_bf16(rem);
+                rem -= bf16_to_f32(t[jj][q]);
             }
-            o[2 * jj] = (uint32_t)t[0] | ((uint32_t)t[1] << 16);
-            o[2 * jj + 1] = (uint32_t)t[2] | ((uint32_t)t[3] << 16);
         }
-        B_lds[tid] = (u32x4_t){o[0], o[1], o[2], o[3]};
+        B_lds[tid] = (u32x4_t){(uint32_t)t[0][0] | ((uint32_t)t[1][0] << 16),
+                               (uint32_t)t[0][1] | ((uint32_t)t[1][1] << 16),
+                               (uint32_t)t[0][2] | ((uint32_t)t[1][2] << 16),
+                               (uint32_t)t[0][3] | ((uint32_t)t[1][3] << 16)};
     }
     __syncthreads();
 
     // ---- stream
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
     float *part = a.part + (size_t)split * a.M * a.N;
+    const uint32_t bsel = 0x0C0C0000u | ((uint32_t)(2 * g + 1) << 8) | (uint32_t)(2 * g);
     int a_off = lane, b_off = lane;
-#pragma nounroll
-    for (int it = 0; it < nit; it++) {
+    for (int t = t0; t < t1; t++) {
         // opaque to the compiler: keeps the 32 activation fragments in LDS instead of
         // hoisting them into registers (which would cost waves per SIMD)
         asm volatile("" : "+v"(a_off), "+v"(b_off));
-        f32x4_t acc[TP];
-#pragma unroll
-        for (int tl = 0; tl < TP; tl++) acc[tl] = zero;
+        const unsigned char *bcur = tile_base(t), *bnext = tile_base(t + 1);
+        f32x4_t acc = zero;
 #pragma unroll
         for (int sb = 0; sb < SNSB; sb++) {
+            st[(sb + 3) & 3] = sb == 0 ? stage(bcur, 3) : stage(bnext, sb - 1);
+            // keep the loads here, 3 stages ahead of their use (left alone, the
+            // scheduler sinks them to the end of the tile and the latency shows)
+            __builtin_amdgcn_sched_barrier(0);
+            const SStage &w = st[sb];
+            const float d = half_bits_to_f32(w.hdr.x & 0xFFFF);
+            const float dmin = half_bits_to_f32(w.hdr.x >> 16);
+            const uint32_t s0w = w.hdr.y, s1w = w.hdr.z, s2w = w.hdr.w;
+            const uint32_t sc_lo = s0w & 0x3F3F3F3Fu;
+            const uint32_t m_lo = s1w & 0x3F3F3F3Fu;
+            const uint32_t sc_hi = (s2w & 0x0F0F0F0Fu) | ((s0w >> 2) & 0x30303030u);
+            const uint32_t m_hi = ((s2w >> 4) & 0x0F0F0F0Fu) | ((s1w >> 2) & 0x30303030u);
+            f32x4_t tacc = zero;
 #pragma unroll
-            for (int tl = 0; tl < TP; tl++) {
-                const int slot = sb * TP + tl;
-                st[(slot + PD - 1) % PD] = load_next();
-                // keep each stage's work in program order: loads issued here, this
-                // stage's LDS reads and math not hoisted into earlier stages
-                __builtin_amdgcn_sched_barrier(0);
-                const SStage &w = st[slot % PD];
-                const float d = half_bits_to_f32(w.hdr.x & 0xFFFF);
-                const float dmin = half_bits_to_f32(w.hdr.x >> 16);
-                const uint32_t s0w = w.hdr.y, s1w = w.hdr.z, s2w = w.hdr.w;
-                const uint32_t sc_lo = s0w & 0x3F3F3F3Fu;
-                const uint32_t m_lo = s1w & 0x3F3F3F3Fu;
-                const uint32_t sc_hi = (s2w & 0x0F0F0F0Fu) | ((s0w >> 2) & 0x30303030u);
-                const uint32_t m_hi = ((s2w >> 4) & 0x0F0F0F0Fu) | ((s1w >> 2) & 0x30303030u);
-                f32x4_t tacc = zero;
+            for (int c = 0; c < 4; c++) {
+                u32x4_t blo, bhi;
+                s_decode(w.q[c], blo, bhi);
 #pragma unroll
-                for (int c = 0; c < 4; c++) {
-                    u32x4_t blo, bhi;
-                    s_decode(w.q[c], blo, bhi);
-#pragma unroll
-                    for (int h = 0; h < 2; h++) {
-                        const int j = 2 * c + h;
-                        const uint32_t scw = j < 4 ? sc_lo : sc_hi;
-                        const float sc = (float)((scw >> (8 * (j & 3))) & 0xFF);
-                        const f32x4_t D = mfma16x16x32(A_lds[(sb * 8 + j) * 64 + a_off], h ? bhi : blo, zero);
-                        tacc += sc * D;
-                    }
+                for (int h = 0; h < 2; h++) {
+                    const int j = 2 * c + h;
+                    const uint32_t scw = j < 4 ? sc_lo : sc_hi;
+                    const float sc = (float)((scw >> (8 * (j & 3))) & 0xFF);
+                    const f32x4_t D = mfma16x16x32(A_lds[(sb * 8 + j) * 64 + a_off], h ? bhi : blo, zero);
+                    tacc += sc * D;
                 }
-                // B slots of lane group g: {m_2g x4, m_2g+1 x4} and the same for sc
-                const uint32_t mw = g < 2 ? m_lo : m_hi, sw = g < 2 ? sc_lo : sc_hi;
-                const int k0 = (2 * g) & 3, k1 = (2 * g + 1) & 3;
-                const uint32_t m0 = byte_bf16x2(mw, k0), m1 = byte_bf16x2(mw, k1);
-                const uint32_t c0 = byte_bf16x2(sw, k0), c1 = byte_bf16x2(sw, k1);
-                const u32x4_t ab = B_lds[sb * 64 + b_off];
-                const f32x4_t Dm = mfma16x16x32(ab, (u32x4_t){m0, m0, m1, m1}, zero);
-                const f32x4_t Ds = mfma16x16x32(ab, (u32x4_t){c0, c0, c1, c1}, zero);
-                acc[tl] += d * (tacc - 128.f * Ds) - dmin * Dm;
             }
+            const uint32_t mb = bias_pair(m_lo, m_hi, bsel), cb = bias_pair(sc_lo, sc_hi, bsel);
+            const u32x4_t ab = B_lds[sb * 64 + b_off];
+            const f32x4_t Dm = mfma16x16x32(ab, (u32x4_t){mb, mb, mb, mb}, zero);
+            const f32x4_t Ds = mfma16x16x32(ab, (u32x4_t){cb, cb, cb, cb}, zero);
+            acc += d * (tacc - 128.f * Ds) - dmin * Dm;
         }
-        // tiles past t1 (the ragged end of the last iteration) store tile 0's result
-        // again to tile 0's address: no branch around the stores (a branch there
-        // makes the compiler keep far more registers live)
-        const int tfirst = t0 + it * TP;
+        const int n = t * 16 + cl;
 #pragma unroll
-        for (int tl = 0; tl < TP; tl++) {
-            const int t = tfirst + tl;
-            const bool real = t < t1;
-            const int n = (real ? t : tfirst) * 16 + cl;
-#pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const int R = 4 * g + v;
-                const float val = real ? acc[tl][v] : acc[0][v];
-                if (R < a.M) part[(size_t)R * a.N + n] = val;
-            }
+        for (int v = 0; v < 4; v++) {
+            const int R = 4 * g + v;
+            if (R < a.M) part[(size_t)R * a.N + n] = acc[v];
         }
     }
 }
@@ -247,17 +225,16 @@ void k_q4k_stream(Q4kFusedArgs a, int tpw) {
 
 bool q4k_stream_ok(int M, int N, int K) { return M >= 1 && M <= 16 && (K / 256) % SNSB == 0 && N % 16 == 0; }
 
-Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves, int tp, int pd) {
+Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves, int wpg) {
     Q4kStreamPlan p;
-    p.tp = tp;
-    p.pd = pd;
+    p.wpg = wpg;
     const int KB = K / 256, ntile = N / 16;
     p.splits = KB / SNSB;
     const long long wave_tiles = (long long)ntile * p.splits;
     int tpw = (int)((wave_tiles + target_waves - 1) / target_waves);
     if (tpw < 1) tpw = 1;
     p.tpw = tpw;
-    p.grid_x = ceil_div(ceil_div(ntile, tpw), 4);
+    p.grid_x = ceil_div(ceil_div(ntile, tpw), wpg);
     p.lds_bytes = (size_t)SNSB * 8 * 64 * 16 + SNSB * 64 * 16 + SNSB * 8 * 16 * 4;
     p.part_bytes = (size_t)p.splits * M * N * 4;
     return p;
@@ -265,15 +242,13 @@ Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves, int tp, int
 
 hipError_t launch_q4k_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st) {
     const dim3 grid(p.grid_x, p.splits);
-#define QS_CASE(TP, PD)                                                                          \
-    if (p.tp == TP && p.pd == PD) {                                                               \
-        hipLaunchKernelGGL((k_q4k_stream<TP, PD>), grid, dim3(256), p.lds_bytes, st, a, p.tpw);   \
+#define QS_CASE(WPG)                                                                             \
+    if (p.wpg == WPG) {                                                                           \
+        hipLaunchKernelGGL((k_q4k_stream<WPG>), grid, dim3(64 * WPG), p.lds_bytes, st, a, p.tpw); \
         return hipGetLastError();                                                                 \
     }
-    QS_CASE(1, 4)
-    QS_CASE(2, 4)
-    QS_CASE(2, 8)
-    QS_CASE(4, 8)
+    QS_CASE(4)
+    QS_CASE(8)
 #undef QS_CASE
     return hipErrorInvalidValue;
 }
