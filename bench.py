@@ -180,7 +180,7 @@ def main():
                    "t_new": wl.t_new, "layers": s.n_layers, "hidden": s.hidden,
                    "vocab": s.vocab, "top_k": s.top_k, "weights": s.weight_fmt,
                    "step": "draft_step + verify_prefix", "hip_graph": bool(graph)},
-        "roofline": {"kernel": "output head (bf16 skinny MFMA GEMM, 248320 x 5120)",
+        "roofline": {"kernel": "output head k_head_stream (bf16 MFMA, 248320 x 5120, 7 rows)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "launch_ms": head_ms, "algorithmic_bytes": alg},
