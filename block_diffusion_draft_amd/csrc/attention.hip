@@ -22,10 +22,12 @@ namespace {
 constexpr int KT = 64;           // keys per inner step
 constexpr int MAXQR = 32;        // query rows per workgroup (G <= 4)
 
+template <int D>
 __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int d = a.d, G = a.n_q / a.n_kv, QR = G * a.T;
+    constexpr int d = D;                    // head dim as a constant: fixed trip counts
+    const int G = a.n_q / a.n_kv, QR = G * a.T;
     const int RTQ = ceil_div(QR, 16);
     if (!a.valid[b]) return;
     const int n = a.ctx_len[b];
@@ -51,16 +53,27 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     __shared__ float Ss[MAXQR * KT];
     __shared__ float m_run[MAXQR], l_run[MAXQR], alpha[MAXQR];
 
-    // Q rows: row = hq * T + t  <-  Q[b][t][kvh*G + hq][:]
-    for (int e = tid; e < RTQ * 16 * (d / 8); e += 256) {
-        const int row = e / (d / 8), q8 = e % (d / 8);
-        u32x4_t v = {0, 0, 0, 0};
-        if (row < QR) {
-            const int hq = row / a.T, t = row % a.T;
-            const uint16_t *src = a.Q + (((size_t)b * a.T + t) * a.n_q + kvh * G + hq) * d + 8 * q8;
-            v = *reinterpret_cast<const u32x4_t *>(src);
+    // Q rows: row = hq * T + t  <-  Q[b][t][kvh*G + hq][:] (rows >= QR: zeros)
+    {
+        constexpr int QPT = MAXQR * (d / 8) / 256;
+        u32x4_t qv[QPT];
+#pragma unroll
+        for (int i = 0; i < QPT; i++) {
+            const int e = tid + 256 * i;
+            const int row = e / (d / 8), q8 = e % (d / 8);
+            const int rc = min(row, QR - 1);
+            const int hq = rc / a.T, t = rc % a.T;
+            qv[i] = *reinterpret_cast<const u32x4_t *>(
+                a.Q + (((size_t)b * a.T + t) * a.n_q + kvh * G + hq) * d + 8 * q8);
         }
-        *reinterpret_cast<u32x4_t *>(&Qs[row * DS + 8 * q8]) = v;
+#pragma unroll
+        for (int i = 0; i < QPT; i++) {
+            const int e = tid + 256 * i;
+            const int row = e / (d / 8), q8 = e % (d / 8);
+            if (row < RTQ * 16)
+                *reinterpret_cast<u32x4_t *>(&Qs[row * DS + 8 * q8]) =
+                    row < QR ? qv[i] : (u32x4_t){0, 0, 0, 0};
+        }
     }
     if (tid < MAXQR) {
         m_run[tid] = -INFINITY;
@@ -78,30 +91,42 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     for (int kk = 0; kk < nkeys; kk += KT) {
         const int nk = min(KT, nkeys - kk);
         __syncthreads();
-        // stage K rows and V^T for keys kk .. kk+nk-1
-        for (int e = tid; e < KT * (d / 8); e += 256) {
-            const int j = e / (d / 8), q8 = e % (d / 8);
-            u32x4_t kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-            if (j < nk) {
-                const uint16_t *ks, *vs;
-                if (blk) {
-                    const size_t off = (((size_t)b * a.T + j) * a.n_kv + kvh) * d + 8 * q8;
-                    ks = a.Kb + off;
-                    vs = a.Vb + off;
-                } else {
-                    const size_t off = (((size_t)b * a.n_kv + kvh) * a.cap + (k0 + kk + j)) * d + 8 * q8;
-                    ks = a.k_cache + off;
-                    vs = a.v_cache + off;
-                }
-                kv = *reinterpret_cast<const u32x4_t *>(ks);
-                vv = *reinterpret_cast<const u32x4_t *>(vs);
-            }
-            *reinterpret_cast<u32x4_t *>(&Ks[j * DS + 8 * q8]) = kv;
-            const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+        // stage K rows and V^T for keys kk .. kk+nk-1: all loads first (rows past nk
+        // clamped to a real row, their values replaced by zeros)
+        constexpr int SPT = KT * (d / 8) / 256;          // 16-byte vectors per thread
+        u32x4_t kv[SPT], vv[SPT];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                Vt[(8 * q8 + 2 * i) * (KT + 8) + j] = (uint16_t)(w4[i] & 0xFFFF);
-                Vt[(8 * q8 + 2 * i + 1) * (KT + 8) + j] = (uint16_t)(w4[i] >> 16);
+        for (int i = 0; i < SPT; i++) {
+            const int e = tid + 256 * i;
+            const int j = e / (d / 8), q8 = e % (d / 8);
+            const int jc = min(j, nk - 1);
+            size_t off;
+            const uint16_t *kbase, *vbase;
+            if (blk) {
+                off = (((size_t)b * a.T + jc) * a.n_kv + kvh) * d + 8 * q8;
+                kbase = a.Kb;
+                vbase = a.Vb;
+            } else {
+                off = (((size_t)b * a.n_kv + kvh) * a.cap + (k0 + kk + jc)) * d + 8 * q8;
+                kbase = a.k_cache;
+                vbase = a.v_cache;
+            }
+            kv[i] = *reinterpret_cast<const u32x4_t *>(kbase + off);
+            vv[i] = *reinterpret_cast<const u32x4_t *>(vbase + off);
+        }
+#pragma unroll
+        for (int i = 0; i < SPT; i++) {
+            const int e = tid + 256 * i;
+            const int j = e / (d / 8), q8 = e % (d / 8);
+            const bool in = j < nk;
+            const u32x4_t z = {0, 0, 0, 0};
+            *reinterpret_cast<u32x4_t *>(&Ks[j * DS + 8 * q8]) = in ? kv[i] : z;
+            const u32x4_t w = in ? vv[i] : z;
+            const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                Vt[(8 * q8 + 2 * q) * (KT + 8) + j] = (uint16_t)(w4[q] & 0xFFFF);
+                Vt[(8 * q8 + 2 * q + 1) * (KT + 8) + j] = (uint16_t)(w4[q] >> 16);
             }
         }
         __syncthreads();
@@ -195,6 +220,8 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t st) {
     dim3 grid(a.n_chunks + 1, a.n_kv, a.B);
-    hipLaunchKernelGGL(k_attention, grid, dim3(256), 0, st, a);
+    if (a.d == 128) hipLaunchKernelGGL(k_attention<128>, grid, dim3(256), 0, st, a);
+    else if (a.d == 64) hipLaunchKernelGGL(k_attention<64>, grid, dim3(256), 0, st, a);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }

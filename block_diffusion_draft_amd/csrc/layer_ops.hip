@@ -102,14 +102,24 @@ __global__ __launch_bounds__(256) void k_reduce_rows(const float *part, int spli
     const size_t stride = (size_t)(pair ? 2 * M_out : M_out) * N;
     const float *p = part + (size_t)r * N + c0 + 4 * lane;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-    for (int k = wave; k < splits; k += 4) {
-        const float4 a = *reinterpret_cast<const float4 *>(p + k * stride);
-        s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
-        if (pair) {
-            const float4 b = *reinterpret_cast<const float4 *>(p + k * stride + (size_t)pair * N);
-            s.x += b.x; s.y += b.y; s.z += b.z; s.w += b.w;
+    // this wave's splits k = wave, wave + 4, ...: 8 of them in flight per batch
+    for (int k0 = wave; k0 < splits; k0 += 32) {
+        float4 va[8], vb[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const float *q = p + (size_t)min(k0 + 4 * u, splits - 1) * stride;
+            va[u] = *reinterpret_cast<const float4 *>(q);
+            vb[u] = pair ? *reinterpret_cast<const float4 *>(q + (size_t)pair * N)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+            if (k0 + 4 * u < splits) {
+                s.x += va[u].x + vb[u].x;
+                s.y += va[u].y + vb[u].y;
+                s.z += va[u].z + vb[u].z;
+                s.w += va[u].w + vb[u].w;
+            }
     }
     red[wave][lane] = s;
     __syncthreads();
@@ -178,22 +188,26 @@ __global__ __launch_bounds__(256) void k_swiglu(const float *part, int splits, i
     if (c >= F) return;
     const size_t stride = (size_t)(pair ? 2 * M : M) * N;
     const float *p = part + (size_t)r * N + c;
-    float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
-    int k = 0;
-    for (; k + 2 <= splits; k += 2) {
-        const float *p0 = p + k * stride, *p1 = p0 + stride;
-        g0 += p0[0] + (pair ? p0[(size_t)pair * N] : 0.f);
-        u0 += p0[F] + (pair ? p0[(size_t)pair * N + F] : 0.f);
-        g1 += p1[0] + (pair ? p1[(size_t)pair * N] : 0.f);
-        u1 += p1[F] + (pair ? p1[(size_t)pair * N + F] : 0.f);
-    }
-    for (; k < splits; k++) {
-        const float *p0 = p + k * stride;
-        g0 += p0[0] + (pair ? p0[(size_t)pair * N] : 0.f);
-        u0 += p0[F] + (pair ? p0[(size_t)pair * N + F] : 0.f);
+    float gs = 0.f, us = 0.f;
+    for (int k0 = 0; k0 < splits; k0 += 8) {
+        float gv[8], uv[8], gq[8], uq[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const float *p0 = p + (size_t)min(k0 + u, splits - 1) * stride;
+            gv[u] = p0[0];
+            uv[u] = p0[F];
+            gq[u] = pair ? p0[(size_t)pair * N] : 0.f;
+            uq[u] = pair ? p0[(size_t)pair * N + F] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+            if (k0 + u < splits) {
+                gs += gv[u] + gq[u];
+                us += uv[u] + uq[u];
+            }
     }
     const float inv = row_inv(rs, r);
-    const float gt = (g0 + g1) * inv, up = (u0 + u1) * inv;
+    const float gt = gs * inv, up = us * inv;
     const float v = gt / (1.f + expf(-gt)) * up;
     const uint16_t hb = f32_to_bf16(v);
     ob[(size_t)r * ldo + c] = hb;
@@ -224,11 +238,25 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
     const float *x = a.qkv + (size_t)r * (qd + 2 * kd) + (size_t)hh * d;
     const size_t pstride = (size_t)a.B * (a.T + a.t_new) * (qd + 2 * kd);
     float x1 = 0.f, x2 = 0.f;
-    if (lane < half)
-        for (int s = 0; s < a.splits; s++) {
-            x1 += x[s * pstride + lane];
-            x2 += x[s * pstride + lane + half];
+    if (lane < half) {
+        // 8 splits of loads in flight per batch (indices past the end are clamped and
+        // their values dropped)
+        for (int s0 = 0; s0 < a.splits; s0 += 8) {
+            float v1[8], v2[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int sp = min(s0 + u, a.splits - 1);
+                v1[u] = x[sp * pstride + lane];
+                v2[u] = x[sp * pstride + lane + half];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                if (s0 + u < a.splits) {
+                    x1 += v1[u];
+                    x2 += v2[u];
+                }
         }
+    }
     // the projection input's deferred RMSNorm
     const float rinv = is_blk ? row_inv(a.blk, r) : row_inv(a.ctx, r - nblk);
     x1 *= rinv;
@@ -324,16 +352,16 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
     const float *O = a.O + ((size_t)(b * a.n_kv + kvh) * nch1 * QR + hq * T + t) * d + cc * MC + col;
     const size_t cstride = (size_t)QR * d;
     const float *wt = w + t * nch1;
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    int c = 0;
-    for (; c + 4 <= nch1; c += 4) {
-        s0 += wt[c] * O[(size_t)c * cstride];
-        s1 += wt[c + 1] * O[(size_t)(c + 1) * cstride];
-        s2 += wt[c + 2] * O[(size_t)(c + 2) * cstride];
-        s3 += wt[c + 3] * O[(size_t)(c + 3) * cstride];
+    // 16 chunk partials in flight per batch (clamped indices, weights of the padding 0)
+    float ov = 0.f;
+    for (int c0 = 0; c0 < nch1; c0 += 16) {
+        float pv[16];
+#pragma unroll
+        for (int u = 0; u < 16; u++) pv[u] = O[(size_t)min(c0 + u, nch1 - 1) * cstride];
+#pragma unroll
+        for (int u = 0; u < 16; u++)
+            if (c0 + u < nch1) ov += wt[c0 + u] * pv[u];
     }
-    for (; c < nch1; c++) s0 += wt[c] * O[(size_t)c * cstride];
-    const float ov = (s0 + s1) + (s2 + s3);
     os[t * MC + col] = ov;
     a.o[((size_t)b * T + t) * qd + c0 + col] = ov;
     __syncthreads();

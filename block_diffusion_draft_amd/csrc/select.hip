@@ -52,12 +52,24 @@ __global__ __launch_bounds__(256) void k_viterbi(const int32_t *cand_ids, const 
         const uint16_t *ar = code_a + (size_t)(ua >= 0 ? ua : 0) * r + 8 * g;
         const uint16_t *br = code_b + (size_t)(vb >= 0 ? vb : 0) * r + 8 * g;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int ks = 0; ks < nks; ks++) {
-            u32x4_t av = *reinterpret_cast<const u32x4_t *>(ar + ks * 32);
-            u32x4_t bv = *reinterpret_cast<const u32x4_t *>(br + ks * 32);
-            if (ua < 0) av = (u32x4_t){0, 0, 0, 0};
-            if (vb < 0) bv = (u32x4_t){0, 0, 0, 0};
-            acc = mfma16x16x32(av, bv, acc);
+        // 8 k-steps of fragments in flight, then their MFMAs (indices past the rank are
+        // clamped: in bounds, and their products skipped)
+        for (int ks0 = 0; ks0 < nks; ks0 += 8) {
+            u32x4_t av[8], bv[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int ks = min(ks0 + u, nks - 1);
+                av[u] = *reinterpret_cast<const u32x4_t *>(ar + ks * 32);
+                bv[u] = *reinterpret_cast<const u32x4_t *>(br + ks * 32);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                if (ks0 + u < nks) {
+                    const u32x4_t a0 = ua < 0 ? (u32x4_t){0, 0, 0, 0} : av[u];
+                    const u32x4_t b0 = vb < 0 ? (u32x4_t){0, 0, 0, 0} : bv[u];
+                    acc = mfma16x16x32(a0, b0, acc);
+                }
+            }
         }
 #pragma unroll
         for (int v = 0; v < 4; v++) Tm[t][4 * g + v][c] = s * acc[v];
