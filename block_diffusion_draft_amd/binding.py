@@ -80,6 +80,8 @@ def lib():
     L.q4k_gemm.restype = c_int
     L.q4k_dequantize.argtypes = [c_void_p, c_void_p, ctypes.c_longlong, c_void_p]
     L.q4k_dequantize.restype = c_int
+    L.q4k_to_tiled.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p]
+    L.q4k_to_tiled.restype = c_int
     L.dflash_status_str.argtypes = [c_int]
     L.dflash_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -87,7 +89,8 @@ def lib():
 
 
 EXPORTS = ["dflash_workspace_bytes", "dflash_draft_step", "dflash_verify_prefix",
-           "q4k_gemm_workspace_bytes", "q4k_gemm", "q4k_dequantize", "dflash_status_str"]
+           "q4k_gemm_workspace_bytes", "q4k_gemm", "q4k_to_tiled", "q4k_dequantize",
+           "dflash_status_str"]
 
 
 def check(rc):
@@ -119,11 +122,24 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _linear_dims(s):
+    """(rows = out, cols = in) of each linear weight field of the weights struct."""
+    qd, kd, H = s.n_q * s.head_dim, s.n_kv * s.head_dim, s.hidden
+    dims = {"fc": (H, s.n_taps * H)}
+    for l in range(s.n_layers):
+        dims.update({f"l{l}.wq": (qd, H), f"l{l}.wk": (kd, H), f"l{l}.wv": (kd, H),
+                     f"l{l}.wo": (H, qd), f"l{l}.wg": (s.ffn, H), f"l{l}.wu": (s.ffn, H),
+                     f"l{l}.wd": (H, s.ffn)})
+    return dims
+
+
 class DeviceWeights:
     """Drafter weights resident in device memory, plus the C struct pointing at them.
 
     `W` is the host weight dict of synth.make_weights (linear weights as
-    ("q4k", bytes) or ("bf16", uint16 array); the rest uint16 arrays).
+    ("q4k", row-major Q4_K bytes) or ("bf16", uint16 array); the rest uint16
+    arrays).  Q4_K matrices are regrouped on the device into the library's tiled
+    layout (q4k_to_tiled) after the upload.
     """
 
     def __init__(self, shape, W, device="cuda"):
@@ -131,8 +147,9 @@ class DeviceWeights:
         self.shape = shape
         self.tensors = {}
         shared = {}
+        dims = _linear_dims(shape)
 
-        def up(name, arr):
+        def up(name, arr, q4k):
             arr = np.ascontiguousarray(arr)
             key = arr.__array_interface__["data"][0]
             if key in shared:                      # tied embedding / output head
@@ -141,6 +158,10 @@ class DeviceWeights:
                 dt = torch.uint8 if arr.dtype == np.uint8 else torch.int16
                 t = torch.from_numpy(arr.view(np.uint8 if arr.dtype == np.uint8 else np.int16))
                 t = t.to(device, dtype=dt)
+                if q4k:
+                    tiled = torch.empty_like(t)
+                    q4k_to_tiled(t, tiled, *dims[name])
+                    t = tiled
                 shared[key] = t
             self.tensors[name] = t
             return t.data_ptr()
@@ -148,7 +169,7 @@ class DeviceWeights:
         s = Weights()
         for name, val in W.items():
             arr = val[1] if isinstance(val, tuple) else val
-            p = up(name, arr)
+            p = up(name, arr, isinstance(val, tuple) and val[0] == "q4k")
             m = re.match(r"^l(\d+)\.(\w+)$", name)
             if m:
                 setattr(s.layer[int(m.group(1))], m.group(2), p)
@@ -186,6 +207,11 @@ def q4k_gemm(w, x, y, workspace):
 
 def q4k_gemm_workspace_bytes(M, N, K):
     return lib().q4k_gemm_workspace_bytes(M, N, K)
+
+
+def q4k_to_tiled(src, dst, N, K):
+    """Regroup a row-major Q4_K matrix [N][K] (device uint8) into the tiled layout."""
+    check(lib().q4k_to_tiled(_ptr(src), _ptr(dst), N, K, _stream()))
 
 
 def q4k_dequantize(w, out):

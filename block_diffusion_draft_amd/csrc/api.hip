@@ -141,13 +141,16 @@ struct Ctx {
     template <class T> T *at(size_t off) const { return reinterpret_cast<T *>(ws + off); }
 };
 
-// Q4_K product into partials: the streaming kernel for up to 16 rows, else the tiled
-// one.  Returns the number of splits or a negative status.
-int run_q4k(const Q4kFusedArgs &a, hipStream_t st) {
+// Q4_K product into partials: the streaming kernel for up to 16 rows, else the
+// row-tiled one.  Returns the number of splits or a negative status; *pair_left is
+// the row pair the partial still holds (0 once the kernel has added the halves).
+int run_q4k(const Q4kFusedArgs &a, hipStream_t st, int *pair_left) {
     const int K = a.KB * 256;
+    *pair_left = a.pair;
     if (q4k_stream_ok(a.M, a.N, K)) {
-        const Q4kStreamPlan p = q4k_stream_plan(a.M, a.N, K);
+        const Q4kStreamPlan p = q4k_stream_plan(a.M, a.N, K, a.pair);
         HIPCHK(launch_q4k_stream(a, p, st));
+        if (p.pair_done) *pair_left = 0;
         return p.splits;
     }
     const Q4kFusedPlan p = q4k_fused_plan(a.M, a.N, K);
@@ -157,10 +160,13 @@ int run_q4k(const Q4kFusedArgs &a, hipStream_t st) {
 
 // y = A . W^T over up to 3 weight matrices stacked along N, as fp32 partial sums in
 // the workspace's partial buffer: Q4_K -> [splits][M][N] from the dequantize-fused
-// MFMA kernel; bf16 -> [M][N] (one split) from the tiled MFMA kernel.  Returns the
+// MFMA kernel; bf16 -> [M][N] (one split) from the tiled MFMA kernel.  Rows r and
+// r + pair (pair > 0) are the (hi, lo) halves of one activation row; *pair_left is
+// the pair the partial still holds (the reduction adds those rows).  Returns the
 // number of splits (> 0) or a negative status.
 int run_gemm(const Ctx &x, const void *const *w, const int *seg_n, int nseg, const uint16_t *A,
-             int lda, int M, int K) {
+             int lda, int M, int K, int pair, int *pair_left) {
+    *pair_left = pair;
     int N = 0;
     int seg_end[3] = {0, 0, 0};
     for (int i = 0; i < 3; i++) {
@@ -181,7 +187,8 @@ int run_gemm(const Ctx &x, const void *const *w, const int *seg_n, int nseg, con
         a.src.A = A;
         a.src.lda = lda;
         a.part = part;
-        return run_q4k(a, x.st);
+        a.pair = pair;
+        return run_q4k(a, x.st, pair_left);
     }
     Bf16GemmArgs a = {};
     for (int i = 0; i < 3; i++) {
@@ -278,11 +285,11 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
     uint16_t *mid2 = x.at<uint16_t>(p.o_mid2);
     uint16_t *f = x.at<uint16_t>(p.o_f);
     const size_t cache_layer = (size_t)batch * p.n_kv * cache_cap * p.d;
-    int splits;
-#define GEMM(...)                              \
-    do {                                       \
-        splits = run_gemm(x, __VA_ARGS__);     \
-        if (splits < 0) return splits;         \
+    int splits, pair_left;
+#define GEMM(...)                                          \
+    do {                                                   \
+        splits = run_gemm(x, __VA_ARGS__, &pair_left);     \
+        if (splits < 0) return splits;                     \
     } while (0)
 
     // S0: block assembly h, per-sequence validity, first layer's input bf16(h * g_in)
@@ -296,7 +303,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
     {
         const void *ws[1] = {w->fc};
         const int sn[1] = {H};
-        GEMM(ws, sn, 1, taps, cfg->n_taps * H, p.M_ctx, cfg->n_taps * H);
+        GEMM(ws, sn, 1, taps, cfg->n_taps * H, p.M_ctx, cfg->n_taps * H, 0);
         HIPCHK(launch_reduce_norm(part, splits, p.M_ctx, H, 0, 0, fcout, ssq_c, w->hidden_norm,
                                   xc + (size_t)p.M_blk * H, nullptr, H, 0, x.st));
     }
@@ -310,7 +317,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
         {
             const void *ws[3] = {lw.wq, lw.wk, lw.wv};
             const int sn[3] = {p.qd, p.kd, p.kd};
-            GEMM(ws, sn, 3, xc, H, p.M_qkv, H);
+            GEMM(ws, sn, 3, xc, H, p.M_qkv, H, 0);
         }
         // S4: split sum, per-head norms, rotary embedding, cache append
         {
@@ -349,7 +356,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
         {
             const void *ws[1] = {lw.wo};
             const int sn[1] = {H};
-            GEMM(ws, sn, 1, x.at<uint16_t>(p.o_Y), p.qd, p.M_blk, p.qd);
+            GEMM(ws, sn, 1, x.at<uint16_t>(p.o_Y), p.qd, p.M_blk, p.qd, 0);
             HIPCHK(launch_reduce_norm(part, splits, p.M_blk, H, 0, 1, h, ssq_u, lw.post_norm, u2,
                                       u2 + (size_t)p.M_blk * H, H, 0, x.st));
         }
@@ -361,9 +368,9 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
             const int sn[2] = {p.F, p.F};
             const bool probe_ffn = probe && probe->kernel == DFLASH_PROBE_FFN_GATE_UP && probe->layer == l;
             if (probe_ffn) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_start, x.st));
-            GEMM(ws, sn, 2, u2, H, 2 * p.M_blk, H);
+            GEMM(ws, sn, 2, u2, H, 2 * p.M_blk, H, p.M_blk);
             if (probe_ffn) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_stop, x.st));
-            HIPCHK(launch_swiglu(part, splits, p.M_blk, 2 * p.F, p.M_blk, mid2,
+            HIPCHK(launch_swiglu(part, splits, p.M_blk, 2 * p.F, pair_left, mid2,
                                  mid2 + (size_t)p.M_blk * p.F, p.F, rowscale(ssq_u, 0), x.st));
         }
         // down projection + residual; then the next layer's input norm, or after the last
@@ -371,9 +378,9 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
         {
             const void *ws[1] = {lw.wd};
             const int sn[1] = {H};
-            GEMM(ws, sn, 1, mid2, p.F, 2 * p.M_blk, p.F);
+            GEMM(ws, sn, 1, mid2, p.F, 2 * p.M_blk, p.F, p.M_blk);
             const uint16_t *gain = last ? w->final_norm : w->layer[l + 1].in_norm;
-            HIPCHK(launch_reduce_norm(part, splits, p.M_blk, H, p.M_blk, 1, h, ssq_x, gain,
+            HIPCHK(launch_reduce_norm(part, splits, p.M_blk, H, pair_left, 1, h, ssq_x, gain,
                                       last ? f : xc, nullptr, H, last ? 1 : 0, x.st));
         }
         if (dbg_hidden)
@@ -436,10 +443,24 @@ int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
     a.src.A = x;
     a.src.lda = K;
     a.part = (float *)workspace;
-    const int splits = run_q4k(a, st);
+    a.pair = 0;
+    int pair_left;
+    const int splits = run_q4k(a, st, &pair_left);
     if (splits < 0) return splits;
     HIPCHK(launch_reduce_epilogue(a.part, splits, M, N, 0, EPI_STORE_BF16, nullptr, y, nullptr, N,
                                   RowScale{}, st));
+    return DFLASH_OK;
+}
+
+int q4k_to_tiled(const void *src, void *dst, int N, int K, void *stream) {
+    if (!src || !dst) return DFLASH_EINVAL;
+    if (N < 16 || N % 16 || K < 256 || K % 256) return DFLASH_ESHAPE;
+    if (!aligned16(src) || !aligned16(dst)) return DFLASH_EALIGN;
+    const size_t bytes = (size_t)N * (K / 256) * 144;
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return DFLASH_EINVAL;      // overlap
+    HIPCHK(launch_q4k_to_tiled((const unsigned char *)src, (unsigned char *)dst, N, K / 256,
+                               (hipStream_t)stream));
     return DFLASH_OK;
 }
 

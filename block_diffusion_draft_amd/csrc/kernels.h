@@ -8,6 +8,14 @@
 
 // ---------------------------------------------------------------- Q4_K decode
 hipError_t launch_q4k_dequant(const void *w, float *out, long long n_blocks, hipStream_t st);
+// Row-major Q4_K [N rows][K/256 blocks] -> the tiled layout the GEMM kernels stream:
+// unit (t, kb) of 2304 bytes at (t * K/256 + kb) * 2304 holds the 16 block headers of
+// rows 16 t .. 16 t + 15 (16 bytes each), then two halves h of 64 slots s = 16 g + r
+// (16 bytes each): quant bytes 8 g .. 8 g + 7 of chunk 2 h, then of chunk 2 h + 1, of
+// row r's block (chunk c = quant bytes 32 c .. 32 c + 31).
+constexpr int Q4K_UNIT_BYTES = 2304;
+hipError_t launch_q4k_to_tiled(const unsigned char *src, unsigned char *dst, int N, int KB,
+                               hipStream_t st);
 
 // ---------------------------------------------------------------- bf16 GEMMs
 struct Bf16GemmArgs {
@@ -116,7 +124,8 @@ struct Q4kFusedArgs {
     int nseg;
     int M, N, KB;                // GEMM rows, columns, K/256
     Q4kSrc src;
-    float *part;                 // [splits][M][N]
+    float *part;                 // [splits][M][N], or [splits][pair][N] when combined
+    int pair;                    // > 0: rows r and r + pair are the (hi, lo) halves of one row
 };
 struct Q4kFusedPlan {
     int rt, nsb, ct, steps, splits, row_groups, grid_x;
@@ -126,14 +135,19 @@ Q4kFusedPlan q4k_fused_plan(int M, int N, int K);
 hipError_t launch_q4k_fused(const Q4kFusedArgs &a, const Q4kFusedPlan &p, hipStream_t st);
 
 // Streaming variant for M <= 16 rows and K/256 a multiple of 4: splits of 4 super-blocks,
-// each wave streams tpw consecutive column tiles.  Same partial layout [splits][M][N].
+// each wave streams tpw consecutive column tiles.  Partials [splits][M][N]; when
+// pair is 4 or 8 and M = 2 pair, the kernel adds each (hi, lo) row pair itself and
+// writes [splits][pair][N] (pair_done).
 struct Q4kStreamPlan {
     int splits, tpw, grid_x;
     int wpg;                     // waves per workgroup
+    int px;                      // lane distance of the row pair (16, 32) or 0
+    bool pair_done;
     size_t lds_bytes, part_bytes;
 };
 bool q4k_stream_ok(int M, int N, int K);
-Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves = 2048, int wpg = 4);
+Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int pair = 0, int target_waves = 2048,
+                              int wpg = 4);
 hipError_t launch_q4k_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st);
 
 // Output rows r < M_out: v = sum over splits of partial rows r (+ r + pair), N a multiple

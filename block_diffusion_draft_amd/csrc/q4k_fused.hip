@@ -2,7 +2,8 @@
 //
 // Format (FastFlowLM card "Qwen3.8-27B-DFlash2-NPU2", "Weights" row: the draft's fc,
 // q/k/v/o and MLP matrices in Q4_K): 144-byte super-blocks of 256 weights along K,
-// w = d * sc_j * q - dmin * m_j for sub-block j (32 weights), q in 0..15.
+// w = d * sc_j * q - dmin * m_j for sub-block j (32 weights), q in 0..15, held in the
+// tiled layout of q4k_tiled.hip (16 rows x one super-block per 2304-byte unit).
 //
 // Arithmetic.  For output column n, activation row r and super-block b:
 //     sum_k x_rk w_k = d sum_j sc_j (sum_k x_rk q_k)  -  dmin sum_j m_j S_rj,
@@ -33,11 +34,17 @@ struct WStage {
     u32x2_t q[4];
 };
 
-__device__ __forceinline__ WStage load_stage(const unsigned char *blk, int g) {
+// one (tile, super-block) unit of the tiled layout (q4k_tiled.hip): this lane reads the
+// header of row cl and its quant slot in each half (chunks 0, 1 and 2, 3)
+__device__ __forceinline__ WStage load_stage(const unsigned char *unit, int cl, int lane) {
     WStage s;
-    s.hdr = *reinterpret_cast<const u32x4_t *>(blk);
-#pragma unroll
-    for (int c = 0; c < 4; c++) s.q[c] = *reinterpret_cast<const u32x2_t *>(blk + 16 + 32 * c + 8 * g);
+    s.hdr = *reinterpret_cast<const u32x4_t *>(unit + 16 * cl);
+    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(unit + 256 + 16 * lane);
+    const u32x4_t b = *reinterpret_cast<const u32x4_t *>(unit + 1280 + 16 * lane);
+    s.q[0] = (u32x2_t){a.x, a.y};
+    s.q[1] = (u32x2_t){a.z, a.w};
+    s.q[2] = (u32x2_t){b.x, b.y};
+    s.q[3] = (u32x2_t){b.z, b.w};
     return s;
 }
 
@@ -98,11 +105,13 @@ void k_q4k_fused(Q4kFusedArgs a) {
         const int si = (a.nseg > 1 && c16 >= a.seg_end[0]) + (a.nseg > 2 && c16 >= a.seg_end[1]);
         const unsigned char *wseg = si == 0 ? a.w[0] : (si == 1 ? a.w[1] : a.w[2]);
         const int nbase = si == 0 ? 0 : (si == 1 ? a.seg_end[0] : a.seg_end[1]);
-        wrow[ti] = wseg + ((size_t)(c16 + cl - nbase) * a.KB + sb0) * 144;
+        wrow[ti] = wseg + ((size_t)((c16 - nbase) >> 4) * a.KB + sb0) * Q4K_UNIT_BYTES;
     }
     // step order: super-block major (step / CT), tile minor (step % CT), so the LDS
     // operands of a super-block are read once and reused for the wave's CT tiles
-    auto stage_at = [&](int step) { return load_stage(wrow[step % CT] + (step / CT) * 144, g); };
+    auto stage_at = [&](int step) {
+        return load_stage(wrow[step % CT] + (step / CT) * Q4K_UNIT_BYTES, cl, lane);
+    };
 
     // ---- LDS layout
     u32x4_t *A_lds = reinterpret_cast<u32x4_t *>(lds);                                  // [nsb][8][rt_n][64]

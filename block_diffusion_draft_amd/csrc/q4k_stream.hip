@@ -1,9 +1,12 @@
 // Q4_K dequantize-fused GEMM for at most 16 activation rows (one draft block of 8 rows,
-// or its bf16 hi/lo pair), gfx950.  Split-K partials [split][M][N].
+// or its bf16 hi/lo pair), gfx950.  Split-K partials [split][rows][N].
 //
 // Format (FastFlowLM card "Qwen3.8-27B-DFlash2-NPU2", "Weights" row: the draft's fc,
 // q/k/v/o and MLP matrices in Q4_K): 144-byte super-blocks of 256 weights along K,
-// w = d * sc_j * q - dmin * m_j for sub-block j (32 weights), q in 0..15.
+// w = d * sc_j * q - dmin * m_j for sub-block j (32 weights), q in 0..15.  The
+// matrices sit in HBM in the tiled layout of q4k_tiled.hip: the 16 rows of a column
+// tile and one super-block form one contiguous 2304-byte unit, headers first, so
+// every load below reads whole cache lines that no other wave touches.
 //
 // Arithmetic, per output column n, row r and super-block:
 //     sum_k x_rk w_k = d (sum_j sc_j sum_k x_rk q_k) - dmin sum_j m_j S_rj,
@@ -12,18 +15,20 @@
 //    permute per two weights), so D_j = sum_k x_rk (128 + q_k) with fp32 accumulation;
 //  * T = sum_j sc_j D_j takes 4 FMAs per sub-block and lane;
 //  * sum_j sc_j S_rj and sum_j m_j S_rj are two more MFMAs per super-block whose A
-//    operand holds each fp32 S_rj as four bf16 terms summing to it exactly and whose B
-//    operand holds the 6-bit sc_j or m_j (exact in bf16);
+//    operand holds each fp32 S_rj as three bf16 terms summing to it exactly and whose
+//    B operand holds the 6-bit sc_j or m_j (exact in bf16);
 //  * the super-block adds d (T - 128 sum_j sc_j S_rj) - dmin sum_j m_j S_rj.
 //
 // Work split: a workgroup (4 waves) owns one split of 4 super-blocks (1024 values of
 // K) and 4 runs of tpw consecutive 16-column tiles, one run per wave.  The split's
-// activation rows are staged once in LDS in MFMA lane order, with the bias operand.
-// Each wave then streams its tiles' super-blocks from HBM as one flat sequence of
-// (tile, super-block) stages, 4 stages in flight, in a branch-free loop (loads past
-// the end are clamped to the last stage, in bounds and unused), so the loads stay in
-// flight across tiles.  Each tile's 16 x M partial is stored when its 4 super-blocks
-// are done.  Workgroups never communicate; a reduction kernel sums the splits.
+// activation rows are staged once in LDS in MFMA lane order; their sub-block sums
+// come from MFMAs against a ones operand.  Each wave then streams its tiles'
+// super-blocks as one flat sequence of (tile, super-block) stages, 4 stages in
+// flight, in a branch-free loop (loads past the end are clamped to the last stage,
+// in bounds and unused), so the loads stay in flight across tiles.  The weights are
+// read once, with non-temporal loads.  Each tile's partial is stored when its 4
+// super-blocks are done; for a (hi, lo) row pair the two halves are added first.
+// Workgroups never communicate; a reduction kernel sums the splits.
 #include "common.h"
 #include "kernels.h"
 
@@ -32,26 +37,26 @@ namespace {
 constexpr int SNSB = 4;        // super-blocks per split
 
 struct SStage {
-    u32x4_t hdr;               // d, dmin, 12 scale bytes (same for the 4 lane groups)
-    u32x2_t q[4];              // 8 nibble bytes of each 32-byte chunk, lane group g
+    u32x4_t hdr;               // d, dmin, 12 scale bytes of column cl's block
+    u32x4_t q[2];              // chunks (2 h, 2 h + 1): 8 quant bytes each, lane group g
 };
 
-// one stage: a wave-uniform base address plus this lane's 32-bit byte offsets: the
-// column's super-block (header) and lane group g's 8 bytes within it (+ 8 g)
-__device__ __forceinline__ SStage s_load(const unsigned char *base, uint32_t off, uint32_t goff) {
+// one stage: the unit's base address; this lane reads the header of row cl and its
+// two 16-byte quant slots
+__device__ __forceinline__ SStage s_load(const unsigned char *unit, int cl, int lane) {
     SStage s;
-    s.hdr = *reinterpret_cast<const u32x4_t *>(base + off);
-#pragma unroll
-    for (int c = 0; c < 4; c++) s.q[c] = *reinterpret_cast<const u32x2_t *>(base + (off + goff + 16 + 32 * c));
+    s.hdr = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(unit + 16 * cl));
+    s.q[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(unit + 256 + 16 * lane));
+    s.q[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(unit + 1280 + 16 * lane));
     return s;
 }
 
 // 8 quant bytes -> bf16 (128 + q) operands, natural k order: low nibbles (first
 // sub-block of the chunk) and high nibbles (second sub-block)
-__device__ __forceinline__ void s_decode(u32x2_t q, u32x4_t &lo, u32x4_t &hi) {
+__device__ __forceinline__ void s_decode(uint32_t qx, uint32_t qy, u32x4_t &lo, u32x4_t &hi) {
     const uint32_t C = 0x43434343u;
-    const uint32_t lx = q.x & 0x0F0F0F0Fu, ly = q.y & 0x0F0F0F0Fu;
-    const uint32_t hx = (q.x >> 4) & 0x0F0F0F0Fu, hy = (q.y >> 4) & 0x0F0F0F0Fu;
+    const uint32_t lx = qx & 0x0F0F0F0Fu, ly = qy & 0x0F0F0F0Fu;
+    const uint32_t hx = (qx >> 4) & 0x0F0F0F0Fu, hy = (qy >> 4) & 0x0F0F0F0Fu;
     // byte selectors: {q0, 0x43, q1, 0x43} and {q2, 0x43, q3, 0x43}
     lo.x = __builtin_amdgcn_perm(C, lx, 0x04010400u);
     lo.y = __builtin_amdgcn_perm(C, lx, 0x04030402u);
@@ -72,7 +77,8 @@ __device__ __forceinline__ uint32_t bias_pair(uint32_t lo, uint32_t hi, uint32_t
     return __builtin_amdgcn_perm(__float_as_uint(fb), __float_as_uint(fa), 0x07060302u);
 }
 
-template <int WPG>
+// PX > 0: rows r and r + PX / 4 are one (hi, lo) pair, held PX lanes apart
+template <int WPG, int PX>
 __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw) {
     constexpr int NT = 64 * WPG;                    // threads per workgroup
     extern __shared__ __align__(16) unsigned char lds[];
@@ -89,22 +95,19 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw
     const int t1 = min(t0 + tpw, ntile);
     const int tlast = (t1 > t0 ? t1 : ntile) - 1;       // clamp target, always a real tile
 
-    // ---- weight stream.  Stage (tile t, super-block sb) sits at tile_base(t) + sb * 144
-    // + this lane's offset (column cl's row, lane group g's bytes); loads run 3 stages
-    // ahead, so tile t's loop issues (t, 3) and (t + 1, 0..2); tiles past t1 - 1 clamp
-    // to tlast (in bounds, unused).
-    const int row_bytes = a.KB * 144;
-    const uint32_t lane_off = (uint32_t)(cl * row_bytes + sb0 * 144), goff = 8 * g;
+    // ---- weight stream.  Stage (tile t, super-block sb) is the unit at tile_base(t)
+    // + sb * 2304; loads run 3 stages ahead, so tile t's loop issues (t, 3) and
+    // (t + 1, 0..2); tiles past t1 - 1 clamp to tlast (in bounds, unused).
     auto tile_base = [&](int t) -> const unsigned char * {
         const int tt = t < t1 ? t : tlast;
         const int c16 = tt * 16;
         const int si = (a.nseg > 1 && c16 >= a.seg_end[0]) + (a.nseg > 2 && c16 >= a.seg_end[1]);
         const unsigned char *wseg = si == 0 ? a.w[0] : (si == 1 ? a.w[1] : a.w[2]);
         const int nbase = si == 0 ? 0 : (si == 1 ? a.seg_end[0] : a.seg_end[1]);
-        return wseg + (size_t)(c16 - nbase) * row_bytes;
+        return wseg + ((size_t)((c16 - nbase) >> 4) * a.KB + sb0) * Q4K_UNIT_BYTES;
     };
     auto stage = [&](const unsigned char *tb, int sb) -> SStage {
-        return s_load(tb + sb * 144, lane_off, goff);
+        return s_load(tb + sb * Q4K_UNIT_BYTES, cl, lane);
     };
     SStage st[4];
     {
@@ -114,62 +117,64 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw
         st[2] = stage(b0, 2);
     }
 
-    // ---- activations of this split -> LDS (lane order), sub-block sums S
-    constexpr int PER = SNSB * 8 * 64 / NT;
-    u32x4_t av[PER];
+    // ---- activations of this split -> LDS in lane order: entry (sbi, j, lane) holds
+    // row cl's values k = (sb0 + sbi) 256 + 32 j + 8 g .. + 7 (rows >= M: zeros)
+    constexpr int PER = SNSB * 8 / WPG;             // entries per thread
+    {
+        const int Rc = min(cl, a.M - 1);
+        const uint16_t *arow = a.src.A + (size_t)Rc * a.src.lda + (size_t)sb0 * 256 + 8 * g;
+        u32x4_t av[PER];
 #pragma unroll
-    for (int i = 0; i < PER; i++) {
-        const int e = tid + NT * i;
-        const int ln = e & 63, rest = e >> 6;
-        const int j = rest & 7, sbi = rest >> 3;
-        const int R = ln & 15;
-        const int Rc = min(R, a.M - 1);
-        const size_t k = (size_t)(sb0 + sbi) * 256 + 32 * j + 8 * (ln >> 4);
-        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(a.src.A + (size_t)Rc * a.src.lda + k);
-        av[i] = R < a.M ? v : (u32x4_t){0u, 0u, 0u, 0u};
+        for (int i = 0; i < PER; i++) {
+            const int e = wave + WPG * i;           // (sbi, j) = (e >> 3, e & 7)
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(arow + (e >> 3) * 256 + 32 * (e & 7));
+            av[i] = cl < a.M ? v : (u32x4_t){0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < PER; i++) A_lds[(wave + WPG * i) * 64 + lane] = av[i];
     }
+    __syncthreads();
+    // sub-block sums S[sbi][j][r]: MFMA of the entry with a ones operand (every
+    // column of the product is the row sum)
+    {
+        const uint32_t one2 = 0x3F803F80u;
+        const u32x4_t ones = {one2, one2, one2, one2};
 #pragma unroll
-    for (int i = 0; i < PER; i++) {
-        const int e = tid + NT * i;
-        const int ln = e & 63, rest = e >> 6;
-        const u32x4_t v = av[i];
-        float s = 0.f;
-        s += bf16_to_f32(v.x & 0xFFFF) + bf16_to_f32(v.x >> 16);
-        s += bf16_to_f32(v.y & 0xFFFF) + bf16_to_f32(v.y >> 16);
-        s += bf16_to_f32(v.z & 0xFFFF) + bf16_to_f32(v.z >> 16);
-        s += bf16_to_f32(v.w & 0xFFFF) + bf16_to_f32(v.w >> 16);
-        s += __shfl_xor(s, 16, WAVE);
-        s += __shfl_xor(s, 32, WAVE);
-        A_lds[e] = v;
-        if ((ln >> 4) == 0) S_lds[rest * 16 + (ln & 15)] = s;
+        for (int i = 0; i < PER; i++) {
+            const int e = wave + WPG * i;
+            const f32x4_t D = mfma16x16x32(A_lds[e * 64 + lane], ones, (f32x4_t){0.f, 0.f, 0.f, 0.f});
+            if (cl == 0) *reinterpret_cast<f32x4_t *>(&S_lds[e * 16 + 4 * g]) = D;
+        }
     }
     __syncthreads();
     // bias A operand: lane (row r, group gg) holds S_a, S_b (a = 2 gg, b = 2 gg + 1) as
-    // four bf16 terms each (8 + 8 + 8 + 8 bits >= the 24 of an fp32 significand: exact),
-    // interleaved: dword q = term q of S_a | term q of S_b << 16
-    if (tid < SNSB * 64) {
-        const int sbi = tid >> 6, ln = tid & 63;
+    // three bf16 terms each, taken by truncation (each term keeps the top 8 significant
+    // bits of what is left, so three hold an fp32 significand exactly), interleaved:
+    // dword q = term q of S_a | term q of S_b << 16; dword 3 = 0
+    for (int e = tid; e < SNSB * 64; e += NT) {
+        const int sbi = e >> 6, ln = e & 63;
         const int r = ln & 15, gg = ln >> 4;
-        uint16_t t[2][4];
+        uint32_t tb[2][3];
 #pragma unroll
         for (int jj = 0; jj < 2; jj++) {
             float rem = S_lds[(sbi * 8 + 2 * gg + jj) * 16 + r];
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                t[jj][q] = f32_to_bf16(rem);
-                rem -= bf16_to_f32(t[jj][q]);
+            for (int q = 0; q < 3; q++) {
+                const uint32_t tq = __float_as_uint(rem) & 0xFFFF0000u;
+                tb[jj][q] = tq;
+                rem -= __uint_as_float(tq);
             }
         }
-        B_lds[tid] = (u32x4_t){(uint32_t)t[0][0] | ((uint32_t)t[1][0] << 16),
-                               (uint32_t)t[0][1] | ((uint32_t)t[1][1] << 16),
-                               (uint32_t)t[0][2] | ((uint32_t)t[1][2] << 16),
-                               (uint32_t)t[0][3] | ((uint32_t)t[1][3] << 16)};
+        B_lds[e] = (u32x4_t){__builtin_amdgcn_perm(tb[1][0], tb[0][0], 0x07060302u),
+                             __builtin_amdgcn_perm(tb[1][1], tb[0][1], 0x07060302u),
+                             __builtin_amdgcn_perm(tb[1][2], tb[0][2], 0x07060302u), 0u};
     }
     __syncthreads();
 
     // ---- stream
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-    float *part = a.part + (size_t)split * a.M * a.N;
+    const int m_out = PX ? PX / 4 : a.M;            // rows of the partial written
+    float *part = a.part + (size_t)split * m_out * a.N;
     const uint32_t bsel = 0x0C0C0000u | ((uint32_t)(2 * g + 1) << 8) | (uint32_t)(2 * g);
     int a_off = lane, b_off = lane;
     for (int t = t0; t < t1; t++) {
@@ -195,8 +200,10 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw
             f32x4_t tacc = zero;
 #pragma unroll
             for (int c = 0; c < 4; c++) {
+                const u32x4_t &qv = w.q[c >> 1];
                 u32x4_t blo, bhi;
-                s_decode(w.q[c], blo, bhi);
+                if (c & 1) s_decode(qv.z, qv.w, blo, bhi);
+                else s_decode(qv.x, qv.y, blo, bhi);
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
                     const int j = 2 * c + h;
@@ -212,11 +219,15 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw
             const f32x4_t Ds = mfma16x16x32(ab, (u32x4_t){cb, cb, cb, cb}, zero);
             acc += d * (tacc - 128.f * Ds) - dmin * Dm;
         }
+        if (PX) {
+#pragma unroll
+            for (int v = 0; v < 4; v++) acc[v] += __shfl_xor(acc[v], PX, WAVE);
+        }
         const int n = t * 16 + cl;
 #pragma unroll
         for (int v = 0; v < 4; v++) {
             const int R = 4 * g + v;
-            if (R < a.M) part[(size_t)R * a.N + n] = acc[v];
+            if (R < m_out) part[(size_t)R * a.N + n] = acc[v];
         }
     }
 }
@@ -225,7 +236,7 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw
 
 bool q4k_stream_ok(int M, int N, int K) { return M >= 1 && M <= 16 && (K / 256) % SNSB == 0 && N % 16 == 0; }
 
-Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves, int wpg) {
+Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int pair, int target_waves, int wpg) {
     Q4kStreamPlan p;
     p.wpg = wpg;
     const int KB = K / 256, ntile = N / 16;
@@ -235,20 +246,24 @@ Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int target_waves, int wpg) {
     if (tpw < 1) tpw = 1;
     p.tpw = tpw;
     p.grid_x = ceil_div(ceil_div(ntile, tpw), wpg);
+    // the (hi, lo) halves of a pair sit pair / 4 lane groups = 4 pair lanes apart
+    p.pair_done = (pair == 4 || pair == 8) && M == 2 * pair;
+    p.px = p.pair_done ? 4 * pair : 0;
     p.lds_bytes = (size_t)SNSB * 8 * 64 * 16 + SNSB * 64 * 16 + SNSB * 8 * 16 * 4;
-    p.part_bytes = (size_t)p.splits * M * N * 4;
+    p.part_bytes = (size_t)p.splits * (p.pair_done ? pair : M) * N * 4;
     return p;
 }
 
 hipError_t launch_q4k_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st) {
     const dim3 grid(p.grid_x, p.splits);
-#define QS_CASE(WPG)                                                                             \
-    if (p.wpg == WPG) {                                                                           \
-        hipLaunchKernelGGL((k_q4k_stream<WPG>), grid, dim3(64 * WPG), p.lds_bytes, st, a, p.tpw); \
-        return hipGetLastError();                                                                 \
+#define QS_CASE(WPG, PX)                                                                              \
+    if (p.wpg == WPG && p.px == PX) {                                                                 \
+        hipLaunchKernelGGL((k_q4k_stream<WPG, PX>), grid, dim3(64 * WPG), p.lds_bytes, st, a, p.tpw); \
+        return hipGetLastError();                                                                     \
     }
-    QS_CASE(4)
-    QS_CASE(8)
+    QS_CASE(4, 0)
+    QS_CASE(4, 16)
+    QS_CASE(4, 32)
 #undef QS_CASE
     return hipErrorInvalidValue;
 }

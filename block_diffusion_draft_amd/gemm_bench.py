@@ -6,9 +6,10 @@ Each shape (fc 25600->5120; q 5120->4096; k, v 5120->1024; o 4096->5120; gate, u
 5120->17408; down 17408->5120; FastFlowLM card "Qwen3.8-27B-DFlash2-NPU2", spec table
 "Draft" row) runs through the library's q4k_gemm entry point (product + split-K
 reduction to bf16) on bf16 N(0,1) activations and N(0, 0.02) weights packed to Q4_K
-(seed 1).  Calls rotate over enough copies of the weight matrix to span at least
---min-bytes, so no call is served from the last-level cache.  Prints one JSON line
-per shape: microseconds per call and the Q4_K weight bytes per second.
+(seed 1), regrouped on the device into the tiled layout.  Calls rotate over enough
+copies of the weight matrix to span at least --min-bytes, so no call is served from
+the last-level cache.  Prints one JSON line per shape: microseconds per call and the
+Q4_K weight bytes per second.
 """
 import argparse
 import json
@@ -32,7 +33,10 @@ def main():
         w_host = synth.q4k_normal(synth.GEMM_SEED, f"gemm.{name}", N, K, 0.02)
         wbytes = w_host.size
         copies = max(1, -(-args.min_bytes // wbytes))
-        w0 = torch.from_numpy(w_host).cuda()
+        w_rows = torch.from_numpy(w_host).cuda()
+        w0 = torch.empty_like(w_rows)
+        binding.q4k_to_tiled(w_rows, w0, N, K)        # the library's device layout
+        del w_rows
         ws = [w0] + [w0.clone() for _ in range(copies - 1)]
         x = torch.from_numpy(synth.normal_bf16(synth.GEMM_SEED, f"gemm.{name}.x", (M, K), 1.0)
                              .view(np.int16)).cuda()

@@ -16,6 +16,9 @@
  *   q4k_gemm             y = x . W^T with W in Q4_K super-blocks (the format of
  *                        the draft's fc, q/k/v/o and MLP matrices: same card,
  *                        "Weights" row), fp32 accumulation, bf16 output.
+ *   q4k_to_tiled         regroups a row-major Q4_K matrix into the tiled device
+ *                        layout every Q4_K entry point above reads (done once, when
+ *                        the weights are loaded).
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE memory owned by the caller.  The library
@@ -75,8 +78,9 @@ typedef struct {
     float pair_scale;  /* selector pair-score scale, 1/sqrt(sel_rank) */
 } dflash_config;
 
-/* Linear weights are [out][in] row-major (y = x . W^T).  In Q4_K each row is
- * in/256 consecutive 144-byte super-blocks; in bf16 it is `in` values. */
+/* Linear weights are [out][in] (y = x . W^T).  bf16: row-major, `in` values per
+ * row.  Q4_K: the tiled layout written by q4k_to_tiled (the row-major Q4_K matrix,
+ * each row in/256 consecutive 144-byte super-blocks, regrouped; same size). */
 typedef struct {
     const void *wq, *wk, *wv, *wo, *wg, *wu, *wd;
     const uint16_t *in_norm, *post_norm;   /* [hidden] */
@@ -160,13 +164,28 @@ int dflash_verify_prefix(const int32_t *draft, const int32_t *target, int batch,
 size_t q4k_gemm_workspace_bytes(int M, int N, int K);
 
 /*
- * y[M][N] (bf16) = x[M][K] (bf16) . W^T, W [N][K] in Q4_K, fp32 accumulation.
+ * y[M][N] (bf16) = x[M][K] (bf16) . W^T, W [N][K] in Q4_K (tiled layout, see
+ * q4k_to_tiled), fp32 accumulation.
  * K % 256 == 0, N % 16 == 0, 1 <= M <= 4096.  w, x, y and workspace 16-byte aligned.
  */
 int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
              void *workspace, size_t ws_bytes, void *stream);
 
-/* Decode n_blocks consecutive Q4_K super-blocks to fp32 (256 values each). */
+/*
+ * Tiled Q4_K layout (FastFlowLM card "Qwen3.8-27B-DFlash2-NPU2", "Weights" row, for
+ * the Q4_K format itself).  src: a row-major Q4_K matrix [N][K] (each row K/256
+ * super-blocks of 144 bytes: fp16 d, fp16 dmin, 12 scale bytes, 128 quant bytes read
+ * as 4 chunks of 32).  dst (same size, N K / 256 * 144 bytes) receives, for every
+ * 16-row tile t and super-block kb, one 2304-byte unit at (t K/256 + kb) 2304:
+ *   bytes [0, 256): the 16 block headers, row 16 t + r at 16 r;
+ *   bytes 256 + 1024 h + 16 (16 g + r) .. + 15 (h < 2, g < 4, r < 16): quant bytes
+ *   8 g .. 8 g + 7 of chunk 2 h, then of chunk 2 h + 1, of row 16 t + r's block.
+ * Every byte is copied, none changed.  N % 16 == 0, K % 256 == 0, both > 0; src and
+ * dst device pointers, 16-byte aligned, not overlapping.  Enqueued on `stream`.
+ */
+int q4k_to_tiled(const void *src, void *dst, int N, int K, void *stream);
+
+/* Decode n_blocks consecutive row-major Q4_K super-blocks to fp32 (256 values each). */
 int q4k_dequantize(const void *w, float *out, long long n_blocks, void *stream);
 
 /* Text of a dflash_status code. */

@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("dflash_draft_step", "dflash_verify_prefix", "q4k_gemm", "q4k_dequantize",
+    for n in ("dflash_draft_step", "dflash_verify_prefix", "q4k_gemm", "q4k_to_tiled", "q4k_dequantize",
               "dflash_workspace_bytes", "q4k_gemm_workspace_bytes", "dflash_status_str"):
         assert n in names
     assert sorted(binding.EXPORTS) == names
@@ -115,3 +115,8 @@ def test_q4k_gemm_and_verify_reject_bad_arguments():
     assert L.dflash_verify_prefix(FAKE, FAKE, 1, 0, FAKE, FAKE, None) == -1
     assert L.dflash_verify_prefix(None, FAKE, 1, 7, FAKE, FAKE, None) == -1
     assert L.q4k_dequantize(FAKE, FAKE, 0, None) == -1
+    assert L.q4k_to_tiled(None, FAKE, 16, 256, None) == -1
+    assert L.q4k_to_tiled(FAKE, FAKE + (1 << 30), 24, 256, None) == -2
+    assert L.q4k_to_tiled(FAKE, FAKE + (1 << 30), 16, 300, None) == -2
+    assert L.q4k_to_tiled(FAKE + 8, FAKE + (1 << 30), 16, 256, None) == -3
+    assert L.q4k_to_tiled(FAKE, FAKE + 1024, 16, 256, None) == -1   # overlapping buffers

@@ -49,8 +49,38 @@ def test_q4k_dequantize_bit_exact_full_matrix(name, N, K):
                               ref.astype(np.float32).reshape(-1).view(np.uint32)), (name, r0)
 
 
+def tiled_reference(w, N, K):
+    """The tiled Q4_K layout written out from its definition (a byte permutation of
+    the row-major blocks: 16 headers, then per half h the 16-byte slots 16 g + r
+    holding bytes 8 g .. 8 g + 7 of chunks 2 h and 2 h + 1)."""
+    KB = K // 256
+    blk = w.reshape(N // 16, 16, KB, 144).transpose(0, 2, 1, 3)       # [t][kb][r][144]
+    hdr = blk[..., :16].reshape(N // 16, KB, 256)
+    q = blk[..., 16:].reshape(N // 16, KB, 16, 4, 4, 8)                 # [t][kb][r][c][g][8]
+    halves = []
+    for h in range(2):
+        pair = np.concatenate([q[:, :, :, 2 * h], q[:, :, :, 2 * h + 1]], axis=-1)  # [t][kb][r][g][16]
+        halves.append(pair.transpose(0, 1, 3, 2, 4).reshape(N // 16, KB, 1024))   # slot 16 g + r
+    return np.concatenate([hdr] + halves, axis=-1).reshape(-1)
+
+
+def dev_tiled(w, N, K):
+    src = dev_u8(w)
+    dst = torch.empty_like(src)
+    binding.q4k_to_tiled(src, dst, N, K)
+    return dst
+
+
+@pytest.mark.parametrize("N,K", [(16, 256), (48, 768), (5120, 4096)])
+def test_q4k_to_tiled_byte_exact(N, K):
+    say(f"[q4k_to_tiled] {N}x{K}")
+    w = synth.q4k_normal(7, "tiled", N, K, 0.02)
+    got = dev_tiled(w, N, K).cpu().numpy()
+    assert np.array_equal(got, tiled_reference(w, N, K))
+
+
 def gemm_check(w, x, N, K, M):
-    wd = dev_u8(w)
+    wd = dev_tiled(w, N, K)
     xd = dev_bf16(x)
     y = torch.empty((M, N), dtype=torch.int16, device="cuda")
     ws = torch.empty(binding.q4k_gemm_workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
