@@ -111,7 +111,8 @@ int check_config(const dflash_config *c) {
         return DFLASH_ESHAPE;
     if (c->head_dim != 64 && c->head_dim != 128) return DFLASH_ESHAPE;
     if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->n_q_heads % c->n_kv_heads) return DFLASH_ESHAPE;
-    if (c->n_q_heads / c->n_kv_heads > 4 || c->n_q_heads % 2) return DFLASH_ESHAPE;
+    if (c->n_q_heads / c->n_kv_heads > 4 || c->n_q_heads % 2 || c->n_q_heads > 64)
+        return DFLASH_ESHAPE;
     const int qd = c->n_q_heads * c->head_dim;
     if (qd % 256 || qd > 8192) return DFLASH_ESHAPE;
     if (c->block != DFLASH_BLOCK) return DFLASH_ESHAPE;

@@ -71,6 +71,13 @@ __device__ __forceinline__ float row_inv(const RowScale &s, int r) {
     const int br = s.map ? (r / 7) * 8 + r % 7 + 1 : r;
     const float *p = s.ssq + (size_t)br * s.nchunk;
     float ss = 0.f;
-    for (int i = 0; i < s.nchunk; i++) ss += p[i];
+    for (int i0 = 0; i0 < s.nchunk; i0 += 8) {          // 8 loads in flight, summed in order
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) v[u] = p[min(i0 + u, s.nchunk - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+            if (i0 + u < s.nchunk) ss += v[u];
+    }
     return rsqrtf(ss / s.n + s.eps);
 }

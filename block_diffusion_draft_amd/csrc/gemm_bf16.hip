@@ -195,8 +195,12 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a, int ti
 // every load covers full lines.  The group passes through a 4 KB per-wave LDS buffer
 // (16-byte chunks XOR-swizzled by row: conflict-free writes and fragment reads) into
 // MFMA lane order.  Groups are loaded HS_D - 1 ahead in registers, across tiles.
+// The outputs of up to 8 consecutive tiles stay in registers and are then written as
+// 128 consecutive columns per row (lanes over columns, whole lines): written tile by
+// tile in the MFMA layout, the rows' 64-byte pieces cost the stream about 8%.
 constexpr int HS_WAVES = 8;
 constexpr int HS_D = 4;
+constexpr int HS_TB = 8;           // tiles per output batch
 
 __global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a, int tiles_per_wave) {
     extern __shared__ __align__(16) u32x4_t lds[];
@@ -234,52 +238,97 @@ __global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a, int tiles_p
 #pragma unroll
     for (int u = 0; u < HS_D - 1; u++) load_group(ring[u]);
 
-    for (int e = tid; e < nks * 32 + 16; e += 512) {
-        const int ks = e >> 5, slot = e & 31, gg = slot >> 3, r = slot & 7;
-        u32x4_t v = {0, 0, 0, 0};
-        if (e < nks * 32 && r < a.M)
-            v = *reinterpret_cast<const u32x4_t *>(a.A + (size_t)r * a.lda + ks * 32 + 8 * gg);
-        Alds[e] = v;
+    // row scales (deferred RMSNorm): lane l < 8 sums row l's partial sums of squares,
+    // loaded 8 at a time; issued before the activation loads so both are in flight
+    const RowScale &rs = a.rs;
+    float ssl = 0.f;
+    if (rs.ssq && lane < 8 && lane < a.M) {
+        const int br = rs.map ? (lane / 7) * 8 + lane % 7 + 1 : lane;
+        const float *sp = rs.ssq + (size_t)br * rs.nchunk;
+        for (int i0 = 0; i0 < rs.nchunk; i0 += 8) {
+            float pv[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) pv[u] = sp[min(i0 + u, rs.nchunk - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                if (i0 + u < rs.nchunk) ssl += pv[u];
+        }
+    }
+    // activations -> LDS in lane order (8 loads in flight per thread)
+    const int nA = nks * 32 + 16;
+    for (int e0 = tid; e0 < nA; e0 += 8 * 512) {
+        u32x4_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int e = min(e0 + 512 * u, nks * 32 - 1);
+            const int ks = e >> 5, slot = e & 31, gg = slot >> 3, r = min(slot & 7, a.M - 1);
+            v[u] = *reinterpret_cast<const u32x4_t *>(a.A + (size_t)r * a.lda + ks * 32 + 8 * gg);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int e = e0 + 512 * u;
+            const int r = e & 7;
+            if (e < nA) Alds[e] = (e < nks * 32 && r < a.M) ? v[u] : (u32x4_t){0, 0, 0, 0};
+        }
     }
     __syncthreads();
 
     float inv8[8];
 #pragma unroll
-    for (int r = 0; r < 8; r++) inv8[r] = r < a.M ? row_inv(a.rs, r) : 0.f;
-    float rinv[4];
-#pragma unroll
-    for (int v = 0; v < 4; v++) rinv[v] = g == 0 ? inv8[v] : (g == 1 ? inv8[4 + v] : 0.f);
+    for (int r = 0; r < 8; r++) {
+        const float ss = __shfl(ssl, r, WAVE);
+        inv8[r] = r < a.M ? (rs.ssq ? rsqrtf(ss / rs.n + rs.eps) : 1.f) : 0.f;
+    }
 
     // lanes of rows >= 8 read the zero entry
     const int aoff = c < 8 ? g * 8 + c : 0;
     const int astep = c < 8 ? 32 : 0;
     const int abase = c < 8 ? 0 : nks * 32;
-    for (int tile = t0; tile < t1; tile++) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int q0 = 0; q0 < ngr; q0 += HS_D) {
+    for (int tb = t0; tb < t1; tb += HS_TB) {
+        // tile tb + u -> res[u]: D rows 4 g + v, column c of the tile
+        f32x4_t res[HS_TB];
 #pragma unroll
-            for (int u = 0; u < HS_D; u++) {
-                load_group(ring[(u + HS_D - 1) % HS_D]);
-                u32x4_t *T = Tb + (u & 1) * 256;
+        for (int u0 = 0; u0 < HS_TB; u0++) {
+            res[u0] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            if (tb + u0 >= t1) continue;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            for (int q0 = 0; q0 < ngr; q0 += HS_D) {
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int r = 4 * i + lr;
-                    T[r * 16 + (ls ^ r)] = ring[u][i];
-                }
+                for (int u = 0; u < HS_D; u++) {
+                    load_group(ring[(u + HS_D - 1) % HS_D]);
+                    u32x4_t *T = Tb + (u & 1) * 256;
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const u32x4_t bf = T[c * 16 + ((4 * j + g) ^ c)];
-                    const u32x4_t af = Alds[abase + ((q0 + u) * 4 + j) * astep + aoff];
-                    acc = mfma16x16x32(af, bf, acc);
+                    for (int i = 0; i < 4; i++) {
+                        const int r = 4 * i + lr;
+                        T[r * 16 + (ls ^ r)] = ring[u][i];
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const u32x4_t bf = T[c * 16 + ((4 * j + g) ^ c)];
+                        const u32x4_t af = Alds[abase + ((q0 + u) * 4 + j) * astep + aoff];
+                        acc = mfma16x16x32(af, bf, acc);
+                    }
                 }
             }
+            res[u0] = acc;
         }
-        if (g < 2) {
-            const int n = tile * 16 + c;
+        // row m, columns 16 tb + 64 h + lane: tile 4 h + lane / 16, column lane % 16,
+        // held by lane 16 (m / 4) + lane % 16 as component m % 4
+        const int ncols = min(HS_TB, t1 - tb) * 16;
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const int m = 4 * g + v;
-                if (m < a.M) a.C[(size_t)m * a.ldc + n] = acc[v] * rinv[v];
+        for (int m = 0; m < 8; m++) {
+            if (m >= a.M) break;
+            const int src = 16 * (m / 4) + (lane & 15);
+#pragma unroll
+            for (int h = 0; h < HS_TB / 4; h++) {
+                float v = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float x = __shfl(res[4 * h + j][m % 4], src, WAVE);
+                    v = (lane >> 4) == j ? x : v;
+                }
+                const int col = 64 * h + lane;
+                if (col < ncols) a.C[(size_t)m * a.ldc + (size_t)tb * 16 + col] = v * inv8[m];
             }
         }
     }

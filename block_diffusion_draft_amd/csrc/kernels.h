@@ -147,7 +147,7 @@ struct Q4kStreamPlan {
 };
 bool q4k_stream_ok(int M, int N, int K);
 Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int pair = 0, int target_waves = 2048,
-                              int wpg = 4);
+                              int wpg = 0);
 hipError_t launch_q4k_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st);
 
 // Output rows r < M_out: v = sum over splits of partial rows r (+ r + pair), N a multiple

@@ -301,6 +301,9 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
 // so that z_t = W_c . vec(o_t) = the sum of zp over (h, cc).
 constexpr int MC = 32;              // columns per merge workgroup
 
+constexpr int MB = 40;              // chunk partials per thread loaded up front
+constexpr int MAXE = 4;             // conv-tap outputs per thread (T 2 n_q <= 1024)
+
 __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
     const int h = blockIdx.x, cc = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -314,32 +317,62 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
     float *w = sm;                      // [T][nch1] merge weights
     float *os = sm + T * nch1;          // [T][MC]
     float *zp = a.zp + (((size_t)b * a.n_q + h) * CC + cc) * T * nq2;
+
+    // ---- every load first, so the kernel waits on memory once: this thread's chunk
+    // partials (the first MB chunks), the (m, l) pairs of its wave's rows (rows wave and
+    // wave + 4, the first 64 chunks), and the conv-tap weights of its (t, q) pairs.
+    // Indices are clamped (in bounds); what is not used is discarded by selects.
+    const float *O = a.O + ((size_t)(b * a.n_kv + kvh) * nch1 * QR + hq * T + t) * d + cc * MC + col;
+    const size_t cstride = (size_t)QR * d;
+    float pv[MB];
+#pragma unroll
+    for (int u = 0; u < MB; u++) pv[u] = O[(size_t)min(u, nch1 - 1) * cstride];
+    const float *ml = a.ml + ((size_t)(b * a.n_kv + kvh) * nch1) * QR * 2;
+    float2 mlv[2];
+#pragma unroll
+    for (int ri = 0; ri < 2; ri++) {
+        const int tr = min(wave + 4 * ri, T - 1), c = min(lane, nch1 - 1);
+        mlv[ri] = *reinterpret_cast<const float2 *>(ml + ((size_t)c * QR + hq * T + tr) * 2);
+    }
+    const int ne = T * nq2;
+    u32x4_t wv[MAXE][MC / 8];
+#pragma unroll
+    for (int i = 0; i < MAXE; i++) {
+        const int e = min(tid + 256 * i, ne - 1), q = e % nq2;
+        const uint16_t *wr = a.w_conv + (size_t)q * qd + c0;
+#pragma unroll
+        for (int k = 0; k < MC / 8; k++) wv[i][k] = *reinterpret_cast<const u32x4_t *>(wr + 8 * k);
+    }
+
     if (!a.valid[b]) {
         a.o[((size_t)b * T + t) * qd + c0 + col] = 0.f;
-        for (int e = tid; e < T * nq2; e += 256) zp[e] = 0.f;
+        for (int e = tid; e < ne; e += 256) zp[e] = 0.f;
         return;
     }
     const int n = a.ctx_len[b];
     const int hi = n + a.t_new;
     const int lo = hi - a.window > 0 ? hi - a.window : 0;
     const int nch_b = ceil_div(hi - lo, a.chunk);
-    const float *ml = a.ml + ((size_t)(b * a.n_kv + kvh) * nch1) * QR * 2;
-    // merge weights: wave per row (rows wave, wave + 4), lanes over chunks
-    for (int tr = wave; tr < T; tr += 4) {
+    auto used = [&](int c) { return c < nch_b || c == a.n_chunks; };
+    // merge weights exp(m_c - M) / sum_c exp(m_c - M) l_c: wave per row, lanes over chunks
+#pragma unroll
+    for (int ri = 0; ri < 2; ri++) {
+        const int tr = wave + 4 * ri;
+        if (tr >= T) break;
+        auto mlc = [&](int c) -> float2 {            // chunks past the first 64 (long windows)
+            return c < 64 ? mlv[ri] : *reinterpret_cast<const float2 *>(ml + ((size_t)c * QR + hq * T + tr) * 2);
+        };
         float M = -INFINITY;
-        for (int c = lane; c < nch1; c += 64) {
-            const bool used = c < nch_b || c == a.n_chunks;
-            if (used) M = fmaxf(M, ml[((size_t)c * QR + hq * T + tr) * 2]);
-        }
+        for (int c = lane; c < nch1; c += 64)
+            if (used(c)) M = fmaxf(M, mlc(c).x);
         M = wave_max(M);
         float L = 0.f;
         for (int c = lane; c < nch1; c += 64) {
-            const bool used = c < nch_b || c == a.n_chunks;
             float e = 0.f;
-            if (used) {
-                const float *s = ml + ((size_t)c * QR + hq * T + tr) * 2;
-                e = expf(s[0] - M);
-                L += e * s[1];
+            if (used(c)) {
+                const float2 v = mlc(c);
+                e = expf(v.x - M);
+                L += e * v.y;
             }
             w[tr * nch1 + c] = e;
         }
@@ -348,36 +381,39 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
         for (int c = lane; c < nch1; c += 64) w[tr * nch1 + c] *= invL;
     }
     __syncthreads();
-    // merged output: thread (t, col) over the chunks, 4 independent partial sums
-    const float *O = a.O + ((size_t)(b * a.n_kv + kvh) * nch1 * QR + hq * T + t) * d + cc * MC + col;
-    const size_t cstride = (size_t)QR * d;
+    // merged output of (t, col): the weighted chunk partials (unused chunks skipped)
     const float *wt = w + t * nch1;
-    // 16 chunk partials in flight per batch (clamped indices, weights of the padding 0)
     float ov = 0.f;
-    for (int c0 = 0; c0 < nch1; c0 += 16) {
-        float pv[16];
 #pragma unroll
-        for (int u = 0; u < 16; u++) pv[u] = O[(size_t)min(c0 + u, nch1 - 1) * cstride];
+    for (int u = 0; u < MB; u++)
+        if (u < nch1 && used(u)) ov += wt[u] * pv[u];
+    for (int cb = MB; cb < nch1; cb += 16) {
+        float pb[16];
+#pragma unroll
+        for (int u = 0; u < 16; u++) pb[u] = O[(size_t)min(cb + u, nch1 - 1) * cstride];
 #pragma unroll
         for (int u = 0; u < 16; u++)
-            if (c0 + u < nch1) ov += wt[c0 + u] * pv[u];
+            if (cb + u < nch1 && used(cb + u)) ov += wt[cb + u] * pb[u];
     }
     os[t * MC + col] = ov;
     a.o[((size_t)b * T + t) * qd + c0 + col] = ov;
     __syncthreads();
     // conv-tap partials of this slice: (t, q) pairs over the threads
-    for (int e = tid; e < T * nq2; e += 256) {
-        const int tt = e / nq2, q = e % nq2;
-        const uint16_t *wr = a.w_conv + (size_t)q * qd + c0;
+#pragma unroll
+    for (int i = 0; i < MAXE; i++) {
+        const int e = tid + 256 * i;
+        if (e >= ne) break;
+        const int tt = e / nq2;
         const float *ot = os + tt * MC;
         float acc = 0.f;
 #pragma unroll
-        for (int i = 0; i < MC; i += 8) {
-            const u32x4_t wv = *reinterpret_cast<const u32x4_t *>(wr + i);
-            acc += bf16_to_f32(wv.x & 0xFFFF) * ot[i] + bf16_to_f32(wv.x >> 16) * ot[i + 1];
-            acc += bf16_to_f32(wv.y & 0xFFFF) * ot[i + 2] + bf16_to_f32(wv.y >> 16) * ot[i + 3];
-            acc += bf16_to_f32(wv.z & 0xFFFF) * ot[i + 4] + bf16_to_f32(wv.z >> 16) * ot[i + 5];
-            acc += bf16_to_f32(wv.w & 0xFFFF) * ot[i + 6] + bf16_to_f32(wv.w >> 16) * ot[i + 7];
+        for (int k = 0; k < MC / 8; k++) {
+            const u32x4_t v = wv[i][k];
+            const float *o8 = ot + 8 * k;
+            acc += bf16_to_f32(v.x & 0xFFFF) * o8[0] + bf16_to_f32(v.x >> 16) * o8[1];
+            acc += bf16_to_f32(v.y & 0xFFFF) * o8[2] + bf16_to_f32(v.y >> 16) * o8[3];
+            acc += bf16_to_f32(v.z & 0xFFFF) * o8[4] + bf16_to_f32(v.z >> 16) * o8[5];
+            acc += bf16_to_f32(v.w & 0xFFFF) * o8[6] + bf16_to_f32(v.w >> 16) * o8[7];
         }
         zp[e] = acc;
     }
@@ -389,7 +425,6 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
 constexpr int CONV_HEADS = 2;       // heads per conv workgroup
 
 __global__ __launch_bounds__(256) void k_conv_apply(MergeConvArgs a) {
-    __shared__ float zpart[256];
     __shared__ float z[2 * CONV_HEADS];
     const int b = blockIdx.x / a.T, t = blockIdx.x % a.T, tid = threadIdx.x;
     const int qd = a.n_q * a.d, nq2 = 2 * a.n_q, CC = a.d / MC;
@@ -399,24 +434,43 @@ __global__ __launch_bounds__(256) void k_conv_apply(MergeConvArgs a) {
     constexpr int NQ = 2 * CONV_HEADS, PER_Q = 256 / NQ;
     const int qi = tid / PER_Q, part = tid % PER_Q;
     const int q = qi < CONV_HEADS ? h0 + qi : a.n_q + h0 + qi - CONV_HEADS;
-    float s = 0.f;
-    for (int p = part; p < np; p += PER_Q) s += a.zp[(((size_t)b * np + p) * a.T + t) * nq2 + q];
-    zpart[tid] = s;
-    __syncthreads();
-    if (tid < NQ) {
-        float acc = 0.f;
-        for (int i = 0; i < PER_Q; i++) acc += zpart[tid * PER_Q + i];
-        z[tid] = acc;
-    }
-    __syncthreads();
+    // the attention outputs this thread scales are loaded together with the partials
     const float *ot = a.o + ((size_t)b * a.T + t) * qd;
-    const float *op = ot - qd;
-    uint16_t *Y = a.Y + ((size_t)b * a.T + t) * qd;
+    const float *op = t > 0 ? ot - qd : ot;             // row t - 1 (t = 0: unused)
     const int i0 = h0 * a.d, i1 = min(i0 + CONV_HEADS * a.d, qd);
-    for (int i = i0 + tid; i < i1; i += 256) {
-        const int k = (i - i0) / a.d;
-        const float prev = t > 0 ? op[i] : 0.f;
-        Y[i] = f32_to_bf16(z[k] * ot[i] + z[CONV_HEADS + k] * prev);
+    constexpr int NI = CONV_HEADS * 128 / 256;           // outputs per thread (d <= 128)
+    float ocur[NI], oprev[NI];
+#pragma unroll
+    for (int u = 0; u < NI; u++) {
+        const int i = min(i0 + tid + 256 * u, i1 - 1);
+        ocur[u] = ot[i];
+        oprev[u] = op[i];
+    }
+    constexpr int NP = 4;                                // partials per thread per batch
+    float s = 0.f;
+    for (int p0 = part; p0 < np; p0 += NP * PER_Q) {
+        float v[NP];
+#pragma unroll
+        for (int u = 0; u < NP; u++) {
+            const int p = min(p0 + u * PER_Q, np - 1);
+            v[u] = a.zp[(((size_t)b * np + p) * a.T + t) * nq2 + q];
+        }
+#pragma unroll
+        for (int u = 0; u < NP; u++)
+            if (p0 + u * PER_Q < np) s += v[u];
+    }
+    // PER_Q == 64: tap value qi is the sum over wave qi
+    s = wave_sum(s);
+    if ((tid & 63) == 0) z[qi] = s;
+    __syncthreads();
+    uint16_t *Y = a.Y + ((size_t)b * a.T + t) * qd;
+#pragma unroll
+    for (int u = 0; u < NI; u++) {
+        const int i = i0 + tid + 256 * u;
+        if (i < i1) {
+            const int k = (i - i0) / a.d;
+            Y[i] = f32_to_bf16(z[k] * ocur[u] + (t > 0 ? z[CONV_HEADS + k] * oprev[u] : 0.f));
+        }
     }
 }
 

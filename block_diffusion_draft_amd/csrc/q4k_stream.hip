@@ -19,8 +19,8 @@
 //    B operand holds the 6-bit sc_j or m_j (exact in bf16);
 //  * the super-block adds d (T - 128 sum_j sc_j S_rj) - dmin sum_j m_j S_rj.
 //
-// Work split: a workgroup (4 waves) owns one split of 4 super-blocks (1024 values of
-// K) and 4 runs of tpw consecutive 16-column tiles, one run per wave.  The split's
+// Work split: a workgroup (4 or 8 waves) owns one split of 4 super-blocks (1024 values
+// of K) and one run of tpw consecutive 16-column tiles per wave.  The split's
 // activation rows are staged once in LDS in MFMA lane order; their sub-block sums
 // come from MFMAs against a ones operand.  Each wave then streams its tiles'
 // super-blocks as one flat sequence of (tile, super-block) stages, 4 stages in
@@ -238,13 +238,16 @@ bool q4k_stream_ok(int M, int N, int K) { return M >= 1 && M <= 16 && (K / 256) 
 
 Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int pair, int target_waves, int wpg) {
     Q4kStreamPlan p;
-    p.wpg = wpg;
     const int KB = K / 256, ntile = N / 16;
     p.splits = KB / SNSB;
     const long long wave_tiles = (long long)ntile * p.splits;
     int tpw = (int)((wave_tiles + target_waves - 1) / target_waves);
     if (tpw < 1) tpw = 1;
     p.tpw = tpw;
+    // wpg 0: 8-wave workgroups when every wave has a single tile (one activation
+    // staging then feeds twice the tiles), else 4
+    p.wpg = wpg > 0 ? wpg : (tpw == 1 ? 8 : 4);
+    wpg = p.wpg;
     p.grid_x = ceil_div(ceil_div(ntile, tpw), wpg);
     // the (hi, lo) halves of a pair sit pair / 4 lane groups = 4 pair lanes apart
     p.pair_done = (pair == 4 || pair == 8) && M == 2 * pair;
@@ -264,6 +267,9 @@ hipError_t launch_q4k_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipS
     QS_CASE(4, 0)
     QS_CASE(4, 16)
     QS_CASE(4, 32)
+    QS_CASE(8, 0)
+    QS_CASE(8, 16)
+    QS_CASE(8, 32)
 #undef QS_CASE
     return hipErrorInvalidValue;
 }

@@ -19,13 +19,16 @@ namespace {
 constexpr int MAXK = 16;
 constexpr int MAXP = 16;
 
-// One workgroup per sequence.  The pair scores of adjacent positions are K x K
-// products of gathered codebook rows, T_t = s A[ids_t] B[ids_{t+1}]^T, computed as
-// 16x16xr MFMA tiles (exact bf16 products, fp32 accumulation) straight from the
+// One workgroup (8 waves) per sequence.  The pair scores of adjacent positions are
+// K x K products of gathered codebook rows, T_t = s A[ids_t] B[ids_{t+1}]^T, computed
+// as 16x16xr MFMA tiles (exact bf16 products, fp32 accumulation) straight from the
 // gathered rows: lane (i, k-group) loads its 16-byte fragments of A[ids_t[i]] and
 // B[ids_{t+1}[i]] for every k-step, all loads in flight at once.  Wave w handles
-// positions t = w, w + 4, ...; the dynamic programme then runs on K lanes.
-__global__ __launch_bounds__(256) void k_viterbi(const int32_t *cand_ids, const float *cand_logp,
+// positions t = w, w + 8, ... (one each for the 8-token block); the dynamic
+// programme then runs on K lanes.
+constexpr int VIT_WAVES = 8;
+
+__global__ __launch_bounds__(64 * VIT_WAVES) void k_viterbi(const int32_t *cand_ids, const float *cand_logp,
                                                  const uint16_t *code_a, const uint16_t *code_b,
                                                  int P, int K, int r, float s, const int32_t *valid,
                                                  int32_t *draft) {
@@ -39,7 +42,7 @@ __global__ __launch_bounds__(256) void k_viterbi(const int32_t *cand_ids, const 
         if (tid < P) draft[(size_t)b * P + tid] = -1;
         return;
     }
-    for (int e = tid; e < P * MAXK; e += 256) {
+    for (int e = tid; e < P * MAXK; e += 64 * VIT_WAVES) {
         const int t = e / MAXK, i = e % MAXK;
         ids[t][i] = i < K ? cand_ids[(size_t)b * P * K + t * K + i] : -1;
         lp[t][i] = i < K ? cand_logp[(size_t)b * P * K + t * K + i] : -INFINITY;
@@ -47,7 +50,7 @@ __global__ __launch_bounds__(256) void k_viterbi(const int32_t *cand_ids, const 
     __syncthreads();
     const int c = lane & 15, g = lane >> 4;
     const int nks = r / 32;
-    for (int t = wave; t + 1 < P; t += 4) {
+    for (int t = wave; t + 1 < P; t += VIT_WAVES) {
         const int ua = ids[t][c], vb = ids[t + 1][c];
         const uint16_t *ar = code_a + (size_t)(ua >= 0 ? ua : 0) * r + 8 * g;
         const uint16_t *br = code_b + (size_t)(vb >= 0 ? vb : 0) * r + 8 * g;
@@ -128,7 +131,7 @@ __global__ void k_verify(const int32_t *draft, const int32_t *target, int B, int
 hipError_t launch_viterbi(const int32_t *cand_ids, const float *cand_logp, const uint16_t *code_a,
                           const uint16_t *code_b, int B, int P, int K, int r, float pair_scale,
                           const int32_t *valid, int32_t *draft_tokens, hipStream_t st) {
-    hipLaunchKernelGGL(k_viterbi, dim3(B), dim3(256), 0, st, cand_ids, cand_logp, code_a, code_b,
+    hipLaunchKernelGGL(k_viterbi, dim3(B), dim3(64 * VIT_WAVES), 0, st, cand_ids, cand_logp, code_a, code_b,
                        P, K, r, pair_scale, valid, draft_tokens);
     return hipGetLastError();
 }

@@ -66,10 +66,10 @@ typedef enum { DFLASH_W_Q4K = 0, DFLASH_W_BF16 = 1 } dflash_weight_fmt;
  * 8 KV heads of 128, window 2048, vocab 248320, 5 taps, block 8, top 16, rank
  * 256 (FastFlowLM card spec table "Draft" row; aiqre page "Specification").
  * Supported by the kernels: hidden, ffn and n_q*head_dim multiples of 256; hidden
- * and n_q*head_dim at most 8192; head_dim 64 or 128; n_q even and a multiple of
- * n_kv with n_q / n_kv <= 4; block == 8; 1 <= top_k <= 16; sel_rank a multiple of
- * 32 up to 4096; vocab >= top_k, a multiple of 16, at most 1,048,576; window at
- * most 65536. */
+ * and n_q*head_dim at most 8192; head_dim 64 or 128; n_q even, at most 64 and a
+ * multiple of n_kv with n_q / n_kv <= 4; block == 8; 1 <= top_k <= 16; sel_rank a
+ * multiple of 32 up to 4096; vocab >= top_k, a multiple of 16, at most 1,048,576;
+ * window at most 65536. */
 typedef struct {
     int n_layers, hidden, ffn, n_q_heads, n_kv_heads, head_dim, window, vocab;
     int n_taps, block, top_k, sel_rank, weight_fmt;
