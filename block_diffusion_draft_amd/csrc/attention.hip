@@ -14,12 +14,16 @@
 // chunks (log-sum-exp merge).  The last chunk index holds the 8 block rows.
 // P is rounded to bf16 for the MFMA and the row sum is taken over the same
 // rounded values, so the normalisation matches the products.
+// K and V rows sit in LDS as loaded (key-major); the V operand of O = P V (keys
+// along the MFMA's k) comes from gfx950's transposing LDS read, which hands each
+// lane 4 consecutive keys of one column.  O leaves through LDS as whole rows.
 #include "common.h"
 #include "kernels.h"
 
 namespace {
 
 constexpr int KT = 64;           // keys per inner step
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 constexpr int MAXQR = 32;        // query rows per workgroup (G <= 4)
 
 template <int D>
@@ -45,13 +49,19 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
         nkeys = min(a.chunk, hi - k0);
     }
 
-    const int DS = d + 8;                   // padded LDS row stride (bf16)
+    const int DS = d + 8;                   // padded LDS row stride of Q and K (bf16)
+    constexpr int VS = D + 16;              // V row stride: 4 rows of a transposing read
+                                            // land 8 banks apart (no conflicts)
+    constexpr int OS = D + 4;               // fp32 row stride of the output staging
+    // K and V rows; after the key loop the same bytes stage O (fp32 [QR][OS])
+    __shared__ __align__(16) uint16_t KVs[KT * (128 + 8) + KT * (128 + 16)];
+    uint16_t *Ks = KVs, *Vs = KVs + KT * (128 + 8);
+    float *Os = reinterpret_cast<float *>(KVs);
     __shared__ __align__(16) uint16_t Qs[MAXQR * (128 + 8)];
-    __shared__ __align__(16) uint16_t Ks[KT * (128 + 8)];
-    __shared__ __align__(16) uint16_t Vt[128 * (KT + 8)];
     __shared__ __align__(16) uint16_t Ps[MAXQR * (KT + 8)];
     __shared__ float Ss[MAXQR * KT];
     __shared__ float m_run[MAXQR], l_run[MAXQR], alpha[MAXQR];
+    static_assert(MAXQR * (128 + 4) * 4 <= (KT * (128 + 8) + KT * (128 + 16)) * 2, "O staging fits");
 
     // Q rows: row = hq * T + t  <-  Q[b][t][kvh*G + hq][:] (rows >= QR: zeros)
     {
@@ -121,13 +131,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
             const bool in = j < nk;
             const u32x4_t z = {0, 0, 0, 0};
             *reinterpret_cast<u32x4_t *>(&Ks[j * DS + 8 * q8]) = in ? kv[i] : z;
-            const u32x4_t w = in ? vv[i] : z;
-            const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                Vt[(8 * q8 + 2 * q) * (KT + 8) + j] = (uint16_t)(w4[q] & 0xFFFF);
-                Vt[(8 * q8 + 2 * q + 1) * (KT + 8) + j] = (uint16_t)(w4[q] >> 16);
-            }
+            *reinterpret_cast<u32x4_t *>(&Vs[j * VS + 8 * q8]) = in ? vv[i] : z;
         }
         __syncthreads();
         // S = Q K^T (scaled, masked)
@@ -161,13 +165,17 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
             const float m_old = m_run[row];
             const float m_new = fmaxf(m_old, mx);
             float ls = 0.f;
+            uint32_t pw[4];
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const float p = sv[i] == -INFINITY ? 0.f : expf(sv[i] - m_new);
-                const uint16_t pb = f32_to_bf16(p);
-                Ps[row * (KT + 8) + part * 8 + i] = pb;
-                ls += bf16_to_f32(pb);
+            for (int i = 0; i < 8; i += 2) {
+                const float p0 = sv[i] == -INFINITY ? 0.f : expf(sv[i] - m_new);
+                const float p1 = sv[i + 1] == -INFINITY ? 0.f : expf(sv[i + 1] - m_new);
+                const uint16_t b0 = f32_to_bf16(p0), b1 = f32_to_bf16(p1);
+                pw[i / 2] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+                ls += bf16_to_f32(b0);
+                ls += bf16_to_f32(b1);
             }
+            *reinterpret_cast<u32x4_t *>(&Ps[row * (KT + 8) + part * 8]) = (u32x4_t){pw[0], pw[1], pw[2], pw[3]};
             ls += __shfl_xor(ls, 1, WAVE);
             ls += __shfl_xor(ls, 2, WAVE);
             ls += __shfl_xor(ls, 4, WAVE);
@@ -189,26 +197,41 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
                 for (int v = 0; v < 4; v++) acc[u][v] *= alpha[rt * 16 + 4 * g + v];
                 for (int ks = 0; ks < KT / 32; ks++) {
                     const u32x4_t pa = *reinterpret_cast<const u32x4_t *>(&Ps[(rt * 16 + cl) * (KT + 8) + ks * 32 + 8 * g]);
-                    const u32x4_t vb = *reinterpret_cast<const u32x4_t *>(&Vt[(dt * 16 + cl) * (KT + 8) + ks * 32 + 8 * g]);
+                    // lane (g, cl) needs V[ks 32 + 8 g + 0..7][dt 16 + cl]: two transposing
+                    // reads; source lane (k, q) = (cl >> 2, cl & 3) names row base + k,
+                    // columns 4 q .. 4 q + 3, and lane cl receives column cl of the 4 rows
+                    const uint16_t *vrow = &Vs[(ks * 32 + 8 * g + (cl >> 2)) * VS + dt * 16 + 4 * (cl & 3)];
+                    const v4i16_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16_t *)(vrow));
+                    const v4i16_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16_t *)(vrow + 4 * VS));
+                    const u32x4_t vb = {(uint32_t)(uint16_t)v0.x | ((uint32_t)(uint16_t)v0.y << 16),
+                                        (uint32_t)(uint16_t)v0.z | ((uint32_t)(uint16_t)v0.w << 16),
+                                        (uint32_t)(uint16_t)v1.x | ((uint32_t)(uint16_t)v1.y << 16),
+                                        (uint32_t)(uint16_t)v1.z | ((uint32_t)(uint16_t)v1.w << 16)};
                     acc[u] = mfma16x16x32(pa, vb, acc[u]);
                 }
             }
         }
     }
     __syncthreads();
-    const int nch1 = a.n_chunks + 1;
-    const size_t base = ((size_t)(b * a.n_kv + kvh) * nch1 + c) * QR;
+    // O tiles -> LDS rows, then whole rows to global (16 bytes per lane)
 #pragma unroll
     for (int u = 0; u < 4; u++) {
         const int ti = wave + 4 * u;
         if (ti < nto) {
             const int rt = ti / (d / 16), dt = ti % (d / 16);
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const int row = rt * 16 + 4 * g + v;
-                if (row < QR) a.O[(base + row) * d + dt * 16 + cl] = acc[u][v];
-            }
+            for (int v = 0; v < 4; v++) Os[(rt * 16 + 4 * g + v) * OS + dt * 16 + cl] = acc[u][v];
         }
+    }
+    __syncthreads();
+    const int nch1 = a.n_chunks + 1;
+    const size_t base = ((size_t)(b * a.n_kv + kvh) * nch1 + c) * QR;
+    for (int e = tid; e < QR * (d / 4); e += 256) {
+        const int row = e / (d / 4), c4 = e % (d / 4);
+        *reinterpret_cast<float4 *>(&a.O[(base + row) * d + 4 * c4]) =
+            *reinterpret_cast<const float4 *>(&Os[row * OS + 4 * c4]);
     }
     if (tid < QR) {
         a.ml[(base + tid) * 2] = m_run[tid];
