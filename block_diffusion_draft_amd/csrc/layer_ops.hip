@@ -293,15 +293,16 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
 
 // ---------------------------------------------------------------- merge + dynamic conv
 // k_attn_merge: one workgroup per (query head h, 32-column slice cc of the head,
-// sequence b); thread (t, col) of the 8 x 32 block.  Combines the split-window
-// partials of head h (log-sum-exp merge: weight exp(m_c - M) / sum_c exp(m_c - M) l_c
+// sequence b); each wave sums a quarter of the chunks over the 8 x 32 block (16 bytes
+// per lane), the waves' sums are added in LDS.  Combines the split-window partials of
+// head h (log-sum-exp merge: weight exp(m_c - M) / sum_c exp(m_c - M) l_c
 // on the unnormalised chunk outputs) into o[b][t][h d + 32 cc + col] (fp32), then
 // contributes this slice's share of the convolution taps
 //     zp[b][h][cc][t][q] = sum_{e in slice} W_c[q][h d + e] o[b][t][h d + e],  q < 2 n_q,
 // so that z_t = W_c . vec(o_t) = the sum of zp over (h, cc).
 constexpr int MC = 32;              // columns per merge workgroup
 
-constexpr int MB = 40;              // chunk partials per thread loaded up front
+constexpr int MW = 12;              // chunk partials per lane loaded up front (x 4 waves)
 constexpr int MAXE = 4;             // conv-tap outputs per thread (T 2 n_q <= 1024)
 
 __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
@@ -311,22 +312,26 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
     const int kvh = h / G, hq = h % G;
     const int nch1 = a.n_chunks + 1;
     const int nq2 = 2 * a.n_q, CC = d / MC;
-    const int t = tid / MC, col = tid % MC;             // T * MC == 256
     const int c0 = h * d + cc * MC;
     extern __shared__ float sm[];
     float *w = sm;                      // [T][nch1] merge weights
-    float *os = sm + T * nch1;          // [T][MC]
+    float *os = sm + T * nch1;          // [T][MC] merged output slice
+    float *wp = os + T * MC;            // [4 waves][T][MC] per-wave partial sums
     float *zp = a.zp + (((size_t)b * a.n_q + h) * CC + cc) * T * nq2;
 
-    // ---- every load first, so the kernel waits on memory once: this thread's chunk
-    // partials (the first MB chunks), the (m, l) pairs of its wave's rows (rows wave and
-    // wave + 4, the first 64 chunks), and the conv-tap weights of its (t, q) pairs.
-    // Indices are clamped (in bounds); what is not used is discarded by selects.
-    const float *O = a.O + ((size_t)(b * a.n_kv + kvh) * nch1 * QR + hq * T + t) * d + cc * MC + col;
+    // ---- every load first, so the kernel waits on memory once.  Wave w sums chunks
+    // w, w + 4, ...: lane (t, c4) = (lane / 8, lane % 8) holds row t, columns 4 c4 ..
+    // 4 c4 + 3 of the slice (16-byte loads).  Also the (m, l) pairs of the wave's rows
+    // (rows wave and wave + 4, the first 64 chunks) and the conv-tap weights of the
+    // thread's (t, q) pairs.  Indices are clamped (in bounds); what is not used is
+    // discarded by selects.
+    const int lt = lane >> 3, c4 = lane & 7;
+    const float *O = a.O + ((size_t)(b * a.n_kv + kvh) * nch1 * QR + hq * T + lt) * d + cc * MC + 4 * c4;
     const size_t cstride = (size_t)QR * d;
-    float pv[MB];
+    float4 pv[MW];
 #pragma unroll
-    for (int u = 0; u < MB; u++) pv[u] = O[(size_t)min(u, nch1 - 1) * cstride];
+    for (int u = 0; u < MW; u++)
+        pv[u] = *reinterpret_cast<const float4 *>(O + (size_t)min(wave + 4 * u, nch1 - 1) * cstride);
     const float *ml = a.ml + ((size_t)(b * a.n_kv + kvh) * nch1) * QR * 2;
     float2 mlv[2];
 #pragma unroll
@@ -344,6 +349,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
         for (int k = 0; k < MC / 8; k++) wv[i][k] = *reinterpret_cast<const u32x4_t *>(wr + 8 * k);
     }
 
+    const int t = tid / MC, col = tid % MC;             // T * MC == 256
     if (!a.valid[b]) {
         a.o[((size_t)b * T + t) * qd + c0 + col] = 0.f;
         for (int e = tid; e < ne; e += 256) zp[e] = 0.f;
@@ -381,20 +387,29 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
         for (int c = lane; c < nch1; c += 64) w[tr * nch1 + c] *= invL;
     }
     __syncthreads();
-    // merged output of (t, col): the weighted chunk partials (unused chunks skipped)
-    const float *wt = w + t * nch1;
-    float ov = 0.f;
+    // this wave's chunks, weighted (unused chunks skipped)
+    const float *wt = w + lt * nch1;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto add = [&](int c, float4 v) {
+        if (c < nch1 && used(c)) {
+            const float wc = wt[c];
+            acc.x += wc * v.x; acc.y += wc * v.y; acc.z += wc * v.z; acc.w += wc * v.w;
+        }
+    };
 #pragma unroll
-    for (int u = 0; u < MB; u++)
-        if (u < nch1 && used(u)) ov += wt[u] * pv[u];
-    for (int cb = MB; cb < nch1; cb += 16) {
-        float pb[16];
+    for (int u = 0; u < MW; u++) add(wave + 4 * u, pv[u]);
+    for (int cb = wave + 4 * MW; cb < nch1; cb += 4 * 8) {     // long windows
+        float4 pb[8];
 #pragma unroll
-        for (int u = 0; u < 16; u++) pb[u] = O[(size_t)min(cb + u, nch1 - 1) * cstride];
+        for (int u = 0; u < 8; u++) pb[u] = *reinterpret_cast<const float4 *>(O + (size_t)min(cb + 4 * u, nch1 - 1) * cstride);
 #pragma unroll
-        for (int u = 0; u < 16; u++)
-            if (cb + u < nch1 && used(cb + u)) ov += wt[cb + u] * pb[u];
+        for (int u = 0; u < 8; u++) add(cb + 4 * u, pb[u]);
     }
+    *reinterpret_cast<float4 *>(&wp[(wave * T + lt) * MC + 4 * c4]) = acc;
+    __syncthreads();
+    // merged output of (t, col): the 4 waves' sums in wave order
+    const float ov = wp[(0 * T + t) * MC + col] + wp[(1 * T + t) * MC + col] + wp[(2 * T + t) * MC + col] +
+                     wp[(3 * T + t) * MC + col];
     os[t * MC + col] = ov;
     a.o[((size_t)b * T + t) * qd + c0 + col] = ov;
     __syncthreads();
@@ -405,17 +420,17 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
         if (e >= ne) break;
         const int tt = e / nq2;
         const float *ot = os + tt * MC;
-        float acc = 0.f;
+        float acc2 = 0.f;
 #pragma unroll
         for (int k = 0; k < MC / 8; k++) {
             const u32x4_t v = wv[i][k];
             const float *o8 = ot + 8 * k;
-            acc += bf16_to_f32(v.x & 0xFFFF) * o8[0] + bf16_to_f32(v.x >> 16) * o8[1];
-            acc += bf16_to_f32(v.y & 0xFFFF) * o8[2] + bf16_to_f32(v.y >> 16) * o8[3];
-            acc += bf16_to_f32(v.z & 0xFFFF) * o8[4] + bf16_to_f32(v.z >> 16) * o8[5];
-            acc += bf16_to_f32(v.w & 0xFFFF) * o8[6] + bf16_to_f32(v.w >> 16) * o8[7];
+            acc2 += bf16_to_f32(v.x & 0xFFFF) * o8[0] + bf16_to_f32(v.x >> 16) * o8[1];
+            acc2 += bf16_to_f32(v.y & 0xFFFF) * o8[2] + bf16_to_f32(v.y >> 16) * o8[3];
+            acc2 += bf16_to_f32(v.z & 0xFFFF) * o8[4] + bf16_to_f32(v.z >> 16) * o8[5];
+            acc2 += bf16_to_f32(v.w & 0xFFFF) * o8[6] + bf16_to_f32(v.w >> 16) * o8[7];
         }
-        zp[e] = acc;
+        zp[e] = acc2;
     }
 }
 
@@ -511,7 +526,7 @@ hipError_t launch_qk_norm_rope(const RopeArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st) {
-    const size_t lds = (size_t)(a.T * (a.n_chunks + 1) + a.T * MC) * 4;
+    const size_t lds = (size_t)(a.T * (a.n_chunks + 1) + a.T * MC + 4 * a.T * MC) * 4;
     hipLaunchKernelGGL(k_attn_merge, dim3(a.n_q, a.d / MC, a.B), dim3(256), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
