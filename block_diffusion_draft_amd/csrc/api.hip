@@ -390,8 +390,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
     }
 #undef GEMM
 
-    // S9 + S10: logits of the proposal rows with the shared output head,
-    // then log-softmax statistics and top-K
+    // S9 + S10: logits of the proposal rows with the shared output head
     float *logits = dbg_logits ? dbg_logits : x.at<float>(p.o_logits);
     {
         Bf16GemmArgs a = {};
@@ -407,11 +406,10 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
         else HIPCHK(launch_bf16_gemm_tiled(a, x.st));
         if (probe_lm) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_stop, x.st));
     }
-    HIPCHK(launch_topk(logits, p.R, p.V, p.K, p.P, valid, x.at<float>(p.o_topk), cand_ids, cand_logp,
-                       x.st));
-    // S11: selector path
-    HIPCHK(launch_viterbi(cand_ids, cand_logp, w->code_a, w->code_b, batch, p.P, p.K, p.r,
-                          cfg->pair_scale, valid, draft_tokens, x.st));
+    // S10 + S11: log-softmax statistics, top-K, and the selector path
+    HIPCHK(launch_topk_path(logits, batch, p.P, p.V, p.K, valid, x.at<float>(p.o_topk), w->code_a,
+                            w->code_b, p.r, cfg->pair_scale, cand_ids, cand_logp, draft_tokens,
+                            x.st));
     return DFLASH_OK;
 }
 

@@ -96,19 +96,18 @@ struct MergeConvArgs {
 };
 hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st);
 
-// ---------------------------------------------------------------- LM head / top-K
-// log-softmax statistics and top-K per row of fp32 logits [R][V] (ids by logit desc,
-// id asc; logp = logit - logsumexp); rows of invalid sequences get -1 / -inf.
-// ws: topk_workspace_floats(R, V) floats.
+// ---------------------------------------------------------------- LM head / top-K / path
+// Log-softmax statistics and top-K per row of fp32 logits [B P][V] (ids by logit desc,
+// id asc; logp = logit - logsumexp), then per sequence the Viterbi path through its P
+// rows of candidates (pair score pair_scale <A[u], B[v]>); invalid sequences get -1 /
+// -inf candidates and -1 tokens.  ws: topk_workspace_floats(B P, V) floats.  P, K <= 16.
 size_t topk_workspace_floats(int R, int V);
-hipError_t launch_topk(const float *logits, int R, int V, int K, int rows_per_seq,
-                       const int32_t *valid, float *ws, int32_t *cand_ids, float *cand_logp,
-                       hipStream_t st);
+hipError_t launch_topk_path(const float *logits, int B, int P, int V, int K, const int32_t *valid,
+                            float *ws, const uint16_t *code_a, const uint16_t *code_b, int r,
+                            float pair_scale, int32_t *cand_ids, float *cand_logp,
+                            int32_t *draft_tokens, hipStream_t st);
 
-// ---------------------------------------------------------------- selector / verify
-hipError_t launch_viterbi(const int32_t *cand_ids, const float *cand_logp, const uint16_t *code_a,
-                          const uint16_t *code_b, int B, int P, int K, int r, float pair_scale,
-                          const int32_t *valid, int32_t *draft_tokens, hipStream_t st);
+// ---------------------------------------------------------------- verify
 hipError_t launch_verify(const int32_t *draft, const int32_t *target, int B, int n,
                          int32_t *accept_len, int32_t *out_tokens, hipStream_t st);
 

@@ -19,7 +19,7 @@
 //    B operand holds the 6-bit sc_j or m_j (exact in bf16);
 //  * the super-block adds d (T - 128 sum_j sc_j S_rj) - dmin sum_j m_j S_rj.
 //
-// Work split: a workgroup (4 or 8 waves) owns one split of 4 super-blocks (1024 values
+// Work split: a workgroup (8 waves) owns one split of 4 super-blocks (1024 values
 // of K) and one run of tpw consecutive 16-column tiles per wave.  The split's
 // activation rows are staged once in LDS in MFMA lane order; their sub-block sums
 // come from MFMAs against a ones operand.  Each wave then streams its tiles'
@@ -244,9 +244,9 @@ Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int pair, int target_waves, i
     int tpw = (int)((wave_tiles + target_waves - 1) / target_waves);
     if (tpw < 1) tpw = 1;
     p.tpw = tpw;
-    // wpg 0: 8-wave workgroups when every wave has a single tile (one activation
-    // staging then feeds twice the tiles), else 4
-    p.wpg = wpg > 0 ? wpg : (tpw == 1 ? 8 : 4);
+    // wpg 0: 8-wave workgroups (one activation staging feeds 8 runs of tiles; measured
+    // 3-7% faster than 4 waves at every drafter shape)
+    p.wpg = wpg > 0 ? wpg : 8;
     wpg = p.wpg;
     p.grid_x = ceil_div(ceil_div(ntile, tpw), wpg);
     // the (hi, lo) halves of a pair sit pair / 4 lane groups = 4 pair lanes apart

@@ -1,4 +1,5 @@
-// Log-softmax statistics and top-K candidates of the shared output head, gfx950.
+// Log-softmax statistics, top-K candidates of the shared output head and the
+// candidate-path selector, gfx950.
 //
 // FastFlowLM card "Qwen3.8-27B-DFlash2-NPU2": the draft shares the target's output
 // head (spec table "Draft" row) and keeps the top 16 candidates per proposal
@@ -18,6 +19,15 @@
 //     its chunks instead.
 // Every choice is an arg-max under a total order, so the result is exact and does
 // not depend on thread scheduling.
+//
+// Pass 4 runs inside the selector's workgroup (one per sequence): its waves select the
+// sequence's rows, then the candidate-path search runs on them.  Selector (same card,
+// spec table "Draft" row: candidate selector, top 16, rank 256; "Weights" row: two
+// 248320 x 256 codebooks; "How it is used": one coherent path through the top 16
+// candidates per position): the path objective used here is the sum over positions of
+// the candidates' log-probabilities plus s <A[u], B[v]> for every pair of adjacent
+// chosen candidates u (earlier) and v (later), maximised by Viterbi; ties go to the
+// lowest candidate index.
 #include "common.h"
 #include "kernels.h"
 
@@ -168,21 +178,12 @@ __global__ __launch_bounds__(256) void k_collect(const float *logits, int V, int
     }
 }
 
-// 4. wave per row: exact top-K of the candidates (or of the whole row on overflow)
-__global__ __launch_bounds__(64) void k_select(const float *logits, int V, int nch, int K,
-                                               const int *count, const float *cv, const int32_t *ci,
-                                               const float *lse, int rows_per_seq,
-                                               const int32_t *valid, int32_t *cand_ids,
-                                               float *cand_logp) {
-    const int r = blockIdx.x, lane = threadIdx.x;
-    const bool ok = valid[r / rows_per_seq] != 0;
-    if (!ok) {
-        if (lane < K) {
-            cand_ids[(size_t)r * K + lane] = -1;
-            cand_logp[(size_t)r * K + lane] = -INFINITY;
-        }
-        return;
-    }
+// 4. one wave, row r: exact top-K of the candidates (or of the whole row on overflow)
+// into sid[k], slp[k] (k < K; LDS of the calling workgroup)
+__device__ void select_row(const float *logits, int V, int nch, int K, int r, const int *count,
+                           const float *cv, const int32_t *ci, const float *lse, int *sid,
+                           float *slp) {
+    const int lane = threadIdx.x & 63;
     const float L = lse[r];
     const int n = count[r];
     if (n <= 64) {
@@ -193,8 +194,8 @@ __global__ __launch_bounds__(64) void k_select(const float *logits, int V, int n
         const unsigned long long sk = wave_sort_desc(key);
         if (lane < K) {
             const bool have = lane < n;
-            cand_ids[(size_t)r * K + lane] = have ? key_id(sk) : -1;
-            cand_logp[(size_t)r * K + lane] = have ? key_value(sk) - L : -INFINITY;
+            sid[lane] = have ? key_id(sk) : -1;
+            slp[lane] = have ? key_value(sk) - L : -INFINITY;
         }
         return;
     }
@@ -218,8 +219,8 @@ __global__ __launch_bounds__(64) void k_select(const float *logits, int V, int n
             for (int k = 0; k < CPL; k++)
                 if (id[k] == bi) id[k] = -1;
             if (lane == 0) {
-                cand_ids[(size_t)r * K + round] = bi;
-                cand_logp[(size_t)r * K + round] = bi >= 0 ? bv - L : -INFINITY;
+                sid[round] = bi;
+                slp[round] = bi >= 0 ? bv - L : -INFINITY;
             }
         }
         return;
@@ -256,8 +257,114 @@ __global__ __launch_bounds__(64) void k_select(const float *logits, int V, int n
         li = ni;
     }
     if (lane < K) {
-        cand_ids[(size_t)r * K + lane] = li;
-        cand_logp[(size_t)r * K + lane] = li >= 0 ? lv - L : -INFINITY;
+        sid[lane] = li;
+        slp[lane] = li >= 0 ? lv - L : -INFINITY;
+    }
+}
+
+
+constexpr int MAXK = 16;
+constexpr int MAXP = 16;
+constexpr int PATH_WAVES = 8;
+
+// One workgroup (8 waves) per sequence.  Waves select the sequence's P rows (pass 4)
+// into LDS and the outputs.  The pair scores of adjacent positions are K x K products of
+// gathered codebook rows, T_t = s A[ids_t] B[ids_{t+1}]^T, computed as 16x16xr MFMA
+// tiles (exact bf16 products, fp32 accumulation) straight from the gathered rows: lane
+// (i, k-group) loads its 16-byte fragments of A[ids_t[i]] and B[ids_{t+1}[i]] for
+// every k-step, all loads in flight at once.  Wave w handles positions t = w, w + 8,
+// ...; the dynamic programme then runs on K lanes.
+__global__ __launch_bounds__(64 * PATH_WAVES) void k_select_path(
+    const float *logits, int V, int nch, int K, const int *count, const float *cv,
+    const int32_t *ci, const float *lse, int P, const int32_t *valid, const uint16_t *code_a,
+    const uint16_t *code_b, int r, float s, int32_t *cand_ids, float *cand_logp, int32_t *draft) {
+    __shared__ int ids[MAXP][MAXK];
+    __shared__ float lp[MAXP][MAXK];
+    __shared__ float Tm[MAXP][MAXK][MAXK];
+    __shared__ float delta[2][MAXK];
+    __shared__ int psi[MAXP][MAXK];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool ok = valid[b] != 0;
+    for (int t = wave; t < P; t += PATH_WAVES) {
+        const int row = b * P + t;
+        if (ok) select_row(logits, V, nch, K, row, count, cv, ci, lse, ids[t], lp[t]);
+        if (lane < MAXK && (lane >= K || !ok)) {
+            ids[t][lane] = -1;
+            lp[t][lane] = -INFINITY;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (lane < K) {
+            cand_ids[(size_t)row * K + lane] = ids[t][lane];
+            cand_logp[(size_t)row * K + lane] = lp[t][lane];
+        }
+    }
+    __syncthreads();
+    if (!ok) {
+        if (tid < P) draft[(size_t)b * P + tid] = -1;
+        return;
+    }
+    const int c = lane & 15, g = lane >> 4;
+    const int nks = r / 32;
+    for (int t = wave; t + 1 < P; t += PATH_WAVES) {
+        const int ua = ids[t][c], vb = ids[t + 1][c];
+        const uint16_t *ar = code_a + (size_t)(ua >= 0 ? ua : 0) * r + 8 * g;
+        const uint16_t *br = code_b + (size_t)(vb >= 0 ? vb : 0) * r + 8 * g;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        // 8 k-steps of fragments in flight, then their MFMAs (indices past the rank are
+        // clamped: in bounds, and their products skipped)
+        for (int ks0 = 0; ks0 < nks; ks0 += 8) {
+            u32x4_t av[8], bv[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int ks = min(ks0 + u, nks - 1);
+                av[u] = *reinterpret_cast<const u32x4_t *>(ar + ks * 32);
+                bv[u] = *reinterpret_cast<const u32x4_t *>(br + ks * 32);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                if (ks0 + u < nks) {
+                    const u32x4_t a0 = ua < 0 ? (u32x4_t){0, 0, 0, 0} : av[u];
+                    const u32x4_t b0 = vb < 0 ? (u32x4_t){0, 0, 0, 0} : bv[u];
+                    acc = mfma16x16x32(a0, b0, acc);
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; v++) Tm[t][4 * g + v][c] = s * acc[v];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // delta over candidates j < K on lanes 0..K-1; ties to the lowest index
+        const int j = lane;
+        float dcur = j < K ? lp[0][j] : -INFINITY;
+        for (int t = 0; t + 1 < P; t++) {
+            if (j < K) delta[t & 1][j] = dcur;
+            __builtin_amdgcn_wave_barrier();
+            float best = -INFINITY;
+            int bi = 0;
+            if (j < K) {
+                best = delta[t & 1][0] + Tm[t][0][j];
+                for (int i = 1; i < K; i++) {
+                    const float v = delta[t & 1][i] + Tm[t][i][j];
+                    if (v > best) { best = v; bi = i; }
+                }
+                psi[t + 1][j] = bi;
+                dcur = lp[t + 1][j] + best;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        if (j < K) delta[(P - 1) & 1][j] = dcur;
+        __builtin_amdgcn_wave_barrier();
+        if (lane == 0) {
+            const int fin = (P - 1) & 1;
+            int jj = 0;
+            for (int i = 1; i < K; i++)
+                if (delta[fin][i] > delta[fin][jj]) jj = i;
+            for (int t = P - 1; t >= 0; t--) {
+                draft[(size_t)b * P + t] = ids[t][jj];
+                if (t > 0) jj = psi[t][jj];
+            }
+        }
     }
 }
 
@@ -268,9 +375,12 @@ size_t topk_workspace_floats(int R, int V) {
     return (size_t)R * (2 * nch + 3 + 2 * CAP);
 }
 
-hipError_t launch_topk(const float *logits, int R, int V, int K, int rows_per_seq,
-                       const int32_t *valid, float *ws, int32_t *cand_ids, float *cand_logp,
-                       hipStream_t st) {
+hipError_t launch_topk_path(const float *logits, int B, int P, int V, int K, const int32_t *valid,
+                            float *ws, const uint16_t *code_a, const uint16_t *code_b, int r,
+                            float pair_scale, int32_t *cand_ids, float *cand_logp,
+                            int32_t *draft_tokens, hipStream_t st) {
+    if (P > MAXP || K > MAXK) return hipErrorInvalidValue;
+    const int R = B * P;
     const int nch = ceil_div(V, CHUNK);
     float *pm = ws, *ps = pm + (size_t)R * nch, *thr = ps + (size_t)R * nch, *lse = thr + R;
     int *count = reinterpret_cast<int *>(lse + R);
@@ -280,8 +390,9 @@ hipError_t launch_topk(const float *logits, int R, int V, int K, int rows_per_se
     hipLaunchKernelGGL(k_chunk_stats, grid, dim3(256), 0, st, logits, V, nch, pm, ps);
     hipLaunchKernelGGL(k_row_threshold, dim3(R), dim3(64), 0, st, pm, ps, nch, K, thr, lse, count);
     hipLaunchKernelGGL(k_collect, grid, dim3(256), 0, st, logits, V, nch, thr, count, cv, ci);
-    hipLaunchKernelGGL(k_select, dim3(R), dim3(64), 0, st, logits, V, nch, K, count, cv, ci, lse,
-                       rows_per_seq, valid, cand_ids, cand_logp);
+    hipLaunchKernelGGL(k_select_path, dim3(B), dim3(64 * PATH_WAVES), 0, st, logits, V, nch, K, count,
+                       cv, ci, lse, P, valid, code_a, code_b, r, pair_scale, cand_ids, cand_logp,
+                       draft_tokens);
     return hipGetLastError();
 }
 
