@@ -293,21 +293,22 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
         if (splits < 0) return splits;                     \
     } while (0)
 
-    // S0: block assembly h, per-sequence validity, first layer's input bf16(h * g_in)
-    // (RMSNorms are deferred: the GEMM consumer scales each output row by 1 / rms)
-    HIPCHK(launch_embed(w->embed, w->mask_emb, last_token, ctx_len, batch, p.T, H, p.V, t_new,
-                        cache_cap, h, w->layer[0].in_norm, xc, ssq_x, valid, x.st));
-    if (dbg_hidden)
-        HIPCHK(hipMemcpyAsync(dbg_hidden, h, (size_t)p.M_blk * H * 4, hipMemcpyDeviceToDevice, x.st));
-
-    // S1: fused taps c = RMSNorm(X . W_fc^T), the context rows of the K/V projection input
+    // S1: fused taps c = RMSNorm(X . W_fc^T), the context rows of the K/V projection input;
+    // its reduction shares one launch with S0 (independent of it): block assembly h,
+    // per-sequence validity, first layer's input bf16(h * g_in).  RMSNorms are deferred:
+    // the GEMM consumer scales each output row by 1 / rms.
     {
         const void *ws[1] = {w->fc};
         const int sn[1] = {H};
         GEMM(ws, sn, 1, taps, cfg->n_taps * H, p.M_ctx, cfg->n_taps * H, 0);
-        HIPCHK(launch_reduce_norm(part, splits, p.M_ctx, H, 0, 0, fcout, ssq_c, w->hidden_norm,
-                                  xc + (size_t)p.M_blk * H, nullptr, H, 0, x.st));
+        const ReduceRowsArgs ra = {part, splits, p.M_ctx, H, 0, 0, fcout, ssq_c, w->hidden_norm,
+                                   xc + (size_t)p.M_blk * H, nullptr, H, 0};
+        const EmbedArgs ea = {w->embed, w->mask_emb, last_token, ctx_len, p.T, H, p.V, t_new,
+                              cache_cap, h, w->layer[0].in_norm, xc, ssq_x, valid};
+        HIPCHK(launch_reduce_norm_embed(ra, ea, batch, x.st));
     }
+    if (dbg_hidden)
+        HIPCHK(hipMemcpyAsync(dbg_hidden, h, (size_t)p.M_blk * H * 4, hipMemcpyDeviceToDevice, x.st));
 
     for (int l = 0; l < L; l++) {
         const dflash_layer_weights &lw = w->layer[l];

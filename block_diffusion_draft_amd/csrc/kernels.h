@@ -53,10 +53,17 @@ hipError_t launch_swiglu(const float *part, int splits, int M, int N, int pair, 
 // per-sequence validity flags + block assembly h[b][0] = E[last], h[b][1..] = mask, and
 // the first layer's input x = bf16(h * gain), [B*T][H], with its row sums of squares
 // in ssq[row][0] (ssq[row][1 .. H/256) = 0)
-hipError_t launch_embed(const uint16_t *embed, const uint16_t *mask_emb, const int32_t *last,
-                        const int32_t *ctx_len, int B, int T, int H, int V, int t_new, int cap,
-                        float *h, const uint16_t *gain, uint16_t *x, float *ssq, int32_t *valid,
-                        hipStream_t st);
+struct EmbedArgs {
+    const uint16_t *embed, *mask;
+    const int32_t *last, *ctx_len;
+    int T, H, V, t_new, cap;
+    float *h;
+    const uint16_t *gain;
+    uint16_t *x;
+    float *ssq;
+    int32_t *valid;
+};
+hipError_t launch_embed(const EmbedArgs &a, int B, hipStream_t st);
 
 struct RopeArgs {
     const float *qkv;            // fp32 partials [splits][B*(T + t_new)][qd + 2 kd]: block rows
@@ -155,6 +162,18 @@ hipError_t launch_q4k_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipS
 // output row map(r): map 0 -> r; map 1 -> the proposal rows of each block of 8 (row
 // r % 8 == 0 skipped, others to (r / 8) * 7 + r % 8 - 1).  The consumer applies the
 // row's 1 / rms (RowScale).
+struct ReduceRowsArgs {
+    const float *part;
+    int splits, M_out, N, pair, add;
+    float *f, *ssq;
+    const uint16_t *gain;
+    uint16_t *out, *out_lo;
+    int ldo, map;
+};
+hipError_t launch_reduce_norm(const ReduceRowsArgs &a, hipStream_t st);
 hipError_t launch_reduce_norm(const float *part, int splits, int M_out, int N, int pair, int add,
                               float *f, float *ssq, const uint16_t *gain, uint16_t *out,
                               uint16_t *out_lo, int ldo, int map, hipStream_t st);
+// the reduction and the block assembly (independent) as one launch
+hipError_t launch_reduce_norm_embed(const ReduceRowsArgs &a, const EmbedArgs &e, int B,
+                                    hipStream_t st);

@@ -27,13 +27,15 @@ __device__ __forceinline__ float block_sum_256(float v, float *scratch) {
 // runs of 8 values, loaded together (H <= 256 * 8 * EMB_V).
 constexpr int EMB_V = 4;
 
-__global__ __launch_bounds__(256) void k_embed(const uint16_t *embed, const uint16_t *mask,
-                                               const int32_t *last, const int32_t *ctx_len,
-                                               int T, int H, int V, int t_new, int cap,
-                                               float *h, const uint16_t *gain, uint16_t *x,
-                                               float *ssq, int32_t *valid) {
+__device__ void embed_row(const EmbedArgs &a, int row) {
+    const uint16_t *embed = a.embed, *mask = a.mask, *gain = a.gain;
+    const int32_t *last = a.last, *ctx_len = a.ctx_len;
+    const int T = a.T, H = a.H, V = a.V, t_new = a.t_new, cap = a.cap;
+    float *h = a.h, *ssq = a.ssq;
+    uint16_t *x = a.x;
+    int32_t *valid = a.valid;
     __shared__ float scratch[4];
-    const int b = blockIdx.x / T, t = blockIdx.x % T, tid = threadIdx.x;
+    const int b = row / T, t = row % T, tid = threadIdx.x;
     const int n = ctx_len[b], tok = last[b];
     const bool ok = n >= 0 && n <= cap - t_new && tok >= 0 && tok < V;
     if (t == 0 && tid == 0) valid[b] = ok ? 1 : 0;
@@ -62,15 +64,15 @@ __global__ __launch_bounds__(256) void k_embed(const uint16_t *embed, const uint
     }
     s = block_sum_256(s, scratch);
     const int nchunk = H / 256;
-    if (tid < nchunk) ssq[(size_t)blockIdx.x * nchunk + tid] = tid == 0 ? s : 0.f;
-    float *row = h + (size_t)blockIdx.x * H;
-    uint16_t *xr = x + (size_t)blockIdx.x * H;
+    if (tid < nchunk) ssq[(size_t)row * nchunk + tid] = tid == 0 ? s : 0.f;
+    float *hr = h + (size_t)row * H;
+    uint16_t *xr = x + (size_t)row * H;
 #pragma unroll
     for (int u = 0; u < EMB_V; u++) {
         const int v = tid + 256 * u;
         if (v < nv) {
             const uint32_t g4[4] = {gw[u].x, gw[u].y, gw[u].z, gw[u].w};
-            float4 *hp = reinterpret_cast<float4 *>(row + 8 * v);
+            float4 *hp = reinterpret_cast<float4 *>(hr + 8 * v);
             hp[0] = make_float4(val[u][0], val[u][1], val[u][2], val[u][3]);
             hp[1] = make_float4(val[u][4], val[u][5], val[u][6], val[u][7]);
             uint32_t o[4];
@@ -91,14 +93,17 @@ __global__ __launch_bounds__(256) void k_embed(const uint16_t *embed, const uint
 // v^2 goes to ssq[r][blockIdx.x], and with out the next GEMM's input bf16(v * gain)
 // (+ its bf16 residual in out_lo) goes to output row map(r).  The RMSNorm's 1 / rms is
 // applied by the consumer of that GEMM (RowScale).
-__global__ __launch_bounds__(256) void k_reduce_rows(const float *part, int splits, int M_out, int N,
-                                                     int pair, int add, float *f, float *ssq,
-                                                     const uint16_t *gain, uint16_t *out,
-                                                     uint16_t *out_lo, int ldo, int map) {
+__device__ void reduce_rows_block(const ReduceRowsArgs &a, int cx, int r) {
+    const float *part = a.part;
+    const int splits = a.splits, M_out = a.M_out, N = a.N, pair = a.pair, add = a.add;
+    const int ldo = a.ldo, map = a.map;
+    float *f = a.f, *ssq = a.ssq;
+    const uint16_t *gain = a.gain;
+    uint16_t *out = a.out, *out_lo = a.out_lo;
     __shared__ float4 red[4][64];
     __shared__ float scratch[4];
-    const int r = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c0 = blockIdx.x * 256;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c0 = cx * 256;
     const size_t stride = (size_t)(pair ? 2 * M_out : M_out) * N;
     const float *p = part + (size_t)r * N + c0 + 4 * lane;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -130,13 +135,28 @@ __global__ __launch_bounds__(256) void k_reduce_rows(const float *part, int spli
     if (add) v += *fp;
     *fp = v;
     const float sq = block_sum_256(v * v, scratch);
-    if (tid == 0) ssq[(size_t)r * gridDim.x + blockIdx.x] = sq;
+    if (tid == 0) ssq[(size_t)r * (N / 256) + cx] = sq;
     if (!out || (map == 1 && r % 8 == 0)) return;
     const int orow = map == 1 ? (r / 8) * 7 + r % 8 - 1 : r;
     const float x = v * bf16_to_f32(gain[c0 + c]);
     const uint16_t hb = f32_to_bf16(x);
     out[(size_t)orow * ldo + c0 + c] = hb;
     if (out_lo) out_lo[(size_t)orow * ldo + c0 + c] = f32_to_bf16(x - bf16_to_f32(hb));
+}
+
+__global__ __launch_bounds__(256) void k_embed(EmbedArgs a) { embed_row(a, blockIdx.x); }
+
+__global__ __launch_bounds__(256) void k_reduce_rows(ReduceRowsArgs a) {
+    reduce_rows_block(a, blockIdx.x, blockIdx.y);
+}
+
+// one launch for two independent jobs: the reduction's (N / 256) x M_out workgroups,
+// then the block assembly's B T workgroups
+__global__ __launch_bounds__(256) void k_reduce_rows_embed(ReduceRowsArgs a, EmbedArgs e) {
+    const int nc = a.N / 256, nred = nc * a.M_out;
+    const int bid = blockIdx.x;
+    if (bid < nred) reduce_rows_block(a, bid % nc, bid / nc);
+    else embed_row(e, bid - nred);
 }
 
 // ---------------------------------------------------------------- split-K reduction
@@ -491,12 +511,8 @@ __global__ __launch_bounds__(256) void k_conv_apply(MergeConvArgs a) {
 
 }  // namespace
 
-hipError_t launch_embed(const uint16_t *embed, const uint16_t *mask_emb, const int32_t *last,
-                        const int32_t *ctx_len, int B, int T, int H, int V, int t_new, int cap,
-                        float *h, const uint16_t *gain, uint16_t *x, float *ssq, int32_t *valid,
-                        hipStream_t st) {
-    hipLaunchKernelGGL(k_embed, dim3(B * T), dim3(256), 0, st, embed, mask_emb, last, ctx_len, T, H,
-                       V, t_new, cap, h, gain, x, ssq, valid);
+hipError_t launch_embed(const EmbedArgs &a, int B, hipStream_t st) {
+    hipLaunchKernelGGL(k_embed, dim3(B * a.T), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -534,10 +550,21 @@ hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+hipError_t launch_reduce_norm(const ReduceRowsArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(k_reduce_rows, dim3(a.N / 256, a.M_out), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_reduce_norm(const float *part, int splits, int M_out, int N, int pair, int add,
                               float *f, float *ssq, const uint16_t *gain, uint16_t *out,
                               uint16_t *out_lo, int ldo, int map, hipStream_t st) {
-    hipLaunchKernelGGL(k_reduce_rows, dim3(N / 256, M_out), dim3(256), 0, st, part, splits, M_out, N,
-                       pair, add, f, ssq, gain, out, out_lo, ldo, map);
+    const ReduceRowsArgs a = {part, splits, M_out, N, pair, add, f, ssq, gain, out, out_lo, ldo, map};
+    return launch_reduce_norm(a, st);
+}
+
+hipError_t launch_reduce_norm_embed(const ReduceRowsArgs &a, const EmbedArgs &e, int B,
+                                    hipStream_t st) {
+    const int grid = (a.N / 256) * a.M_out + B * e.T;
+    hipLaunchKernelGGL(k_reduce_rows_embed, dim3(grid), dim3(256), 0, st, a, e);
     return hipGetLastError();
 }
