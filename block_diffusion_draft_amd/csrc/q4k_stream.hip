@@ -109,17 +109,12 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw
     auto stage = [&](const unsigned char *tb, int sb) -> SStage {
         return s_load(tb + sb * Q4K_UNIT_BYTES, cl, lane);
     };
-    SStage st[4];
-    {
-        const unsigned char *b0 = tile_base(t0);
-        st[0] = stage(b0, 0);
-        st[1] = stage(b0, 1);
-        st[2] = stage(b0, 2);
-    }
-
     // ---- activations of this split -> LDS in lane order: entry (sbi, j, lane) holds
     // row cl's values k = (sb0 + sbi) 256 + 32 j + 8 g .. + 7 (rows >= M: zeros)
+    // (loaded before the first weight stages: the wait for them then does not include
+    // the weights' HBM latency, which overlaps the staging instead)
     constexpr int PER = SNSB * 8 / WPG;             // entries per thread
+    SStage st[4];
     {
         const int Rc = min(cl, a.M - 1);
         const uint16_t *arow = a.src.A + (size_t)Rc * a.src.lda + (size_t)sb0 * 256 + 8 * g;
@@ -127,11 +122,17 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw
 #pragma unroll
         for (int i = 0; i < PER; i++) {
             const int e = wave + WPG * i;           // (sbi, j) = (e >> 3, e & 7)
-            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(arow + (e >> 3) * 256 + 32 * (e & 7));
-            av[i] = cl < a.M ? v : (u32x4_t){0u, 0u, 0u, 0u};
+            av[i] = *reinterpret_cast<const u32x4_t *>(arow + (e >> 3) * 256 + 32 * (e & 7));
         }
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned char *b0 = tile_base(t0);
+        st[0] = stage(b0, 0);
+        st[1] = stage(b0, 1);
+        st[2] = stage(b0, 2);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < PER; i++) A_lds[(wave + WPG * i) * 64 + lane] = av[i];
+        for (int i = 0; i < PER; i++)
+            A_lds[(wave + WPG * i) * 64 + lane] = cl < a.M ? av[i] : (u32x4_t){0u, 0u, 0u, 0u};
     }
     __syncthreads();
     // sub-block sums S[sbi][j][r]: MFMA of the entry with a ones operand (every
