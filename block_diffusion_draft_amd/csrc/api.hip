@@ -115,7 +115,7 @@ int check_config(const dflash_config *c) {
         return DFLASH_ESHAPE;
     const int qd = c->n_q_heads * c->head_dim;
     if (qd % 256 || qd > 8192) return DFLASH_ESHAPE;
-    if (c->block != DFLASH_BLOCK) return DFLASH_ESHAPE;
+    if (c->block < 2 || c->block > DFLASH_BLOCK) return DFLASH_ESHAPE;
     if (c->n_taps < 1 || c->n_taps > 16) return DFLASH_ESHAPE;
     if (c->top_k < 1 || c->top_k > DFLASH_MAX_TOPK) return DFLASH_ESHAPE;
     if (c->vocab < c->top_k || c->vocab % 16) return DFLASH_ESHAPE;
@@ -383,7 +383,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
             GEMM(ws, sn, 1, mid2, p.F, 2 * p.M_blk, p.F, p.M_blk);
             const uint16_t *gain = last ? w->final_norm : w->layer[l + 1].in_norm;
             HIPCHK(launch_reduce_norm(part, splits, p.M_blk, H, pair_left, 1, h, ssq_x, gain,
-                                      last ? f : xc, nullptr, H, last ? 1 : 0, x.st));
+                                      last ? f : xc, nullptr, H, last ? p.T : 0, x.st));
         }
         if (dbg_hidden)
             HIPCHK(hipMemcpyAsync(dbg_hidden + (size_t)(l + 1) * p.M_blk * H, h,
@@ -400,7 +400,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
         a.nseg = 1;
         a.M = p.R; a.N = p.V; a.K = H; a.C = logits; a.ldc = p.V;
         a.A = f; a.lda = H;
-        a.rs = rowscale(ssq_x, 1);             // the final norm of the proposal rows
+        a.rs = rowscale(ssq_x, p.T);           // the final norm of the proposal rows
         const bool probe_lm = probe && probe->kernel == DFLASH_PROBE_LM_HEAD;
         if (probe_lm) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_start, x.st));
         if (p.lm_skinny) HIPCHK(launch_bf16_gemm_skinny(a, x.st));

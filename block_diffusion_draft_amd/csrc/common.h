@@ -62,13 +62,14 @@ __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b -
 struct RowScale {
     const float *ssq;          // [rows][nchunk]; null: scale 1
     int nchunk;
-    int map;                   // 0: row r; 1: proposal row r of blocks of 8 -> row (r/7)*8 + r%7 + 1
+    int map;                   // 0: row r; T > 1: proposal row r of blocks of T (T - 1 proposals
+                               // each) -> block row (r / (T - 1)) T + r % (T - 1) + 1
     float n, eps;
 };
 
 __device__ __forceinline__ float row_inv(const RowScale &s, int r) {
     if (!s.ssq) return 1.f;
-    const int br = s.map ? (r / 7) * 8 + r % 7 + 1 : r;
+    const int br = s.map ? (r / (s.map - 1)) * s.map + r % (s.map - 1) + 1 : r;
     const float *p = s.ssq + (size_t)br * s.nchunk;
     float ss = 0.f;
     for (int i0 = 0; i0 < s.nchunk; i0 += 8) {          // 8 loads in flight, summed in order

@@ -243,7 +243,7 @@ __global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a, int tiles_p
     const RowScale &rs = a.rs;
     float ssl = 0.f;
     if (rs.ssq && lane < 8 && lane < a.M) {
-        const int br = rs.map ? (lane / 7) * 8 + lane % 7 + 1 : lane;
+        const int br = rs.map ? (lane / (rs.map - 1)) * rs.map + lane % (rs.map - 1) + 1 : lane;
         const float *sp = rs.ssq + (size_t)br * rs.nchunk;
         for (int i0 = 0; i0 < rs.nchunk; i0 += 8) {
             float pv[8];

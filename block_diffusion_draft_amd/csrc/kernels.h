@@ -159,9 +159,9 @@ hipError_t launch_q4k_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipS
 // Output rows r < M_out: v = sum over splits of partial rows r (+ r + pair), N a multiple
 // of 256; add ? f[r] += v : f[r] = v (fp32), with per-256-column sums of squares in
 // ssq [M_out][N/256].  Then, if out: bf16(v * gain) (and its residual in out_lo) at
-// output row map(r): map 0 -> r; map 1 -> the proposal rows of each block of 8 (row
-// r % 8 == 0 skipped, others to (r / 8) * 7 + r % 8 - 1).  The consumer applies the
-// row's 1 / rms (RowScale).
+// output row map(r): map 0 -> r; map T > 1 -> the proposal rows of each block of T
+// (row r % T == 0 skipped, others to (r / T) (T - 1) + r % T - 1).  The consumer
+// applies the row's 1 / rms (RowScale).
 struct ReduceRowsArgs {
     const float *part;
     int splits, M_out, N, pair, add;

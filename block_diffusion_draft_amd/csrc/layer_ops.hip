@@ -136,8 +136,8 @@ __device__ void reduce_rows_block(const ReduceRowsArgs &a, int cx, int r) {
     *fp = v;
     const float sq = block_sum_256(v * v, scratch);
     if (tid == 0) ssq[(size_t)r * (N / 256) + cx] = sq;
-    if (!out || (map == 1 && r % 8 == 0)) return;
-    const int orow = map == 1 ? (r / 8) * 7 + r % 8 - 1 : r;
+    if (!out || (map > 0 && r % map == 0)) return;
+    const int orow = map > 0 ? (r / map) * (map - 1) + r % map - 1 : r;
     const float x = v * bf16_to_f32(gain[c0 + c]);
     const uint16_t hb = f32_to_bf16(x);
     out[(size_t)orow * ldo + c0 + c] = hb;
@@ -345,8 +345,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
     // (rows wave and wave + 4, the first 64 chunks) and the conv-tap weights of the
     // thread's (t, q) pairs.  Indices are clamped (in bounds); what is not used is
     // discarded by selects.
-    const int lt = lane >> 3, c4 = lane & 7;
-    const float *O = a.O + ((size_t)(b * a.n_kv + kvh) * nch1 * QR + hq * T + lt) * d + cc * MC + 4 * c4;
+    const int lt = lane >> 3, c4 = lane & 7;            // rows lt >= T (blocks under 8) idle
+    const float *O = a.O + ((size_t)(b * a.n_kv + kvh) * nch1 * QR + hq * T + min(lt, T - 1)) * d +
+                     cc * MC + 4 * c4;
     const size_t cstride = (size_t)QR * d;
     float4 pv[MW];
 #pragma unroll
@@ -369,9 +370,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
         for (int k = 0; k < MC / 8; k++) wv[i][k] = *reinterpret_cast<const u32x4_t *>(wr + 8 * k);
     }
 
-    const int t = tid / MC, col = tid % MC;             // T * MC == 256
+    const int t = tid / MC, col = tid % MC;             // 8 * MC == 256; rows t >= T idle
     if (!a.valid[b]) {
-        a.o[((size_t)b * T + t) * qd + c0 + col] = 0.f;
+        if (t < T) a.o[((size_t)b * T + t) * qd + c0 + col] = 0.f;
         for (int e = tid; e < ne; e += 256) zp[e] = 0.f;
         return;
     }
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
     }
     __syncthreads();
     // this wave's chunks, weighted (unused chunks skipped)
-    const float *wt = w + lt * nch1;
+    const float *wt = w + min(lt, T - 1) * nch1;
     float4 acc = {0.f, 0.f, 0.f, 0.f};
     auto add = [&](int c, float4 v) {
         if (c < nch1 && used(c)) {
@@ -425,13 +426,15 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
 #pragma unroll
         for (int u = 0; u < 8; u++) add(cb + 4 * u, pb[u]);
     }
-    *reinterpret_cast<float4 *>(&wp[(wave * T + lt) * MC + 4 * c4]) = acc;
+    if (lt < T) *reinterpret_cast<float4 *>(&wp[(wave * T + lt) * MC + 4 * c4]) = acc;
     __syncthreads();
     // merged output of (t, col): the 4 waves' sums in wave order
-    const float ov = wp[(0 * T + t) * MC + col] + wp[(1 * T + t) * MC + col] + wp[(2 * T + t) * MC + col] +
-                     wp[(3 * T + t) * MC + col];
-    os[t * MC + col] = ov;
-    a.o[((size_t)b * T + t) * qd + c0 + col] = ov;
+    if (t < T) {
+        const float ov = wp[(0 * T + t) * MC + col] + wp[(1 * T + t) * MC + col] +
+                         wp[(2 * T + t) * MC + col] + wp[(3 * T + t) * MC + col];
+        os[t * MC + col] = ov;
+        a.o[((size_t)b * T + t) * qd + c0 + col] = ov;
+    }
     __syncthreads();
     // conv-tap partials of this slice: (t, q) pairs over the threads
 #pragma unroll

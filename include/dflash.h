@@ -48,7 +48,8 @@ extern "C" {
 #endif
 
 #define DFLASH_MAX_LAYERS 8
-#define DFLASH_BLOCK 8          /* block of 8 = 1 anchor + 7 proposals */
+#define DFLASH_BLOCK 8          /* the drafter's block: 1 anchor + 7 proposals; also the
+                                   largest block and t_new the kernels take */
 #define DFLASH_MAX_TOPK 16
 
 typedef enum {
@@ -67,9 +68,10 @@ typedef enum { DFLASH_W_Q4K = 0, DFLASH_W_BF16 = 1 } dflash_weight_fmt;
  * 256 (FastFlowLM card spec table "Draft" row; aiqre page "Specification").
  * Supported by the kernels: hidden, ffn and n_q*head_dim multiples of 256; hidden
  * and n_q*head_dim at most 8192; head_dim 64 or 128; n_q even, at most 64 and a
- * multiple of n_kv with n_q / n_kv <= 4; block == 8; 1 <= top_k <= 16; sel_rank a
- * multiple of 32 up to 4096; vocab >= top_k, a multiple of 16, at most 1,048,576;
- * window at most 65536. */
+ * multiple of n_kv with n_q / n_kv <= 4; 2 <= block <= 8 (P = block - 1 proposals;
+ * the JetBrains card "Qwen3.8-3.6-27B-blend DFlash2", "Quick start", runs a quantized
+ * drafter with block size 5); 1 <= top_k <= 16; sel_rank a multiple of 32 up to 4096;
+ * vocab >= top_k, a multiple of 16, at most 1,048,576; window at most 65536. */
 typedef struct {
     int n_layers, hidden, ffn, n_q_heads, n_kv_heads, head_dim, window, vocab;
     int n_taps, block, top_k, sel_rank, weight_fmt;
@@ -127,12 +129,12 @@ size_t dflash_workspace_bytes(const dflash_config *cfg, int batch, int t_new);
  *               rotary embedding at positions n..n+t_new-1; values as projected);
  *               rows [max(0, n+t_new-window), n) are read.  Block position t
  *               sits at rotary position n+t_new+t.
- *  draft_tokens int32 [batch][7]: the chosen path.
- *  cand_ids     int32 [batch][7][top_k], cand_logp fp32 [batch][7][top_k]:
+ *  draft_tokens int32 [batch][P]: the chosen path, P = block - 1 (7 for the 27B draft).
+ *  cand_ids     int32 [batch][P][top_k], cand_logp fp32 [batch][P][top_k]:
  *               candidates ordered by (logit desc, id asc) and their log-softmax.
- *  dbg_hidden   nullable fp32 [n_layers+1][batch][8][hidden]: the residual stream
+ *  dbg_hidden   nullable fp32 [n_layers+1][batch][block][hidden]: the residual stream
  *               after block assembly and after each layer.
- *  dbg_logits   nullable fp32 [batch][7][vocab].
+ *  dbg_logits   nullable fp32 [batch][P][vocab].
  *  workspace    device, >= dflash_workspace_bytes(cfg, batch, t_new), 256-byte aligned.
  *  probe        nullable; see dflash_probe.
  *

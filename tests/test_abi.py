@@ -89,7 +89,9 @@ def test_draft_step_rejects_bad_arguments_before_launch():
     assert call_step(cfg, w, cap=4) == -1                   # cache smaller than t_new
     assert call_step(tiny_cfg(head_dim=96), w) == -2        # ESHAPE
     assert call_step(tiny_cfg(top_k=17), w) == -2
-    assert call_step(tiny_cfg(block=5), w) == -2
+    assert call_step(tiny_cfg(block=9), w) == -2             # blocks of 2..8
+    assert call_step(tiny_cfg(block=1), w) == -2
+    assert call_step(tiny_cfg(n_q_heads=128, n_kv_heads=32, head_dim=64), w) == -2   # n_q <= 64
     assert call_step(tiny_cfg(n_kv_heads=3), w) == -2
     assert call_step(tiny_cfg(hidden=200), w) == -2
     assert call_step(tiny_cfg(sel_rank=48), w) == -2

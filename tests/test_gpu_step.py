@@ -191,3 +191,20 @@ def test_tiny_step_tied_logits_take_lowest_ids():
     assert np.allclose(g["lp"], -np.log(V), atol=1e-4)
     ref = parity.run_oracle(wl, W, bufs.inputs)
     assert (ref["cand_ids"] == np.arange(K)).all()
+
+
+@pytest.mark.parametrize("block,batch", [(5, 2), (4, 1), (4, 2), (2, 3)])
+def test_tiny_step_block_lengths(block, batch):
+    """Shorter blocks (P = block - 1 proposals; the pages' MLX example drafts with a
+    block of 5): block 5 x 2 sequences runs the MLP products over 20 rows (row-tiled
+    kernel); block 4 x 1 and x 2 make the (hi, lo) row pairs 4 and 8 rows apart (added
+    inside the streaming kernel); block 2 leaves one proposal per sequence."""
+    shape = dataclasses.replace(synth.TINY, block=block)
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], shape=shape, batch=batch, seed=20 + block)
+    say(f"[step] tiny block {block}, batch {batch}")
+    bufs = runner.StepBuffers(wl)
+    bufs.step()
+    ref = parity.run_oracle(wl, bufs.host_W, bufs.inputs)
+    g = full_check(wl, bufs, ref)
+    assert g["draft"].shape == (batch, block - 1)
+    check_verify(bufs, g)
