@@ -90,6 +90,11 @@ def randint(seed, name, shape, lo, hi):
     return out
 
 
+def uniform(seed, name, shape):
+    """float32 uniform on [0, 1): multiples of 2^-24 (exact in float32 and float64)."""
+    return randint(seed, name, shape, 0, 1 << 24).astype(np.float32) * np.float32(2.0 ** -24)
+
+
 def q4k_pack(w):
     """float32 [rows, cols] (cols % 256 == 0) -> Q4_K bytes uint8 [rows * cols/256 * 144]."""
     w = np.ascontiguousarray(w, dtype=np.float32)

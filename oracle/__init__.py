@@ -23,6 +23,8 @@ Modules:
   draft    - the draft forward: tap fusion, layers, LM head, top-K
   select   - Viterbi path through the candidates, and brute force
   verify   - greedy accept-longest-prefix
+  sample   - sampled acceptance (exact rejection sampling against the target's
+             temperature / top-k / top-p distribution)
   budget   - parameter budget of the drafter shapes
 
 Every function here is pinned by a test in tests/test_oracle_*.py against values
