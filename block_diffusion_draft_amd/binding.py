@@ -73,6 +73,12 @@ def lib():
     L.dflash_verify_prefix.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p,
                                        c_void_p]
     L.dflash_verify_prefix.restype = c_int
+    L.dflash_verify_sampled_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    L.dflash_verify_sampled_workspace_bytes.restype = c_size_t
+    L.dflash_verify_sampled.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
+                                        c_float, c_int, c_float, c_void_p, c_size_t, c_void_p,
+                                        c_void_p, c_void_p]
+    L.dflash_verify_sampled.restype = c_int
     L.q4k_gemm_workspace_bytes.argtypes = [c_int, c_int, c_int]
     L.q4k_gemm_workspace_bytes.restype = c_size_t
     L.q4k_gemm.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_size_t,
@@ -89,6 +95,7 @@ def lib():
 
 
 EXPORTS = ["dflash_workspace_bytes", "dflash_draft_step", "dflash_verify_prefix",
+           "dflash_verify_sampled_workspace_bytes", "dflash_verify_sampled",
            "q4k_gemm_workspace_bytes", "q4k_gemm", "q4k_to_tiled", "q4k_dequantize",
            "dflash_status_str"]
 
@@ -196,6 +203,22 @@ def verify_prefix(draft, target, accept_len, out_tokens):
     B, n = draft.shape
     check(lib().dflash_verify_prefix(_ptr(draft), _ptr(target), B, n, _ptr(accept_len),
                                      _ptr(out_tokens), _stream()))
+
+
+def verify_sampled_workspace_bytes(batch, n, vocab):
+    return lib().dflash_verify_sampled_workspace_bytes(batch, n, vocab)
+
+
+def verify_sampled(draft, target_logits, uniforms, temperature, top_k, top_p, workspace,
+                   accept_len, out_tokens):
+    """Enqueue sampled acceptance (device tensors: draft int32 [B, n], target_logits fp32
+    [B, n + 1, V], uniforms fp32 [B, n + 1, 2], outputs int32 [B] and [B, n + 1])."""
+    B, n = draft.shape
+    V = target_logits.shape[2]
+    check(lib().dflash_verify_sampled(_ptr(draft), _ptr(target_logits), _ptr(uniforms), B, n, V,
+                                      temperature, top_k, top_p, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _ptr(accept_len), _ptr(out_tokens), _stream()))
 
 
 def q4k_gemm(w, x, y, workspace):

@@ -2,6 +2,7 @@
 // launch sequence of one step on the caller's stream.  Nothing is allocated.
 #include "../../include/dflash.h"
 #include "kernels.h"
+#include <cmath>
 
 #include <string.h>
 
@@ -419,6 +420,37 @@ int dflash_verify_prefix(const int32_t *draft, const int32_t *target, int batch,
     if (!draft || !target || !accept_len || !out_tokens) return DFLASH_EINVAL;
     if (batch < 1 || n < 1 || n > 64) return DFLASH_EINVAL;
     HIPCHK(launch_verify(draft, target, batch, n, accept_len, out_tokens, (hipStream_t)stream));
+    return DFLASH_OK;
+}
+
+static bool sample_shape_ok(int batch, int n, int vocab) {
+    return batch >= 1 && n >= 1 && n <= DFLASH_SAMPLE_MAX_N && vocab >= 1 &&
+           vocab <= DFLASH_SAMPLE_MAX_VOCAB && (long long)batch * (n + 1) <= 65535;
+}
+
+size_t dflash_verify_sampled_workspace_bytes(int batch, int n, int vocab) {
+    if (!sample_shape_ok(batch, n, vocab)) return 0;
+    return topk_workspace_floats(batch * (n + 1), vocab) * sizeof(float);
+}
+
+int dflash_verify_sampled(const int32_t *draft, const float *target_logits, const float *uniforms,
+                          int batch, int n, int vocab, float temperature, int top_k, float top_p,
+                          void *workspace, size_t ws_bytes, int32_t *accept_len,
+                          int32_t *out_tokens, void *stream) {
+    if (!draft || !target_logits || !uniforms || !accept_len || !out_tokens) return DFLASH_EINVAL;
+    if (batch < 1 || n < 1 || vocab < 1) return DFLASH_EINVAL;
+    if (!(temperature > 0.f) || !std::isfinite(temperature)) return DFLASH_EINVAL;
+    if (!(top_p > 0.f && top_p <= 1.f)) return DFLASH_EINVAL;
+    if (top_k < 1 || top_k > vocab) return DFLASH_EINVAL;
+    if (!sample_shape_ok(batch, n, vocab) || top_k > DFLASH_SAMPLE_MAX_TOPK) return DFLASH_ESHAPE;
+    const void *ptrs[5] = {draft, target_logits, uniforms, accept_len, out_tokens};
+    for (const void *q : ptrs)
+        if ((uintptr_t)q % 4) return DFLASH_EALIGN;
+    const size_t need = dflash_verify_sampled_workspace_bytes(batch, n, vocab);
+    if (!workspace || ws_bytes < need || !aligned16(workspace)) return DFLASH_EWORKSPACE;
+    HIPCHK(launch_topk_sample(target_logits, batch, n, vocab, top_k, (float *)workspace, draft,
+                              uniforms, temperature, top_p, accept_len, out_tokens,
+                              (hipStream_t)stream));
     return DFLASH_OK;
 }
 

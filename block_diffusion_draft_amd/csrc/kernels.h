@@ -114,6 +114,14 @@ hipError_t launch_topk_path(const float *logits, int B, int P, int V, int K, con
                             float pair_scale, int32_t *cand_ids, float *cand_logp,
                             int32_t *draft_tokens, hipStream_t st);
 
+// Sampled acceptance of B sequences of n drafted tokens against target logits
+// [B][n + 1][V]: top-K of every row (the same threshold passes), then per sequence the
+// rejection-sampling walk (uniform draws u [B][n + 1][2]).  ws: topk_workspace_floats(
+// B (n + 1), V) floats.  n + 1 <= 64, K <= 64, K <= V.
+hipError_t launch_topk_sample(const float *logits, int B, int n, int V, int K, float *ws,
+                              const int32_t *draft, const float *u, float temperature, float top_p,
+                              int32_t *accept_len, int32_t *out_tokens, hipStream_t st);
+
 // ---------------------------------------------------------------- verify
 hipError_t launch_verify(const int32_t *draft, const int32_t *target, int B, int n,
                          int32_t *accept_len, int32_t *out_tokens, hipStream_t st);

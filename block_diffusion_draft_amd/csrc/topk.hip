@@ -18,7 +18,7 @@
 //     reach theta (many equal logits), the row is selected by an exact scan of all
 //     its chunks instead.
 // Every choice is an arg-max under a total order, so the result is exact and does
-// not depend on thread scheduling.
+// not depend on thread scheduling.  K <= 64 (the threshold is a lane maximum).
 //
 // Pass 4 runs inside the selector's workgroup (one per sequence): its waves select the
 // sequence's rows, then the candidate-path search runs on them.  Selector (same card,
@@ -179,12 +179,12 @@ __global__ __launch_bounds__(256) void k_collect(const float *logits, int V, int
 }
 
 // 4. one wave, row r: exact top-K of the candidates (or of the whole row on overflow)
-// into sid[k], slp[k] (k < K; LDS of the calling workgroup)
+// into sid[k], slp[k] = logit - lse[r] (k < K; LDS of the calling workgroup)
 __device__ void select_row(const float *logits, int V, int nch, int K, int r, const int *count,
                            const float *cv, const int32_t *ci, const float *lse, int *sid,
                            float *slp) {
     const int lane = threadIdx.x & 63;
-    const float L = lse[r];
+    const float L = lse ? lse[r] : 0.f;             // null: the raw logits
     const int n = count[r];
     if (n <= 64) {
         // one candidate per lane: sort the wave, the first K lanes are the answer
@@ -368,6 +368,91 @@ __global__ __launch_bounds__(64 * PATH_WAVES) void k_select_path(
     }
 }
 
+// ---------------------------------------------------------------- sampled acceptance
+// Mindket kit page "Qwen3.8-27B-DFlash2-GGUF by z-lab": sampling keeps the target's
+// distribution ("For newcomers and experts"), sampler temperature 1.0, top-p 0.95,
+// top-k 20 ("Good to know").  The draft's proposals are deterministic (the selector's
+// path), so rejection sampling runs against a point-mass proposal: x_j is accepted when
+// u < p_j(x_j); on rejection a token is drawn from p_j without x_j; when all n are
+// accepted a bonus token is drawn from p_n.  p_j = softmax(logits / T) over the top_k
+// logits, cut to the smallest (prob desc, id asc) prefix with mass >= top_p.
+
+constexpr int SAMPLE_MAXK = 64;
+constexpr int SAMPLE_MAXROWS = 64;
+constexpr int SAMPLE_WAVES = 8;
+
+__device__ __forceinline__ float wave_incl_scan(float v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float t = __shfl_up(v, o, WAVE);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// inverse CDF over the lanes' weights r (lane order): the first eligible lane whose
+// cumulative weight exceeds u * total; the last eligible lane if rounding runs past the
+// end (lane 0 if none is eligible)
+__device__ __forceinline__ int draw_lane(float r, float u, bool elig) {
+    const float total = wave_sum(r);
+    const float c = wave_incl_scan(r);
+    const unsigned long long hit = __ballot(elig && c > u * total);
+    if (hit) return __builtin_ctzll(hit);
+    const unsigned long long e = __ballot(elig);
+    return e ? 63 - __builtin_clzll(e) : 0;
+}
+
+// One workgroup per sequence: waves select the sequence's n + 1 rows (top_k by logit
+// desc, id asc) into LDS, then wave 0 walks the positions in order, one lane per
+// candidate.
+__global__ __launch_bounds__(64 * SAMPLE_WAVES) void k_sample_accept(
+    const float *logits, int V, int nch, int K, const int *count, const float *cv,
+    const int32_t *ci, const int32_t *draft, const float *u, int n, float temperature,
+    float top_p, int32_t *accept_len, int32_t *out) {
+    __shared__ int sid[SAMPLE_MAXROWS][SAMPLE_MAXK];
+    __shared__ float sv[SAMPLE_MAXROWS][SAMPLE_MAXK];
+    const int b = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rows = n + 1;
+    for (int j = wave; j < rows; j += SAMPLE_WAVES)
+        select_row(logits, V, nch, K, b * rows + j, count, cv, ci, nullptr, sid[j], sv[j]);
+    __syncthreads();
+    if (wave != 0) return;
+    const float *ub = u + (size_t)b * rows * 2;
+    int32_t *ob = out + (size_t)b * rows;
+    int k = n;
+    for (int j = 0; j < rows; j++) {
+        const bool in = lane < K;
+        const int id = in ? sid[j][lane] : -1;
+        const float w = in ? expf((sv[j][lane] - sv[j][0]) / temperature) : 0.f;
+        const float S = wave_sum(w);
+        float before = __shfl_up(wave_incl_scan(w), 1, WAVE);   // mass of the lanes below
+        if (lane == 0) before = 0.f;
+        const bool keep = in && before < top_p * S;             // a prefix of the lanes
+        const float wk = keep ? w : 0.f;
+        if (j == n) {                                           // every proposal accepted
+            const int c = draw_lane(wk, ub[2 * j + 1], keep);
+            if (lane == 0) ob[j] = sid[j][c];
+            break;
+        }
+        const int x = draft[(size_t)b * n + j];
+        const float Sm = wave_sum(wk);
+        const unsigned long long hm = __ballot(keep && id == x);
+        const float px = hm ? __shfl(wk, __builtin_ctzll(hm), WAVE) / Sm : 0.f;
+        if (ub[2 * j] < px) {
+            if (lane == 0) ob[j] = x;
+            continue;
+        }
+        const bool elig = keep && id != x;
+        const int c = draw_lane(elig ? w : 0.f, ub[2 * j + 1], elig);
+        if (lane == 0) ob[j] = sid[j][c];
+        k = j;
+        break;
+    }
+    if (lane > k && lane < rows) ob[lane] = -1;
+    if (lane == 0) accept_len[b] = k;
+}
+
 }  // namespace
 
 size_t topk_workspace_floats(int R, int V) {
@@ -393,6 +478,25 @@ hipError_t launch_topk_path(const float *logits, int B, int P, int V, int K, con
     hipLaunchKernelGGL(k_select_path, dim3(B), dim3(64 * PATH_WAVES), 0, st, logits, V, nch, K, count,
                        cv, ci, lse, P, valid, code_a, code_b, r, pair_scale, cand_ids, cand_logp,
                        draft_tokens);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_sample(const float *logits, int B, int n, int V, int K, float *ws,
+                              const int32_t *draft, const float *u, float temperature, float top_p,
+                              int32_t *accept_len, int32_t *out_tokens, hipStream_t st) {
+    if (n + 1 > SAMPLE_MAXROWS || K > SAMPLE_MAXK || K > V) return hipErrorInvalidValue;
+    const int R = B * (n + 1);
+    const int nch = ceil_div(V, CHUNK);
+    float *pm = ws, *ps = pm + (size_t)R * nch, *thr = ps + (size_t)R * nch, *lse = thr + R;
+    int *count = reinterpret_cast<int *>(lse + R);
+    float *cv = reinterpret_cast<float *>(count + R);
+    int32_t *ci = reinterpret_cast<int32_t *>(cv + (size_t)R * CAP);
+    const dim3 grid(ceil_div(nch, 4), R);
+    hipLaunchKernelGGL(k_chunk_stats, grid, dim3(256), 0, st, logits, V, nch, pm, ps);
+    hipLaunchKernelGGL(k_row_threshold, dim3(R), dim3(64), 0, st, pm, ps, nch, K, thr, lse, count);
+    hipLaunchKernelGGL(k_collect, grid, dim3(256), 0, st, logits, V, nch, thr, count, cv, ci);
+    hipLaunchKernelGGL(k_sample_accept, dim3(B), dim3(64 * SAMPLE_WAVES), 0, st, logits, V, nch, K,
+                       count, cv, ci, draft, u, n, temperature, top_p, accept_len, out_tokens);
     return hipGetLastError();
 }
 

@@ -95,6 +95,25 @@ def uniform(seed, name, shape):
     return randint(seed, name, shape, 0, 1 << 24).astype(np.float32) * np.float32(2.0 ** -24)
 
 
+def target_logits(seed, name, draft, V, std=2.0, lift=0.9):
+    """Synthetic target logits [B, n + 1, V] fp32 for drafted tokens draft [B, n]: N(0, std)
+    per entry; at each proposal position, with probability `lift` (seeded), the drafted
+    token's logit is set to the row maximum plus U(2, 7), so that the target usually
+    ranks the draft first with a probability spread over roughly 0.4 .. 0.99, and the
+    accepted lengths spread over 0 .. n."""
+    draft = np.asarray(draft)
+    B, n = draft.shape
+    z = normal_f32(seed, name, (B, n + 1, V), std)
+    coin = uniform(seed, name + ".lift", (B, n))
+    off = uniform(seed, name + ".off", (B, n)) * np.float32(5.0) + np.float32(2.0)
+    for b in range(B):
+        for j in range(n):
+            x = int(draft[b, j])
+            if coin[b, j] < lift and 0 <= x < V:
+                z[b, j, x] = z[b, j].max() + off[b, j]
+    return z
+
+
 def q4k_pack(w):
     """float32 [rows, cols] (cols % 256 == 0) -> Q4_K bytes uint8 [rows * cols/256 * 144]."""
     w = np.ascontiguousarray(w, dtype=np.float32)

@@ -13,6 +13,12 @@
  *   dflash_verify_prefix greedy acceptance: keep the longest drafted prefix the
  *                        target agrees with, plus one target token.  Same card,
  *                        sections "How it is used" and "FastFlowLM measurements".
+ *   dflash_verify_sampled
+ *                        sampled acceptance: exact rejection sampling of the drafted
+ *                        tokens against the target's temperature / top-k / top-p
+ *                        distribution.  Mindket kit page "Qwen3.8-27B-DFlash2-GGUF by
+ *                        z-lab", sections "For newcomers and experts" and "Good to
+ *                        know".
  *   q4k_gemm             y = x . W^T with W in Q4_K super-blocks (the format of
  *                        the draft's fc, q/k/v/o and MLP matrices: same card,
  *                        "Weights" row), fp32 accumulation, bf16 output.
@@ -51,6 +57,9 @@ extern "C" {
 #define DFLASH_BLOCK 8          /* the drafter's block: 1 anchor + 7 proposals; also the
                                    largest block and t_new the kernels take */
 #define DFLASH_MAX_TOPK 16
+#define DFLASH_SAMPLE_MAX_N 63          /* dflash_verify_sampled: drafted tokens per row */
+#define DFLASH_SAMPLE_MAX_TOPK 64       /* dflash_verify_sampled: target top_k */
+#define DFLASH_SAMPLE_MAX_VOCAB (1 << 20)
 
 typedef enum {
     DFLASH_OK = 0,
@@ -161,6 +170,48 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
  */
 int dflash_verify_prefix(const int32_t *draft, const int32_t *target, int batch, int n,
                          int32_t *accept_len, int32_t *out_tokens, void *stream);
+
+/* Workspace bytes dflash_verify_sampled needs (0 if the shape is not supported). */
+size_t dflash_verify_sampled_workspace_bytes(int batch, int n, int vocab);
+
+/*
+ * Sampled acceptance for `batch` rows: exact rejection sampling of the drafted tokens
+ * against the target's sampling distribution (Mindket kit page "Qwen3.8-27B-DFlash2-GGUF
+ * by z-lab": "For newcomers and experts", sampling keeps the target's distribution;
+ * "Good to know", temperature 1.0, top-p 0.95, top-k 20).
+ *  draft         int32 [batch][n] drafted tokens (the selector's path).
+ *  target_logits fp32 [batch][n+1][vocab]: row j holds the target's logits after block
+ *                position j (position 0 = the last accepted token).
+ *  uniforms      fp32 [batch][n+1][2] in [0, 1): [j][0] decides acceptance of draft[j],
+ *                [j][1] draws the token emitted at j (after a rejection, or the bonus
+ *                token at j = n).
+ *  p_j           target distribution of row j: logits / temperature, the top_k largest
+ *                (ties: lowest id first), softmax over those, then the smallest prefix
+ *                in (probability desc, id asc) order whose mass reaches top_p,
+ *                renormalised.
+ *  procedure     for j = 0..n-1: accept draft[j] when uniforms[j][0] < p_j(draft[j]);
+ *                otherwise emit a token drawn from p_j with draft[j] removed and stop.
+ *                When all n are accepted, emit a token drawn from p_n.  A draw takes the
+ *                first token (same order) whose cumulative weight exceeds u times the
+ *                total weight.  The proposals are deterministic, so the proposal
+ *                distribution is a point mass; each emitted token then follows p_j
+ *                given the tokens before it.
+ *  accept_len    int32 [batch]: k, the number of accepted drafted tokens.
+ *  out_tokens    int32 [batch][n+1]: draft[0..k-1], the emitted token, then -1.
+ *  workspace     device, >= dflash_verify_sampled_workspace_bytes(batch, n, vocab),
+ *                16-byte aligned.
+ * 1 <= n <= DFLASH_SAMPLE_MAX_N, 1 <= top_k <= min(vocab, DFLASH_SAMPLE_MAX_TOPK),
+ * 0 < top_p <= 1, temperature > 0 and finite, vocab <= DFLASH_SAMPLE_MAX_VOCAB,
+ * batch * (n+1) <= 65535; int32 / fp32 pointers 4-byte aligned.  Each row needs a
+ * finite maximum.  A drafted token outside [0, vocab) has probability 0 (rejected).
+ * The probabilities are computed in fp32: a decision whose threshold lies within
+ * fp32 rounding of the uniform may differ from an exact-arithmetic evaluation.
+ */
+int dflash_verify_sampled(const int32_t *draft, const float *target_logits,
+                          const float *uniforms, int batch, int n, int vocab,
+                          float temperature, int top_k, float top_p, void *workspace,
+                          size_t workspace_bytes, int32_t *accept_len, int32_t *out_tokens,
+                          void *stream);
 
 /* Workspace bytes q4k_gemm needs for an M x N x K product. */
 size_t q4k_gemm_workspace_bytes(int M, int N, int K);

@@ -21,8 +21,10 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("dflash_draft_step", "dflash_verify_prefix", "q4k_gemm", "q4k_to_tiled", "q4k_dequantize",
-              "dflash_workspace_bytes", "q4k_gemm_workspace_bytes", "dflash_status_str"):
+    for n in ("dflash_draft_step", "dflash_verify_prefix", "dflash_verify_sampled",
+              "dflash_verify_sampled_workspace_bytes", "q4k_gemm", "q4k_to_tiled",
+              "q4k_dequantize", "dflash_workspace_bytes", "q4k_gemm_workspace_bytes",
+              "dflash_status_str"):
         assert n in names
     assert sorted(binding.EXPORTS) == names
 
@@ -122,3 +124,43 @@ def test_q4k_gemm_and_verify_reject_bad_arguments():
     assert L.q4k_to_tiled(FAKE, FAKE + (1 << 30), 16, 300, None) == -2
     assert L.q4k_to_tiled(FAKE + 8, FAKE + (1 << 30), 16, 256, None) == -3
     assert L.q4k_to_tiled(FAKE, FAKE + 1024, 16, 256, None) == -1   # overlapping buffers
+
+
+def call_sampled(draft=FAKE, logits=FAKE, u=FAKE, batch=2, n=7, vocab=4096, T=1.0, k=20, p=0.95,
+                 ws=FAKE, ws_bytes=1 << 40, acc=FAKE, out=FAKE):
+    return binding.lib().dflash_verify_sampled(draft, logits, u, batch, n, vocab, T, k, p, ws,
+                                               ws_bytes, acc, out, None)
+
+
+def test_verify_sampled_rejects_bad_arguments_before_launch():
+    L = binding.lib()
+    assert L.dflash_verify_sampled_workspace_bytes(2, 7, 4096) > 0
+    assert L.dflash_verify_sampled_workspace_bytes(2, 7, 248320) > \
+        L.dflash_verify_sampled_workspace_bytes(1, 7, 248320)
+    for bad in ((0, 7, 4096), (1, 0, 4096), (1, 64, 4096), (1, 7, 0), (1, 7, (1 << 20) + 1),
+                (8192, 7, 4096)):
+        assert L.dflash_verify_sampled_workspace_bytes(*bad) == 0, bad
+    assert call_sampled(draft=None) == -1                   # EINVAL
+    assert call_sampled(logits=None) == -1
+    assert call_sampled(u=None) == -1
+    assert call_sampled(out=None) == -1
+    assert call_sampled(batch=0) == -1
+    assert call_sampled(n=0) == -1
+    assert call_sampled(T=0.0) == -1
+    assert call_sampled(T=-1.0) == -1
+    assert call_sampled(T=float("inf")) == -1
+    assert call_sampled(T=float("nan")) == -1
+    assert call_sampled(p=0.0) == -1
+    assert call_sampled(p=1.01) == -1
+    assert call_sampled(p=float("nan")) == -1
+    assert call_sampled(k=0) == -1
+    assert call_sampled(k=51, vocab=50) == -1               # top_k above the vocabulary
+    assert call_sampled(n=64) == -2                         # ESHAPE
+    assert call_sampled(k=65) == -2
+    assert call_sampled(vocab=(1 << 20) + 1) == -2
+    assert call_sampled(batch=8192) == -2                   # batch (n + 1) rows > 65535
+    assert call_sampled(logits=FAKE + 2) == -3              # EALIGN
+    assert call_sampled(acc=FAKE + 1) == -3
+    assert call_sampled(ws=None) == -4                      # EWORKSPACE
+    assert call_sampled(ws_bytes=16) == -4
+    assert call_sampled(ws=FAKE + 4) == -4
