@@ -5,6 +5,10 @@ resident in HBM: dflash_draft_step (tap fusion, 5 drafter layers, shared output
 head with top-16, Viterbi selector) followed by dflash_verify_prefix.  The
 workload is the pages' 27B-draft shape at batch 1 with a 4096-row context.
 
+With --accept sampled the acceptance is dflash_verify_sampled instead (rejection
+sampling against synthetic fp32 target logits [1][8][248320] resident in HBM, at the
+pages' sampler settings).
+
 Prints one JSON line: draft blocks/s, the roofline of the dominant kernel (the
 248320 x 5120 bf16 output head, timed live with HIP events around its launch
 inside every timed step), and the float64 CPU reference timed on this host on
@@ -91,6 +95,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
+    ap.add_argument("--accept", choices=("greedy", "sampled"), default="greedy",
+                    help="acceptance after the draft: greedy prefix (the default), or "
+                         "rejection sampling against fp32 target logits [B][8][V] at "
+                         "temperature 1.0, top-k 20, top-p 0.95")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run 3 plain device copies of this size (the "
                          "reference kernel that calibrates rocprofv3 byte counters)")
@@ -117,6 +125,16 @@ def main():
     tgt[:, 4] = (d[:, 4] + 1) % s.vocab
     tgt[:, 5:] = synth.randint(wl.seed, "target_tail", (wl.batch, s.block - 5), 0, s.vocab)
     target = torch.from_numpy(tgt).cuda()
+    sampled = args.accept == "sampled"
+    if sampled:
+        P = s.block - 1
+        z = synth.target_logits(wl.seed, "bench.target_logits", d, s.vocab)
+        u = synth.uniform(wl.seed, "bench.uniforms", (wl.batch, P + 1, 2))
+        tlog = torch.from_numpy(z).cuda()
+        unif = torch.from_numpy(u).cuda()
+        sws = torch.empty(binding.verify_sampled_workspace_bytes(wl.batch, P, s.vocab),
+                          dtype=torch.uint8, device="cuda")
+        del z
 
     K, Wm = args.steps, args.warmup
     ev = [(binding.HipEvent(), binding.HipEvent()) for _ in range(K)]
@@ -124,7 +142,11 @@ def main():
 
     def one_step(probe=None):
         bufs.step(dbg=False, probe=probe)
-        bufs.verify(target)
+        if sampled:
+            binding.verify_sampled(bufs.draft, tlog, unif, 1.0, 20, 0.95, sws, bufs.accept_len,
+                                   bufs.out_tokens)
+        else:
+            bufs.verify(target)
 
     for _ in range(Wm):
         one_step()
@@ -179,7 +201,9 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "ctx_len": wl.ctx_len,
                    "t_new": wl.t_new, "layers": s.n_layers, "hidden": s.hidden,
                    "vocab": s.vocab, "top_k": s.top_k, "weights": s.weight_fmt,
-                   "step": "draft_step + verify_prefix", "hip_graph": bool(graph)},
+                   "step": ("draft_step + verify_sampled (T 1.0, top-k 20, top-p 0.95)"
+                            if sampled else "draft_step + verify_prefix"),
+                   "hip_graph": bool(graph)},
         "roofline": {"kernel": "output head k_head_stream (bf16 MFMA, 248320 x 5120, 7 rows)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
@@ -187,6 +211,8 @@ def main():
         "step_hbm_frac": None,
     }
     step_bytes = step_algorithmic_bytes(wl)
+    if sampled:      # the target's logits and the uniforms, read once
+        step_bytes += wl.batch * s.block * (s.vocab + 2) * 4
     res["step_hbm_frac"] = step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)
     if args.copy_bytes > 0:
         n = args.copy_bytes // 4
