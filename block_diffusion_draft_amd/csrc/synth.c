@@ -209,3 +209,54 @@ void synth_q4k_normal(uint64_t seed, uint64_t stream, int64_t rows, int64_t cols
         }
     }
 }
+
+/* ---------------------------------------------------------------- Q8_0
+ * 34-byte blocks of 32 weights along a row: fp16 scale d (little endian), then 32
+ * signed bytes q; w = d q.  Host-side quantizer (a data generator, not part of the
+ * draft path): d = max |x| / 127 rounded to fp16, q = x / d rounded to nearest
+ * (halves away from zero) and clamped to [-127, 127]; an all-zero block stores d = 0. */
+static void pack_q8_0_block(const float *x, uint8_t *blk) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; i++) amax = fmax(amax, fabs((double)x[i]));
+    uint16_t dh = f32_to_f16((float)(amax / 127.0));
+    double d = f16_to_f64(dh);
+    blk[0] = (uint8_t)(dh & 0xFF);
+    blk[1] = (uint8_t)(dh >> 8);
+    for (int i = 0; i < 32; i++) {
+        double q = d > 0.0 ? round((double)x[i] / d) : 0.0;
+        if (q > 127.0) q = 127.0;
+        if (q < -127.0) q = -127.0;
+        blk[2 + i] = (uint8_t)(int8_t)q;
+    }
+}
+
+/* w [rows][cols] float32, cols % 32 == 0 -> out [rows][cols/32][34] */
+void synth_q8_0_pack(const float *w, int64_t rows, int64_t cols, uint8_t *out) {
+    int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < nb; b++)
+            pack_q8_0_block(w + r * cols + b * 32, out + (r * nb + b) * 34);
+}
+
+/* Q8_0 blocks of a [rows, cols] matrix of std * N(0,1) weights of the stream, element
+ * (r, c) = normal #(r*cols + c) (the same values synth_q4k_normal quantizes). */
+void synth_q8_0_normal(uint64_t seed, uint64_t stream, int64_t rows, int64_t cols, float std,
+                       uint8_t *out) {
+    uint64_t key = stream_key(seed, stream);
+    int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        float x[32];
+        for (int64_t b = 0; b < nb; b++) {
+            uint64_t base = (uint64_t)(r * cols + b * 32);
+            for (int i = 0; i < 32; i += 2) {
+                double z0, z1;
+                normal_pair(key, (base + (uint64_t)i) >> 1, &z0, &z1);
+                x[i] = (float)(std * z0);
+                x[i + 1] = (float)(std * z1);
+            }
+            pack_q8_0_block(x, out + (r * nb + b) * 34);
+        }
+    }
+}

@@ -8,7 +8,7 @@ pages measure on prompts and benchmark suites that are not available here, and
 for the draft step only the shapes, the context length and the number of
 appended rows matter, so seeded synthetic tensors stand in for them):
   * linear weights (fc, q/k/v/o, gate/up/down): N(0, 0.02), packed to Q4_K
-    (or kept bf16 for the unquantised workload);
+    (or Q8_0, or kept bf16 for the unquantised workload);
   * shared embedding / output head, dynamic-conv W_c, selector projection and
     codebooks, mask embedding: bf16 N(0, 0.02);
   * norm gains: 1.0 (``gain_jitter`` > 0 gives 1 + jitter * N(0, 1));
@@ -55,8 +55,11 @@ def lib():
         L.synth_randint.argtypes = [u64, u64, i64, i32, i32, vp]
         L.synth_q4k_pack.argtypes = [vp, i64, i64, vp]
         L.synth_q4k_normal.argtypes = [u64, u64, i64, i64, f32, vp]
+        L.synth_q8_0_pack.argtypes = [vp, i64, i64, vp]
+        L.synth_q8_0_normal.argtypes = [u64, u64, i64, i64, f32, vp]
         for f in (L.synth_normal_f32, L.synth_normal_bf16, L.synth_randint,
-                  L.synth_q4k_pack, L.synth_q4k_normal):
+                  L.synth_q4k_pack, L.synth_q4k_normal, L.synth_q8_0_pack,
+                  L.synth_q8_0_normal):
             f.restype = None
         _lib = L
     return _lib
@@ -129,6 +132,24 @@ def q4k_normal(seed, name, rows, cols, std=0.02):
     assert cols % 256 == 0
     out = np.empty(rows * (cols // 256) * 144, dtype=np.uint8)
     lib().synth_q4k_normal(seed, stream_id(name), rows, cols, std, out.ctypes.data)
+    return out
+
+
+def q8_0_pack(w):
+    """float32 [rows, cols] (cols % 32 == 0) -> Q8_0 bytes uint8 [rows * cols/32 * 34]."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    assert cols % 32 == 0
+    out = np.empty(rows * (cols // 32) * 34, dtype=np.uint8)
+    lib().synth_q8_0_pack(w.ctypes.data, rows, cols, out.ctypes.data)
+    return out
+
+
+def q8_0_normal(seed, name, rows, cols, std=0.02):
+    """Q8_0 bytes of a [rows, cols] matrix of std * N(0, 1) weights (stream `name`)."""
+    assert cols % 32 == 0
+    out = np.empty(rows * (cols // 32) * 34, dtype=np.uint8)
+    lib().synth_q8_0_normal(seed, stream_id(name), rows, cols, std, out.ctypes.data)
     return out
 
 
@@ -224,7 +245,7 @@ def linear_shapes(s):
 def make_weights(s, seed, gain_jitter=0.0):
     """All drafter weights of shape `s` as a dict (the checker's format).
 
-    Linear weights: ("q4k", uint8 bytes) or ("bf16", uint16 [rows, cols]).
+    Linear weights: ("q4k" or "q8_0", uint8 bytes) or ("bf16", uint16 [rows, cols]).
     Everything else: uint16 bf16 arrays.  embed and lm_head are the same array
     (the draft shares the target's embedding table and output head).
     """
@@ -232,6 +253,8 @@ def make_weights(s, seed, gain_jitter=0.0):
     for name, rows, cols in linear_shapes(s):
         if s.weight_fmt == "q4k":
             W[name] = ("q4k", q4k_normal(seed, name, rows, cols, 0.02))
+        elif s.weight_fmt == "q8_0":
+            W[name] = ("q8_0", q8_0_normal(seed, name, rows, cols, 0.02))
         else:
             W[name] = ("bf16", normal_bf16(seed, name, (rows, cols), 0.02))
 

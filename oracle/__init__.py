@@ -20,6 +20,7 @@ Sources (the pages this follows):
 Modules:
   bf16     - bf16 <-> float64 conversion (the storage format of the inputs)
   q4k      - Q4_K super-block decode
+  q8_0     - Q8_0 block decode
   draft    - the draft forward: tap fusion, layers, LM head, top-K
   select   - Viterbi path through the candidates, and brute force
   verify   - greedy accept-longest-prefix

@@ -29,7 +29,7 @@ here is stated where it is used and listed in the design notes):
 """
 import numpy as np
 
-from . import q4k
+from . import q4k, q8_0
 from .bf16 import bf16_to_f64, f64_to_bf16
 
 
@@ -92,11 +92,13 @@ def topk_desc(logits, k):
 def dense(w, rows, cols):
     """A linear weight -> float64 [rows, cols].
 
-    w is either ("q4k", uint8 bytes) or ("bf16", uint16 [rows, cols]).
+    w is ("q4k", uint8 bytes), ("q8_0", uint8 bytes) or ("bf16", uint16 [rows, cols]).
     """
     fmt, data = w
     if fmt == "q4k":
         return q4k.decode_matrix(data, rows, cols)
+    if fmt == "q8_0":
+        return q8_0.decode_matrix(data, rows, cols)
     if fmt == "bf16":
         a = np.asarray(data).reshape(rows, cols)
         return bf16_to_f64(a)
@@ -158,7 +160,7 @@ def draft_step(cfg, W, taps, last_token, ctx_len, k_cache, v_cache, want_logits=
 
     cfg: dict with n_layers, hidden, ffn, n_q, n_kv, head_dim, window, vocab,
          n_taps, block, top_k, rms_eps, rope_theta.
-    W:   dict of weights.  Linear weights are ("q4k", bytes) or ("bf16", u16):
+    W:   dict of weights.  Linear weights are ("q4k" or "q8_0", bytes) or ("bf16", u16):
          fc [H, n_taps H], and per layer l: wq [n_q d, H], wk/wv [n_kv d, H],
          wo [H, n_q d], wg/wu [F, H], wd [H, F].  bf16 uint16 arrays: hidden_norm,
          final_norm [H], mask_emb [H], embed [V, H], lm_head [V, H], and per layer
