@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libdflash.so")
 MAX_LAYERS = 8
 BLOCK = 8
 
-W_Q4K, W_BF16 = 0, 1
+W_Q4K, W_BF16, W_Q8_0 = 0, 1, 2
+WEIGHT_FMT = {"q4k": W_Q4K, "bf16": W_BF16, "q8_0": W_Q8_0}
 PROBE_NONE, PROBE_LM_HEAD, PROBE_FFN_GATE_UP = 0, 1, 2
 
 c_int, c_float, c_void_p, c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -88,6 +89,15 @@ def lib():
     L.q4k_dequantize.restype = c_int
     L.q4k_to_tiled.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p]
     L.q4k_to_tiled.restype = c_int
+    L.q8_0_gemm_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    L.q8_0_gemm_workspace_bytes.restype = c_size_t
+    L.q8_0_gemm.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p,
+                            c_size_t, c_void_p]
+    L.q8_0_gemm.restype = c_int
+    L.q8_0_to_tiled.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p]
+    L.q8_0_to_tiled.restype = c_int
+    L.q8_0_dequantize.argtypes = [c_void_p, c_void_p, ctypes.c_longlong, c_void_p]
+    L.q8_0_dequantize.restype = c_int
     L.dflash_status_str.argtypes = [c_int]
     L.dflash_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -97,6 +107,7 @@ def lib():
 EXPORTS = ["dflash_workspace_bytes", "dflash_draft_step", "dflash_verify_prefix",
            "dflash_verify_sampled_workspace_bytes", "dflash_verify_sampled",
            "q4k_gemm_workspace_bytes", "q4k_gemm", "q4k_to_tiled", "q4k_dequantize",
+           "q8_0_gemm_workspace_bytes", "q8_0_gemm", "q8_0_to_tiled", "q8_0_dequantize",
            "dflash_status_str"]
 
 
@@ -109,7 +120,7 @@ def make_config(shape):
     """Config struct from a synth.Shape-like object."""
     return Config(shape.n_layers, shape.hidden, shape.ffn, shape.n_q, shape.n_kv, shape.head_dim,
                   shape.window, shape.vocab, shape.n_taps, shape.block, shape.top_k,
-                  shape.sel_rank, W_Q4K if shape.weight_fmt == "q4k" else W_BF16,
+                  shape.sel_rank, WEIGHT_FMT[shape.weight_fmt],
                   shape.rms_eps, shape.rope_theta, shape.pair_scale)
 
 
@@ -144,9 +155,9 @@ class DeviceWeights:
     """Drafter weights resident in device memory, plus the C struct pointing at them.
 
     `W` is the host weight dict of synth.make_weights (linear weights as
-    ("q4k", row-major Q4_K bytes) or ("bf16", uint16 array); the rest uint16
-    arrays).  Q4_K matrices are regrouped on the device into the library's tiled
-    layout (q4k_to_tiled) after the upload.
+    ("q4k" / "q8_0", row-major block bytes) or ("bf16", uint16 array); the rest uint16
+    arrays).  Q4_K and Q8_0 matrices are regrouped on the device into the library's
+    tiled layouts (q4k_to_tiled, q8_0_to_tiled) after the upload.
     """
 
     def __init__(self, shape, W, device="cuda"):
@@ -156,7 +167,7 @@ class DeviceWeights:
         shared = {}
         dims = _linear_dims(shape)
 
-        def up(name, arr, q4k):
+        def up(name, arr, fmt):
             arr = np.ascontiguousarray(arr)
             key = arr.__array_interface__["data"][0]
             if key in shared:                      # tied embedding / output head
@@ -165,9 +176,9 @@ class DeviceWeights:
                 dt = torch.uint8 if arr.dtype == np.uint8 else torch.int16
                 t = torch.from_numpy(arr.view(np.uint8 if arr.dtype == np.uint8 else np.int16))
                 t = t.to(device, dtype=dt)
-                if q4k:
+                if fmt in ("q4k", "q8_0"):
                     tiled = torch.empty_like(t)
-                    q4k_to_tiled(t, tiled, *dims[name])
+                    (q4k_to_tiled if fmt == "q4k" else q8_0_to_tiled)(t, tiled, *dims[name])
                     t = tiled
                 shared[key] = t
             self.tensors[name] = t
@@ -176,7 +187,7 @@ class DeviceWeights:
         s = Weights()
         for name, val in W.items():
             arr = val[1] if isinstance(val, tuple) else val
-            p = up(name, arr, isinstance(val, tuple) and val[0] == "q4k")
+            p = up(name, arr, val[0] if isinstance(val, tuple) else "bf16")
             m = re.match(r"^l(\d+)\.(\w+)$", name)
             if m:
                 setattr(s.layer[int(m.group(1))], m.group(2), p)
@@ -235,6 +246,26 @@ def q4k_gemm_workspace_bytes(M, N, K):
 def q4k_to_tiled(src, dst, N, K):
     """Regroup a row-major Q4_K matrix [N][K] (device uint8) into the tiled layout."""
     check(lib().q4k_to_tiled(_ptr(src), _ptr(dst), N, K, _stream()))
+
+
+def q8_0_gemm(w, x, y, workspace):
+    M, K = x.shape
+    N = y.shape[1]
+    check(lib().q8_0_gemm(_ptr(w), _ptr(x), _ptr(y), M, N, K, _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream()))
+
+
+def q8_0_gemm_workspace_bytes(M, N, K):
+    return lib().q8_0_gemm_workspace_bytes(M, N, K)
+
+
+def q8_0_to_tiled(src, dst, N, K):
+    """Regroup a row-major Q8_0 matrix [N][K] (device uint8) into the tiled layout."""
+    check(lib().q8_0_to_tiled(_ptr(src), _ptr(dst), N, K, _stream()))
+
+
+def q8_0_dequantize(w, out):
+    check(lib().q8_0_dequantize(_ptr(w), _ptr(out), out.numel() // 32, _stream()))
 
 
 def q4k_dequantize(w, out):

@@ -29,6 +29,8 @@ size_t gemm_part_bytes(int fmt, int M, int N, int K) {
     if (fmt == DFLASH_W_Q4K)
         return q4k_stream_ok(M, N, K) ? q4k_stream_plan(M, N, K).part_bytes
                                       : q4k_fused_plan(M, N, K).part_bytes;
+    if (fmt == DFLASH_W_Q8_0 && q8_stream_ok(M, N, K))
+        return q8_stream_plan(M, N, K).part_bytes;
     return (size_t)M * N * 4;
 }
 
@@ -125,7 +127,9 @@ int check_config(const dflash_config *c) {
     if (c->sel_rank < 32 || c->sel_rank % 32 || c->sel_rank > 4096) return DFLASH_ESHAPE;
     if (c->window < 0) return DFLASH_EINVAL;
     if (c->window > 65536) return DFLASH_ESHAPE;     // attention-merge weights live in LDS
-    if (c->weight_fmt != DFLASH_W_Q4K && c->weight_fmt != DFLASH_W_BF16) return DFLASH_EINVAL;
+    if (c->weight_fmt != DFLASH_W_Q4K && c->weight_fmt != DFLASH_W_BF16 &&
+        c->weight_fmt != DFLASH_W_Q8_0)
+        return DFLASH_EINVAL;
     if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return DFLASH_EINVAL;
     return DFLASH_OK;
 }
@@ -160,6 +164,35 @@ int run_q4k(const Q4kFusedArgs &a, hipStream_t st, int *pair_left) {
     return p.splits;
 }
 
+// Q8_0 product into partials: the streaming kernel for up to 16 rows (K a multiple of
+// 1024), else the tiled MFMA kernel with the Q8_0 loader ([M][N], one split).
+int run_q8(const Q4kFusedArgs &a, hipStream_t st, int *pair_left) {
+    const int K = a.KB * 256;
+    *pair_left = a.pair;
+    if (q8_stream_ok(a.M, a.N, K)) {
+        const Q4kStreamPlan p = q8_stream_plan(a.M, a.N, K, a.pair);
+        HIPCHK(launch_q8_stream(a, p, st));
+        if (p.pair_done) *pair_left = 0;
+        return p.splits;
+    }
+    Bf16GemmArgs g = {};
+    for (int i = 0; i < 3; i++) {
+        g.w[i] = reinterpret_cast<const uint16_t *>(a.w[i]);
+        g.seg_end[i] = a.seg_end[i];
+    }
+    g.nseg = a.nseg;
+    g.A = a.src.A;
+    g.lda = a.src.lda;
+    g.M = a.M;
+    g.N = a.N;
+    g.K = K;
+    g.C = a.part;
+    g.ldc = a.N;
+    g.wfmt = 1;
+    HIPCHK(launch_bf16_gemm_tiled(g, st));
+    return 1;
+}
+
 // y = A . W^T over up to 3 weight matrices stacked along N, as fp32 partial sums in
 // the workspace's partial buffer: Q4_K -> [splits][M][N] from the dequantize-fused
 // MFMA kernel; bf16 -> [M][N] (one split) from the tiled MFMA kernel.  Rows r and
@@ -176,7 +209,7 @@ int run_gemm(const Ctx &x, const void *const *w, const int *seg_n, int nseg, con
         seg_end[i] = N;
     }
     float *part = x.at<float>(x.p->o_part);
-    if (x.c->weight_fmt == DFLASH_W_Q4K) {
+    if (x.c->weight_fmt == DFLASH_W_Q4K || x.c->weight_fmt == DFLASH_W_Q8_0) {
         Q4kFusedArgs a;
         for (int i = 0; i < 3; i++) {
             a.w[i] = (const unsigned char *)(i < nseg ? w[i] : w[0]);
@@ -190,7 +223,8 @@ int run_gemm(const Ctx &x, const void *const *w, const int *seg_n, int nseg, con
         a.src.lda = lda;
         a.part = part;
         a.pair = pair;
-        return run_q4k(a, x.st, pair_left);
+        return x.c->weight_fmt == DFLASH_W_Q4K ? run_q4k(a, x.st, pair_left)
+                                               : run_q8(a, x.st, pair_left);
     }
     Bf16GemmArgs a = {};
     for (int i = 0; i < 3; i++) {
@@ -481,6 +515,55 @@ int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
     if (splits < 0) return splits;
     HIPCHK(launch_reduce_epilogue(a.part, splits, M, N, 0, EPI_STORE_BF16, nullptr, y, nullptr, N,
                                   RowScale{}, st));
+    return DFLASH_OK;
+}
+
+size_t q8_0_gemm_workspace_bytes(int M, int N, int K) {
+    if (M < 1 || M > 4096 || N < 16 || N % 16 || K < 256 || K % 256) return 0;
+    return gemm_part_bytes(DFLASH_W_Q8_0, M, N, K);
+}
+
+int q8_0_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
+              void *workspace, size_t ws_bytes, void *stream) {
+    if (!w || !x || !y) return DFLASH_EINVAL;
+    if (M < 1 || M > 4096 || N < 16 || N % 16 || K < 256 || K % 256) return DFLASH_ESHAPE;
+    if (!aligned16(w) || !aligned16(x) || !aligned16(y)) return DFLASH_EALIGN;
+    const size_t need = q8_0_gemm_workspace_bytes(M, N, K);
+    if (!workspace || ws_bytes < need || !aligned16(workspace)) return DFLASH_EWORKSPACE;
+    const hipStream_t st = (hipStream_t)stream;
+    Q4kFusedArgs a;
+    a.w[0] = a.w[1] = a.w[2] = (const unsigned char *)w;
+    a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = N;
+    a.nseg = 1;
+    a.M = M; a.N = N; a.KB = K / 256;
+    a.src.A = x;
+    a.src.lda = K;
+    a.part = (float *)workspace;
+    a.pair = 0;
+    int pair_left;
+    const int splits = run_q8(a, st, &pair_left);
+    if (splits < 0) return splits;
+    HIPCHK(launch_reduce_epilogue(a.part, splits, M, N, 0, EPI_STORE_BF16, nullptr, y, nullptr, N,
+                                  RowScale{}, st));
+    return DFLASH_OK;
+}
+
+int q8_0_to_tiled(const void *src, void *dst, int N, int K, void *stream) {
+    if (!src || !dst) return DFLASH_EINVAL;
+    if (N < 16 || N % 16 || K < 256 || K % 256) return DFLASH_ESHAPE;
+    if (!aligned16(src) || !aligned16(dst)) return DFLASH_EALIGN;
+    const size_t bytes = (size_t)N * (K / 32) * Q8_BLOCK_BYTES;
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return DFLASH_EINVAL;      // overlap
+    HIPCHK(launch_q8_0_to_tiled((const unsigned char *)src, (unsigned char *)dst, N, K / 256,
+                                (hipStream_t)stream));
+    return DFLASH_OK;
+}
+
+int q8_0_dequantize(const void *w, float *out, long long n_blocks, void *stream) {
+    if (!w || !out || n_blocks < 1) return DFLASH_EINVAL;
+    if (!aligned16(w) || !aligned16(out)) return DFLASH_EALIGN;
+    HIPCHK(launch_q8_0_dequant(w, out, n_blocks, (hipStream_t)stream));
     return DFLASH_OK;
 }
 

@@ -19,7 +19,7 @@ hipError_t launch_q4k_to_tiled(const unsigned char *src, unsigned char *dst, int
 
 // ---------------------------------------------------------------- bf16 GEMMs
 struct Bf16GemmArgs {
-    const uint16_t *w[3];        // bf16 weights [N_seg][K], stacked along N
+    const uint16_t *w[3];        // bf16 weights [N_seg][K] (wfmt 1: Q8_0 tiled bytes), stacked along N
     int seg_end[3];
     int nseg;
     const uint16_t *A;           // bf16 [M][lda]
@@ -28,6 +28,7 @@ struct Bf16GemmArgs {
     float *C;                    // fp32 [M][ldc]
     int ldc;
     RowScale rs;                 // output row r multiplied by row_inv(rs, r) (ssq null: none)
+    int wfmt;                    // 0: bf16 weights; 1: Q8_0 in the tiled layout (tiled GEMM only)
 };
 // tiled 128x128 MFMA GEMM, any M
 hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st);
@@ -185,3 +186,21 @@ hipError_t launch_reduce_norm(const float *part, int splits, int M_out, int N, i
 // the reduction and the block assembly (independent) as one launch
 hipError_t launch_reduce_norm_embed(const ReduceRowsArgs &a, const EmbedArgs &e, int B,
                                     hipStream_t st);
+
+// ---------------------------------------------------------------- Q8_0
+// Row-major Q8_0 (34-byte blocks of 32 weights: fp16 d, 32 signed bytes) and the
+// tiled layout the GEMM kernels read: unit (t, g) of 4352 bytes at (t K/256 + g) 4352
+// holds the 8 block scales of rows 16 t .. 16 t + 15 (16 bytes each), then per block
+// pair p < 4 the 16-byte slots 16 h + r: bytes 8 h .. 8 h + 7 of block 8 g + 2 p of
+// row r, then of block 8 g + 2 p + 1.
+constexpr int Q8_BLOCK_BYTES = 34;
+constexpr int Q8_UNIT_BYTES = 4352;
+hipError_t launch_q8_0_dequant(const void *w, float *out, long long n_blocks, hipStream_t st);
+hipError_t launch_q8_0_to_tiled(const unsigned char *src, unsigned char *dst, int N, int G,
+                                hipStream_t st);
+// streaming GEMM for M <= 16 rows, K a multiple of 1024 (splits of 4 K-groups), the same
+// plan fields and partial layout as the Q4_K streaming kernel (a.KB = K / 256)
+bool q8_stream_ok(int M, int N, int K);
+Q4kStreamPlan q8_stream_plan(int M, int N, int K, int pair = 0, int target_waves = 2048,
+                             int wpg = 0);
+hipError_t launch_q8_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st);

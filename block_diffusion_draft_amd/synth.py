@@ -212,6 +212,11 @@ TINY = Shape(n_layers=1, hidden=256, ffn=768, n_q=4, n_kv=2, head_dim=64, window
 FULL = Shape(n_layers=5, hidden=5120, ffn=17408, n_q=32, n_kv=8, head_dim=128, window=2048,
              vocab=248320, top_k=16, sel_rank=256)
 FULL_BF16 = dataclasses.replace(FULL, weight_fmt="bf16")
+FULL_Q8_0 = dataclasses.replace(FULL, weight_fmt="q8_0")
+# a mid-size drafter whose every product has K a multiple of 1024 (the 16-row Q8_0
+# streaming kernel's split), small enough for the oracle in seconds
+MID = Shape(n_layers=2, hidden=1024, ffn=2048, n_q=8, n_kv=2, head_dim=128, window=64,
+            vocab=8192, top_k=16, sel_rank=64)
 
 WORKLOADS = {
     "tiny": Workload("tiny-1L-h256-v4096-ctx48", TINY, batch=1, ctx_len=48, t_new=8, seed=0),
@@ -221,6 +226,8 @@ WORKLOADS = {
                          ctx_len=32768, t_new=8, seed=4),
     "full_b64_bf16": Workload("dflash2-27b-draft-bf16-b64-ctx8192", FULL_BF16, batch=64,
                               ctx_len=8192, t_new=8, seed=5),
+    "full_b1_q8_0": Workload("dflash2-27b-draft-q8_0-b1-ctx4096", FULL_Q8_0, batch=1,
+                             ctx_len=4096, t_new=8, seed=6),
 }
 
 # the drafter's matrix shapes (name, N out, K in) at M = 8 activation rows

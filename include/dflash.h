@@ -22,6 +22,10 @@
  *   q4k_gemm             y = x . W^T with W in Q4_K super-blocks (the format of
  *                        the draft's fc, q/k/v/o and MLP matrices: same card,
  *                        "Weights" row), fp32 accumulation, bf16 output.
+ *   q8_0_gemm            the same product with W in Q8_0 blocks (the pages' second
+ *                        quantised draft file: Mindket kit page "Qwen3.8-27B-DFlash2-
+ *                        GGUF by z-lab", draft-file table); q8_0_to_tiled and
+ *                        q8_0_dequantize as for Q4_K.
  *   q4k_to_tiled         regroups a row-major Q4_K matrix into the tiled device
  *                        layout every Q4_K entry point above reads (done once, when
  *                        the weights are loaded).
@@ -70,7 +74,7 @@ typedef enum {
     DFLASH_EHIP = -5          /* a HIP call failed */
 } dflash_status;
 
-typedef enum { DFLASH_W_Q4K = 0, DFLASH_W_BF16 = 1 } dflash_weight_fmt;
+typedef enum { DFLASH_W_Q4K = 0, DFLASH_W_BF16 = 1, DFLASH_W_Q8_0 = 2 } dflash_weight_fmt;
 
 /* Drafter shape.  The 27B draft: 5 layers, hidden 5120, FFN 17408, 32 query and
  * 8 KV heads of 128, window 2048, vocab 248320, 5 taps, block 8, top 16, rank
@@ -237,6 +241,38 @@ int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
  * dst device pointers, 16-byte aligned, not overlapping.  Enqueued on `stream`.
  */
 int q4k_to_tiled(const void *src, void *dst, int N, int K, void *stream);
+
+/*
+ * Q8_0 (Mindket kit page "Qwen3.8-27B-DFlash2-GGUF by z-lab": the draft-file table lists
+ * a Q8_0 file; the bytes are the GGUF Q8_0 block): 34 bytes per 32 consecutive weights
+ * of a row, fp16 scale d (little endian) then 32 signed bytes q; w = d q.  A row-major
+ * matrix [N][K] is N rows of K/32 blocks.  With weight_fmt DFLASH_W_Q8_0 the draft
+ * step's fc, q/k/v/o and MLP matrices are Q8_0 in the tiled layout below.
+ *
+ * q8_0_to_tiled: src row-major Q8_0 [N][K] -> dst (same size, N K / 32 * 34 bytes): for
+ * every 16-row tile t and 256-wide K-group g one 4352-byte unit at (t K/256 + g) 4352:
+ *   bytes [0, 256): the 8 block scales of row 16 t + r (fp16, block order) at 16 r;
+ *   bytes 256 + 1024 p + 16 (16 h + r) .. + 15 (p, h < 4, r < 16): quant bytes
+ *   8 h .. 8 h + 7 of block 8 g + 2 p of row 16 t + r, then of block 8 g + 2 p + 1.
+ * Every byte is copied, none changed.  N % 16 == 0, K % 256 == 0, both > 0; device
+ * pointers, 16-byte aligned, not overlapping.
+ */
+int q8_0_to_tiled(const void *src, void *dst, int N, int K, void *stream);
+
+/* Workspace bytes q8_0_gemm needs for an M x N x K product. */
+size_t q8_0_gemm_workspace_bytes(int M, int N, int K);
+
+/*
+ * y[M][N] (bf16) = x[M][K] (bf16) . W^T, W [N][K] in Q8_0 (tiled layout), fp32
+ * accumulation.  Up to 16 rows with K % 1024 == 0 the products d q are exact; otherwise
+ * each decoded weight is rounded to bf16 before the MFMA (relative error <= 2^-9).
+ * K % 256 == 0, N % 16 == 0, 1 <= M <= 4096.  w, x, y and workspace 16-byte aligned.
+ */
+int q8_0_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
+              void *workspace, size_t ws_bytes, void *stream);
+
+/* Decode n_blocks consecutive row-major Q8_0 blocks to fp32 (32 values each, exact). */
+int q8_0_dequantize(const void *w, float *out, long long n_blocks, void *stream);
 
 /* Decode n_blocks consecutive row-major Q4_K super-blocks to fp32 (256 values each). */
 int q4k_dequantize(const void *w, float *out, long long n_blocks, void *stream);

@@ -24,6 +24,7 @@ def test_header_declares_the_boundary():
     for n in ("dflash_draft_step", "dflash_verify_prefix", "dflash_verify_sampled",
               "dflash_verify_sampled_workspace_bytes", "q4k_gemm", "q4k_to_tiled",
               "q4k_dequantize", "dflash_workspace_bytes", "q4k_gemm_workspace_bytes",
+              "q8_0_gemm", "q8_0_gemm_workspace_bytes", "q8_0_to_tiled", "q8_0_dequantize",
               "dflash_status_str"):
         assert n in names
     assert sorted(binding.EXPORTS) == names
@@ -80,6 +81,10 @@ def call_step(cfg, w, batch=1, t_new=8, taps=FAKE, ws=FAKE, ws_bytes=1 << 40, ca
                                None, None, ws, ws_bytes, None, None)
 
 
+def L_ok(cfg):
+    return binding.lib().dflash_workspace_bytes(ctypes.byref(cfg), 1, 8) > 0
+
+
 def test_draft_step_rejects_bad_arguments_before_launch():
     cfg = tiny_cfg()
     w = fake_weights(cfg)
@@ -98,6 +103,7 @@ def test_draft_step_rejects_bad_arguments_before_launch():
     assert call_step(tiny_cfg(hidden=200), w) == -2
     assert call_step(tiny_cfg(sel_rank=48), w) == -2
     assert call_step(tiny_cfg(weight_fmt=7), w) == -1
+    assert L_ok(tiny_cfg(weight_fmt=2))                      # Q8_0 is a supported format
     assert call_step(cfg, w, taps=FAKE + 2) == -3           # EALIGN
     assert call_step(cfg, w, ws=None) == -4                 # EWORKSPACE
     assert call_step(cfg, w, ws_bytes=16) == -4
@@ -124,6 +130,27 @@ def test_q4k_gemm_and_verify_reject_bad_arguments():
     assert L.q4k_to_tiled(FAKE, FAKE + (1 << 30), 16, 300, None) == -2
     assert L.q4k_to_tiled(FAKE + 8, FAKE + (1 << 30), 16, 256, None) == -3
     assert L.q4k_to_tiled(FAKE, FAKE + 1024, 16, 256, None) == -1   # overlapping buffers
+
+
+def test_q8_0_entries_reject_bad_arguments():
+    L = binding.lib()
+    assert L.q8_0_gemm(FAKE, FAKE, FAKE, 8, 5120, 5000, FAKE, 1 << 40, None) == -2
+    assert L.q8_0_gemm(FAKE, FAKE, FAKE, 8, 5121, 5120, FAKE, 1 << 40, None) == -2
+    assert L.q8_0_gemm(FAKE, FAKE, FAKE, 0, 5120, 5120, FAKE, 1 << 40, None) == -2
+    assert L.q8_0_gemm(FAKE, FAKE, FAKE, 4097, 5120, 5120, FAKE, 1 << 40, None) == -2
+    assert L.q8_0_gemm(FAKE + 4, FAKE, FAKE, 8, 5120, 5120, FAKE, 1 << 40, None) == -3
+    assert L.q8_0_gemm(FAKE, FAKE, FAKE, 8, 5120, 5120, FAKE, 16, None) == -4
+    assert L.q8_0_gemm(None, FAKE, FAKE, 8, 5120, 5120, FAKE, 1 << 40, None) == -1
+    assert L.q8_0_gemm_workspace_bytes(8, 5120, 25600) > 0
+    assert L.q8_0_gemm_workspace_bytes(300, 5120, 1280) == 300 * 5120 * 4   # tiled: one split
+    assert L.q8_0_gemm_workspace_bytes(8, 5120, 100) == 0
+    assert L.q8_0_dequantize(FAKE, FAKE, 0, None) == -1
+    assert L.q8_0_dequantize(FAKE + 2, FAKE, 1, None) == -3
+    assert L.q8_0_to_tiled(None, FAKE, 16, 256, None) == -1
+    assert L.q8_0_to_tiled(FAKE, FAKE + (1 << 30), 24, 256, None) == -2
+    assert L.q8_0_to_tiled(FAKE, FAKE + (1 << 30), 16, 288, None) == -2
+    assert L.q8_0_to_tiled(FAKE + 8, FAKE + (1 << 30), 16, 256, None) == -3
+    assert L.q8_0_to_tiled(FAKE, FAKE + 1024, 16, 256, None) == -1   # overlapping buffers
 
 
 def call_sampled(draft=FAKE, logits=FAKE, u=FAKE, batch=2, n=7, vocab=4096, T=1.0, k=20, p=0.95,
