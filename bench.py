@@ -5,7 +5,8 @@ resident in HBM: dflash_draft_step (tap fusion, 5 drafter layers, shared output
 head with top-16, Viterbi selector) followed by dflash_verify_prefix.  The
 workload is the pages' 27B-draft shape at batch 1 with a 4096-row context.
 
-With --accept sampled the acceptance is dflash_verify_sampled instead (rejection
+With --weights q8_0 the drafter's matrices are Q8_0 instead of Q4_K (same shapes,
+same seed recipe).  With --accept sampled the acceptance is dflash_verify_sampled instead (rejection
 sampling against synthetic fp32 target logits [1][8][248320] resident in HBM, at the
 pages' sampler settings).
 
@@ -95,6 +96,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
+    ap.add_argument("--weights", choices=("q4k", "q8_0"), default="q4k",
+                    help="drafter weight format: Q4_K (the default) or Q8_0")
     ap.add_argument("--accept", choices=("greedy", "sampled"), default="greedy",
                     help="acceptance after the draft: greedy prefix (the default), or "
                          "rejection sampling against fp32 target logits [B][8][V] at "
@@ -112,7 +115,7 @@ def main():
     import torch
     from block_diffusion_draft_amd import binding, runner, synth
 
-    wl = synth.WORKLOADS[WORKLOAD]
+    wl = synth.WORKLOADS[WORKLOAD if args.weights == "q4k" else "full_b1_q8_0"]
     s = wl.shape
     print(f"[bench] preparing {wl.name}", file=sys.stderr, flush=True)
     bufs = runner.StepBuffers(wl, dbg=False)
@@ -237,7 +240,7 @@ def step_algorithmic_bytes(wl):
     qd, kd = s.n_q * s.head_dim, s.n_kv * s.head_dim
     lin = s.n_taps * s.hidden * s.hidden + s.n_layers * (
         qd * s.hidden + 2 * kd * s.hidden + s.hidden * qd + 3 * s.ffn * s.hidden)
-    wbytes = lin * 144 // 256 if s.weight_fmt == "q4k" else lin * 2
+    wbytes = {"q4k": lin * 144 // 256, "q8_0": lin * 34 // 32}.get(s.weight_fmt, lin * 2)
     small = s.n_layers * (2 * s.hidden + 2 * s.head_dim + 2 * s.n_q * qd) * 2 + 3 * s.hidden * 2
     head = s.vocab * s.hidden * 2
     win = min(s.window, wl.ctx_len + wl.t_new)
