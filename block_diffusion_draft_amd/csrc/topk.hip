@@ -6,21 +6,23 @@
 // position (section "How it is used").  Candidates are ordered by (logit desc,
 // token id asc); cand_logp = logit - logsumexp(logits).
 //
-// Threshold selection, four short passes per row of V fp32 logits:
-//  1. wave per 1024-logit chunk: the chunk's max and sum of exp(logit - max);
-//  2. wave per row: logsumexp, and theta = the K-th largest of the 64 lanes' maxima
-//     of the chunk maxima (a wave sort).  Those K maxima are K distinct logits, so
-//     the row's K-th largest logit is >= theta: every top-K candidate is >= theta;
-//  3. wave per chunk: every logit >= theta is appended to the row's candidate list
-//     (an integer atomic hands out slots; the order of the list does not matter);
-//  4. wave per row: the K best candidates by (value desc, id asc): a wave sort when
-//     at most 64 reached theta, else K rounds of arg-max.  If more than CAP logits
-//     reach theta (many equal logits), the row is selected by an exact scan of all
-//     its chunks instead.
+// Threshold selection, three short passes per row of V fp32 logits:
+//  1. wave per 1024-logit chunk: the chunk's max and sum of exp(logit - max) (and the
+//     row's candidate count reset);
+//  2. wave per chunk: theta = the K-th largest of the 64 lane maxima of the row's chunk
+//     maxima (a wave sort; each lane maximum is a distinct logit, so K logits are
+//     >= theta and every top-K candidate is >= theta), then every logit >= theta of
+//     the chunk is appended to the row's candidate list (an integer atomic hands out
+//     slots; the order of the list does not matter);
+//     (the row's first wave also forms its logsumexp from the chunk statistics);
+//  3. wave per row: the K best candidates by
+//     (value desc, id asc): a wave sort when at most 64 reached theta, else K rounds
+//     of arg-max.  If more than CAP logits reach theta (many equal logits), the row is
+//     selected by an exact scan of all its chunks instead.
 // Every choice is an arg-max under a total order, so the result is exact and does
 // not depend on thread scheduling.  K <= 64 (the threshold is a lane maximum).
 //
-// Pass 4 runs inside the selector's workgroup (one per sequence): its waves select the
+// Pass 3 runs inside the selector's workgroup (one per sequence): its waves select the
 // sequence's rows, then the candidate-path search runs on them.  Selector (same card,
 // spec table "Draft" row: candidate selector, top 16, rank 256; "Weights" row: two
 // 248320 x 256 codebooks; "How it is used": one coherent path through the top 16
@@ -34,9 +36,9 @@
 namespace {
 
 constexpr int PER_LANE = 16;
-constexpr int CHUNK = 64 * PER_LANE;     // logits per wave in passes 1 and 3
+constexpr int CHUNK = 64 * PER_LANE;     // logits per wave in passes 1 and 2
 constexpr int CAP = 1024;                // candidate slots per row
-constexpr int CPL = CAP / 64;            // candidates per lane in pass 4
+constexpr int CPL = CAP / 64;            // candidates per lane in pass 3
 
 __device__ __forceinline__ bool take(float v, int i, float bv, int bi) {
     return i >= 0 && (bi < 0 || cand_better(v, i, bv, bi));
@@ -83,10 +85,11 @@ __device__ __forceinline__ Key wave_sort_desc(Key x) {
 
 // 1. chunk max and sum of exp(logit - max)
 __global__ __launch_bounds__(256) void k_chunk_stats(const float *logits, int V, int nch, float *pm,
-                                                     float *ps) {
+                                                     float *ps, int *count) {
     const int lane = threadIdx.x & 63;
     const int c = blockIdx.x * 4 + (threadIdx.x >> 6), r = blockIdx.y;
     if (c >= nch) return;
+    if (c == 0 && lane == 0) count[r] = 0;
     const float *row = logits + (size_t)r * V + (size_t)c * CHUNK;
     const int n = min(CHUNK, V - c * CHUNK);
     float val[PER_LANE];
@@ -108,54 +111,59 @@ __global__ __launch_bounds__(256) void k_chunk_stats(const float *logits, int V,
     }
 }
 
-// 2. one wave per row: logsumexp and the threshold; resets the row's candidate count
-__global__ __launch_bounds__(64) void k_row_threshold(const float *pm, const float *ps, int nch, int K,
-                                                      float *thr, float *lse, int *count) {
-    const int r = blockIdx.x, lane = threadIdx.x;
-    float m[PER_LANE], s[PER_LANE];
-    float mx = -INFINITY;
+// theta of row r: the K-th largest of the 64 lane maxima of its chunk maxima; with
+// lse non-null (one wave per row) also the row's logsumexp from its chunk statistics
+__device__ __forceinline__ float row_theta(const float *pm, const float *ps, int nch, int K, int r,
+                                           float *lse) {
+    const int lane = threadIdx.x & 63;
+    float m[PER_LANE];
+    float lm = -INFINITY;
 #pragma unroll
     for (int k = 0; k < PER_LANE; k++) {
         const int c = lane + 64 * k;
         m[k] = c < nch ? pm[(size_t)r * nch + c] : -INFINITY;
-        s[k] = c < nch ? ps[(size_t)r * nch + c] : 0.f;
-        mx = fmaxf(mx, m[k]);
+        lm = fmaxf(lm, m[k]);
     }
-    mx = wave_max(mx);
-    float se = 0.f;
+    if (lse) {
+        float sm[PER_LANE];
 #pragma unroll
-    for (int k = 0; k < PER_LANE; k++) se += m[k] == -INFINITY ? 0.f : s[k] * expf(m[k] - mx);
-    se = wave_sum(se);
-    // theta = the K-th largest of the 64 lane maxima (each lane maximum is a chunk
-    // maximum, i.e. a distinct logit, so K logits are >= theta)
-    float lm = -INFINITY;
+        for (int k = 0; k < PER_LANE; k++) {
+            const int c = lane + 64 * k;
+            sm[k] = c < nch ? ps[(size_t)r * nch + c] : 0.f;
+        }
+        const float mx = wave_max(lm);
+        float se = 0.f;
 #pragma unroll
-    for (int k = 0; k < PER_LANE; k++) lm = fmaxf(lm, m[k]);
+        for (int k = 0; k < PER_LANE; k++) se += m[k] == -INFINITY ? 0.f : sm[k] * expf(m[k] - mx);
+        se = wave_sum(se);
+        if (lane == 0) lse[r] = mx + logf(se);
+    }
     const float sorted = wave_sort_desc(lm);
-    const float th = __shfl(sorted, K - 1, WAVE);
-    if (lane == 0) {
-        thr[r] = th;
-        lse[r] = mx + logf(se);
-        count[r] = 0;
-    }
+    return __shfl(sorted, K - 1, WAVE);
 }
 
-// 3. wave per chunk: append the logits >= theta to the row's candidate list
-__global__ __launch_bounds__(256) void k_collect(const float *logits, int V, int nch, const float *thr,
+// 2. wave per chunk: the row's theta (and, in the row's first wave, its logsumexp), then
+// append the chunk's logits >= theta to the row's candidate list
+__global__ __launch_bounds__(256) void k_collect(const float *logits, int V, int nch, int K,
+                                                 const float *pm, const float *ps, float *lse,
                                                  int *count, float *cv, int32_t *ci) {
     const int lane = threadIdx.x & 63;
     const int c = blockIdx.x * 4 + (threadIdx.x >> 6), r = blockIdx.y;
     if (c >= nch) return;
-    const float th = thr[r];
     const float *row = logits + (size_t)r * V + (size_t)c * CHUNK;
     const int n = min(CHUNK, V - c * CHUNK);
     float val[PER_LANE];
+#pragma unroll
+    for (int k = 0; k < PER_LANE; k++) {
+        const int i = lane + 64 * k;
+        val[k] = i < n ? row[i] : -INFINITY;
+    }
+    const float th = row_theta(pm, ps, nch, K, r, c == 0 ? lse : nullptr);   // loads overlap
     unsigned long long mask[PER_LANE];
     int total = 0;
 #pragma unroll
     for (int k = 0; k < PER_LANE; k++) {
         const int i = lane + 64 * k;
-        val[k] = i < n ? row[i] : -INFINITY;
         mask[k] = __ballot(i < n && val[k] >= th);
         total += __popcll(mask[k]);
     }
@@ -178,13 +186,11 @@ __global__ __launch_bounds__(256) void k_collect(const float *logits, int V, int
     }
 }
 
-// 4. one wave, row r: exact top-K of the candidates (or of the whole row on overflow)
-// into sid[k], slp[k] = logit - lse[r] (k < K; LDS of the calling workgroup)
+// 3. one wave, row r: exact top-K of the candidates (or of the whole row on overflow)
+// into sid[k], slp[k] = logit - L (k < K; LDS of the calling workgroup)
 __device__ void select_row(const float *logits, int V, int nch, int K, int r, const int *count,
-                           const float *cv, const int32_t *ci, const float *lse, int *sid,
-                           float *slp) {
+                           const float *cv, const int32_t *ci, float L, int *sid, float *slp) {
     const int lane = threadIdx.x & 63;
-    const float L = lse ? lse[r] : 0.f;             // null: the raw logits
     const int n = count[r];
     if (n <= 64) {
         // one candidate per lane: sort the wave, the first K lanes are the answer
@@ -267,7 +273,7 @@ constexpr int MAXK = 16;
 constexpr int MAXP = 16;
 constexpr int PATH_WAVES = 8;
 
-// One workgroup (8 waves) per sequence.  Waves select the sequence's P rows (pass 4)
+// One workgroup (8 waves) per sequence.  Waves select the sequence's P rows (pass 3)
 // into LDS and the outputs.  The pair scores of adjacent positions are K x K products of
 // gathered codebook rows, T_t = s A[ids_t] B[ids_{t+1}]^T, computed as 16x16xr MFMA
 // tiles (exact bf16 products, fp32 accumulation) straight from the gathered rows: lane
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(64 * PATH_WAVES) void k_select_path(
     const bool ok = valid[b] != 0;
     for (int t = wave; t < P; t += PATH_WAVES) {
         const int row = b * P + t;
-        if (ok) select_row(logits, V, nch, K, row, count, cv, ci, lse, ids[t], lp[t]);
+        if (ok) select_row(logits, V, nch, K, row, count, cv, ci, lse[row], ids[t], lp[t]);
         if (lane < MAXK && (lane >= K || !ok)) {
             ids[t][lane] = -1;
             lp[t][lane] = -INFINITY;
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(64 * SAMPLE_WAVES) void k_sample_accept(
     const int b = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rows = n + 1;
     for (int j = wave; j < rows; j += SAMPLE_WAVES)
-        select_row(logits, V, nch, K, b * rows + j, count, cv, ci, nullptr, sid[j], sv[j]);
+        select_row(logits, V, nch, K, b * rows + j, count, cv, ci, 0.f, sid[j], sv[j]);
     __syncthreads();
     if (wave != 0) return;
     const float *ub = u + (size_t)b * rows * 2;
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(64 * SAMPLE_WAVES) void k_sample_accept(
 
 size_t topk_workspace_floats(int R, int V) {
     const int nch = ceil_div(V, CHUNK);
-    return (size_t)R * (2 * nch + 3 + 2 * CAP);
+    return (size_t)R * (2 * nch + 2 + 2 * CAP);
 }
 
 hipError_t launch_topk_path(const float *logits, int B, int P, int V, int K, const int32_t *valid,
@@ -467,14 +473,14 @@ hipError_t launch_topk_path(const float *logits, int B, int P, int V, int K, con
     if (P > MAXP || K > MAXK) return hipErrorInvalidValue;
     const int R = B * P;
     const int nch = ceil_div(V, CHUNK);
-    float *pm = ws, *ps = pm + (size_t)R * nch, *thr = ps + (size_t)R * nch, *lse = thr + R;
+    float *pm = ws, *ps = pm + (size_t)R * nch, *lse = ps + (size_t)R * nch;
     int *count = reinterpret_cast<int *>(lse + R);
     float *cv = reinterpret_cast<float *>(count + R);
     int32_t *ci = reinterpret_cast<int32_t *>(cv + (size_t)R * CAP);
     const dim3 grid(ceil_div(nch, 4), R);
-    hipLaunchKernelGGL(k_chunk_stats, grid, dim3(256), 0, st, logits, V, nch, pm, ps);
-    hipLaunchKernelGGL(k_row_threshold, dim3(R), dim3(64), 0, st, pm, ps, nch, K, thr, lse, count);
-    hipLaunchKernelGGL(k_collect, grid, dim3(256), 0, st, logits, V, nch, thr, count, cv, ci);
+    hipLaunchKernelGGL(k_chunk_stats, grid, dim3(256), 0, st, logits, V, nch, pm, ps, count);
+    hipLaunchKernelGGL(k_collect, grid, dim3(256), 0, st, logits, V, nch, K, pm, ps, lse, count, cv,
+                       ci);
     hipLaunchKernelGGL(k_select_path, dim3(B), dim3(64 * PATH_WAVES), 0, st, logits, V, nch, K, count,
                        cv, ci, lse, P, valid, code_a, code_b, r, pair_scale, cand_ids, cand_logp,
                        draft_tokens);
@@ -487,14 +493,14 @@ hipError_t launch_topk_sample(const float *logits, int B, int n, int V, int K, f
     if (n + 1 > SAMPLE_MAXROWS || K > SAMPLE_MAXK || K > V) return hipErrorInvalidValue;
     const int R = B * (n + 1);
     const int nch = ceil_div(V, CHUNK);
-    float *pm = ws, *ps = pm + (size_t)R * nch, *thr = ps + (size_t)R * nch, *lse = thr + R;
+    float *pm = ws, *ps = pm + (size_t)R * nch, *lse = ps + (size_t)R * nch;
     int *count = reinterpret_cast<int *>(lse + R);
     float *cv = reinterpret_cast<float *>(count + R);
     int32_t *ci = reinterpret_cast<int32_t *>(cv + (size_t)R * CAP);
     const dim3 grid(ceil_div(nch, 4), R);
-    hipLaunchKernelGGL(k_chunk_stats, grid, dim3(256), 0, st, logits, V, nch, pm, ps);
-    hipLaunchKernelGGL(k_row_threshold, dim3(R), dim3(64), 0, st, pm, ps, nch, K, thr, lse, count);
-    hipLaunchKernelGGL(k_collect, grid, dim3(256), 0, st, logits, V, nch, thr, count, cv, ci);
+    hipLaunchKernelGGL(k_chunk_stats, grid, dim3(256), 0, st, logits, V, nch, pm, ps, count);
+    hipLaunchKernelGGL(k_collect, grid, dim3(256), 0, st, logits, V, nch, K, pm, ps, nullptr, count,
+                       cv, ci);
     hipLaunchKernelGGL(k_sample_accept, dim3(B), dim3(64 * SAMPLE_WAVES), 0, st, logits, V, nch, K,
                        count, cv, ci, draft, u, n, temperature, top_p, accept_len, out_tokens);
     return hipGetLastError();

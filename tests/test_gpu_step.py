@@ -208,3 +208,23 @@ def test_tiny_step_block_lengths(block, batch):
     g = full_check(wl, bufs, ref)
     assert g["draft"].shape == (batch, block - 1)
     check_verify(bufs, g)
+
+
+@pytest.mark.parametrize("fmt,head_dim,batch", [("q4k", 128, 1), ("q4k", 128, 2), ("q4k", 64, 1),
+                                                ("q8_0", 64, 2)])
+def test_mid_step_streaming_products(fmt, head_dim, batch):
+    """A 2-layer drafter (hidden 1024) whose products all have K a multiple of 1024, so
+    at 8 and 16 rows they run on the 16-row streaming kernels (Q4_K and Q8_0), with the
+    (hi, lo) pair added in-kernel; heads of 128 and of 64."""
+    n_q = 1024 // head_dim
+    s = dataclasses.replace(synth.MID, weight_fmt=fmt, head_dim=head_dim, n_q=n_q,
+                            n_kv=n_q // 4)
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], shape=s, batch=batch, ctx_len=96,
+                             seed=50 + batch + head_dim)
+    say(f"[step] mid {fmt} head_dim {head_dim} batch {batch}")
+    bufs = runner.StepBuffers(wl)
+    bufs.step()
+    torch.cuda.synchronize()
+    ref = parity.run_oracle(wl, bufs.host_W, bufs.inputs)
+    g = full_check(wl, bufs, ref)
+    check_verify(bufs, g)
