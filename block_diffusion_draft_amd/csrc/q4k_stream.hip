@@ -22,7 +22,8 @@
 // Work split: a workgroup (8 waves) owns one split of 4 super-blocks (1024 values
 // of K) and one run of tpw consecutive 16-column tiles per wave.  The split's
 // activation rows are staged once in LDS in MFMA lane order; their sub-block sums
-// come from MFMAs against a ones operand.  Each wave then streams its tiles'
+// come from the staging lanes (a sum of 8 and two lane exchanges), and each lane keeps
+// the bias operands it needs in registers.  Each wave then streams its tiles'
 // super-blocks as one flat sequence of (tile, super-block) stages, 4 stages in
 // flight, in a branch-free loop (loads past the end are clamped to the last stage,
 // in bounds and unused), so the loads stay in flight across tiles.  The weights are
@@ -83,8 +84,7 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw
     constexpr int NT = 64 * WPG;                    // threads per workgroup
     extern __shared__ __align__(16) unsigned char lds[];
     u32x4_t *A_lds = reinterpret_cast<u32x4_t *>(lds);              // [SNSB][8][64]
-    u32x4_t *B_lds = A_lds + SNSB * 8 * 64;                          // [SNSB][64]
-    float *S_lds = reinterpret_cast<float *>(B_lds + SNSB * 64);     // [SNSB][8][16]
+    float *S_lds = reinterpret_cast<float *>(A_lds + SNSB * 8 * 64); // [SNSB][8][16]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -130,35 +130,35 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw
         st[1] = stage(b0, 1);
         st[2] = stage(b0, 2);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < PER; i++)
-            A_lds[(wave + WPG * i) * 64 + lane] = cl < a.M ? av[i] : (u32x4_t){0u, 0u, 0u, 0u};
-    }
-    __syncthreads();
-    // sub-block sums S[sbi][j][r]: MFMA of the entry with a ones operand (every
-    // column of the product is the row sum)
-    {
-        const uint32_t one2 = 0x3F803F80u;
-        const u32x4_t ones = {one2, one2, one2, one2};
+        // sub-block sums S[sbi][j][r] of the staged rows: each lane adds its 8 values
+        // (bf16 -> fp32 is exact), then the 4 lanes holding a row's sub-block add theirs
 #pragma unroll
         for (int i = 0; i < PER; i++) {
             const int e = wave + WPG * i;
-            const f32x4_t D = mfma16x16x32(A_lds[e * 64 + lane], ones, (f32x4_t){0.f, 0.f, 0.f, 0.f});
-            if (cl == 0) *reinterpret_cast<f32x4_t *>(&S_lds[e * 16 + 4 * g]) = D;
+            const u32x4_t v = cl < a.M ? av[i] : (u32x4_t){0u, 0u, 0u, 0u};
+            float sa = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; w++)
+                sa += __uint_as_float(v[w] << 16) + __uint_as_float(v[w] & 0xFFFF0000u);
+            sa += __shfl_xor(sa, 16, WAVE);
+            sa += __shfl_xor(sa, 32, WAVE);
+            if (g == 0) S_lds[e * 16 + cl] = sa;
+            A_lds[e * 64 + lane] = v;
         }
     }
     __syncthreads();
-    // bias A operand: lane (row r, group gg) holds S_a, S_b (a = 2 gg, b = 2 gg + 1) as
-    // three bf16 terms each, taken by truncation (each term keeps the top 8 significant
-    // bits of what is left, so three hold an fp32 significand exactly), interleaved:
-    // dword q = term q of S_a | term q of S_b << 16; dword 3 = 0
-    for (int e = tid; e < SNSB * 64; e += NT) {
-        const int sbi = e >> 6, ln = e & 63;
-        const int r = ln & 15, gg = ln >> 4;
+    // bias A operands of this lane (row r = cl, group gg = g), one per super-block of the
+    // split, kept in registers: S_a, S_b (a = 2 gg, b = 2 gg + 1) as three bf16 terms
+    // each, taken by truncation (each term keeps the top 8 significant bits of what is
+    // left, so three hold an fp32 significand exactly), interleaved: dword q = term q of
+    // S_a | term q of S_b << 16; dword 3 = 0
+    u32x4_t abias[SNSB];
+#pragma unroll
+    for (int sbi = 0; sbi < SNSB; sbi++) {
         uint32_t tb[2][3];
 #pragma unroll
         for (int jj = 0; jj < 2; jj++) {
-            float rem = S_lds[(sbi * 8 + 2 * gg + jj) * 16 + r];
+            float rem = S_lds[(sbi * 8 + 2 * g + jj) * 16 + cl];
 #pragma unroll
             for (int q = 0; q < 3; q++) {
                 const uint32_t tq = __float_as_uint(rem) & 0xFFFF0000u;
@@ -166,22 +166,21 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw
                 rem -= __uint_as_float(tq);
             }
         }
-        B_lds[e] = (u32x4_t){__builtin_amdgcn_perm(tb[1][0], tb[0][0], 0x07060302u),
-                             __builtin_amdgcn_perm(tb[1][1], tb[0][1], 0x07060302u),
-                             __builtin_amdgcn_perm(tb[1][2], tb[0][2], 0x07060302u), 0u};
+        abias[sbi] = (u32x4_t){__builtin_amdgcn_perm(tb[1][0], tb[0][0], 0x07060302u),
+                               __builtin_amdgcn_perm(tb[1][1], tb[0][1], 0x07060302u),
+                               __builtin_amdgcn_perm(tb[1][2], tb[0][2], 0x07060302u), 0u};
     }
-    __syncthreads();
 
     // ---- stream
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
     const int m_out = PX ? PX / 4 : a.M;            // rows of the partial written
     float *part = a.part + (size_t)split * m_out * a.N;
     const uint32_t bsel = 0x0C0C0000u | ((uint32_t)(2 * g + 1) << 8) | (uint32_t)(2 * g);
-    int a_off = lane, b_off = lane;
+    int a_off = lane;
     for (int t = t0; t < t1; t++) {
         // opaque to the compiler: keeps the 32 activation fragments in LDS instead of
         // hoisting them into registers (which would cost waves per SIMD)
-        asm volatile("" : "+v"(a_off), "+v"(b_off));
+        asm volatile("" : "+v"(a_off));
         const unsigned char *bcur = tile_base(t), *bnext = tile_base(t + 1);
         f32x4_t acc = zero;
 #pragma unroll
@@ -215,7 +214,7 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw
                 }
             }
             const uint32_t mb = bias_pair(m_lo, m_hi, bsel), cb = bias_pair(sc_lo, sc_hi, bsel);
-            const u32x4_t ab = B_lds[sb * 64 + b_off];
+            const u32x4_t ab = abias[sb];
             const f32x4_t Dm = mfma16x16x32(ab, (u32x4_t){mb, mb, mb, mb}, zero);
             const f32x4_t Ds = mfma16x16x32(ab, (u32x4_t){cb, cb, cb, cb}, zero);
             acc += d * (tacc - 128.f * Ds) - dmin * Dm;
@@ -253,7 +252,7 @@ Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int pair, int target_waves, i
     // the (hi, lo) halves of a pair sit pair / 4 lane groups = 4 pair lanes apart
     p.pair_done = (pair == 4 || pair == 8) && M == 2 * pair;
     p.px = p.pair_done ? 4 * pair : 0;
-    p.lds_bytes = (size_t)SNSB * 8 * 64 * 16 + SNSB * 64 * 16 + SNSB * 8 * 16 * 4;
+    p.lds_bytes = (size_t)SNSB * 8 * 64 * 16 + SNSB * 8 * 16 * 4;
     p.part_bytes = (size_t)p.splits * (p.pair_done ? pair : M) * N * 4;
     return p;
 }
