@@ -5,7 +5,9 @@ resident in HBM: dflash_draft_step (tap fusion, 5 drafter layers, shared output
 head with top-16, Viterbi selector) followed by dflash_verify_prefix.  The
 workload is the pages' 27B-draft shape at batch 1 with a 4096-row context.
 
-With --weights q8_0 the drafter's matrices are Q8_0 instead of Q4_K (same shapes,
+--workload full_b16 / full_b64_bf16 measure the pages' batched draft steps instead (16
+sequences with 32768-row contexts and Q4_K weights; 64 with 8192 and bf16 weights); the
+default stays the batch-1 workload.  With --weights q8_0 the drafter's matrices are Q8_0 instead of Q4_K (same shapes,
 same seed recipe).  With --accept sampled the acceptance is dflash_verify_sampled instead (rejection
 sampling against synthetic fp32 target logits [1][8][248320] resident in HBM, at the
 pages' sampler settings).
@@ -28,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-WORKLOAD = "full_b1"
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def kernel_source_hash():
@@ -55,16 +57,29 @@ def load_traffic():
     return float(kv["hbm_bytes_per_launch"])
 
 
+def first_sequence(inp):
+    """The inputs of sequence 0 only (sequences are independent)."""
+    from block_diffusion_draft_amd import synth
+    out = {k: inp[k][:1] for k in ("taps", "last_token", "ctx_len")}
+    for c in ("k_cache", "v_cache"):
+        v = inp[c]
+        out[c] = v[:, :1] if isinstance(v, np.ndarray) else \
+            synth.WindowCache(v.rows[:1], v.lo[:1], v.shape)
+    return out
+
+
 def cpu_baseline(wl, bufs, min_s=10.0):
     """The oracle as it stands, on this host: whole float64 draft steps of the same
     workload (tap fusion, every layer, the full output head with top-K, the
-    selector), repeated until at least min_s seconds of CPU work have run."""
+    selector), repeated until at least min_s seconds of CPU work have run.  For a
+    batch of several sequences the sample is sequence 0 alone (one block per step)."""
     from oracle import draft as od
     from oracle import select as osel
     from oracle.bf16 import bf16_to_f64
     s = wl.shape
     W = bufs.host_W
-    inp = bufs.inputs
+    inp = bufs.inputs if wl.batch == 1 else first_sequence(bufs.inputs)
+    nseq = 1
     # numpy's BLAS runs on OMP_NUM_THREADS threads (all available cores when unset)
     avail = len(os.sched_getaffinity(0))
     threads = min(avail, int(os.environ.get("OMP_NUM_THREADS") or avail))
@@ -75,18 +90,19 @@ def cpu_baseline(wl, bufs, min_s=10.0):
     while True:
         out = od.draft_step(cfg, W, inp["taps"], inp["last_token"], inp["ctx_len"],
                             inp["k_cache"], inp["v_cache"], want_logits=False)
-        for b in range(wl.batch):
+        for b in range(nseq):
             T = osel.pair_scores(out["cand_ids"][b], A, B, s.pair_scale)
             osel.viterbi(out["cand_logp"][b], T)
         n += 1
         el = time.perf_counter() - t0
         if el >= min_s:
             break
-    return {"value": wl.batch * n / el, "unit": "draft blocks/s", "cores": threads,
+    what = (f"{n} whole {wl.name} steps" if wl.batch == 1 else
+            f"{n} steps of sequence 0 of {wl.name}")
+    return {"value": nseq * n / el, "unit": "draft blocks/s", "cores": threads,
             "kind": "oracle",
-            "sample": (f"{n} whole {wl.name} steps (batch {wl.batch}: tap fusion, "
-                       f"{s.n_layers} layers, full {s.vocab}-row output head with top-"
-                       f"{s.top_k}, selector) in {el:.1f} s")}
+            "sample": (f"{what} (batch 1: tap fusion, {s.n_layers} layers, full "
+                       f"{s.vocab}-row output head with top-{s.top_k}, selector) in {el:.1f} s")}
 
 
 def main():
@@ -98,6 +114,10 @@ def main():
     ap.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
     ap.add_argument("--weights", choices=("q4k", "q8_0"), default="q4k",
                     help="drafter weight format: Q4_K (the default) or Q8_0")
+    ap.add_argument("--workload", choices=("full_b1", "full_b16", "full_b64_bf16"),
+                    default="full_b1",
+                    help="the 27B-draft workload: 1 sequence with a 4096-row context (the "
+                         "default), 16 sequences with 32768 (Q4_K), 64 with 8192 (bf16)")
     ap.add_argument("--accept", choices=("greedy", "sampled"), default="greedy",
                     help="acceptance after the draft: greedy prefix (the default), or "
                          "rejection sampling against fp32 target logits [B][8][V] at "
@@ -115,7 +135,12 @@ def main():
     import torch
     from block_diffusion_draft_amd import binding, runner, synth
 
-    wl = synth.WORKLOADS[WORKLOAD if args.weights == "q4k" else "full_b1_q8_0"]
+    key = args.workload
+    if args.weights == "q8_0":
+        if key != "full_b1":
+            sys.exit("--weights q8_0 is measured on the batch-1 workload")
+        key = "full_b1_q8_0"
+    wl = synth.WORKLOADS[key]
     s = wl.shape
     print(f"[bench] preparing {wl.name}", file=sys.stderr, flush=True)
     bufs = runner.StepBuffers(wl, dbg=False)
@@ -189,10 +214,14 @@ def main():
     torch.cuda.synchronize()
     head_ms = float(np.mean([a.elapsed_ms(b) for a, b in ev]))
     R = wl.batch * (s.block - 1)
-    # the head's algorithmic bytes: its bf16 weights and input rows once, fp32 logits out
+    # the head's algorithmic bytes: its bf16 weights and input rows once, fp32 logits out;
+    # at many rows its 2 R V H flops take longer than those bytes at the peaks: then it is
+    # an MFMA-bound kernel and is reported in TFLOP/s
     alg = s.vocab * s.hidden * 2 + R * s.hidden * 2 + R * s.vocab * 4
+    flops = 2.0 * R * s.vocab * s.hidden
+    mfma_bound = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > alg / (HBM_PEAK_GBS * 1e9)
     achieved = alg / (head_ms * 1e-3) / 1e9
-    traffic = load_traffic()
+    traffic = load_traffic() if wl.batch == 1 else None
 
     res = {
         "metric": "draft blocks/s (8 tok) at 27B-draft shape, 1 GPU; % of HBM roofline",
@@ -207,10 +236,19 @@ def main():
                    "step": ("draft_step + verify_sampled (T 1.0, top-k 20, top-p 0.95)"
                             if sampled else "draft_step + verify_prefix"),
                    "hip_graph": bool(graph)},
-        "roofline": {"kernel": "output head k_head_stream (bf16 MFMA, 248320 x 5120, 7 rows)",
-                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "launch_ms": head_ms, "algorithmic_bytes": alg},
+        "roofline": ({"kernel": "output head k_head_stream (bf16 MFMA, 248320 x 5120, 7 rows)",
+                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                      "launch_ms": head_ms, "algorithmic_bytes": alg} if wl.batch == 1 else
+                     {"kernel": f"output head (bf16 MFMA, {s.vocab} x {s.hidden}, {R} rows)",
+                      "bound": "mfma" if mfma_bound else "hbm",
+                      "achieved": (flops / (head_ms * 1e-3) / 1e12) if mfma_bound else achieved,
+                      "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+                      "unit": "TFLOP/s" if mfma_bound else "GB/s",
+                      "frac": (flops / (head_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS) if mfma_bound
+                      else achieved / HBM_PEAK_GBS,
+                      "traffic": traffic, "launch_ms": head_ms, "algorithmic_bytes": alg,
+                      "algorithmic_flops": flops}),
         "step_hbm_frac": None,
     }
     step_bytes = step_algorithmic_bytes(wl)

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdflash.so")
-SOURCES = ["api.hip", "q4k_dequant.hip", "q4k_tiled.hip", "q4k_fused.hip", "q4k_stream.hip", "q8_0.hip", "gemm_bf16.hip", "layer_ops.hip", "attention.hip",
+SOURCES = ["api.hip", "q4k_dequant.hip", "q4k_tiled.hip", "q4k_stream.hip", "q8_0.hip", "gemm_bf16.hip", "gemm_big.hip", "layer_ops.hip", "attention.hip",
            "topk.hip", "verify.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

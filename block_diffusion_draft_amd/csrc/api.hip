@@ -25,12 +25,23 @@ struct Plan {
 };
 
 // fp32 partial sums of one GEMM: [splits][M][N] (Q4_K split-K) or [M][N] (bf16)
+// Which kernel runs a product: the 16-row streaming kernels (Q4_K, Q8_0) where their
+// shape rules allow, else the many-row GEMM; bf16 up to 16 rows on the tiled kernel.
+int big_fmt(int fmt) { return fmt == DFLASH_W_Q4K ? 2 : (fmt == DFLASH_W_Q8_0 ? 1 : 0); }
+bool use_stream(int fmt, int M, int N, int K) {
+    return fmt == DFLASH_W_Q4K ? q4k_stream_ok(M, N, K)
+                               : (fmt == DFLASH_W_Q8_0 && q8_stream_ok(M, N, K));
+}
+bool use_big(int fmt, int M, int N, int K) {
+    if (fmt != DFLASH_W_BF16 && use_stream(fmt, M, N, K)) return false;
+    if (fmt == DFLASH_W_BF16 && M <= 16) return false;
+    return big_gemm_ok(big_fmt(fmt), M, N, K);
+}
+
 size_t gemm_part_bytes(int fmt, int M, int N, int K) {
-    if (fmt == DFLASH_W_Q4K)
-        return q4k_stream_ok(M, N, K) ? q4k_stream_plan(M, N, K).part_bytes
-                                      : q4k_fused_plan(M, N, K).part_bytes;
-    if (fmt == DFLASH_W_Q8_0 && q8_stream_ok(M, N, K))
-        return q8_stream_plan(M, N, K).part_bytes;
+    if (use_big(fmt, M, N, K)) return big_gemm_plan(M, N, K).part_bytes;
+    if (fmt == DFLASH_W_Q4K && q4k_stream_ok(M, N, K)) return q4k_stream_plan(M, N, K).part_bytes;
+    if (fmt == DFLASH_W_Q8_0 && q8_stream_ok(M, N, K)) return q8_stream_plan(M, N, K).part_bytes;
     return (size_t)M * N * 4;
 }
 
@@ -147,34 +158,50 @@ struct Ctx {
     template <class T> T *at(size_t off) const { return reinterpret_cast<T *>(ws + off); }
 };
 
-// Q4_K product into partials: the streaming kernel for up to 16 rows, else the
-// row-tiled one.  Returns the number of splits or a negative status; *pair_left is
-// the row pair the partial still holds (0 once the kernel has added the halves).
-int run_q4k(const Q4kFusedArgs &a, hipStream_t st, int *pair_left) {
-    const int K = a.KB * 256;
-    *pair_left = a.pair;
-    if (q4k_stream_ok(a.M, a.N, K)) {
-        const Q4kStreamPlan p = q4k_stream_plan(a.M, a.N, K, a.pair);
-        HIPCHK(launch_q4k_stream(a, p, st));
-        if (p.pair_done) *pair_left = 0;
-        return p.splits;
+// The many-row GEMM (more than 16 rows) into partials [splits][M][N]; returns the
+// number of splits or a negative status.
+int run_big(int wfmt, const void *const *w, const int *seg_end, int nseg, const uint16_t *A,
+            int lda, int M, int N, int K, float *part, hipStream_t st) {
+    BigGemmArgs g = {};
+    for (int i = 0; i < 3; i++) {
+        g.w[i] = w[i];
+        g.seg_end[i] = seg_end[i];
     }
-    const Q4kFusedPlan p = q4k_fused_plan(a.M, a.N, K);
-    HIPCHK(launch_q4k_fused(a, p, st));
+    g.nseg = nseg;
+    g.wfmt = wfmt;
+    g.A = A;
+    g.lda = lda;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.C = part;
+    g.ldc = N;
+    const BigGemmPlan p = big_gemm_plan(M, N, K);
+    HIPCHK(launch_big_gemm(g, p, st));
     return p.splits;
 }
 
-// Q8_0 product into partials: the streaming kernel for up to 16 rows (K a multiple of
-// 1024), else the tiled MFMA kernel with the Q8_0 loader ([M][N], one split).
-int run_q8(const Q4kFusedArgs &a, hipStream_t st, int *pair_left) {
+// Q4_K / Q8_0 product into partials: the streaming kernels for up to 16 rows, else the
+// many-row GEMM.  Returns the number of splits or a negative status; *pair_left is the
+// row pair the partial still holds (0 once the kernel has added the halves).
+int run_quant(int fmt, const Q4kFusedArgs &a, hipStream_t st, int *pair_left) {
     const int K = a.KB * 256;
     *pair_left = a.pair;
-    if (q8_stream_ok(a.M, a.N, K)) {
-        const Q4kStreamPlan p = q8_stream_plan(a.M, a.N, K, a.pair);
-        HIPCHK(launch_q8_stream(a, p, st));
+    const bool q4k = fmt == DFLASH_W_Q4K;
+    if (use_stream(fmt, a.M, a.N, K)) {
+        const Q4kStreamPlan p = q4k ? q4k_stream_plan(a.M, a.N, K, a.pair)
+                                    : q8_stream_plan(a.M, a.N, K, a.pair);
+        HIPCHK(q4k ? launch_q4k_stream(a, p, st) : launch_q8_stream(a, p, st));
         if (p.pair_done) *pair_left = 0;
         return p.splits;
     }
+    if (use_big(fmt, a.M, a.N, K)) {
+        const void *w[3] = {a.w[0], a.w[1], a.w[2]};
+        return run_big(big_fmt(fmt), w, a.seg_end, a.nseg, a.src.A, a.src.lda, a.M, a.N, K,
+                       a.part, st);
+    }
+    if (q4k) return DFLASH_ESHAPE;     // (every Q4_K shape takes one of the two above)
+    // (Q8_0 shapes the many-row GEMM does not take): the tiled kernel's Q8_0 loader
     Bf16GemmArgs g = {};
     for (int i = 0; i < 3; i++) {
         g.w[i] = reinterpret_cast<const uint16_t *>(a.w[i]);
@@ -194,8 +221,8 @@ int run_q8(const Q4kFusedArgs &a, hipStream_t st, int *pair_left) {
 }
 
 // y = A . W^T over up to 3 weight matrices stacked along N, as fp32 partial sums in
-// the workspace's partial buffer: Q4_K -> [splits][M][N] from the dequantize-fused
-// MFMA kernel; bf16 -> [M][N] (one split) from the tiled MFMA kernel.  Rows r and
+// the workspace's partial buffer [splits][M][N]: up to 16 rows the streaming Q4_K /
+// Q8_0 kernels (or the tiled MFMA kernel for bf16), more rows the many-row GEMM.  Rows r and
 // r + pair (pair > 0) are the (hi, lo) halves of one activation row; *pair_left is
 // the pair the partial still holds (the reduction adds those rows).  Returns the
 // number of splits (> 0) or a negative status.
@@ -223,8 +250,11 @@ int run_gemm(const Ctx &x, const void *const *w, const int *seg_n, int nseg, con
         a.src.lda = lda;
         a.part = part;
         a.pair = pair;
-        return x.c->weight_fmt == DFLASH_W_Q4K ? run_q4k(a, x.st, pair_left)
-                                               : run_q8(a, x.st, pair_left);
+        return run_quant(x.c->weight_fmt, a, x.st, pair_left);
+    }
+    if (use_big(DFLASH_W_BF16, M, N, K)) {
+        const void *wv[3] = {w[0], nseg > 1 ? w[1] : w[0], nseg > 2 ? w[2] : w[0]};
+        return run_big(0, wv, seg_end, nseg, A, lda, M, N, K, part, x.st);
     }
     Bf16GemmArgs a = {};
     for (int i = 0; i < 3; i++) {
@@ -438,8 +468,22 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
         a.rs = rowscale(ssq_x, p.T);           // the final norm of the proposal rows
         const bool probe_lm = probe && probe->kernel == DFLASH_PROBE_LM_HEAD;
         if (probe_lm) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_start, x.st));
-        if (p.lm_skinny) HIPCHK(launch_bf16_gemm_skinny(a, x.st));
-        else HIPCHK(launch_bf16_gemm_tiled(a, x.st));
+        if (p.lm_skinny) {
+            HIPCHK(launch_bf16_gemm_skinny(a, x.st));
+        } else if (big_gemm_ok(0, p.R, p.V, H)) {
+            BigGemmArgs g = {};
+            g.w[0] = g.w[1] = g.w[2] = w->lm_head;
+            g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = p.V;
+            g.nseg = 1;
+            g.wfmt = 0;
+            g.A = f; g.lda = H; g.M = p.R; g.N = p.V; g.K = H; g.C = logits; g.ldc = p.V;
+            g.rs = a.rs;
+            BigGemmPlan bp = big_gemm_plan(p.R, p.V, H);
+            bp.splits = 1;                     // the row scale is applied in the epilogue
+            HIPCHK(launch_big_gemm(g, bp, x.st));
+        } else {
+            HIPCHK(launch_bf16_gemm_tiled(a, x.st));
+        }
         if (probe_lm) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_stop, x.st));
     }
     // S10 + S11: log-softmax statistics, top-K, and the selector path
@@ -511,7 +555,7 @@ int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
     a.part = (float *)workspace;
     a.pair = 0;
     int pair_left;
-    const int splits = run_q4k(a, st, &pair_left);
+    const int splits = run_quant(DFLASH_W_Q4K, a, st, &pair_left);
     if (splits < 0) return splits;
     HIPCHK(launch_reduce_epilogue(a.part, splits, M, N, 0, EPI_STORE_BF16, nullptr, y, nullptr, N,
                                   RowScale{}, st));
@@ -541,7 +585,7 @@ int q8_0_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K
     a.part = (float *)workspace;
     a.pair = 0;
     int pair_left;
-    const int splits = run_q8(a, st, &pair_left);
+    const int splits = run_quant(DFLASH_W_Q8_0, a, st, &pair_left);
     if (splits < 0) return splits;
     HIPCHK(launch_reduce_epilogue(a.part, splits, M, N, 0, EPI_STORE_BF16, nullptr, y, nullptr, N,
                                   RowScale{}, st));

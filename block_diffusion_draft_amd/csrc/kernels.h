@@ -142,13 +142,6 @@ struct Q4kFusedArgs {
     float *part;                 // [splits][M][N], or [splits][pair][N] when combined
     int pair;                    // > 0: rows r and r + pair are the (hi, lo) halves of one row
 };
-struct Q4kFusedPlan {
-    int rt, nsb, ct, steps, splits, row_groups, grid_x;
-    size_t lds_bytes, part_bytes;
-};
-Q4kFusedPlan q4k_fused_plan(int M, int N, int K);
-hipError_t launch_q4k_fused(const Q4kFusedArgs &a, const Q4kFusedPlan &p, hipStream_t st);
-
 // Streaming variant for M <= 16 rows and K/256 a multiple of 4: splits of 4 super-blocks,
 // each wave streams tpw consecutive column tiles.  Partials [splits][M][N]; when
 // pair is 4 or 8 and M = 2 pair, the kernel adds each (hi, lo) row pair itself and
@@ -204,3 +197,27 @@ bool q8_stream_ok(int M, int N, int K);
 Q4kStreamPlan q8_stream_plan(int M, int N, int K, int pair = 0, int target_waves = 2048,
                              int wpg = 0);
 hipError_t launch_q8_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st);
+
+// ---------------------------------------------------------------- many-row GEMM
+// C[split][M][N] fp32 = A[M][K] bf16 . W^T over the split's share of K; W stacked along
+// N from up to 3 matrices in bf16 ([N][K]), Q8_0 or Q4_K (tiled layouts), decoded to
+// bf16 MFMA operands per 256 x 256 tile.  One split: rows scaled by row_inv(rs, r).
+struct BigGemmArgs {
+    const void *w[3];
+    int seg_end[3];
+    int nseg;
+    int wfmt;                    // 0 bf16, 1 Q8_0, 2 Q4_K
+    const uint16_t *A;
+    int lda;
+    int M, N, K;
+    float *C;
+    int ldc;
+    RowScale rs;
+};
+struct BigGemmPlan {
+    int bm, grid_x, grid_y, splits;
+    size_t lds_bytes, part_bytes;
+};
+bool big_gemm_ok(int wf, int M, int N, int K);
+BigGemmPlan big_gemm_plan(int M, int N, int K);
+hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream_t st);

@@ -115,11 +115,12 @@ def test_q8_0_gemm_row_counts(M, K):
     gemm_check(w, x, N, K, M, exact_products=(M <= 16 and K % 1024 == 0))
 
 
-@pytest.mark.parametrize("shape,batch", [("mid", 1), ("mid", 2), ("tiny", 2)])
+@pytest.mark.parametrize("shape,batch", [("mid", 1), ("mid", 2), ("mid", 16), ("tiny", 2)])
 def test_small_step_q8_0(shape, batch):
     """Whole draft steps with Q8_0 weights: a 2-layer drafter whose products all take the
-    streaming kernel (1 sequence) or the tiled one (2 sequences: 32 MLP rows), and the
-    tiny drafter (K = 256 and 1280: the tiled kernel)."""
+    streaming kernel (1 sequence) or the tiled one (2 sequences: 32 MLP rows; 16
+    sequences: 256 MLP rows over two row tiles), and the tiny drafter (K = 256 and 1280:
+    the tiled kernel)."""
     s = dataclasses.replace(synth.MID if shape == "mid" else synth.TINY, weight_fmt="q8_0")
     wl = dataclasses.replace(synth.WORKLOADS["tiny"], shape=s, batch=batch, ctx_len=96,
                              seed=40 + batch)

@@ -228,3 +228,20 @@ def test_mid_step_streaming_products(fmt, head_dim, batch):
     ref = parity.run_oracle(wl, bufs.host_W, bufs.inputs)
     g = full_check(wl, bufs, ref)
     check_verify(bufs, g)
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q8_0", "bf16"])
+def test_mid_step_many_rows(fmt):
+    """4 sequences of a 2-layer drafter: every product has more than 16 rows (32 block
+    rows, 64 with the context rows or the (hi, lo) pairs) and runs on the many-row GEMM
+    with the format's weight decode, split-K where the tiles are few; the output head
+    (28 rows) too, with the deferred final norm applied in its epilogue."""
+    s = dataclasses.replace(synth.MID, weight_fmt=fmt)
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], shape=s, batch=4, ctx_len=96, seed=61)
+    say(f"[step] mid {fmt} batch 4")
+    bufs = runner.StepBuffers(wl)
+    bufs.step()
+    torch.cuda.synchronize()
+    ref = parity.run_oracle(wl, bufs.host_W, bufs.inputs)
+    g = full_check(wl, bufs, ref)
+    check_verify(bufs, g)
