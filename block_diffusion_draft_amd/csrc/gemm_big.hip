@@ -279,9 +279,130 @@ __global__ __launch_bounds__(NTH) void k_gemm_big(BigGemmArgs a) {
     }
 }
 
+// bf16 weights: both operands travel global -> LDS by direct 16-byte loads
+// (global_load_lds_dwordx4, no registers), K advancing 32 per stage through a ring of NS
+// LDS buffers, so NS - 1 stages are in flight while one is multiplied.  A stage holds
+// 32-row groups of 32 rows x 64 bytes (2 KB); lane L of a load instruction fills the
+// 16-byte slot L of one 1 KB half, i.e. row 16 h + L / 4, chunk slot L % 4, and it loads
+// the chunk (L % 4) ^ ((row / 4) % 4) of that row: four lanes cover a row's 64 bytes, and
+// the 16 rows read together by an MFMA operand load (one chunk each) fall on 16
+// distinct 16-byte bank groups.  Rows and columns past M / N load row M - 1 / column
+// N - 1 (in bounds) and are never stored.
+constexpr int BKD = 32;
+
+__device__ __forceinline__ int dma_pos(int row, int chunk) { return 4 * row + (chunk ^ ((row >> 2) & 3)); }
+
+template <int BM, int NS>
+__global__ __launch_bounds__(NTH) void k_gemm_big_dma(BigGemmArgs a) {
+    constexpr int RG = BM / 32, WM = BM / 2, FM = WM / 32;
+    constexpr int NG = RG + 8;                        // 2 KB groups per stage (A, then W)
+    constexpr int PW = 2 * NG / 8;                    // load instructions per wave and stage
+    extern __shared__ __align__(16) u32x4_t lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int nst = a.K / BKD;
+    const int s0 = (int)((long long)nst * blockIdx.z / gridDim.z);
+    const int s1 = (int)((long long)nst * (blockIdx.z + 1) / gridDim.z);
+
+    // this lane's source pointer for each of the wave's load instructions (k of stage added)
+    const uint16_t *src[PW];
+#pragma unroll
+    for (int j = 0; j < PW; j++) {
+        const int h = wave + 8 * j;                   // 1 KB half: group h / 2, rows 16 (h % 2) ..
+        const int g = h >> 1, row = 16 * (h & 1) + (lane >> 2);
+        const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+        if (g < RG) {
+            const int r = min(m0 + 32 * g + row, a.M - 1);
+            src[j] = a.A + (size_t)r * a.lda + 8 * chunk;
+        } else {
+            const int n = min(n0 + 32 * (g - RG) + row, a.N - 1);
+            int nb;
+            const unsigned char *ws = seg_of(a, n, nb);
+            src[j] = reinterpret_cast<const uint16_t *>(ws) + (size_t)(n - nb) * a.K + 8 * chunk;
+        }
+    }
+    auto issue = [&](int s, int buf) {
+        const int k0 = s * BKD;
+#pragma unroll
+        for (int j = 0; j < PW; j++) {
+            const int h = wave + 8 * j;
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1))) *)(src[j] + k0),
+                (void __attribute__((address_space(3))) *)(lds + (buf * NG * 2 + h) * 64), 16, 0, 0);
+        }
+    };
+
+    f32x16_t acc[FM][2];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+
+    // read positions of this lane's MFMA operands for the two k steps of a stage
+    const int rl = lane & 31;
+    const int rp0 = dma_pos(rl, lane >> 5), rp1 = dma_pos(rl, 2 + (lane >> 5));
+
+    // prologue: stages s0 .. s0 + NS - 2 in flight (past the end: the last stage again,
+    // into a buffer no stage reads, so every iteration waits on the same count)
+#pragma unroll
+    for (int p = 0; p < NS - 1; p++) issue(min(s0 + p, s1 - 1), p);
+    for (int s = s0; s < s1; s++) {
+        const int buf = (s - s0) % NS;
+        // stage s has landed (the NS - 2 later ones may be in flight) in every wave; a
+        // bare barrier, since a workgroup fence would wait for every load in flight
+        __builtin_amdgcn_s_waitcnt(0xF70 | ((NS - 2) * PW));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // the buffer of stage s - 1 is free: stage s + NS - 1 goes there
+        issue(min(s + NS - 1, s1 - 1), (s - s0 + NS - 1) % NS);
+        const u32x4_t *Ab = lds + buf * NG * 128;
+        const u32x4_t *Bb = Ab + RG * 128;
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+            const int rp = ks ? rp1 : rp0;
+            u32x4_t bf[2];
+#pragma unroll
+            for (int j = 0; j < 2; j++) bf[j] = Bb[(wn * 2 + j) * 128 + rp];
+#pragma unroll
+            for (int i = 0; i < FM; i++) {
+                const u32x4_t af = Ab[(wm * FM + i) * 128 + rp];
+#pragma unroll
+                for (int j = 0; j < 2; j++) acc[i][j] = mfma32x32x16(af, bf[j], acc[i][j]);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);      // no load may land after the workgroup ends
+
+    const int hl = lane >> 5, c = lane & 31;
+    float *C = a.C + (size_t)blockIdx.z * a.M * a.ldc;
+    const bool scale = gridDim.z == 1 && a.rs.ssq;
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * hl + (v & 3);
+            if (m >= a.M) continue;
+            const float ri = scale ? row_inv(a.rs, m) : 1.f;
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const int n = n0 + wn * 64 + 32 * j + c;
+                if (n < a.N) C[(size_t)m * a.ldc + n] = acc[i][j][v] * ri;
+            }
+        }
+    }
+}
+
 }  // namespace
 
 size_t big_gemm_lds_bytes(int BM) { return ((size_t)2 * 4 * (BM / 32) + 2 * 4 * 8) * 64 * 16; }
+constexpr int DMA_NS = 4;
+size_t big_gemm_dma_lds_bytes(int BM) { return (size_t)DMA_NS * (BM / 32 + 8) * 2048; }
 
 BigGemmPlan big_gemm_plan(int M, int N, int K) {
     BigGemmPlan p;
@@ -296,6 +417,7 @@ BigGemmPlan big_gemm_plan(int M, int N, int K) {
            p.splits < 16)
         p.splits *= 2;
     p.lds_bytes = big_gemm_lds_bytes(p.bm);
+    // (the bf16 kernel's ring is smaller; its launch sets its own size)
     p.part_bytes = (size_t)p.splits * M * N * 4;
     return p;
 }
@@ -320,6 +442,20 @@ hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream
         }                                                                                            \
         hipLaunchKernelGGL((k_gemm_big<WF, BMV>), grid, dim3(NTH), p.lds_bytes, st, a);             \
         return hipGetLastError();                                                                    \
+    }
+    if (a.wfmt == 0 && a.K % BKD == 0 && a.K / BKD >= p.splits) {
+        static bool dma_set[2] = {false, false};
+        const int bi = p.bm == 256;
+        const size_t lb = big_gemm_dma_lds_bytes(p.bm);
+        const void *fn = bi ? (const void *)k_gemm_big_dma<256, DMA_NS> : (const void *)k_gemm_big_dma<128, DMA_NS>;
+        if (!dma_set[bi]) {
+            hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lb);
+            if (e != hipSuccess) return e;
+            dma_set[bi] = true;
+        }
+        if (bi) hipLaunchKernelGGL((k_gemm_big_dma<256, DMA_NS>), grid, dim3(NTH), lb, st, a);
+        else hipLaunchKernelGGL((k_gemm_big_dma<128, DMA_NS>), grid, dim3(NTH), lb, st, a);
+        return hipGetLastError();
     }
     BIG_CASE(0, 128)
     BIG_CASE(0, 256)
