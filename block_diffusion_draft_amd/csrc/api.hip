@@ -478,7 +478,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
             g.wfmt = 0;
             g.A = f; g.lda = H; g.M = p.R; g.N = p.V; g.K = H; g.C = logits; g.ldc = p.V;
             g.rs = a.rs;
-            BigGemmPlan bp = big_gemm_plan(p.R, p.V, H);
+            BigGemmPlan bp = big_gemm_plan_grid(p.R, p.V, H);
             bp.splits = 1;                     // the row scale is applied in the epilogue
             HIPCHK(launch_big_gemm(g, bp, x.st));
         } else {

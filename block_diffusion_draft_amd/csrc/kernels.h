@@ -215,9 +215,14 @@ struct BigGemmArgs {
     RowScale rs;
 };
 struct BigGemmPlan {
-    int bm, grid_x, grid_y, splits;
-    size_t lds_bytes, part_bytes;
+    int bm, grid_x, grid_y;      // tile rows (128 / 256); N and M tiles
+    int splits;                  // partial slots [splits][M][N] the consumer sums
+    int wgs;                     // 0: grid (N tiles, M tiles, splits); else stream-K workgroups
+    size_t part_bytes;
 };
 bool big_gemm_ok(int wf, int M, int N, int K);
+// grid or stream-K, whichever fills the CUs better
 BigGemmPlan big_gemm_plan(int M, int N, int K);
+// grid only (set splits = 1 for a single slot)
+BigGemmPlan big_gemm_plan_grid(int M, int N, int K);
 hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream_t st);
