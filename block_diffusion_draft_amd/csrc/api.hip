@@ -39,7 +39,7 @@ bool use_big(int fmt, int M, int N, int K) {
 }
 
 size_t gemm_part_bytes(int fmt, int M, int N, int K) {
-    if (use_big(fmt, M, N, K)) return big_gemm_plan(M, N, K).part_bytes;
+    if (use_big(fmt, M, N, K)) return big_gemm_plan(big_fmt(fmt), M, N, K).part_bytes;
     if (fmt == DFLASH_W_Q4K && q4k_stream_ok(M, N, K)) return q4k_stream_plan(M, N, K).part_bytes;
     if (fmt == DFLASH_W_Q8_0 && q8_stream_ok(M, N, K)) return q8_stream_plan(M, N, K).part_bytes;
     return (size_t)M * N * 4;
@@ -176,7 +176,7 @@ int run_big(int wfmt, const void *const *w, const int *seg_end, int nseg, const 
     g.K = K;
     g.C = part;
     g.ldc = N;
-    const BigGemmPlan p = big_gemm_plan(M, N, K);
+    const BigGemmPlan p = big_gemm_plan(wfmt, M, N, K);
     HIPCHK(launch_big_gemm(g, p, st));
     return p.splits;
 }
@@ -478,8 +478,8 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
             g.wfmt = 0;
             g.A = f; g.lda = H; g.M = p.R; g.N = p.V; g.K = H; g.C = logits; g.ldc = p.V;
             g.rs = a.rs;
-            BigGemmPlan bp = big_gemm_plan_grid(p.R, p.V, H);
-            bp.splits = 1;                     // the row scale is applied in the epilogue
+            // one split: the row scale is applied in the epilogue
+            const BigGemmPlan bp = big_gemm_plan_grid(p.R, p.V, H);
             HIPCHK(launch_big_gemm(g, bp, x.st));
         } else {
             HIPCHK(launch_bf16_gemm_tiled(a, x.st));

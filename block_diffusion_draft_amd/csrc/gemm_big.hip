@@ -535,47 +535,56 @@ BigGemmPlan big_gemm_plan_grid(int M, int N, int K) {
     p.grid_x = ceil_div(N, BN);
     p.grid_y = ceil_div(M, p.bm);
     p.wgs = 0;
-    // split K while there are fewer than about two workgroups per CU, keeping at least
-    // 8 stages (512 of K) per split
-    const int nst = K / BK;
     p.splits = 1;
-    while ((long long)p.grid_x * p.grid_y * p.splits * 2 <= 512 && nst / (p.splits * 2) >= 8 &&
-           p.splits < 16)
-        p.splits *= 2;
-    p.part_bytes = (size_t)p.splits * M * N * 4;
+    p.part_bytes = (size_t)M * N * 4;
     return p;
 }
 
-BigGemmPlan big_gemm_plan(int M, int N, int K) {
+BigGemmPlan big_gemm_plan(int wf, int M, int N, int K) {
+    // Estimated time, in stage times (one 64-deep K stage of one tile on one CU, measured
+    // ≈ 2.0 µs for bf16 256-row tiles, ≈ 1.3 µs for 128-row ones, 1.3× that with weight
+    // decoding), of each schedule; the least wins.  Grid with S splits: its rounds of
+    // one workgroup per CU, each of nst / S stages and an epilogue of about two; stream-K:
+    // one range per CU, 1.15× per stage (the CUs are at different K offsets, so fewer
+    // operand reads hit L2), plus the epilogues of its pieces.  Each partial slot costs
+    // its write and the consumer's read (M N 4 bytes each way at about 5 TB/s).
     BigGemmPlan p = big_gemm_plan_grid(M, N, K);
-    // stream-K when its estimated time (in stage times: the range, plus about two per
-    // piece epilogue) is below 0.9 of the grid's (its rounds of workgroups, one per CU)
     const int G = cu_count();
     const long long T = (long long)p.grid_x * p.grid_y;
     const int nst = K / BK;
-    const long long U = T * nst;
-    if (U < 4LL * G) return p;
+    const double ts = (p.bm == 256 ? 2.0 : 1.3) * (wf ? 1.3 : 1.0);
+    const double slot = 2.0 * M * (double)N * 4 / 5e12 * 1e6 / ts;
     const double epi = 2.0;
-    const double rounds = (double)((T * p.splits + G - 1) / G);
-    const double t_grid = rounds * ((double)nst / p.splits + epi);
-    const double per = (double)((U + G - 1) / G);
-    const double t_sk = per + epi * (1.0 + (double)((long long)per + nst - 1) / nst);
-    if (t_sk >= 0.9 * t_grid) return p;
-    // (cached: the slot count walks every tile)
-    static thread_local struct { int M, N, K, G, slots; } cache[8] = {};
-    static thread_local int next = 0;
-    int slots = 0;
-    for (auto &c : cache)
-        if (c.M == M && c.N == N && c.K == K && c.G == G) slots = c.slots;
-    if (!slots) {
-        slots = sk_slots(T, nst, G);
-        cache[next] = {M, N, K, G, slots};
-        next = (next + 1) % 8;
+    double best = 1e300;
+    for (int S = 1; S <= 16 && (S == 1 || nst / S >= 4); S++) {
+        const double rounds = (double)((T * S + G - 1) / G);
+        const double c = rounds * ((double)nst / S + epi) + S * slot;
+        if (c < best) {
+            best = c;
+            p.splits = S;
+        }
     }
-    if (slots > max(16, p.splits)) return p;       // (partials: at most the grid's 16 splits)
-    p.wgs = G;
-    p.splits = slots;
-    p.part_bytes = (size_t)slots * M * N * 4;
+    const long long U = T * nst;
+    if (U >= 4LL * G) {
+        // (cached: the slot count walks every tile)
+        static thread_local struct { int M, N, K, G, slots; } cache[8] = {};
+        static thread_local int next = 0;
+        int slots = 0;
+        for (auto &c : cache)
+            if (c.M == M && c.N == N && c.K == K && c.G == G) slots = c.slots;
+        if (!slots) {
+            slots = sk_slots(T, nst, G);
+            cache[next] = {M, N, K, G, slots};
+            next = (next + 1) % 8;
+        }
+        const long long per = (U + G - 1) / G;
+        const double c = 1.15 * per + epi * (1 + (per + nst - 1) / nst) + slots * slot;
+        if (slots <= 16 && c < best) {
+            p.wgs = G;
+            p.splits = slots;
+        }
+    }
+    p.part_bytes = (size_t)p.splits * M * N * 4;
     return p;
 }
 

@@ -221,8 +221,8 @@ struct BigGemmPlan {
     size_t part_bytes;
 };
 bool big_gemm_ok(int wf, int M, int N, int K);
-// grid or stream-K, whichever fills the CUs better
-BigGemmPlan big_gemm_plan(int M, int N, int K);
-// grid only (set splits = 1 for a single slot)
+// the schedule (grid with K splits, or stream-K) of least estimated time; wf as in BigGemmArgs
+BigGemmPlan big_gemm_plan(int wf, int M, int N, int K);
+// grid, one split
 BigGemmPlan big_gemm_plan_grid(int M, int N, int K);
 hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream_t st);

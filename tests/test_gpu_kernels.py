@@ -126,12 +126,13 @@ def test_q4k_gemm_row_counts(M):
     gemm_check(w, x, N, K, M)
 
 
-@pytest.mark.parametrize("M,N,K", [(160, 4096, 4096), (256, 8704, 5120)])
-def test_q4k_gemm_stream_k(M, N, K):
-    """Shapes whose 256-row tiles would leave a partly empty last round of workgroups
-    (16 and 34 tiles): the many-row GEMM cuts the (tile, K stage) units into one range
-    per CU, pieces of a tile in their own partial slots, unused slots zeroed."""
-    say(f"[q4k_gemm stream-K] M={M} {N}x{K}")
+@pytest.mark.parametrize("M,N,K", [(160, 4096, 4096), (256, 8704, 5120), (136, 34816, 4096)])
+def test_q4k_gemm_schedules(M, N, K):
+    """Many-row GEMM schedules: 16 and 34 tiles of 256 rows run as one round of K splits
+    (13 and 7 splits); 136 tiles (ragged rows) as stream-K, each CU one equal range of
+    (tile, K stage) units, the pieces of a tile in their own partial slots (3), unused
+    slots zeroed."""
+    say(f"[q4k_gemm schedules] M={M} {N}x{K}")
     w = synth.q4k_normal(8, "sk", N, K, 0.02)
     x = synth.normal_bf16(8, "sk.x", (M, K), 1.0)
     gemm_check(w, x, N, K, M)

@@ -119,10 +119,10 @@ def test_q8_0_gemm_row_counts(M, K):
     gemm_check(w, x, N, K, M, exact_products=(M <= 16 and K % 1024 == 0))
 
 
-@pytest.mark.parametrize("M,N,K", [(160, 4096, 4096), (256, 8704, 5120)])
-def test_q8_0_gemm_stream_k(M, N, K):
-    """Stream-K shapes of the many-row GEMM (16 and 34 tiles of 256 rows)."""
-    say(f"[q8_0_gemm stream-K] M={M} {N}x{K}")
+@pytest.mark.parametrize("M,N,K", [(160, 4096, 4096), (256, 8704, 5120), (136, 34816, 4096)])
+def test_q8_0_gemm_schedules(M, N, K):
+    """Many-row GEMM schedules: one round of K splits (16 and 34 tiles), stream-K (136)."""
+    say(f"[q8_0_gemm schedules] M={M} {N}x{K}")
     w = synth.q8_0_normal(8, "q8.sk", N, K, 0.02)
     x = synth.normal_bf16(8, "q8.sk.x", (M, K), 1.0)
     gemm_check(w, x, N, K, M, exact_products=False)
