@@ -10,6 +10,11 @@
         a WRITE_SIZE run, each counter scaled by what it reads for a plain device copy
         of N bytes in the same run (N bytes fetched, N written): the mean over the
         --copies largest copy-kernel dispatches.
+    python -m block_diffusion_draft_amd.rocprof_summary mfma DIR [PATTERN]
+        per (kernel, grid) matrix-core use from a run with the counters
+        SQ_VALU_MFMA_BUSY_CYCLES (MFMA busy cycles summed over the SIMDs; 32 per
+        32x32x16 bf16 MFMA) and GRBM_GUI_ACTIVE (the launch's GPU cycles, summed over
+        the 8 XCDs): busy / (SIMDs x cycles), SIMDs = 4 per CU.
 """
 import argparse
 import csv
@@ -85,6 +90,29 @@ def _counter(d, name, kernel_pat):
     return vals, grids
 
 
+def mfma(d, pattern="", cus=256, xcds=8, out=sys.stdout):
+    per = {}
+    for r in _rows(d, "counter_collection.csv"):
+        if pattern and not re.search(pattern, r["Kernel_Name"]):
+            continue
+        e = per.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"],
+                                              "grid": int(r.get("Grid_Size") or 0)})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    agg = {}
+    for e in per.values():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in e or not e.get("GRBM_GUI_ACTIVE"):
+            continue
+        cyc = e["GRBM_GUI_ACTIVE"] / xcds
+        agg.setdefault((short(e["name"], 48), e["grid"]), []).append(
+            (e["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * cus * cyc), e["SQ_VALU_MFMA_BUSY_CYCLES"], cyc))
+    out.write(f"{'kernel':48s} {'grid':>10s} {'launches':>8s} {'mfma_busy':>9s} "
+              f"{'mfma_cycles':>13s} {'gpu_cycles':>11s}\n")
+    for (n, g), v in sorted(agg.items(), key=lambda kv: -sum(x[2] for x in kv[1])):
+        k = len(v)
+        out.write(f"{n:48s} {g:10d} {k:8d} {sum(x[0] for x in v) / k:9.3f} "
+                  f"{sum(x[1] for x in v) / k:13.0f} {sum(x[2] for x in v) / k:11.0f}\n")
+
+
 def source_hash(files):
     h = hashlib.sha256()
     for f in files:
@@ -116,6 +144,7 @@ def main():
     sub = ap.add_subparsers(dest="cmd", required=True)
     a = sub.add_parser("stats"); a.add_argument("dir")
     a = sub.add_parser("trace"); a.add_argument("dir"); a.add_argument("pattern", nargs="?", default="")
+    a = sub.add_parser("mfma"); a.add_argument("dir"); a.add_argument("pattern", nargs="?", default="")
     a = sub.add_parser("traffic")
     a.add_argument("--fetch", required=True); a.add_argument("--write", required=True)
     a.add_argument("--kernel", required=True); a.add_argument("--copy-bytes", type=int, required=True)
@@ -127,6 +156,8 @@ def main():
         stats(args.dir)
     elif args.cmd == "trace":
         trace(args.dir, args.pattern)
+    elif args.cmd == "mfma":
+        mfma(args.dir, args.pattern)
     else:
         r = traffic(args.fetch, args.write, args.kernel, args.copy_bytes, args.copies)
         lines = [f"kernel_pattern {args.kernel}",
