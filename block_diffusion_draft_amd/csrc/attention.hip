@@ -98,13 +98,12 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     for (int u = 0; u < 4; u++) acc[u] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     const int g = lane >> 4, cl = lane & 15;
 
-    for (int kk = 0; kk < nkeys; kk += KT) {
+    // K and V rows of keys kk .. kk + KT - 1 into registers (rows past the chunk clamped
+    // to a real row; their values are replaced by zeros when staged)
+    constexpr int SPT = KT * (d / 8) / 256;              // 16-byte vectors per thread
+    u32x4_t kv[SPT], vv[SPT];
+    auto load_kv = [&](int kk) {
         const int nk = min(KT, nkeys - kk);
-        __syncthreads();
-        // stage K rows and V^T for keys kk .. kk+nk-1: all loads first (rows past nk
-        // clamped to a real row, their values replaced by zeros)
-        constexpr int SPT = KT * (d / 8) / 256;          // 16-byte vectors per thread
-        u32x4_t kv[SPT], vv[SPT];
 #pragma unroll
         for (int i = 0; i < SPT; i++) {
             const int e = tid + 256 * i;
@@ -124,6 +123,13 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
             kv[i] = *reinterpret_cast<const u32x4_t *>(kbase + off);
             vv[i] = *reinterpret_cast<const u32x4_t *>(vbase + off);
         }
+    };
+    load_kv(0);
+    for (int kk = 0; kk < nkeys; kk += KT) {
+        const int nk = min(KT, nkeys - kk);
+        __syncthreads();
+        // stage this step's K rows and V rows, then issue the next step's loads so that
+        // they land while this step is multiplied
 #pragma unroll
         for (int i = 0; i < SPT; i++) {
             const int e = tid + 256 * i;
@@ -133,6 +139,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
             *reinterpret_cast<u32x4_t *>(&Ks[j * DS + 8 * q8]) = in ? kv[i] : z;
             *reinterpret_cast<u32x4_t *>(&Vs[j * VS + 8 * q8]) = in ? vv[i] : z;
         }
+        if (kk + KT < nkeys) load_kv(kk + KT);
         __syncthreads();
         // S = Q K^T (scaled, masked)
         for (int ti = wave; ti < RTQ * 4; ti += 4) {
