@@ -322,7 +322,7 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
 // so that z_t = W_c . vec(o_t) = the sum of zp over (h, cc).
 constexpr int MC = 32;              // columns per merge workgroup
 
-constexpr int MW = 12;              // chunk partials per lane loaded up front (x 4 waves)
+constexpr int MW = 9;               // chunk partials per lane loaded up front (x 4 waves)
 constexpr int MAXE = 4;             // conv-tap outputs per thread (T 2 n_q <= 1024)
 
 __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
@@ -337,6 +337,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
     float *w = sm;                      // [T][nch1] merge weights
     float *os = sm + T * nch1;          // [T][MC] merged output slice
     float *wp = os + T * MC;            // [4 waves][T][MC] per-wave partial sums
+    // [2 n_q][MC / 8] W_c slice, at the next 16-byte boundary
+    u32x4_t *wcs = reinterpret_cast<u32x4_t *>(sm + (T * (nch1 + 5 * MC) + 3) / 4 * 4);
     float *zp = a.zp + (((size_t)b * a.n_q + h) * CC + cc) * T * nq2;
 
     // ---- every load first, so the kernel waits on memory once.  Wave w sums chunks
@@ -361,13 +363,14 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
         mlv[ri] = *reinterpret_cast<const float2 *>(ml + ((size_t)c * QR + hq * T + tr) * 2);
     }
     const int ne = T * nq2;
-    u32x4_t wv[MAXE][MC / 8];
+    // the slice of W_c ([2 n_q][MC] bf16, 16-byte pieces: piece p = row p / 4, columns
+    // 8 (p % 4) ..), staged in LDS for the conv-tap partials
+    u32x4_t wl[2];
 #pragma unroll
-    for (int i = 0; i < MAXE; i++) {
-        const int e = min(tid + 256 * i, ne - 1), q = e % nq2;
-        const uint16_t *wr = a.w_conv + (size_t)q * qd + c0;
-#pragma unroll
-        for (int k = 0; k < MC / 8; k++) wv[i][k] = *reinterpret_cast<const u32x4_t *>(wr + 8 * k);
+    for (int j = 0; j < 2; j++) {
+        const int pc = min(tid + 256 * j, nq2 * (MC / 8) - 1);
+        wl[j] = *reinterpret_cast<const u32x4_t *>(a.w_conv + (size_t)(pc / (MC / 8)) * qd + c0 +
+                                                   8 * (pc % (MC / 8)));
     }
 
     const int t = tid / MC, col = tid % MC;             // 8 * MC == 256; rows t >= T idle
@@ -427,6 +430,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
         for (int u = 0; u < 8; u++) add(cb + 4 * u, pb[u]);
     }
     if (lt < T) *reinterpret_cast<float4 *>(&wp[(wave * T + lt) * MC + 4 * c4]) = acc;
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+        if (tid + 256 * j < nq2 * (MC / 8)) wcs[tid + 256 * j] = wl[j];
     __syncthreads();
     // merged output of (t, col): the 4 waves' sums in wave order
     if (t < T) {
@@ -441,12 +447,12 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
     for (int i = 0; i < MAXE; i++) {
         const int e = tid + 256 * i;
         if (e >= ne) break;
-        const int tt = e / nq2;
+        const int tt = e / nq2, q = e % nq2;
         const float *ot = os + tt * MC;
         float acc2 = 0.f;
 #pragma unroll
         for (int k = 0; k < MC / 8; k++) {
-            const u32x4_t v = wv[i][k];
+            const u32x4_t v = wcs[q * (MC / 8) + k];
             const float *o8 = ot + 8 * k;
             acc2 += bf16_to_f32(v.x & 0xFFFF) * o8[0] + bf16_to_f32(v.x >> 16) * o8[1];
             acc2 += bf16_to_f32(v.y & 0xFFFF) * o8[2] + bf16_to_f32(v.y >> 16) * o8[3];
@@ -545,7 +551,9 @@ hipError_t launch_qk_norm_rope(const RopeArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st) {
-    const size_t lds = (size_t)(a.T * (a.n_chunks + 1) + a.T * MC + 4 * a.T * MC) * 4;
+    // (then the W_c slice, from the next 16-byte boundary)
+    size_t lds = (size_t)(a.T * (a.n_chunks + 1) + a.T * MC + 4 * a.T * MC) * 4;
+    lds = (lds + 15) / 16 * 16 + (size_t)2 * a.n_q * MC * 2;
     hipLaunchKernelGGL(k_attn_merge, dim3(a.n_q, a.d / MC, a.B), dim3(256), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
