@@ -58,8 +58,11 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     uint16_t *Ks = KVs, *Vs = KVs + KT * (128 + 8);
     float *Os = reinterpret_cast<float *>(KVs);
     __shared__ __align__(16) uint16_t Qs[MAXQR * (128 + 8)];
-    __shared__ __align__(16) uint16_t Ps[MAXQR * (KT + 8)];
-    __shared__ float Ss[MAXQR * KT];
+    // scores (fp32) and, once every score of the step is in registers, the bf16 P rows
+    // in the same bytes (keeps the workgroup at 53 KB of LDS: 3 per CU)
+    __shared__ __align__(16) float Ss[MAXQR * KT];
+    uint16_t *Ps = reinterpret_cast<uint16_t *>(Ss);
+    static_assert(MAXQR * (KT + 8) * 2 <= MAXQR * KT * 4, "P fits in the score buffer");
     __shared__ float m_run[MAXQR], l_run[MAXQR], alpha[MAXQR];
     static_assert(MAXQR * (128 + 4) * 4 <= (KT * (128 + 8) + KT * (128 + 16)) * 2, "O staging fits");
 
@@ -157,15 +160,18 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
         }
         __syncthreads();
         // online softmax: 8 threads per query row, 8 keys each
-        if ((tid >> 3) < RTQ * 16) {
+        const bool srow = (tid >> 3) < RTQ * 16;
+        float sv[8];
+        if (srow) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) sv[i] = Ss[(tid >> 3) * KT + (tid & 7) * 8 + i];
+        }
+        __syncthreads();                    // every score read before P overwrites them
+        if (srow) {
             const int row = tid >> 3, part = tid & 7;
             float mx = -INFINITY;
-            float sv[8];
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                sv[i] = Ss[row * KT + part * 8 + i];
-                mx = fmaxf(mx, sv[i]);
-            }
+            for (int i = 0; i < 8; i++) mx = fmaxf(mx, sv[i]);
             mx = fmaxf(mx, __shfl_xor(mx, 1, WAVE));
             mx = fmaxf(mx, __shfl_xor(mx, 2, WAVE));
             mx = fmaxf(mx, __shfl_xor(mx, 4, WAVE));
