@@ -198,40 +198,57 @@ __global__ __launch_bounds__(256) void k_reduce(const float *part, int splits, i
 }
 
 // ---------------------------------------------------------------- SwiGLU from split partials
-// Workgroup per (256 columns, output row r): gate and up (columns c and c + N/2 of the
-// [gate | up] product) summed over the splits and the [hi; lo] row pair, scaled by the
-// row's deferred 1 / rms, then silu(gate) * up as a bf16 (hi, lo) pair.
+// Workgroup per (1024 columns, output row r), four consecutive columns per thread
+// (16-byte loads): gate and up (columns c and c + N/2 of the [gate | up] product) summed
+// over the splits (in split order) and the [hi; lo] row pair, scaled by the row's
+// deferred 1 / rms (formed once per workgroup), then silu(gate) * up as a bf16 (hi, lo)
+// pair.  Needs N / 2 a multiple of 4.
 __global__ __launch_bounds__(256) void k_swiglu(const float *part, int splits, int M, int N, int pair,
                                                 uint16_t *ob, uint16_t *ob_lo, int ldo, RowScale rs) {
-    const int r = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+    const int r = blockIdx.y, c = 4 * (blockIdx.x * 256 + threadIdx.x);
     const int F = N / 2;
-    if (c >= F) return;
+    __shared__ float s_inv;
+    if (threadIdx.x == 0) s_inv = row_inv(rs, r);
     const size_t stride = (size_t)(pair ? 2 * M : M) * N;
-    const float *p = part + (size_t)r * N + c;
-    float gs = 0.f, us = 0.f;
-    for (int k0 = 0; k0 < splits; k0 += 8) {
-        float gv[8], uv[8], gq[8], uq[8];
+    const float *p = part + (size_t)r * N + min(c, F - 4);
+    float4 gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < splits; k0 += 4) {
+        float4 gv[4], uv[4], gq[4], uq[4];
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
+        for (int u = 0; u < 4; u++) {
             const float *p0 = p + (size_t)min(k0 + u, splits - 1) * stride;
-            gv[u] = p0[0];
-            uv[u] = p0[F];
-            gq[u] = pair ? p0[(size_t)pair * N] : 0.f;
-            uq[u] = pair ? p0[(size_t)pair * N + F] : 0.f;
+            gv[u] = *reinterpret_cast<const float4 *>(p0);
+            uv[u] = *reinterpret_cast<const float4 *>(p0 + F);
+            const float4 z = {0.f, 0.f, 0.f, 0.f};
+            gq[u] = pair ? *reinterpret_cast<const float4 *>(p0 + (size_t)pair * N) : z;
+            uq[u] = pair ? *reinterpret_cast<const float4 *>(p0 + (size_t)pair * N + F) : z;
         }
 #pragma unroll
-        for (int u = 0; u < 8; u++)
+        for (int u = 0; u < 4; u++)
             if (k0 + u < splits) {
-                gs += gv[u] + gq[u];
-                us += uv[u] + uq[u];
+                gs.x += gv[u].x + gq[u].x; gs.y += gv[u].y + gq[u].y;
+                gs.z += gv[u].z + gq[u].z; gs.w += gv[u].w + gq[u].w;
+                us.x += uv[u].x + uq[u].x; us.y += uv[u].y + uq[u].y;
+                us.z += uv[u].z + uq[u].z; us.w += uv[u].w + uq[u].w;
             }
     }
-    const float inv = row_inv(rs, r);
-    const float gt = gs * inv, up = us * inv;
-    const float v = gt / (1.f + expf(-gt)) * up;
-    const uint16_t hb = f32_to_bf16(v);
-    ob[(size_t)r * ldo + c] = hb;
-    if (ob_lo) ob_lo[(size_t)r * ldo + c] = f32_to_bf16(v - bf16_to_f32(hb));
+    __syncthreads();
+    if (c >= F) return;
+    const float inv = s_inv;
+    const float g4[4] = {gs.x, gs.y, gs.z, gs.w}, u4[4] = {us.x, us.y, us.z, us.w};
+    uint16_t hb[4], lb[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float gt = g4[i] * inv, up = u4[i] * inv;
+        const float v = gt / (1.f + expf(-gt)) * up;
+        hb[i] = f32_to_bf16(v);
+        lb[i] = f32_to_bf16(v - bf16_to_f32(hb[i]));
+    }
+    *reinterpret_cast<u32x2_t *>(ob + (size_t)r * ldo + c) =
+        (u32x2_t){(uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+    if (ob_lo)
+        *reinterpret_cast<u32x2_t *>(ob_lo + (size_t)r * ldo + c) =
+            (u32x2_t){(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
 }
 
 // ---------------------------------------------------------------- q/k norm, rotary, append
@@ -539,7 +556,8 @@ hipError_t launch_reduce_epilogue(const float *part, int splits, int M, int N, i
 
 hipError_t launch_swiglu(const float *part, int splits, int M, int N, int pair, uint16_t *out,
                          uint16_t *out_lo, int ldo, const RowScale &rs, hipStream_t st) {
-    hipLaunchKernelGGL(k_swiglu, dim3(ceil_div(N / 2, 256), M), dim3(256), 0, st, part, splits, M, N,
+    if ((N / 2) % 4 || ldo % 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_swiglu, dim3(ceil_div(N / 2, 1024), M), dim3(256), 0, st, part, splits, M, N,
                        pair, out, out_lo, ldo, rs);
     return hipGetLastError();
 }
