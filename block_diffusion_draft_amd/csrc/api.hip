@@ -479,7 +479,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
             g.A = f; g.lda = H; g.M = p.R; g.N = p.V; g.K = H; g.C = logits; g.ldc = p.V;
             g.rs = a.rs;
             // one split: the row scale is applied in the epilogue
-            const BigGemmPlan bp = big_gemm_plan_grid(p.R, p.V, H);
+            const BigGemmPlan bp = big_gemm_plan_grid(0, p.R, p.V, H);
             HIPCHK(launch_big_gemm(g, bp, x.st));
         } else {
             HIPCHK(launch_bf16_gemm_tiled(a, x.st));

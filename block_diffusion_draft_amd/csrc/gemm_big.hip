@@ -65,11 +65,11 @@ __device__ __forceinline__ u32x4_t scale8(const float (&q)[8], float s, float t)
 // Epilogue: lane l of tile (i, j), register v holds row 8 (v / 4) + 4 (l / 32) + v % 4,
 // column l % 32.  With the row scale, it is computed once per row of the tile into LDS
 // (rinv, free once every wave has left the K loop).
-template <int BM, int FM>
-__device__ __forceinline__ void store_tile(const BigGemmArgs &a, const f32x16_t (&acc)[FM][2],
+template <int BM, int FM, int FN = 2>
+__device__ __forceinline__ void store_tile(const BigGemmArgs &a, const f32x16_t (&acc)[FM][FN],
                                            float *rinv, int m0, int n0, int wm, int wn, int tid,
                                            int slot, bool scale) {
-    constexpr int WM = BM / 2;
+    constexpr int WM = BM / 2, WN = 32 * FN;
     const int lane = tid & 63, hl = lane >> 5, c = lane & 31;
     float *C = a.C + (size_t)slot * a.M * a.ldc;
     if (scale) {
@@ -85,8 +85,8 @@ __device__ __forceinline__ void store_tile(const BigGemmArgs &a, const f32x16_t 
             if (m0 + r >= a.M) continue;
             const float ri = scale ? rinv[r] : 1.f;
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const int n = n0 + wn * 64 + 32 * j + c;
+            for (int j = 0; j < FN; j++) {
+                const int n = n0 + wn * WN + 32 * j + c;
                 if (n < a.N) C[(size_t)(m0 + r) * a.ldc + n] = acc[i][j][v] * ri;
             }
         }
@@ -94,12 +94,12 @@ __device__ __forceinline__ void store_tile(const BigGemmArgs &a, const f32x16_t 
 }
 
 // zeroes slots [from, to) of a tile (N and ldc are multiples of 4)
-template <int BM>
+template <int BM, int TBN = BN>
 __device__ __forceinline__ void zero_slots(const BigGemmArgs &a, int m0, int n0, int from, int to, int tid) {
     for (int z = from; z < to; z++) {
         float *C = a.C + (size_t)z * a.M * a.ldc;
-        for (int e = tid; e < BM * BN / 4; e += NTH) {
-            const int m = m0 + e / (BN / 4), n = n0 + 4 * (e % (BN / 4));
+        for (int e = tid; e < BM * TBN / 4; e += NTH) {
+            const int m = m0 + e / (TBN / 4), n = n0 + 4 * (e % (TBN / 4));
             if (m < a.M && n < a.N)
                 *reinterpret_cast<float4 *>(C + (size_t)m * a.ldc + n) = make_float4(0.f, 0.f, 0.f, 0.f);
         }
@@ -133,13 +133,13 @@ struct Pieces {
             u1 = (long long)(g + 1) * U / sc.wgs;
         }
     }
-    template <int BM>
+    template <int BM, int TBN = BN>
     __device__ __forceinline__ bool next(const BigGemmArgs &a, const BigSched &sc, Piece &p) {
         if (u >= u1) return false;
         if (sc.wgs == 0) {
             const int nst = a.K / BK;
             p.m0 = blockIdx.y * BM;
-            p.n0 = blockIdx.x * BN;
+            p.n0 = blockIdx.x * TBN;
             p.s0 = (int)((long long)nst * blockIdx.z / gridDim.z);
             p.s1 = (int)((long long)nst * (blockIdx.z + 1) / gridDim.z);
             p.slot = blockIdx.z;
@@ -154,7 +154,7 @@ struct Pieces {
         const long long x = (long long)t * sc.nst;
         p.slot = g - ((int)(((x + 1) * sc.wgs + U - 1) / U) - 1);   // (range holding unit x)
         p.m0 = (t % sc.ty) * BM;
-        p.n0 = (t / sc.ty) * BN;
+        p.n0 = (t / sc.ty) * TBN;
         p.scale = sc.slots == 1 && a.rs.ssq;
         p.last = p.s1 == sc.nst;
         u += p.s1 - p.s0;
@@ -276,12 +276,12 @@ constexpr int BKD = 32, DMA_NS = 4;
 
 __device__ __forceinline__ int dma_pos(int row, int chunk) { return 4 * row + (chunk ^ ((row >> 2) & 3)); }
 
-// one tile piece over 32-deep stages [s0, s1)
-template <int BM, int NS>
+// one tile piece (BM x TBN) over 32-deep stages [s0, s1)
+template <int BM, int NS, int TBN>
 __device__ __forceinline__ void dma_piece(const BigGemmArgs &a, u32x4_t *lds, int m0, int n0, int s0,
                                           int s1, int slot, bool scale) {
-    constexpr int RG = BM / 32, WM = BM / 2, FM = WM / 32;
-    constexpr int NG = RG + 8;                        // 2 KB groups per stage (A, then W)
+    constexpr int RG = BM / 32, WM = BM / 2, FM = WM / 32, FN = TBN / 128;
+    constexpr int NG = RG + TBN / 32;                 // 2 KB groups per stage (A, then W)
     constexpr int PW = 2 * NG / 8;                    // load instructions per wave and stage
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -315,11 +315,11 @@ __device__ __forceinline__ void dma_piece(const BigGemmArgs &a, u32x4_t *lds, in
         }
     };
 
-    f32x16_t acc[FM][2];
+    f32x16_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < FN; j++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
@@ -346,31 +346,31 @@ __device__ __forceinline__ void dma_piece(const BigGemmArgs &a, u32x4_t *lds, in
 #pragma unroll
         for (int ks = 0; ks < 2; ks++) {
             const int rp = ks ? rp1 : rp0;
-            u32x4_t bf[2];
+            u32x4_t bf[FN];
 #pragma unroll
-            for (int j = 0; j < 2; j++) bf[j] = Bb[(wn * 2 + j) * 128 + rp];
+            for (int j = 0; j < FN; j++) bf[j] = Bb[(wn * FN + j) * 128 + rp];
 #pragma unroll
             for (int i = 0; i < FM; i++) {
                 const u32x4_t af = Ab[(wm * FM + i) * 128 + rp];
 #pragma unroll
-                for (int j = 0; j < 2; j++) acc[i][j] = mfma32x32x16(af, bf[j], acc[i][j]);
+                for (int j = 0; j < FN; j++) acc[i][j] = mfma32x32x16(af, bf[j], acc[i][j]);
             }
         }
     }
     __builtin_amdgcn_s_waitcnt(0xF70);      // no load may land after the piece ends
 
-    store_tile<BM, FM>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot, scale);
+    store_tile<BM, FM, FN>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot, scale);
 }
 
-template <int BM>
+template <int BM, int TBN>
 __global__ __launch_bounds__(NTH) void k_gemm_big_dma(BigGemmArgs a, BigSched sc) {
     extern __shared__ __align__(16) u32x4_t lds[];
     Pieces it(a, sc);
     Piece pc;
-    for (bool first = true; it.next<BM>(a, sc, pc); first = false) {
+    for (bool first = true; it.next<BM, TBN>(a, sc, pc); first = false) {
         if (!first) __syncthreads();                  // the previous piece is done with LDS
-        dma_piece<BM, DMA_NS>(a, lds, pc.m0, pc.n0, 2 * pc.s0, 2 * pc.s1, pc.slot, pc.scale);
-        if (pc.last) zero_slots<BM>(a, pc.m0, pc.n0, pc.slot + 1, sc.slots, threadIdx.x);
+        dma_piece<BM, DMA_NS, TBN>(a, lds, pc.m0, pc.n0, 2 * pc.s0, 2 * pc.s1, pc.slot, pc.scale);
+        if (pc.last) zero_slots<BM, TBN>(a, pc.m0, pc.n0, pc.slot + 1, sc.slots, threadIdx.x);
     }
 }
 
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(NTH) void k_gemm_big_q(BigGemmArgs a, BigSched sc) 
 
 }  // namespace
 
-size_t dma_lds_bytes(int BM) { return (size_t)DMA_NS * (BM / 32 + 8) * 2048; }
+size_t dma_lds_bytes(int BM, int TBN) { return (size_t)DMA_NS * (BM / 32 + TBN / 32) * 2048; }
 size_t q_lds_bytes(int BM) { return ((size_t)QNS * BM * 8 + 2 * 2048) * 16; }
 
 namespace {
@@ -529,10 +529,15 @@ int sk_slots(long long T, int nst, int G) {
 
 }  // namespace
 
-BigGemmPlan big_gemm_plan_grid(int M, int N, int K) {
+BigGemmPlan big_gemm_plan_grid(int wf, int M, int N, int K) {
     BigGemmPlan p;
     p.bm = M <= 128 ? 128 : 256;
-    p.grid_x = ceil_div(N, BN);
+    // bf16 at up to 128 rows with enough columns for a tile per CU even at 512 wide (the
+    // output head): 128 x 512 tiles, each wave 64 x 128, as few LDS operand bytes per
+    // MFMA as the 256 x 256 tile (measured 565 against 603 µs at 112 x 248320 x 5120;
+    // slower on the drafter's narrower products, which need their tiles for splits)
+    p.bn = wf == 0 && M <= 128 && ceil_div(N, 512) >= cu_count() ? 512 : BN;
+    p.grid_x = ceil_div(N, p.bn);
     p.grid_y = ceil_div(M, p.bm);
     p.wgs = 0;
     p.splits = 1;
@@ -548,11 +553,11 @@ BigGemmPlan big_gemm_plan(int wf, int M, int N, int K) {
     // one range per CU, 1.15× per stage (the CUs are at different K offsets, so fewer
     // operand reads hit L2), plus the epilogues of its pieces.  Each partial slot costs
     // its write and the consumer's read (M N 4 bytes each way at about 5 TB/s).
-    BigGemmPlan p = big_gemm_plan_grid(M, N, K);
+    BigGemmPlan p = big_gemm_plan_grid(wf, M, N, K);
     const int G = cu_count();
     const long long T = (long long)p.grid_x * p.grid_y;
     const int nst = K / BK;
-    const double ts = (p.bm == 256 ? 2.0 : 1.3) * (wf ? 1.3 : 1.0);
+    const double ts = (p.bm == 256 || p.bn == 512 ? 2.0 : 1.3) * (wf ? 1.3 : 1.0);
     const double slot = 2.0 * M * (double)N * 4 / 5e12 * 1e6 / ts;
     const double epi = 2.0;
     double best = 1e300;
@@ -601,9 +606,11 @@ hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream
     const int bi = p.bm == 256;
     const void *fn;
     size_t lb;
+    if ((a.wfmt != 0 || bi) && p.bn != BN) return hipErrorInvalidValue;
     if (a.wfmt == 0) {
-        fn = bi ? (const void *)k_gemm_big_dma<256> : (const void *)k_gemm_big_dma<128>;
-        lb = dma_lds_bytes(p.bm);
+        fn = bi ? (const void *)k_gemm_big_dma<256, 256>
+                : (p.bn == 512 ? (const void *)k_gemm_big_dma<128, 512> : (const void *)k_gemm_big_dma<128, 256>);
+        lb = dma_lds_bytes(p.bm, p.bn);
     } else if (a.wfmt == 1) {
         fn = bi ? (const void *)k_gemm_big_q<1, 256> : (const void *)k_gemm_big_q<1, 128>;
         lb = q_lds_bytes(p.bm);
@@ -611,11 +618,12 @@ hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream
         fn = bi ? (const void *)k_gemm_big_q<2, 256> : (const void *)k_gemm_big_q<2, 128>;
         lb = q_lds_bytes(p.bm);
     }
-    static bool attr_set[3][2] = {};
-    if (!attr_set[a.wfmt][bi]) {
+    static bool attr_set[3][2][2] = {};
+    const int wide = p.bn == 512;
+    if (!attr_set[a.wfmt][bi][wide]) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lb);
         if (e != hipSuccess) return e;
-        attr_set[a.wfmt][bi] = true;
+        attr_set[a.wfmt][bi][wide] = true;
     }
     void *args[] = {const_cast<BigGemmArgs *>(&a), &sc};
     const hipError_t e = hipLaunchKernel(fn, grid, dim3(NTH), args, lb, st);

@@ -215,7 +215,8 @@ struct BigGemmArgs {
     RowScale rs;
 };
 struct BigGemmPlan {
-    int bm, grid_x, grid_y;      // tile rows (128 / 256); N and M tiles
+    int bm, bn, grid_x, grid_y;  // tile rows (128 / 256) and columns (256; 512 for bf16 at
+                                 // up to 128 rows); N and M tiles
     int splits;                  // partial slots [splits][M][N] the consumer sums
     int wgs;                     // 0: grid (N tiles, M tiles, splits); else stream-K workgroups
     size_t part_bytes;
@@ -224,5 +225,5 @@ bool big_gemm_ok(int wf, int M, int N, int K);
 // the schedule (grid with K splits, or stream-K) of least estimated time; wf as in BigGemmArgs
 BigGemmPlan big_gemm_plan(int wf, int M, int N, int K);
 // grid, one split
-BigGemmPlan big_gemm_plan_grid(int M, int N, int K);
+BigGemmPlan big_gemm_plan_grid(int wf, int M, int N, int K);
 hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream_t st);
