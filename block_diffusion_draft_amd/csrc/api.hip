@@ -71,7 +71,7 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
     // the batch already fills the chip (fewer partials to merge)
     const int win = c->window;
     const long long wgs64 = (long long)B * p.n_kv * ((win + 63) / 64);
-    p.attn_chunk = wgs64 >= 16384 ? 256 : (wgs64 >= 4096 ? 128 : 64);
+    p.attn_chunk = wgs64 >= 4096 ? 256 : 64;
     p.attn_nch = win > 0 ? (win + p.attn_chunk - 1) / p.attn_chunk : 0;
     p.topk_nch = (p.V + topk_chunk_size() - 1) / topk_chunk_size();
     // output-head rows held in LDS: K/32 fragments of 512 bytes (+1 zero entry)
