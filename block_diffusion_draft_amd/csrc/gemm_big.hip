@@ -601,6 +601,8 @@ bool big_gemm_ok(int wf, int M, int N, int K) {
 hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream_t st) {
     if (!big_gemm_ok(a.wfmt, a.M, a.N, a.K) || a.wfmt < 0 || a.wfmt > 2) return hipErrorInvalidValue;
     if (p.wgs && (p.wgs % 8 || a.ldc % 4)) return hipErrorInvalidValue;
+    // operand rows are fetched as 16-byte pieces straight into LDS
+    if (reinterpret_cast<uintptr_t>(a.A) % 16 || a.lda % 8) return hipErrorInvalidValue;
     BigSched sc = {p.wgs, p.grid_x, p.grid_y, a.K / BK, p.splits};
     const dim3 grid = p.wgs ? dim3(p.wgs) : dim3(p.grid_x, p.grid_y, p.splits);
     const int bi = p.bm == 256;
@@ -618,12 +620,15 @@ hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream
         fn = bi ? (const void *)k_gemm_big_q<2, 256> : (const void *)k_gemm_big_q<2, 128>;
         lb = q_lds_bytes(p.bm);
     }
-    static bool attr_set[3][2][2] = {};
+    // (the LDS limit is raised once per device and kernel)
+    static bool attr_set[64][3][2][2] = {};
     const int wide = p.bn == 512;
-    if (!attr_set[a.wfmt][bi][wide]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!attr_set[dev][a.wfmt][bi][wide]) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lb);
         if (e != hipSuccess) return e;
-        attr_set[a.wfmt][bi][wide] = true;
+        attr_set[dev][a.wfmt][bi][wide] = true;
     }
     void *args[] = {const_cast<BigGemmArgs *>(&a), &sc};
     const hipError_t e = hipLaunchKernel(fn, grid, dim3(NTH), args, lb, st);
