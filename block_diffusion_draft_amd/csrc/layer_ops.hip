@@ -251,6 +251,17 @@ __global__ __launch_bounds__(256) void k_swiglu(const float *part, int splits, i
             (u32x2_t){(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
 }
 
+// row_inv for a whole wave (every lane calls it, same r): lane i loads partial i (and
+// i + 64, ...), the partials are added by a wave reduction
+__device__ __forceinline__ float row_inv_wave(const RowScale &s, int r, int lane) {
+    if (!s.ssq) return 1.f;
+    const int br = s.map ? (r / (s.map - 1)) * s.map + r % (s.map - 1) + 1 : r;
+    const float *p = s.ssq + (size_t)br * s.nchunk;
+    float ss = 0.f;
+    for (int i = lane; i < s.nchunk; i += 64) ss += p[i];
+    return rsqrtf(wave_sum(ss) / s.n + s.eps);
+}
+
 // ---------------------------------------------------------------- q/k norm, rotary, append
 // One wave per (row, head).  Lane j < d/2 owns the rotary pair (j, j + d/2).
 __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
@@ -276,26 +287,27 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
     const size_t pstride = (size_t)a.B * (a.T + a.t_new) * (qd + 2 * kd);
     float x1 = 0.f, x2 = 0.f;
     if (lane < half) {
-        // 8 splits of loads in flight per batch (indices past the end are clamped and
-        // their values dropped)
-        for (int s0 = 0; s0 < a.splits; s0 += 8) {
-            float v1[8], v2[8];
+        // up to 4 splits of loads in flight per batch, only the splits present
+        for (int s0 = 0; s0 < a.splits; s0 += 4) {
+            float v1[4], v2[4];
 #pragma unroll
-            for (int u = 0; u < 8; u++) {
-                const int sp = min(s0 + u, a.splits - 1);
-                v1[u] = x[sp * pstride + lane];
-                v2[u] = x[sp * pstride + lane + half];
+            for (int u = 0; u < 4; u++) {
+                v1[u] = v2[u] = 0.f;
+                if (s0 + u < a.splits) {
+                    v1[u] = x[(s0 + u) * pstride + lane];
+                    v2[u] = x[(s0 + u) * pstride + lane + half];
+                }
             }
 #pragma unroll
-            for (int u = 0; u < 8; u++)
-                if (s0 + u < a.splits) {
-                    x1 += v1[u];
-                    x2 += v2[u];
-                }
+            for (int u = 0; u < 4; u++) {
+                x1 += v1[u];
+                x2 += v2[u];
+            }
         }
     }
-    // the projection input's deferred RMSNorm
-    const float rinv = is_blk ? row_inv(a.blk, r) : row_inv(a.ctx, r - nblk);
+    // the projection input's deferred RMSNorm (its partial sums of squares split over
+    // the lanes)
+    const float rinv = is_blk ? row_inv_wave(a.blk, r, lane) : row_inv_wave(a.ctx, r - nblk, lane);
     x1 *= rinv;
     x2 *= rinv;
     if (is_q || is_k) {
