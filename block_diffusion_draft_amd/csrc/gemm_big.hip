@@ -501,19 +501,11 @@ size_t q_lds_bytes(int BM) { return ((size_t)QNS * BM * 8 + 2 * 2048) * 16; }
 
 namespace {
 
-// compute units of the current device (the stream-K range count), a multiple of 8
-int cu_count() {
-    static int cus[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cus[dev]) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 8)
-            v = 256;
-        cus[dev] = v & ~7;
-    }
-    return cus[dev];
-}
+// Stream-K range count and the CU count the schedule is planned for: 256, the CUs of
+// this part.  Fixed rather than read from the device, so that a product's partial sums
+// (hence its rounding) are the same on every device; on a part with another CU count
+// the 256 ranges simply run in more or fewer rounds.
+int cu_count() { return 256; }
 
 // most pieces any tile is cut into by G stream-K ranges over T tiles of nst stages
 int sk_slots(long long T, int nst, int G) {
