@@ -107,18 +107,19 @@ __device__ void reduce_rows_block(const ReduceRowsArgs &a, int cx, int r) {
     const size_t stride = (size_t)(pair ? 2 * M_out : M_out) * N;
     const float *p = part + (size_t)r * N + c0 + 4 * lane;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    // this wave's splits k = wave, wave + 4, ...: 8 of them in flight per batch
-    for (int k0 = wave; k0 < splits; k0 += 32) {
-        float4 va[8], vb[8];
+    // this wave's splits k = wave, wave + 4, ...: 4 of them in flight per batch (few
+    // registers, so more workgroups stay resident)
+    for (int k0 = wave; k0 < splits; k0 += 16) {
+        float4 va[4], vb[4];
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
+        for (int u = 0; u < 4; u++) {
             const float *q = p + (size_t)min(k0 + 4 * u, splits - 1) * stride;
             va[u] = *reinterpret_cast<const float4 *>(q);
             vb[u] = pair ? *reinterpret_cast<const float4 *>(q + (size_t)pair * N)
                          : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
-        for (int u = 0; u < 8; u++)
+        for (int u = 0; u < 4; u++)
             if (k0 + 4 * u < splits) {
                 s.x += va[u].x + vb[u].x;
                 s.y += va[u].y + vb[u].y;
