@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void k_reduce(const float *part, int splits, i
 
 // ---------------------------------------------------------------- SwiGLU from split partials
 // Workgroup per (1024 columns, output row r), four consecutive columns per thread
-// (16-byte loads): gate and up (columns c and c + N/2 of the [gate | up] product) summed
+// (16-byte loads, three splits in flight): gate and up (columns c and c + N/2 of the [gate | up] product) summed
 // over the splits (in split order) and the [hi; lo] row pair, scaled by the row's
 // deferred 1 / rms (formed once per workgroup), then silu(gate) * up as a bf16 (hi, lo)
 // pair.  Needs N / 2 a multiple of 4.
@@ -213,10 +213,10 @@ __global__ __launch_bounds__(256) void k_swiglu(const float *part, int splits, i
     const size_t stride = (size_t)(pair ? 2 * M : M) * N;
     const float *p = part + (size_t)r * N + min(c, F - 4);
     float4 gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < splits; k0 += 4) {
-        float4 gv[4], uv[4], gq[4], uq[4];
+    for (int k0 = 0; k0 < splits; k0 += 3) {
+        float4 gv[3], uv[3], gq[3], uq[3];
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
+        for (int u = 0; u < 3; u++) {
             const float *p0 = p + (size_t)min(k0 + u, splits - 1) * stride;
             gv[u] = *reinterpret_cast<const float4 *>(p0);
             uv[u] = *reinterpret_cast<const float4 *>(p0 + F);
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256) void k_swiglu(const float *part, int splits, i
             uq[u] = pair ? *reinterpret_cast<const float4 *>(p0 + (size_t)pair * N + F) : z;
         }
 #pragma unroll
-        for (int u = 0; u < 4; u++)
+        for (int u = 0; u < 3; u++)
             if (k0 + u < splits) {
                 gs.x += gv[u].x + gq[u].x; gs.y += gv[u].y + gq[u].y;
                 gs.z += gv[u].z + gq[u].z; gs.w += gv[u].w + gq[u].w;
