@@ -352,9 +352,12 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
 // so that z_t = W_c . vec(o_t) = the sum of zp over (h, cc).
 constexpr int MC = 32;              // columns per merge workgroup
 
-constexpr int MW = 9;               // chunk partials per lane loaded up front (x 4 waves)
+// MW: chunk partials per lane loaded up front (x 4 waves): 9 covers the 33 chunks of a
+// 2048-key window in 64-key chunks; 3 the 9 of 256-key chunks (fewer registers, more
+// resident workgroups).  Chunks past 4 MW are read in further batches, same order.
 constexpr int MAXE = 4;             // conv-tap outputs per thread (T 2 n_q <= 1024)
 
+template <int MW>
 __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
     const int h = blockIdx.x, cc = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -585,7 +588,10 @@ hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st) {
     // (then the W_c slice, from the next 16-byte boundary)
     size_t lds = (size_t)(a.T * (a.n_chunks + 1) + a.T * MC + 4 * a.T * MC) * 4;
     lds = (lds + 15) / 16 * 16 + (size_t)2 * a.n_q * MC * 2;
-    hipLaunchKernelGGL(k_attn_merge, dim3(a.n_q, a.d / MC, a.B), dim3(256), lds, st, a);
+    if (a.n_chunks + 1 <= 12)
+        hipLaunchKernelGGL(k_attn_merge<3>, dim3(a.n_q, a.d / MC, a.B), dim3(256), lds, st, a);
+    else
+        hipLaunchKernelGGL(k_attn_merge<9>, dim3(a.n_q, a.d / MC, a.B), dim3(256), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_conv_apply, dim3(a.B * a.T, a.n_q / CONV_HEADS), dim3(256), 0, st, a);
