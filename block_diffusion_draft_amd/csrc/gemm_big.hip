@@ -32,7 +32,8 @@ namespace {
 constexpr int BN = 256, BK = 64, NTH = 512;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
-// schedule of the workgroups: wgs == 0: grid (N tiles, M tiles, K splits); else stream-K
+// schedule of the workgroups: wgs == 0: one workgroup per (N tile, M tile, K split)
+// item (a 1-D grid, items dealt to XCDs in contiguous runs); else stream-K
 // over wgs workgroups (a multiple of 8), tx x ty tiles of nst stages, `slots` slots
 struct BigSched {
     int wgs, tx, ty, nst, slots;
@@ -137,13 +138,21 @@ struct Pieces {
     __device__ __forceinline__ bool next(const BigGemmArgs &a, const BigSched &sc, Piece &p) {
         if (u >= u1) return false;
         if (sc.wgs == 0) {
+            // grid of tx * ty * slots workgroups, one piece each: workgroup b takes item
+            // L, the items in (split, N tile, M tile) order with M fastest, dealt so that
+            // each XCD runs a contiguous run of items (the M tiles of one weight slab,
+            // and neighbouring slabs of one K split, share that XCD's L2)
+            const int total = sc.tx * sc.ty * sc.slots, q = total >> 3, r = total & 7;
+            const int x8 = blockIdx.x & 7;
+            const int L = x8 * q + min(x8, r) + (int)(blockIdx.x >> 3);
+            const int z = L / (sc.tx * sc.ty), rem = L - z * sc.tx * sc.ty;
             const int nst = a.K / BK;
-            p.m0 = blockIdx.y * BM;
-            p.n0 = blockIdx.x * TBN;
-            p.s0 = (int)((long long)nst * blockIdx.z / gridDim.z);
-            p.s1 = (int)((long long)nst * (blockIdx.z + 1) / gridDim.z);
-            p.slot = blockIdx.z;
-            p.scale = gridDim.z == 1 && a.rs.ssq;
+            p.m0 = (rem % sc.ty) * BM;
+            p.n0 = (rem / sc.ty) * TBN;
+            p.s0 = (int)((long long)nst * z / sc.slots);
+            p.s1 = (int)((long long)nst * (z + 1) / sc.slots);
+            p.slot = z;
+            p.scale = sc.slots == 1 && a.rs.ssq;
             p.last = false;
             u = u1;
             return true;
@@ -596,7 +605,7 @@ hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream
     // operand rows are fetched as 16-byte pieces straight into LDS
     if (reinterpret_cast<uintptr_t>(a.A) % 16 || a.lda % 8) return hipErrorInvalidValue;
     BigSched sc = {p.wgs, p.grid_x, p.grid_y, a.K / BK, p.splits};
-    const dim3 grid = p.wgs ? dim3(p.wgs) : dim3(p.grid_x, p.grid_y, p.splits);
+    const dim3 grid(p.wgs ? p.wgs : p.grid_x * p.grid_y * p.splits);
     const int bi = p.bm == 256;
     const void *fn;
     size_t lb;
