@@ -22,8 +22,10 @@
 // leave a partly empty last round of workgroups: the (tile, 64-deep K stage) units are
 // cut into one equal range per CU; a range covers pieces of one to a few tiles, the
 // piece with ordinal j of its tile goes to slot j, and a tile's last piece zeroes the
-// tile's unused slots.  With a single slot, an optional row scale (deferred RMSNorm) is
-// applied in the epilogue.
+// tile's unused slots.  Either way the work is dealt so that each XCD (workgroup b
+// runs on XCD b mod 8) takes a contiguous run of it: the M tiles of a weight slab
+// then share that XCD's L2.  With a single slot, an optional row scale (deferred
+// RMSNorm) is applied in the epilogue.
 #include "common.h"
 #include "kernels.h"
 
