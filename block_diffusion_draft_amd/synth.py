@@ -249,12 +249,13 @@ def linear_shapes(s):
     return out
 
 
-def make_weights(s, seed, gain_jitter=0.0):
+def make_weights(s, seed, gain_jitter=0.0, code_std=0.02):
     """All drafter weights of shape `s` as a dict (the checker's format).
 
     Linear weights: ("q4k" or "q8_0", uint8 bytes) or ("bf16", uint16 [rows, cols]).
     Everything else: uint16 bf16 arrays.  embed and lm_head are the same array
-    (the draft shares the target's embedding table and output head).
+    (the draft shares the target's embedding table and output head).  code_std is
+    the standard deviation of the two selector codebooks (``selector_codebooks``).
     """
     W = {}
     for name, rows, cols in linear_shapes(s):
@@ -284,9 +285,17 @@ def make_weights(s, seed, gain_jitter=0.0):
     W["lm_head"] = E
     W["mask_emb"] = normal_bf16(seed, "mask_emb", (s.hidden,), 0.02)
     W["sel_proj"] = normal_bf16(seed, "sel_proj", (s.sel_rank, s.hidden), 0.02)
-    W["code_a"] = normal_bf16(seed, "code_a", (s.vocab, s.sel_rank), 0.02)
-    W["code_b"] = normal_bf16(seed, "code_b", (s.vocab, s.sel_rank), 0.02)
+    W["code_a"], W["code_b"] = selector_codebooks(s, seed, code_std)
     return W
+
+
+def selector_codebooks(s, seed, std=0.02):
+    """The two [vocab, rank] bf16 selector codebooks, N(0, std).  At the workloads'
+    std 0.02 the pair term s <A[u], B[v]> is about 4e-4, far below the gaps between
+    candidate log-probabilities; std 1 makes it N(0, 1), so the transitions decide
+    the selected path."""
+    return (normal_bf16(seed, "code_a", (s.vocab, s.sel_rank), std),
+            normal_bf16(seed, "code_b", (s.vocab, s.sel_rank), std))
 
 
 class WindowCache:

@@ -171,6 +171,22 @@ def test_full_step_b1_parity():
     ref = parity.run_oracle(wl, bufs.host_W, bufs.inputs)
     g = full_check(wl, bufs, ref)
     check_verify(bufs, g)
+    # the same step with N(0, 1) selector codebooks: the pair term ~ N(0, 1) decides
+    # the path (top 16, rank 256); it must be the float64 Viterbi path over the GPU's
+    # own candidates and differ from the per-position argmax
+    from tests.test_gpu_select import path_checks
+    ca, cb = synth.selector_codebooks(wl.shape, wl.seed + 1000, std=1.0)
+    bufs.dw.tensors["code_a"].copy_(torch.from_numpy(ca.view(np.int16)))
+    bufs.dw.tensors["code_b"].copy_(torch.from_numpy(cb.view(np.int16)))
+    bufs.step(dbg=False)
+    torch.cuda.synchronize()
+    ids, lp = bufs.cand_ids.cpu().numpy(), bufs.cand_logp.cpu().numpy()
+    draft = bufs.draft.cpu().numpy()
+    assert np.array_equal(ids, g["ids"])              # candidates do not depend on codebooks
+    nonarg = path_checks(ids, lp, draft, ca, cb, wl.shape.pair_scale, brute=False)
+    say(f"  N(0, 1) codebooks: path {draft[0].tolist()} (argmax path "
+        f"{ids[0, :, 0].tolist()})")
+    assert nonarg == 1
 
 
 def test_tiny_step_tied_logits_take_lowest_ids():
