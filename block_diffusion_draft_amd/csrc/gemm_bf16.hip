@@ -3,10 +3,7 @@
 //  * tiled: 128 x 128 output tile per workgroup (2 x 2 waves of 64 x 64), K in
 //    steps of 32 staged through double-buffered LDS in MFMA lane order.  Used for
 //    the unquantised drafter matrices at many rows and for the shared output head
-//    when more than 16 rows need logits.  The same kernel reads Q8_0 weights in their
-//    tiled layout (more than 16 rows, or K not a multiple of 1024): each k-step is
-//    one Q8_0 block, decoded on load to bf16(d q) (round to nearest even, relative
-//    error <= 2^-9 per weight; the 16-row streaming kernel keeps d q exact).
+//    when more than 16 rows need logits.
 //  * skinny: at most 8 rows (the 7 proposal rows of one draft block).  The rows
 //    sit in LDS for the whole launch; every wave streams its own contiguous run
 //    of 16-row weight tiles over the full K with 8 fragment loads in flight, so
@@ -26,31 +23,7 @@ __device__ __forceinline__ const uint16_t *seg_row(const Bf16GemmArgs &a, int n)
 
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
-// row n of a Q8_0 matrix set in the tiled layout: the base of its tile's units and
-// its row within the tile
-__device__ __forceinline__ const unsigned char *q8_tile_row(const Bf16GemmArgs &a, int n, int &r) {
-    int si = 0;
-    while (si + 1 < a.nseg && n >= a.seg_end[si]) si++;
-    const int nn = n - (si == 0 ? 0 : a.seg_end[si - 1]);
-    r = nn & 15;
-    return reinterpret_cast<const unsigned char *>(a.w[si]) +
-           (size_t)(nn >> 4) * (a.K / 256) * Q8_UNIT_BYTES;
-}
-
-// bf16(d q) of 8 signed bytes, k order
-__device__ __forceinline__ u32x4_t q8_scaled(u32x2_t q, float d) {
-    u32x4_t o;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const uint32_t w = q[i >> 1] >> (16 * (i & 1));
-        const float lo = d * (float)(int8_t)(w & 0xFF), hi = d * (float)(int8_t)(w >> 8);
-        o[i] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-    }
-    return o;
-}
-
-// WF 0: bf16 weights [N][K]; WF 1: Q8_0 weights in the tiled layout
-template <int WF>
+// bf16 weights [N][K]
 __global__ __launch_bounds__(256) void k_gemm_tiled(Bf16GemmArgs a) {
     __shared__ u32x4_t As[2][8][64];
     __shared__ u32x4_t Bs[2][8][64];
@@ -61,15 +34,12 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(Bf16GemmArgs a) {
 
     const uint16_t *arow[2];
     const uint16_t *brow[2];
-    const unsigned char *bq[2];
-    int rq[2] = {0, 0};
 #pragma unroll
     for (int h = 0; h < 2; h++) {
         const int m = m0 + lr + 64 * h;
         arow[h] = m < a.M ? a.A + (size_t)m * a.lda : nullptr;
         const int n = n0 + lr + 64 * h;
-        if (WF == 0) brow[h] = n < a.N ? seg_row(a, n) : nullptr;
-        else bq[h] = n < a.N ? q8_tile_row(a, n, rq[h]) : nullptr;
+        brow[h] = n < a.N ? seg_row(a, n) : nullptr;
     }
     const int nk = a.K / 32;
     u32x4_t ra[2], rb[2];
@@ -78,21 +48,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(Bf16GemmArgs a) {
         for (int h = 0; h < 2; h++) {
             const int k = kt * 32 + 8 * lg;
             ra[h] = arow[h] ? *reinterpret_cast<const u32x4_t *>(arow[h] + k) : (u32x4_t){0, 0, 0, 0};
-            if (WF == 0) {
-                rb[h] = brow[h] ? *reinterpret_cast<const u32x4_t *>(brow[h] + k)
-                                : (u32x4_t){0, 0, 0, 0};
-            } else if (bq[h]) {
-                // k-step kt = block kt: unit kt / 8 of the row's tile, block j = kt % 8
-                const unsigned char *unit = bq[h] + (size_t)(kt >> 3) * Q8_UNIT_BYTES;
-                const int j = kt & 7;
-                const u32x2_t q = *reinterpret_cast<const u32x2_t *>(
-                    unit + 256 + 1024 * (j >> 1) + 16 * (16 * lg + rq[h]) + 8 * (j & 1));
-                const float d = half_bits_to_f32(*reinterpret_cast<const uint16_t *>(
-                    unit + 16 * rq[h] + 2 * j));
-                rb[h] = q8_scaled(q, d);
-            } else {
-                rb[h] = (u32x4_t){0, 0, 0, 0};
-            }
+            rb[h] = brow[h] ? *reinterpret_cast<const u32x4_t *>(brow[h] + k) : (u32x4_t){0, 0, 0, 0};
         }
     };
     auto lstore = [&](int buf) {
@@ -385,12 +341,7 @@ __global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a, int tiles_p
 
 hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st) {
     dim3 grid(ceil_div(a.N, 128), ceil_div(a.M, 128));
-    if (a.wfmt == 1) {
-        if (a.K % 256) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(k_gemm_tiled<1>, grid, dim3(256), 0, st, a);
-    } else {
-        hipLaunchKernelGGL(k_gemm_tiled<0>, grid, dim3(256), 0, st, a);
-    }
+    hipLaunchKernelGGL(k_gemm_tiled, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -5,10 +5,12 @@
 //
 // At 100+ rows the drafter's products are MFMA-bound (2 M flops per weight against
 // 0.56-2 bytes), so the weights are decoded once per 256 x 256 output tile into bf16
-// MFMA operands (Q4_K: d sc q - dmin m, Q8_0: d q, rounded to nearest even: relative
-// error <= 2^-9 per weight) and the tile runs on v_mfma_f32_32x32x16_bf16 (on this chip
-// the 32x32 form runs at twice the rate of the 16x16x32 one: 2.4 against 1.3 PFLOP/s
-// measured with independent chains).
+// MFMA operands and the tile runs on v_mfma_f32_32x32x16_bf16 (on this chip the 32x32
+// form runs at twice the rate of the 16x16x32 one: 2.4 against 1.3 PFLOP/s measured
+// with independent chains).  A quantised weight w (Q4_K: d sc q - dmin m, Q8_0: d q,
+// formed in fp32) enters as two bf16 terms, hi = bf16(w) and lo = bf16(w - hi), each
+// multiplied by the same activation operand: hi + lo carries w to 2^-18 of itself,
+// below the fp32 accumulation's own rounding over K of a few thousand.
 //
 // Workgroup: 8 waves (2 along M x 4 along N), each a 128 x 64 block (BM = 256; 64 x 64
 // for BM = 128) of 32 x 32 MFMA tiles.  The operands sit in LDS in MFMA lane order,
@@ -16,7 +18,7 @@
 // W) travel global -> LDS by direct loads (global_load_lds_dwordx4: no registers, no
 // LDS store instructions) through a ring of K stages, several stages in flight while one
 // is multiplied; Q8_0 / Q4_K weights are loaded into registers two stages ahead and
-// decoded into a double-buffered LDS tile.
+// decoded into a double-buffered LDS tile of (hi, lo) operands.
 //
 // Work split: a grid over (N tile, M tile, K split), or stream-K where the tiles would
 // leave a partly empty last round of workgroups: the (tile, 64-deep K stage) units are
@@ -59,10 +61,24 @@ struct WRaw {
     u32x4_t v[4];
 };
 
-// bf16 of x0 * s - t for the 8 integers of a fragment entry
-__device__ __forceinline__ u32x4_t scale8(const float (&q)[8], float s, float t) {
-    return (u32x4_t){pack_bf16x2(q[0] * s - t, q[1] * s - t), pack_bf16x2(q[2] * s - t, q[3] * s - t),
-                     pack_bf16x2(q[4] * s - t, q[5] * s - t), pack_bf16x2(q[6] * s - t, q[7] * s - t)};
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// bf16 (round to nearest even, v_cvt_pk_bf16_f32) of two floats, a in the low half
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// the 8 weights w_b = q_b s - t of a fragment entry as bf16 (hi, lo) operands
+__device__ __forceinline__ void split8(const float (&q)[8], float s, float t, u32x4_t &hi,
+                                       u32x4_t &lo) {
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const float w0 = q[2 * p] * s - t, w1 = q[2 * p + 1] * s - t;
+        const uint32_t h = cvt_bf16x2(w0, w1);
+        hi[p] = h;
+        lo[p] = cvt_bf16x2(w0 - __uint_as_float(h << 16), w1 - __uint_as_float(h & 0xFFFF0000u));
+    }
 }
 
 // Epilogue: lane l of tile (i, j), register v holds row 8 (v / 4) + 4 (l / 32) + v % 4,
@@ -191,88 +207,77 @@ __device__ __forceinline__ void wq_setup(const BigGemmArgs &a, int n0, int tid,
     }
 }
 
-// raw bytes of the stage at k0 (64 deep): Q8_0: the 16 bytes of blocks 2 p, 2 p + 1 of
-// the lane's slot and their two fp16 scales; Q4_K: 8 bytes of the lane's slot (chunk c of
-// the super-block) and the column's 16-byte header.  Four loads per thread.
+// raw bytes of the 32-deep stage st (K [32 st, 32 st + 32)): Q8_0: 8 bytes of block st
+// of the lane's slot (k group ln / 16) and the block's fp16 scale; Q4_K: the 8 bytes of
+// chunk c = (st % 8) / 2 of the lane's slot (sub-block st % 8 is their low or high
+// nibbles) and the column's 16-byte header.  Two loads per task, four per thread.
 template <int WF>
-__device__ __forceinline__ void wq_load(WRaw &rw, const unsigned char *const (&wbase)[2], int tid, int k0) {
-    if (WF == 1) {
-        const int g = k0 >> 8, p = (k0 & 255) >> 6;
+__device__ __forceinline__ void wq_load(WRaw &rw, const unsigned char *const (&wbase)[2], int tid, int st) {
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int ln = (tid + NTH * i) & 63;
+    for (int i = 0; i < 2; i++) {
+        const int ln = (tid + NTH * i) & 63;
+        if (WF == 1) {
+            const int g = st >> 3, blk = st & 7, pr = blk >> 1;
             const unsigned char *unit = wbase[i] + (size_t)g * Q8_UNIT_BYTES;
-            rw.v[2 * i] = *reinterpret_cast<const u32x4_t *>(unit + 256 + 1024 * p + 16 * ln);
-            rw.v[2 * i + 1].x = *reinterpret_cast<const uint32_t *>(unit + 16 * (ln & 15) + 4 * p);
-        }
-    } else {
-        const int sb = k0 >> 8, c = (k0 & 255) >> 6;
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int ln = (tid + NTH * i) & 63;
+            const u32x2_t q = *reinterpret_cast<const u32x2_t *>(unit + 256 + 1024 * pr + 16 * ln + 8 * (blk & 1));
+            const uint32_t sc = *reinterpret_cast<const uint32_t *>(unit + 16 * (ln & 15) + 4 * pr);
+            rw.v[2 * i] = (u32x4_t){q.x, q.y, (uint32_t)blk, 0u};
+            rw.v[2 * i + 1] = (u32x4_t){sc, 0u, 0u, 0u};
+        } else {
+            const int sb = st >> 3, j = st & 7, c = j >> 1;
             const unsigned char *unit = wbase[i] + (size_t)sb * Q4K_UNIT_BYTES;
             const u32x2_t q = *reinterpret_cast<const u32x2_t *>(unit + 256 + 1024 * (c >> 1) + 16 * ln + 8 * (c & 1));
-            rw.v[2 * i] = (u32x4_t){q.x, q.y, (uint32_t)c, 0u};
+            rw.v[2 * i] = (u32x4_t){q.x, q.y, (uint32_t)j, 0u};
             rw.v[2 * i + 1] = *reinterpret_cast<const u32x4_t *>(unit + 16 * (ln & 15));
         }
     }
 }
 
-// decode a stage's raw bytes into bf16 MFMA operands in the W tile Bb ([4 ks][8][64],
-// slot swz): entry o0 holds k 0..31 of the stage, o1 k 32..63
+// decode a stage's raw bytes into the (hi, lo) MFMA operands of the W tile Bb
+// ([2 (hi, lo)][2 ks][8][64], slot swz): task (column, k group kg) fills entry kg of its
+// column's fragment: ks = kg / 2, lane (column % 32) + 32 (kg % 2)
 template <int WF>
 __device__ __forceinline__ void wq_store(u32x4_t *Bb, const WRaw &rw, const bool (&wok)[2], int tid) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int e = tid + NTH * i, cg = e / 64, ln = e & 63;
-        u32x4_t o0 = {0u, 0u, 0u, 0u}, o1 = {0u, 0u, 0u, 0u};
+        u32x4_t oh = {0u, 0u, 0u, 0u}, ol = {0u, 0u, 0u, 0u};
         if (wok[i]) {
             const u32x4_t q = rw.v[2 * i], h = rw.v[2 * i + 1];
-            float lo[8], hi[8];
+            float v[8];
             if (WF == 1) {
 #pragma unroll
-                for (int b = 0; b < 8; b++) {
-                    lo[b] = (float)(int8_t)((b < 4 ? q.x : q.y) >> (8 * (b & 3)));
-                    hi[b] = (float)(int8_t)((b < 4 ? q.z : q.w) >> (8 * (b & 3)));
-                }
-                o0 = scale8(lo, half_bits_to_f32(h.x & 0xFFFFu), 0.f);
-                o1 = scale8(hi, half_bits_to_f32(h.x >> 16), 0.f);
+                for (int b = 0; b < 8; b++)
+                    v[b] = (float)(int8_t)((b < 4 ? q.x : q.y) >> (8 * (b & 3)));
+                const uint32_t sc = (q.z & 1) ? (h.x >> 16) : (h.x & 0xFFFFu);
+                split8(v, half_bits_to_f32(sc), 0.f, oh, ol);
             } else {
+                // sub-block j: the low (j even) or high (j odd) nibbles of the chunk
+                const int j = (int)q.z, shift = 4 * (j & 1);
 #pragma unroll
-                for (int b = 0; b < 8; b++) {
-                    const uint32_t w = (b < 4 ? q.x : q.y) >> (8 * (b & 3));
-                    lo[b] = (float)(w & 15u);
-                    hi[b] = (float)((w >> 4) & 15u);
-                }
-                // header: d, dmin, 6-bit scales and mins of sub-blocks 2 c, 2 c + 1
-                const int c = (int)q.z;
+                for (int b = 0; b < 8; b++)
+                    v[b] = (float)((((b < 4 ? q.x : q.y) >> (8 * (b & 3))) >> shift) & 15u);
+                // header: d, dmin, 6-bit scale and min of sub-block j
                 const float d = half_bits_to_f32(h.x & 0xFFFFu);
                 const float dmin = half_bits_to_f32(h.x >> 16);
                 const uint32_t sb[3] = {h.y, h.z, h.w};
                 auto byte = [&](int i2) { return (sb[i2 >> 2] >> (8 * (i2 & 3))) & 0xFFu; };
-                float sc[2], mn[2];
-#pragma unroll
-                for (int u = 0; u < 2; u++) {
-                    const int j = 2 * c + u;
-                    uint32_t s6, m6;
-                    if (j < 4) {
-                        s6 = byte(j) & 63u;
-                        m6 = byte(j + 4) & 63u;
-                    } else {
-                        s6 = (byte(j + 4) & 15u) | ((byte(j - 4) >> 6) << 4);
-                        m6 = (byte(j + 4) >> 4) | ((byte(j) >> 6) << 4);
-                    }
-                    sc[u] = d * (float)s6;
-                    mn[u] = dmin * (float)m6;
+                uint32_t s6, m6;
+                if (j < 4) {
+                    s6 = byte(j) & 63u;
+                    m6 = byte(j + 4) & 63u;
+                } else {
+                    s6 = (byte(j + 4) & 15u) | ((byte(j - 4) >> 6) << 4);
+                    m6 = (byte(j + 4) >> 4) | ((byte(j) >> 6) << 4);
                 }
-                o0 = scale8(lo, sc[0], mn[0]);
-                o1 = scale8(hi, sc[1], mn[1]);
+                split8(v, d * (float)s6, dmin * (float)m6, oh, ol);
             }
         }
-        const int kgr = ln >> 4, col = 16 * cg + (ln & 15);
-        const int li = (col & 31) + 32 * (kgr & 1);
-        Bb[((kgr >> 1) * 8 + (col >> 5)) * 64 + swz(li, kgr)] = o0;
-        Bb[((2 + (kgr >> 1)) * 8 + (col >> 5)) * 64 + swz(li, 4 + kgr)] = o1;
+        const int kg = ln >> 4, col = 16 * cg + (ln & 15);
+        const int li = (col & 31) + 32 * (kg & 1);
+        const int at = ((kg >> 1) * 8 + (col >> 5)) * 64 + swz(li, kg);
+        Bb[at] = oh;
+        Bb[1024 + at] = ol;
     }
 }
 
@@ -385,25 +390,23 @@ __global__ __launch_bounds__(NTH) void k_gemm_big_dma(BigGemmArgs a, BigSched sc
     }
 }
 
-// Q8_0 / Q4_K weights: A through a ring of QNS stages of 64 K (two in flight while one
-// is multiplied): stage rows of 128 bytes, eight lanes per row, lane L of a load
-// instruction at slot L of its 1 KB piece (row 8 piece + L / 8) loading chunk
-// (L % 8) ^ ((row / 2) % 8), so the 16 rows of an MFMA operand load fall on distinct bank
-// groups.  The raw weight bytes of a stage are loaded into registers two stages ahead
-// (two register sets, alternating) and decoded into the double-buffered W tile after
-// the current stage's MFMAs.
+// Q8_0 / Q4_K weights, 32-deep K stages: A global -> LDS by direct loads through a ring
+// of QNS stages (the bf16 path's 64-byte row pieces and chunk swizzle), the raw weight
+// bytes of a stage loaded into registers two stages ahead (two register sets,
+// alternating) and decoded into the double-buffered (hi, lo) W tile after the current
+// stage's MFMAs.  Each k step multiplies the A operand by both terms of the weights.
 constexpr int QNS = 3;
 
-// one tile piece over 64-deep stages [s0, s1)
+// one tile piece over 32-deep stages [s0, s1)
 template <int WF, int BM>
 __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int m0, int n0, int s0,
                                         int s1, int slot, bool scale) {
-    constexpr int WM = BM / 2, FM = WM / 32;
-    constexpr int PA = BM / 64;                       // A load instructions per wave and stage
-    constexpr int AST = BM * 8;                       // entries of one A stage
+    constexpr int RG = BM / 32, WM = BM / 2, FM = WM / 32;
+    constexpr int PA = 2 * RG / 8;                    // A load instructions per wave and stage
+    constexpr int AST = RG * 128;                     // entries of one A stage
     constexpr int PWQ = 4;                            // weight loads per thread and stage
-    u32x4_t *As = lds;                                // [QNS][BM][8]
-    u32x4_t *Bs = lds + QNS * AST;                    // [2][4 ks][8][64]
+    u32x4_t *As = lds;                                // [QNS][RG][128]
+    u32x4_t *Bs = lds + QNS * AST;                    // [2][2 (hi, lo)][2 ks][8][64]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -412,15 +415,16 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
     const uint16_t *asrc[PA];
 #pragma unroll
     for (int j = 0; j < PA; j++) {
-        const int row = 8 * (wave + 8 * j) + (lane >> 3);
-        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-        asrc[j] = a.A + (size_t)min(m0 + row, a.M - 1) * a.lda + 8 * chunk;
+        const int h = wave + 8 * j;                   // 1 KB half: group h / 2, rows 16 (h % 2) ..
+        const int g = h >> 1, row = 16 * (h & 1) + (lane >> 2);
+        const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+        asrc[j] = a.A + (size_t)min(m0 + 32 * g + row, a.M - 1) * a.lda + 8 * chunk;
     }
-    auto issue_a = [&](int s, int buf) {
+    auto issue_a = [&](int st, int buf) {
 #pragma unroll
         for (int j = 0; j < PA; j++)
             __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1))) *)(asrc[j] + s * BK),
+                (const void __attribute__((address_space(1))) *)(asrc[j] + st * BKD),
                 (void __attribute__((address_space(3))) *)(As + buf * AST + (wave + 8 * j) * 64), 16, 0, 0);
     };
     const unsigned char *wbase[2];
@@ -435,19 +439,26 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-    const int rl = lane & 31, rsw = (rl >> 1) & 7;
+    const int rl = lane & 31;
+    const int rp0 = dma_pos(rl, lane >> 5), rp1 = dma_pos(rl, 2 + (lane >> 5));
     auto compute = [&](const u32x4_t *Ab, const u32x4_t *Bb) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-            const int c = 2 * ks + (lane >> 5);
-            u32x4_t bf[2];
+        for (int ks = 0; ks < 2; ks++) {
+            const int c = 2 * ks + (lane >> 5), rp = ks ? rp1 : rp0;
+            u32x4_t bh[2], bl[2];
 #pragma unroll
-            for (int j = 0; j < 2; j++) bf[j] = Bb[(ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
+            for (int j = 0; j < 2; j++) {
+                bh[j] = Bb[(ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
+                bl[j] = Bb[1024 + (ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
+            }
 #pragma unroll
             for (int i = 0; i < FM; i++) {
-                const u32x4_t af = Ab[(32 * (wm * FM + i) + rl) * 8 + (c ^ rsw)];
+                const u32x4_t af = Ab[(wm * FM + i) * 128 + rp];
 #pragma unroll
-                for (int j = 0; j < 2; j++) acc[i][j] = mfma32x32x16(af, bf[j], acc[i][j]);
+                for (int j = 0; j < 2; j++) {
+                    acc[i][j] = mfma32x32x16(af, bh[j], acc[i][j]);
+                    acc[i][j] = mfma32x32x16(af, bl[j], acc[i][j]);
+                }
             }
         }
     };
@@ -457,19 +468,19 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
         __builtin_amdgcn_s_waitcnt(0xF70 | (PA + PWQ));
         asm volatile("" ::: "memory");
     };
-    // stage s: A(s) and the decoded W(s) are in LDS once every wave passes the barrier;
-    // rn1 holds the raw weights of stage s + 1 (in flight), rn2 receives stage s + 2.
+    // stage st: A(st) and the decoded W(st) are in LDS once every wave passes the barrier;
+    // rn1 holds the raw weights of stage st + 1 (in flight), rn2 receives stage st + 2.
     // Stages past the end load the last stage again into buffers no stage reads, so the
     // wait counts stay fixed.
-    auto body = [&](int s, WRaw &rn1, WRaw &rn2) {
-        const int i = s - s0;
+    auto body = [&](int st, WRaw &rn1, WRaw &rn2) {
+        const int i = st - s0;
         __builtin_amdgcn_s_waitcnt(0xC07F);           // this wave's LDS stores done
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        const int s2 = min(s + 2, s1 - 1);
+        const int s2 = min(st + 2, s1 - 1);
         issue_a(s2, (i + 2) % QNS);
-        wq_load<WF>(rn2, wbase, tid, s2 * BK);
+        wq_load<WF>(rn2, wbase, tid, s2);
         asm volatile("" ::: "memory");                // (issued before the MFMAs)
         compute(As + (i % QNS) * AST, Bs + (i & 1) * 2048);
         wait_one();
@@ -477,17 +488,17 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
     };
     WRaw ra, rb;
     issue_a(s0, 0);
-    wq_load<WF>(ra, wbase, tid, s0 * BK);
+    wq_load<WF>(ra, wbase, tid, s0);
     issue_a(min(s0 + 1, s1 - 1), 1);
-    wq_load<WF>(rb, wbase, tid, min(s0 + 1, s1 - 1) * BK);
+    wq_load<WF>(rb, wbase, tid, min(s0 + 1, s1 - 1));
     wait_one();
     wq_store<WF>(Bs, ra, wok, tid);
-    int s = s0;
-    for (; s + 1 < s1; s += 2) {
-        body(s, rb, ra);
-        body(s + 1, ra, rb);
+    int st = s0;
+    for (; st + 1 < s1; st += 2) {
+        body(st, rb, ra);
+        body(st + 1, ra, rb);
     }
-    if (s < s1) body(s, rb, ra);
+    if (st < s1) body(st, rb, ra);
     __builtin_amdgcn_s_waitcnt(0xF70);      // no load may land after the piece ends
 
     store_tile<BM, FM>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot, scale);
@@ -500,7 +511,7 @@ __global__ __launch_bounds__(NTH) void k_gemm_big_q(BigGemmArgs a, BigSched sc) 
     Piece pc;
     for (bool first = true; it.next<BM>(a, sc, pc); first = false) {
         if (!first) __syncthreads();                  // the previous piece is done with LDS
-        q_piece<WF, BM>(a, lds, pc.m0, pc.n0, pc.s0, pc.s1, pc.slot, pc.scale);
+        q_piece<WF, BM>(a, lds, pc.m0, pc.n0, 2 * pc.s0, 2 * pc.s1, pc.slot, pc.scale);
         if (pc.last) zero_slots<BM>(a, pc.m0, pc.n0, pc.slot + 1, sc.slots, threadIdx.x);
     }
 }
@@ -508,7 +519,7 @@ __global__ __launch_bounds__(NTH) void k_gemm_big_q(BigGemmArgs a, BigSched sc) 
 }  // namespace
 
 size_t dma_lds_bytes(int BM, int TBN) { return (size_t)DMA_NS * (BM / 32 + TBN / 32) * 2048; }
-size_t q_lds_bytes(int BM) { return ((size_t)QNS * BM * 8 + 2 * 2048) * 16; }
+size_t q_lds_bytes(int BM) { return ((size_t)QNS * BM * 4 + 2 * 2048) * 16; }
 
 namespace {
 

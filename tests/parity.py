@@ -36,6 +36,21 @@ def run_oracle(wl, W, inputs, seqs=None, want_logits=True):
                              want_logits=want_logits)
 
 
+def run_oracle_chunked(wl, W, inputs, chunk=8, say=print):
+    """The oracle over every sequence, `chunk` sequences per call (a progress line per
+    call); the per-sequence outputs concatenated along the batch axis."""
+    parts = []
+    for b0 in range(0, wl.batch, chunk):
+        seqs = list(range(b0, min(wl.batch, b0 + chunk)))
+        say(f"  oracle: sequences {seqs[0]}..{seqs[-1]} of {wl.batch}")
+        parts.append(run_oracle(wl, W, inputs, seqs=seqs))
+    out = {}
+    for k, v in parts[0].items():
+        axis = 1 if k in ("hidden", "new_k", "new_v") else 0
+        out[k] = np.concatenate([p[k] for p in parts], axis=axis)
+    return out
+
+
 def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
