@@ -20,6 +20,9 @@ BLOCK = 8
 W_Q4K, W_BF16, W_Q8_0 = 0, 1, 2
 WEIGHT_FMT = {"q4k": W_Q4K, "bf16": W_BF16, "q8_0": W_Q8_0}
 PROBE_NONE, PROBE_LM_HEAD, PROBE_FFN_GATE_UP = 0, 1, 2
+LAYOUT_ROWMAJOR, LAYOUT_TILED = 0, 0x444C4954
+STATUS = {0: "OK", -1: "EINVAL", -2: "ESHAPE", -3: "EALIGN", -4: "EWORKSPACE", -5: "EHIP",
+          -6: "ELAYOUT"}
 
 c_int, c_float, c_void_p, c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -40,7 +43,8 @@ class Weights(ctypes.Structure):
     _fields_ = [("fc", c_void_p), ("hidden_norm", c_void_p),
                 ("layer", LayerWeights * MAX_LAYERS)] + \
                [(n, c_void_p) for n in ("final_norm", "embed", "lm_head", "mask_emb", "sel_proj",
-                                        "code_a", "code_b")]
+                                        "code_a", "code_b")] + \
+               [("linear_layout", ctypes.c_uint32)]
 
 
 class Probe(ctypes.Structure):
@@ -85,6 +89,11 @@ def lib():
     L.q4k_gemm.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_size_t,
                            c_void_p]
     L.q4k_gemm.restype = c_int
+    L.q4k_gemm_tiled_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    L.q4k_gemm_tiled_workspace_bytes.restype = c_size_t
+    L.q4k_gemm_tiled.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p,
+                                 c_size_t, c_void_p]
+    L.q4k_gemm_tiled.restype = c_int
     L.q4k_dequantize.argtypes = [c_void_p, c_void_p, ctypes.c_longlong, c_void_p]
     L.q4k_dequantize.restype = c_int
     L.q4k_to_tiled.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p]
@@ -94,6 +103,11 @@ def lib():
     L.q8_0_gemm.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p,
                             c_size_t, c_void_p]
     L.q8_0_gemm.restype = c_int
+    L.q8_0_gemm_tiled_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    L.q8_0_gemm_tiled_workspace_bytes.restype = c_size_t
+    L.q8_0_gemm_tiled.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p,
+                                  c_size_t, c_void_p]
+    L.q8_0_gemm_tiled.restype = c_int
     L.q8_0_to_tiled.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p]
     L.q8_0_to_tiled.restype = c_int
     L.q8_0_dequantize.argtypes = [c_void_p, c_void_p, ctypes.c_longlong, c_void_p]
@@ -106,14 +120,17 @@ def lib():
 
 EXPORTS = ["dflash_workspace_bytes", "dflash_draft_step", "dflash_verify_prefix",
            "dflash_verify_sampled_workspace_bytes", "dflash_verify_sampled",
-           "q4k_gemm_workspace_bytes", "q4k_gemm", "q4k_to_tiled", "q4k_dequantize",
-           "q8_0_gemm_workspace_bytes", "q8_0_gemm", "q8_0_to_tiled", "q8_0_dequantize",
+           "q4k_gemm_workspace_bytes", "q4k_gemm", "q4k_gemm_tiled_workspace_bytes",
+           "q4k_gemm_tiled", "q4k_to_tiled", "q4k_dequantize",
+           "q8_0_gemm_workspace_bytes", "q8_0_gemm", "q8_0_gemm_tiled_workspace_bytes",
+           "q8_0_gemm_tiled", "q8_0_to_tiled", "q8_0_dequantize",
            "dflash_status_str"]
 
 
 def check(rc):
     if rc != 0:
-        raise DflashError(f"dflash status {rc}: {lib().dflash_status_str(rc).decode()}")
+        raise DflashError(f"dflash status {rc} ({STATUS.get(rc, '?')}): "
+                          f"{lib().dflash_status_str(rc).decode()}")
 
 
 def make_config(shape):
@@ -185,6 +202,7 @@ class DeviceWeights:
             return t.data_ptr()
 
         s = Weights()
+        s.linear_layout = LAYOUT_TILED          # quantised matrices are regrouped below
         for name, val in W.items():
             arr = val[1] if isinstance(val, tuple) else val
             p = up(name, arr, val[0] if isinstance(val, tuple) else "bf16")
@@ -243,6 +261,17 @@ def q4k_gemm_workspace_bytes(M, N, K):
     return lib().q4k_gemm_workspace_bytes(M, N, K)
 
 
+def q4k_gemm_tiled(w, x, y, workspace):
+    M, K = x.shape
+    N = y.shape[1]
+    check(lib().q4k_gemm_tiled(_ptr(w), _ptr(x), _ptr(y), M, N, K, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream()))
+
+
+def q4k_gemm_tiled_workspace_bytes(M, N, K):
+    return lib().q4k_gemm_tiled_workspace_bytes(M, N, K)
+
+
 def q4k_to_tiled(src, dst, N, K):
     """Regroup a row-major Q4_K matrix [N][K] (device uint8) into the tiled layout."""
     check(lib().q4k_to_tiled(_ptr(src), _ptr(dst), N, K, _stream()))
@@ -257,6 +286,17 @@ def q8_0_gemm(w, x, y, workspace):
 
 def q8_0_gemm_workspace_bytes(M, N, K):
     return lib().q8_0_gemm_workspace_bytes(M, N, K)
+
+
+def q8_0_gemm_tiled(w, x, y, workspace):
+    M, K = x.shape
+    N = y.shape[1]
+    check(lib().q8_0_gemm_tiled(_ptr(w), _ptr(x), _ptr(y), M, N, K, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream()))
+
+
+def q8_0_gemm_tiled_workspace_bytes(M, N, K):
+    return lib().q8_0_gemm_tiled_workspace_bytes(M, N, K)
 
 
 def q8_0_to_tiled(src, dst, N, K):

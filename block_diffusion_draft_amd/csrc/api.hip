@@ -200,24 +200,7 @@ int run_quant(int fmt, const Q4kFusedArgs &a, hipStream_t st, int *pair_left) {
         return run_big(big_fmt(fmt), w, a.seg_end, a.nseg, a.src.A, a.src.lda, a.M, a.N, K,
                        a.part, st);
     }
-    if (q4k) return DFLASH_ESHAPE;     // (every Q4_K shape takes one of the two above)
-    // (Q8_0 shapes the many-row GEMM does not take): the tiled kernel's Q8_0 loader
-    Bf16GemmArgs g = {};
-    for (int i = 0; i < 3; i++) {
-        g.w[i] = reinterpret_cast<const uint16_t *>(a.w[i]);
-        g.seg_end[i] = a.seg_end[i];
-    }
-    g.nseg = a.nseg;
-    g.A = a.src.A;
-    g.lda = a.src.lda;
-    g.M = a.M;
-    g.N = a.N;
-    g.K = K;
-    g.C = a.part;
-    g.ldc = a.N;
-    g.wfmt = 1;
-    HIPCHK(launch_bf16_gemm_tiled(g, st));
-    return 1;
+    return DFLASH_ESHAPE;      // (every valid Q4_K / Q8_0 shape takes one of the two above)
 }
 
 // y = A . W^T over up to 3 weight matrices stacked along N, as fp32 partial sums in
@@ -285,6 +268,7 @@ const char *dflash_status_str(int s) {
         case DFLASH_EALIGN: return "pointer not 16-byte aligned";
         case DFLASH_EWORKSPACE: return "workspace missing or too small";
         case DFLASH_EHIP: return "HIP runtime error";
+        case DFLASH_ELAYOUT: return "quantised weights not declared in the tiled layout";
         default: return "unknown status";
     }
 }
@@ -296,13 +280,16 @@ size_t dflash_workspace_bytes(const dflash_config *cfg, int batch, int t_new) {
     return p.total;
 }
 
-int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int batch,
-                      const uint16_t *taps, int t_new, const int32_t *last_token,
-                      const int32_t *ctx_len, uint16_t *k_cache, uint16_t *v_cache,
-                      int cache_cap, int32_t *draft_tokens, int32_t *cand_ids,
-                      float *cand_logp, float *dbg_hidden, float *dbg_logits,
-                      void *workspace, size_t ws_bytes, const dflash_probe *probe,
-                      void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side validation of a draft step's arguments (everything but the workspace).
+int check_step(const dflash_config *cfg, const dflash_weights *w, int batch, const uint16_t *taps,
+               int t_new, const int32_t *last_token, const int32_t *ctx_len,
+               const uint16_t *k_cache, const uint16_t *v_cache, int cache_cap,
+               const int32_t *draft_tokens, const int32_t *cand_ids, const float *cand_logp,
+               const float *dbg_hidden, const float *dbg_logits) {
     int rc = check_config(cfg);
     if (rc != DFLASH_OK) return rc;
     if (!w || !taps || !last_token || !ctx_len || !k_cache || !v_cache || !draft_tokens ||
@@ -315,7 +302,7 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
         return DFLASH_EINVAL;
     const void *ptrs[] = {w->fc, w->hidden_norm, w->final_norm, w->embed, w->lm_head,
                           w->mask_emb, w->code_a, w->code_b, taps, k_cache, v_cache,
-                          workspace, dbg_hidden, dbg_logits};
+                          dbg_hidden, dbg_logits};
     for (const void *q : ptrs)
         if (q && !aligned16(q)) return DFLASH_EALIGN;
     for (int l = 0; l < cfg->n_layers; l++) {
@@ -327,11 +314,21 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
             if (!aligned16(q)) return DFLASH_EALIGN;
         }
     }
-    Plan p;
-    make_plan(cfg, batch, t_new, p);
-    if (!workspace || ws_bytes < p.total || ((uintptr_t)workspace & 255)) return DFLASH_EWORKSPACE;
+    // quantised matrices are read in the tiled layouts only: the caller must say so
+    if (cfg->weight_fmt != DFLASH_W_BF16 && w->linear_layout != DFLASH_LAYOUT_TILED)
+        return DFLASH_ELAYOUT;
+    return DFLASH_OK;
+}
 
-    Ctx x{cfg, &p, (unsigned char *)workspace, (hipStream_t)stream};
+// The launch sequence of one step on a validated call, workspace of p.total bytes.
+int draft_step_impl(const dflash_config *cfg, const dflash_weights *w, int batch,
+                    const uint16_t *taps, int t_new, const int32_t *last_token,
+                    const int32_t *ctx_len, uint16_t *k_cache, uint16_t *v_cache,
+                    int cache_cap, int32_t *draft_tokens, int32_t *cand_ids,
+                    float *cand_logp, float *dbg_hidden, float *dbg_logits,
+                    unsigned char *workspace, const Plan &p, const dflash_probe *probe,
+                    hipStream_t stream) {
+    Ctx x{cfg, &p, workspace, stream};
     const int H = p.H, L = p.L;
     float *h = x.at<float>(p.o_h);
     uint16_t *xc = x.at<uint16_t>(p.o_xc);
@@ -493,6 +490,28 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
     return DFLASH_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int batch,
+                      const uint16_t *taps, int t_new, const int32_t *last_token,
+                      const int32_t *ctx_len, uint16_t *k_cache, uint16_t *v_cache,
+                      int cache_cap, int32_t *draft_tokens, int32_t *cand_ids,
+                      float *cand_logp, float *dbg_hidden, float *dbg_logits,
+                      void *workspace, size_t ws_bytes, const dflash_probe *probe,
+                      void *stream) {
+    const int rc = check_step(cfg, w, batch, taps, t_new, last_token, ctx_len, k_cache, v_cache,
+                              cache_cap, draft_tokens, cand_ids, cand_logp, dbg_hidden, dbg_logits);
+    if (rc != DFLASH_OK) return rc;
+    Plan p;
+    make_plan(cfg, batch, t_new, p);
+    if (!workspace || ws_bytes < p.total || ((uintptr_t)workspace & 255)) return DFLASH_EWORKSPACE;
+    return draft_step_impl(cfg, w, batch, taps, t_new, last_token, ctx_len, k_cache, v_cache,
+                           cache_cap, draft_tokens, cand_ids, cand_logp, dbg_hidden, dbg_logits,
+                           (unsigned char *)workspace, p, probe, (hipStream_t)stream);
+}
+
 int dflash_verify_prefix(const int32_t *draft, const int32_t *target, int batch, int n,
                          int32_t *accept_len, int32_t *out_tokens, void *stream) {
     if (!draft || !target || !accept_len || !out_tokens) return DFLASH_EINVAL;
@@ -532,64 +551,122 @@ int dflash_verify_sampled(const int32_t *draft, const float *target_logits, cons
     return DFLASH_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+bool qgemm_shape_ok(int M, int N, int K) {
+    return M >= 1 && M <= 4096 && N >= 16 && N % 16 == 0 && K >= 256 && K % 256 == 0;
+}
+
+size_t quant_matrix_bytes(int fmt, int N, int K) {
+    return fmt == DFLASH_W_Q4K ? (size_t)N * (K / 256) * 144 : (size_t)N * (K / 32) * Q8_BLOCK_BYTES;
+}
+
+// y = x . W^T for a tiled Q4_K / Q8_0 matrix: product into partials, split sum to bf16
+int quant_gemm_tiled(int fmt, const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
+                     float *part, hipStream_t st) {
+    Q4kFusedArgs a;
+    a.w[0] = a.w[1] = a.w[2] = (const unsigned char *)w;
+    a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = N;
+    a.nseg = 1;
+    a.M = M; a.N = N; a.KB = K / 256;
+    a.src.A = x;
+    a.src.lda = K;
+    a.part = part;
+    a.pair = 0;
+    int pair_left;
+    const int splits = run_quant(fmt, a, st, &pair_left);
+    if (splits < 0) return splits;
+    HIPCHK(launch_reduce_epilogue(a.part, splits, M, N, 0, EPI_STORE_BF16, nullptr, y, nullptr, N,
+                                  RowScale{}, st));
+    return DFLASH_OK;
+}
+
+// argument checks shared by the four GEMM entry points
+int quant_gemm_check(const void *w, const uint16_t *x, const uint16_t *y, int M, int N, int K,
+                     const void *workspace, size_t ws_bytes, size_t need) {
+    if (!w || !x || !y) return DFLASH_EINVAL;
+    if (!qgemm_shape_ok(M, N, K)) return DFLASH_ESHAPE;
+    if (!aligned16(w) || !aligned16(x) || !aligned16(y)) return DFLASH_EALIGN;
+    if (!workspace || ws_bytes < need || !aligned16(workspace)) return DFLASH_EWORKSPACE;
+    return DFLASH_OK;
+}
+
+size_t quant_gemm_tiled_ws(int fmt, int M, int N, int K) {
+    if (!qgemm_shape_ok(M, N, K)) return 0;
+    return gemm_part_bytes(fmt, M, N, K);
+}
+
+// row-major W: the tiled copy first in the workspace, then the partials
+size_t quant_gemm_rowmajor_ws(int fmt, int M, int N, int K) {
+    if (!qgemm_shape_ok(M, N, K)) return 0;
+    return align256(quant_matrix_bytes(fmt, N, K)) + gemm_part_bytes(fmt, M, N, K);
+}
+
+int quant_gemm_rowmajor(int fmt, const void *w, const uint16_t *x, uint16_t *y, int M, int N,
+                        int K, void *workspace, size_t ws_bytes, hipStream_t st) {
+    const int rc = quant_gemm_check(w, x, y, M, N, K, workspace, ws_bytes,
+                                    quant_gemm_rowmajor_ws(fmt, M, N, K));
+    if (rc != DFLASH_OK) return rc;
+    if ((uintptr_t)workspace & 255) return DFLASH_EWORKSPACE;
+    unsigned char *tiled = (unsigned char *)workspace;
+    const size_t wb = quant_matrix_bytes(fmt, N, K);
+    const uintptr_t s0 = (uintptr_t)w, d0 = (uintptr_t)tiled;
+    if (s0 < d0 + ws_bytes && d0 < s0 + wb) return DFLASH_EINVAL;      // W inside the workspace
+    if (fmt == DFLASH_W_Q4K)
+        HIPCHK(launch_q4k_to_tiled((const unsigned char *)w, tiled, N, K / 256, st));
+    else
+        HIPCHK(launch_q8_0_to_tiled((const unsigned char *)w, tiled, N, K / 256, st));
+    return quant_gemm_tiled(fmt, tiled, x, y, M, N, K, (float *)(tiled + align256(wb)), st);
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t q4k_gemm_workspace_bytes(int M, int N, int K) {
-    if (M < 1 || M > 4096 || N < 16 || N % 16 || K < 256 || K % 256) return 0;
-    return gemm_part_bytes(DFLASH_W_Q4K, M, N, K);
+    return quant_gemm_rowmajor_ws(DFLASH_W_Q4K, M, N, K);
 }
 
 int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
              void *workspace, size_t ws_bytes, void *stream) {
-    if (!w || !x || !y) return DFLASH_EINVAL;
-    if (M < 1 || M > 4096 || N < 16 || N % 16 || K < 256 || K % 256) return DFLASH_ESHAPE;
-    if (!aligned16(w) || !aligned16(x) || !aligned16(y)) return DFLASH_EALIGN;
-    const size_t need = q4k_gemm_workspace_bytes(M, N, K);
-    if (!workspace || ws_bytes < need || !aligned16(workspace)) return DFLASH_EWORKSPACE;
-    const hipStream_t st = (hipStream_t)stream;
-    Q4kFusedArgs a;
-    a.w[0] = a.w[1] = a.w[2] = (const unsigned char *)w;
-    a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = N;
-    a.nseg = 1;
-    a.M = M; a.N = N; a.KB = K / 256;
-    a.src.A = x;
-    a.src.lda = K;
-    a.part = (float *)workspace;
-    a.pair = 0;
-    int pair_left;
-    const int splits = run_quant(DFLASH_W_Q4K, a, st, &pair_left);
-    if (splits < 0) return splits;
-    HIPCHK(launch_reduce_epilogue(a.part, splits, M, N, 0, EPI_STORE_BF16, nullptr, y, nullptr, N,
-                                  RowScale{}, st));
-    return DFLASH_OK;
+    return quant_gemm_rowmajor(DFLASH_W_Q4K, w, x, y, M, N, K, workspace, ws_bytes,
+                               (hipStream_t)stream);
+}
+
+size_t q4k_gemm_tiled_workspace_bytes(int M, int N, int K) {
+    return quant_gemm_tiled_ws(DFLASH_W_Q4K, M, N, K);
+}
+
+int q4k_gemm_tiled(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
+                   void *workspace, size_t ws_bytes, void *stream) {
+    const int rc = quant_gemm_check(w, x, y, M, N, K, workspace, ws_bytes,
+                                    quant_gemm_tiled_ws(DFLASH_W_Q4K, M, N, K));
+    if (rc != DFLASH_OK) return rc;
+    return quant_gemm_tiled(DFLASH_W_Q4K, w, x, y, M, N, K, (float *)workspace, (hipStream_t)stream);
 }
 
 size_t q8_0_gemm_workspace_bytes(int M, int N, int K) {
-    if (M < 1 || M > 4096 || N < 16 || N % 16 || K < 256 || K % 256) return 0;
-    return gemm_part_bytes(DFLASH_W_Q8_0, M, N, K);
+    return quant_gemm_rowmajor_ws(DFLASH_W_Q8_0, M, N, K);
 }
 
 int q8_0_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
               void *workspace, size_t ws_bytes, void *stream) {
-    if (!w || !x || !y) return DFLASH_EINVAL;
-    if (M < 1 || M > 4096 || N < 16 || N % 16 || K < 256 || K % 256) return DFLASH_ESHAPE;
-    if (!aligned16(w) || !aligned16(x) || !aligned16(y)) return DFLASH_EALIGN;
-    const size_t need = q8_0_gemm_workspace_bytes(M, N, K);
-    if (!workspace || ws_bytes < need || !aligned16(workspace)) return DFLASH_EWORKSPACE;
-    const hipStream_t st = (hipStream_t)stream;
-    Q4kFusedArgs a;
-    a.w[0] = a.w[1] = a.w[2] = (const unsigned char *)w;
-    a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = N;
-    a.nseg = 1;
-    a.M = M; a.N = N; a.KB = K / 256;
-    a.src.A = x;
-    a.src.lda = K;
-    a.part = (float *)workspace;
-    a.pair = 0;
-    int pair_left;
-    const int splits = run_quant(DFLASH_W_Q8_0, a, st, &pair_left);
-    if (splits < 0) return splits;
-    HIPCHK(launch_reduce_epilogue(a.part, splits, M, N, 0, EPI_STORE_BF16, nullptr, y, nullptr, N,
-                                  RowScale{}, st));
-    return DFLASH_OK;
+    return quant_gemm_rowmajor(DFLASH_W_Q8_0, w, x, y, M, N, K, workspace, ws_bytes,
+                               (hipStream_t)stream);
+}
+
+size_t q8_0_gemm_tiled_workspace_bytes(int M, int N, int K) {
+    return quant_gemm_tiled_ws(DFLASH_W_Q8_0, M, N, K);
+}
+
+int q8_0_gemm_tiled(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
+                    void *workspace, size_t ws_bytes, void *stream) {
+    const int rc = quant_gemm_check(w, x, y, M, N, K, workspace, ws_bytes,
+                                    quant_gemm_tiled_ws(DFLASH_W_Q8_0, M, N, K));
+    if (rc != DFLASH_OK) return rc;
+    return quant_gemm_tiled(DFLASH_W_Q8_0, w, x, y, M, N, K, (float *)workspace, (hipStream_t)stream);
 }
 
 int q8_0_to_tiled(const void *src, void *dst, int N, int K, void *stream) {

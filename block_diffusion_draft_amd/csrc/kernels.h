@@ -19,7 +19,7 @@ hipError_t launch_q4k_to_tiled(const unsigned char *src, unsigned char *dst, int
 
 // ---------------------------------------------------------------- bf16 GEMMs
 struct Bf16GemmArgs {
-    const uint16_t *w[3];        // bf16 weights [N_seg][K] (wfmt 1: Q8_0 tiled bytes), stacked along N
+    const uint16_t *w[3];        // bf16 weights [N_seg][K], stacked along N
     int seg_end[3];
     int nseg;
     const uint16_t *A;           // bf16 [M][lda]
@@ -28,7 +28,6 @@ struct Bf16GemmArgs {
     float *C;                    // fp32 [M][ldc]
     int ldc;
     RowScale rs;                 // output row r multiplied by row_inv(rs, r) (ssq null: none)
-    int wfmt;                    // 0: bf16 weights; 1: Q8_0 in the tiled layout (tiled GEMM only)
 };
 // tiled 128x128 MFMA GEMM, any M
 hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st);
@@ -201,7 +200,8 @@ hipError_t launch_q8_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipSt
 // ---------------------------------------------------------------- many-row GEMM
 // C[split][M][N] fp32 = A[M][K] bf16 . W^T over the split's share of K; W stacked along
 // N from up to 3 matrices in bf16 ([N][K]), Q8_0 or Q4_K (tiled layouts), decoded to
-// bf16 MFMA operands per 256 x 256 tile.  One split: rows scaled by row_inv(rs, r).
+// bf16 (hi, lo) MFMA operand pairs per 256 x 256 tile.  One split: rows scaled by
+// row_inv(rs, r).
 struct BigGemmArgs {
     const void *w[3];
     int seg_end[3];

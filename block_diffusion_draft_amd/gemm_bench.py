@@ -4,12 +4,12 @@
 
 Each shape (fc 25600->5120; q 5120->4096; k, v 5120->1024; o 4096->5120; gate, up
 5120->17408; down 17408->5120; FastFlowLM card "Qwen3.8-27B-DFlash2-NPU2", spec table
-"Draft" row) runs through the library's q4k_gemm entry point (product + split-K
+"Draft" row) runs through the library's q4k_gemm_tiled entry point (product + split-K
 reduction to bf16) on bf16 N(0,1) activations and N(0, 0.02) weights packed to Q4_K
 (seed 1), regrouped on the device into the tiled layout.  Calls rotate over enough
 copies of the weight matrix to span at least --min-bytes, so no call is served from
 the last-level cache.  Prints one JSON line per shape: microseconds per call and the
-Q4_K weight bytes per second.  --fmt q8_0 runs the same shapes through q8_0_gemm with
+Q4_K weight bytes per second.  --fmt q8_0 runs the same shapes through q8_0_gemm_tiled with
 the weights packed to Q8_0 (Mindket kit page "Qwen3.8-27B-DFlash2-GGUF by z-lab",
 draft-file table).
 """
@@ -35,8 +35,9 @@ def main():
     q8 = args.fmt == "q8_0"
     pack = synth.q8_0_normal if q8 else synth.q4k_normal
     to_tiled = binding.q8_0_to_tiled if q8 else binding.q4k_to_tiled
-    gemm = binding.q8_0_gemm if q8 else binding.q4k_gemm
-    ws_bytes = binding.q8_0_gemm_workspace_bytes if q8 else binding.q4k_gemm_workspace_bytes
+    gemm = binding.q8_0_gemm_tiled if q8 else binding.q4k_gemm_tiled
+    ws_bytes = (binding.q8_0_gemm_tiled_workspace_bytes if q8
+                else binding.q4k_gemm_tiled_workspace_bytes)
     for name, N, K in synth.GEMM_SHAPES:
         w_host = pack(synth.GEMM_SEED, f"gemm.{name}", N, K, 0.02)
         wbytes = w_host.size

@@ -21,7 +21,8 @@
  *                        know".
  *   q4k_gemm             y = x . W^T with W in Q4_K super-blocks (the format of
  *                        the draft's fc, q/k/v/o and MLP matrices: same card,
- *                        "Weights" row), fp32 accumulation, bf16 output.
+ *                        "Weights" row), fp32 accumulation, bf16 output; W row-major
+ *                        as in a GGUF file (q4k_gemm_tiled: W in the tiled layout).
  *   q8_0_gemm            the same product with W in Q8_0 blocks (the pages' second
  *                        quantised draft file: Mindket kit page "Qwen3.8-27B-DFlash2-
  *                        GGUF by z-lab", draft-file table); q8_0_to_tiled and
@@ -71,8 +72,18 @@ typedef enum {
     DFLASH_ESHAPE = -2,       /* shape not supported by the kernels */
     DFLASH_EALIGN = -3,       /* pointer misaligned (16-byte alignment required) */
     DFLASH_EWORKSPACE = -4,   /* workspace missing or too small */
-    DFLASH_EHIP = -5          /* a HIP call failed */
+    DFLASH_EHIP = -5,         /* a HIP call failed */
+    DFLASH_ELAYOUT = -6       /* quantised weights not declared in the tiled layout */
 } dflash_status;
+
+/* Layout tag of the quantised linear weights in dflash_weights.linear_layout.  The
+ * draft step reads Q4_K and Q8_0 matrices only in the tiled layouts written by
+ * q4k_to_tiled / q8_0_to_tiled; the caller states that it converted them by setting
+ * the tag to DFLASH_LAYOUT_TILED (a zero-initialised struct says row-major, and a
+ * step with quantised weights then returns DFLASH_ELAYOUT instead of reading
+ * row-major bytes as tiled ones).  bf16 weights are row-major and ignore the tag. */
+#define DFLASH_LAYOUT_ROWMAJOR 0u
+#define DFLASH_LAYOUT_TILED 0x444C4954u     /* "TILD" */
 
 typedef enum { DFLASH_W_Q4K = 0, DFLASH_W_BF16 = 1, DFLASH_W_Q8_0 = 2 } dflash_weight_fmt;
 
@@ -94,8 +105,8 @@ typedef struct {
 } dflash_config;
 
 /* Linear weights are [out][in] (y = x . W^T).  bf16: row-major, `in` values per
- * row.  Q4_K: the tiled layout written by q4k_to_tiled (the row-major Q4_K matrix,
- * each row in/256 consecutive 144-byte super-blocks, regrouped; same size). */
+ * row.  Q4_K / Q8_0: the tiled layouts written by q4k_to_tiled / q8_0_to_tiled (the
+ * row-major matrix regrouped; same size), declared by linear_layout. */
 typedef struct {
     const void *wq, *wk, *wv, *wo, *wg, *wu, *wd;
     const uint16_t *in_norm, *post_norm;   /* [hidden] */
@@ -113,6 +124,7 @@ typedef struct {
     const uint16_t *mask_emb;              /* [hidden] embedding of the mask positions */
     const uint16_t *sel_proj;              /* [sel_rank][hidden] selector projection (not read) */
     const uint16_t *code_a, *code_b;       /* [vocab][sel_rank] selector codebooks */
+    uint32_t linear_layout;                /* DFLASH_LAYOUT_TILED (required for Q4_K / Q8_0) */
 } dflash_weights;
 
 /* Optional live timing of one kernel inside dflash_draft_step: HIP events
@@ -217,16 +229,35 @@ int dflash_verify_sampled(const int32_t *draft, const float *target_logits,
                           size_t workspace_bytes, int32_t *accept_len, int32_t *out_tokens,
                           void *stream);
 
-/* Workspace bytes q4k_gemm needs for an M x N x K product. */
+/* Workspace bytes q4k_gemm needs for an M x N x K product (the tiled copy of W plus
+ * the split-K partial sums); 0 if the shape is not supported. */
 size_t q4k_gemm_workspace_bytes(int M, int N, int K);
 
 /*
- * y[M][N] (bf16) = x[M][K] (bf16) . W^T, W [N][K] in Q4_K (tiled layout, see
- * q4k_to_tiled), fp32 accumulation.
+ * y[M][N] (bf16) = x[M][K] (bf16) . W^T, W [N][K] in Q4_K as stored in a GGUF file:
+ * row-major, each row K/256 consecutive 144-byte super-blocks (fp16 d, fp16 dmin, 12
+ * bytes of 6-bit scales and mins, 128 quant bytes; w = d sc_j q - dmin m_j for
+ * sub-block j), fp32 accumulation.  FastFlowLM card "Qwen3.8-27B-DFlash2-NPU2",
+ * "Weights" row.  The call regroups W into the tiled layout inside its workspace
+ * (q4k_to_tiled) and runs q4k_gemm_tiled; a caller that multiplies by one matrix
+ * many times converts it once and calls q4k_gemm_tiled.
  * K % 256 == 0, N % 16 == 0, 1 <= M <= 4096.  w, x, y and workspace 16-byte aligned.
  */
 int q4k_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
              void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes q4k_gemm_tiled needs for an M x N x K product; 0 if unsupported. */
+size_t q4k_gemm_tiled_workspace_bytes(int M, int N, int K);
+
+/*
+ * The product of q4k_gemm with W already in the tiled layout of q4k_to_tiled (the
+ * layout the draft step reads).  Up to 16 rows with K % 1024 == 0 every product
+ * d sc_j q and dmin m_j enters the sum exactly; otherwise each decoded weight enters
+ * as two bf16 terms whose sum is within 2^-18 of it (below fp32 accumulation error).
+ * Same shape and alignment rules as q4k_gemm.
+ */
+int q4k_gemm_tiled(const void *w_tiled, const uint16_t *x, uint16_t *y, int M, int N, int K,
+                   void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Tiled Q4_K layout (FastFlowLM card "Qwen3.8-27B-DFlash2-NPU2", "Weights" row, for
@@ -259,17 +290,29 @@ int q4k_to_tiled(const void *src, void *dst, int N, int K, void *stream);
  */
 int q8_0_to_tiled(const void *src, void *dst, int N, int K, void *stream);
 
-/* Workspace bytes q8_0_gemm needs for an M x N x K product. */
+/* Workspace bytes q8_0_gemm needs for an M x N x K product (the tiled copy of W
+ * plus the split-K partial sums); 0 if the shape is not supported. */
 size_t q8_0_gemm_workspace_bytes(int M, int N, int K);
 
 /*
- * y[M][N] (bf16) = x[M][K] (bf16) . W^T, W [N][K] in Q8_0 (tiled layout), fp32
- * accumulation.  Up to 16 rows with K % 1024 == 0 the products d q are exact; otherwise
- * each decoded weight is rounded to bf16 before the MFMA (relative error <= 2^-9).
+ * y[M][N] (bf16) = x[M][K] (bf16) . W^T, W [N][K] in row-major Q8_0 (GGUF blocks, see
+ * above), fp32 accumulation.  The call regroups W into the tiled layout inside its
+ * workspace and runs q8_0_gemm_tiled.
  * K % 256 == 0, N % 16 == 0, 1 <= M <= 4096.  w, x, y and workspace 16-byte aligned.
  */
 int q8_0_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
               void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes q8_0_gemm_tiled needs for an M x N x K product; 0 if unsupported. */
+size_t q8_0_gemm_tiled_workspace_bytes(int M, int N, int K);
+
+/*
+ * The product of q8_0_gemm with W in the tiled layout of q8_0_to_tiled.  Up to 16 rows
+ * with K % 1024 == 0 the products d q enter the sum exactly; otherwise each decoded
+ * weight d q enters as two bf16 terms whose sum is within 2^-18 of it.
+ */
+int q8_0_gemm_tiled(const void *w_tiled, const uint16_t *x, uint16_t *y, int M, int N, int K,
+                    void *workspace, size_t ws_bytes, void *stream);
 
 /* Decode n_blocks consecutive row-major Q8_0 blocks to fp32 (32 values each, exact). */
 int q8_0_dequantize(const void *w, float *out, long long n_blocks, void *stream);

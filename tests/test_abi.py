@@ -24,7 +24,9 @@ def test_header_declares_the_boundary():
     for n in ("dflash_draft_step", "dflash_verify_prefix", "dflash_verify_sampled",
               "dflash_verify_sampled_workspace_bytes", "q4k_gemm", "q4k_to_tiled",
               "q4k_dequantize", "dflash_workspace_bytes", "q4k_gemm_workspace_bytes",
-              "q8_0_gemm", "q8_0_gemm_workspace_bytes", "q8_0_to_tiled", "q8_0_dequantize",
+              "q4k_gemm_tiled", "q4k_gemm_tiled_workspace_bytes",
+              "q8_0_gemm", "q8_0_gemm_workspace_bytes", "q8_0_gemm_tiled",
+              "q8_0_gemm_tiled_workspace_bytes", "q8_0_to_tiled", "q8_0_dequantize",
               "dflash_status_str"):
         assert n in names
     assert sorted(binding.EXPORTS) == names
@@ -38,8 +40,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = binding.lib()
-    for rc in (0, -1, -2, -3, -4, -5):
+    for rc in (0, -1, -2, -3, -4, -5, -6):
         assert L.dflash_status_str(rc)
+        assert b"unknown" not in L.dflash_status_str(rc)
     assert b"unknown" in L.dflash_status_str(42)
 
 
@@ -71,6 +74,7 @@ def fake_weights(cfg):
     for l in range(cfg.n_layers):
         for f, _ in binding.LayerWeights._fields_:
             setattr(w.layer[l], f, FAKE)
+    w.linear_layout = binding.LAYOUT_TILED
     return w
 
 
@@ -112,6 +116,22 @@ def test_draft_step_rejects_bad_arguments_before_launch():
     assert call_step(cfg, w) == -1
 
 
+def test_draft_step_requires_the_tiled_layout_tag():
+    """Quantised matrices are read in the tiled layout only; a weights struct that does
+    not declare it (a zero-initialised tag says row-major) is refused before launch."""
+    for fmt in (binding.W_Q4K, binding.W_Q8_0):
+        cfg = tiny_cfg(weight_fmt=fmt)
+        w = fake_weights(cfg)
+        w.linear_layout = binding.LAYOUT_ROWMAJOR
+        assert call_step(cfg, w) == -6                      # ELAYOUT
+        w.linear_layout = 0x12345678
+        assert call_step(cfg, w) == -6
+    cfg = tiny_cfg(weight_fmt=binding.W_BF16)                # bf16: row-major, tag ignored
+    w = fake_weights(cfg)
+    w.linear_layout = binding.LAYOUT_ROWMAJOR
+    assert call_step(cfg, w, ws=None) == -4                  # passes the tag, stops at EWORKSPACE
+
+
 def test_q4k_gemm_and_verify_reject_bad_arguments():
     L = binding.lib()
     assert L.q4k_gemm(FAKE, FAKE, FAKE, 8, 5120, 5000, FAKE, 1 << 40, None) == -2
@@ -122,6 +142,15 @@ def test_q4k_gemm_and_verify_reject_bad_arguments():
     assert L.q4k_gemm(None, FAKE, FAKE, 8, 5120, 5120, FAKE, 1 << 40, None) == -1
     assert L.q4k_gemm_workspace_bytes(8, 5120, 25600) > 0
     assert L.q4k_gemm_workspace_bytes(8, 5120, 100) == 0
+    # row-major W: the workspace also holds the tiled copy of W
+    assert L.q4k_gemm_workspace_bytes(8, 5120, 25600) >= \
+        L.q4k_gemm_tiled_workspace_bytes(8, 5120, 25600) + 5120 * 100 * 144
+    assert L.q4k_gemm_tiled(FAKE, FAKE, FAKE, 8, 5120, 5000, FAKE, 1 << 40, None) == -2
+    assert L.q4k_gemm_tiled(FAKE + 4, FAKE, FAKE, 8, 5120, 5120, FAKE, 1 << 40, None) == -3
+    assert L.q4k_gemm_tiled(FAKE, FAKE, FAKE, 8, 5120, 5120, FAKE, 16, None) == -4
+    assert L.q4k_gemm_tiled(None, FAKE, FAKE, 8, 5120, 5120, FAKE, 1 << 40, None) == -1
+    assert L.q4k_gemm(FAKE, FAKE, FAKE, 8, 5120, 5120, FAKE + 16, 1 << 40, None) == -4  # 256-aligned
+    assert L.q4k_gemm(FAKE, FAKE, FAKE, 8, 5120, 5120, FAKE, 1 << 40, None) == -1  # W in workspace
     assert L.dflash_verify_prefix(FAKE, FAKE, 1, 0, FAKE, FAKE, None) == -1
     assert L.dflash_verify_prefix(None, FAKE, 1, 7, FAKE, FAKE, None) == -1
     assert L.q4k_dequantize(FAKE, FAKE, 0, None) == -1
@@ -144,6 +173,11 @@ def test_q8_0_entries_reject_bad_arguments():
     assert L.q8_0_gemm_workspace_bytes(8, 5120, 25600) > 0
     assert L.q8_0_gemm_workspace_bytes(300, 5120, 1280) >= 300 * 5120 * 4   # many-row GEMM
     assert L.q8_0_gemm_workspace_bytes(8, 5120, 100) == 0
+    assert L.q8_0_gemm_tiled_workspace_bytes(300, 5120, 1280) >= 300 * 5120 * 4
+    assert L.q8_0_gemm_workspace_bytes(8, 5120, 25600) >= \
+        L.q8_0_gemm_tiled_workspace_bytes(8, 5120, 25600) + 5120 * 800 * 34
+    assert L.q8_0_gemm_tiled(FAKE, FAKE, FAKE, 8, 5121, 5120, FAKE, 1 << 40, None) == -2
+    assert L.q8_0_gemm_tiled(FAKE, FAKE, FAKE, 8, 5120, 5120, FAKE, 16, None) == -4
     assert L.q8_0_dequantize(FAKE, FAKE, 0, None) == -1
     assert L.q8_0_dequantize(FAKE + 2, FAKE, 1, None) == -3
     assert L.q8_0_to_tiled(None, FAKE, 16, 256, None) == -1
@@ -191,3 +225,23 @@ def test_verify_sampled_rejects_bad_arguments_before_launch():
     assert call_sampled(ws=None) == -4                      # EWORKSPACE
     assert call_sampled(ws_bytes=16) == -4
     assert call_sampled(ws=FAKE + 4) == -4
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="a GPU is visible: valid fake pointers would be used")
+def test_valid_calls_without_a_gpu_return_ehip():
+    """On a host without a GPU a call that passes every host check reaches its first
+    HIP call, which fails: the status is DFLASH_EHIP, nothing crashes."""
+    L = binding.lib()
+    cfg = tiny_cfg()
+    assert call_step(cfg, fake_weights(cfg), ws=FAKE * 256) == -5
+    assert L.dflash_verify_prefix(FAKE, FAKE, 1, 7, FAKE, FAKE, None) == -5
+    assert L.q4k_gemm_tiled(FAKE, FAKE, FAKE, 8, 5120, 5120, FAKE, 1 << 40, None) == -5
+    assert L.q4k_dequantize(FAKE, FAKE, 1, None) == -5
