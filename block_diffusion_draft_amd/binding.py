@@ -21,8 +21,9 @@ W_Q4K, W_BF16, W_Q8_0 = 0, 1, 2
 WEIGHT_FMT = {"q4k": W_Q4K, "bf16": W_BF16, "q8_0": W_Q8_0}
 PROBE_NONE, PROBE_LM_HEAD, PROBE_FFN_GATE_UP = 0, 1, 2
 LAYOUT_ROWMAJOR, LAYOUT_TILED = 0, 0x444C4954
+NOALLOC_SCRATCH_BYTES = 32 << 20        # DFLASH_NOALLOC_SCRATCH_BYTES
 STATUS = {0: "OK", -1: "EINVAL", -2: "ESHAPE", -3: "EALIGN", -4: "EWORKSPACE", -5: "EHIP",
-          -6: "ELAYOUT"}
+          -6: "ELAYOUT", -7: "ESCRATCH"}
 
 c_int, c_float, c_void_p, c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -75,6 +76,11 @@ def lib():
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, P(Probe),
                                     c_void_p]
     L.dflash_draft_step.restype = c_int
+    L.dflash_draft_step_noalloc.argtypes = [P(Config), P(Weights), c_int, c_void_p, c_int,
+                                            c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_void_p]
+    L.dflash_draft_step_noalloc.restype = c_int
     L.dflash_verify_prefix.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p,
                                        c_void_p]
     L.dflash_verify_prefix.restype = c_int
@@ -119,6 +125,7 @@ def lib():
 
 
 EXPORTS = ["dflash_workspace_bytes", "dflash_draft_step", "dflash_verify_prefix",
+           "dflash_draft_step_noalloc",
            "dflash_verify_sampled_workspace_bytes", "dflash_verify_sampled",
            "q4k_gemm_workspace_bytes", "q4k_gemm", "q4k_gemm_tiled_workspace_bytes",
            "q4k_gemm_tiled", "q4k_to_tiled", "q4k_dequantize",
@@ -226,6 +233,18 @@ def draft_step(cfg, dw, taps, last_token, ctx_len, k_cache, v_cache, draft_token
                                  workspace.numel() * workspace.element_size(),
                                  None if probe is None else ctypes.byref(probe), _stream())
     check(rc)
+
+
+def draft_step_noalloc(cfg, dw, taps, last_token, ctx_len, k_cache, v_cache, draft_tokens,
+                       cand_ids, cand_logp, dbg_hidden=None, dbg_logits=None):
+    """Enqueue one draft step on the library's static device scratch (no workspace)."""
+    B, t_new = taps.shape[0], taps.shape[1]
+    cap = k_cache.shape[3]
+    check(lib().dflash_draft_step_noalloc(ctypes.byref(cfg), ctypes.byref(dw.struct), B,
+                                          _ptr(taps), t_new, _ptr(last_token), _ptr(ctx_len),
+                                          _ptr(k_cache), _ptr(v_cache), cap, _ptr(draft_tokens),
+                                          _ptr(cand_ids), _ptr(cand_logp), _ptr(dbg_hidden),
+                                          _ptr(dbg_logits), _stream()))
 
 
 def verify_prefix(draft, target, accept_len, out_tokens):

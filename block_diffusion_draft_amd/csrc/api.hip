@@ -4,6 +4,7 @@
 #include "kernels.h"
 #include <cmath>
 
+#include <mutex>
 #include <string.h>
 
 int topk_chunk_size();
@@ -269,6 +270,7 @@ const char *dflash_status_str(int s) {
         case DFLASH_EWORKSPACE: return "workspace missing or too small";
         case DFLASH_EHIP: return "HIP runtime error";
         case DFLASH_ELAYOUT: return "quantised weights not declared in the tiled layout";
+        case DFLASH_ESCRATCH: return "request exceeds the static scratch of the no-allocation entry point";
         default: return "unknown status";
     }
 }
@@ -490,9 +492,66 @@ int draft_step_impl(const dflash_config *cfg, const dflash_weights *w, int batch
     return DFLASH_OK;
 }
 
+// ---- the no-allocation step: its workspace is a file-scope device array.  Each GPU
+// the library runs on holds its own copy (allocated when the code object is loaded on
+// that device, kept until the process ends); host code reaches it only through the
+// address hipGetSymbolAddress returns for that device (the array's name on the host is
+// a stand-in, not a device address).
+__device__ __align__(256) unsigned char scratch[DFLASH_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[MAX_DEVICES];
+
+// device address of `scratch` on the device of `stream`, looked up once per device with
+// that device current; null (and *rc set) on failure
+void *scratch_of(hipStream_t stream, int *rc) {
+    int dev = -1;
+    if (stream) {
+        hipDevice_t d;
+        if (hipStreamGetDevice(stream, &d) != hipSuccess) { *rc = DFLASH_EHIP; return nullptr; }
+        dev = (int)d;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        *rc = DFLASH_EHIP;
+        return nullptr;
+    }
+    if (dev < 0 || dev >= MAX_DEVICES) { *rc = DFLASH_EHIP; return nullptr; }
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) { *rc = DFLASH_EHIP; return nullptr; }
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) { *rc = DFLASH_EHIP; return nullptr; }
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !ptr) { *rc = DFLASH_EHIP; return nullptr; }
+        scratch_ptr[dev] = ptr;
+    }
+    return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+int dflash_draft_step_noalloc(const dflash_config *cfg, const dflash_weights *w, int batch,
+                              const uint16_t *taps, int t_new, const int32_t *last_token,
+                              const int32_t *ctx_len, uint16_t *k_cache, uint16_t *v_cache,
+                              int cache_cap, int32_t *draft_tokens, int32_t *cand_ids,
+                              float *cand_logp, float *dbg_hidden, float *dbg_logits,
+                              void *stream) {
+    int rc = check_step(cfg, w, batch, taps, t_new, last_token, ctx_len, k_cache, v_cache,
+                        cache_cap, draft_tokens, cand_ids, cand_logp, dbg_hidden, dbg_logits);
+    if (rc != DFLASH_OK) return rc;
+    Plan p;
+    make_plan(cfg, batch, t_new, p);
+    if (p.total > DFLASH_NOALLOC_SCRATCH_BYTES) return DFLASH_ESCRATCH;
+    void *ws = scratch_of((hipStream_t)stream, &rc);
+    if (!ws) return rc;
+    return draft_step_impl(cfg, w, batch, taps, t_new, last_token, ctx_len, k_cache, v_cache,
+                           cache_cap, draft_tokens, cand_ids, cand_logp, dbg_hidden, dbg_logits,
+                           (unsigned char *)ws, p, nullptr, (hipStream_t)stream);
+}
 
 int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int batch,
                       const uint16_t *taps, int t_new, const int32_t *last_token,

@@ -73,7 +73,8 @@ typedef enum {
     DFLASH_EALIGN = -3,       /* pointer misaligned (16-byte alignment required) */
     DFLASH_EWORKSPACE = -4,   /* workspace missing or too small */
     DFLASH_EHIP = -5,         /* a HIP call failed */
-    DFLASH_ELAYOUT = -6       /* quantised weights not declared in the tiled layout */
+    DFLASH_ELAYOUT = -6,      /* quantised weights not declared in the tiled layout */
+    DFLASH_ESCRATCH = -7      /* the request needs more than the static scratch holds */
 } dflash_status;
 
 /* Layout tag of the quantised linear weights in dflash_weights.linear_layout.  The
@@ -174,6 +175,28 @@ int dflash_draft_step(const dflash_config *cfg, const dflash_weights *w, int bat
                       float *cand_logp, float *dbg_hidden, float *dbg_logits,
                       void *workspace, size_t ws_bytes, const dflash_probe *probe,
                       void *stream);
+
+/*
+ * dflash_draft_step without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The step's workspace is a static device array of
+ * DFLASH_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until
+ * the process ends (the GPU is the device of `stream`, or the current device for the
+ * NULL stream).  The call itself allocates nothing.  Arguments and results are those
+ * of dflash_draft_step (no probe).  A configuration whose workspace
+ * (dflash_workspace_bytes) exceeds the array returns DFLASH_ESCRATCH before anything
+ * is launched; the 27B-draft shape at batch 1 fits (23.3 MiB).  Every call on one GPU
+ * uses the same array, which keeps the last call's contents (nothing in it needs to
+ * start at zero): calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller.
+ */
+#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int dflash_draft_step_noalloc(const dflash_config *cfg, const dflash_weights *w, int batch,
+                              const uint16_t *taps, int t_new, const int32_t *last_token,
+                              const int32_t *ctx_len, uint16_t *k_cache, uint16_t *v_cache,
+                              int cache_cap, int32_t *draft_tokens, int32_t *cand_ids,
+                              float *cand_logp, float *dbg_hidden, float *dbg_logits,
+                              void *stream);
 
 /*
  * Greedy prefix acceptance for `batch` rows.

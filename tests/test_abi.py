@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = binding.lib()
-    for rc in (0, -1, -2, -3, -4, -5, -6):
+    for rc in (0, -1, -2, -3, -4, -5, -6, -7):
         assert L.dflash_status_str(rc)
         assert b"unknown" not in L.dflash_status_str(rc)
     assert b"unknown" in L.dflash_status_str(42)
@@ -114,6 +114,23 @@ def test_draft_step_rejects_bad_arguments_before_launch():
     assert call_step(cfg, w, ws=FAKE + 16) == -4            # workspace must be 256-aligned
     w.layer[0].wq = None
     assert call_step(cfg, w) == -1
+
+
+def test_noalloc_step_checks_arguments_and_scratch_size_before_launch():
+    """The no-allocation step validates like the workspace step, and refuses (before any
+    HIP call) a configuration whose workspace exceeds its static scratch."""
+    L = binding.lib()
+    full = binding.make_config(synth.FULL)
+    w = fake_weights(full)
+    call = lambda cfg, b: L.dflash_draft_step_noalloc(ctypes.byref(cfg), ctypes.byref(w), b,
+                                                      FAKE, 8, FAKE, FAKE, FAKE, FAKE, 64, FAKE,
+                                                      FAKE, FAKE, None, None, None)
+    assert binding.workspace_bytes(full, 16, 8) > binding.NOALLOC_SCRATCH_BYTES
+    assert call(full, 16) == -7                             # ESCRATCH
+    assert call(full, 0) == -1
+    assert call(tiny_cfg(head_dim=96), 1) == -2
+    w.linear_layout = 0
+    assert call(full, 1) == -6
 
 
 def test_draft_step_requires_the_tiled_layout_tag():
