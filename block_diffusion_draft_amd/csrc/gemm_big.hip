@@ -585,15 +585,15 @@ BigGemmPlan big_gemm_plan(int wf, int M, int N, int K) {
     }
     const long long U = T * nst;
     if (U >= 4LL * G) {
-        // (cached: the slot count walks every tile)
-        static thread_local struct { int M, N, K, G, slots; } cache[8] = {};
+        // (cached on exactly the inputs of sk_slots: the slot count walks every tile)
+        static thread_local struct { long long T; int nst, G, slots; } cache[8] = {};
         static thread_local int next = 0;
         int slots = 0;
         for (auto &c : cache)
-            if (c.M == M && c.N == N && c.K == K && c.G == G) slots = c.slots;
+            if (c.slots && c.T == T && c.nst == nst && c.G == G) slots = c.slots;
         if (!slots) {
             slots = sk_slots(T, nst, G);
-            cache[next] = {M, N, K, G, slots};
+            cache[next] = {T, nst, G, slots};
             next = (next + 1) % 8;
         }
         const long long per = (U + G - 1) / G;
