@@ -10,6 +10,15 @@
         a WRITE_SIZE run, each counter scaled by what it reads for a plain device copy
         of N bytes in the same run (N bytes fetched, N written): the mean over the
         --copies largest copy-kernel dispatches.
+    python -m block_diffusion_draft_amd.rocprof_summary launches --fetch DIR --write DIR
+            --sq DIR --trace DIR --kernel PATTERN --copy-bytes N
+        per launch shape (grid) of the kernels matching PATTERN: average duration (kernel
+        trace), HBM bytes per launch (FETCH_SIZE and WRITE_SIZE scaled by the copy as
+        in ``traffic``) and the achieved GB/s, and from a run with SQ counters the VALU
+        and MFMA instructions per wave, the VALU busy fraction SQ_ACTIVE_INST_VALU x 4 /
+        (SIMDs x cycles), the MFMA busy fraction SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x
+        cycles), cycles = GRBM_GUI_ACTIVE / 8 XCDs, and the launch's waves per SIMD
+        (SQ_WAVES / SIMDs).
     python -m block_diffusion_draft_amd.rocprof_summary mfma DIR [PATTERN]
         per (kernel, grid) matrix-core use from a run with the counters
         SQ_VALU_MFMA_BUSY_CYCLES (MFMA busy cycles summed over the SIMDs; 32 per
@@ -139,12 +148,73 @@ def traffic(fetch_dir, write_dir, kernel, copy_bytes, copies=3, copy_pat="copyBu
     return res
 
 
+def _per_dispatch(d, pattern):
+    """{dispatch id: {"name", "grid", counter: value summed over dimensions}}."""
+    per = {}
+    for r in _rows(d, "counter_collection.csv"):
+        if not re.search(pattern, r["Kernel_Name"]):
+            continue
+        e = per.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"],
+                                              "grid": int(r.get("Grid_Size") or 0)})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def launches(fetch_dir, write_dir, sq_dir, trace_dir, kernel, copy_bytes, copies=3,
+             copy_pat="copyBuffer", cus=256, xcds=8, out=sys.stdout):
+    scales = {}
+    for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        c, _ = _counter(d, cname, copy_pat)
+        cv = sorted(c.values())[-copies:]
+        scales[cname] = copy_bytes / (sum(cv) / len(cv) * 1024.0)
+    agg = {}
+    for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for e in _per_dispatch(d, kernel).values():
+            if cname in e:
+                agg.setdefault((short(e["name"], 40), e["grid"]), {}).setdefault(cname, []).append(
+                    e[cname] * 1024.0 * scales[cname])
+    for e in _per_dispatch(sq_dir, kernel).values():
+        a = agg.setdefault((short(e["name"], 40), e["grid"]), {})
+        for k, v in e.items():
+            if k not in ("name", "grid"):
+                a.setdefault(k, []).append(v)
+    for r in _rows(trace_dir, "kernel_trace.csv"):
+        if not re.search(kernel, r["Kernel_Name"]):
+            continue
+        g = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0) * int(r.get("Grid_Size_Y") or 1) * \
+            int(r.get("Grid_Size_Z") or 1)
+        key = (short(r["Kernel_Name"], 40), g)
+        if key in agg:
+            agg[key].setdefault("us", []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    mean = lambda v: sum(v) / len(v) if v else float("nan")
+    out.write(f"{'kernel':40s} {'grid':>8s} {'us':>7s} {'hbm_MB':>8s} {'GB/s':>7s} "
+              f"{'valu/wave':>9s} {'mfma/wave':>9s} {'valu_busy':>9s} {'mfma_busy':>9s} "
+              f"{'waves/simd':>10s}\n")
+    for (n, g), a in sorted(agg.items(), key=lambda kv: -mean(kv[1].get("us", [0]))):
+        us = mean(a.get("us", []))
+        hbm = mean(a.get("FETCH_SIZE", [])) + mean(a.get("WRITE_SIZE", []))
+        cyc = mean(a.get("GRBM_GUI_ACTIVE", [])) / xcds
+        waves = mean(a.get("SQ_WAVES", []))
+        simds = 4 * cus
+        out.write(f"{n:40s} {g:8d} {us:7.1f} {hbm / 1e6:8.2f} {hbm / us / 1e3:7.0f} "
+                  f"{mean(a.get('SQ_INSTS_VALU', [])) / waves:9.0f} "
+                  f"{mean(a.get('SQ_INSTS_MFMA', [])) / waves:9.0f} "
+                  f"{mean(a.get('SQ_ACTIVE_INST_VALU', [])) * 4 / (simds * cyc):9.3f} "
+                  f"{mean(a.get('SQ_VALU_MFMA_BUSY_CYCLES', [])) / (simds * cyc):9.3f} "
+                  f"{waves / simds:10.2f}\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     a = sub.add_parser("stats"); a.add_argument("dir")
     a = sub.add_parser("trace"); a.add_argument("dir"); a.add_argument("pattern", nargs="?", default="")
     a = sub.add_parser("mfma"); a.add_argument("dir"); a.add_argument("pattern", nargs="?", default="")
+    a = sub.add_parser("launches")
+    for o in ("--fetch", "--write", "--sq", "--trace", "--kernel"):
+        a.add_argument(o, required=True)
+    a.add_argument("--copy-bytes", type=int, required=True)
     a = sub.add_parser("traffic")
     a.add_argument("--fetch", required=True); a.add_argument("--write", required=True)
     a.add_argument("--kernel", required=True); a.add_argument("--copy-bytes", type=int, required=True)
@@ -158,6 +228,8 @@ def main():
         trace(args.dir, args.pattern)
     elif args.cmd == "mfma":
         mfma(args.dir, args.pattern)
+    elif args.cmd == "launches":
+        launches(args.fetch, args.write, args.sq, args.trace, args.kernel, args.copy_bytes)
     else:
         r = traffic(args.fetch, args.write, args.kernel, args.copy_bytes, args.copies)
         lines = [f"kernel_pattern {args.kernel}",
