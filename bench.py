@@ -12,10 +12,13 @@ same seed recipe).  With --accept sampled the acceptance is dflash_verify_sample
 sampling against synthetic fp32 target logits [1][8][248320] resident in HBM, at the
 pages' sampler settings).
 
-Prints one JSON line: draft blocks/s, the roofline of the dominant kernel (the
-248320 x 5120 bf16 output head, timed live with HIP events around its launch
-inside every timed step), and the float64 CPU reference timed on this host on
-a bounded sample of the same workload.
+Prints one JSON line: draft blocks/s from the median of the K step times (each step
+timed by its own pair of HIP events, steps back to back), with p10 / p90 / mean; the
+roofline of the dominant kernel (the 248320 x 5120 bf16 output head), timed with HIP
+events that the library records on the step's stream immediately around the head's
+launch, over K eager steps run right after the timed graph replays (HIP does not
+time events recorded inside a captured graph); and the float64 CPU reference timed
+on this host on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
@@ -195,18 +198,24 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
 
+    # timed region: K steps back to back, an event pair around each (no host sync
+    # in between), plus one pair around the whole run
     t_start, t_stop = binding.HipEvent(), binding.HipEvent()
+    step_ev = [binding.HipEvent() for _ in range(K + 1)]
     torch.cuda.synchronize()
     t_start.record()
-    if graph is not None:
-        for i in range(K):
+    for i in range(K):
+        step_ev[i].record()
+        if graph is not None:
             graph.replay()
-    else:
-        for i in range(K):
+        else:
             one_step(probes[i])
+    step_ev[K].record()
     t_stop.record()
     torch.cuda.synchronize()
-    ms = t_start.elapsed_ms(t_stop) / K
+    ms_mean = t_start.elapsed_ms(t_stop) / K
+    step_ms = np.array([step_ev[i].elapsed_ms(step_ev[i + 1]) for i in range(K)])
+    ms = float(np.median(step_ms))
 
     # live timing of the dominant kernel (eager pass with probes)
     for i in range(K):
@@ -228,6 +237,8 @@ def main():
         "value": wl.batch / (ms * 1e-3),
         "unit": "draft blocks/s",
         "n_gpus": 1, "steps": K, "warmup": Wm, "ms_per_step": ms,
+        "step_ms": {"median": ms, "p10": float(np.percentile(step_ms, 10)),
+                    "p90": float(np.percentile(step_ms, 90)), "mean": ms_mean},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "ctx_len": wl.ctx_len,

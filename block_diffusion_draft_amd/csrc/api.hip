@@ -162,8 +162,9 @@ struct Ctx {
 // The many-row GEMM (more than 16 rows) into partials [splits][M][N]; returns the
 // number of splits or a negative status.
 int run_big(int wfmt, const void *const *w, const int *seg_end, int nseg, const uint16_t *A,
-            int lda, int M, int N, int K, float *part, hipStream_t st) {
+            int lda, int M, int N, int K, float *part, hipStream_t st, int pair = 0) {
     BigGemmArgs g = {};
+    g.lo_row = pair;
     for (int i = 0; i < 3; i++) {
         g.w[i] = w[i];
         g.seg_end[i] = seg_end[i];
@@ -199,7 +200,7 @@ int run_quant(int fmt, const Q4kFusedArgs &a, hipStream_t st, int *pair_left) {
     if (use_big(fmt, a.M, a.N, K)) {
         const void *w[3] = {a.w[0], a.w[1], a.w[2]};
         return run_big(big_fmt(fmt), w, a.seg_end, a.nseg, a.src.A, a.src.lda, a.M, a.N, K,
-                       a.part, st);
+                       a.part, st, a.pair);
     }
     return DFLASH_ESHAPE;      // (every valid Q4_K / Q8_0 shape takes one of the two above)
 }

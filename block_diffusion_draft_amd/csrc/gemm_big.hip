@@ -10,7 +10,9 @@
 // with independent chains).  A quantised weight w (Q4_K: d sc q - dmin m, Q8_0: d q,
 // formed in fp32) enters as two bf16 terms, hi = bf16(w) and lo = bf16(w - hi), each
 // multiplied by the same activation operand: hi + lo carries w to 2^-18 of itself,
-// below the fp32 accumulation's own rounding over K of a few thousand.
+// below the fp32 accumulation's own rounding over K of a few thousand.  Where the
+// activations are themselves (hi, lo) pairs (rows >= lo_row, the MLP inputs), the lo
+// rows skip the weights' lo term: that product is within 2^-18 of the pair's sum.
 //
 // Workgroup: 8 waves (2 along M x 4 along N), each a 128 x 64 block (BM = 256; 64 x 64
 // for BM = 128) of 32 x 32 MFMA tiles.  The operands sit in LDS in MFMA lane order,
@@ -441,6 +443,9 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
 
     const int rl = lane & 31;
     const int rp0 = dma_pos(rl, lane >> 5), rp1 = dma_pos(rl, 2 + (lane >> 5));
+    // this wave's rows are all lo terms of activation pairs: their products with the
+    // weights' lo terms (<= 2^-18 of the sum) are skipped (wave-uniform)
+    const bool lo_rows = a.lo_row > 0 && m0 + wm * WM >= a.lo_row;
     auto compute = [&](const u32x4_t *Ab, const u32x4_t *Bb) {
 #pragma unroll
         for (int ks = 0; ks < 2; ks++) {
@@ -457,7 +462,7 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
 #pragma unroll
                 for (int j = 0; j < 2; j++) {
                     acc[i][j] = mfma32x32x16(af, bh[j], acc[i][j]);
-                    acc[i][j] = mfma32x32x16(af, bl[j], acc[i][j]);
+                    if (!lo_rows) acc[i][j] = mfma32x32x16(af, bl[j], acc[i][j]);
                 }
             }
         }

@@ -213,6 +213,9 @@ struct BigGemmArgs {
     float *C;
     int ldc;
     RowScale rs;
+    int lo_row;                  // rows >= lo_row are the lo terms of (hi, lo) activation
+                                 // pairs (0: none): their product with the weights' own
+                                 // lo terms (2^-18 of the sum) is skipped
 };
 struct BigGemmPlan {
     int bm, bn, grid_x, grid_y;  // tile rows (128 / 256) and columns (256; 512 for bf16 at
