@@ -19,9 +19,10 @@ struct Plan {
     int attn_chunk, attn_nch;
     int topk_nch;
     bool lm_skinny;
+    int head_nrun, head_rc;      // column runs of the skinny head's statistics (rc 0: none)
     // byte offsets into the workspace
     size_t o_valid, o_h, o_xc, o_u2, o_fcout, o_Q, o_Kb, o_Vb, o_attnO, o_attnML, o_o, o_zp,
-        o_Y, o_mid2, o_f, o_logits, o_topk, o_ssq_x, o_ssq_c, o_ssq_u, o_part;
+        o_Y, o_mid2, o_f, o_logits, o_topk, o_rstat, o_ssq_x, o_ssq_c, o_ssq_u, o_part;
     size_t total;
 };
 
@@ -78,6 +79,19 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
     // output-head rows held in LDS: K/32 fragments of 512 bytes (+1 zero entry)
     p.lm_skinny = p.R <= 8 && p.H % 256 == 0 &&
                   ((size_t)(p.H / 32) * 32 + 16 + 8 * 512) * 16 <= 160 * 1024;
+    // the streaming head leaves per-run softmax statistics for the selector (one launch
+    // after the head instead of two passes over the logits) where the runs fit it
+    p.head_nrun = p.head_rc = 0;
+    if (p.lm_skinny) {
+        head_runs(p.V, p.H, &p.head_nrun, &p.head_rc);
+    } else if (big_gemm_ok(0, p.R, p.V, p.H)) {
+        // the many-row head: one run per N tile of its grid
+        const BigGemmPlan hp = big_gemm_plan_grid(0, p.R, p.V, p.H);
+        p.head_nrun = hp.grid_x;
+        p.head_rc = hp.bn;
+    }
+    if (p.head_rc > 512 || (p.head_rc & (p.head_rc - 1)) || p.head_nrun > 2048)
+        p.head_nrun = p.head_rc = 0;
 
     size_t part = 0;
     const int fmt = c->weight_fmt;
@@ -109,6 +123,7 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
     p.o_f = take((size_t)p.R * p.H * 2);
     p.o_logits = take((size_t)p.R * p.V * 4);
     p.o_topk = take(topk_workspace_floats(p.R, p.V) * 4);
+    p.o_rstat = take((size_t)p.R * p.head_nrun * 2 * 4);
     p.o_ssq_x = take((size_t)p.M_blk * (p.H / 256) * 4);
     p.o_ssq_c = take((size_t)p.M_ctx * (p.H / 256) * 4);
     p.o_ssq_u = take((size_t)p.M_blk * (p.H / 256) * 4);
@@ -466,6 +481,7 @@ int draft_step_impl(const dflash_config *cfg, const dflash_weights *w, int batch
         a.M = p.R; a.N = p.V; a.K = H; a.C = logits; a.ldc = p.V;
         a.A = f; a.lda = H;
         a.rs = rowscale(ssq_x, p.T);           // the final norm of the proposal rows
+        if (p.head_rc) a.rstat = x.at<float>(p.o_rstat);
         const bool probe_lm = probe && probe->kernel == DFLASH_PROBE_LM_HEAD;
         if (probe_lm) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_start, x.st));
         if (p.lm_skinny) {
@@ -478,6 +494,7 @@ int draft_step_impl(const dflash_config *cfg, const dflash_weights *w, int batch
             g.wfmt = 0;
             g.A = f; g.lda = H; g.M = p.R; g.N = p.V; g.K = H; g.C = logits; g.ldc = p.V;
             g.rs = a.rs;
+            g.rstat = a.rstat;
             // one split: the row scale is applied in the epilogue
             const BigGemmPlan bp = big_gemm_plan_grid(0, p.R, p.V, H);
             HIPCHK(launch_big_gemm(g, bp, x.st));
@@ -487,9 +504,15 @@ int draft_step_impl(const dflash_config *cfg, const dflash_weights *w, int batch
         if (probe_lm) HIPCHK(hipEventRecord((hipEvent_t)probe->ev_stop, x.st));
     }
     // S10 + S11: log-softmax statistics, top-K, and the selector path
-    HIPCHK(launch_topk_path(logits, batch, p.P, p.V, p.K, valid, x.at<float>(p.o_topk), w->code_a,
-                            w->code_b, p.r, cfg->pair_scale, cand_ids, cand_logp, draft_tokens,
-                            x.st));
+    if (p.head_rc)
+        HIPCHK(launch_topk_path_runs(logits, x.at<float>(p.o_rstat), p.head_nrun, p.head_rc, batch,
+                                     p.P, p.V, p.K, valid, x.at<float>(p.o_topk), w->code_a,
+                                     w->code_b, p.r, cfg->pair_scale, cand_ids, cand_logp,
+                                     draft_tokens, x.st));
+    else
+        HIPCHK(launch_topk_path(logits, batch, p.P, p.V, p.K, valid, x.at<float>(p.o_topk),
+                                w->code_a, w->code_b, p.r, cfg->pair_scale, cand_ids, cand_logp,
+                                draft_tokens, x.st));
     return DFLASH_OK;
 }
 

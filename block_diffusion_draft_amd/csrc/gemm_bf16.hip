@@ -166,6 +166,13 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a, int ti
 #pragma unroll
     for (int v = 0; v < 4; v++) rinv[v] = g == 0 ? inv8[v] : (g == 1 ? inv8[4 + v] : 0.f);
 
+    // running softmax statistics of this wave's columns, per row (lane-uniform)
+    float rmax[8], rsum[8];
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+        rmax[m] = -INFINITY;
+        rsum[m] = 0.f;
+    }
     // lanes of rows >= 8 read the zero entry
     const int aoff = c < 8 ? g * 8 + c : 0;
     const int astep = c < 8 ? 32 : 0;
@@ -201,6 +208,9 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a, int ti
 // The outputs of up to 8 consecutive tiles stay in registers and are then written as
 // 128 consecutive columns per row (lanes over columns, whole lines): written tile by
 // tile in the MFMA layout, the rows' 64-byte pieces cost the stream about 8%.
+// With a.rstat, each wave also leaves the softmax statistics of its run of columns per
+// row: the run's max M and sum of exp(v - M) over the values it wrote (merged across
+// its output batches), the pair at rstat[2 (row nrun + wave index)].
 constexpr int HS_WAVES = 8;
 constexpr int HS_D = 4;
 constexpr int HS_TB = 8;           // tiles per output batch
@@ -283,6 +293,13 @@ __global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a, int tiles_p
         inv8[r] = r < a.M ? (rs.ssq ? rsqrtf(ss / rs.n + rs.eps) : 1.f) : 0.f;
     }
 
+    // running softmax statistics of this wave's columns, per row (lane-uniform)
+    float rmax[8], rsum[8];
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+        rmax[m] = -INFINITY;
+        rsum[m] = 0.f;
+    }
     // lanes of rows >= 8 read the zero entry
     const int aoff = c < 8 ? g * 8 + c : 0;
     const int astep = c < 8 ? 32 : 0;
@@ -318,9 +335,10 @@ __global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a, int tiles_p
         // row m, columns 16 tb + 64 h + lane: tile 4 h + lane / 16, column lane % 16,
         // held by lane 16 (m / 4) + lane % 16 as component m % 4
         const int ncols = min(HS_TB, t1 - tb) * 16;
+        float vh[8][HS_TB / 4];                    // row m's values of this lane (rows >= M: -inf)
 #pragma unroll
         for (int m = 0; m < 8; m++) {
-            if (m >= a.M) break;
+            const bool mok = m < a.M;
             const int src = 16 * (m / 4) + (lane & 15);
 #pragma unroll
             for (int h = 0; h < HS_TB / 4; h++) {
@@ -331,9 +349,57 @@ __global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a, int tiles_p
                     v = (lane >> 4) == j ? x : v;
                 }
                 const int col = 64 * h + lane;
-                if (col < ncols) a.C[(size_t)m * a.ldc + (size_t)tb * 16 + col] = v * inv8[m];
+                v *= inv8[m];
+                vh[m][h] = mok && col < ncols ? v : -INFINITY;
+                if (mok && col < ncols) a.C[(size_t)m * a.ldc + (size_t)tb * 16 + col] = v;
             }
         }
+        if (a.rstat) {
+            // the 8 rows' reductions interleaved (independent shuffle chains)
+            float bm[8], bs[8];
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                bm[m] = vh[m][0];
+#pragma unroll
+                for (int h = 1; h < HS_TB / 4; h++) bm[m] = fmaxf(bm[m], vh[m][h]);
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+                for (int m = 0; m < 8; m++) bm[m] = fmaxf(bm[m], __shfl_xor(bm[m], o, WAVE));
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                bs[m] = 0.f;
+#pragma unroll
+                for (int h = 0; h < HS_TB / 4; h++)
+                    bs[m] += vh[m][h] == -INFINITY ? 0.f : __expf(vh[m][h] - bm[m]);
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+                for (int m = 0; m < 8; m++) bs[m] += __shfl_xor(bs[m], o, WAVE);
+            // merge with the earlier batches of the run (a row's batch max is finite when
+            // the row exists: a batch has a column)
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                if (bm[m] == -INFINITY) continue;
+                const float nm = fmaxf(rmax[m], bm[m]);
+                rsum[m] = (rmax[m] == -INFINITY ? 0.f : rsum[m] * __expf(rmax[m] - nm)) +
+                          bs[m] * __expf(bm[m] - nm);
+                rmax[m] = nm;
+            }
+        }
+    }
+    if (a.rstat && lane < 8 && lane < a.M) {
+        // lane m writes row m's pair (register arrays indexed by constants only)
+        float mx = rmax[0], sm = rsum[0];
+#pragma unroll
+        for (int m = 1; m < 8; m++) {
+            mx = lane == m ? rmax[m] : mx;
+            sm = lane == m ? rsum[m] : sm;
+        }
+        const int nrun = gridDim.x * HS_WAVES, w = blockIdx.x * HS_WAVES + wave;
+        *reinterpret_cast<float2 *>(a.rstat + 2 * ((size_t)lane * nrun + w)) = make_float2(mx, sm);
     }
 }
 
@@ -343,6 +409,19 @@ hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st) {
     dim3 grid(ceil_div(a.N, 128), ceil_div(a.M, 128));
     hipLaunchKernelGGL(k_gemm_tiled, grid, dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+void head_runs(int N, int K, int *nrun, int *run_cols) {
+    const int ntiles = N / 16;
+    if (K % (128 * HS_D) != 0 || ntiles < 1) {
+        *nrun = 0;
+        *run_cols = 0;
+        return;
+    }
+    const int tpw = ceil_div(ntiles, 256 * HS_WAVES);
+    const int waves = ceil_div(ntiles, tpw);
+    *nrun = ceil_div(waves, HS_WAVES) * HS_WAVES;
+    *run_cols = (tpw & (tpw - 1)) == 0 ? 16 * tpw : 0;      // (the selector takes 2^k-wide runs)
 }
 
 hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st) {
@@ -362,6 +441,7 @@ hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st) {
         hipLaunchKernelGGL(k_head_stream, dim3(ceil_div(waves, HS_WAVES)), dim3(512), lds, st, a, tpw);
         return hipGetLastError();
     }
+    if (a.rstat) return hipErrorInvalidValue;            // (statistics: the kernel above only)
     const int tpw = ceil_div(ntiles, 2048);               // ~2048 waves, 2 workgroups per CU
     const int waves = ceil_div(ntiles, tpw);
     const size_t lds = ((size_t)(a.K / 32) * 32 + 1) * 16;

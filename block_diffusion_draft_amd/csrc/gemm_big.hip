@@ -112,6 +112,65 @@ __device__ __forceinline__ void store_tile(const BigGemmArgs &a, const f32x16_t 
             }
         }
     }
+    if (scale && a.rstat) {
+        // softmax statistics of the tile's columns per row (one column run per tile).
+        // Each wave stages a 32-row block of its values in LDS, lane (row, half) = (l % 32,
+        // l / 32) reduces half a row's WN columns serially (one shuffle joins the halves);
+        // the 4 waves
+        // of a row band merge through LDS; one thread per row writes the pair.
+        float *ws = rinv + BM;                     // [BM][4 waves][2]
+        // (row stride WN + 1: the 32 lanes of a half-wave read 32 banks)
+        constexpr int TS = WN + 1;
+        float *tb = rinv + 9 * BM + (wm * 4 + wn) * 32 * TS;
+        const int sr = lane & 31, sh = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int rr = 8 * (v >> 2) + 4 * hl + (v & 3);
+                const float ri = rinv[wm * WM + 32 * i + rr];
+#pragma unroll
+                for (int j = 0; j < FN; j++) {
+                    const int n = n0 + wn * WN + 32 * j + c;
+                    tb[rr * TS + 32 * j + c] = n < a.N ? acc[i][j][v] * ri : -INFINITY;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);    // this wave's LDS stores done
+            __builtin_amdgcn_wave_barrier();
+            const float *src = tb + sr * TS + sh * (WN / 2);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < WN / 2; k++) mx = fmaxf(mx, src[k]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+            float se = 0.f;
+#pragma unroll
+            for (int k = 0; k < WN / 2; k++) se += src[k] == -INFINITY ? 0.f : __expf(src[k] - mx);
+            se += __shfl_xor(se, 32, WAVE);
+            if (sh == 0) {
+                const int r = wm * WM + 32 * i + sr;
+                ws[(r * 4 + wn) * 2] = mx;
+                ws[(r * 4 + wn) * 2 + 1] = se;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();       // (the next block reuses the staging)
+        }
+        __syncthreads();
+        const int nrun = ceil_div(a.N, 4 * WN);
+        for (int r = tid; r < BM; r += NTH) {
+            if (m0 + r >= a.M) continue;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < 4; w++) M = fmaxf(M, ws[(r * 4 + w) * 2]);
+            float S = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; w++) {
+                const float m = ws[(r * 4 + w) * 2];
+                S += m == -INFINITY ? 0.f : ws[(r * 4 + w) * 2 + 1] * expf(m - M);
+            }
+            *reinterpret_cast<float2 *>(a.rstat + 2 * ((size_t)(m0 + r) * nrun + n0 / (4 * WN))) =
+                make_float2(M, S);
+        }
+    }
 }
 
 // zeroes slots [from, to) of a tile (N and ldc are multiples of 4)

@@ -28,12 +28,19 @@ struct Bf16GemmArgs {
     float *C;                    // fp32 [M][ldc]
     int ldc;
     RowScale rs;                 // output row r multiplied by row_inv(rs, r) (ssq null: none)
+    float *rstat;                // nullable (skinny head only): per output row and column
+                                 // run, the run's max and sum of exp(value - max)
 };
 // tiled 128x128 MFMA GEMM, any M
 hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st);
 // rows <= 8, one weight matrix (nseg == 1): activations resident in LDS, every wave
 // streams whole weight tiles
 hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st);
+// Column runs of the skinny head's softmax statistics for an N x K head: each wave of the
+// streaming head kernel covers run_cols consecutive columns and, given a.rstat, writes per
+// row r and run w the pair (max, sum exp(v - max)) at rstat[2 (r nrun + w)].  run_cols 0:
+// the shape takes the kernel without statistics.
+void head_runs(int N, int K, int *nrun, int *run_cols);
 
 // ---------------------------------------------------------------- layer ops
 enum EpiMode { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_SWIGLU_BF16 = 2, EPI_STORE_BF16 = 3 };
@@ -113,6 +120,14 @@ hipError_t launch_topk_path(const float *logits, int B, int P, int V, int K, con
                             float *ws, const uint16_t *code_a, const uint16_t *code_b, int r,
                             float pair_scale, int32_t *cand_ids, float *cand_logp,
                             int32_t *draft_tokens, hipStream_t st);
+// The same selection and path from the head's column-run statistics (head_runs): one
+// launch; per row the threshold and logsumexp come from the runs' (max, sum) pairs and
+// only the runs whose max reaches the threshold are read back.  ws: as above.
+hipError_t launch_topk_path_runs(const float *logits, const float *rstat, int nrun, int run_cols,
+                                 int B, int P, int V, int K, const int32_t *valid, float *ws,
+                                 const uint16_t *code_a, const uint16_t *code_b, int r,
+                                 float pair_scale, int32_t *cand_ids, float *cand_logp,
+                                 int32_t *draft_tokens, hipStream_t st);
 
 // Sampled acceptance of B sequences of n drafted tokens against target logits
 // [B][n + 1][V]: top-K of every row (the same threshold passes), then per sequence the
@@ -216,6 +231,9 @@ struct BigGemmArgs {
     int lo_row;                  // rows >= lo_row are the lo terms of (hi, lo) activation
                                  // pairs (0: none): their product with the weights' own
                                  // lo terms (2^-18 of the sum) is skipped
+    float *rstat;                // nullable, one split with a row scale (the output head):
+                                 // per row and N tile (run of bn columns) the tile's max
+                                 // and sum of exp(v - max) at rstat[2 (row grid_x + tile)]
 };
 struct BigGemmPlan {
     int bm, bn, grid_x, grid_y;  // tile rows (128 / 256) and columns (256; 512 for bf16 at

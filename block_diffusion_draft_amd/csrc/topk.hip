@@ -23,7 +23,14 @@
 // not depend on thread scheduling.  K <= 64 (the threshold is a lane maximum).
 //
 // Pass 3 runs inside the selector's workgroup (one per sequence): its waves select the
-// sequence's rows, then the candidate-path search runs on them.  Selector (same card,
+// sequence's rows, then the candidate-path search runs on them.
+//
+// With the statistics of the output head's column runs (the streaming head writes, per
+// row and per run of 16 tpw columns, the run's max and sum of exp(v - max)), passes 1 and
+// 2 are not launched: the selector's wave for a row reads the run statistics (all loads
+// in flight), forms the row's logsumexp and theta = the K-th largest of the 64 lane
+// maxima of the run maxima (again K distinct logits reach it), and reads back only the
+// runs whose maximum reaches theta: their logits >= theta form the candidate list.  Selector (same card,
 // spec table "Draft" row: candidate selector, top 16, rank 256; "Weights" row: two
 // 248320 x 256 codebooks; "How it is used": one coherent path through the top 16
 // candidates per position): the path objective used here is the sum over positions of
@@ -269,6 +276,182 @@ __device__ void select_row(const float *logits, int V, int nch, int K, int r, co
 }
 
 
+// top-K of n candidates (v, id) held in LDS (n <= RCAP), into sid / slp (logit - L)
+constexpr int RCAP = 512;                // candidate logits per row (LDS, run selection)
+constexpr int RUNCAP = 256;              // candidate runs per row
+constexpr int RPL = 32;                  // run statistics per lane (runs per row <= 2048)
+
+__device__ void select_lds_list(int n, const float *cvl, const int *cil, int K, float L,
+                                int *sid, float *slp) {
+    const int lane = threadIdx.x & 63;
+    if (n <= 64) {
+        const unsigned long long key = lane < n ? cand_key(cvl[lane], cil[lane]) : 0ull;
+        const unsigned long long sk = wave_sort_desc(key);
+        if (lane < K) {
+            const bool have = lane < n;
+            sid[lane] = have ? key_id(sk) : -1;
+            slp[lane] = have ? key_value(sk) - L : -INFINITY;
+        }
+        return;
+    }
+    constexpr int PL = RCAP / 64;
+    float v[PL];
+    int id[PL];
+#pragma unroll
+    for (int k = 0; k < PL; k++) {
+        const int s = lane + 64 * k;
+        v[k] = s < n ? cvl[s] : -INFINITY;
+        id[k] = s < n ? cil[s] : -1;
+    }
+    for (int round = 0; round < K; round++) {
+        float bv = -INFINITY;
+        int bi = -1;
+#pragma unroll
+        for (int k = 0; k < PL; k++)
+            if (take(v[k], id[k], bv, bi)) { bv = v[k]; bi = id[k]; }
+        wave_best(bv, bi);
+#pragma unroll
+        for (int k = 0; k < PL; k++)
+            if (id[k] == bi) id[k] = -1;
+        if (lane == 0) {
+            sid[round] = bi;
+            slp[round] = bi >= 0 ? bv - L : -INFINITY;
+        }
+    }
+}
+
+// exact running top-K over every logit of row r (lanes < K hold the list)
+__device__ void select_full_scan(const float *logits, int V, int nch, int K, int r, float L,
+                                 int *sid, float *slp) {
+    const int lane = threadIdx.x & 63;
+    float lv = -INFINITY;
+    int li = -1;
+    const float *row = logits + (size_t)r * V;
+    for (int c = 0; c < nch; c++) {
+        float v[PER_LANE];
+        int id[PER_LANE];
+#pragma unroll
+        for (int k = 0; k < PER_LANE; k++) {
+            const int i = c * CHUNK + lane + 64 * k;
+            v[k] = i < V ? row[i] : -INFINITY;
+            id[k] = i < V ? i : -1;
+        }
+        float nv = -INFINITY;
+        int ni = -1;
+        for (int round = 0; round < K; round++) {
+            float bv = lv;
+            int bi = li;
+#pragma unroll
+            for (int k = 0; k < PER_LANE; k++)
+                if (take(v[k], id[k], bv, bi)) { bv = v[k]; bi = id[k]; }
+            wave_best(bv, bi);
+            if (li == bi) li = -1;
+#pragma unroll
+            for (int k = 0; k < PER_LANE; k++)
+                if (id[k] == bi) id[k] = -1;
+            if (lane == round) { nv = bv; ni = bi; }
+        }
+        lv = nv;
+        li = ni;
+    }
+    if (lane < K) {
+        sid[lane] = li;
+        slp[lane] = li >= 0 ? lv - L : -INFINITY;
+    }
+}
+
+// one wave, row r: top-K from the head's run statistics (nrun <= 64 RPL runs of rc = 2^lrc
+// <= 512 columns); cvl, cil, crun, cmax: this wave's LDS scratch.  theta1 = the K-th
+// largest of the 64 lane maxima of the run maxima; among the runs reaching it (at least
+// K), theta2 = the K-th largest run maximum, which is the K-th largest of all run maxima:
+// the K runs above it each hold a logit >= theta2, so every top-K logit is >= theta2 and
+// lies in a run whose maximum reaches theta2.  Those runs' logits >= theta2 are the
+// candidates (with more than 64 runs at theta1, theta1 is used instead).
+__device__ void select_row_runs(const float *logits, int V, int nrun, int lrc, int K, int r,
+                                const float *rstat, float *cvl, int *cil, int *crun, float *cmax,
+                                int *sid, float *slp) {
+    const int lane = threadIdx.x & 63;
+    const int rc = 1 << lrc;
+    const float2 *st = reinterpret_cast<const float2 *>(rstat) + (size_t)r * nrun;
+    float rm[RPL], rsm[RPL];
+#pragma unroll
+    for (int u = 0; u < RPL; u++) {                 // every load in flight (clamped: in bounds)
+        const float2 v = st[min(lane + 64 * u, nrun - 1)];
+        const bool ok = lane + 64 * u < nrun;
+        rm[u] = ok ? v.x : -INFINITY;
+        rsm[u] = ok ? v.y : 0.f;
+    }
+    float lm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < RPL; u++) lm = fmaxf(lm, rm[u]);
+    const float M = wave_max(lm);
+    float se = 0.f;
+#pragma unroll
+    for (int u = 0; u < RPL; u++) se += rm[u] == -INFINITY ? 0.f : rsm[u] * expf(rm[u] - M);
+    const float L = M + logf(wave_sum(se));
+    const float th1 = __shfl(wave_sort_desc(lm), K - 1, WAVE);
+    // runs reaching theta1, with their maxima
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int nc = 0;
+#pragma unroll
+    for (int u = 0; u < RPL; u++) {
+        const bool c = rm[u] >= th1;
+        const unsigned long long mk = __ballot(c);
+        const int slot = nc + __popcll(mk & below);
+        if (c && slot < RUNCAP) {
+            crun[slot] = lane + 64 * u;
+            cmax[slot] = rm[u];
+        }
+        nc += __popcll(mk);
+    }
+    __builtin_amdgcn_wave_barrier();
+    float th = th1;
+    if (nc <= 64) {
+        // theta2: the K-th largest maximum of those runs; keep the runs reaching it
+        const float mv = lane < nc ? cmax[lane] : -INFINITY;
+        const int rv = lane < nc ? crun[lane] : 0;
+        th = __shfl(wave_sort_desc(mv), K - 1, WAVE);
+        const bool c = lane < nc && mv >= th;
+        const unsigned long long mk = __ballot(c);
+        __builtin_amdgcn_wave_barrier();
+        if (c) crun[__popcll(mk & below)] = rv;
+        nc = __popcll(mk);
+        __builtin_amdgcn_wave_barrier();
+    }
+    int n = 0;
+    if (nc <= RUNCAP) {
+        // their logits >= theta (32 loads per lane in flight per batch)
+        const int ncols = nc << lrc;
+        for (int e0 = 0; e0 < ncols && n <= RCAP; e0 += 64 * 32) {
+            float v[32];
+            int id[32];
+#pragma unroll
+            for (int u = 0; u < 32; u++) {
+                const int e = e0 + 64 * u + lane;
+                const int col = crun[e < ncols ? e >> lrc : 0] * rc + (e & (rc - 1));
+                id[u] = e < ncols && col < V ? col : -1;
+                v[u] = logits[(size_t)r * V + (id[u] >= 0 ? col : 0)];
+            }
+#pragma unroll
+            for (int u = 0; u < 32; u++) {
+                const bool t = id[u] >= 0 && v[u] >= th;
+                const unsigned long long mk = __ballot(t);
+                const int slot = n + __popcll(mk & below);
+                if (t && slot < RCAP) {
+                    cvl[slot] = v[u];
+                    cil[slot] = id[u];
+                }
+                n += __popcll(mk);
+            }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (nc > RUNCAP || n > RCAP)                   // (many equal logits): exact scan
+        select_full_scan(logits, V, ceil_div(V, CHUNK), K, r, L, sid, slp);
+    else
+        select_lds_list(n, cvl, cil, K, L, sid, slp);
+}
+
 constexpr int MAXK = 16;
 constexpr int MAXP = 16;
 constexpr int PATH_WAVES = 8;
@@ -282,18 +465,30 @@ constexpr int PATH_WAVES = 8;
 // ...; the dynamic programme then runs on K lanes.
 __global__ __launch_bounds__(64 * PATH_WAVES) void k_select_path(
     const float *logits, int V, int nch, int K, const int *count, const float *cv,
-    const int32_t *ci, const float *lse, int P, const int32_t *valid, const uint16_t *code_a,
-    const uint16_t *code_b, int r, float s, int32_t *cand_ids, float *cand_logp, int32_t *draft) {
+    const int32_t *ci, const float *lse, const float *rstat, int nrun, int lrc, int P,
+    const int32_t *valid, const uint16_t *code_a, const uint16_t *code_b, int r, float s,
+    int32_t *cand_ids, float *cand_logp, int32_t *draft) {
     __shared__ int ids[MAXP][MAXK];
     __shared__ float lp[MAXP][MAXK];
     __shared__ float Tm[MAXP][MAXK][MAXK];
     __shared__ float delta[2][MAXK];
     __shared__ int psi[MAXP][MAXK];
+    // run selection: per wave the candidate logits and runs of its row
+    __shared__ float cvl[PATH_WAVES][RCAP];
+    __shared__ int cil[PATH_WAVES][RCAP];
+    __shared__ int crun[PATH_WAVES][RUNCAP];
+    __shared__ float cmax[PATH_WAVES][RUNCAP];
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool ok = valid[b] != 0;
     for (int t = wave; t < P; t += PATH_WAVES) {
         const int row = b * P + t;
-        if (ok) select_row(logits, V, nch, K, row, count, cv, ci, lse[row], ids[t], lp[t]);
+        if (ok) {
+            if (rstat)
+                select_row_runs(logits, V, nrun, lrc, K, row, rstat, cvl[wave], cil[wave],
+                                crun[wave], cmax[wave], ids[t], lp[t]);
+            else
+                select_row(logits, V, nch, K, row, count, cv, ci, lse[row], ids[t], lp[t]);
+        }
         if (lane < MAXK && (lane >= K || !ok)) {
             ids[t][lane] = -1;
             lp[t][lane] = -INFINITY;
@@ -482,8 +677,26 @@ hipError_t launch_topk_path(const float *logits, int B, int P, int V, int K, con
     hipLaunchKernelGGL(k_collect, grid, dim3(256), 0, st, logits, V, nch, K, pm, ps, lse, count, cv,
                        ci);
     hipLaunchKernelGGL(k_select_path, dim3(B), dim3(64 * PATH_WAVES), 0, st, logits, V, nch, K, count,
-                       cv, ci, lse, P, valid, code_a, code_b, r, pair_scale, cand_ids, cand_logp,
-                       draft_tokens);
+                       cv, ci, lse, (const float *)nullptr, 0, 0, P, valid, code_a, code_b, r,
+                       pair_scale, cand_ids, cand_logp, draft_tokens);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_path_runs(const float *logits, const float *rstat, int nrun, int run_cols,
+                                 int B, int P, int V, int K, const int32_t *valid, float *ws,
+                                 const uint16_t *code_a, const uint16_t *code_b, int r,
+                                 float pair_scale, int32_t *cand_ids, float *cand_logp,
+                                 int32_t *draft_tokens, hipStream_t st) {
+    int lrc = 0;
+    while ((1 << lrc) < run_cols) lrc++;
+    if (P > MAXP || K > MAXK || nrun < 1 || nrun > 64 * RPL || run_cols < 1 || run_cols > 512 ||
+        (1 << lrc) != run_cols || (long long)nrun * run_cols < V)
+        return hipErrorInvalidValue;
+    (void)ws;
+    hipLaunchKernelGGL(k_select_path, dim3(B), dim3(64 * PATH_WAVES), 0, st, logits, V,
+                       ceil_div(V, CHUNK), K, (const int *)nullptr, (const float *)nullptr,
+                       (const int32_t *)nullptr, (const float *)nullptr, rstat, nrun, lrc, P,
+                       valid, code_a, code_b, r, pair_scale, cand_ids, cand_logp, draft_tokens);
     return hipGetLastError();
 }
 

@@ -261,3 +261,45 @@ def test_mid_step_many_rows(fmt):
     ref = parity.run_oracle(wl, bufs.host_W, bufs.inputs)
     g = full_check(wl, bufs, ref)
     check_verify(bufs, g)
+
+
+@pytest.mark.parametrize("case,batch", [("all_equal", 1), ("tied_block", 1), ("all_equal", 4),
+                                        ("tied_block", 4)])
+def test_mid_step_head_run_selection_ties(case, batch):
+    """The 1024-wide drafter takes the selection from the output head's column-run
+    statistics: at batch 1 the streaming head's runs of 16 columns, at batch 4 the
+    many-row head's 256-column tiles.  Every head row equal: all logits tie, every run
+    reaches the threshold and the exact scan must return ids 0..K-1 with log-prob
+    -log(V).  A block of 40 equal rows among random ones: candidates tie inside the
+    run lists, and the top K must still be exact by (logit desc, id asc) on the GPU's
+    own logits."""
+    s = synth.MID
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], shape=s, batch=batch, ctx_len=96,
+                             seed=141)
+    say(f"[step] mid head-run selection, {case}, batch {batch}")
+    W = synth.make_weights(s, wl.seed)
+    E = W["embed"].copy()
+    if case == "all_equal":
+        E[:] = E[:1]
+    else:
+        # 40 copies of proposal row 0's best head row: 41 equal top logits in that row
+        probe = runner.StepBuffers(wl, weights=W)
+        probe.step(dbg=False)
+        u = int(probe.cand_ids.cpu().numpy()[0, 0, 0])
+        E[1000:1040] = E[u]
+        del probe
+    W["embed"] = E
+    W["lm_head"] = E
+    bufs = runner.StepBuffers(wl, weights=W)
+    bufs.step()
+    g = gpu_outputs(bufs)
+    K, V = s.top_k, s.vocab
+    if case == "all_equal":
+        assert (g["ids"] == np.arange(K)).all()
+        assert np.allclose(g["lp"], -np.log(V), atol=1e-4)
+    else:
+        want = sorted([u] + list(range(1000, 1040)))[:K]
+        assert g["ids"][0, 0].tolist() == want
+    parity.check_topk_reanchored(g["logits"], g["ids"], g["lp"], K)
+    ref = parity.run_oracle(wl, W, bufs.inputs)
+    assert np.abs(g["logits"] - ref["logits"]).max() <= parity.LOGIT_MAX_ABS
