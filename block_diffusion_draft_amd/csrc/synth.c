@@ -16,11 +16,14 @@
  *     clamped at or below zero, refines them by least squares on the chosen
  *     codes, then quantises scales and mins to 6 bits against fp16 super-block
  *     factors.
+ *   - The Q8_0 and FP8 (E4M3, one scale per row) packers quantise the same normals
+ *     (see their sections below).
  *
  * Built with gcc -O3 -fopenmp into libdflash_synth.so and called through ctypes.
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 static inline uint64_t mix64(uint64_t x) {
@@ -258,5 +261,70 @@ void synth_q8_0_normal(uint64_t seed, uint64_t stream, int64_t rows, int64_t col
             }
             pack_q8_0_block(x, out + (r * nb + b) * 34);
         }
+    }
+}
+
+/* ---------------------------------------------------------------- FP8 (E4M3)
+ * One code per weight (sign, 4 exponent bits of bias 7, 3 mantissa bits; largest
+ * finite 448) and one float32 scale per row: w = s code.  Host-side quantizer (a data
+ * generator, not part of the draft path): s = max |x| / 448 of the row (1 for an
+ * all-zero row), code = x / s rounded to the nearest E4M3 value, ties to the even
+ * mantissa.  Output: the rows' codes, then the rows' scales (little endian). */
+static uint8_t f64_to_e4m3(double v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a < 0x1p-6) return sign | (uint8_t)nearbyint(a * 0x1p9);   /* 8 -> code 0x08 */
+    int e;
+    double m = frexp(a, &e);          /* a = m 2^e, m in [0.5, 1) */
+    double q = nearbyint(m * 16.0);   /* 4 significant bits */
+    if (q == 16.0) { q = 8.0; e += 1; }
+    int E = e - 1 + 7;
+    int code = (E << 3) | ((int)q - 8);
+    if (code > 0x7E) code = 0x7E;
+    return sign | (uint8_t)code;
+}
+
+static void pack_fp8_row(const float *x, int64_t cols, uint8_t *codes, float *scale) {
+    double amax = 0.0;
+    for (int64_t i = 0; i < cols; i++) amax = fmax(amax, fabs((double)x[i]));
+    float s = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+    *scale = s;
+    for (int64_t i = 0; i < cols; i++) codes[i] = f64_to_e4m3((double)x[i] / (double)s);
+}
+
+/* w [rows][cols] float32 -> out: rows * cols codes, then rows float32 scales */
+void synth_fp8_pack(const float *w, int64_t rows, int64_t cols, uint8_t *out) {
+    float *sc = (float *)(out + rows * cols);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        float s;
+        pack_fp8_row(w + r * cols, cols, out + r * cols, &s);
+        memcpy(sc + r, &s, 4);
+    }
+}
+
+/* FP8 bytes of a [rows, cols] matrix of std * N(0,1) weights of the stream, element
+ * (r, c) = normal #(r*cols + c) (the same values the Q4_K and Q8_0 packers quantise). */
+void synth_fp8_normal(uint64_t seed, uint64_t stream, int64_t rows, int64_t cols, float std,
+                      uint8_t *out) {
+    uint64_t key = stream_key(seed, stream);
+    float *sc = (float *)(out + rows * cols);
+#pragma omp parallel
+    {
+        float *x = (float *)malloc((size_t)cols * sizeof(float));
+#pragma omp for schedule(static)
+        for (int64_t r = 0; r < rows; r++) {
+            uint64_t base = (uint64_t)(r * cols);
+            for (int64_t i = 0; i < cols; i += 2) {
+                double z0, z1;
+                normal_pair(key, (base + (uint64_t)i) >> 1, &z0, &z1);
+                x[i] = (float)(std * z0);
+                x[i + 1] = (float)(std * z1);
+            }
+            float s;
+            pack_fp8_row(x, cols, out + r * cols, &s);
+            memcpy(sc + r, &s, 4);
+        }
+        free(x);
     }
 }

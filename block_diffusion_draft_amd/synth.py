@@ -8,7 +8,8 @@ pages measure on prompts and benchmark suites that are not available here, and
 for the draft step only the shapes, the context length and the number of
 appended rows matter, so seeded synthetic tensors stand in for them):
   * linear weights (fc, q/k/v/o, gate/up/down): N(0, 0.02), packed to Q4_K
-    (or Q8_0, or kept bf16 for the unquantised workload);
+    (or Q8_0, or FP8 E4M3 with a scale per row, or kept bf16 for the unquantised
+    workload);
   * shared embedding / output head, dynamic-conv W_c, selector projection and
     codebooks, mask embedding: bf16 N(0, 0.02);
   * norm gains: 1.0 (``gain_jitter`` > 0 gives 1 + jitter * N(0, 1));
@@ -57,9 +58,11 @@ def lib():
         L.synth_q4k_normal.argtypes = [u64, u64, i64, i64, f32, vp]
         L.synth_q8_0_pack.argtypes = [vp, i64, i64, vp]
         L.synth_q8_0_normal.argtypes = [u64, u64, i64, i64, f32, vp]
+        L.synth_fp8_pack.argtypes = [vp, i64, i64, vp]
+        L.synth_fp8_normal.argtypes = [u64, u64, i64, i64, f32, vp]
         for f in (L.synth_normal_f32, L.synth_normal_bf16, L.synth_randint,
                   L.synth_q4k_pack, L.synth_q4k_normal, L.synth_q8_0_pack,
-                  L.synth_q8_0_normal):
+                  L.synth_q8_0_normal, L.synth_fp8_pack, L.synth_fp8_normal):
             f.restype = None
         _lib = L
     return _lib
@@ -153,6 +156,29 @@ def q8_0_normal(seed, name, rows, cols, std=0.02):
     return out
 
 
+def fp8_bytes(rows, cols):
+    """Bytes of an FP8 matrix: one E4M3 code per weight, then one float32 scale per row."""
+    return rows * cols + 4 * rows
+
+
+def fp8_pack(w):
+    """float32 [rows, cols] -> FP8 bytes uint8 [rows * cols + 4 rows] (codes, then scales)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    assert cols % 2 == 0
+    out = np.empty(fp8_bytes(rows, cols), dtype=np.uint8)
+    lib().synth_fp8_pack(w.ctypes.data, rows, cols, out.ctypes.data)
+    return out
+
+
+def fp8_normal(seed, name, rows, cols, std=0.02):
+    """FP8 bytes of a [rows, cols] matrix of std * N(0, 1) weights (stream `name`)."""
+    assert cols % 2 == 0
+    out = np.empty(fp8_bytes(rows, cols), dtype=np.uint8)
+    lib().synth_fp8_normal(seed, stream_id(name), rows, cols, std, out.ctypes.data)
+    return out
+
+
 def bf16_from_f32(x):
     """float32 -> bf16 bits, round to nearest even (finite values)."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
@@ -213,6 +239,7 @@ FULL = Shape(n_layers=5, hidden=5120, ffn=17408, n_q=32, n_kv=8, head_dim=128, w
              vocab=248320, top_k=16, sel_rank=256)
 FULL_BF16 = dataclasses.replace(FULL, weight_fmt="bf16")
 FULL_Q8_0 = dataclasses.replace(FULL, weight_fmt="q8_0")
+FULL_FP8 = dataclasses.replace(FULL, weight_fmt="fp8")
 # a mid-size drafter whose every product has K a multiple of 1024 (the 16-row Q8_0
 # streaming kernel's split), small enough for the oracle in seconds
 MID = Shape(n_layers=2, hidden=1024, ffn=2048, n_q=8, n_kv=2, head_dim=128, window=64,
@@ -228,6 +255,8 @@ WORKLOADS = {
                               ctx_len=8192, t_new=8, seed=5),
     "full_b1_q8_0": Workload("dflash2-27b-draft-q8_0-b1-ctx4096", FULL_Q8_0, batch=1,
                              ctx_len=4096, t_new=8, seed=6),
+    "full_b1_fp8": Workload("dflash2-27b-draft-fp8-b1-ctx4096", FULL_FP8, batch=1,
+                            ctx_len=4096, t_new=8, seed=7),
 }
 
 # the drafter's matrix shapes (name, N out, K in) at M = 8 activation rows
@@ -252,7 +281,7 @@ def linear_shapes(s):
 def make_weights(s, seed, gain_jitter=0.0, code_std=0.02):
     """All drafter weights of shape `s` as a dict (the checker's format).
 
-    Linear weights: ("q4k" or "q8_0", uint8 bytes) or ("bf16", uint16 [rows, cols]).
+    Linear weights: ("q4k", "q8_0" or "fp8", uint8 bytes) or ("bf16", uint16 [rows, cols]).
     Everything else: uint16 bf16 arrays.  embed and lm_head are the same array
     (the draft shares the target's embedding table and output head).  code_std is
     the standard deviation of the two selector codebooks (``selector_codebooks``).
@@ -263,6 +292,8 @@ def make_weights(s, seed, gain_jitter=0.0, code_std=0.02):
             W[name] = ("q4k", q4k_normal(seed, name, rows, cols, 0.02))
         elif s.weight_fmt == "q8_0":
             W[name] = ("q8_0", q8_0_normal(seed, name, rows, cols, 0.02))
+        elif s.weight_fmt == "fp8":
+            W[name] = ("fp8", fp8_normal(seed, name, rows, cols, 0.02))
         else:
             W[name] = ("bf16", normal_bf16(seed, name, (rows, cols), 0.02))
 
