@@ -7,8 +7,9 @@ workload is the pages' 27B-draft shape at batch 1 with a 4096-row context.
 
 --workload full_b16 / full_b64_bf16 measure the pages' batched draft steps instead (16
 sequences with 32768-row contexts and Q4_K weights; 64 with 8192 and bf16 weights); the
-default stays the batch-1 workload.  With --weights q8_0 the drafter's matrices are Q8_0 instead of Q4_K (same shapes,
-same seed recipe).  With --accept sampled the acceptance is dflash_verify_sampled instead (rejection
+default stays the batch-1 workload.  With --weights q8_0 (or fp8) the drafter's matrices
+are Q8_0 (or FP8 E4M3 with a scale per row) instead of Q4_K (same shapes, same seed
+recipe).  With --accept sampled the acceptance is dflash_verify_sampled instead (rejection
 sampling against synthetic fp32 target logits [1][8][248320] resident in HBM, at the
 pages' sampler settings).
 
@@ -115,8 +116,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
-    ap.add_argument("--weights", choices=("q4k", "q8_0"), default="q4k",
-                    help="drafter weight format: Q4_K (the default) or Q8_0")
+    ap.add_argument("--weights", choices=("q4k", "q8_0", "fp8"), default="q4k",
+                    help="drafter weight format: Q4_K (the default), Q8_0 or FP8")
     ap.add_argument("--workload", choices=("full_b1", "full_b16", "full_b64_bf16"),
                     default="full_b1",
                     help="the 27B-draft workload: 1 sequence with a 4096-row context (the "
@@ -139,10 +140,10 @@ def main():
     from block_diffusion_draft_amd import binding, runner, synth
 
     key = args.workload
-    if args.weights == "q8_0":
+    if args.weights != "q4k":
         if key != "full_b1":
-            sys.exit("--weights q8_0 is measured on the batch-1 workload")
-        key = "full_b1_q8_0"
+            sys.exit(f"--weights {args.weights} is measured on the batch-1 workload")
+        key = "full_b1_" + args.weights
     wl = synth.WORKLOADS[key]
     s = wl.shape
     print(f"[bench] preparing {wl.name}", file=sys.stderr, flush=True)
@@ -289,7 +290,9 @@ def step_algorithmic_bytes(wl):
     qd, kd = s.n_q * s.head_dim, s.n_kv * s.head_dim
     lin = s.n_taps * s.hidden * s.hidden + s.n_layers * (
         qd * s.hidden + 2 * kd * s.hidden + s.hidden * qd + 3 * s.ffn * s.hidden)
-    wbytes = {"q4k": lin * 144 // 256, "q8_0": lin * 34 // 32}.get(s.weight_fmt, lin * 2)
+    rows = s.hidden + s.n_layers * (qd + 2 * kd + s.hidden + 2 * s.ffn + s.hidden)
+    wbytes = {"q4k": lin * 144 // 256, "q8_0": lin * 34 // 32,
+              "fp8": lin + 4 * rows}.get(s.weight_fmt, lin * 2)
     small = s.n_layers * (2 * s.hidden + 2 * s.head_dim + 2 * s.n_q * qd) * 2 + 3 * s.hidden * 2
     head = s.vocab * s.hidden * 2
     win = min(s.window, wl.ctx_len + wl.t_new)

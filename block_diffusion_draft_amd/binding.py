@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libdflash.so")
 MAX_LAYERS = 8
 BLOCK = 8
 
-W_Q4K, W_BF16, W_Q8_0 = 0, 1, 2
-WEIGHT_FMT = {"q4k": W_Q4K, "bf16": W_BF16, "q8_0": W_Q8_0}
+W_Q4K, W_BF16, W_Q8_0, W_FP8 = 0, 1, 2, 3
+WEIGHT_FMT = {"q4k": W_Q4K, "bf16": W_BF16, "q8_0": W_Q8_0, "fp8": W_FP8}
 PROBE_NONE, PROBE_LM_HEAD, PROBE_FFN_GATE_UP = 0, 1, 2
 LAYOUT_ROWMAJOR, LAYOUT_TILED = 0, 0x444C4954
 NOALLOC_SCRATCH_BYTES = 32 << 20        # DFLASH_NOALLOC_SCRATCH_BYTES
@@ -118,6 +118,20 @@ def lib():
     L.q8_0_to_tiled.restype = c_int
     L.q8_0_dequantize.argtypes = [c_void_p, c_void_p, ctypes.c_longlong, c_void_p]
     L.q8_0_dequantize.restype = c_int
+    L.fp8_gemm_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    L.fp8_gemm_workspace_bytes.restype = c_size_t
+    L.fp8_gemm.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p,
+                           c_size_t, c_void_p]
+    L.fp8_gemm.restype = c_int
+    L.fp8_gemm_tiled_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    L.fp8_gemm_tiled_workspace_bytes.restype = c_size_t
+    L.fp8_gemm_tiled.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p,
+                                 c_size_t, c_void_p]
+    L.fp8_gemm_tiled.restype = c_int
+    L.fp8_to_tiled.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p]
+    L.fp8_to_tiled.restype = c_int
+    L.fp8_dequantize.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p]
+    L.fp8_dequantize.restype = c_int
     L.dflash_status_str.argtypes = [c_int]
     L.dflash_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -131,6 +145,8 @@ EXPORTS = ["dflash_workspace_bytes", "dflash_draft_step", "dflash_verify_prefix"
            "q4k_gemm_tiled", "q4k_to_tiled", "q4k_dequantize",
            "q8_0_gemm_workspace_bytes", "q8_0_gemm", "q8_0_gemm_tiled_workspace_bytes",
            "q8_0_gemm_tiled", "q8_0_to_tiled", "q8_0_dequantize",
+           "fp8_gemm_workspace_bytes", "fp8_gemm", "fp8_gemm_tiled_workspace_bytes",
+           "fp8_gemm_tiled", "fp8_to_tiled", "fp8_dequantize",
            "dflash_status_str"]
 
 
@@ -179,9 +195,9 @@ class DeviceWeights:
     """Drafter weights resident in device memory, plus the C struct pointing at them.
 
     `W` is the host weight dict of synth.make_weights (linear weights as
-    ("q4k" / "q8_0", row-major block bytes) or ("bf16", uint16 array); the rest uint16
-    arrays).  Q4_K and Q8_0 matrices are regrouped on the device into the library's
-    tiled layouts (q4k_to_tiled, q8_0_to_tiled) after the upload.
+    ("q4k" / "q8_0" / "fp8", row-major bytes) or ("bf16", uint16 array); the rest uint16
+    arrays).  Q4_K, Q8_0 and FP8 matrices are regrouped on the device into the library's
+    tiled layouts (q4k_to_tiled, q8_0_to_tiled, fp8_to_tiled) after the upload.
     """
 
     def __init__(self, shape, W, device="cuda"):
@@ -200,9 +216,10 @@ class DeviceWeights:
                 dt = torch.uint8 if arr.dtype == np.uint8 else torch.int16
                 t = torch.from_numpy(arr.view(np.uint8 if arr.dtype == np.uint8 else np.int16))
                 t = t.to(device, dtype=dt)
-                if fmt in ("q4k", "q8_0"):
+                if fmt in ("q4k", "q8_0", "fp8"):
                     tiled = torch.empty_like(t)
-                    (q4k_to_tiled if fmt == "q4k" else q8_0_to_tiled)(t, tiled, *dims[name])
+                    {"q4k": q4k_to_tiled, "q8_0": q8_0_to_tiled,
+                     "fp8": fp8_to_tiled}[fmt](t, tiled, *dims[name])
                     t = tiled
                 shared[key] = t
             self.tensors[name] = t
@@ -325,6 +342,39 @@ def q8_0_to_tiled(src, dst, N, K):
 
 def q8_0_dequantize(w, out):
     check(lib().q8_0_dequantize(_ptr(w), _ptr(out), out.numel() // 32, _stream()))
+
+
+def fp8_gemm(w, x, y, workspace):
+    M, K = x.shape
+    N = y.shape[1]
+    check(lib().fp8_gemm(_ptr(w), _ptr(x), _ptr(y), M, N, K, _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream()))
+
+
+def fp8_gemm_workspace_bytes(M, N, K):
+    return lib().fp8_gemm_workspace_bytes(M, N, K)
+
+
+def fp8_gemm_tiled(w, x, y, workspace):
+    M, K = x.shape
+    N = y.shape[1]
+    check(lib().fp8_gemm_tiled(_ptr(w), _ptr(x), _ptr(y), M, N, K, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream()))
+
+
+def fp8_gemm_tiled_workspace_bytes(M, N, K):
+    return lib().fp8_gemm_tiled_workspace_bytes(M, N, K)
+
+
+def fp8_to_tiled(src, dst, N, K):
+    """Regroup a row-major FP8 matrix [N][K] (+ row scales; device uint8) into the tiled layout."""
+    check(lib().fp8_to_tiled(_ptr(src), _ptr(dst), N, K, _stream()))
+
+
+def fp8_dequantize(w, out):
+    """out: fp32 [N, K] device tensor; w: the matrix's N K + 4 N bytes."""
+    N, K = out.shape
+    check(lib().fp8_dequantize(_ptr(w), _ptr(out), N, K, _stream()))
 
 
 def q4k_dequantize(w, out):

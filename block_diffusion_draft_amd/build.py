@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdflash.so")
-SOURCES = ["api.hip", "q4k_dequant.hip", "q4k_tiled.hip", "q4k_stream.hip", "q8_0.hip", "gemm_bf16.hip", "gemm_big.hip", "layer_ops.hip", "attention.hip",
+SOURCES = ["api.hip", "q4k_dequant.hip", "q4k_tiled.hip", "q4k_stream.hip", "q8_0.hip", "fp8.hip", "gemm_bf16.hip", "gemm_big.hip", "layer_ops.hip", "attention.hip",
            "topk.hip", "verify.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -21,7 +21,8 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 
 
 # per-file extras: MFMA results in VGPRs (no accumulator-register round trips)
-EXTRA = {"q4k_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"q4k_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src):

@@ -27,12 +27,26 @@ struct Plan {
 };
 
 // fp32 partial sums of one GEMM: [splits][M][N] (Q4_K split-K) or [M][N] (bf16)
-// Which kernel runs a product: the 16-row streaming kernels (Q4_K, Q8_0) where their
-// shape rules allow, else the many-row GEMM; bf16 up to 16 rows on the tiled kernel.
-int big_fmt(int fmt) { return fmt == DFLASH_W_Q4K ? 2 : (fmt == DFLASH_W_Q8_0 ? 1 : 0); }
+// Which kernel runs a product: the 16-row streaming kernels (Q4_K, Q8_0, FP8) where
+// their shape rules allow, else the many-row GEMM; bf16 up to 16 rows on the tiled kernel.
+int big_fmt(int fmt) {
+    return fmt == DFLASH_W_Q4K ? 2 : (fmt == DFLASH_W_Q8_0 ? 1 : (fmt == DFLASH_W_FP8 ? 3 : 0));
+}
+bool quant_fmt(int fmt) {
+    return fmt == DFLASH_W_Q4K || fmt == DFLASH_W_Q8_0 || fmt == DFLASH_W_FP8;
+}
 bool use_stream(int fmt, int M, int N, int K) {
-    return fmt == DFLASH_W_Q4K ? q4k_stream_ok(M, N, K)
-                               : (fmt == DFLASH_W_Q8_0 && q8_stream_ok(M, N, K));
+    switch (fmt) {
+        case DFLASH_W_Q4K: return q4k_stream_ok(M, N, K);
+        case DFLASH_W_Q8_0: return q8_stream_ok(M, N, K);
+        case DFLASH_W_FP8: return f8_stream_ok(M, N, K);
+        default: return false;
+    }
+}
+Q4kStreamPlan stream_plan(int fmt, int M, int N, int K, int pair = 0) {
+    return fmt == DFLASH_W_Q4K ? q4k_stream_plan(M, N, K, pair)
+                               : (fmt == DFLASH_W_Q8_0 ? q8_stream_plan(M, N, K, pair)
+                                                       : f8_stream_plan(M, N, K, pair));
 }
 bool use_big(int fmt, int M, int N, int K) {
     if (fmt != DFLASH_W_BF16 && use_stream(fmt, M, N, K)) return false;
@@ -42,8 +56,7 @@ bool use_big(int fmt, int M, int N, int K) {
 
 size_t gemm_part_bytes(int fmt, int M, int N, int K) {
     if (use_big(fmt, M, N, K)) return big_gemm_plan(big_fmt(fmt), M, N, K).part_bytes;
-    if (fmt == DFLASH_W_Q4K && q4k_stream_ok(M, N, K)) return q4k_stream_plan(M, N, K).part_bytes;
-    if (fmt == DFLASH_W_Q8_0 && q8_stream_ok(M, N, K)) return q8_stream_plan(M, N, K).part_bytes;
+    if (quant_fmt(fmt) && use_stream(fmt, M, N, K)) return stream_plan(fmt, M, N, K).part_bytes;
     return (size_t)M * N * 4;
 }
 
@@ -154,9 +167,7 @@ int check_config(const dflash_config *c) {
     if (c->sel_rank < 32 || c->sel_rank % 32 || c->sel_rank > 4096) return DFLASH_ESHAPE;
     if (c->window < 0) return DFLASH_EINVAL;
     if (c->window > 65536) return DFLASH_ESHAPE;     // attention-merge weights live in LDS
-    if (c->weight_fmt != DFLASH_W_Q4K && c->weight_fmt != DFLASH_W_BF16 &&
-        c->weight_fmt != DFLASH_W_Q8_0)
-        return DFLASH_EINVAL;
+    if (!quant_fmt(c->weight_fmt) && c->weight_fmt != DFLASH_W_BF16) return DFLASH_EINVAL;
     if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return DFLASH_EINVAL;
     return DFLASH_OK;
 }
@@ -198,17 +209,17 @@ int run_big(int wfmt, const void *const *w, const int *seg_end, int nseg, const 
     return p.splits;
 }
 
-// Q4_K / Q8_0 product into partials: the streaming kernels for up to 16 rows, else the
-// many-row GEMM.  Returns the number of splits or a negative status; *pair_left is the
-// row pair the partial still holds (0 once the kernel has added the halves).
+// Q4_K / Q8_0 / FP8 product into partials: the streaming kernels for up to 16 rows, else
+// the many-row GEMM.  Returns the number of splits or a negative status; *pair_left is
+// the row pair the partial still holds (0 once the kernel has added the halves).
 int run_quant(int fmt, const Q4kFusedArgs &a, hipStream_t st, int *pair_left) {
     const int K = a.KB * 256;
     *pair_left = a.pair;
-    const bool q4k = fmt == DFLASH_W_Q4K;
     if (use_stream(fmt, a.M, a.N, K)) {
-        const Q4kStreamPlan p = q4k ? q4k_stream_plan(a.M, a.N, K, a.pair)
-                                    : q8_stream_plan(a.M, a.N, K, a.pair);
-        HIPCHK(q4k ? launch_q4k_stream(a, p, st) : launch_q8_stream(a, p, st));
+        const Q4kStreamPlan p = stream_plan(fmt, a.M, a.N, K, a.pair);
+        HIPCHK(fmt == DFLASH_W_Q4K ? launch_q4k_stream(a, p, st)
+                                   : (fmt == DFLASH_W_Q8_0 ? launch_q8_stream(a, p, st)
+                                                           : launch_f8_stream(a, p, st)));
         if (p.pair_done) *pair_left = 0;
         return p.splits;
     }
@@ -217,12 +228,12 @@ int run_quant(int fmt, const Q4kFusedArgs &a, hipStream_t st, int *pair_left) {
         return run_big(big_fmt(fmt), w, a.seg_end, a.nseg, a.src.A, a.src.lda, a.M, a.N, K,
                        a.part, st, a.pair);
     }
-    return DFLASH_ESHAPE;      // (every valid Q4_K / Q8_0 shape takes one of the two above)
+    return DFLASH_ESHAPE;      // (every valid quantised shape takes one of the two above)
 }
 
 // y = A . W^T over up to 3 weight matrices stacked along N, as fp32 partial sums in
 // the workspace's partial buffer [splits][M][N]: up to 16 rows the streaming Q4_K /
-// Q8_0 kernels (or the tiled MFMA kernel for bf16), more rows the many-row GEMM.  Rows r and
+// Q8_0 / FP8 kernels (or the tiled MFMA kernel for bf16), more rows the many-row GEMM.  Rows r and
 // r + pair (pair > 0) are the (hi, lo) halves of one activation row; *pair_left is
 // the pair the partial still holds (the reduction adds those rows).  Returns the
 // number of splits (> 0) or a negative status.
@@ -236,7 +247,7 @@ int run_gemm(const Ctx &x, const void *const *w, const int *seg_n, int nseg, con
         seg_end[i] = N;
     }
     float *part = x.at<float>(x.p->o_part);
-    if (x.c->weight_fmt == DFLASH_W_Q4K || x.c->weight_fmt == DFLASH_W_Q8_0) {
+    if (quant_fmt(x.c->weight_fmt)) {
         Q4kFusedArgs a;
         for (int i = 0; i < 3; i++) {
             a.w[i] = (const unsigned char *)(i < nseg ? w[i] : w[0]);
@@ -643,10 +654,12 @@ bool qgemm_shape_ok(int M, int N, int K) {
 }
 
 size_t quant_matrix_bytes(int fmt, int N, int K) {
-    return fmt == DFLASH_W_Q4K ? (size_t)N * (K / 256) * 144 : (size_t)N * (K / 32) * Q8_BLOCK_BYTES;
+    if (fmt == DFLASH_W_Q4K) return (size_t)N * (K / 256) * 144;
+    if (fmt == DFLASH_W_Q8_0) return (size_t)N * (K / 32) * Q8_BLOCK_BYTES;
+    return (size_t)N * K + (size_t)N * 4;                  // FP8: codes, then row scales
 }
 
-// y = x . W^T for a tiled Q4_K / Q8_0 matrix: product into partials, split sum to bf16
+// y = x . W^T for a tiled Q4_K / Q8_0 / FP8 matrix: product into partials, split sum to bf16
 int quant_gemm_tiled(int fmt, const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
                      float *part, hipStream_t st) {
     Q4kFusedArgs a;
@@ -699,8 +712,10 @@ int quant_gemm_rowmajor(int fmt, const void *w, const uint16_t *x, uint16_t *y, 
     if (s0 < d0 + ws_bytes && d0 < s0 + wb) return DFLASH_EINVAL;      // W inside the workspace
     if (fmt == DFLASH_W_Q4K)
         HIPCHK(launch_q4k_to_tiled((const unsigned char *)w, tiled, N, K / 256, st));
-    else
+    else if (fmt == DFLASH_W_Q8_0)
         HIPCHK(launch_q8_0_to_tiled((const unsigned char *)w, tiled, N, K / 256, st));
+    else
+        HIPCHK(launch_fp8_to_tiled((const unsigned char *)w, tiled, N, K / 256, st));
     return quant_gemm_tiled(fmt, tiled, x, y, M, N, K, (float *)(tiled + align256(wb)), st);
 }
 
@@ -768,6 +783,48 @@ int q8_0_dequantize(const void *w, float *out, long long n_blocks, void *stream)
     if (!w || !out || n_blocks < 1) return DFLASH_EINVAL;
     if (!aligned16(w) || !aligned16(out)) return DFLASH_EALIGN;
     HIPCHK(launch_q8_0_dequant(w, out, n_blocks, (hipStream_t)stream));
+    return DFLASH_OK;
+}
+
+size_t fp8_gemm_workspace_bytes(int M, int N, int K) {
+    return quant_gemm_rowmajor_ws(DFLASH_W_FP8, M, N, K);
+}
+
+int fp8_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
+             void *workspace, size_t ws_bytes, void *stream) {
+    return quant_gemm_rowmajor(DFLASH_W_FP8, w, x, y, M, N, K, workspace, ws_bytes,
+                               (hipStream_t)stream);
+}
+
+size_t fp8_gemm_tiled_workspace_bytes(int M, int N, int K) {
+    return quant_gemm_tiled_ws(DFLASH_W_FP8, M, N, K);
+}
+
+int fp8_gemm_tiled(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
+                   void *workspace, size_t ws_bytes, void *stream) {
+    const int rc = quant_gemm_check(w, x, y, M, N, K, workspace, ws_bytes,
+                                    quant_gemm_tiled_ws(DFLASH_W_FP8, M, N, K));
+    if (rc != DFLASH_OK) return rc;
+    return quant_gemm_tiled(DFLASH_W_FP8, w, x, y, M, N, K, (float *)workspace, (hipStream_t)stream);
+}
+
+int fp8_to_tiled(const void *src, void *dst, int N, int K, void *stream) {
+    if (!src || !dst) return DFLASH_EINVAL;
+    if (N < 16 || N % 16 || K < 256 || K % 256) return DFLASH_ESHAPE;
+    if (!aligned16(src) || !aligned16(dst)) return DFLASH_EALIGN;
+    const size_t bytes = quant_matrix_bytes(DFLASH_W_FP8, N, K);
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return DFLASH_EINVAL;      // overlap
+    HIPCHK(launch_fp8_to_tiled((const unsigned char *)src, (unsigned char *)dst, N, K / 256,
+                               (hipStream_t)stream));
+    return DFLASH_OK;
+}
+
+int fp8_dequantize(const void *w, float *out, int N, int K, void *stream) {
+    if (!w || !out) return DFLASH_EINVAL;
+    if (N < 1 || K < 1 || K % 4 || (long long)N * K > (1LL << 40)) return DFLASH_ESHAPE;
+    if (!aligned16(w) || !aligned16(out)) return DFLASH_EALIGN;
+    HIPCHK(launch_fp8_dequant(w, out, N, K, (hipStream_t)stream));
     return DFLASH_OK;
 }
 

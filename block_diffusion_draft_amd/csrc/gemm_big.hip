@@ -1,6 +1,6 @@
 // Dense-contraction GEMM for many activation rows (the batched draft steps), gfx950:
 // C[slot][M][N] (fp32) = A[M][K] (bf16) . W[N][K]^T over the slot's share of K, with W
-// in bf16, Q8_0 or Q4_K (tiled layouts of q8_0.hip / q4k_tiled.hip).  The consumers sum
+// in bf16, Q8_0, Q4_K or FP8 (tiled layouts of q8_0.hip / q4k_tiled.hip / fp8.hip).  The consumers sum
 // the slots (reduce kernels), as for every other GEMM of the step.
 //
 // At 100+ rows the drafter's products are MFMA-bound (2 M flops per weight against
@@ -12,7 +12,9 @@
 // multiplied by the same activation operand: hi + lo carries w to 2^-18 of itself,
 // below the fp32 accumulation's own rounding over K of a few thousand.  Where the
 // activations are themselves (hi, lo) pairs (rows >= lo_row, the MLP inputs), the lo
-// rows skip the weights' lo term: that product is within 2^-18 of the pair's sum.
+// rows skip the weights' lo term: that product is within 2^-18 of the pair's sum.  FP8
+// (E4M3) codes are exact in bf16: they enter as a single term, and their row scale
+// multiplies the output column in the epilogue.
 //
 // Workgroup: 8 waves (2 along M x 4 along N), each a 128 x 64 block (BM = 256; 64 x 64
 // for BM = 128) of 32 x 32 MFMA tiles.  The operands sit in LDS in MFMA lane order,
@@ -83,16 +85,31 @@ __device__ __forceinline__ void split8(const float (&q)[8], float s, float t, u3
     }
 }
 
+// FP8 row scale of output column n (clamped into range): the float after the codes of
+// the column's weight segment
+__device__ __forceinline__ float fp8_col_scale(const BigGemmArgs &a, int n) {
+    n = min(n, a.N - 1);
+    int nb;
+    const unsigned char *ws = seg_of(a, n, nb);
+    const int si = (a.nseg > 1 && n >= a.seg_end[0]) + (a.nseg > 2 && n >= a.seg_end[1]);
+    const int rows = (si == 0 ? a.seg_end[0] : (si == 1 ? a.seg_end[1] : a.seg_end[2])) - nb;
+    return reinterpret_cast<const float *>(ws + (size_t)rows * a.K)[n - nb];
+}
+
 // Epilogue: lane l of tile (i, j), register v holds row 8 (v / 4) + 4 (l / 32) + v % 4,
 // column l % 32.  With the row scale, it is computed once per row of the tile into LDS
-// (rinv, free once every wave has left the K loop).
-template <int BM, int FM, int FN = 2>
+// (rinv, free once every wave has left the K loop).  CS: FP8 weights, whose row scale
+// multiplies each output column.
+template <int BM, int FM, int FN = 2, bool CS = false>
 __device__ __forceinline__ void store_tile(const BigGemmArgs &a, const f32x16_t (&acc)[FM][FN],
                                            float *rinv, int m0, int n0, int wm, int wn, int tid,
                                            int slot, bool scale) {
     constexpr int WM = BM / 2, WN = 32 * FN;
     const int lane = tid & 63, hl = lane >> 5, c = lane & 31;
     float *C = a.C + (size_t)slot * a.M * a.ldc;
+    float cs[FN];
+#pragma unroll
+    for (int j = 0; j < FN; j++) cs[j] = CS ? fp8_col_scale(a, n0 + wn * WN + 32 * j + c) : 1.f;
     if (scale) {
         __syncthreads();
         for (int r = tid; r < BM; r += NTH) rinv[r] = row_inv(a.rs, min(m0 + r, a.M - 1));
@@ -108,11 +125,12 @@ __device__ __forceinline__ void store_tile(const BigGemmArgs &a, const f32x16_t 
 #pragma unroll
             for (int j = 0; j < FN; j++) {
                 const int n = n0 + wn * WN + 32 * j + c;
-                if (n < a.N) C[(size_t)(m0 + r) * a.ldc + n] = acc[i][j][v] * ri;
+                if (n < a.N) C[(size_t)(m0 + r) * a.ldc + n] = CS ? acc[i][j][v] * cs[j] * ri
+                                                                  : acc[i][j][v] * ri;
             }
         }
     }
-    if (scale && a.rstat) {
+    if (!CS && scale && a.rstat) {
         // softmax statistics of the tile's columns per row (one column run per tile).
         // Each wave stages a 32-row block of its values in LDS, lane (row, half) = (l % 32,
         // l / 32) reduces half a row's WN columns serially (one shuffle joins the halves);
@@ -250,7 +268,7 @@ struct Pieces {
     }
 };
 
-// ---- Q8_0 / Q4_K weight tasks.  Task e = tid + NTH i (i < 2) of a thread: 16-column
+// ---- Q8_0 / Q4_K / FP8 weight tasks.  Task e = tid + NTH i (i < 2) of a thread: 16-column
 // group cg = e / 64 of the tile, lane ln = e % 64 of the MFMA fragment (column ln % 16,
 // k group ln / 16).  wbase: the column group's first tiled unit.
 template <int WF>
@@ -264,20 +282,30 @@ __device__ __forceinline__ void wq_setup(const BigGemmArgs &a, int n0, int tid,
         int nb;
         const unsigned char *ws = seg_of(a, wok[i] ? n : a.N - 1, nb);
         const int nn = (wok[i] ? n : a.N - 1) - nb;
-        wbase[i] = ws + (size_t)(nn >> 4) * (a.K / 256) * (WF == 1 ? Q8_UNIT_BYTES : Q4K_UNIT_BYTES);
+        wbase[i] = ws + (size_t)(nn >> 4) * (a.K / 256) *
+                            (WF == 1 ? Q8_UNIT_BYTES : (WF == 2 ? Q4K_UNIT_BYTES : FP8_UNIT_BYTES));
     }
 }
 
 // raw bytes of the 32-deep stage st (K [32 st, 32 st + 32)): Q8_0: 8 bytes of block st
 // of the lane's slot (k group ln / 16) and the block's fp16 scale; Q4_K: the 8 bytes of
 // chunk c = (st % 8) / 2 of the lane's slot (sub-block st % 8 is their low or high
-// nibbles) and the column's 16-byte header.  Two loads per task, four per thread.
+// nibbles) and the column's 16-byte header; FP8: the 8 codes of k-step st % 8 of the
+// lane's slot.  Two loads per task, four per thread (FP8: one and two).
+template <int WF>
+constexpr int wq_loads() { return WF == 3 ? 2 : 4; }
+
 template <int WF>
 __device__ __forceinline__ void wq_load(WRaw &rw, const unsigned char *const (&wbase)[2], int tid, int st) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int ln = (tid + NTH * i) & 63;
-        if (WF == 1) {
+        if (WF == 3) {
+            const int g = st >> 3, ks = st & 7;
+            const unsigned char *unit = wbase[i] + (size_t)g * FP8_UNIT_BYTES;
+            const u32x2_t q = *reinterpret_cast<const u32x2_t *>(unit + 1024 * (ks >> 1) + 16 * ln + 8 * (ks & 1));
+            rw.v[2 * i] = (u32x4_t){q.x, q.y, 0u, 0u};
+        } else if (WF == 1) {
             const int g = st >> 3, blk = st & 7, pr = blk >> 1;
             const unsigned char *unit = wbase[i] + (size_t)g * Q8_UNIT_BYTES;
             const u32x2_t q = *reinterpret_cast<const u32x2_t *>(unit + 256 + 1024 * pr + 16 * ln + 8 * (blk & 1));
@@ -294,9 +322,16 @@ __device__ __forceinline__ void wq_load(WRaw &rw, const unsigned char *const (&w
     }
 }
 
+// two E4M3 codes (bytes 0, 1 or 2, 3 of v) -> their bf16 values (exact), first in the low half
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t v) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, HI));
+}
+
 // decode a stage's raw bytes into the (hi, lo) MFMA operands of the W tile Bb
 // ([2 (hi, lo)][2 ks][8][64], slot swz): task (column, k group kg) fills entry kg of its
-// column's fragment: ks = kg / 2, lane (column % 32) + 32 (kg % 2)
+// column's fragment: ks = kg / 2, lane (column % 32) + 32 (kg % 2).  FP8: the codes'
+// bf16 values only (no lo term)
 template <int WF>
 __device__ __forceinline__ void wq_store(u32x4_t *Bb, const WRaw &rw, const bool (&wok)[2], int tid) {
 #pragma unroll
@@ -306,7 +341,10 @@ __device__ __forceinline__ void wq_store(u32x4_t *Bb, const WRaw &rw, const bool
         if (wok[i]) {
             const u32x4_t q = rw.v[2 * i], h = rw.v[2 * i + 1];
             float v[8];
-            if (WF == 1) {
+            if (WF == 3) {
+                oh = (u32x4_t){e4m3x2_bf16<false>(q.x), e4m3x2_bf16<true>(q.x),
+                               e4m3x2_bf16<false>(q.y), e4m3x2_bf16<true>(q.y)};
+            } else if (WF == 1) {
 #pragma unroll
                 for (int b = 0; b < 8; b++)
                     v[b] = (float)(int8_t)((b < 4 ? q.x : q.y) >> (8 * (b & 3)));
@@ -338,7 +376,7 @@ __device__ __forceinline__ void wq_store(u32x4_t *Bb, const WRaw &rw, const bool
         const int li = (col & 31) + 32 * (kg & 1);
         const int at = ((kg >> 1) * 8 + (col >> 5)) * 64 + swz(li, kg);
         Bb[at] = oh;
-        Bb[1024 + at] = ol;
+        if (WF != 3) Bb[1024 + at] = ol;
     }
 }
 
@@ -451,7 +489,7 @@ __global__ __launch_bounds__(NTH) void k_gemm_big_dma(BigGemmArgs a, BigSched sc
     }
 }
 
-// Q8_0 / Q4_K weights, 32-deep K stages: A global -> LDS by direct loads through a ring
+// Q8_0 / Q4_K / FP8 weights, 32-deep K stages: A global -> LDS by direct loads through a ring
 // of QNS stages (the bf16 path's 64-byte row pieces and chunk swizzle), the raw weight
 // bytes of a stage loaded into registers two stages ahead (two register sets,
 // alternating) and decoded into the double-buffered (hi, lo) W tile after the current
@@ -465,7 +503,7 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
     constexpr int RG = BM / 32, WM = BM / 2, FM = WM / 32;
     constexpr int PA = 2 * RG / 8;                    // A load instructions per wave and stage
     constexpr int AST = RG * 128;                     // entries of one A stage
-    constexpr int PWQ = 4;                            // weight loads per thread and stage
+    constexpr int PWQ = wq_loads<WF>();               // weight loads per thread and stage
     u32x4_t *As = lds;                                // [QNS][RG][128]
     u32x4_t *Bs = lds + QNS * AST;                    // [2][2 (hi, lo)][2 ks][8][64]
 
@@ -513,7 +551,7 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 bh[j] = Bb[(ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
-                bl[j] = Bb[1024 + (ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
+                if (WF != 3) bl[j] = Bb[1024 + (ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
             }
 #pragma unroll
             for (int i = 0; i < FM; i++) {
@@ -521,7 +559,7 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
 #pragma unroll
                 for (int j = 0; j < 2; j++) {
                     acc[i][j] = mfma32x32x16(af, bh[j], acc[i][j]);
-                    if (!lo_rows) acc[i][j] = mfma32x32x16(af, bl[j], acc[i][j]);
+                    if (WF != 3 && !lo_rows) acc[i][j] = mfma32x32x16(af, bl[j], acc[i][j]);
                 }
             }
         }
@@ -565,7 +603,7 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
     if (st < s1) body(st, rb, ra);
     __builtin_amdgcn_s_waitcnt(0xF70);      // no load may land after the piece ends
 
-    store_tile<BM, FM>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot, scale);
+    store_tile<BM, FM, 2, WF == 3>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot, scale);
 }
 
 template <int WF, int BM>
@@ -677,7 +715,7 @@ bool big_gemm_ok(int wf, int M, int N, int K) {
 }
 
 hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream_t st) {
-    if (!big_gemm_ok(a.wfmt, a.M, a.N, a.K) || a.wfmt < 0 || a.wfmt > 2) return hipErrorInvalidValue;
+    if (!big_gemm_ok(a.wfmt, a.M, a.N, a.K) || a.wfmt < 0 || a.wfmt > 3) return hipErrorInvalidValue;
     if (p.wgs && (p.wgs % 8 || a.ldc % 4)) return hipErrorInvalidValue;
     // operand rows are fetched as 16-byte pieces straight into LDS
     if (reinterpret_cast<uintptr_t>(a.A) % 16 || a.lda % 8) return hipErrorInvalidValue;
@@ -694,12 +732,15 @@ hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream
     } else if (a.wfmt == 1) {
         fn = bi ? (const void *)k_gemm_big_q<1, 256> : (const void *)k_gemm_big_q<1, 128>;
         lb = q_lds_bytes(p.bm);
+    } else if (a.wfmt == 3) {
+        fn = bi ? (const void *)k_gemm_big_q<3, 256> : (const void *)k_gemm_big_q<3, 128>;
+        lb = q_lds_bytes(p.bm);
     } else {
         fn = bi ? (const void *)k_gemm_big_q<2, 256> : (const void *)k_gemm_big_q<2, 128>;
         lb = q_lds_bytes(p.bm);
     }
     // (the LDS limit is raised once per device and kernel)
-    static bool attr_set[64][3][2][2] = {};
+    static bool attr_set[64][4][2][2] = {};
     const int wide = p.bn == 512;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;

@@ -212,16 +212,33 @@ Q4kStreamPlan q8_stream_plan(int M, int N, int K, int pair = 0, int target_waves
                              int wpg = 0);
 hipError_t launch_q8_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st);
 
+// ---------------------------------------------------------------- FP8 (E4M3)
+// Row-major FP8 matrix: N K E4M3 codes (row n at n K), then N fp32 row scales; tiled
+// layout: unit (t, g) of 4096 bytes at (t K/256 + g) 4096 holds per pair p < 4 the
+// 16-byte slots 16 h + r: codes 64 p + 8 h .. + 7 of row 16 t + r's K-group g, then
+// codes 64 p + 32 + 8 h .. + 7; the scales follow the codes unchanged.
+constexpr int FP8_UNIT_BYTES = 4096;
+hipError_t launch_fp8_dequant(const void *w, float *out, int N, int K, hipStream_t st);
+hipError_t launch_fp8_to_tiled(const unsigned char *src, unsigned char *dst, int N, int G,
+                               hipStream_t st);
+// streaming GEMM for M <= 16 rows, K a multiple of 1024, the plan fields and partial
+// layout of the Q4_K streaming kernel (a.KB = K / 256); the row scales are applied
+bool f8_stream_ok(int M, int N, int K);
+Q4kStreamPlan f8_stream_plan(int M, int N, int K, int pair = 0, int target_waves = 2048,
+                             int wpg = 0);
+hipError_t launch_f8_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st);
+
 // ---------------------------------------------------------------- many-row GEMM
 // C[split][M][N] fp32 = A[M][K] bf16 . W^T over the split's share of K; W stacked along
-// N from up to 3 matrices in bf16 ([N][K]), Q8_0 or Q4_K (tiled layouts), decoded to
-// bf16 (hi, lo) MFMA operand pairs per 256 x 256 tile.  One split: rows scaled by
-// row_inv(rs, r).
+// N from up to 3 matrices in bf16 ([N][K]), Q8_0, Q4_K or FP8 (tiled layouts), decoded
+// to bf16 MFMA operands per 256 x 256 tile ((hi, lo) pairs for Q8_0 and Q4_K; FP8 codes
+// are exact in bf16 and their row scale multiplies the output column).  One split: rows
+// scaled by row_inv(rs, r).
 struct BigGemmArgs {
     const void *w[3];
     int seg_end[3];
     int nseg;
-    int wfmt;                    // 0 bf16, 1 Q8_0, 2 Q4_K
+    int wfmt;                    // 0 bf16, 1 Q8_0, 2 Q4_K, 3 FP8
     const uint16_t *A;
     int lda;
     int M, N, K;

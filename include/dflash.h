@@ -27,6 +27,10 @@
  *                        quantised draft file: Mindket kit page "Qwen3.8-27B-DFlash2-
  *                        GGUF by z-lab", draft-file table); q8_0_to_tiled and
  *                        q8_0_dequantize as for Q4_K.
+ *   fp8_gemm             the same product with W as FP8 (E4M3) codes and one scale
+ *                        per row (aiqre model page "Qwen3.8-27B-DFlash2", "Memory":
+ *                        an fp8 format at one byte per parameter); fp8_to_tiled and
+ *                        fp8_dequantize as for Q4_K.
  *   q4k_to_tiled         regroups a row-major Q4_K matrix into the tiled device
  *                        layout every Q4_K entry point above reads (done once, when
  *                        the weights are loaded).
@@ -78,15 +82,15 @@ typedef enum {
 } dflash_status;
 
 /* Layout tag of the quantised linear weights in dflash_weights.linear_layout.  The
- * draft step reads Q4_K and Q8_0 matrices only in the tiled layouts written by
- * q4k_to_tiled / q8_0_to_tiled; the caller states that it converted them by setting
+ * draft step reads Q4_K, Q8_0 and FP8 matrices only in the tiled layouts written by
+ * q4k_to_tiled / q8_0_to_tiled / fp8_to_tiled; the caller states that it converted them by setting
  * the tag to DFLASH_LAYOUT_TILED (a zero-initialised struct says row-major, and a
  * step with quantised weights then returns DFLASH_ELAYOUT instead of reading
  * row-major bytes as tiled ones).  bf16 weights are row-major and ignore the tag. */
 #define DFLASH_LAYOUT_ROWMAJOR 0u
 #define DFLASH_LAYOUT_TILED 0x444C4954u     /* "TILD" */
 
-typedef enum { DFLASH_W_Q4K = 0, DFLASH_W_BF16 = 1, DFLASH_W_Q8_0 = 2 } dflash_weight_fmt;
+typedef enum { DFLASH_W_Q4K = 0, DFLASH_W_BF16 = 1, DFLASH_W_Q8_0 = 2, DFLASH_W_FP8 = 3 } dflash_weight_fmt;
 
 /* Drafter shape.  The 27B draft: 5 layers, hidden 5120, FFN 17408, 32 query and
  * 8 KV heads of 128, window 2048, vocab 248320, 5 taps, block 8, top 16, rank
@@ -106,8 +110,8 @@ typedef struct {
 } dflash_config;
 
 /* Linear weights are [out][in] (y = x . W^T).  bf16: row-major, `in` values per
- * row.  Q4_K / Q8_0: the tiled layouts written by q4k_to_tiled / q8_0_to_tiled (the
- * row-major matrix regrouped; same size), declared by linear_layout. */
+ * row.  Q4_K / Q8_0 / FP8: the tiled layouts written by q4k_to_tiled / q8_0_to_tiled /
+ * fp8_to_tiled (the row-major matrix regrouped; same size), declared by linear_layout. */
 typedef struct {
     const void *wq, *wk, *wv, *wo, *wg, *wu, *wd;
     const uint16_t *in_norm, *post_norm;   /* [hidden] */
@@ -125,7 +129,7 @@ typedef struct {
     const uint16_t *mask_emb;              /* [hidden] embedding of the mask positions */
     const uint16_t *sel_proj;              /* [sel_rank][hidden] selector projection (not read) */
     const uint16_t *code_a, *code_b;       /* [vocab][sel_rank] selector codebooks */
-    uint32_t linear_layout;                /* DFLASH_LAYOUT_TILED (required for Q4_K / Q8_0) */
+    uint32_t linear_layout;                /* DFLASH_LAYOUT_TILED (required for Q4_K / Q8_0 / FP8) */
 } dflash_weights;
 
 /* Optional live timing of one kernel inside dflash_draft_step: HIP events
@@ -339,6 +343,50 @@ int q8_0_gemm_tiled(const void *w_tiled, const uint16_t *x, uint16_t *y, int M, 
 
 /* Decode n_blocks consecutive row-major Q8_0 blocks to fp32 (32 values each, exact). */
 int q8_0_dequantize(const void *w, float *out, long long n_blocks, void *stream);
+
+/*
+ * FP8 (aiqre model page "Qwen3.8-27B-DFlash2", "Memory": besides bf16 and int4 the
+ * drafter's weights come in an fp8 format at one byte per parameter, 1.8 GiB; the page
+ * names no encoding).  Read as OCP FP8 E4M3: sign, 4 exponent bits of bias 7, 3 mantissa
+ * bits, no infinities, codes 0x7F / 0xFF NaN, largest finite 448; one fp32 scale per
+ * output row.  A row-major matrix [N][K] is its N K codes in row order (row n at byte
+ * n K), then N little-endian fp32 scales at byte N K: w[n][k] = s[n] e4m3(code[n][k]).
+ * With weight_fmt DFLASH_W_FP8 the draft step's fc, q/k/v/o and MLP matrices are FP8
+ * in the tiled layout below.  Every E4M3 value is exact in bf16, so the GEMMs multiply
+ * the codes' values exactly and apply the row scale to the fp32 sum.
+ *
+ * fp8_to_tiled: src row-major FP8 [N][K] -> dst (same size, N K + 4 N bytes): for every
+ * 16-row tile t and 256-wide K-group g one 4096-byte unit at (t K/256 + g) 4096:
+ *   bytes 1024 p + 16 (16 h + r) .. + 15 (p, h < 4, r < 16): codes 64 p + 8 h .. + 7 of
+ *   row 16 t + r's K-group g, then its codes 64 p + 32 + 8 h .. + 7;
+ * then the N scales at byte N K, unchanged.  Every byte is copied, none changed.
+ * N % 16 == 0, K % 256 == 0, both > 0; device pointers, 16-byte aligned, not overlapping.
+ */
+int fp8_to_tiled(const void *src, void *dst, int N, int K, void *stream);
+
+/* Workspace bytes fp8_gemm needs for an M x N x K product (the tiled copy of W plus
+ * the split-K partial sums); 0 if the shape is not supported. */
+size_t fp8_gemm_workspace_bytes(int M, int N, int K);
+
+/*
+ * y[M][N] (bf16) = x[M][K] (bf16) . W^T, W [N][K] in row-major FP8 (see above), fp32
+ * accumulation.  The call regroups W into the tiled layout inside its workspace and
+ * runs fp8_gemm_tiled.  K % 256 == 0, N % 16 == 0, 1 <= M <= 4096.  w, x, y and
+ * workspace 16-byte aligned.  A NaN code gives NaN outputs in its row's column.
+ */
+int fp8_gemm(const void *w, const uint16_t *x, uint16_t *y, int M, int N, int K,
+             void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes fp8_gemm_tiled needs for an M x N x K product; 0 if unsupported. */
+size_t fp8_gemm_tiled_workspace_bytes(int M, int N, int K);
+
+/* The product of fp8_gemm with W in the tiled layout of fp8_to_tiled. */
+int fp8_gemm_tiled(const void *w_tiled, const uint16_t *x, uint16_t *y, int M, int N, int K,
+                   void *workspace, size_t ws_bytes, void *stream);
+
+/* Decode a row-major FP8 matrix [N][K] to fp32: out[n K + k] = s[n] e4m3(code), the exact
+ * product rounded once to fp32.  N, K >= 1, K % 4 == 0; 16-byte aligned pointers. */
+int fp8_dequantize(const void *w, float *out, int N, int K, void *stream);
 
 /* Decode n_blocks consecutive row-major Q4_K super-blocks to fp32 (256 values each). */
 int q4k_dequantize(const void *w, float *out, long long n_blocks, void *stream);

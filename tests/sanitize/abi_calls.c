@@ -121,6 +121,12 @@ int main(int argc, char **argv) {
     EXPECT(q8_0_to_tiled(P(FAKE), P(FAKE + (1ul << 30)), 24, 256, NULL), DFLASH_ESHAPE);
     EXPECT(q4k_dequantize(P(FAKE), P(FAKE), 0, NULL), DFLASH_EINVAL);
     EXPECT(q8_0_dequantize(P(FAKE + 2), P(FAKE), 1, NULL), DFLASH_EALIGN);
+    EXPECT(fp8_gemm_workspace_bytes(8, 5120, 100), 0);
+    EXPECT(fp8_gemm(P(FAKE), P(FAKE), P(FAKE), 8, 5120, 5120, P(FAKE), 1ull << 40, NULL), DFLASH_EINVAL);
+    EXPECT(fp8_gemm_tiled(P(FAKE), P(FAKE), P(FAKE), 8, 5121, 5120, P(FAKE), 1ull << 40, NULL),
+           DFLASH_ESHAPE);
+    EXPECT(fp8_to_tiled(P(FAKE), P(FAKE + 4096), 16, 256, NULL), DFLASH_EINVAL);
+    EXPECT(fp8_dequantize(P(FAKE), P(FAKE), 4, 250, NULL), DFLASH_ESHAPE);
 
     if (no_gpu) {
         /* valid on the host: the first HIP call fails */

@@ -27,6 +27,8 @@ def test_header_declares_the_boundary():
               "q4k_gemm_tiled", "q4k_gemm_tiled_workspace_bytes",
               "q8_0_gemm", "q8_0_gemm_workspace_bytes", "q8_0_gemm_tiled",
               "q8_0_gemm_tiled_workspace_bytes", "q8_0_to_tiled", "q8_0_dequantize",
+              "fp8_gemm", "fp8_gemm_workspace_bytes", "fp8_gemm_tiled",
+              "fp8_gemm_tiled_workspace_bytes", "fp8_to_tiled", "fp8_dequantize",
               "dflash_status_str"):
         assert n in names
     assert sorted(binding.EXPORTS) == names
@@ -108,6 +110,8 @@ def test_draft_step_rejects_bad_arguments_before_launch():
     assert call_step(tiny_cfg(sel_rank=48), w) == -2
     assert call_step(tiny_cfg(weight_fmt=7), w) == -1
     assert L_ok(tiny_cfg(weight_fmt=2))                      # Q8_0 is a supported format
+    assert L_ok(tiny_cfg(weight_fmt=3))                      # and FP8
+    assert call_step(tiny_cfg(weight_fmt=4), w) == -1
     assert call_step(cfg, w, taps=FAKE + 2) == -3           # EALIGN
     assert call_step(cfg, w, ws=None) == -4                 # EWORKSPACE
     assert call_step(cfg, w, ws_bytes=16) == -4
@@ -136,7 +140,7 @@ def test_noalloc_step_checks_arguments_and_scratch_size_before_launch():
 def test_draft_step_requires_the_tiled_layout_tag():
     """Quantised matrices are read in the tiled layout only; a weights struct that does
     not declare it (a zero-initialised tag says row-major) is refused before launch."""
-    for fmt in (binding.W_Q4K, binding.W_Q8_0):
+    for fmt in (binding.W_Q4K, binding.W_Q8_0, binding.W_FP8):
         cfg = tiny_cfg(weight_fmt=fmt)
         w = fake_weights(cfg)
         w.linear_layout = binding.LAYOUT_ROWMAJOR
@@ -202,6 +206,34 @@ def test_q8_0_entries_reject_bad_arguments():
     assert L.q8_0_to_tiled(FAKE, FAKE + (1 << 30), 16, 288, None) == -2
     assert L.q8_0_to_tiled(FAKE + 8, FAKE + (1 << 30), 16, 256, None) == -3
     assert L.q8_0_to_tiled(FAKE, FAKE + 1024, 16, 256, None) == -1   # overlapping buffers
+
+
+def test_fp8_entries_reject_bad_arguments():
+    L = binding.lib()
+    assert L.fp8_gemm(FAKE, FAKE, FAKE, 8, 5120, 5000, FAKE, 1 << 40, None) == -2
+    assert L.fp8_gemm(FAKE, FAKE, FAKE, 8, 5121, 5120, FAKE, 1 << 40, None) == -2
+    assert L.fp8_gemm(FAKE, FAKE, FAKE, 0, 5120, 5120, FAKE, 1 << 40, None) == -2
+    assert L.fp8_gemm(FAKE, FAKE, FAKE, 4097, 5120, 5120, FAKE, 1 << 40, None) == -2
+    assert L.fp8_gemm(FAKE + 4, FAKE, FAKE, 8, 5120, 5120, FAKE, 1 << 40, None) == -3
+    assert L.fp8_gemm(FAKE, FAKE, FAKE, 8, 5120, 5120, FAKE, 16, None) == -4
+    assert L.fp8_gemm(None, FAKE, FAKE, 8, 5120, 5120, FAKE, 1 << 40, None) == -1
+    assert L.fp8_gemm(FAKE, FAKE, FAKE, 8, 5120, 5120, FAKE, 1 << 40, None) == -1  # W in workspace
+    # the row-major call holds the tiled copy (codes and row scales) before the partials
+    assert L.fp8_gemm_workspace_bytes(8, 5120, 25600) >= \
+        L.fp8_gemm_tiled_workspace_bytes(8, 5120, 25600) + 5120 * 25600 + 5120 * 4
+    assert L.fp8_gemm_workspace_bytes(300, 5120, 1280) >= 300 * 5120 * 4     # many-row GEMM
+    assert L.fp8_gemm_workspace_bytes(8, 5120, 100) == 0
+    assert L.fp8_gemm_tiled(FAKE, FAKE, FAKE, 8, 5121, 5120, FAKE, 1 << 40, None) == -2
+    assert L.fp8_gemm_tiled(FAKE, FAKE, FAKE, 8, 5120, 5120, FAKE, 16, None) == -4
+    assert L.fp8_dequantize(None, FAKE, 4, 256, None) == -1
+    assert L.fp8_dequantize(FAKE, FAKE, 0, 256, None) == -2
+    assert L.fp8_dequantize(FAKE, FAKE, 4, 250, None) == -2
+    assert L.fp8_dequantize(FAKE + 2, FAKE, 4, 256, None) == -3
+    assert L.fp8_to_tiled(None, FAKE, 16, 256, None) == -1
+    assert L.fp8_to_tiled(FAKE, FAKE + (1 << 30), 24, 256, None) == -2
+    assert L.fp8_to_tiled(FAKE, FAKE + (1 << 30), 16, 288, None) == -2
+    assert L.fp8_to_tiled(FAKE + 8, FAKE + (1 << 30), 16, 256, None) == -3
+    assert L.fp8_to_tiled(FAKE, FAKE + 4096, 16, 256, None) == -1   # overlapping (4160 bytes)
 
 
 def call_sampled(draft=FAKE, logits=FAKE, u=FAKE, batch=2, n=7, vocab=4096, T=1.0, k=20, p=0.95,
