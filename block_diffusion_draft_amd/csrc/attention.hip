@@ -172,9 +172,9 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
             float mx = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 8; i++) mx = fmaxf(mx, sv[i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 1, WAVE));
-            mx = fmaxf(mx, __shfl_xor(mx, 2, WAVE));
-            mx = fmaxf(mx, __shfl_xor(mx, 4, WAVE));
+            mx = fmaxf(mx, xor_lane<1>(mx));
+            mx = fmaxf(mx, xor_lane<2>(mx));
+            mx = fmaxf(mx, xor_lane<4>(mx));
             const float m_old = m_run[row];
             const float m_new = fmaxf(m_old, mx);
             float ls = 0.f;
@@ -189,9 +189,9 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
                 ls += bf16_to_f32(b1);
             }
             *reinterpret_cast<u32x4_t *>(&Ps[row * (KT + 8) + part * 8]) = (u32x4_t){pw[0], pw[1], pw[2], pw[3]};
-            ls += __shfl_xor(ls, 1, WAVE);
-            ls += __shfl_xor(ls, 2, WAVE);
-            ls += __shfl_xor(ls, 4, WAVE);
+            ls += xor_lane<1>(ls);
+            ls += xor_lane<2>(ls);
+            ls += xor_lane<4>(ls);
             if (part == 0) {
                 const float al = m_old == -INFINITY ? 0.f : expf(m_old - m_new);
                 alpha[row] = al;

@@ -46,15 +46,58 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t 
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// The value of lane (lane ^ J) of the wave, J a power of two below 64.  J < 16 stays in
+// the VALU (DPP: quad permutes for 1 and 2; for 4 and 8 the row shifts by J up and down,
+// chosen by the lane's bit J), 16 is a ds_swizzle (xor within 32 lanes), 32 a
+// ds_bpermute: the short distances of a butterfly avoid the LDS crossbar's latency.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+    const int x = (int)v;
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    } else if constexpr (J == 4 || J == 8) {
+        const int up = __builtin_amdgcn_update_dpp(x, x, 0x100 + J, 0xF, 0xF, false);  // row_shl: lane + J
+        const int dn = __builtin_amdgcn_update_dpp(x, x, 0x110 + J, 0xF, 0xF, false);  // row_shr: lane - J
+        return (uint32_t)((__lane_id() & J) ? dn : up);
+    } else if constexpr (J == 16) {
+        return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x401F);   // and 31, xor 16
+    } else {
+        static_assert(J == 32, "lane distance");
+        return (uint32_t)__shfl_xor(x, 32, WAVE);
+    }
+}
+
+template <int J>
+__device__ __forceinline__ float xor_lane(float v) {
+    return __uint_as_float(xor_lane<J>(__float_as_uint(v)));
+}
+
+// xor_lane for a distance known after unrolling (the switch folds away)
+template <class T>
+__device__ __forceinline__ T xor_lane_n(T v, int j) {
+    switch (j) {
+        case 1: return xor_lane<1>(v);
+        case 2: return xor_lane<2>(v);
+        case 4: return xor_lane<4>(v);
+        case 8: return xor_lane<8>(v);
+        case 16: return xor_lane<16>(v);
+        default: return xor_lane<32>(v);
+    }
+}
+
+// butterfly reductions over the wave (distances 32, 16, .., 1: every lane ends with the
+// same value, summed in the same order in every lane)
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    for (int o = 32; o > 0; o >>= 1) v += xor_lane_n(v, o);
     return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, xor_lane_n(v, o));
     return v;
 }
 

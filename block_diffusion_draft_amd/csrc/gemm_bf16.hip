@@ -366,7 +366,7 @@ __global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a, int tiles_p
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1)
 #pragma unroll
-                for (int m = 0; m < 8; m++) bm[m] = fmaxf(bm[m], __shfl_xor(bm[m], o, WAVE));
+                for (int m = 0; m < 8; m++) bm[m] = fmaxf(bm[m], xor_lane_n(bm[m], o));
 #pragma unroll
             for (int m = 0; m < 8; m++) {
                 bs[m] = 0.f;
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a, int tiles_p
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1)
 #pragma unroll
-                for (int m = 0; m < 8; m++) bs[m] += __shfl_xor(bs[m], o, WAVE);
+                for (int m = 0; m < 8; m++) bs[m] += xor_lane_n(bs[m], o);
             // merge with the earlier batches of the run (a row's batch max is finite when
             // the row exists: a batch has a column)
 #pragma unroll

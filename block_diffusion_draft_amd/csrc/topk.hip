@@ -54,11 +54,17 @@ __device__ __forceinline__ bool take(float v, int i, float bv, int bi) {
 __device__ __forceinline__ void wave_best(float &v, int &i) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(v, o, WAVE);
-        const int oi = __shfl_xor(i, o, WAVE);
+        const float ov = xor_lane_n(v, o);
+        const int oi = (int)xor_lane_n((uint32_t)i, o);
         if (take(ov, oi, v, i)) { v = ov; i = oi; }
     }
 }
+
+__device__ __forceinline__ unsigned long long xor_lane_key(unsigned long long k, int j) {
+    const uint32_t lo = xor_lane_n((uint32_t)k, j), hi = xor_lane_n((uint32_t)(k >> 32), j);
+    return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ float xor_lane_key(float k, int j) { return xor_lane_n(k, j); }
 
 // (value desc, id asc) as one unsigned 64-bit key: larger key = better candidate
 __device__ __forceinline__ unsigned long long cand_key(float v, int id) {
@@ -82,7 +88,7 @@ __device__ __forceinline__ Key wave_sort_desc(Key x) {
     for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
-            const Key o = __shfl_xor(x, j, WAVE);
+            const Key o = xor_lane_key(x, j);
             const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
             x = keep_max ? (x > o ? x : o) : (x < o ? x : o);
         }
@@ -541,14 +547,18 @@ __global__ __launch_bounds__(64 * PATH_WAVES) void k_select_path(
         for (int t = 0; t + 1 < P; t++) {
             if (j < K) delta[t & 1][j] = dcur;
             __builtin_amdgcn_wave_barrier();
-            float best = -INFINITY;
-            int bi = 0;
             if (j < K) {
-                best = delta[t & 1][0] + Tm[t][0][j];
-                for (int i = 1; i < K; i++) {
-                    const float v = delta[t & 1][i] + Tm[t][i][j];
-                    if (v > best) { best = v; bi = i; }
-                }
+                // every predecessor's score read first (-inf past K), then the running
+                // best in index order: ties keep the lowest index
+                float sc[MAXK];
+#pragma unroll
+                for (int i = 0; i < MAXK; i++)
+                    sc[i] = i < K ? delta[t & 1][i] + Tm[t][i][j] : -INFINITY;
+                float best = sc[0];
+                int bi = 0;
+#pragma unroll
+                for (int i = 1; i < MAXK; i++)
+                    if (sc[i] > best) { best = sc[i]; bi = i; }
                 psi[t + 1][j] = bi;
                 dcur = lp[t + 1][j] + best;
             }
@@ -558,9 +568,13 @@ __global__ __launch_bounds__(64 * PATH_WAVES) void k_select_path(
         __builtin_amdgcn_wave_barrier();
         if (lane == 0) {
             const int fin = (P - 1) & 1;
+            float dv[MAXK];
+#pragma unroll
+            for (int i = 0; i < MAXK; i++) dv[i] = i < K ? delta[fin][i] : -INFINITY;
             int jj = 0;
-            for (int i = 1; i < K; i++)
-                if (delta[fin][i] > delta[fin][jj]) jj = i;
+#pragma unroll
+            for (int i = 1; i < MAXK; i++)
+                if (dv[i] > dv[jj]) jj = i;
             for (int t = P - 1; t >= 0; t--) {
                 draft[(size_t)b * P + t] = ids[t][jj];
                 if (t > 0) jj = psi[t][jj];
