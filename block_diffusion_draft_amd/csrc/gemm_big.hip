@@ -551,7 +551,7 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 bh[j] = Bb[(ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
-                if (WF != 3) bl[j] = Bb[1024 + (ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
+                if (WF != 3 && !lo_rows) bl[j] = Bb[1024 + (ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
             }
 #pragma unroll
             for (int i = 0; i < FM; i++) {
