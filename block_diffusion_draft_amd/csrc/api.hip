@@ -19,7 +19,8 @@ struct Plan {
     int attn_chunk, attn_nch;
     int topk_nch;
     bool lm_skinny;
-    int head_nrun, head_rc;      // column runs of the skinny head's statistics (rc 0: none)
+    int head_nrun, head_rc;      // column runs of the head's statistics (rc 0: none)
+    int head_rt;                 // > 0: balanced runs over this many 16-column tiles
     // byte offsets into the workspace
     size_t o_valid, o_h, o_xc, o_u2, o_fcout, o_Q, o_Kb, o_Vb, o_attnO, o_attnML, o_o, o_zp,
         o_Y, o_mid2, o_f, o_logits, o_topk, o_rstat, o_ssq_x, o_ssq_c, o_ssq_u, o_part;
@@ -94,9 +95,9 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
                   ((size_t)(p.H / 32) * 32 + 16 + 8 * 512) * 16 <= 160 * 1024;
     // the streaming head leaves per-run softmax statistics for the selector (one launch
     // after the head instead of two passes over the logits) where the runs fit it
-    p.head_nrun = p.head_rc = 0;
+    p.head_nrun = p.head_rc = p.head_rt = 0;
     if (p.lm_skinny) {
-        head_runs(p.V, p.H, &p.head_nrun, &p.head_rc);
+        head_runs(p.V, p.H, &p.head_nrun, &p.head_rc, &p.head_rt);
     } else if (big_gemm_ok(0, p.R, p.V, p.H)) {
         // the many-row head: one run per N tile of its grid
         const BigGemmPlan hp = big_gemm_plan_grid(0, p.R, p.V, p.H);
@@ -104,7 +105,7 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
         p.head_rc = hp.bn;
     }
     if (p.head_rc > 512 || (p.head_rc & (p.head_rc - 1)) || p.head_nrun > 2048)
-        p.head_nrun = p.head_rc = 0;
+        p.head_nrun = p.head_rc = p.head_rt = 0;
 
     size_t part = 0;
     const int fmt = c->weight_fmt;
@@ -516,8 +517,8 @@ int draft_step_impl(const dflash_config *cfg, const dflash_weights *w, int batch
     }
     // S10 + S11: log-softmax statistics, top-K, and the selector path
     if (p.head_rc)
-        HIPCHK(launch_topk_path_runs(logits, x.at<float>(p.o_rstat), p.head_nrun, p.head_rc, batch,
-                                     p.P, p.V, p.K, valid, x.at<float>(p.o_topk), w->code_a,
+        HIPCHK(launch_topk_path_runs(logits, x.at<float>(p.o_rstat), p.head_nrun, p.head_rc,
+                                     p.head_rt, batch, p.P, p.V, p.K, valid, x.at<float>(p.o_topk), w->code_a,
                                      w->code_b, p.r, cfg->pair_scale, cand_ids, cand_logp,
                                      draft_tokens, x.st));
     else

@@ -199,7 +199,11 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a, int ti
 }
 
 // Output head for at most 8 activation rows, weights read as whole cache lines.
-// One workgroup of 8 waves per CU; the rows sit in LDS in MFMA lane order.  A wave
+// One workgroup of 8 waves per CU; the rows sit in LDS in MFMA lane order.  The N / 16
+// weight tiles are dealt to the grid's waves in balanced runs (wave w of nw takes tiles
+// [w T / nw, (w + 1) T / nw)), so a grid of one workgroup per CU keeps every CU
+// streaming the same number of bytes (at V = 248320: 7 or 8 tiles per wave on all 256
+// CUs, where runs of 8 left 13 CUs idle).  A wave
 // streams its run of 16-row weight tiles in groups of 16 rows x 128 columns: each of a
 // group's 4 loads reads 4 rows x 256 contiguous bytes (non-temporal: read once), so
 // every load covers full lines.  The group passes through a 4 KB per-wave LDS buffer
@@ -215,7 +219,7 @@ constexpr int HS_WAVES = 8;
 constexpr int HS_D = 4;
 constexpr int HS_TB = 8;           // tiles per output batch
 
-__global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a, int tiles_per_wave) {
+__global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a) {
     extern __shared__ __align__(16) u32x4_t lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -223,8 +227,9 @@ __global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a, int tiles_p
     const int nks = a.K / 32;
     const int ngr = a.K / 128;                       // groups per tile, a multiple of HS_D
     const int ntiles = a.N / 16;
-    const int t0 = (blockIdx.x * HS_WAVES + wave) * tiles_per_wave;
-    const int t1 = min(t0 + tiles_per_wave, ntiles);
+    const int nw = gridDim.x * HS_WAVES, w = blockIdx.x * HS_WAVES + wave;
+    const int t0 = (int)((long long)w * ntiles / nw);
+    const int t1 = (int)((long long)(w + 1) * ntiles / nw);
     const int nst = t1 > t0 ? (t1 - t0) * ngr : 0;
     const int tlast = (t1 > t0 ? t1 : ntiles) - 1;
     u32x4_t *Alds = lds;                                          // [nks][32] + zero entry
@@ -398,8 +403,7 @@ __global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a, int tiles_p
             mx = lane == m ? rmax[m] : mx;
             sm = lane == m ? rsum[m] : sm;
         }
-        const int nrun = gridDim.x * HS_WAVES, w = blockIdx.x * HS_WAVES + wave;
-        *reinterpret_cast<float2 *>(a.rstat + 2 * ((size_t)lane * nrun + w)) = make_float2(mx, sm);
+        *reinterpret_cast<float2 *>(a.rstat + 2 * ((size_t)lane * nw + w)) = make_float2(mx, sm);
     }
 }
 
@@ -411,25 +415,28 @@ hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-void head_runs(int N, int K, int *nrun, int *run_cols) {
+namespace {
+// waves of the streaming head: one workgroup per CU (256 CUs), fewer for small N
+int head_waves(int ntiles) { return ceil_div(min(ntiles, 256 * HS_WAVES), HS_WAVES) * HS_WAVES; }
+}  // namespace
+
+void head_runs(int N, int K, int *nrun, int *run_cols, int *run_tiles) {
     const int ntiles = N / 16;
-    if (K % (128 * HS_D) != 0 || ntiles < 1) {
-        *nrun = 0;
-        *run_cols = 0;
-        return;
-    }
-    const int tpw = ceil_div(ntiles, 256 * HS_WAVES);
-    const int waves = ceil_div(ntiles, tpw);
-    *nrun = ceil_div(waves, HS_WAVES) * HS_WAVES;
-    *run_cols = (tpw & (tpw - 1)) == 0 ? 16 * tpw : 0;      // (the selector takes 2^k-wide runs)
+    *nrun = *run_cols = *run_tiles = 0;
+    if (K % (128 * HS_D) != 0 || ntiles < 1) return;
+    const int nw = head_waves(ntiles);
+    int rc = 16;                                            // widest run, rounded up to 2^k
+    while (rc < 16 * ceil_div(ntiles, nw)) rc *= 2;
+    *nrun = nw;
+    *run_cols = rc;
+    *run_tiles = ntiles;
 }
 
 hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st) {
     const int ntiles = a.N / 16;
     if (a.K % (128 * HS_D) == 0) {
         // one workgroup of HS_WAVES waves per CU
-        const int tpw = ceil_div(ntiles, 256 * HS_WAVES);
-        const int waves = ceil_div(ntiles, tpw);
+        const int waves = head_waves(ntiles);
         const size_t lds = ((size_t)(a.K / 32) * 32 + 16 + HS_WAVES * 512) * 16;
         static size_t hs_lds_set = 0;
         if (lds > hs_lds_set) {
@@ -438,7 +445,7 @@ hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st) {
             if (e != hipSuccess) return e;
             hs_lds_set = lds;
         }
-        hipLaunchKernelGGL(k_head_stream, dim3(ceil_div(waves, HS_WAVES)), dim3(512), lds, st, a, tpw);
+        hipLaunchKernelGGL(k_head_stream, dim3(waves / HS_WAVES), dim3(512), lds, st, a);
         return hipGetLastError();
     }
     if (a.rstat) return hipErrorInvalidValue;            // (statistics: the kernel above only)

@@ -36,11 +36,12 @@ hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st);
 // rows <= 8, one weight matrix (nseg == 1): activations resident in LDS, every wave
 // streams whole weight tiles
 hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st);
-// Column runs of the skinny head's softmax statistics for an N x K head: each wave of the
-// streaming head kernel covers run_cols consecutive columns and, given a.rstat, writes per
-// row r and run w the pair (max, sum exp(v - max)) at rstat[2 (r nrun + w)].  run_cols 0:
-// the shape takes the kernel without statistics.
-void head_runs(int N, int K, int *nrun, int *run_cols);
+// Column runs of the skinny head's softmax statistics for an N x K head: wave w of the
+// streaming head kernel's nrun waves covers the 16-column tiles [w T / nrun, (w + 1) T /
+// nrun) of the T = run_tiles tiles (at most run_cols columns, a power of two) and, given
+// a.rstat, writes per row r the pair (max, sum exp(v - max)) of its run at
+// rstat[2 (r nrun + w)].  run_cols 0: the shape takes the kernel without statistics.
+void head_runs(int N, int K, int *nrun, int *run_cols, int *run_tiles);
 
 // ---------------------------------------------------------------- layer ops
 enum EpiMode { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_SWIGLU_BF16 = 2, EPI_STORE_BF16 = 3 };
@@ -120,11 +121,15 @@ hipError_t launch_topk_path(const float *logits, int B, int P, int V, int K, con
                             float *ws, const uint16_t *code_a, const uint16_t *code_b, int r,
                             float pair_scale, int32_t *cand_ids, float *cand_logp,
                             int32_t *draft_tokens, hipStream_t st);
-// The same selection and path from the head's column-run statistics (head_runs): one
-// launch; per row the threshold and logsumexp come from the runs' (max, sum) pairs and
-// only the runs whose max reaches the threshold are read back.  ws: as above.
+// The same selection and path from the head's column-run statistics: one launch; per
+// row the threshold and logsumexp come from the runs' (max, sum) pairs and only the runs
+// whose max reaches the threshold are read back.  run_tiles 0: run w is columns
+// [w run_cols, (w + 1) run_cols); run_tiles T > 0: the balanced runs of head_runs (run w
+// is the 16-column tiles [w T / nrun, (w + 1) T / nrun), at most run_cols columns).
+// ws: as above.
 hipError_t launch_topk_path_runs(const float *logits, const float *rstat, int nrun, int run_cols,
-                                 int B, int P, int V, int K, const int32_t *valid, float *ws,
+                                 int run_tiles, int B, int P, int V, int K, const int32_t *valid,
+                                 float *ws,
                                  const uint16_t *code_a, const uint16_t *code_b, int r,
                                  float pair_scale, int32_t *cand_ids, float *cand_logp,
                                  int32_t *draft_tokens, hipStream_t st);

@@ -20,7 +20,9 @@
 //  * the super-block adds d (T - 128 sum_j sc_j S_rj) - dmin sum_j m_j S_rj.
 //
 // Work split: a workgroup (8 waves) owns one split of 4 super-blocks (1024 values
-// of K) and one run of tpw consecutive 16-column tiles per wave.  The split's
+// of K); the split's column tiles are dealt to its waves in balanced runs (wave w of
+// the split's nw takes tiles [w T / nw, (w + 1) T / nw)), and the grid has about one
+// workgroup per CU, so every CU streams nearly the same number of bytes.  The split's
 // activation rows are staged once in LDS in MFMA lane order; their sub-block sums
 // come from the staging lanes (a sum of 8 and two lane exchanges), and each lane keeps
 // the bias operands it needs in registers.  Each wave then streams its tiles'
@@ -80,7 +82,7 @@ __device__ __forceinline__ uint32_t bias_pair(uint32_t lo, uint32_t hi, uint32_t
 
 // PX > 0: rows r and r + PX / 4 are one (hi, lo) pair, held PX lanes apart
 template <int WPG, int PX>
-__global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw) {
+__global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a) {
     constexpr int NT = 64 * WPG;                    // threads per workgroup
     extern __shared__ __align__(16) unsigned char lds[];
     u32x4_t *A_lds = reinterpret_cast<u32x4_t *>(lds);              // [SNSB][8][64]
@@ -91,8 +93,9 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a, int tpw
     const int g = lane >> 4, cl = lane & 15;
     const int split = blockIdx.y, sb0 = split * SNSB;
     const int ntile = a.N / 16;
-    const int t0 = (blockIdx.x * WPG + wave) * tpw;
-    const int t1 = min(t0 + tpw, ntile);
+    const int nw = gridDim.x * WPG, w = blockIdx.x * WPG + wave;
+    const int t0 = (int)((long long)w * ntile / nw);
+    const int t1 = (int)((long long)(w + 1) * ntile / nw);
     const int tlast = (t1 > t0 ? t1 : ntile) - 1;       // clamp target, always a real tile
 
     // ---- weight stream.  Stage (tile t, super-block sb) is the unit at tile_base(t)
@@ -240,15 +243,14 @@ Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int pair, int target_waves, i
     Q4kStreamPlan p;
     const int KB = K / 256, ntile = N / 16;
     p.splits = KB / SNSB;
-    const long long wave_tiles = (long long)ntile * p.splits;
-    int tpw = (int)((wave_tiles + target_waves - 1) / target_waves);
-    if (tpw < 1) tpw = 1;
-    p.tpw = tpw;
     // wpg 0: 8-wave workgroups (one activation staging feeds 8 runs of tiles; measured
     // 3-7% faster than 4 waves at every drafter shape)
     p.wpg = wpg > 0 ? wpg : 8;
     wpg = p.wpg;
-    p.grid_x = ceil_div(ceil_div(ntile, tpw), wpg);
+    // about target_waves waves in all (one 8-wave workgroup per CU at the default), and
+    // no more workgroups per split than it has tiles for a wave each
+    p.grid_x = max(1, min(target_waves / (wpg * p.splits), ceil_div(ntile, wpg)));
+    p.tpw = ceil_div(ntile, p.grid_x * wpg);            // (the longest run)
     // the (hi, lo) halves of a pair sit pair / 4 lane groups = 4 pair lanes apart
     p.pair_done = (pair == 4 || pair == 8) && M == 2 * pair;
     p.px = p.pair_done ? 4 * pair : 0;
@@ -261,7 +263,7 @@ hipError_t launch_q4k_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipS
     const dim3 grid(p.grid_x, p.splits);
 #define QS_CASE(WPG, PX)                                                                              \
     if (p.wpg == WPG && p.px == PX) {                                                                 \
-        hipLaunchKernelGGL((k_q4k_stream<WPG, PX>), grid, dim3(64 * WPG), p.lds_bytes, st, a, p.tpw); \
+        hipLaunchKernelGGL((k_q4k_stream<WPG, PX>), grid, dim3(64 * WPG), p.lds_bytes, st, a);        \
         return hipGetLastError();                                                                     \
     }
     QS_CASE(4, 0)

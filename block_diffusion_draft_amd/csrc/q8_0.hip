@@ -105,7 +105,7 @@ __device__ __forceinline__ u32x4_t q8_decode(uint32_t w0, uint32_t w1) {
 
 // PX > 0: rows r and r + PX / 4 are one (hi, lo) pair, held PX lanes apart
 template <int WPG, int PX>
-__global__ __launch_bounds__(64 * WPG) void k_q8_stream(Q4kFusedArgs a, int tpw) {
+__global__ __launch_bounds__(64 * WPG) void k_q8_stream(Q4kFusedArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     u32x4_t *A_lds = reinterpret_cast<u32x4_t *>(lds);                     // [SG][8][64]
     f32x4_t *C_lds = reinterpret_cast<f32x4_t *>(A_lds + Q8_SG * 8 * 64);  // [SG][8][4]
@@ -115,8 +115,10 @@ __global__ __launch_bounds__(64 * WPG) void k_q8_stream(Q4kFusedArgs a, int tpw)
     const int g = lane >> 4, cl = lane & 15;
     const int split = blockIdx.y, g0 = split * Q8_SG;
     const int ntile = a.N / 16;
-    const int t0 = (blockIdx.x * WPG + wave) * tpw;
-    const int t1 = min(t0 + tpw, ntile);
+    // balanced runs of the split's column tiles over its nw waves
+    const int nw = gridDim.x * WPG, w = blockIdx.x * WPG + wave;
+    const int t0 = (int)((long long)w * ntile / nw);
+    const int t1 = (int)((long long)(w + 1) * ntile / nw);
     const int tlast = (t1 > t0 ? t1 : ntile) - 1;       // clamp target, always a real tile
 
     // stage (tile t, group sg of the split) is the unit at tile_base(t) + sg * 4352;
@@ -237,12 +239,11 @@ Q4kStreamPlan q8_stream_plan(int M, int N, int K, int pair, int target_waves, in
     Q4kStreamPlan p;
     const int G = K / 256, ntile = N / 16;
     p.splits = G / Q8_SG;
-    const long long wave_tiles = (long long)ntile * p.splits;
-    int tpw = (int)((wave_tiles + target_waves - 1) / target_waves);
-    if (tpw < 1) tpw = 1;
-    p.tpw = tpw;
     p.wpg = wpg > 0 ? wpg : 8;
-    p.grid_x = ceil_div(ceil_div(ntile, tpw), p.wpg);
+    // about target_waves waves in all, no more workgroups per split than it has tiles
+    // for a wave each
+    p.grid_x = max(1, min(target_waves / (p.wpg * p.splits), ceil_div(ntile, p.wpg)));
+    p.tpw = ceil_div(ntile, p.grid_x * p.wpg);          // (the longest run)
     p.pair_done = (pair == 4 || pair == 8) && M == 2 * pair;
     p.px = p.pair_done ? 4 * pair : 0;
     p.lds_bytes = (size_t)Q8_SG * 8 * 64 * 16 + (size_t)Q8_SG * 8 * 4 * 16;
@@ -254,7 +255,7 @@ hipError_t launch_q8_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipSt
     const dim3 grid(p.grid_x, p.splits);
 #define Q8_CASE(WPG, PX)                                                                             \
     if (p.wpg == WPG && p.px == PX) {                                                                \
-        hipLaunchKernelGGL((k_q8_stream<WPG, PX>), grid, dim3(64 * WPG), p.lds_bytes, st, a, p.tpw); \
+        hipLaunchKernelGGL((k_q8_stream<WPG, PX>), grid, dim3(64 * WPG), p.lds_bytes, st, a);        \
         return hipGetLastError();                                                                    \
     }
     Q8_CASE(4, 0)

@@ -366,16 +366,18 @@ __device__ void select_full_scan(const float *logits, int V, int nch, int K, int
     }
 }
 
-// one wave, row r: top-K from the head's run statistics (nrun <= 64 RPL runs of rc = 2^lrc
-// <= 512 columns); cvl, cil, crun, cmax: this wave's LDS scratch.  theta1 = the K-th
+// one wave, row r: top-K from the head's run statistics (nrun <= 64 RPL runs of at most
+// rc = 2^lrc <= 512 columns: run w is columns [w rc, (w + 1) rc) when nt is 0, else the
+// 16-column tiles [w nt / nrun, (w + 1) nt / nrun)); cvl, cil, crun, cwid, cmax: this
+// wave's LDS scratch.  theta1 = the K-th
 // largest of the 64 lane maxima of the run maxima; among the runs reaching it (at least
 // K), theta2 = the K-th largest run maximum, which is the K-th largest of all run maxima:
 // the K runs above it each hold a logit >= theta2, so every top-K logit is >= theta2 and
 // lies in a run whose maximum reaches theta2.  Those runs' logits >= theta2 are the
 // candidates (with more than 64 runs at theta1, theta1 is used instead).
-__device__ void select_row_runs(const float *logits, int V, int nrun, int lrc, int K, int r,
-                                const float *rstat, float *cvl, int *cil, int *crun, float *cmax,
-                                int *sid, float *slp) {
+__device__ void select_row_runs(const float *logits, int V, int nrun, int lrc, int nt, int K,
+                                int r, const float *rstat, float *cvl, int *cil, int *crun,
+                                int *cwid, float *cmax, int *sid, float *slp) {
     const int lane = threadIdx.x & 63;
     const int rc = 1 << lrc;
     const float2 *st = reinterpret_cast<const float2 *>(rstat) + (size_t)r * nrun;
@@ -426,6 +428,20 @@ __device__ void select_row_runs(const float *logits, int V, int nrun, int lrc, i
     }
     int n = 0;
     if (nc <= RUNCAP) {
+        // the runs' first columns and widths (32-bit products: nrun nt < 2^27)
+        for (int q = lane; q < nc; q += 64) {
+            const int w = crun[q];
+            int c0 = w << lrc, cw = rc;
+            if (nt) {
+                const int a0 = (int)((unsigned)(w * nt) / (unsigned)nrun);
+                const int a1 = (int)((unsigned)((w + 1) * nt) / (unsigned)nrun);
+                c0 = 16 * a0;
+                cw = 16 * (a1 - a0);
+            }
+            crun[q] = c0;
+            cwid[q] = cw;
+        }
+        __builtin_amdgcn_wave_barrier();
         // their logits >= theta (32 loads per lane in flight per batch)
         const int ncols = nc << lrc;
         for (int e0 = 0; e0 < ncols && n <= RCAP; e0 += 64 * 32) {
@@ -434,8 +450,9 @@ __device__ void select_row_runs(const float *logits, int V, int nrun, int lrc, i
 #pragma unroll
             for (int u = 0; u < 32; u++) {
                 const int e = e0 + 64 * u + lane;
-                const int col = crun[e < ncols ? e >> lrc : 0] * rc + (e & (rc - 1));
-                id[u] = e < ncols && col < V ? col : -1;
+                const int q = e < ncols ? e >> lrc : 0, off = e & (rc - 1);
+                const int col = crun[q] + off;
+                id[u] = e < ncols && off < cwid[q] && col < V ? col : -1;
                 v[u] = logits[(size_t)r * V + (id[u] >= 0 ? col : 0)];
             }
 #pragma unroll
@@ -471,7 +488,7 @@ constexpr int PATH_WAVES = 8;
 // ...; the dynamic programme then runs on K lanes.
 __global__ __launch_bounds__(64 * PATH_WAVES) void k_select_path(
     const float *logits, int V, int nch, int K, const int *count, const float *cv,
-    const int32_t *ci, const float *lse, const float *rstat, int nrun, int lrc, int P,
+    const int32_t *ci, const float *lse, const float *rstat, int nrun, int lrc, int nt, int P,
     const int32_t *valid, const uint16_t *code_a, const uint16_t *code_b, int r, float s,
     int32_t *cand_ids, float *cand_logp, int32_t *draft) {
     __shared__ int ids[MAXP][MAXK];
@@ -483,6 +500,7 @@ __global__ __launch_bounds__(64 * PATH_WAVES) void k_select_path(
     __shared__ float cvl[PATH_WAVES][RCAP];
     __shared__ int cil[PATH_WAVES][RCAP];
     __shared__ int crun[PATH_WAVES][RUNCAP];
+    __shared__ int cwid[PATH_WAVES][RUNCAP];
     __shared__ float cmax[PATH_WAVES][RUNCAP];
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool ok = valid[b] != 0;
@@ -490,8 +508,8 @@ __global__ __launch_bounds__(64 * PATH_WAVES) void k_select_path(
         const int row = b * P + t;
         if (ok) {
             if (rstat)
-                select_row_runs(logits, V, nrun, lrc, K, row, rstat, cvl[wave], cil[wave],
-                                crun[wave], cmax[wave], ids[t], lp[t]);
+                select_row_runs(logits, V, nrun, lrc, nt, K, row, rstat, cvl[wave], cil[wave],
+                                crun[wave], cwid[wave], cmax[wave], ids[t], lp[t]);
             else
                 select_row(logits, V, nch, K, row, count, cv, ci, lse[row], ids[t], lp[t]);
         }
@@ -691,14 +709,14 @@ hipError_t launch_topk_path(const float *logits, int B, int P, int V, int K, con
     hipLaunchKernelGGL(k_collect, grid, dim3(256), 0, st, logits, V, nch, K, pm, ps, lse, count, cv,
                        ci);
     hipLaunchKernelGGL(k_select_path, dim3(B), dim3(64 * PATH_WAVES), 0, st, logits, V, nch, K, count,
-                       cv, ci, lse, (const float *)nullptr, 0, 0, P, valid, code_a, code_b, r,
+                       cv, ci, lse, (const float *)nullptr, 0, 0, 0, P, valid, code_a, code_b, r,
                        pair_scale, cand_ids, cand_logp, draft_tokens);
     return hipGetLastError();
 }
 
 hipError_t launch_topk_path_runs(const float *logits, const float *rstat, int nrun, int run_cols,
-                                 int B, int P, int V, int K, const int32_t *valid, float *ws,
-                                 const uint16_t *code_a, const uint16_t *code_b, int r,
+                                 int run_tiles, int B, int P, int V, int K, const int32_t *valid,
+                                 float *ws, const uint16_t *code_a, const uint16_t *code_b, int r,
                                  float pair_scale, int32_t *cand_ids, float *cand_logp,
                                  int32_t *draft_tokens, hipStream_t st) {
     int lrc = 0;
@@ -706,10 +724,14 @@ hipError_t launch_topk_path_runs(const float *logits, const float *rstat, int nr
     if (P > MAXP || K > MAXK || nrun < 1 || nrun > 64 * RPL || run_cols < 1 || run_cols > 512 ||
         (1 << lrc) != run_cols || (long long)nrun * run_cols < V)
         return hipErrorInvalidValue;
+    // balanced runs: they cover the tiles exactly, none wider than run_cols
+    if (run_tiles < 0 || (run_tiles && ((long long)run_tiles * 16 < V || run_tiles > 65536 ||
+                                        16 * ceil_div(run_tiles, nrun) > run_cols)))
+        return hipErrorInvalidValue;
     (void)ws;
     hipLaunchKernelGGL(k_select_path, dim3(B), dim3(64 * PATH_WAVES), 0, st, logits, V,
                        ceil_div(V, CHUNK), K, (const int *)nullptr, (const float *)nullptr,
-                       (const int32_t *)nullptr, (const float *)nullptr, rstat, nrun, lrc, P,
+                       (const int32_t *)nullptr, (const float *)nullptr, rstat, nrun, lrc, run_tiles, P,
                        valid, code_a, code_b, r, pair_scale, cand_ids, cand_logp, draft_tokens);
     return hipGetLastError();
 }

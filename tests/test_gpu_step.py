@@ -263,20 +263,28 @@ def test_mid_step_many_rows(fmt):
     check_verify(bufs, g)
 
 
-@pytest.mark.parametrize("case,batch", [("all_equal", 1), ("tied_block", 1), ("all_equal", 4),
-                                        ("tied_block", 4)])
-def test_mid_step_head_run_selection_ties(case, batch):
+# a vocabulary of 4133 16-column tiles: the streaming head's 2048 waves take balanced
+# runs of 2 or 3 tiles (32 or 48 columns)
+RAGGED_VOCAB = 16 * 4133
+
+
+@pytest.mark.parametrize("case,batch,vocab", [("all_equal", 1, 0), ("tied_block", 1, 0),
+                                              ("all_equal", 4, 0), ("tied_block", 4, 0),
+                                              ("all_equal", 1, RAGGED_VOCAB),
+                                              ("tied_block", 1, RAGGED_VOCAB)])
+def test_mid_step_head_run_selection_ties(case, batch, vocab):
     """The 1024-wide drafter takes the selection from the output head's column-run
-    statistics: at batch 1 the streaming head's runs of 16 columns, at batch 4 the
-    many-row head's 256-column tiles.  Every head row equal: all logits tie, every run
-    reaches the threshold and the exact scan must return ids 0..K-1 with log-prob
-    -log(V).  A block of 40 equal rows among random ones: candidates tie inside the
-    run lists, and the top K must still be exact by (logit desc, id asc) on the GPU's
-    own logits."""
-    s = synth.MID
+    statistics: at batch 1 the streaming head's runs (one 16-column tile per wave at
+    V = 8192; 2 or 3 tiles at the ragged vocabulary), at batch 4 the many-row head's
+    256-column tiles.  Every head row equal: all logits tie, every run reaches the
+    threshold and the exact scan must return ids 0..K-1 with log-prob -log(V).  A block
+    of 40 equal rows among random ones (across run boundaries): candidates tie inside
+    the run lists, and the top K must still be exact by (logit desc, id asc) on the
+    GPU's own logits."""
+    s = synth.MID if not vocab else dataclasses.replace(synth.MID, vocab=vocab)
     wl = dataclasses.replace(synth.WORKLOADS["tiny"], shape=s, batch=batch, ctx_len=96,
                              seed=141)
-    say(f"[step] mid head-run selection, {case}, batch {batch}")
+    say(f"[step] mid head-run selection, {case}, batch {batch}, vocab {s.vocab}")
     W = synth.make_weights(s, wl.seed)
     E = W["embed"].copy()
     if case == "all_equal":
@@ -303,3 +311,19 @@ def test_mid_step_head_run_selection_ties(case, batch):
     parity.check_topk_reanchored(g["logits"], g["ids"], g["lp"], K)
     ref = parity.run_oracle(wl, W, bufs.inputs)
     assert np.abs(g["logits"] - ref["logits"]).max() <= parity.LOGIT_MAX_ABS
+
+
+def test_mid_step_ragged_head_runs():
+    """Full parity at a vocabulary whose 16-column tiles do not divide evenly over the
+    streaming head's waves (balanced runs of 2 or 3 tiles), with the selector's
+    codebooks N(0, 1) so that the path depends on every candidate."""
+    s = dataclasses.replace(synth.MID, vocab=RAGGED_VOCAB)
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], shape=s, batch=1, ctx_len=96, seed=143)
+    say(f"[step] mid ragged head runs, vocab {s.vocab}")
+    W = synth.make_weights(s, wl.seed, code_std=1.0)
+    bufs = runner.StepBuffers(wl, weights=W)
+    bufs.step()
+    torch.cuda.synchronize()
+    ref = parity.run_oracle(wl, bufs.host_W, bufs.inputs)
+    g = full_check(wl, bufs, ref)
+    check_verify(bufs, g)
