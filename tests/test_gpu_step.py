@@ -246,15 +246,21 @@ def test_mid_step_streaming_products(fmt, head_dim, batch):
     check_verify(bufs, g)
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q8_0", "bf16"])
-def test_mid_step_many_rows(fmt):
-    """4 sequences of a 2-layer drafter: every product has more than 16 rows (32 block
-    rows, 64 with the context rows or the (hi, lo) pairs) and runs on the many-row GEMM
-    with the format's weight decode, split-K where the tiles are few; the output head
-    (28 rows) too, with the deferred final norm applied in its epilogue."""
+@pytest.mark.parametrize("fmt,batch,vocab", [("q4k", 4, 0), ("q8_0", 4, 0), ("bf16", 4, 0),
+                                             ("q4k", 128, 0), ("fp8", 128, 0),
+                                             ("bf16", 128, 16 * 4133)])
+def test_mid_step_many_rows(fmt, batch, vocab):
+    """Many sequences of a 2-layer drafter: every product has more than 16 rows and runs
+    on the many-row GEMM with the format's weight decode.  4 sequences: 32 block rows, 64
+    with the context rows or the (hi, lo) pairs, split-K where the tiles are few, the
+    output head (28 rows) with the deferred final norm in its epilogue.  128 sequences:
+    1024 block rows over 4 row tiles, 2048 MLP rows over 8, the 896-row head, and (bf16)
+    a vocabulary of 4133 16-column tiles whose last 256-column head tile is ragged."""
     s = dataclasses.replace(synth.MID, weight_fmt=fmt)
-    wl = dataclasses.replace(synth.WORKLOADS["tiny"], shape=s, batch=4, ctx_len=96, seed=61)
-    say(f"[step] mid {fmt} batch 4")
+    if vocab:
+        s = dataclasses.replace(s, vocab=vocab)
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], shape=s, batch=batch, ctx_len=96, seed=61)
+    say(f"[step] mid {fmt} batch {batch}, vocab {s.vocab}")
     bufs = runner.StepBuffers(wl)
     bufs.step()
     torch.cuda.synchronize()
