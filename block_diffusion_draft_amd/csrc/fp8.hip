@@ -164,13 +164,17 @@ __global__ __launch_bounds__(64 * WPG) void k_f8_stream(Q4kFusedArgs a) {
         // opaque to the compiler: keeps the activation fragments in LDS
         asm volatile("" : "+v"(a_off));
         const unsigned char *bcur = tile_base(t), *bnext = tile_base(t + 1);
+        // in the run's last tile the loads ahead re-read unit (t, 3), just requested (an
+        // L2 hit, unused)
+        const bool more = t + 1 < t1;
         const float s = s_next;
         s_next = col_scale(t + 1);
         f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sg = 0; sg < F8_SG; sg++) {
             st[(sg + 3) & 3] = sg == 0 ? f8_load(bcur + 3 * FP8_UNIT_BYTES, lane)
-                                       : f8_load(bnext + (sg - 1) * FP8_UNIT_BYTES, lane);
+                                       : f8_load(more ? bnext + (sg - 1) * FP8_UNIT_BYTES
+                                                      : bcur + 3 * FP8_UNIT_BYTES, lane);
             __builtin_amdgcn_sched_barrier(0);
             const F8Stage &w = st[sg];
 #pragma unroll

@@ -100,7 +100,10 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a) {
 
     // ---- weight stream.  Stage (tile t, super-block sb) is the unit at tile_base(t)
     // + sb * 2304; loads run 3 stages ahead, so tile t's loop issues (t, 3) and
-    // (t + 1, 0..2); tiles past t1 - 1 clamp to tlast (in bounds, unused).
+    // (t + 1, 0..2).  In the run's last tile the three loads ahead re-read unit (t, 3),
+    // just requested, so they hit in L2 (in bounds, unused; re-reading the tile's first
+    // units instead, evicted by then, cost 3 units of HBM traffic per wave: 14 MB per
+    // gate|up launch).
     auto tile_base = [&](int t) -> const unsigned char * {
         const int tt = t < t1 ? t : tlast;
         const int c16 = tt * 16;
@@ -185,10 +188,11 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a) {
         // hoisting them into registers (which would cost waves per SIMD)
         asm volatile("" : "+v"(a_off));
         const unsigned char *bcur = tile_base(t), *bnext = tile_base(t + 1);
+        const bool more = t + 1 < t1;               // (wave-uniform)
         f32x4_t acc = zero;
 #pragma unroll
         for (int sb = 0; sb < SNSB; sb++) {
-            st[(sb + 3) & 3] = sb == 0 ? stage(bcur, 3) : stage(bnext, sb - 1);
+            st[(sb + 3) & 3] = sb == 0 ? stage(bcur, 3) : stage(more ? bnext : bcur, more ? sb - 1 : 3);
             // keep the loads here, 3 stages ahead of their use (left alone, the
             // scheduler sinks them to the end of the tile and the latency shows)
             __builtin_amdgcn_sched_barrier(0);

@@ -181,10 +181,13 @@ __global__ __launch_bounds__(64 * WPG) void k_q8_stream(Q4kFusedArgs a) {
         // opaque to the compiler: keeps the activation fragments in LDS
         asm volatile("" : "+v"(a_off), "+v"(c_off));
         const unsigned char *bcur = tile_base(t), *bnext = tile_base(t + 1);
+        // in the run's last tile the loads ahead re-read unit (t, 3), just requested (an
+        // L2 hit, unused)
+        const bool more = t + 1 < t1;
         f32x4_t acc = zero;
 #pragma unroll
         for (int sg = 0; sg < Q8_SG; sg++) {
-            st[(sg + 3) & 3] = sg == 0 ? stage(bcur, 3) : stage(bnext, sg - 1);
+            st[(sg + 3) & 3] = sg == 0 ? stage(bcur, 3) : stage(more ? bnext : bcur, more ? sg - 1 : 3);
             __builtin_amdgcn_sched_barrier(0);
             const Q8Stage &w = st[sg];
 #pragma unroll

@@ -162,6 +162,13 @@ def _per_dispatch(d, pattern):
 
 def launches(fetch_dir, write_dir, sq_dir, trace_dir, kernel, copy_bytes, copies=3,
              copy_pat="copyBuffer", cus=256, xcds=8, out=sys.stdout):
+    """Per launch shape of the kernels matching `kernel`: duration, scaled HBM bytes and
+    SQ counters.  The counter runs and the kernel-trace run are runs of the same command,
+    so a dispatch id names the same launch in each; the trace supplies each dispatch's
+    grid shape (x by y: launches of equal total size but different shape stay apart)."""
+    shape = {}
+    for r in _rows(trace_dir, "kernel_trace.csv"):
+        shape[r["Dispatch_Id"]] = f"{r.get('Grid_Size_X') or r.get('Grid_Size')}x{r.get('Grid_Size_Y') or 1}"
     scales = {}
     for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         c, _ = _counter(d, cname, copy_pat)
@@ -169,26 +176,24 @@ def launches(fetch_dir, write_dir, sq_dir, trace_dir, kernel, copy_bytes, copies
         scales[cname] = copy_bytes / (sum(cv) / len(cv) * 1024.0)
     agg = {}
     for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        for e in _per_dispatch(d, kernel).values():
+        for di, e in _per_dispatch(d, kernel).items():
             if cname in e:
-                agg.setdefault((short(e["name"], 40), e["grid"]), {}).setdefault(cname, []).append(
-                    e[cname] * 1024.0 * scales[cname])
-    for e in _per_dispatch(sq_dir, kernel).values():
-        a = agg.setdefault((short(e["name"], 40), e["grid"]), {})
+                key = (short(e["name"], 40), shape.get(di, str(e["grid"])))
+                agg.setdefault(key, {}).setdefault(cname, []).append(e[cname] * 1024.0 * scales[cname])
+    for di, e in _per_dispatch(sq_dir, kernel).items():
+        a = agg.setdefault((short(e["name"], 40), shape.get(di, str(e["grid"]))), {})
         for k, v in e.items():
             if k not in ("name", "grid"):
                 a.setdefault(k, []).append(v)
     for r in _rows(trace_dir, "kernel_trace.csv"):
         if not re.search(kernel, r["Kernel_Name"]):
             continue
-        g = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0) * int(r.get("Grid_Size_Y") or 1) * \
-            int(r.get("Grid_Size_Z") or 1)
-        key = (short(r["Kernel_Name"], 40), g)
+        key = (short(r["Kernel_Name"], 40), shape[r["Dispatch_Id"]])
         if key in agg:
             agg[key].setdefault("us", []).append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     mean = lambda v: sum(v) / len(v) if v else float("nan")
-    out.write(f"{'kernel':40s} {'grid':>8s} {'us':>7s} {'hbm_MB':>8s} {'GB/s':>7s} "
+    out.write(f"{'kernel':40s} {'grid':>10s} {'us':>7s} {'hbm_MB':>8s} {'GB/s':>7s} "
               f"{'valu/wave':>9s} {'mfma/wave':>9s} {'valu_busy':>9s} {'mfma_busy':>9s} "
               f"{'waves/simd':>10s}\n")
     for (n, g), a in sorted(agg.items(), key=lambda kv: -mean(kv[1].get("us", [0]))):
@@ -197,7 +202,7 @@ def launches(fetch_dir, write_dir, sq_dir, trace_dir, kernel, copy_bytes, copies
         cyc = mean(a.get("GRBM_GUI_ACTIVE", [])) / xcds
         waves = mean(a.get("SQ_WAVES", []))
         simds = 4 * cus
-        out.write(f"{n:40s} {g:8d} {us:7.1f} {hbm / 1e6:8.2f} {hbm / us / 1e3:7.0f} "
+        out.write(f"{n:40s} {g:>10s} {us:7.1f} {hbm / 1e6:8.2f} {hbm / us / 1e3:7.0f} "
                   f"{mean(a.get('SQ_INSTS_VALU', [])) / waves:9.0f} "
                   f"{mean(a.get('SQ_INSTS_MFMA', [])) / waves:9.0f} "
                   f"{mean(a.get('SQ_ACTIVE_INST_VALU', [])) * 4 / (simds * cyc):9.3f} "
