@@ -42,9 +42,10 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 // schedule of the workgroups: wgs == 0: one workgroup per (N tile, M tile, K split)
 // item (a 1-D grid, items dealt to XCDs in contiguous runs); else stream-K
-// over wgs workgroups (a multiple of 8), tx x ty tiles of nst stages, `slots` slots
+// over wgs workgroups (a multiple of 8), tx x ty tiles of nst stages, `slots` slots;
+// gs > 0: grouped stream-K (below) over groups of gs weight slabs
 struct BigSched {
-    int wgs, tx, ty, nst, slots;
+    int wgs, tx, ty, nst, slots, gs;
 };
 
 // weight segment of output column n: its base pointer and the first column of the segment
@@ -211,19 +212,37 @@ __device__ __forceinline__ void zero_slots(const BigGemmArgs &a, int m0, int n0,
 // weight slab) run on one XCD (workgroups are dealt round robin over the 8 XCDs) and
 // share its L2.  A piece's slot is its distance from the range holding the tile's
 // first unit; `last`: the tile's last piece (it zeroes the slots after its own).
+// Grouped stream-K: the units (group of gs weight slabs, stage s) are cut into
+// wgs / (ty gs) ranges, and range q is worked by ty gs workgroups on one XCD, one per
+// (M tile, slab of the group), which start together at the same K offset: each stage
+// of a slab and of an M tile's rows comes from HBM once and serves the group's other
+// tiles from L2 (the M-fastest ranges left the tiles sharing a slab or a row block at
+// different K offsets: at 64 sequences gate|up fetched 2.56 GB per launch, 7.2x its
+// weights).
 struct Piece {
     int m0, n0, s0, s1, slot;
     bool scale, last;
 };
 struct Pieces {
     long long u, u1, U;
-    int g;
+    int g, m, j;
     __device__ __forceinline__ Pieces(const BigGemmArgs &a, const BigSched &sc) {
+        m = j = 0;
         if (sc.wgs == 0) {
             u = 0;
             u1 = 1;
             U = 1;
             g = 0;
+        } else if (sc.gs) {
+            // workgroup b on XCD b % 8, index i = b / 8 there: M tile i % ty, slab
+            // (i / ty) % gs of its group, range x (wgs / 8 / (ty gs)) + i / (ty gs)
+            const int i = blockIdx.x >> 3, tg = sc.ty * sc.gs, R = sc.wgs / tg;
+            m = i % sc.ty;
+            j = (i / sc.ty) % sc.gs;
+            g = (blockIdx.x & 7) * ((sc.wgs >> 3) / tg) + i / tg;
+            U = (long long)ceil_div(sc.tx, sc.gs) * sc.nst;
+            u = (long long)g * U / R;
+            u1 = (long long)(g + 1) * U / R;
         } else {
             g = (blockIdx.x & 7) * (sc.wgs >> 3) + (blockIdx.x >> 3);
             U = (long long)sc.tx * sc.ty * sc.nst;
@@ -233,6 +252,9 @@ struct Pieces {
     }
     template <int BM, int TBN = BN>
     __device__ __forceinline__ bool next(const BigGemmArgs &a, const BigSched &sc, Piece &p) {
+        // grouped: a group's slab j may lie past the last slab; the pieces are skipped
+        while (sc.gs && u < u1 && (int)(u / sc.nst) * sc.gs + j >= sc.tx)
+            u = min(u1, (u / sc.nst + 1) * sc.nst);
         if (u >= u1) return false;
         if (sc.wgs == 0) {
             // grid of tx * ty * slots workgroups, one piece each: workgroup b takes item
@@ -258,9 +280,10 @@ struct Pieces {
         p.s0 = (int)(u - (long long)t * sc.nst);
         p.s1 = (int)min((long long)sc.nst, p.s0 + (u1 - u));
         const long long x = (long long)t * sc.nst;
-        p.slot = g - ((int)(((x + 1) * sc.wgs + U - 1) / U) - 1);   // (range holding unit x)
-        p.m0 = (t % sc.ty) * BM;
-        p.n0 = (t / sc.ty) * TBN;
+        const int R = sc.gs ? sc.wgs / (sc.ty * sc.gs) : sc.wgs;      // ranges
+        p.slot = g - ((int)(((x + 1) * R + U - 1) / U) - 1);         // (range holding unit x)
+        p.m0 = (sc.gs ? m : t % sc.ty) * BM;
+        p.n0 = (sc.gs ? t * sc.gs + j : t / sc.ty) * TBN;
         p.scale = sc.slots == 1 && a.rs.ssq;
         p.last = p.s1 == sc.nst;
         u += p.s1 - p.s0;
@@ -656,6 +679,7 @@ BigGemmPlan big_gemm_plan_grid(int wf, int M, int N, int K) {
     p.grid_x = ceil_div(N, p.bn);
     p.grid_y = ceil_div(M, p.bm);
     p.wgs = 0;
+    p.gs = 0;
     p.splits = 1;
     p.part_bytes = (size_t)M * N * 4;
     return p;
@@ -687,21 +711,33 @@ BigGemmPlan big_gemm_plan(int wf, int M, int N, int K) {
     }
     const long long U = T * nst;
     if (U >= 4LL * G) {
+        // grouped stream-K where the M tiles divide each XCD's workgroups: the largest
+        // group of gs slabs (gs dividing G / 8 / ty) whose last group leaves at most 10%
+        // of its workgroups idle; ranges over (group, stage) units, else over tiles
+        int gs = 0;
+        if (p.grid_y > 1 && (G / 8) % p.grid_y == 0)
+            for (int c = (G / 8) / p.grid_y; c >= 1 && !gs; c /= 2) {
+                const int ng = ceil_div(p.grid_x, c);
+                if ((G / 8) % (p.grid_y * c) == 0 && 10 * (ng * c - p.grid_x) <= ng * c) gs = c;
+            }
+        const long long Ts = gs ? ceil_div(p.grid_x, gs) : T;
+        const int Gs = gs ? G / (p.grid_y * gs) : G;
         // (cached on exactly the inputs of sk_slots: the slot count walks every tile)
         static thread_local struct { long long T; int nst, G, slots; } cache[8] = {};
         static thread_local int next = 0;
         int slots = 0;
         for (auto &c : cache)
-            if (c.slots && c.T == T && c.nst == nst && c.G == G) slots = c.slots;
+            if (c.slots && c.T == Ts && c.nst == nst && c.G == Gs) slots = c.slots;
         if (!slots) {
-            slots = sk_slots(T, nst, G);
-            cache[next] = {T, nst, G, slots};
+            slots = sk_slots(Ts, nst, Gs);
+            cache[next] = {Ts, nst, Gs, slots};
             next = (next + 1) % 8;
         }
         const long long per = (U + G - 1) / G;
         const double c = 1.15 * per + epi * (1 + (per + nst - 1) / nst) + slots * slot;
         if (slots <= 16 && c < best) {
             p.wgs = G;
+            p.gs = gs;
             p.splits = slots;
         }
     }
@@ -719,7 +755,8 @@ hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream
     if (p.wgs && (p.wgs % 8 || a.ldc % 4)) return hipErrorInvalidValue;
     // operand rows are fetched as 16-byte pieces straight into LDS
     if (reinterpret_cast<uintptr_t>(a.A) % 16 || a.lda % 8) return hipErrorInvalidValue;
-    BigSched sc = {p.wgs, p.grid_x, p.grid_y, a.K / BK, p.splits};
+    if (p.gs && (p.gs < 1 || (p.wgs / 8) % (p.grid_y * p.gs))) return hipErrorInvalidValue;
+    BigSched sc = {p.wgs, p.grid_x, p.grid_y, a.K / BK, p.splits, p.gs};
     const dim3 grid(p.wgs ? p.wgs : p.grid_x * p.grid_y * p.splits);
     const int bi = p.bm == 256;
     const void *fn;

@@ -262,6 +262,7 @@ struct BigGemmPlan {
                                  // up to 128 rows); N and M tiles
     int splits;                  // partial slots [splits][M][N] the consumer sums
     int wgs;                     // 0: grid (N tiles, M tiles, splits); else stream-K workgroups
+    int gs;                      // > 0: grouped stream-K over groups of gs weight slabs
     size_t part_bytes;
 };
 bool big_gemm_ok(int wf, int M, int N, int K);

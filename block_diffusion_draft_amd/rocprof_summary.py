@@ -210,6 +210,46 @@ def launches(fetch_dir, write_dir, sq_dir, trace_dir, kernel, copy_bytes, copies
                   f"{waves / simds:10.2f}\n")
 
 
+def hbm(fetch_dir, write_dir, trace_dir, kernel="", copy_bytes=1 << 31, copies=3,
+        copy_pat="copyBuffer", out=sys.stdout):
+    """Every kernel of a step, per launch shape: launches, mean duration (trace run) and
+    FETCH_SIZE / WRITE_SIZE per launch in MB (each scaled by what it reads for the plain
+    device copy of copy_bytes in the same run), and their sum over the duration.  The
+    three runs are runs of the same command; dispatch ids join them."""
+    shape, dur = {}, {}
+    for r in _rows(trace_dir, "kernel_trace.csv"):
+        sh = f"{r.get('Grid_Size_X') or r.get('Grid_Size')}x{r.get('Grid_Size_Y') or 1}x{r.get('Grid_Size_Z') or 1}"
+        shape[r["Dispatch_Id"]] = sh
+        if re.search(kernel, r["Kernel_Name"]):
+            dur.setdefault((short(r["Kernel_Name"], 40), sh), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    agg = {}
+    for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        c, _ = _counter(d, cname, copy_pat)
+        cv = sorted(c.values())[-copies:]
+        scale = copy_bytes / (sum(cv) / len(cv) * 1024.0)
+        names = {}
+        per = {}
+        for r in _rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != cname or not re.search(kernel, r["Kernel_Name"]):
+                continue
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        for di, v in per.items():
+            key = (short(names[di], 40), shape.get(di, "?"))
+            agg.setdefault(key, {}).setdefault(cname, []).append(v * 1024.0 * scale)
+    mean = lambda v: sum(v) / len(v) if v else 0.0
+    out.write(f"{'kernel':40s} {'grid':>20s} {'launches':>8s} {'us':>8s} {'fetch_MB':>9s} "
+              f"{'write_MB':>9s} {'GB/s':>7s}\n")
+    keys = sorted(set(dur) | set(agg), key=lambda k: -mean(dur.get(k, [])) * len(dur.get(k, [])))
+    for k in keys:
+        a = agg.get(k, {})
+        us = mean(dur.get(k, []))
+        f, w = mean(a.get("FETCH_SIZE", [])), mean(a.get("WRITE_SIZE", []))
+        out.write(f"{k[0]:40s} {k[1]:>20s} {len(dur.get(k, [])):8d} {us:8.1f} {f / 1e6:9.2f} "
+                  f"{w / 1e6:9.2f} {(f + w) / us / 1e3 if us else 0.0:7.0f}\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -219,6 +259,11 @@ def main():
     a = sub.add_parser("launches")
     for o in ("--fetch", "--write", "--sq", "--trace", "--kernel"):
         a.add_argument(o, required=True)
+    a.add_argument("--copy-bytes", type=int, required=True)
+    a = sub.add_parser("hbm")
+    for o in ("--fetch", "--write", "--trace"):
+        a.add_argument(o, required=True)
+    a.add_argument("--kernel", default="")
     a.add_argument("--copy-bytes", type=int, required=True)
     a = sub.add_parser("traffic")
     a.add_argument("--fetch", required=True); a.add_argument("--write", required=True)
@@ -235,6 +280,8 @@ def main():
         mfma(args.dir, args.pattern)
     elif args.cmd == "launches":
         launches(args.fetch, args.write, args.sq, args.trace, args.kernel, args.copy_bytes)
+    elif args.cmd == "hbm":
+        hbm(args.fetch, args.write, args.trace, args.kernel, args.copy_bytes)
     else:
         r = traffic(args.fetch, args.write, args.kernel, args.copy_bytes, args.copies)
         lines = [f"kernel_pattern {args.kernel}",

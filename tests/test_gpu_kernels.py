@@ -127,12 +127,16 @@ def test_q4k_gemm_row_counts(M):
     gemm_check(w, x, N, K, M)
 
 
-@pytest.mark.parametrize("M,N,K", [(160, 4096, 4096), (256, 8704, 5120), (136, 34816, 4096)])
+@pytest.mark.parametrize("M,N,K", [(160, 4096, 4096), (256, 8704, 5120), (136, 34816, 4096),
+                                   (512, 34816, 2048), (1000, 8704, 4096)])
 def test_q4k_gemm_schedules(M, N, K):
     """Many-row GEMM schedules: 16 and 34 tiles of 256 rows run as one round of K splits
     (13 and 7 splits); 136 tiles (ragged rows) as stream-K, each CU one equal range of
     (tile, K stage) units, the pieces of a tile in their own partial slots (3), unused
-    slots zeroed."""
+    slots zeroed; 2 and 4 M tiles (the last ragged) as grouped stream-K, ranges of
+    (group of 16 / 4 weight slabs, K stage) units each worked by one workgroup per (M
+    tile, slab of the group), some slabs of the last group past the matrix (2 and 3
+    slots)."""
     say(f"[q4k_gemm schedules] M={M} {N}x{K}")
     w = synth.q4k_normal(8, "sk", N, K, 0.02)
     x = synth.normal_bf16(8, "sk.x", (M, K), 1.0)

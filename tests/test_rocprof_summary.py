@@ -91,3 +91,21 @@ def test_launches_keep_equal_sized_grids_of_different_shape_apart(tmp_path):
     # FETCH_SIZE scaled x 2: 1000 KiB -> 2.048 MB, 500 KiB -> 1.024 MB
     assert float(lines["26112x5"][2]) == pytest.approx(2.048, abs=0.006)
     assert float(lines["7680x17"][2]) == pytest.approx(1.024, abs=0.006)
+
+
+def test_hbm_lists_every_kernel_by_shape(tmp_path):
+    k = "void k_q4k_stream<8, 32>(Q4kFusedArgs)"
+    fetch, write, tr = (str(tmp_path / x) for x in "fwt")
+    write_counters(fetch, "f", [(1, 130560, k, "FETCH_SIZE", 1000.0), (2, 130560, k, "FETCH_SIZE", 500.0),
+                                (3, 8, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 512.0)])
+    write_counters(write, "w", [(1, 130560, k, "WRITE_SIZE", 100.0), (2, 130560, k, "WRITE_SIZE", 0.0),
+                                (3, 8, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 1024.0)])
+    write_trace(tr, [(1, k, 26112, 5, 0, 20000), (2, k, 7680, 17, 30000, 40000),
+                     (3, "__amd_rocclr_copyBuffer", 8, 1, 50000, 51000)])
+    out = io.StringIO()
+    rs.hbm(fetch, write, tr, "", 1 << 20, copies=1, out=out)
+    rows = {l.split()[-6]: l.split()[-6:] for l in out.getvalue().splitlines()[1:]}
+    assert set(rows) == {"26112x5x1", "7680x17x1", "8x1x1"}
+    # grid, launches, us, fetch MB (x 2), write MB (x 1), GB/s
+    assert rows["26112x5x1"][1:5] == ["1", "20.0", "2.05", "0.10"]
+    assert rows["7680x17x1"][1:5] == ["1", "10.0", "1.02", "0.00"]
