@@ -20,9 +20,11 @@
 // for BM = 128) of 32 x 32 MFMA tiles.  The operands sit in LDS in MFMA lane order,
 // 16-byte entries placed so that operand reads are free of bank conflicts.  A (and bf16
 // W) travel global -> LDS by direct loads (global_load_lds_dwordx4: no registers, no
-// LDS store instructions) through a ring of K stages, several stages in flight while one
-// is multiplied; Q8_0 / Q4_K weights are loaded into registers two stages ahead and
-// decoded into a double-buffered LDS tile of (hi, lo) operands.
+// LDS store instructions) through a ring of K stages, the next ones in flight while one
+// is multiplied (bf16: 64-deep stages, a ring of 2, for the 256 x 256 and 128 x 512
+// tiles; 32-deep, a ring of 4, for 128 x 256); Q8_0 / Q4_K weights are loaded into
+// registers two stages ahead and decoded into a double-buffered LDS tile of (hi, lo)
+// operands.
 //
 // Work split: a grid over (N tile, M tile, K split), or stream-K where the tiles would
 // leave a partly empty last round of workgroups: the (tile, 64-deep K stage) units are
@@ -39,6 +41,10 @@ namespace {
 
 constexpr int BN = 256, BK = 64, NTH = 512;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+// s_waitcnt immediate that waits until at most n (< 64) vector loads are outstanding and
+// leaves the other counters alone: vmcnt is split over bits 3:0 and 15:14
+constexpr int vm_wait(int n) { return 0xF70 | (n & 15) | ((n >> 4) << 14); }
 
 // schedule of the workgroups: wgs == 0: one workgroup per (N tile, M tile, K split)
 // item (a 1-D grid, items dealt to XCDs in contiguous runs); else stream-K
@@ -403,24 +409,44 @@ __device__ __forceinline__ void wq_store(u32x4_t *Bb, const WRaw &rw, const bool
     }
 }
 
-// bf16 weights: both operands through a ring of NS stages of 32 K.  A stage holds
-// 32-row groups of 32 rows x 64 bytes (2 KB); lane L of a load instruction fills the
-// 16-byte slot L of one 1 KB half, i.e. row 16 h + L / 4, chunk slot L % 4, and it loads
-// the chunk (L % 4) ^ ((row / 4) % 4) of that row: four lanes cover a row's 64 bytes, and
-// the 16 rows read together by an MFMA operand load (one chunk each) fall on 16
-// distinct 16-byte bank groups.  Rows and columns past M / N load row M - 1 / column
+// bf16 weights: both operands through a ring of NS stages of BKD = 32 or 64 K.  A stage
+// holds 32-row groups of 32 rows x 2 BKD bytes; a row's bytes are CH = BKD / 8 16-byte
+// chunks.  Lane L of a load instruction fills the 16-byte slot L of one 1 KB piece of a
+// group, i.e. row RPK h + L / CH (RPK = 64 / CH rows per piece), chunk slot L % CH, and it
+// loads the chunk (L % CH) ^ sw(row) of that row, sw(row) = (row / 4) % 4 for 32 K and
+// (row / 2) % 8 for 64 K: CH lanes cover a row's bytes of the stage, and the 16 rows read
+// together by an MFMA operand load (one chunk each) fall on 16 distinct 16-byte bank
+// groups.  64-deep stages read 128 bytes of each row per load (whole lines): in a
+// load-only probe over the output head's matrix, 64-byte row pieces streamed at 4.1-4.4
+// TB/s and 128-byte ones at 6.9.  Rows and columns past M / N load row M - 1 / column
 // N - 1 (in bounds) and are never stored.
-constexpr int BKD = 32, DMA_NS = 4;
+template <int BKD>
+__device__ __forceinline__ int dma_pos(int row, int chunk) {
+    if constexpr (BKD == 32) return 4 * row + (chunk ^ ((row >> 2) & 3));
+    else return 8 * row + (chunk ^ ((row >> 1) & 7));
+}
 
-__device__ __forceinline__ int dma_pos(int row, int chunk) { return 4 * row + (chunk ^ ((row >> 2) & 3)); }
+// stage depth per tile, and the ring: as many stages as fit 160 KB of LDS, at most 4.
+// 64-deep stages (rings of 2) measured faster for the 256 x 256 tiles (the 64-sequence
+// step 6.49-6.54 -> 6.21-6.28 ms, gate|up 395 -> 363 us: half the barriers per K and
+// whole-line row pieces) and the 128 x 512 output-head tiles (112 rows: 543 -> 510 us);
+// 128 x 256 tiles with 64-deep stages (a ring of 3) ran that head in 529 us.
+template <int BM, int TBN> constexpr int dma_bkd() { return BM == 256 || TBN == 512 ? 64 : 32; }
+constexpr int dma_ring(int BM, int TBN, int bkd) {
+    const int n = 163840 / ((BM + TBN) * 2 * bkd);
+    return n < 4 ? n : 4;
+}
+template <int BM, int TBN> constexpr int dma_ns() { return dma_ring(BM, TBN, dma_bkd<BM, TBN>()); }
 
-// one tile piece (BM x TBN) over 32-deep stages [s0, s1)
-template <int BM, int NS, int TBN>
+// one tile piece (BM x TBN) over BKD-deep stages [s0, s1)
+template <int BM, int NS, int TBN, int BKD>
 __device__ __forceinline__ void dma_piece(const BigGemmArgs &a, u32x4_t *lds, int m0, int n0, int s0,
                                           int s1, int slot, bool scale) {
     constexpr int RG = BM / 32, WM = BM / 2, FM = WM / 32, FN = TBN / 128;
-    constexpr int NG = RG + TBN / 32;                 // 2 KB groups per stage (A, then W)
-    constexpr int PW = 2 * NG / 8;                    // load instructions per wave and stage
+    constexpr int NG = RG + TBN / 32;                 // 32-row groups per stage (A, then W)
+    constexpr int CH = BKD / 8, RPK = 64 / CH, LPG = 32 / RPK, GE = 32 * CH;
+    constexpr int PW = NG * LPG / 8;                  // load instructions per wave and stage
+    static_assert(NG * LPG % 8 == 0, "whole load instructions per wave");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
@@ -429,9 +455,10 @@ __device__ __forceinline__ void dma_piece(const BigGemmArgs &a, u32x4_t *lds, in
     const uint16_t *src[PW];
 #pragma unroll
     for (int j = 0; j < PW; j++) {
-        const int h = wave + 8 * j;                   // 1 KB half: group h / 2, rows 16 (h % 2) ..
-        const int g = h >> 1, row = 16 * (h & 1) + (lane >> 2);
-        const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+        const int h = wave + 8 * j;                   // 1 KB piece: group h / LPG, rows RPK (h % LPG) ..
+        const int g = h / LPG, row = RPK * (h % LPG) + lane / CH;
+        const int sw = BKD == 32 ? (row >> 2) & 3 : (row >> 1) & 7;
+        const int chunk = (lane % CH) ^ sw;
         if (g < RG) {
             const int r = min(m0 + 32 * g + row, a.M - 1);
             src[j] = a.A + (size_t)r * a.lda + 8 * chunk;
@@ -449,7 +476,7 @@ __device__ __forceinline__ void dma_piece(const BigGemmArgs &a, u32x4_t *lds, in
             const int h = wave + 8 * j;
             __builtin_amdgcn_global_load_lds(
                 (const void __attribute__((address_space(1))) *)(src[j] + k0),
-                (void __attribute__((address_space(3))) *)(lds + (buf * NG * 2 + h) * 64), 16, 0, 0);
+                (void __attribute__((address_space(3))) *)(lds + buf * NG * GE + h * 64), 16, 0, 0);
         }
     };
 
@@ -461,9 +488,12 @@ __device__ __forceinline__ void dma_piece(const BigGemmArgs &a, u32x4_t *lds, in
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-    // read positions of this lane's MFMA operands for the two k steps of a stage
+    // read positions of this lane's MFMA operands for the BKD / 16 k steps of a stage
+    constexpr int KS = BKD / 16;
     const int rl = lane & 31;
-    const int rp0 = dma_pos(rl, lane >> 5), rp1 = dma_pos(rl, 2 + (lane >> 5));
+    int rp[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) rp[ks] = dma_pos<BKD>(rl, 2 * ks + (lane >> 5));
 
     // prologue: stages s0 .. s0 + NS - 2 in flight (past the end: the last stage again,
     // into a buffer no stage reads, so every iteration waits on the same count)
@@ -473,23 +503,23 @@ __device__ __forceinline__ void dma_piece(const BigGemmArgs &a, u32x4_t *lds, in
         const int buf = (s - s0) % NS;
         // stage s has landed (the NS - 2 later ones may be in flight) in every wave; a
         // bare barrier, since a workgroup fence would wait for every load in flight
-        __builtin_amdgcn_s_waitcnt(0xF70 | ((NS - 2) * PW));
+        static_assert((NS - 2) * PW < 64, "vmcnt holds 6 bits");
+        __builtin_amdgcn_s_waitcnt(vm_wait((NS - 2) * PW));
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         // the buffer of stage s - 1 is free: stage s + NS - 1 goes there
         issue(min(s + NS - 1, s1 - 1), (s - s0 + NS - 1) % NS);
-        const u32x4_t *Ab = lds + buf * NG * 128;
-        const u32x4_t *Bb = Ab + RG * 128;
+        const u32x4_t *Ab = lds + buf * NG * GE;
+        const u32x4_t *Bb = Ab + RG * GE;
 #pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-            const int rp = ks ? rp1 : rp0;
+        for (int ks = 0; ks < KS; ks++) {
             u32x4_t bf[FN];
 #pragma unroll
-            for (int j = 0; j < FN; j++) bf[j] = Bb[(wn * FN + j) * 128 + rp];
+            for (int j = 0; j < FN; j++) bf[j] = Bb[(wn * FN + j) * GE + rp[ks]];
 #pragma unroll
             for (int i = 0; i < FM; i++) {
-                const u32x4_t af = Ab[(wm * FM + i) * 128 + rp];
+                const u32x4_t af = Ab[(wm * FM + i) * GE + rp[ks]];
 #pragma unroll
                 for (int j = 0; j < FN; j++) acc[i][j] = mfma32x32x16(af, bf[j], acc[i][j]);
             }
@@ -507,7 +537,9 @@ __global__ __launch_bounds__(NTH) void k_gemm_big_dma(BigGemmArgs a, BigSched sc
     Piece pc;
     for (bool first = true; it.next<BM, TBN>(a, sc, pc); first = false) {
         if (!first) __syncthreads();                  // the previous piece is done with LDS
-        dma_piece<BM, DMA_NS, TBN>(a, lds, pc.m0, pc.n0, 2 * pc.s0, 2 * pc.s1, pc.slot, pc.scale);
+        constexpr int BKD = dma_bkd<BM, TBN>(), SPB = BK / BKD;   // stages per 64-deep unit
+        dma_piece<BM, dma_ns<BM, TBN>(), TBN, BKD>(a, lds, pc.m0, pc.n0, SPB * pc.s0, SPB * pc.s1,
+                                                    pc.slot, pc.scale);
         if (pc.last) zero_slots<BM, TBN>(a, pc.m0, pc.n0, pc.slot + 1, sc.slots, threadIdx.x);
     }
 }
@@ -517,7 +549,7 @@ __global__ __launch_bounds__(NTH) void k_gemm_big_dma(BigGemmArgs a, BigSched sc
 // bytes of a stage loaded into registers two stages ahead (two register sets,
 // alternating) and decoded into the double-buffered (hi, lo) W tile after the current
 // stage's MFMAs.  Each k step multiplies the A operand by both terms of the weights.
-constexpr int QNS = 3;
+constexpr int QNS = 3, QBKD = 32;
 
 // one tile piece over 32-deep stages [s0, s1)
 template <int WF, int BM>
@@ -546,7 +578,7 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
 #pragma unroll
         for (int j = 0; j < PA; j++)
             __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1))) *)(asrc[j] + st * BKD),
+                (const void __attribute__((address_space(1))) *)(asrc[j] + st * QBKD),
                 (void __attribute__((address_space(3))) *)(As + buf * AST + (wave + 8 * j) * 64), 16, 0, 0);
     };
     const unsigned char *wbase[2];
@@ -562,7 +594,7 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
     const int rl = lane & 31;
-    const int rp0 = dma_pos(rl, lane >> 5), rp1 = dma_pos(rl, 2 + (lane >> 5));
+    const int rp0 = dma_pos<QBKD>(rl, lane >> 5), rp1 = dma_pos<QBKD>(rl, 2 + (lane >> 5));
     // this wave's rows are all lo terms of activation pairs: their products with the
     // weights' lo terms (<= 2^-18 of the sum) are skipped (wave-uniform)
     const bool lo_rows = a.lo_row > 0 && m0 + wm * WM >= a.lo_row;
@@ -590,7 +622,8 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
     // wait until at most one stage's loads are in flight (the one issued last)
     auto wait_one = [&]() {
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0xF70 | (PA + PWQ));
+        static_assert(PA + PWQ < 64, "vmcnt holds 6 bits");
+        __builtin_amdgcn_s_waitcnt(vm_wait(PA + PWQ));
         asm volatile("" ::: "memory");
     };
     // stage st: A(st) and the decoded W(st) are in LDS once every wave passes the barrier;
@@ -643,7 +676,11 @@ __global__ __launch_bounds__(NTH) void k_gemm_big_q(BigGemmArgs a, BigSched sc) 
 
 }  // namespace
 
-size_t dma_lds_bytes(int BM, int TBN) { return (size_t)DMA_NS * (BM / 32 + TBN / 32) * 2048; }
+size_t dma_lds_bytes(int BM, int TBN) {
+    // ring: NS stages of (BM + TBN) rows x 2 BKD bytes
+    const int bkd = BM == 256 ? dma_bkd<256, 256>() : TBN == 512 ? dma_bkd<128, 512>() : dma_bkd<128, 256>();
+    return (size_t)dma_ring(BM, TBN, bkd) * (BM + TBN) * 2 * bkd;
+}
 size_t q_lds_bytes(int BM) { return ((size_t)QNS * BM * 4 + 2 * 2048) * 16; }
 
 namespace {
