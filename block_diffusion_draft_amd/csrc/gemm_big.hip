@@ -37,6 +37,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace {
 
 constexpr int BN = 256, BK = 64, NTH = 512;
@@ -339,13 +341,13 @@ __device__ __forceinline__ void wq_load(WRaw &rw, const unsigned char *const (&w
             const unsigned char *unit = wbase[i] + (size_t)g * Q8_UNIT_BYTES;
             const u32x2_t q = *reinterpret_cast<const u32x2_t *>(unit + 256 + 1024 * pr + 16 * ln + 8 * (blk & 1));
             const uint32_t sc = *reinterpret_cast<const uint32_t *>(unit + 16 * (ln & 15) + 4 * pr);
-            rw.v[2 * i] = (u32x4_t){q.x, q.y, (uint32_t)blk, 0u};
+            rw.v[2 * i] = (u32x4_t){q.x, q.y, 0u, 0u};
             rw.v[2 * i + 1] = (u32x4_t){sc, 0u, 0u, 0u};
         } else {
             const int sb = st >> 3, j = st & 7, c = j >> 1;
             const unsigned char *unit = wbase[i] + (size_t)sb * Q4K_UNIT_BYTES;
             const u32x2_t q = *reinterpret_cast<const u32x2_t *>(unit + 256 + 1024 * (c >> 1) + 16 * ln + 8 * (c & 1));
-            rw.v[2 * i] = (u32x4_t){q.x, q.y, (uint32_t)j, 0u};
+            rw.v[2 * i] = (u32x4_t){q.x, q.y, 0u, 0u};
             rw.v[2 * i + 1] = *reinterpret_cast<const u32x4_t *>(unit + 16 * (ln & 15));
         }
     }
@@ -359,48 +361,49 @@ __device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t v) {
 
 // decode a stage's raw bytes into the (hi, lo) MFMA operands of the W tile Bb
 // ([2 (hi, lo)][2 ks][8][64], slot swz): task (column, k group kg) fills entry kg of its
-// column's fragment: ks = kg / 2, lane (column % 32) + 32 (kg % 2).  FP8: the codes'
-// bf16 values only (no lo term)
+// column's fragment: ks = kg / 2, lane (column % 32) + 32 (kg % 2).  sub = stage % 8 (the
+// Q4_K sub-block, the Q8_0 block of the pair).  FP8: the codes' bf16 values only (no lo
+// term).  Columns past N store zeros.
 template <int WF>
-__device__ __forceinline__ void wq_store(u32x4_t *Bb, const WRaw &rw, const bool (&wok)[2], int tid) {
+__device__ __forceinline__ void wq_store(u32x4_t *Bb, const WRaw &rw, const bool (&wok)[2], int tid, int sub) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int e = tid + NTH * i, cg = e / 64, ln = e & 63;
-        u32x4_t oh = {0u, 0u, 0u, 0u}, ol = {0u, 0u, 0u, 0u};
-        if (wok[i]) {
-            const u32x4_t q = rw.v[2 * i], h = rw.v[2 * i + 1];
-            float v[8];
-            if (WF == 3) {
-                oh = (u32x4_t){e4m3x2_bf16<false>(q.x), e4m3x2_bf16<true>(q.x),
-                               e4m3x2_bf16<false>(q.y), e4m3x2_bf16<true>(q.y)};
-            } else if (WF == 1) {
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
+        u32x4_t oh = zero, ol = zero;
+        const u32x4_t q = rw.v[2 * i], h = rw.v[2 * i + 1];
+        float v[8];
+        if constexpr (WF == 3) {
+            oh = (u32x4_t){e4m3x2_bf16<false>(q.x), e4m3x2_bf16<true>(q.x),
+                           e4m3x2_bf16<false>(q.y), e4m3x2_bf16<true>(q.y)};
+        } else if constexpr (WF == 1) {
 #pragma unroll
-                for (int b = 0; b < 8; b++)
-                    v[b] = (float)(int8_t)((b < 4 ? q.x : q.y) >> (8 * (b & 3)));
-                const uint32_t sc = (q.z & 1) ? (h.x >> 16) : (h.x & 0xFFFFu);
-                split8(v, half_bits_to_f32(sc), 0.f, oh, ol);
-            } else {
-                // sub-block j: the low (j even) or high (j odd) nibbles of the chunk
-                const int j = (int)q.z, shift = 4 * (j & 1);
+            for (int b = 0; b < 8; b++)
+                v[b] = (float)(int8_t)((b < 4 ? q.x : q.y) >> (8 * (b & 3)));
+            const uint32_t sc = (sub & 1) ? (h.x >> 16) : (h.x & 0xFFFFu);
+            split8(v, half_bits_to_f32(sc), 0.f, oh, ol);
+        } else {
+            // sub-block j: the low (j even) or high (j odd) nibbles of the chunk
+            const int j = sub, shift = 4 * (j & 1);
+            const uint32_t mx = (q.x >> shift) & 0x0F0F0F0Fu, my = (q.y >> shift) & 0x0F0F0F0Fu;
 #pragma unroll
-                for (int b = 0; b < 8; b++)
-                    v[b] = (float)((((b < 4 ? q.x : q.y) >> (8 * (b & 3))) >> shift) & 15u);
-                // header: d, dmin, 6-bit scale and min of sub-block j
-                const float d = half_bits_to_f32(h.x & 0xFFFFu);
-                const float dmin = half_bits_to_f32(h.x >> 16);
-                const uint32_t sb[3] = {h.y, h.z, h.w};
-                auto byte = [&](int i2) { return (sb[i2 >> 2] >> (8 * (i2 & 3))) & 0xFFu; };
-                uint32_t s6, m6;
-                if (j < 4) {
-                    s6 = byte(j) & 63u;
-                    m6 = byte(j + 4) & 63u;
-                } else {
-                    s6 = (byte(j + 4) & 15u) | ((byte(j - 4) >> 6) << 4);
-                    m6 = (byte(j + 4) >> 4) | ((byte(j) >> 6) << 4);
-                }
-                split8(v, d * (float)s6, dmin * (float)m6, oh, ol);
-            }
+            for (int b = 0; b < 8; b++) v[b] = (float)(((b < 4 ? mx : my) >> (8 * (b & 3))) & 0xFFu);
+            // header: d, dmin, 6-bit scale and min of sub-block j (scale bytes j, j + 4
+            // and j % 4 of h.y, h.z, h.w)
+            const float d = half_bits_to_f32(h.x & 0xFFFFu);
+            const float dmin = half_bits_to_f32(h.x >> 16);
+            auto byte = [&](int i2) {
+                const uint32_t w = i2 < 4 ? h.y : (i2 < 8 ? h.z : h.w);
+                return (w >> (8 * (i2 & 3))) & 0xFFu;
+            };
+            const uint32_t bj = byte(j), bj4 = byte(j + 4), bjl = byte(j & 3);
+            const uint32_t lo4 = (uint32_t)((j - 4) >> 31);       // all ones for j < 4
+            const uint32_t s6 = ((bj & 63u) & lo4) | (((bj4 & 15u) | ((bjl >> 6) << 4)) & ~lo4);
+            const uint32_t m6 = ((bj4 & 63u) & lo4) | (((bj4 >> 4) | ((bj >> 6) << 4)) & ~lo4);
+            split8(v, d * (float)s6, dmin * (float)m6, oh, ol);
         }
+        oh = wok[i] ? oh : zero;
+        ol = wok[i] ? ol : zero;
         const int kg = ln >> 4, col = 16 * cg + (ln & 15);
         const int li = (col & 31) + 32 * (kg & 1);
         const int at = ((kg >> 1) * 8 + (col >> 5)) * 64 + swz(li, kg);
@@ -595,30 +598,6 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
 
     const int rl = lane & 31;
     const int rp0 = dma_pos<QBKD>(rl, lane >> 5), rp1 = dma_pos<QBKD>(rl, 2 + (lane >> 5));
-    // this wave's rows are all lo terms of activation pairs: their products with the
-    // weights' lo terms (<= 2^-18 of the sum) are skipped (wave-uniform)
-    const bool lo_rows = a.lo_row > 0 && m0 + wm * WM >= a.lo_row;
-    auto compute = [&](const u32x4_t *Ab, const u32x4_t *Bb) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-            const int c = 2 * ks + (lane >> 5), rp = ks ? rp1 : rp0;
-            u32x4_t bh[2], bl[2];
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                bh[j] = Bb[(ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
-                if (WF != 3 && !lo_rows) bl[j] = Bb[1024 + (ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
-            }
-#pragma unroll
-            for (int i = 0; i < FM; i++) {
-                const u32x4_t af = Ab[(wm * FM + i) * 128 + rp];
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    acc[i][j] = mfma32x32x16(af, bh[j], acc[i][j]);
-                    if (WF != 3 && !lo_rows) acc[i][j] = mfma32x32x16(af, bl[j], acc[i][j]);
-                }
-            }
-        }
-    };
     // wait until at most one stage's loads are in flight (the one issued last)
     auto wait_one = [&]() {
         asm volatile("" ::: "memory");
@@ -626,37 +605,89 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
         __builtin_amdgcn_s_waitcnt(vm_wait(PA + PWQ));
         asm volatile("" ::: "memory");
     };
-    // stage st: A(st) and the decoded W(st) are in LDS once every wave passes the barrier;
-    // rn1 holds the raw weights of stage st + 1 (in flight), rn2 receives stage st + 2.
-    // Stages past the end load the last stage again into buffers no stage reads, so the
-    // wait counts stay fixed.
-    auto body = [&](int st, WRaw &rn1, WRaw &rn2) {
-        const int i = st - s0;
-        __builtin_amdgcn_s_waitcnt(0xC07F);           // this wave's LDS stores done
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        const int s2 = min(st + 2, s1 - 1);
-        issue_a(s2, (i + 2) % QNS);
-        wq_load<WF>(rn2, wbase, tid, s2);
-        asm volatile("" ::: "memory");                // (issued before the MFMAs)
-        compute(As + (i % QNS) * AST, Bs + (i & 1) * 2048);
+    // LO: this wave's rows are all lo terms of activation pairs, and their products with
+    // the weights' lo terms (<= 2^-18 of the sum) are skipped.  DF: the wave decodes the
+    // next stage before its MFMAs (the waves of the second M half), so that the two waves
+    // on a SIMD (w and w + 4) overlap one's MFMAs with the other's decode.
+    auto run = [&](auto lo_tag, auto df_tag) {
+        constexpr bool TWO = WF != 3 && !decltype(lo_tag)::value;   // both weight terms
+        constexpr bool DF = decltype(df_tag)::value;                // decode first
+        auto compute = [&](const u32x4_t *Ab, const u32x4_t *Bb) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                const int c = 2 * ks + (lane >> 5), rp = ks ? rp1 : rp0;
+                u32x4_t bh[2], bl[2];
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    bh[j] = Bb[(ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
+                    if constexpr (TWO) bl[j] = Bb[1024 + (ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
+                }
+#pragma unroll
+                for (int i = 0; i < FM; i++) {
+                    const u32x4_t af = Ab[(wm * FM + i) * 128 + rp];
+#pragma unroll
+                    for (int j = 0; j < 2; j++) {
+                        acc[i][j] = mfma32x32x16(af, bh[j], acc[i][j]);
+                        if constexpr (TWO) acc[i][j] = mfma32x32x16(af, bl[j], acc[i][j]);
+                    }
+                }
+            }
+        };
+        // stage st: A(st) and the decoded W(st) are in LDS once every wave passes the
+        // barrier; rn1 holds the raw weights of stage st + 1 (loaded a stage ago), rn2
+        // receives stage st + 2; the decode of stage st + 1 goes to the other W buffer.
+        // Stages past the end load the last stage again into buffers no stage reads, so
+        // the wait counts stay fixed.
+        auto body = [&](int st, WRaw &rn1, WRaw &rn2) {
+            const int i = st - s0;
+            __builtin_amdgcn_s_waitcnt(0xC07F);           // this wave's LDS stores done
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            const int s2 = min(st + 2, s1 - 1);
+            issue_a(s2, (i + 2) % QNS);
+            wq_load<WF>(rn2, wbase, tid, s2);
+            asm volatile("" ::: "memory");                // (issued before the MFMAs)
+            // the decode waits for rn1 first
+            const u32x4_t *Ab = As + (i % QNS) * AST, *Bb = Bs + (i & 1) * 2048;
+            u32x4_t *Bn = Bs + ((i + 1) & 1) * 2048;
+            const int sub = min(st + 1, s1 - 1) & 7;
+            if constexpr (!DF) {
+                compute(Ab, Bb);
+                wait_one();
+                wq_store<WF>(Bn, rn1, wok, tid, sub);
+            } else {
+                wait_one();
+                wq_store<WF>(Bn, rn1, wok, tid, sub);
+                compute(Ab, Bb);
+            }
+        };
+        WRaw ra, rb;
+        issue_a(s0, 0);
+        wq_load<WF>(ra, wbase, tid, s0);
+        issue_a(min(s0 + 1, s1 - 1), 1);
+        wq_load<WF>(rb, wbase, tid, min(s0 + 1, s1 - 1));
         wait_one();
-        wq_store<WF>(Bs + ((i + 1) & 1) * 2048, rn1, wok, tid);
+        wq_store<WF>(Bs, ra, wok, tid, s0 & 7);
+        int st = s0;
+        for (; st + 1 < s1; st += 2) {
+            body(st, rb, ra);
+            body(st + 1, ra, rb);
+        }
+        if (st < s1) body(st, rb, ra);
     };
-    WRaw ra, rb;
-    issue_a(s0, 0);
-    wq_load<WF>(ra, wbase, tid, s0);
-    issue_a(min(s0 + 1, s1 - 1), 1);
-    wq_load<WF>(rb, wbase, tid, min(s0 + 1, s1 - 1));
-    wait_one();
-    wq_store<WF>(Bs, ra, wok, tid);
-    int st = s0;
-    for (; st + 1 < s1; st += 2) {
-        body(st, rb, ra);
-        body(st + 1, ra, rb);
+    // (each case is its own straight-line stage loop: a branch inside the loop body
+    // made the register allocation spill)
+    using T = std::integral_constant<bool, true>;
+    using F = std::integral_constant<bool, false>;
+    const bool lo = a.lo_row > 0 && m0 + wm * WM >= a.lo_row;
+    if (lo) {
+        if (wm) run(T(), T());
+        else run(T(), F());
+    } else {
+        if (wm) run(F(), T());
+        else run(F(), F());
     }
-    if (st < s1) body(st, rb, ra);
     __builtin_amdgcn_s_waitcnt(0xF70);      // no load may land after the piece ends
 
     store_tile<BM, FM, 2, WF == 3>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot, scale);
