@@ -420,7 +420,7 @@ int draft_step_impl(const dflash_config *cfg, const dflash_weights *w, int batch
             a.B = batch; a.T = p.T; a.t_new = t_new; a.n_q = p.n_q; a.n_kv = p.n_kv; a.d = p.d;
             a.blk = rowscale(ssq_x, 0); a.ctx = rowscale(ssq_c, 0);
             a.q_norm = lw.q_norm; a.k_norm = lw.k_norm; a.eps = eps;
-            a.theta = cfg->rope_theta; a.ctx_len = ctx_len; a.valid = valid;
+            a.log2_theta = log2((double)cfg->rope_theta); a.ctx_len = ctx_len; a.valid = valid;
             a.Q = x.at<uint16_t>(p.o_Q); a.Kb = x.at<uint16_t>(p.o_Kb); a.Vb = x.at<uint16_t>(p.o_Vb);
             a.k_cache = kc; a.v_cache = vc; a.cap = cache_cap;
             HIPCHK(launch_qk_norm_rope(a, x.st));

@@ -80,7 +80,8 @@ struct RopeArgs {
     int B, T, t_new, n_q, n_kv, d;
     RowScale blk, ctx;           // deferred input norms of the block rows and context rows
     const uint16_t *q_norm, *k_norm;
-    float eps, theta;
+    float eps;
+    double log2_theta;           // log2 of the rotary base
     const int32_t *ctx_len, *valid;
     uint16_t *Q, *Kb, *Vb;       // bf16 [B][T][heads][d]
     uint16_t *k_cache, *v_cache; // layer base, [B][n_kv][cap][d]

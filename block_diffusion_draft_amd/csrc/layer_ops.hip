@@ -318,9 +318,15 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
         if (lane < half) {
             x1 *= inv * bf16_to_f32(g[lane]);
             x2 *= inv * bf16_to_f32(g[lane + half]);
-            // rotation angle pos * theta^(-2 lane / d), evaluated in fp64
-            const double ang = (double)pos * pow((double)a.theta, -2.0 * lane / d);
-            const float c = (float)cos(ang), s = (float)sin(ang);
+            // rotation angle pos * theta^(-2 lane / d): the inverse frequency and the
+            // product in fp64, the angle reduced modulo 2 pi in fp64 (a two-term 2 pi;
+            // the fma rounds only the small remainder), then fp32 sine and cosine of the
+            // reduced angle (|r| <= pi, where the fp32 routines need no long reduction)
+            const double ang = (double)pos * exp2(-2.0 * lane / d * a.log2_theta);
+            const double k = rint(ang * 0.15915494309189535);              // ang / (2 pi)
+            const double rr = fma(-k, 2.4492935982947064e-16, fma(-k, 6.283185307179586, ang));
+            float s, c;
+            sincosf((float)rr, &s, &c);
             const float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
             x1 = y1;
             x2 = y2;
