@@ -304,16 +304,14 @@ struct Pieces {
 // k group ln / 16).  wbase: the column group's first tiled unit.
 template <int WF>
 __device__ __forceinline__ void wq_setup(const BigGemmArgs &a, int n0, int tid,
-                                         const unsigned char *(&wbase)[2], bool (&wok)[2]) {
+                                         const unsigned char *(&wbase)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int e = tid + NTH * i;
-        const int n = n0 + 16 * (e / 64) + (e & 15);
-        wok[i] = n < a.N;
+        const int n = min(n0 + 16 * (e / 64) + (e & 15), a.N - 1);   // (columns past N: the last)
         int nb;
-        const unsigned char *ws = seg_of(a, wok[i] ? n : a.N - 1, nb);
-        const int nn = (wok[i] ? n : a.N - 1) - nb;
-        wbase[i] = ws + (size_t)(nn >> 4) * (a.K / 256) *
+        const unsigned char *ws = seg_of(a, n, nb);
+        wbase[i] = ws + (size_t)((n - nb) >> 4) * (a.K / 256) *
                             (WF == 1 ? Q8_UNIT_BYTES : (WF == 2 ? Q4K_UNIT_BYTES : FP8_UNIT_BYTES));
     }
 }
@@ -363,9 +361,10 @@ __device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t v) {
 // ([2 (hi, lo)][2 ks][8][64], slot swz): task (column, k group kg) fills entry kg of its
 // column's fragment: ks = kg / 2, lane (column % 32) + 32 (kg % 2).  sub = stage % 8 (the
 // Q4_K sub-block, the Q8_0 block of the pair).  FP8: the codes' bf16 values only (no lo
-// term).  Columns past N store zeros.
+// term).  Columns past N decode the last column's bytes (wq_setup clamps them): their
+// products reach only output columns past N, which are never stored.
 template <int WF>
-__device__ __forceinline__ void wq_store(u32x4_t *Bb, const WRaw &rw, const bool (&wok)[2], int tid, int sub) {
+__device__ __forceinline__ void wq_store(u32x4_t *Bb, const WRaw &rw, int tid, int sub) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int e = tid + NTH * i, cg = e / 64, ln = e & 63;
@@ -402,8 +401,6 @@ __device__ __forceinline__ void wq_store(u32x4_t *Bb, const WRaw &rw, const bool
             const uint32_t m6 = ((bj4 & 63u) & lo4) | (((bj4 >> 4) | ((bj >> 6) << 4)) & ~lo4);
             split8(v, d * (float)s6, dmin * (float)m6, oh, ol);
         }
-        oh = wok[i] ? oh : zero;
-        ol = wok[i] ? ol : zero;
         const int kg = ln >> 4, col = 16 * cg + (ln & 15);
         const int li = (col & 31) + 32 * (kg & 1);
         const int at = ((kg >> 1) * 8 + (col >> 5)) * 64 + swz(li, kg);
@@ -585,8 +582,7 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
                 (void __attribute__((address_space(3))) *)(As + buf * AST + (wave + 8 * j) * 64), 16, 0, 0);
     };
     const unsigned char *wbase[2];
-    bool wok[2];
-    wq_setup<WF>(a, n0, tid, wbase, wok);
+    wq_setup<WF>(a, n0, tid, wbase);
 
     f32x16_t acc[FM][2];
 #pragma unroll
@@ -655,10 +651,10 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
             if constexpr (!DF) {
                 compute(Ab, Bb);
                 wait_one();
-                wq_store<WF>(Bn, rn1, wok, tid, sub);
+                wq_store<WF>(Bn, rn1, tid, sub);
             } else {
                 wait_one();
-                wq_store<WF>(Bn, rn1, wok, tid, sub);
+                wq_store<WF>(Bn, rn1, tid, sub);
                 compute(Ab, Bb);
             }
         };
@@ -668,7 +664,7 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
         issue_a(min(s0 + 1, s1 - 1), 1);
         wq_load<WF>(rb, wbase, tid, min(s0 + 1, s1 - 1));
         wait_one();
-        wq_store<WF>(Bs, ra, wok, tid, s0 & 7);
+        wq_store<WF>(Bs, ra, tid, s0 & 7);
         int st = s0;
         for (; st + 1 < s1; st += 2) {
             body(st, rb, ra);
