@@ -547,8 +547,9 @@ __global__ __launch_bounds__(NTH) void k_gemm_big_dma(BigGemmArgs a, BigSched sc
 // Q8_0 / Q4_K / FP8 weights, 32-deep K stages: A global -> LDS by direct loads through a ring
 // of QNS stages (the bf16 path's 64-byte row pieces and chunk swizzle), the raw weight
 // bytes of a stage loaded into registers two stages ahead (two register sets,
-// alternating) and decoded into the double-buffered (hi, lo) W tile after the current
-// stage's MFMAs.  Each k step multiplies the A operand by both terms of the weights.
+// alternating) and decoded into the double-buffered (hi, lo) W tile: after the current
+// stage's MFMAs by the waves of the first M half, before them by those of the second.
+// Each k step multiplies the A operand by both terms of the weights.
 constexpr int QNS = 3, QBKD = 32;
 
 // one tile piece over 32-deep stages [s0, s1)
@@ -644,13 +645,12 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
             issue_a(s2, (i + 2) % QNS);
             wq_load<WF>(rn2, wbase, tid, s2);
             asm volatile("" ::: "memory");                // (issued before the MFMAs)
-            // the decode waits for rn1 first
             const u32x4_t *Ab = As + (i % QNS) * AST, *Bb = Bs + (i & 1) * 2048;
             u32x4_t *Bn = Bs + ((i + 1) & 1) * 2048;
             const int sub = min(st + 1, s1 - 1) & 7;
             if constexpr (!DF) {
                 compute(Ab, Bb);
-                wait_one();
+                wait_one();                               // rn1 has landed
                 wq_store<WF>(Bn, rn1, tid, sub);
             } else {
                 wait_one();
