@@ -99,10 +99,10 @@ bool make_plan(const dflash_config *c, int B, int t_new, Plan &p) {
     if (p.lm_skinny) {
         head_runs(p.V, p.H, &p.head_nrun, &p.head_rc, &p.head_rt);
     } else if (big_gemm_ok(0, p.R, p.V, p.H)) {
-        // the many-row head: one run per N tile of its grid
+        // the many-row head: runs of one or two waves' columns within its tiles
         const BigGemmPlan hp = big_gemm_plan_grid(0, p.R, p.V, p.H);
-        p.head_nrun = hp.grid_x;
-        p.head_rc = hp.bn;
+        p.head_rc = big_gemm_head_run_cols(hp.bn);
+        p.head_nrun = (p.V + p.head_rc - 1) / p.head_rc;
     }
     if (p.head_rc > 512 || (p.head_rc & (p.head_rc - 1)) || p.head_nrun > 2048)
         p.head_nrun = p.head_rc = p.head_rt = 0;

@@ -105,6 +105,11 @@ __device__ __forceinline__ float fp8_col_scale(const BigGemmArgs &a, int n) {
     return reinterpret_cast<const float *>(ws + (size_t)rows * a.K)[n - nb];
 }
 
+// columns per run of the softmax statistics the many-row head leaves for the selector,
+// for waves of wn columns: one wave's columns, or two waves' (at most 2048 runs per row
+// of a 248320-row vocabulary)
+constexpr int big_head_run_cols(int wn) { return wn > 128 ? wn : 128; }
+
 // Epilogue: lane l of tile (i, j), register v holds row 8 (v / 4) + 4 (l / 32) + v % 4,
 // column l % 32.  With the row scale, it is computed once per row of the tile into LDS
 // (rinv, free once every wave has left the K loop).  CS: FP8 weights, whose row scale
@@ -140,11 +145,12 @@ __device__ __forceinline__ void store_tile(const BigGemmArgs &a, const f32x16_t 
         }
     }
     if (!CS && scale && a.rstat) {
-        // softmax statistics of the tile's columns per row (one column run per tile).
-        // Each wave stages a 32-row block of its values in LDS, lane (row, half) = (l % 32,
-        // l / 32) reduces half a row's WN columns serially (one shuffle joins the halves);
-        // the 4 waves
-        // of a row band merge through LDS; one thread per row writes the pair.
+        // softmax statistics per row of the tile's column runs of RC = max(WN, 128) columns
+        // (one or two waves' columns; the selector reads back only the runs that can hold
+        // a candidate, so finer runs cost it fewer logits).  Each wave stages a 32-row
+        // block of its values in LDS, lane (row, half) = (l % 32, l / 32) reduces half a
+        // row's WN columns serially (one shuffle joins the halves); the waves of a run
+        // merge through LDS; one thread per (row, run) writes the pair.
         float *ws = rinv + BM;                     // [BM][4 waves][2]
         // (row stride WN + 1: the 32 lanes of a half-wave read 32 banks)
         constexpr int TS = WN + 1;
@@ -182,20 +188,21 @@ __device__ __forceinline__ void store_tile(const BigGemmArgs &a, const f32x16_t 
             __builtin_amdgcn_wave_barrier();       // (the next block reuses the staging)
         }
         __syncthreads();
-        const int nrun = ceil_div(a.N, 4 * WN);
-        for (int r = tid; r < BM; r += NTH) {
-            if (m0 + r >= a.M) continue;
+        constexpr int RC = big_head_run_cols(WN), RPW = RC / WN, NRT = 4 / RPW;
+        const int nrun = ceil_div(a.N, RC);
+        for (int e = tid; e < BM * NRT; e += NTH) {
+            const int r = e / NRT, q = e % NRT, run = n0 / RC + q;
+            if (m0 + r >= a.M || run >= nrun) continue;   // (runs wholly past N: none)
             float M = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < 4; w++) M = fmaxf(M, ws[(r * 4 + w) * 2]);
+            for (int w = 0; w < RPW; w++) M = fmaxf(M, ws[(r * 4 + q * RPW + w) * 2]);
             float S = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; w++) {
-                const float m = ws[(r * 4 + w) * 2];
-                S += m == -INFINITY ? 0.f : ws[(r * 4 + w) * 2 + 1] * expf(m - M);
+            for (int w = 0; w < RPW; w++) {
+                const float m = ws[(r * 4 + q * RPW + w) * 2];
+                S += m == -INFINITY ? 0.f : ws[(r * 4 + q * RPW + w) * 2 + 1] * expf(m - M);
             }
-            *reinterpret_cast<float2 *>(a.rstat + 2 * ((size_t)(m0 + r) * nrun + n0 / (4 * WN))) =
-                make_float2(M, S);
+            *reinterpret_cast<float2 *>(a.rstat + 2 * ((size_t)(m0 + r) * nrun + run)) = make_float2(M, S);
         }
     }
 }
@@ -808,6 +815,8 @@ BigGemmPlan big_gemm_plan(int wf, int M, int N, int K) {
     p.part_bytes = (size_t)p.splits * M * N * 4;
     return p;
 }
+
+int big_gemm_head_run_cols(int bn) { return big_head_run_cols(32 * (bn / 128)); }
 
 bool big_gemm_ok(int wf, int M, int N, int K) {
     if (M < 1 || N < 16 || N % 16) return false;

@@ -266,6 +266,8 @@ struct BigGemmPlan {
     int gs;                      // > 0: grouped stream-K over groups of gs weight slabs
     size_t part_bytes;
 };
+// columns per run of the output head's softmax statistics on tiles bn columns wide
+int big_gemm_head_run_cols(int bn);
 bool big_gemm_ok(int wf, int M, int N, int K);
 // the schedule (grid with K splits, or stream-K) of least estimated time; wf as in BigGemmArgs
 BigGemmPlan big_gemm_plan(int wf, int M, int N, int K);
