@@ -93,6 +93,7 @@ __device__ void embed_row(const EmbedArgs &a, int row) {
 // v^2 goes to ssq[r][blockIdx.x], and with out the next GEMM's input bf16(v * gain)
 // (+ its bf16 residual in out_lo) goes to output row map(r).  The RMSNorm's 1 / rms is
 // applied by the consumer of that GEMM (RowScale).
+template <int RB>
 __device__ void reduce_rows_block(const ReduceRowsArgs &a, int cx, int r) {
     const float *part = a.part;
     const int splits = a.splits, M_out = a.M_out, N = a.N, pair = a.pair, add = a.add;
@@ -107,19 +108,20 @@ __device__ void reduce_rows_block(const ReduceRowsArgs &a, int cx, int r) {
     const size_t stride = (size_t)(pair ? 2 * M_out : M_out) * N;
     const float *p = part + (size_t)r * N + c0 + 4 * lane;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    // this wave's splits k = wave, wave + 4, ...: 4 of them in flight per batch (few
-    // registers, so more workgroups stay resident)
-    for (int k0 = wave; k0 < splits; k0 += 16) {
-        float4 va[4], vb[4];
+    // this wave's splits k = wave, wave + 4, ...: RB of them in flight per batch (8 where
+    // there are more than 16 splits: the down projection's 17 and the fc's 25 at batch 1
+    // then take one memory round trip; else 4, fewer registers, more resident waves)
+    for (int k0 = wave; k0 < splits; k0 += 4 * RB) {
+        float4 va[RB], vb[RB];
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
+        for (int u = 0; u < RB; u++) {
             const float *q = p + (size_t)min(k0 + 4 * u, splits - 1) * stride;
             va[u] = *reinterpret_cast<const float4 *>(q);
             vb[u] = pair ? *reinterpret_cast<const float4 *>(q + (size_t)pair * N)
                          : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
-        for (int u = 0; u < 4; u++)
+        for (int u = 0; u < RB; u++)
             if (k0 + 4 * u < splits) {
                 s.x += va[u].x + vb[u].x;
                 s.y += va[u].y + vb[u].y;
@@ -147,16 +149,18 @@ __device__ void reduce_rows_block(const ReduceRowsArgs &a, int cx, int r) {
 
 __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) { embed_row(a, blockIdx.x); }
 
+template <int RB>
 __global__ __launch_bounds__(256) void k_reduce_rows(ReduceRowsArgs a) {
-    reduce_rows_block(a, blockIdx.x, blockIdx.y);
+    reduce_rows_block<RB>(a, blockIdx.x, blockIdx.y);
 }
 
 // one launch for two independent jobs: the reduction's (N / 256) x M_out workgroups,
 // then the block assembly's B T workgroups
+template <int RB>
 __global__ __launch_bounds__(256) void k_reduce_rows_embed(ReduceRowsArgs a, EmbedArgs e) {
     const int nc = a.N / 256, nred = nc * a.M_out;
     const int bid = blockIdx.x;
-    if (bid < nred) reduce_rows_block(a, bid % nc, bid / nc);
+    if (bid < nred) reduce_rows_block<RB>(a, bid % nc, bid / nc);
     else embed_row(e, bid - nred);
 }
 
@@ -198,25 +202,42 @@ __global__ __launch_bounds__(256) void k_reduce(const float *part, int splits, i
     }
 }
 
+// row_inv for a whole wave (every lane calls it, same r): lane i loads partial i (and
+// i + 64, ...), the partials are added by a wave reduction
+__device__ __forceinline__ float row_inv_wave(const RowScale &s, int r, int lane) {
+    if (!s.ssq) return 1.f;
+    const int br = s.map ? (r / (s.map - 1)) * s.map + r % (s.map - 1) + 1 : r;
+    const float *p = s.ssq + (size_t)br * s.nchunk;
+    float ss = 0.f;
+    for (int i = lane; i < s.nchunk; i += 64) ss += p[i];
+    return rsqrtf(wave_sum(ss) / s.n + s.eps);
+}
+
 // ---------------------------------------------------------------- SwiGLU from split partials
 // Workgroup per (1024 columns, output row r), four consecutive columns per thread
 // (16-byte loads, three splits in flight): gate and up (columns c and c + N/2 of the [gate | up] product) summed
 // over the splits (in split order) and the [hi; lo] row pair, scaled by the row's
-// deferred 1 / rms (formed once per workgroup), then silu(gate) * up as a bf16 (hi, lo)
-// pair.  Needs N / 2 a multiple of 4.
+// deferred 1 / rms (formed once per workgroup by its first wave, one load per lane),
+// then silu(gate) * up as a bf16 (hi, lo) pair.  SB splits' loads in flight per batch
+// (6 where there are more than 3 splits: one round trip for batch 1's 5).  Needs N / 2
+// a multiple of 4.
+template <int SB>
 __global__ __launch_bounds__(256) void k_swiglu(const float *part, int splits, int M, int N, int pair,
                                                 uint16_t *ob, uint16_t *ob_lo, int ldo, RowScale rs) {
     const int r = blockIdx.y, c = 4 * (blockIdx.x * 256 + threadIdx.x);
     const int F = N / 2;
     __shared__ float s_inv;
-    if (threadIdx.x == 0) s_inv = row_inv(rs, r);
+    if (threadIdx.x < 64) {
+        const float ri = row_inv_wave(rs, r, threadIdx.x);
+        if (threadIdx.x == 0) s_inv = ri;
+    }
     const size_t stride = (size_t)(pair ? 2 * M : M) * N;
     const float *p = part + (size_t)r * N + min(c, F - 4);
     float4 gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < splits; k0 += 3) {
-        float4 gv[3], uv[3], gq[3], uq[3];
+    for (int k0 = 0; k0 < splits; k0 += SB) {
+        float4 gv[SB], uv[SB], gq[SB], uq[SB];
 #pragma unroll
-        for (int u = 0; u < 3; u++) {
+        for (int u = 0; u < SB; u++) {
             const float *p0 = p + (size_t)min(k0 + u, splits - 1) * stride;
             gv[u] = *reinterpret_cast<const float4 *>(p0);
             uv[u] = *reinterpret_cast<const float4 *>(p0 + F);
@@ -225,7 +246,7 @@ __global__ __launch_bounds__(256) void k_swiglu(const float *part, int splits, i
             uq[u] = pair ? *reinterpret_cast<const float4 *>(p0 + (size_t)pair * N + F) : z;
         }
 #pragma unroll
-        for (int u = 0; u < 3; u++)
+        for (int u = 0; u < SB; u++)
             if (k0 + u < splits) {
                 gs.x += gv[u].x + gq[u].x; gs.y += gv[u].y + gq[u].y;
                 gs.z += gv[u].z + gq[u].z; gs.w += gv[u].w + gq[u].w;
@@ -250,17 +271,6 @@ __global__ __launch_bounds__(256) void k_swiglu(const float *part, int splits, i
     if (ob_lo)
         *reinterpret_cast<u32x2_t *>(ob_lo + (size_t)r * ldo + c) =
             (u32x2_t){(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
-}
-
-// row_inv for a whole wave (every lane calls it, same r): lane i loads partial i (and
-// i + 64, ...), the partials are added by a wave reduction
-__device__ __forceinline__ float row_inv_wave(const RowScale &s, int r, int lane) {
-    if (!s.ssq) return 1.f;
-    const int br = s.map ? (r / (s.map - 1)) * s.map + r % (s.map - 1) + 1 : r;
-    const float *p = s.ssq + (size_t)br * s.nchunk;
-    float ss = 0.f;
-    for (int i = lane; i < s.nchunk; i += 64) ss += p[i];
-    return rsqrtf(wave_sum(ss) / s.n + s.eps);
 }
 
 // ---------------------------------------------------------------- q/k norm, rotary, append
@@ -288,11 +298,12 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
     const size_t pstride = (size_t)a.B * (a.T + a.t_new) * (qd + 2 * kd);
     float x1 = 0.f, x2 = 0.f;
     if (lane < half) {
-        // up to 4 splits of loads in flight per batch, only the splits present
-        for (int s0 = 0; s0 < a.splits; s0 += 4) {
-            float v1[4], v2[4];
+        // up to 8 splits of loads in flight per batch (one round trip for the 5 splits
+        // of the q|k|v product at batch 1), only the splits present
+        for (int s0 = 0; s0 < a.splits; s0 += 8) {
+            float v1[8], v2[8];
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
+            for (int u = 0; u < 8; u++) {
                 v1[u] = v2[u] = 0.f;
                 if (s0 + u < a.splits) {
                     v1[u] = x[(s0 + u) * pstride + lane];
@@ -300,7 +311,7 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
+            for (int u = 0; u < 8; u++) {
                 x1 += v1[u];
                 x2 += v2[u];
             }
@@ -579,8 +590,12 @@ hipError_t launch_reduce_epilogue(const float *part, int splits, int M, int N, i
 hipError_t launch_swiglu(const float *part, int splits, int M, int N, int pair, uint16_t *out,
                          uint16_t *out_lo, int ldo, const RowScale &rs, hipStream_t st) {
     if ((N / 2) % 4 || ldo % 4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_swiglu, dim3(ceil_div(N / 2, 1024), M), dim3(256), 0, st, part, splits, M, N,
-                       pair, out, out_lo, ldo, rs);
+    if (splits > 3)
+        hipLaunchKernelGGL(k_swiglu<6>, dim3(ceil_div(N / 2, 1024), M), dim3(256), 0, st, part, splits, M,
+                           N, pair, out, out_lo, ldo, rs);
+    else
+        hipLaunchKernelGGL(k_swiglu<3>, dim3(ceil_div(N / 2, 1024), M), dim3(256), 0, st, part, splits, M,
+                           N, pair, out, out_lo, ldo, rs);
     return hipGetLastError();
 }
 
@@ -605,7 +620,8 @@ hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_reduce_norm(const ReduceRowsArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(k_reduce_rows, dim3(a.N / 256, a.M_out), dim3(256), 0, st, a);
+    if (a.splits > 16) hipLaunchKernelGGL(k_reduce_rows<8>, dim3(a.N / 256, a.M_out), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(k_reduce_rows<4>, dim3(a.N / 256, a.M_out), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -619,6 +635,7 @@ hipError_t launch_reduce_norm(const float *part, int splits, int M_out, int N, i
 hipError_t launch_reduce_norm_embed(const ReduceRowsArgs &a, const EmbedArgs &e, int B,
                                     hipStream_t st) {
     const int grid = (a.N / 256) * a.M_out + B * e.T;
-    hipLaunchKernelGGL(k_reduce_rows_embed, dim3(grid), dim3(256), 0, st, a, e);
+    if (a.splits > 16) hipLaunchKernelGGL(k_reduce_rows_embed<8>, dim3(grid), dim3(256), 0, st, a, e);
+    else hipLaunchKernelGGL(k_reduce_rows_embed<4>, dim3(grid), dim3(256), 0, st, a, e);
     return hipGetLastError();
 }
