@@ -22,6 +22,8 @@
 namespace {
 
 constexpr int F8_SG = 4;        // K-groups of 256 per split of the streaming kernel
+constexpr int F8_AHEAD = 3;     // stages a wave's loads run ahead of their use (ring of F8_SG)
+static_assert(F8_AHEAD >= 1 && F8_AHEAD < F8_SG, "the ring holds the stage in use and those ahead");
 
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(64 * WPG) void k_f8_stream(Q4kFusedArgs a) {
     // values k = (g0 + sg) 256 + 32 j + 8 g .. + 7 (rows >= M: zeros); loaded before the
     // first weight stages so that their wait does not include the weights' latency
     constexpr int PER = F8_SG * 8 / WPG;
-    F8Stage st[4];
+    F8Stage st[F8_SG];
     {
         const int Rc = min(cl, a.M - 1);
         const uint16_t *arow = a.src.A + (size_t)Rc * a.src.lda + (size_t)g0 * 256 + 8 * g;
@@ -146,9 +148,10 @@ __global__ __launch_bounds__(64 * WPG) void k_f8_stream(Q4kFusedArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
         const unsigned char *b0 = tile_base(t0);
+        // (written out: as a loop over the ring the loads lose their non-temporal hint)
         st[0] = f8_load(b0, lane);
-        st[1] = f8_load(b0 + FP8_UNIT_BYTES, lane);
-        st[2] = f8_load(b0 + 2 * FP8_UNIT_BYTES, lane);
+        if (F8_AHEAD > 1) st[1] = f8_load(b0 + FP8_UNIT_BYTES, lane);
+        if (F8_AHEAD > 2) st[2] = f8_load(b0 + 2 * FP8_UNIT_BYTES, lane);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < PER; i++)
@@ -172,9 +175,10 @@ __global__ __launch_bounds__(64 * WPG) void k_f8_stream(Q4kFusedArgs a) {
         f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sg = 0; sg < F8_SG; sg++) {
-            st[(sg + 3) & 3] = sg == 0 ? f8_load(bcur + 3 * FP8_UNIT_BYTES, lane)
-                                       : f8_load(more ? bnext + (sg - 1) * FP8_UNIT_BYTES
-                                                      : bcur + 3 * FP8_UNIT_BYTES, lane);
+            const int ns = sg + F8_AHEAD;           // stage loaded now: (t, ns) or (t + 1, ns - 4)
+            st[ns % F8_SG] = ns < F8_SG ? f8_load(bcur + ns * FP8_UNIT_BYTES, lane)
+                                        : f8_load(more ? bnext + (ns - F8_SG) * FP8_UNIT_BYTES
+                                                       : bcur + (F8_SG - 1) * FP8_UNIT_BYTES, lane);
             __builtin_amdgcn_sched_barrier(0);
             const F8Stage &w = st[sg];
 #pragma unroll

@@ -217,9 +217,10 @@ __device__ __forceinline__ float row_inv_wave(const RowScale &s, int r, int lane
 // Workgroup per (1024 columns, output row r), four consecutive columns per thread
 // (16-byte loads, three splits in flight): gate and up (columns c and c + N/2 of the [gate | up] product) summed
 // over the splits (in split order) and the [hi; lo] row pair, scaled by the row's
-// deferred 1 / rms (formed once per workgroup by its first wave, one load per lane),
-// then silu(gate) * up as a bf16 (hi, lo) pair.  SB splits' loads in flight per batch
-// (6 where there are more than 3 splits: one round trip for batch 1's 5).  Needs N / 2
+// deferred 1 / rms (formed once per workgroup), then silu(gate) * up as a bf16 (hi, lo)
+// pair.  SB splits' loads in flight per batch: 6 where there are more than 3 splits (one
+// round trip for batch 1's 5; the 1 / rms then comes from the first wave, one load per
+// lane), else 3 (1 / rms from one thread: measured faster at 64 sequences).  Needs N / 2
 // a multiple of 4.
 template <int SB>
 __global__ __launch_bounds__(256) void k_swiglu(const float *part, int splits, int M, int N, int pair,
@@ -227,9 +228,13 @@ __global__ __launch_bounds__(256) void k_swiglu(const float *part, int splits, i
     const int r = blockIdx.y, c = 4 * (blockIdx.x * 256 + threadIdx.x);
     const int F = N / 2;
     __shared__ float s_inv;
-    if (threadIdx.x < 64) {
-        const float ri = row_inv_wave(rs, r, threadIdx.x);
-        if (threadIdx.x == 0) s_inv = ri;
+    if (SB > 3) {
+        if (threadIdx.x < 64) {
+            const float ri = row_inv_wave(rs, r, threadIdx.x);
+            if (threadIdx.x == 0) s_inv = ri;
+        }
+    } else if (threadIdx.x == 0) {
+        s_inv = row_inv(rs, r);
     }
     const size_t stride = (size_t)(pair ? 2 * M : M) * N;
     const float *p = part + (size_t)r * N + min(c, F - 4);
@@ -274,7 +279,10 @@ __global__ __launch_bounds__(256) void k_swiglu(const float *part, int splits, i
 }
 
 // ---------------------------------------------------------------- q/k norm, rotary, append
-// One wave per (row, head).  Lane j < d/2 owns the rotary pair (j, j + d/2).
+// One wave per (row, head).  Lane j < d/2 owns the rotary pair (j, j + d/2).  QB splits'
+// loads in flight per batch: 8 where the product has more than 4 splits (one round trip
+// for the 5 of the q|k|v product at batch 1), else 4.
+template <int QB>
 __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
     const int r = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
     const int d = a.d, half = d / 2;
@@ -298,12 +306,11 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
     const size_t pstride = (size_t)a.B * (a.T + a.t_new) * (qd + 2 * kd);
     float x1 = 0.f, x2 = 0.f;
     if (lane < half) {
-        // up to 8 splits of loads in flight per batch (one round trip for the 5 splits
-        // of the q|k|v product at batch 1), only the splits present
-        for (int s0 = 0; s0 < a.splits; s0 += 8) {
-            float v1[8], v2[8];
+        // only the splits present
+        for (int s0 = 0; s0 < a.splits; s0 += QB) {
+            float v1[QB], v2[QB];
 #pragma unroll
-            for (int u = 0; u < 8; u++) {
+            for (int u = 0; u < QB; u++) {
                 v1[u] = v2[u] = 0.f;
                 if (s0 + u < a.splits) {
                     v1[u] = x[(s0 + u) * pstride + lane];
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(64) void k_qk_norm_rope(RopeArgs a) {
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 8; u++) {
+            for (int u = 0; u < QB; u++) {
                 x1 += v1[u];
                 x2 += v2[u];
             }
@@ -601,7 +608,8 @@ hipError_t launch_swiglu(const float *part, int splits, int M, int N, int pair, 
 
 hipError_t launch_qk_norm_rope(const RopeArgs &a, hipStream_t st) {
     dim3 grid(a.B * (a.T + a.t_new), a.n_q + 2 * a.n_kv);
-    hipLaunchKernelGGL(k_qk_norm_rope, grid, dim3(64), 0, st, a);
+    if (a.splits > 4) hipLaunchKernelGGL(k_qk_norm_rope<8>, grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL(k_qk_norm_rope<4>, grid, dim3(64), 0, st, a);
     return hipGetLastError();
 }
 

@@ -26,9 +26,9 @@
 // activation rows are staged once in LDS in MFMA lane order; their sub-block sums
 // come from the staging lanes (a sum of 8 and two lane exchanges), and each lane keeps
 // the bias operands it needs in registers.  Each wave then streams its tiles'
-// super-blocks as one flat sequence of (tile, super-block) stages, 4 stages in
-// flight, in a branch-free loop (loads past the end are clamped to the last stage,
-// in bounds and unused), so the loads stay in flight across tiles.  The weights are
+// super-blocks as one flat sequence of (tile, super-block) stages, loaded SAHEAD
+// stages ahead of their use in a branch-free loop (loads past the end are clamped to
+// the last stage, in bounds and unused), so the loads stay in flight across tiles.  The weights are
 // read once, with non-temporal loads.  Each tile's partial is stored when its 4
 // super-blocks are done; for a (hi, lo) row pair the two halves are added first.
 // Workgroups never communicate; a reduction kernel sums the splits.
@@ -38,6 +38,12 @@
 namespace {
 
 constexpr int SNSB = 4;        // super-blocks per split
+// stages a wave's loads run ahead of their use (the ring holds SNSB stages).  Measured at
+// batch 1: 2 ahead is fastest (gate|up 18.3 -> 17.6 us, down 21.5 -> 20.8 us against 3
+// ahead, the whole step 0.860 -> 0.851 ms); 4 ahead was slower still than 3 (gate|up
+// 23.6 -> 25.2 us): more bytes in flight per wave do not raise the stream's rate.
+constexpr int SAHEAD = 2;
+static_assert(SAHEAD >= 1 && SAHEAD < SNSB, "the ring holds the stage in use and those ahead");
 
 struct SStage {
     u32x4_t hdr;               // d, dmin, 12 scale bytes of column cl's block
@@ -99,11 +105,11 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a) {
     const int tlast = (t1 > t0 ? t1 : ntile) - 1;       // clamp target, always a real tile
 
     // ---- weight stream.  Stage (tile t, super-block sb) is the unit at tile_base(t)
-    // + sb * 2304; loads run 3 stages ahead, so tile t's loop issues (t, 3) and
-    // (t + 1, 0..2).  In the run's last tile the three loads ahead re-read unit (t, 3),
-    // just requested, so they hit in L2 (in bounds, unused; re-reading the tile's first
-    // units instead, evicted by then, cost 3 units of HBM traffic per wave: 14 MB per
-    // gate|up launch).
+    // + sb * 2304; loads run SAHEAD stages ahead, so tile t's loop issues (t, SAHEAD ..
+    // 3) and (t + 1, 0 .. SAHEAD - 1).  In the run's last tile the loads ahead re-read
+    // unit (t, 3), just requested, so they hit in L2 (in bounds, unused; re-reading the
+    // tile's first units instead, evicted by then, cost that many units of HBM traffic
+    // per wave: 14 MB per gate|up launch at 3 ahead).
     auto tile_base = [&](int t) -> const unsigned char * {
         const int tt = t < t1 ? t : tlast;
         const int c16 = tt * 16;
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a) {
     // (loaded before the first weight stages: the wait for them then does not include
     // the weights' HBM latency, which overlaps the staging instead)
     constexpr int PER = SNSB * 8 / WPG;             // entries per thread
-    SStage st[4];
+    SStage st[SNSB];
     {
         const int Rc = min(cl, a.M - 1);
         const uint16_t *arow = a.src.A + (size_t)Rc * a.src.lda + (size_t)sb0 * 256 + 8 * g;
@@ -132,9 +138,10 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
         const unsigned char *b0 = tile_base(t0);
+        // (written out: as a loop over the ring the loads lose their non-temporal hint)
         st[0] = stage(b0, 0);
-        st[1] = stage(b0, 1);
-        st[2] = stage(b0, 2);
+        if (SAHEAD > 1) st[1] = stage(b0, 1);
+        if (SAHEAD > 2) st[2] = stage(b0, 2);
         __builtin_amdgcn_sched_barrier(0);
         // sub-block sums S[sbi][j][r] of the staged rows: each lane adds its 8 values
         // (bf16 -> fp32 is exact), then the 4 lanes holding a row's sub-block add theirs
@@ -192,8 +199,10 @@ __global__ __launch_bounds__(64 * WPG) void k_q4k_stream(Q4kFusedArgs a) {
         f32x4_t acc = zero;
 #pragma unroll
         for (int sb = 0; sb < SNSB; sb++) {
-            st[(sb + 3) & 3] = sb == 0 ? stage(bcur, 3) : stage(more ? bnext : bcur, more ? sb - 1 : 3);
-            // keep the loads here, 3 stages ahead of their use (left alone, the
+            const int ns = sb + SAHEAD;             // stage loaded now: (t, ns) or (t + 1, ns - 4)
+            st[ns % SNSB] = ns < SNSB ? stage(bcur, ns)
+                                      : stage(more ? bnext : bcur, more ? ns - SNSB : SNSB - 1);
+            // keep the loads here, SAHEAD stages ahead of their use (left alone, the
             // scheduler sinks them to the end of the tile and the latency shows)
             __builtin_amdgcn_sched_barrier(0);
             const SStage &w = st[sb];

@@ -29,6 +29,8 @@
 namespace {
 
 constexpr int Q8_SG = 4;        // K-groups of 256 per split of the streaming kernel
+constexpr int Q8_AHEAD = 3;     // stages a wave's loads run ahead of their use (ring of Q8_SG)
+static_assert(Q8_AHEAD >= 1 && Q8_AHEAD < Q8_SG, "the ring holds the stage in use and those ahead");
 
 __global__ __launch_bounds__(256) void k_q8_0_dequant(const unsigned char *w, float *out,
                                                       long long n) {
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(64 * WPG) void k_q8_stream(Q4kFusedArgs a) {
     // values k = (g0 + sg) 256 + 32 j + 8 g .. + 7 (rows >= M: zeros); loaded before the
     // first weight stages so that their wait does not include the weights' latency
     constexpr int PER = Q8_SG * 8 / WPG;
-    Q8Stage st[4];
+    Q8Stage st[Q8_SG];
     {
         const int Rc = min(cl, a.M - 1);
         const uint16_t *arow = a.src.A + (size_t)Rc * a.src.lda + (size_t)g0 * 256 + 8 * g;
@@ -150,9 +152,10 @@ __global__ __launch_bounds__(64 * WPG) void k_q8_stream(Q4kFusedArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
         const unsigned char *b0 = tile_base(t0);
+        // (written out: as a loop over the ring the loads lose their non-temporal hint)
         st[0] = stage(b0, 0);
-        st[1] = stage(b0, 1);
-        st[2] = stage(b0, 2);
+        if (Q8_AHEAD > 1) st[1] = stage(b0, 1);
+        if (Q8_AHEAD > 2) st[2] = stage(b0, 2);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < PER; i++)
@@ -187,7 +190,9 @@ __global__ __launch_bounds__(64 * WPG) void k_q8_stream(Q4kFusedArgs a) {
         f32x4_t acc = zero;
 #pragma unroll
         for (int sg = 0; sg < Q8_SG; sg++) {
-            st[(sg + 3) & 3] = sg == 0 ? stage(bcur, 3) : stage(more ? bnext : bcur, more ? sg - 1 : 3);
+            const int ns = sg + Q8_AHEAD;           // stage loaded now: (t, ns) or (t + 1, ns - 4)
+            st[ns % Q8_SG] = ns < Q8_SG ? stage(bcur, ns)
+                                        : stage(more ? bnext : bcur, more ? ns - Q8_SG : Q8_SG - 1);
             __builtin_amdgcn_sched_barrier(0);
             const Q8Stage &w = st[sg];
 #pragma unroll
