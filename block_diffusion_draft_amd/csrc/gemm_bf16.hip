@@ -4,11 +4,11 @@
 //    steps of 32 staged through double-buffered LDS in MFMA lane order.  Used for
 //    the unquantised drafter matrices at many rows and for the shared output head
 //    when more than 16 rows need logits.
-//  * skinny: at most 8 rows (the 7 proposal rows of one draft block).  The rows
-//    sit in LDS for the whole launch; every wave streams its own contiguous run
-//    of 16-row weight tiles over the full K with 8 fragment loads in flight, so
-//    the output head (248320 x 5120 bf16, the bulk of the step's bytes) is read
-//    exactly once with 16-byte loads and no cross-wave reduction.
+//  * the streaming head (k_head_stream): at most 8 rows (the 7 proposal rows of one
+//    draft block), K a multiple of 256.  The rows sit in LDS for the whole launch;
+//    every wave streams its own run of 16-row weight tiles over the full K with
+//    whole-line loads, so the output head (248320 x 5120 bf16, the bulk of the
+//    step's bytes) is read exactly once with no cross-wave reduction.
 #include "common.h"
 #include "kernels.h"
 
@@ -109,95 +109,6 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(Bf16GemmArgs a) {
         }
 }
 
-// Skinny product for at most 8 activation rows (one block's 7 proposal rows).
-// The rows live in LDS for the whole launch, already in MFMA lane order, so each
-// wave can run the full K of its own weight tiles with no cross-wave reduction.
-// Each wave owns a contiguous range of 16-row weight tiles and streams them as a
-// flat sequence of (tile, k-step) fragments with LM_PD loads in flight.
-constexpr int LM_PD = 8;
-
-__global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a, int tiles_per_wave) {
-    extern __shared__ __align__(16) u32x4_t Alds[];   // [nks][32] lanes with row < 8, + 1 zero entry
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, c = lane & 15;
-    const int nks = a.K / 32;                        // a multiple of LM_PD
-    const int ntiles = a.N / 16;
-    const int t0 = (blockIdx.x * 4 + wave) * tiles_per_wave;
-    const int t1 = min(t0 + tiles_per_wave, ntiles);
-    const int steps = t1 > t0 ? (t1 - t0) * nks : 0;
-
-    // flat stream of fragments (tile, k-step); loads past the wave's range are
-    // clamped to its last fragment (in bounds, value unused)
-    const uint16_t *W = a.w[0] + (size_t)c * a.K + 8 * g;
-    const size_t tile_stride = (size_t)16 * a.K;
-    int lt = t0, lk = 0, nload = 0;
-    auto load_next = [&]() -> u32x4_t {
-        const bool ok = nload < steps;
-        const int tt = ok ? lt : t1 - 1, kk = ok ? lk : nks - 1;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(W + (size_t)tt * tile_stride + kk * 32);
-        nload++;
-        lk++;
-        const bool wrap = lk == nks;
-        lk = wrap ? 0 : lk;
-        lt += wrap ? 1 : 0;
-        return v;
-    };
-    u32x4_t eb[LM_PD];
-    if (steps > 0) {
-#pragma unroll
-        for (int u = 0; u < LM_PD - 1; u++) eb[u] = load_next();
-    }
-    for (int e = tid; e < nks * 32 + 1; e += 256) {
-        const int ks = e >> 5, slot = e & 31, gg = slot >> 3, r = slot & 7;
-        u32x4_t v = {0, 0, 0, 0};
-        if (e < nks * 32 && r < a.M)
-            v = *reinterpret_cast<const u32x4_t *>(a.A + (size_t)r * a.lda + ks * 32 + 8 * gg);
-        Alds[e] = v;
-    }
-    __syncthreads();
-
-    // deferred RMSNorm of the rows this lane stores (rows 4g + v, g < 2): computed for
-    // all 8 rows with wave-uniform (scalar) loads, which do not wait behind the weight
-    // loads already in flight
-    float inv8[8];
-#pragma unroll
-    for (int r = 0; r < 8; r++) inv8[r] = r < a.M ? row_inv(a.rs, r) : 0.f;
-    float rinv[4];
-#pragma unroll
-    for (int v = 0; v < 4; v++) rinv[v] = g == 0 ? inv8[v] : (g == 1 ? inv8[4 + v] : 0.f);
-
-    // running softmax statistics of this wave's columns, per row (lane-uniform)
-    float rmax[8], rsum[8];
-#pragma unroll
-    for (int m = 0; m < 8; m++) {
-        rmax[m] = -INFINITY;
-        rsum[m] = 0.f;
-    }
-    // lanes of rows >= 8 read the zero entry
-    const int aoff = c < 8 ? g * 8 + c : 0;
-    const int astep = c < 8 ? 32 : 0;
-    const int abase = c < 8 ? 0 : nks * 32;
-    for (int tile = t0; tile < t1; tile++) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int ks0 = 0; ks0 < nks; ks0 += LM_PD) {
-#pragma unroll
-            for (int u = 0; u < LM_PD; u++) {
-                eb[(u + LM_PD - 1) % LM_PD] = load_next();
-                const u32x4_t af = Alds[abase + (ks0 + u) * astep + aoff];
-                acc = mfma16x16x32(af, eb[u], acc);
-            }
-        }
-        if (g < 2) {
-            const int n = tile * 16 + c;
-#pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const int m = 4 * g + v;
-                if (m < a.M) a.C[(size_t)m * a.ldc + n] = acc[v] * rinv[v];
-            }
-        }
-    }
-}
-
 // Output head for at most 8 activation rows, weights read as whole cache lines.
 // One workgroup of 8 waves per CU; the rows sit in LDS in MFMA lane order.  The N / 16
 // weight tiles are dealt to the grid's waves in balanced runs (wave w of nw takes tiles
@@ -208,7 +119,9 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a, int ti
 // group's 4 loads reads 4 rows x 256 contiguous bytes (non-temporal: read once), so
 // every load covers full lines.  The group passes through a 4 KB per-wave LDS buffer
 // (16-byte chunks XOR-swizzled by row: conflict-free writes and fragment reads) into
-// MFMA lane order.  Groups are loaded HS_D - 1 ahead in registers, across tiles.
+// MFMA lane order.  Groups are loaded HS_D - 1 ahead in registers, across tiles: one
+// ahead streamed the 2.54 GB of the 27B drafter's head at 6.65 TB/s, three ahead at 6.52
+// and four at 6.51 (batch-1 step, interleaved on one box).
 // The outputs of up to 8 consecutive tiles stay in registers and are then written as
 // 128 consecutive columns per row (lanes over columns, whole lines): written tile by
 // tile in the MFMA layout, the rows' 64-byte pieces cost the stream about 8%.
@@ -216,7 +129,7 @@ __global__ __launch_bounds__(256) void k_bf16_gemm_skinny(Bf16GemmArgs a, int ti
 // row: the run's max M and sum of exp(v - M) over the values it wrote (merged across
 // its output batches), the pair at rstat[2 (row nrun + wave index)].
 constexpr int HS_WAVES = 8;
-constexpr int HS_D = 4;
+constexpr int HS_D = 2;
 constexpr int HS_TB = 8;           // tiles per output batch
 
 __global__ __launch_bounds__(512) void k_head_stream(Bf16GemmArgs a) {
@@ -432,6 +345,7 @@ void head_runs(int N, int K, int *nrun, int *run_cols, int *run_tiles) {
     *run_tiles = ntiles;
 }
 
+// K must be a multiple of 128 HS_D (else hipErrorInvalidValue)
 hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st) {
     const int ntiles = a.N / 16;
     if (a.K % (128 * HS_D) == 0) {
@@ -448,17 +362,5 @@ hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st) {
         hipLaunchKernelGGL(k_head_stream, dim3(waves / HS_WAVES), dim3(512), lds, st, a);
         return hipGetLastError();
     }
-    if (a.rstat) return hipErrorInvalidValue;            // (statistics: the kernel above only)
-    const int tpw = ceil_div(ntiles, 2048);               // ~2048 waves, 2 workgroups per CU
-    const int waves = ceil_div(ntiles, tpw);
-    const size_t lds = ((size_t)(a.K / 32) * 32 + 1) * 16;
-    static size_t lds_set = 0;
-    if (lds > 65536 && lds > lds_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_bf16_gemm_skinny,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        lds_set = lds;
-    }
-    hipLaunchKernelGGL(k_bf16_gemm_skinny, dim3(ceil_div(waves, 4)), dim3(256), lds, st, a, tpw);
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }

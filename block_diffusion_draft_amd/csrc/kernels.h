@@ -33,14 +33,14 @@ struct Bf16GemmArgs {
 };
 // tiled 128x128 MFMA GEMM, any M
 hipError_t launch_bf16_gemm_tiled(const Bf16GemmArgs &a, hipStream_t st);
-// rows <= 8, one weight matrix (nseg == 1): activations resident in LDS, every wave
-// streams whole weight tiles
+// rows <= 8, one weight matrix (nseg == 1), K a multiple of 256 (else
+// hipErrorInvalidValue): activations resident in LDS, every wave streams whole weight tiles
 hipError_t launch_bf16_gemm_skinny(const Bf16GemmArgs &a, hipStream_t st);
 // Column runs of the skinny head's softmax statistics for an N x K head: wave w of the
 // streaming head kernel's nrun waves covers the 16-column tiles [w T / nrun, (w + 1) T /
 // nrun) of the T = run_tiles tiles (at most run_cols columns, a power of two) and, given
 // a.rstat, writes per row r the pair (max, sum exp(v - max)) of its run at
-// rstat[2 (r nrun + w)].  run_cols 0: the shape takes the kernel without statistics.
+// rstat[2 (r nrun + w)].  run_cols 0: the streaming head does not take the shape.
 void head_runs(int N, int K, int *nrun, int *run_cols, int *run_tiles);
 
 // ---------------------------------------------------------------- layer ops
