@@ -21,8 +21,9 @@
 //
 // Work split: a workgroup (8 waves) owns one split of 4 super-blocks (1024 values
 // of K); the split's column tiles are dealt to its waves in balanced runs (wave w of
-// the split's nw takes tiles [w T / nw, (w + 1) T / nw)), and the grid has about one
-// workgroup per CU, so every CU streams nearly the same number of bytes.  The split's
+// the split's nw takes tiles [w T / nw, (w + 1) T / nw)), and the grid has about two
+// workgroups per CU where the matrix has the tiles for it, so every CU streams nearly the
+// same number of bytes.  The split's
 // activation rows are staged once in LDS in MFMA lane order; their sub-block sums
 // come from the staging lanes (a sum of 8 and two lane exchanges), and each lane keeps
 // the bias operands it needs in registers.  Each wave then streams its tiles'
@@ -260,7 +261,7 @@ Q4kStreamPlan q4k_stream_plan(int M, int N, int K, int pair, int target_waves, i
     // 3-7% faster than 4 waves at every drafter shape)
     p.wpg = wpg > 0 ? wpg : 8;
     wpg = p.wpg;
-    // about target_waves waves in all (one 8-wave workgroup per CU at the default), and
+    // about target_waves waves in all (two 8-wave workgroups per CU at the default), and
     // no more workgroups per split than it has tiles for a wave each
     p.grid_x = max(1, min(target_waves / (wpg * p.splits), ceil_div(ntile, wpg)));
     p.tpw = ceil_div(ntile, p.grid_x * wpg);            // (the longest run)
