@@ -217,6 +217,7 @@ hipError_t launch_q8_0_to_tiled(const unsigned char *src, unsigned char *dst, in
 // streaming GEMM for M <= 16 rows, K a multiple of 1024 (splits of 4 K-groups), the same
 // plan fields and partial layout as the Q4_K streaming kernel (a.KB = K / 256)
 bool q8_stream_ok(int M, int N, int K);
+// (2048 waves: 4096 measured 0.3% slower on the batch-1 step)
 Q4kStreamPlan q8_stream_plan(int M, int N, int K, int pair = 0, int target_waves = 2048,
                              int wpg = 0);
 hipError_t launch_q8_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st);
@@ -233,6 +234,7 @@ hipError_t launch_fp8_to_tiled(const unsigned char *src, unsigned char *dst, int
 // streaming GEMM for M <= 16 rows, K a multiple of 1024, the plan fields and partial
 // layout of the Q4_K streaming kernel (a.KB = K / 256); the row scales are applied
 bool f8_stream_ok(int M, int N, int K);
+// (2048 waves: 4096 measured 0.7% slower on the batch-1 step)
 Q4kStreamPlan f8_stream_plan(int M, int N, int K, int pair = 0, int target_waves = 2048,
                              int wpg = 0);
 hipError_t launch_f8_stream(const Q4kFusedArgs &a, const Q4kStreamPlan &p, hipStream_t st);
