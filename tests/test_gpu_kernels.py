@@ -127,6 +127,18 @@ def test_q4k_gemm_row_counts(M):
     gemm_check(w, x, N, K, M)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 16, 1024), (8, 16, 2048), (3, 48, 1024), (16, 48, 2048),
+                                   (8, 272, 2048), (16, 272, 4096)])
+def test_q4k_gemm_stream_few_tiles(M, N, K):
+    """The streaming kernel (up to 16 rows, K a multiple of 1024) where a split has fewer
+    column tiles than its workgroup has waves (1, 3 and 17 tiles for 8 waves): the waves
+    without a tile only run their clamped loads, the others their runs."""
+    say(f"[q4k_gemm stream] M={M} {N}x{K}")
+    w = synth.q4k_normal(9, "few", N, K, 0.02)
+    x = synth.normal_bf16(9, "few.x", (M, K), 1.0)
+    gemm_check(w, x, N, K, M)
+
+
 @pytest.mark.parametrize("M,N,K", [(160, 4096, 4096), (256, 8704, 5120), (136, 34816, 4096),
                                    (512, 34816, 2048), (1000, 8704, 4096)])
 def test_q4k_gemm_schedules(M, N, K):
