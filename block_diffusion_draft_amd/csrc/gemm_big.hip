@@ -22,8 +22,9 @@
 // W) travel global -> LDS by direct loads (global_load_lds_dwordx4: no registers, no
 // LDS store instructions) through a ring of K stages, the next ones in flight while one
 // is multiplied (bf16: 64-deep stages, a ring of 2, for the 256 x 256 and 128 x 512
-// tiles; 32-deep, a ring of 4, for 128 x 256); Q8_0 / Q4_K weights are loaded into
-// registers two stages ahead and decoded into a double-buffered LDS tile of (hi, lo)
+// tiles; 32-deep, a ring of 4, for 128 x 256); Q8_0 / FP8 weights are loaded into
+// registers two stages ahead, Q4_K weights by direct loads into a ring of raw LDS slots
+// four stages ahead, and either is decoded into a double-buffered LDS tile of (hi, lo)
 // operands.
 //
 // Work split: a grid over (N tile, M tile, K split), or stream-K where the tiles would
@@ -696,6 +697,210 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
     store_tile<BM, FM, 2, WF == 3>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot, scale);
 }
 
+// Q4_K weights with their raw bytes staged in LDS instead of registers, so that they can
+// be requested further ahead.  A raw "half" H covers the 4 sub-blocks 4 (H % 2) .. + 3 of
+// super-block H / 2 (128 values of K): per 16-column group, the 1 KB of quant slots of
+// that half of the tiled unit and the unit's 256-byte header area.  Wave w requests the
+// halves of column groups w and w + 8, which are exactly the groups its lanes decode,
+// so a wave only ever reads raw bytes it requested itself.  Halves go into a ring of 2
+// slots; half H + 2 is requested after the barrier of stage 4 H + 3, once the last
+// decode from half H (stage 4 H + 3, decoded during stage 4 H + 2) is done, and is first
+// decoded during stage 4 H + 7: four stages of lead, where the register sets of q_piece
+// gave one (at 16 sequences the stage time sat at the HBM latency, ~4700 cycles for
+// ~1500 of matrix-core work).  Every other step is q_piece's, and the decode is
+// wq_store<2> on the same bytes, so the results are bit-identical to it.
+constexpr int RAW_SLOT = 16 * 64 + 16 * 16;          // u32x4 entries of one raw half slot
+
+template <int BM>
+__device__ __forceinline__ void q4k_piece(const BigGemmArgs &a, u32x4_t *lds, int m0, int n0, int s0,
+                                          int s1, int slot, bool scale) {
+    constexpr int WF = 2;
+    constexpr int RG = BM / 32, WM = BM / 2, FM = WM / 32;
+    constexpr int PA = 2 * RG / 8;                    // A load instructions per wave and stage
+    constexpr int AST = RG * 128;                     // entries of one A stage
+    constexpr int PR = 4;                             // raw load instructions per wave and half
+    u32x4_t *As = lds;                                // [QNS][RG][128]
+    u32x4_t *Bs = lds + QNS * AST;                    // [2][2 (hi, lo)][2 ks][8][64]
+    u32x4_t *Rs = Bs + 2 * 2048;                      // [2 slots][16 groups x 64 quant slots,
+                                                      //           16 groups x 16 headers]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+
+    const uint16_t *asrc[PA];
+#pragma unroll
+    for (int j = 0; j < PA; j++) {
+        const int h = wave + 8 * j;
+        const int g = h >> 1, row = 16 * (h & 1) + (lane >> 2);
+        const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+        asrc[j] = a.A + (size_t)min(m0 + 32 * g + row, a.M - 1) * a.lda + 8 * chunk;
+    }
+    auto issue_a = [&](int st, int buf) {
+#pragma unroll
+        for (int j = 0; j < PA; j++)
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1))) *)(asrc[j] + st * QBKD),
+                (void __attribute__((address_space(3))) *)(As + buf * AST + (wave + 8 * j) * 64), 16, 0, 0);
+    };
+    // first tiled unit of column groups wave and wave + 8 (groups past N: the last one,
+    // in bounds; their columns are never stored)
+    const unsigned char *wcg[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int n = min(n0 + 16 * (wave + 8 * i), a.N - 1);
+        int nb;
+        const unsigned char *ws = seg_of(a, n, nb);
+        wcg[i] = ws + (size_t)((n - nb) >> 4) * (a.K / 256) * Q4K_UNIT_BYTES;
+    }
+    const int h_last = (s1 - 1) >> 2;
+    // half H (past the piece's last: that one again, into a slot no later decode reads
+    // before it is rewritten) into slot H % 2: quant slots by 16-byte lanes, headers by
+    // 4-byte lanes (64 dwords = the unit's 16 headers)
+    auto issue_raw = [&](int H) {
+        const int Hc = min(H, h_last);
+        u32x4_t *R = Rs + (H & 1) * RAW_SLOT;
+        const size_t off = (size_t)(Hc >> 1) * Q4K_UNIT_BYTES;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int cg = wave + 8 * i;
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1))) *)(wcg[i] + off + 256 + 1024 * (Hc & 1) + 16 * lane),
+                (void __attribute__((address_space(3))) *)(R + cg * 64), 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int cg = wave + 8 * i;
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1))) *)(wcg[i] + off + 4 * lane),
+                (void __attribute__((address_space(3))) *)(R + 16 * 64 + cg * 16), 4, 0, 0);
+        }
+    };
+    // the raw bytes of stage st for this thread's two tasks (column group wave + 8 i,
+    // fragment lane `lane`), from half st / 4, as wq_load<2> would have loaded them
+    auto raw_of = [&](int st) -> WRaw {
+        const u32x4_t *R = Rs + ((st >> 2) & 1) * RAW_SLOT;
+        const int c = (st & 7) >> 1;
+        WRaw rw;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int cg = wave + 8 * i;
+            const u32x2_t q = reinterpret_cast<const u32x2_t *>(R + cg * 64 + lane)[c & 1];
+            rw.v[2 * i] = (u32x4_t){q.x, q.y, 0u, 0u};
+            rw.v[2 * i + 1] = R[16 * 64 + cg * 16 + (lane & 15)];
+        }
+        return rw;
+    };
+
+    f32x16_t acc[FM][2];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+
+    const int rl = lane & 31;
+    const int rp0 = dma_pos<QBKD>(rl, lane >> 5), rp1 = dma_pos<QBKD>(rl, 2 + (lane >> 5));
+    auto wait_vm = [&](auto n_tag) {
+        constexpr int n = decltype(n_tag)::value;
+        static_assert(n < 64, "vmcnt holds 6 bits");
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(vm_wait(n));
+        asm volatile("" ::: "memory");
+    };
+    using IA = std::integral_constant<int, PA>;
+    using IAR = std::integral_constant<int, PA + PR>;
+
+    // Loads in issue order: stage st issues A(st + 2), then, when st % 4 == 3, half
+    // st / 4 + 2.  The wait at the end of stage st lets through what was issued after
+    // A(st + 1) (issued during stage st - 1): A(st + 2), and the halves issued during
+    // stages st - 1 and st; so A(st + 1) and every half issued before it, including the
+    // one decoded during stage st + 1 (half (st + 2) / 4, issued by stage st - 3), have
+    // landed before the barrier of stage st + 1.
+    auto run = [&](auto lo_tag, auto df_tag) {
+        constexpr bool TWO = !decltype(lo_tag)::value;
+        constexpr bool DF = decltype(df_tag)::value;
+        auto compute = [&](const u32x4_t *Ab, const u32x4_t *Bb) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                const int c = 2 * ks + (lane >> 5), rp = ks ? rp1 : rp0;
+                u32x4_t bh[2], bl[2];
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    bh[j] = Bb[(ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
+                    if constexpr (TWO) bl[j] = Bb[1024 + (ks * 8 + wn * 2 + j) * 64 + swz(lane, c)];
+                }
+#pragma unroll
+                for (int i = 0; i < FM; i++) {
+                    const u32x4_t af = Ab[(wm * FM + i) * 128 + rp];
+#pragma unroll
+                    for (int j = 0; j < 2; j++) {
+                        acc[i][j] = mfma32x32x16(af, bh[j], acc[i][j]);
+                        if constexpr (TWO) acc[i][j] = mfma32x32x16(af, bl[j], acc[i][j]);
+                    }
+                }
+            }
+        };
+        auto decode = [&](u32x4_t *Bn, int st) {
+            const WRaw rw = raw_of(st);
+            wq_store<WF>(Bn, rw, tid, st & 7);
+        };
+        // prologue: A(s0), A(s0 + 1) and the halves of stages s0 .. s0 + 4, ordered as
+        // the stage loop would have issued them (s0 is even: s0 % 4 is 0 or 2)
+        const int H0 = s0 >> 2;
+        if ((s0 & 3) == 0) {
+            issue_a(s0, 0);
+            issue_raw(H0);
+            issue_a(min(s0 + 1, s1 - 1), 1);
+            issue_raw(H0 + 1);
+            wait_vm(IAR());                           // A(s0), half H0
+        } else {
+            issue_raw(H0);
+            issue_raw(H0 + 1);
+            issue_a(s0, 0);
+            issue_a(min(s0 + 1, s1 - 1), 1);
+            wait_vm(IA());                            // halves H0, H0 + 1, A(s0)
+        }
+        decode(Bs, s0);
+        for (int st = s0; st < s1; st++) {
+            const int i = st - s0, ph = st & 3;
+            __builtin_amdgcn_s_waitcnt(0xC07F);       // this wave's LDS reads and stores done
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            issue_a(min(st + 2, s1 - 1), (i + 2) % QNS);
+            if (ph == 3) issue_raw((st >> 2) + 2);
+            asm volatile("" ::: "memory");            // (issued before the MFMAs)
+            const u32x4_t *Ab = As + (i % QNS) * AST, *Bb = Bs + (i & 1) * 2048;
+            u32x4_t *Bn = Bs + ((i + 1) & 1) * 2048;
+            const bool more = st + 1 < s1;
+            if constexpr (!DF) {
+                compute(Ab, Bb);
+                if (more) decode(Bn, st + 1);
+            } else {
+                if (more) decode(Bn, st + 1);
+                compute(Ab, Bb);
+            }
+            if (ph == 0 || ph == 3) wait_vm(IAR());
+            else wait_vm(IA());
+        }
+    };
+    using T = std::integral_constant<bool, true>;
+    using F = std::integral_constant<bool, false>;
+    const bool lo = a.lo_row > 0 && m0 + wm * WM >= a.lo_row;
+    if (lo) {
+        if (wm) run(T(), T());
+        else run(T(), F());
+    } else {
+        if (wm) run(F(), T());
+        else run(F(), F());
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);      // no load may land after the piece ends
+
+    store_tile<BM, FM, 2, false>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot, scale);
+}
+
 template <int WF, int BM>
 __global__ __launch_bounds__(NTH) void k_gemm_big_q(BigGemmArgs a, BigSched sc) {
     extern __shared__ __align__(16) u32x4_t lds[];
@@ -703,7 +908,10 @@ __global__ __launch_bounds__(NTH) void k_gemm_big_q(BigGemmArgs a, BigSched sc) 
     Piece pc;
     for (bool first = true; it.next<BM>(a, sc, pc); first = false) {
         if (!first) __syncthreads();                  // the previous piece is done with LDS
-        q_piece<WF, BM>(a, lds, pc.m0, pc.n0, 2 * pc.s0, 2 * pc.s1, pc.slot, pc.scale);
+        if constexpr (WF == 2)
+            q4k_piece<BM>(a, lds, pc.m0, pc.n0, 2 * pc.s0, 2 * pc.s1, pc.slot, pc.scale);
+        else
+            q_piece<WF, BM>(a, lds, pc.m0, pc.n0, 2 * pc.s0, 2 * pc.s1, pc.slot, pc.scale);
         if (pc.last) zero_slots<BM>(a, pc.m0, pc.n0, pc.slot + 1, sc.slots, threadIdx.x);
     }
 }
@@ -715,7 +923,10 @@ size_t dma_lds_bytes(int BM, int TBN) {
     const int bkd = BM == 256 ? dma_bkd<256, 256>() : TBN == 512 ? dma_bkd<128, 512>() : dma_bkd<128, 256>();
     return (size_t)dma_ring(BM, TBN, bkd) * (BM + TBN) * 2 * bkd;
 }
-size_t q_lds_bytes(int BM) { return ((size_t)QNS * BM * 4 + 2 * 2048) * 16; }
+size_t q_lds_bytes(int wf, int BM) {
+    // A ring + decoded (hi, lo) W double buffer; Q4_K adds its two raw half slots
+    return ((size_t)QNS * BM * 4 + 2 * 2048 + (wf == 2 ? 2 * RAW_SLOT : 0)) * 16;
+}
 
 namespace {
 
@@ -841,13 +1052,13 @@ hipError_t launch_big_gemm(const BigGemmArgs &a, const BigGemmPlan &p, hipStream
         lb = dma_lds_bytes(p.bm, p.bn);
     } else if (a.wfmt == 1) {
         fn = bi ? (const void *)k_gemm_big_q<1, 256> : (const void *)k_gemm_big_q<1, 128>;
-        lb = q_lds_bytes(p.bm);
+        lb = q_lds_bytes(a.wfmt, p.bm);
     } else if (a.wfmt == 3) {
         fn = bi ? (const void *)k_gemm_big_q<3, 256> : (const void *)k_gemm_big_q<3, 128>;
-        lb = q_lds_bytes(p.bm);
+        lb = q_lds_bytes(a.wfmt, p.bm);
     } else {
         fn = bi ? (const void *)k_gemm_big_q<2, 256> : (const void *)k_gemm_big_q<2, 128>;
-        lb = q_lds_bytes(p.bm);
+        lb = q_lds_bytes(a.wfmt, p.bm);
     }
     // (the LDS limit is raised once per device and kernel)
     static bool attr_set[64][4][2][2] = {};
