@@ -155,6 +155,20 @@ def test_q4k_gemm_schedules(M, N, K):
     gemm_check(w, x, N, K, M)
 
 
+@pytest.mark.parametrize("M,N,K", [(40, 272, 256), (17, 272, 512), (256, 272, 768),
+                                   (40, 16640, 1024)])
+def test_q4k_gemm_many_rows_short_k(M, N, K):
+    """Many-row GEMM over 1-4 super-blocks: its raw weight bytes go through two LDS
+    slots of half a super-block each, requested four 32-deep stages ahead, so pieces of
+    8, 16 and 24 stages request halves past their end (clamped to the last one); the
+    last shape runs as a grid of 3 K splits of 5, 5 and 6 64-deep units, the second
+    starting in the middle of a half super-block."""
+    say(f"[q4k_gemm many rows short K] M={M} {N}x{K}")
+    w = synth.q4k_normal(10, "shortk", N, K, 0.02)
+    x = synth.normal_bf16(10, "shortk.x", (M, K), 1.0)
+    gemm_check(w, x, N, K, M)
+
+
 def test_q4k_gemm_one_block_edge():
     """Smallest shape: one super-block, one column tile."""
     N, K, M = 16, 256, 2
