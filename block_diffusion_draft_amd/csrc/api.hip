@@ -187,9 +187,13 @@ struct Ctx {
 };
 
 // The many-row GEMM (more than 16 rows) into partials [splits][M][N]; returns the
-// number of splits or a negative status.
+// number of splits or a negative status.  With pair > 0, rows r and r + pair are the
+// (hi, lo) halves of one activation row; *folded is set when the kernel adds them itself
+// (each M tile then takes half a tile of hi rows and their lo rows), leaving partials of
+// M / 2 rows.
 int run_big(int wfmt, const void *const *w, const int *seg_end, int nseg, const uint16_t *A,
-            int lda, int M, int N, int K, float *part, hipStream_t st, int pair = 0) {
+            int lda, int M, int N, int K, float *part, hipStream_t st, int pair = 0,
+            bool *folded = nullptr) {
     BigGemmArgs g = {};
     g.lo_row = pair;
     for (int i = 0; i < 3; i++) {
@@ -207,6 +211,8 @@ int run_big(int wfmt, const void *const *w, const int *seg_end, int nseg, const 
     g.ldc = N;
     const BigGemmPlan p = big_gemm_plan(wfmt, M, N, K);
     HIPCHK(launch_big_gemm(g, p, st));
+    // (the kernels' own test: whole half tiles of hi rows, 256-column tiles)
+    if (folded) *folded = pair > 0 && 2 * pair == M && pair % (p.bm / 2) == 0 && p.bn == 256;
     return p.splits;
 }
 
@@ -226,8 +232,11 @@ int run_quant(int fmt, const Q4kFusedArgs &a, hipStream_t st, int *pair_left) {
     }
     if (use_big(fmt, a.M, a.N, K)) {
         const void *w[3] = {a.w[0], a.w[1], a.w[2]};
-        return run_big(big_fmt(fmt), w, a.seg_end, a.nseg, a.src.A, a.src.lda, a.M, a.N, K,
-                       a.part, st, a.pair);
+        bool folded = false;
+        const int splits = run_big(big_fmt(fmt), w, a.seg_end, a.nseg, a.src.A, a.src.lda, a.M,
+                                   a.N, K, a.part, st, a.pair, &folded);
+        if (folded) *pair_left = 0;
+        return splits;
     }
     return DFLASH_ESHAPE;      // (every valid quantised shape takes one of the two above)
 }
@@ -266,7 +275,10 @@ int run_gemm(const Ctx &x, const void *const *w, const int *seg_n, int nseg, con
     }
     if (use_big(DFLASH_W_BF16, M, N, K)) {
         const void *wv[3] = {w[0], nseg > 1 ? w[1] : w[0], nseg > 2 ? w[2] : w[0]};
-        return run_big(0, wv, seg_end, nseg, A, lda, M, N, K, part, x.st);
+        bool folded = false;
+        const int splits = run_big(0, wv, seg_end, nseg, A, lda, M, N, K, part, x.st, pair, &folded);
+        if (folded) *pair_left = 0;
+        return splits;
     }
     Bf16GemmArgs a = {};
     for (int i = 0; i < 3; i++) {

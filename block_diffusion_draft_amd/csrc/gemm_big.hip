@@ -115,13 +115,59 @@ constexpr int big_head_run_cols(int wn) { return wn > 128 ? wn : 128; }
 // column l % 32.  With the row scale, it is computed once per row of the tile into LDS
 // (rinv, free once every wave has left the K loop).  CS: FP8 weights, whose row scale
 // multiplies each output column.
+// (hi, lo) pair fold.  When the activation rows are (hi, lo) pairs, row r and its lo row
+// lo_row + r (the MLP products of the batched steps), and the hi rows come in whole
+// half tiles, each M tile takes BM / 2 hi rows and their lo rows (act_row), and the
+// waves of the second M half pass their accumulators through LDS, one 32-row block at a
+// time (32 KB), to the wave of the first half that holds the same columns, which adds
+// them: hi + lo, the sum the reduction would otherwise form from a partial twice the
+// size (the same two fp32 terms, so the same result).  The lane layouts of the two
+// waves match row for row; the tile's output rows are m0 / 2 .. m0 / 2 + BM / 2 - 1.
+__device__ __forceinline__ bool fold_pairs_here(const BigGemmArgs &a, int BM) {
+    return a.lo_row > 0 && 2 * a.lo_row == a.M && a.lo_row % (BM / 2) == 0;
+}
+// activation row of tile row L (L = m0 + local row): with folding, M tile t holds hi rows
+// [t BM/2, (t + 1) BM/2) in its first half and their lo rows in its second half (the
+// activations are stored [hi rows; lo rows]); else row L itself
+__device__ __forceinline__ int act_row(const BigGemmArgs &a, int L, int BM, bool fold) {
+    if (!fold) return L;
+    const int t = L / BM, r = L - t * BM, h = BM / 2;
+    return r < h ? t * h + r : a.lo_row + t * h + (r - h);
+}
+template <int FM>
+__device__ __forceinline__ void fold_pairs(f32x16_t (&acc)[FM][2], float *xf, int wm, int wn, int lane) {
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+        __syncthreads();                    // (first block: every wave is done with its operands)
+        if (wm) {
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) xf[((wn * 2 + j) * 16 + v) * 64 + lane] = acc[i][j][v];
+        }
+        __syncthreads();
+        if (!wm) {
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) acc[i][j][v] += xf[((wn * 2 + j) * 16 + v) * 64 + lane];
+        }
+    }
+}
+
+// Folded (fold_pairs): the tile's second M half held the lo rows of the first half's
+// (hi, lo) activation pairs and has been added into it; only the first half's waves
+// store, as rows m0 / 2 + r of a partial of M / 2 rows.
 template <int BM, int FM, int FN = 2, bool CS = false>
 __device__ __forceinline__ void store_tile(const BigGemmArgs &a, const f32x16_t (&acc)[FM][FN],
                                            float *rinv, int m0, int n0, int wm, int wn, int tid,
-                                           int slot, bool scale) {
+                                           int slot, bool scale, bool folded = false) {
     constexpr int WM = BM / 2, WN = 32 * FN;
     const int lane = tid & 63, hl = lane >> 5, c = lane & 31;
-    float *C = a.C + (size_t)slot * a.M * a.ldc;
+    if (folded && wm) return;
+    const int m_rows = folded ? a.M / 2 : a.M;
+    if (folded) m0 /= 2;
+    float *C = a.C + (size_t)slot * m_rows * a.ldc;
     float cs[FN];
 #pragma unroll
     for (int j = 0; j < FN; j++) cs[j] = CS ? fp8_col_scale(a, n0 + wn * WN + 32 * j + c) : 1.f;
@@ -135,7 +181,7 @@ __device__ __forceinline__ void store_tile(const BigGemmArgs &a, const f32x16_t 
 #pragma unroll
         for (int v = 0; v < 16; v++) {
             const int r = wm * WM + 32 * i + 8 * (v >> 2) + 4 * hl + (v & 3);
-            if (m0 + r >= a.M) continue;
+            if (m0 + r >= m_rows) continue;
             const float ri = scale ? rinv[r] : 1.f;
 #pragma unroll
             for (int j = 0; j < FN; j++) {
@@ -210,12 +256,15 @@ __device__ __forceinline__ void store_tile(const BigGemmArgs &a, const f32x16_t 
 
 // zeroes slots [from, to) of a tile (N and ldc are multiples of 4)
 template <int BM, int TBN = BN>
-__device__ __forceinline__ void zero_slots(const BigGemmArgs &a, int m0, int n0, int from, int to, int tid) {
+__device__ __forceinline__ void zero_slots(const BigGemmArgs &a, int m0, int n0, int from, int to, int tid,
+                                           bool folded = false) {
+    const int m_rows = folded ? a.M / 2 : a.M, rows = folded ? BM / 2 : BM;
+    if (folded) m0 /= 2;
     for (int z = from; z < to; z++) {
-        float *C = a.C + (size_t)z * a.M * a.ldc;
-        for (int e = tid; e < BM * TBN / 4; e += NTH) {
+        float *C = a.C + (size_t)z * m_rows * a.ldc;
+        for (int e = tid; e < rows * TBN / 4; e += NTH) {
             const int m = m0 + e / (TBN / 4), n = n0 + 4 * (e % (TBN / 4));
-            if (m < a.M && n < a.N)
+            if (m < m_rows && n < a.N)
                 *reinterpret_cast<float4 *>(C + (size_t)m * a.ldc + n) = make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
@@ -458,6 +507,7 @@ __device__ __forceinline__ void dma_piece(const BigGemmArgs &a, u32x4_t *lds, in
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
+    const bool fold = FN == 2 && fold_pairs_here(a, BM);
 
     // this lane's source pointer for each of the wave's load instructions (k of stage added)
     const uint16_t *src[PW];
@@ -468,7 +518,7 @@ __device__ __forceinline__ void dma_piece(const BigGemmArgs &a, u32x4_t *lds, in
         const int sw = BKD == 32 ? (row >> 2) & 3 : (row >> 1) & 7;
         const int chunk = (lane % CH) ^ sw;
         if (g < RG) {
-            const int r = min(m0 + 32 * g + row, a.M - 1);
+            const int r = act_row(a, min(m0 + 32 * g + row, a.M - 1), BM, fold);
             src[j] = a.A + (size_t)r * a.lda + 8 * chunk;
         } else {
             const int n = min(n0 + 32 * (g - RG) + row, a.N - 1);
@@ -535,7 +585,11 @@ __device__ __forceinline__ void dma_piece(const BigGemmArgs &a, u32x4_t *lds, in
     }
     __builtin_amdgcn_s_waitcnt(0xF70);      // no load may land after the piece ends
 
-    store_tile<BM, FM, FN>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot, scale);
+    if constexpr (FN == 2) {
+        if (fold) fold_pairs<FM>(acc, reinterpret_cast<float *>(lds), wm, wn, lane);
+    }
+    store_tile<BM, FM, FN>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot,
+                           scale && !fold, fold);
 }
 
 template <int BM, int TBN>
@@ -548,7 +602,8 @@ __global__ __launch_bounds__(NTH) void k_gemm_big_dma(BigGemmArgs a, BigSched sc
         constexpr int BKD = dma_bkd<BM, TBN>(), SPB = BK / BKD;   // stages per 64-deep unit
         dma_piece<BM, dma_ns<BM, TBN>(), TBN, BKD>(a, lds, pc.m0, pc.n0, SPB * pc.s0, SPB * pc.s1,
                                                     pc.slot, pc.scale);
-        if (pc.last) zero_slots<BM, TBN>(a, pc.m0, pc.n0, pc.slot + 1, sc.slots, threadIdx.x);
+        if (pc.last) zero_slots<BM, TBN>(a, pc.m0, pc.n0, pc.slot + 1, sc.slots, threadIdx.x,
+                                         TBN == 256 && fold_pairs_here(a, BM));
     }
 }
 
@@ -574,6 +629,7 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
+    const bool folded = fold_pairs_here(a, BM);
 
     const uint16_t *asrc[PA];
 #pragma unroll
@@ -581,7 +637,7 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
         const int h = wave + 8 * j;                   // 1 KB half: group h / 2, rows 16 (h % 2) ..
         const int g = h >> 1, row = 16 * (h & 1) + (lane >> 2);
         const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-        asrc[j] = a.A + (size_t)min(m0 + 32 * g + row, a.M - 1) * a.lda + 8 * chunk;
+        asrc[j] = a.A + (size_t)act_row(a, min(m0 + 32 * g + row, a.M - 1), BM, folded) * a.lda + 8 * chunk;
     }
     auto issue_a = [&](int st, int buf) {
 #pragma unroll
@@ -684,7 +740,8 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
     // made the register allocation spill)
     using T = std::integral_constant<bool, true>;
     using F = std::integral_constant<bool, false>;
-    const bool lo = a.lo_row > 0 && m0 + wm * WM >= a.lo_row;
+    // (folded: every tile's second M half holds lo rows)
+    const bool lo = a.lo_row > 0 && (folded ? wm == 1 : m0 + wm * WM >= a.lo_row);
     if (lo) {
         if (wm) run(T(), T());
         else run(T(), F());
@@ -694,7 +751,9 @@ __device__ __forceinline__ void q_piece(const BigGemmArgs &a, u32x4_t *lds, int 
     }
     __builtin_amdgcn_s_waitcnt(0xF70);      // no load may land after the piece ends
 
-    store_tile<BM, FM, 2, WF == 3>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot, scale);
+    if (folded) fold_pairs<FM>(acc, reinterpret_cast<float *>(lds), wm, wn, lane);
+    store_tile<BM, FM, 2, WF == 3>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot,
+                                   scale && !folded, folded);
 }
 
 // Q4_K weights with their raw bytes staged in LDS instead of registers, so that they can
@@ -727,6 +786,7 @@ __device__ __forceinline__ void q4k_piece(const BigGemmArgs &a, u32x4_t *lds, in
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
+    const bool folded = fold_pairs_here(a, BM);
 
     const uint16_t *asrc[PA];
 #pragma unroll
@@ -734,7 +794,7 @@ __device__ __forceinline__ void q4k_piece(const BigGemmArgs &a, u32x4_t *lds, in
         const int h = wave + 8 * j;
         const int g = h >> 1, row = 16 * (h & 1) + (lane >> 2);
         const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-        asrc[j] = a.A + (size_t)min(m0 + 32 * g + row, a.M - 1) * a.lda + 8 * chunk;
+        asrc[j] = a.A + (size_t)act_row(a, min(m0 + 32 * g + row, a.M - 1), BM, folded) * a.lda + 8 * chunk;
     }
     auto issue_a = [&](int st, int buf) {
 #pragma unroll
@@ -888,7 +948,8 @@ __device__ __forceinline__ void q4k_piece(const BigGemmArgs &a, u32x4_t *lds, in
     };
     using T = std::integral_constant<bool, true>;
     using F = std::integral_constant<bool, false>;
-    const bool lo = a.lo_row > 0 && m0 + wm * WM >= a.lo_row;
+    // (folded: every tile's second M half holds lo rows)
+    const bool lo = a.lo_row > 0 && (folded ? wm == 1 : m0 + wm * WM >= a.lo_row);
     if (lo) {
         if (wm) run(T(), T());
         else run(T(), F());
@@ -898,7 +959,9 @@ __device__ __forceinline__ void q4k_piece(const BigGemmArgs &a, u32x4_t *lds, in
     }
     __builtin_amdgcn_s_waitcnt(0xF70);      // no load may land after the piece ends
 
-    store_tile<BM, FM, 2, false>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot, scale);
+    if (folded) fold_pairs<FM>(acc, reinterpret_cast<float *>(lds), wm, wn, lane);
+    store_tile<BM, FM, 2, false>(a, acc, reinterpret_cast<float *>(lds), m0, n0, wm, wn, tid, slot,
+                                 scale && !folded, folded);
 }
 
 template <int WF, int BM>
@@ -912,7 +975,7 @@ __global__ __launch_bounds__(NTH) void k_gemm_big_q(BigGemmArgs a, BigSched sc) 
             q4k_piece<BM>(a, lds, pc.m0, pc.n0, 2 * pc.s0, 2 * pc.s1, pc.slot, pc.scale);
         else
             q_piece<WF, BM>(a, lds, pc.m0, pc.n0, 2 * pc.s0, 2 * pc.s1, pc.slot, pc.scale);
-        if (pc.last) zero_slots<BM>(a, pc.m0, pc.n0, pc.slot + 1, sc.slots, threadIdx.x);
+        if (pc.last) zero_slots<BM>(a, pc.m0, pc.n0, pc.slot + 1, sc.slots, threadIdx.x, fold_pairs_here(a, BM));
     }
 }
 

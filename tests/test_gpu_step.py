@@ -247,6 +247,7 @@ def test_mid_step_streaming_products(fmt, head_dim, batch):
 
 
 @pytest.mark.parametrize("fmt,batch,vocab", [("q4k", 4, 0), ("q8_0", 4, 0), ("bf16", 4, 0),
+                                             ("q4k", 8, 0), ("q8_0", 16, 0),
                                              ("q4k", 128, 0), ("fp8", 128, 0),
                                              ("bf16", 128, 16 * 4133),
                                              ("bf16", 16, 16 * 8229)])
@@ -254,7 +255,10 @@ def test_mid_step_many_rows(fmt, batch, vocab):
     """Many sequences of a 2-layer drafter: every product has more than 16 rows and runs
     on the many-row GEMM with the format's weight decode.  4 sequences: 32 block rows, 64
     with the context rows or the (hi, lo) pairs, split-K where the tiles are few, the
-    output head (28 rows) with the deferred final norm in its epilogue.  128 sequences:
+    output head (28 rows) with the deferred final norm in its epilogue.  8 and 16
+    sequences (quantised): the MLP products are one 128- or 256-row tile of 64 or 128
+    rows and their lo rows, which the kernel adds itself (partials of half the rows).
+    128 sequences:
     1024 block rows over 4 row tiles, 2048 MLP rows over 8, the 896-row head, and (bf16)
     a vocabulary of 4133 16-column tiles whose last 256-column head tile is ragged.  16
     sequences, bf16, a vocabulary of 8229 16-column tiles: the 112-row head on 128 x 512
