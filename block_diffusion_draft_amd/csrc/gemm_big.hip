@@ -1,7 +1,8 @@
 // Dense-contraction GEMM for many activation rows (the batched draft steps), gfx950:
 // C[slot][M][N] (fp32) = A[M][K] (bf16) . W[N][K]^T over the slot's share of K, with W
 // in bf16, Q8_0, Q4_K or FP8 (tiled layouts of q8_0.hip / q4k_tiled.hip / fp8.hip).  The consumers sum
-// the slots (reduce kernels), as for every other GEMM of the step.
+// the slots (reduce kernels), as for every other GEMM of the step; (hi, lo) activation
+// row pairs are added by the GEMM itself where they fill whole half tiles (fold_pairs).
 //
 // At 100+ rows the drafter's products are MFMA-bound (2 M flops per weight against
 // 0.56-2 bytes), so the weights are decoded once per 256 x 256 output tile into bf16
