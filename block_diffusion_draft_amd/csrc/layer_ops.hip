@@ -524,6 +524,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(MergeConvArgs a) {
 //   z_t[h], z_t[n_q + h] for the two heads = sums of the (h', cc) partials;
 //   y_{t,h} = z_t[h] o_{t,h} + z_t[n_q + h] o_{t-1,h},  o_{-1} = 0.
 constexpr int CONV_HEADS = 2;       // heads per conv workgroup
+// block rows from which k_conv_rows takes the taps: measured at 64 sequences (512 rows)
+// 6.287 -> 6.250 ms per step, at 16 (128 rows) 2.759 -> 2.775 ms, so from 512
+constexpr int CONV_ROWS_MIN = 512;
 
 __global__ __launch_bounds__(256) void k_conv_apply(MergeConvArgs a) {
     __shared__ float z[2 * CONV_HEADS];
@@ -571,6 +574,57 @@ __global__ __launch_bounds__(256) void k_conv_apply(MergeConvArgs a) {
         if (i < i1) {
             const int k = (i - i0) / a.d;
             Y[i] = f32_to_bf16(z[k] * ocur[u] + (t > 0 ? z[CONV_HEADS + k] * oprev[u] : 0.f));
+        }
+    }
+}
+
+// k_conv_rows: the same taps and outputs with one workgroup per (sequence b, block row
+// t), for batches large enough to fill the chip with rows.  The row's partials
+// ([B][n_q][d/32][T][2 n_q]: 2 n_q contiguous values per (head, slice)) are read as whole
+// lines into LDS, where k_conv_apply's 16 workgroups per row each used 8 bytes of every
+// 128-byte line they read; each tap is then summed exactly as k_conv_apply sums it (lane
+// j adds the partials j, j + 64, ... in order, then the same wave sum), so the two
+// kernels give identical bits.
+constexpr int ROW_NI = 16;          // outputs per thread (n_q d <= 4096)
+
+__global__ __launch_bounds__(256) void k_conv_rows(MergeConvArgs a) {
+    extern __shared__ float zrow[];
+    const int b = blockIdx.x / a.T, t = blockIdx.x % a.T, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int qd = a.n_q * a.d, nq2 = 2 * a.n_q, np = a.n_q * (a.d / MC), ZS = nq2 + 1;
+    float *Z = zrow, *z = zrow + np * ZS;
+    // the attention outputs of rows t and t - 1 this thread scales, loaded with the partials
+    const float *ot = a.o + ((size_t)b * a.T + t) * qd;
+    const float *op = t > 0 ? ot - qd : ot;              // row t - 1 (t = 0: unused)
+    float ocur[ROW_NI], oprev[ROW_NI];
+#pragma unroll
+    for (int u = 0; u < ROW_NI; u++) {
+        const int i = min(tid + 256 * u, qd - 1);
+        ocur[u] = ot[i];
+        oprev[u] = op[i];
+    }
+    const float *zp = a.zp + (size_t)b * np * a.T * nq2 + (size_t)t * nq2;
+    for (int e = tid; e < np * nq2 / 4; e += 256) {
+        const int p = e / (nq2 / 4), q = 4 * (e % (nq2 / 4));
+        const float4 v = *reinterpret_cast<const float4 *>(zp + (size_t)p * a.T * nq2 + q);
+        float *d = Z + p * ZS + q;
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+    __syncthreads();
+    for (int q = wave; q < nq2; q += 4) {
+        float s = 0.f;
+        for (int p = lane; p < np; p += 64) s += Z[p * ZS + q];
+        s = wave_sum(s);
+        if (lane == 0) z[q] = s;
+    }
+    __syncthreads();
+    uint16_t *Y = a.Y + ((size_t)b * a.T + t) * qd;
+#pragma unroll
+    for (int u = 0; u < ROW_NI; u++) {
+        const int i = tid + 256 * u;
+        if (i < qd) {
+            const int h = i / a.d;
+            Y[i] = f32_to_bf16(z[h] * ocur[u] + (t > 0 ? z[a.n_q + h] * oprev[u] : 0.f));
         }
     }
 }
@@ -623,7 +677,13 @@ hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st) {
         hipLaunchKernelGGL(k_attn_merge<9>, dim3(a.n_q, a.d / MC, a.B), dim3(256), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_conv_apply, dim3(a.B * a.T, a.n_q / CONV_HEADS), dim3(256), 0, st, a);
+    // one workgroup per row where the rows fill the chip (and the row's partials fit LDS)
+    const int np = a.n_q * (a.d / MC), nq2 = 2 * a.n_q;
+    const size_t zl = ((size_t)np * (nq2 + 1) + nq2) * 4;
+    if (a.B * a.T >= CONV_ROWS_MIN && a.n_q * a.d <= 256 * ROW_NI && nq2 % 4 == 0 && zl <= 64 * 1024)
+        hipLaunchKernelGGL(k_conv_rows, dim3(a.B * a.T), dim3(256), zl, st, a);
+    else
+        hipLaunchKernelGGL(k_conv_apply, dim3(a.B * a.T, a.n_q / CONV_HEADS), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
