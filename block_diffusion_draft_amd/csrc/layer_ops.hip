@@ -154,6 +154,80 @@ __global__ __launch_bounds__(256) void k_reduce_rows(ReduceRowsArgs a) {
     reduce_rows_block<RB>(a, blockIdx.x, blockIdx.y);
 }
 
+// The same reduction with one wave per (row, 256 columns), four per workgroup, and no
+// workgroup barrier, for many rows: each lane holds 4 adjacent columns and issues the
+// loads of up to SB splits at once.  It keeps reduce_rows_block's order of additions (the
+// sums of splits w, w + 4, ... for w = 0..3, added in w order; the sum of squares as four
+// wave sums over 64-column groups, added in group order); the results still differ from
+// it in the last bits (a 5-layer batch-1 step's hidden states by up to 3e-4), so which
+// kernel runs is fixed by the row count.  Measured per step: 64 sequences 6.028 ->
+// 5.960 ms; 16 sequences 2.686 -> 2.701 ms and batch 1 0.849 -> 0.859 ms, where
+// reduce_rows_block stays.
+template <int SB>
+__global__ __launch_bounds__(256) void k_reduce_rows_w(ReduceRowsArgs a) {
+    static_assert(SB % 4 == 0, "a batch holds whole rounds of the four split classes");
+    __shared__ float sqs[4][256];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nc = a.N / 256, item = blockIdx.x * 4 + wave;
+    if (item >= a.M_out * nc) return;
+    const int r = item / nc, cx = item % nc, c0 = cx * 256 + 4 * lane;
+    const int splits = a.splits, pair = a.pair, N = a.N;
+    const size_t stride = (size_t)(pair ? 2 * a.M_out : a.M_out) * N;
+    const float *p = a.part + (size_t)r * N + c0;
+    float4 s[4];
+#pragma unroll
+    for (int w = 0; w < 4; w++) s[w] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = 0; k0 < splits; k0 += SB) {
+        float4 va[SB], vb[SB];
+#pragma unroll
+        for (int u = 0; u < SB; u++) {
+            const float *q = p + (size_t)min(k0 + u, splits - 1) * stride;
+            va[u] = *reinterpret_cast<const float4 *>(q);
+            vb[u] = pair ? *reinterpret_cast<const float4 *>(q + (size_t)pair * N)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < SB; u++)
+            if (k0 + u < splits) {
+                float4 &t = s[u & 3];               // split k0 + u is of class (k0 + u) % 4 = u % 4
+                t.x += va[u].x + vb[u].x;
+                t.y += va[u].y + vb[u].y;
+                t.z += va[u].z + vb[u].z;
+                t.w += va[u].w + vb[u].w;
+            }
+    }
+    float v[4] = {((s[0].x + s[1].x) + s[2].x) + s[3].x, ((s[0].y + s[1].y) + s[2].y) + s[3].y,
+                  ((s[0].z + s[1].z) + s[2].z) + s[3].z, ((s[0].w + s[1].w) + s[2].w) + s[3].w};
+    float *fp = a.f + (size_t)r * N + c0;
+    if (a.add) {
+        const float4 f = *reinterpret_cast<const float4 *>(fp);
+        v[0] += f.x; v[1] += f.y; v[2] += f.z; v[3] += f.w;
+    }
+    *reinterpret_cast<float4 *>(fp) = make_float4(v[0], v[1], v[2], v[3]);
+    // squares regrouped so that lane l holds column 64 g + l of each 64-column group g
+    *reinterpret_cast<float4 *>(&sqs[wave][4 * lane]) =
+        make_float4(v[0] * v[0], v[1] * v[1], v[2] * v[2], v[3] * v[3]);
+    __builtin_amdgcn_wave_barrier();
+    float q[4];
+#pragma unroll
+    for (int g = 0; g < 4; g++) q[g] = wave_sum(sqs[wave][64 * g + lane]);
+    if (lane == 0) a.ssq[(size_t)r * nc + cx] = q[0] + q[1] + q[2] + q[3];
+    if (!a.out || (a.map > 0 && r % a.map == 0)) return;
+    const int orow = a.map > 0 ? (r / a.map) * (a.map - 1) + r % a.map - 1 : r;
+    uint16_t hb[4], lb[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float x = v[i] * bf16_to_f32(a.gain[c0 + i]);
+        hb[i] = f32_to_bf16(x);
+        lb[i] = f32_to_bf16(x - bf16_to_f32(hb[i]));
+    }
+    *reinterpret_cast<u32x2_t *>(a.out + (size_t)orow * a.ldo + c0) =
+        (u32x2_t){(uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+    if (a.out_lo)
+        *reinterpret_cast<u32x2_t *>(a.out_lo + (size_t)orow * a.ldo + c0) =
+            (u32x2_t){(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
+}
+
 // one launch for two independent jobs: the reduction's (N / 256) x M_out workgroups,
 // then the block assembly's B T workgroups
 template <int RB>
@@ -688,6 +762,14 @@ hipError_t launch_merge_conv(const MergeConvArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_reduce_norm(const ReduceRowsArgs &a, hipStream_t st) {
+    // many rows: a wave per (row, 256 columns), its splits' loads in one batch up to 20
+    const unsigned grid = (unsigned)ceil_div(a.M_out * (a.N / 256), 4);
+    if (a.M_out >= 512 && a.ldo % 4 == 0) {
+        if (a.splits > 8) hipLaunchKernelGGL(k_reduce_rows_w<20>, dim3(grid), dim3(256), 0, st, a);
+        else if (a.splits > 4) hipLaunchKernelGGL(k_reduce_rows_w<8>, dim3(grid), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL(k_reduce_rows_w<4>, dim3(grid), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
     if (a.splits > 16) hipLaunchKernelGGL(k_reduce_rows<8>, dim3(a.N / 256, a.M_out), dim3(256), 0, st, a);
     else hipLaunchKernelGGL(k_reduce_rows<4>, dim3(a.N / 256, a.M_out), dim3(256), 0, st, a);
     return hipGetLastError();
